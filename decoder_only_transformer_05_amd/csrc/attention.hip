@@ -1,0 +1,477 @@
+// attention.hip -- causal multi-head self-attention, forward and backward, on gfx950 MFMA.
+//
+// What is computed is section 1.7 attention_forward and section 1.8 attention_backward of
+// "llm.c 的中文注解-20240421" (and the Attention / causal mask sections of "高能技巧！60 行
+// NumPy 代码实现一个 GPT"): per (batch b, head h), S = Q K^T / sqrt(hs) restricted to keys
+// t2 <= t, P = row softmax of S, O = P V; backward dV = P^T dO, dP = dO V^T,
+// dS = P * (dP - rowsum(P * dP)), dQ = dS K / sqrt(hs), dK = dS^T Q / sqrt(hs).
+//
+// How it differs from the pages' loops: the (B,NH,T,T) score and probability matrices
+// are never stored. The forward keeps a running max and sum per query row over 64-key
+// tiles (online softmax) and saves only the row log-sum-exp; the backward recomputes P
+// from Q, K and that log-sum-exp, and uses rowsum(P*dP) = rowsum(dO*O) (precomputed per
+// row). dK/dV and dQ come from two kernels that each own their outputs, so nothing is
+// accumulated with atomics and results are deterministic.
+//
+// MFMA layout trick: S is computed transposed (keys down the rows, one query per lane
+// column), so the softmax statistics of a query live in a single lane (plus its partner
+// lane 32 away), and P^T is already in the register layout of the B operand of the next
+// MFMA (O^T = V^T P^T). No shuffles or LDS round trips are needed between the two
+// products. The head dimension is contracted in the permuted order
+// d(s, half) = 8*(s/4) + 4*half + s%4, which lets one 16-byte LDS read feed four MFMAs;
+// both operands use the same order, so the dot products are unchanged.
+#include <cmath>
+
+#include "kernels.h"
+
+namespace gpt2 {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int TILE = 64;    // queries per workgroup / keys per LDS tile
+constexpr int NTHR = 128;   // two waves, 32 queries (or keys) each
+
+GPT2_DEVICE_INLINE f32x4 load4_masked(const float* p, bool ok) {
+  return ok ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Cooperative load of `rows` x HSP values starting at row `row0` of a strided tensor
+// (row stride `ld`, column offset already applied) into S[TILE][HSP+4]; rows >= T and
+// columns >= hs are zero.
+template <int HSP>
+GPT2_DEVICE_INLINE void load_tile(float (*S)[HSP + 4], const float* base, long long ld,
+                                  int row0, int T, int hs, int tid) {
+  constexpr int F4 = HSP / 4;
+#pragma unroll
+  for (int i = 0; i < TILE * F4 / NTHR; i++) {
+    const int f = tid + NTHR * i;
+    const int row = f / F4, d = 4 * (f % F4);
+    const int t = row0 + row;
+    *reinterpret_cast<f32x4*>(&S[row][d]) =
+        load4_masked(base + (long long)t * ld + d, t < T && d < hs);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------------------
+template <int HSP>
+__global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
+                                                        float* __restrict__ lse,
+                                                        const float* __restrict__ qkv, int T,
+                                                        int C, int NH, int hs,
+                                                        float scale_log2) {
+  constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
+  __shared__ float Ks[TILE][LD];
+  __shared__ float Vs[TILE][LD];
+
+  const int nqt = (T + TILE - 1) / TILE;
+  const int qt = nqt - 1 - blockIdx.x;  // longest rows first
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, hf = lane >> 5;
+  const long long C3 = 3LL * C;
+  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const int q = qt * TILE + wave * 32 + r;
+  const int qm = min(q, T - 1);  // lanes past the end mask as the last row; never stored
+
+  float qf[NS];
+#pragma unroll
+  for (int g = 0; g < HSP / 8; g++) {
+    const int d = 8 * g + 4 * hf;
+    f32x4 v = load4_masked(base + (long long)qm * C3 + d, d < hs);
+#pragma unroll
+    for (int j = 0; j < 4; j++) qf[4 * g + j] = v[j] * scale_log2;
+  }
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kv_end = min(T, (qt + 1) * TILE);
+  const int ntiles = (kv_end + TILE - 1) / TILE;
+  for (int kt = 0; kt < ntiles; kt++) {
+    const int key0 = kt * TILE;
+    __syncthreads();
+    load_tile<HSP>(Ks, base + C, C3, key0, T, hs, tid);
+    load_tile<HSP>(Vs, base + 2 * C, C3, key0, T, hs, tid);
+    __syncthreads();
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
+#pragma unroll
+      for (int g = 0; g < HSP / 8; g++) {
+        f32x4 kv = *reinterpret_cast<const f32x4*>(&Ks[32 * kb + r][8 * g + 4 * hf]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) s[kb] = mfma32x32x2(kv[j], qf[4 * g + j], s[kb]);
+      }
+    }
+    float mx = -INFINITY;
+    const bool diag = key0 + TILE > qt * TILE;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (diag && key > qm) s[kb][i] = -INFINITY;
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);  // finite: key0 = 0 <= qm is in the first tile
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float p = exp2f(s[kb][i] - m_new);
+        s[kb][i] = p;
+        l_run += p;
+      }
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int st = 0; st < 32; st++) {
+        const int kb = st / 16, i = st % 16;
+        const int kl = 32 * kb + 8 * (i / 4) + 4 * hf + (i % 4);
+        oacc[db] = mfma32x32x2(Vs[kl][32 * db + r], s[kb][i], oacc[db]);
+      }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (q < T) {
+    float* o = out + ((long long)b * T + q) * C + (long long)head * hs;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * hf;
+        if (d < hs)
+          *reinterpret_cast<f32x4*>(o + d) =
+              f32x4{oacc[db][4 * ig] * inv, oacc[db][4 * ig + 1] * inv,
+                    oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv};
+      }
+    if (hf == 0) lse[((long long)b * NH + head) * T + q] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// backward: D = rowsum(dO * O) per (b, head, query)
+// ---------------------------------------------------------------------------------------
+__global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const float* __restrict__ dout,
+                                       const float* __restrict__ out, int B, int T, int C,
+                                       int NH, int hs) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)B * NH * T) return;
+  const int q = (int)(idx % T);
+  const int head = (int)((idx / T) % NH);
+  const int b = (int)(idx / ((long long)T * NH));
+  const long long off = ((long long)b * T + q) * C + (long long)head * hs;
+  float s = 0.f;
+  for (int d = 0; d < hs; d += 4) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(dout + off + d);
+    f32x4 o = *reinterpret_cast<const f32x4*>(out + off + d);
+    s += a[0] * o[0] + a[1] * o[1] + a[2] * o[2] + a[3] * o[3];
+  }
+  D[idx] = s;
+}
+
+// dK, dV for a tile of 64 keys (32 per wave), looping over query tiles from the diagonal.
+template <int HSP>
+__global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
+    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
+    const float* __restrict__ lse, const float* __restrict__ Drow, int T, int C, int NH,
+    int hs, float scale, float scale_log2) {
+  constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
+  __shared__ float Qs[TILE][LD];
+  __shared__ float dOs[TILE][LD];
+  __shared__ float Ls[TILE];
+  __shared__ float Ds[TILE];
+
+  const int nkt = (T + TILE - 1) / TILE;
+  const int kt = nkt - 1 - blockIdx.x;  // ordering only; every tile is independent
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, hf = lane >> 5;
+  const long long C3 = 3LL * C;
+  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const float* dobase = dout + (long long)b * T * C + (long long)head * hs;
+  const float* lrow = lse + ((long long)b * NH + head) * T;
+  const float* drow = Drow + ((long long)b * NH + head) * T;
+  const int key = kt * TILE + wave * 32 + r;
+  const int km = min(key, T - 1);
+
+  float kf[NS], vf[NS];
+#pragma unroll
+  for (int g = 0; g < HSP / 8; g++) {
+    const int d = 8 * g + 4 * hf;
+    f32x4 kv = load4_masked(base + (long long)km * C3 + C + d, d < hs);
+    f32x4 vv = load4_masked(base + (long long)km * C3 + 2 * C + d, d < hs);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      kf[4 * g + j] = kv[j];
+      vf[4 * g + j] = vv[j];
+    }
+  }
+  f32x16 dvacc[ND], dkacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      dvacc[db][i] = 0.f;
+      dkacc[db][i] = 0.f;
+    }
+
+  const int nqt = (T + TILE - 1) / TILE;
+  for (int qt = kt; qt < nqt; qt++) {
+    const int q0 = qt * TILE;
+    __syncthreads();
+    load_tile<HSP>(Qs, base, C3, q0, T, hs, tid);
+    load_tile<HSP>(dOs, dobase, C, q0, T, hs, tid);
+    if (tid < TILE) {
+      const int t = q0 + tid;
+      Ls[tid] = t < T ? lrow[t] * kLog2e : 0.f;
+      Ds[tid] = t < T ? drow[t] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      // skip sub-blocks that lie entirely above the diagonal for this wave's keys
+      if (q0 + 32 * qb + 31 < kt * TILE + wave * 32) continue;
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < HSP / 8; g++) {
+        f32x4 qv = *reinterpret_cast<const f32x4*>(&Qs[32 * qb + r][8 * g + 4 * hf]);
+        f32x4 ov = *reinterpret_cast<const f32x4*>(&dOs[32 * qb + r][8 * g + 4 * hf]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          s = mfma32x32x2(qv[j], kf[4 * g + j], s);
+          dp = mfma32x32x2(ov[j], vf[4 * g + j], dp);
+        }
+      }
+      // s[i], dp[i]: query row ql = 32qb + 8(i/4) + 4hf + i%4, key column = this lane's key
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int qa = q0 + ql;
+        const bool ok = qa < T && qa >= key;
+        const float p = ok ? exp2f(s[i] * scale_log2 - Ls[ql]) : 0.f;
+        s[i] = p;
+        dp[i] = p * (dp[i] - Ds[ql]);
+      }
+#pragma unroll
+      for (int db = 0; db < ND; db++)
+#pragma unroll
+        for (int st = 0; st < 16; st++) {
+          const int ql = 32 * qb + 8 * (st / 4) + 4 * hf + (st % 4);
+          dvacc[db] = mfma32x32x2(dOs[ql][32 * db + r], s[st], dvacc[db]);
+          dkacc[db] = mfma32x32x2(Qs[ql][32 * db + r], dp[st], dkacc[db]);
+        }
+    }
+  }
+  if (key < T) {
+    float* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
+    float* dv = dk + C;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * hf;
+        if (d < hs) {
+          *reinterpret_cast<f32x4*>(dk + d) =
+              f32x4{dkacc[db][4 * ig] * scale, dkacc[db][4 * ig + 1] * scale,
+                    dkacc[db][4 * ig + 2] * scale, dkacc[db][4 * ig + 3] * scale};
+          *reinterpret_cast<f32x4*>(dv + d) =
+              f32x4{dvacc[db][4 * ig], dvacc[db][4 * ig + 1], dvacc[db][4 * ig + 2],
+                    dvacc[db][4 * ig + 3]};
+        }
+      }
+  }
+}
+
+// dQ for a tile of 64 queries (32 per wave), looping over key tiles up to the diagonal.
+template <int HSP>
+__global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(
+    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
+    const float* __restrict__ lse, const float* __restrict__ Drow, int T, int C, int NH,
+    int hs, float scale, float scale_log2) {
+  constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
+  __shared__ float Ks[TILE][LD];
+  __shared__ float Vs[TILE][LD];
+
+  const int nqt = (T + TILE - 1) / TILE;
+  const int qt = nqt - 1 - blockIdx.x;
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, hf = lane >> 5;
+  const long long C3 = 3LL * C;
+  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const float* dobase = dout + (long long)b * T * C + (long long)head * hs;
+  const int q = qt * TILE + wave * 32 + r;
+  const int qm = min(q, T - 1);
+  const float lq = lse[((long long)b * NH + head) * T + qm] * kLog2e;
+  const float Dq = Drow[((long long)b * NH + head) * T + qm];
+
+  float qf[NS], of[NS];
+#pragma unroll
+  for (int g = 0; g < HSP / 8; g++) {
+    const int d = 8 * g + 4 * hf;
+    f32x4 qv = load4_masked(base + (long long)qm * C3 + d, d < hs);
+    f32x4 ov = load4_masked(dobase + (long long)qm * C + d, d < hs);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      qf[4 * g + j] = qv[j];
+      of[4 * g + j] = ov[j];
+    }
+  }
+  f32x16 dqacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) dqacc[db][i] = 0.f;
+
+  for (int kt = 0; kt <= qt; kt++) {
+    const int key0 = kt * TILE;
+    __syncthreads();
+    load_tile<HSP>(Ks, base + C, C3, key0, T, hs, tid);
+    load_tile<HSP>(Vs, base + 2 * C, C3, key0, T, hs, tid);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      if (key0 + 32 * kb > qt * TILE + wave * 32 + 31) continue;  // all keys above diagonal
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < HSP / 8; g++) {
+        f32x4 kv = *reinterpret_cast<const f32x4*>(&Ks[32 * kb + r][8 * g + 4 * hf]);
+        f32x4 vv = *reinterpret_cast<const f32x4*>(&Vs[32 * kb + r][8 * g + 4 * hf]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          s = mfma32x32x2(kv[j], qf[4 * g + j], s);
+          dp = mfma32x32x2(vv[j], of[4 * g + j], dp);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const bool ok = key <= qm && key < T;
+        const float p = ok ? exp2f(s[i] * scale_log2 - lq) : 0.f;
+        dp[i] = p * (dp[i] - Dq);
+      }
+#pragma unroll
+      for (int db = 0; db < ND; db++)
+#pragma unroll
+        for (int st = 0; st < 16; st++) {
+          const int kl = 32 * kb + 8 * (st / 4) + 4 * hf + (st % 4);
+          dqacc[db] = mfma32x32x2(Ks[kl][32 * db + r], dp[st], dqacc[db]);
+        }
+    }
+  }
+  if (q < T) {
+    float* dq = dqkv + ((long long)b * T + q) * C3 + (long long)head * hs;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * hf;
+        if (d < hs)
+          *reinterpret_cast<f32x4*>(dq + d) =
+              f32x4{dqacc[db][4 * ig] * scale, dqacc[db][4 * ig + 1] * scale,
+                    dqacc[db][4 * ig + 2] * scale, dqacc[db][4 * ig + 3] * scale};
+      }
+  }
+}
+
+bool check_shape(int B, int T, int C, int NH, int* hsp) {
+  if (B < 1 || T < 1 || C < 1 || NH < 1 || C % NH) return false;
+  const int hs = C / NH;
+  if (hs % 4 || C % 4) return false;
+  if (hs <= 32) *hsp = 32;
+  else if (hs <= 64) *hsp = 64;
+  else if (hs <= 128) *hsp = 128;
+  else return false;
+  return true;
+}
+
+}  // namespace
+
+int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                      hipStream_t stream) {
+  int hsp;
+  if (!check_shape(B, T, C, NH, &hsp)) {
+    set_global_error("attention: unsupported shape B=%d T=%d C=%d NH=%d", B, T, C, NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale_log2 = kLog2e / sqrtf((float)hs);
+  dim3 grid((T + TILE - 1) / TILE, NH, B);
+  const double tri = (double)T * (T + 1) / 2.0;  // causal (query, key) pairs per head
+  ProfScope ps("attn_fwd_kernel", 4.0 * B * NH * hs * tri,
+               4.0 * ((double)B * T * 3 * C + (double)B * T * C + (double)B * NH * T), stream);
+  if (hsp == 32) attn_fwd_kernel<32><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else if (hsp == 64) attn_fwd_kernel<64><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else attn_fwd_kernel<128><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
+                       const float* lse, float* dscratch, int B, int T, int C, int NH,
+                       hipStream_t stream) {
+  int hsp;
+  if (!check_shape(B, T, C, NH, &hsp)) {
+    set_global_error("attention: unsupported shape B=%d T=%d C=%d NH=%d", B, T, C, NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale = 1.0f / sqrtf((float)hs);
+  const float scale_log2 = scale * kLog2e;
+  const long long rows = (long long)B * NH * T;
+  const double BTC = (double)B * T * C, tri = (double)T * (T + 1) / 2.0;
+  {
+    ProfScope ps("attn_bwd_rowdot_kernel", 2.0 * BTC, 4.0 * (2.0 * BTC + rows), stream);
+    attn_bwd_rowdot_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+        dscratch, dout, out, B, T, C, NH, hs);
+  }
+  dim3 grid((T + TILE - 1) / TILE, NH, B);
+  {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
+    ProfScope ps("attn_bwd_dkdv_kernel", 6.0 * B * NH * hs * tri,
+                 4.0 * (3.0 * BTC + BTC + 2.0 * rows + 2.0 * BTC), stream);
+    if (hsp == 32) attn_bwd_dkdv_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hsp == 64) attn_bwd_dkdv_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dkdv_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+  }
+  {  // dQ = dS K
+    ProfScope ps("attn_bwd_dq_kernel", 2.0 * B * NH * hs * tri,
+                 4.0 * (3.0 * BTC + BTC + 2.0 * rows + BTC), stream);
+    if (hsp == 32) attn_bwd_dq_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hsp == 64) attn_bwd_dq_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dq_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+  }
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+}  // namespace gpt2

@@ -1,0 +1,412 @@
+// gemm.hip -- fp32 GEMMs of the training step on gfx950 MFMA (v_mfma_f32_32x32x2_f32).
+//
+// Every linear layer of "llm.c 的中文注解-20240421" (section 1.5 matmul_forward,
+// section 1.6 matmul_backward) is one of three storage patterns of C = A . B:
+//   forward      out  = inp . W^T   A (M,K) row-major, B = W stored (N,K)     ("NT")
+//   grad input   dinp = dout . W    A (M,K) row-major, B = W stored (K,N)     ("NN")
+//   grad weight  dW  += dout^T.inp  A = dout stored (K,M), B = inp (K,N)      ("TN")
+// with fused epilogues: bias, bias+GELU (section 1.9), bias+residual (section 1.11),
+// accumulate, and the GELU backward (section 1.10).
+//
+// Tiling: a 256-thread workgroup owns a 128x128 tile of C; its four waves own 64x64
+// sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances 32 at a time through two LDS
+// buffers: global loads for the next K-slab are issued before the MFMAs of the current one
+// and written to the other buffer afterwards, so one barrier per slab suffices.
+// LDS holds both operands K-major ([k][m] and [k][n], row stride 130 floats): a lane's two
+// MFMA blocks along M take adjacent rows m = 2r and 2r+1, so one 8-byte LDS read feeds two
+// MFMAs, and the results are un-interleaved in the epilogue.
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace gpt2 {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int LDSA = BM + 2, LDSB = BN + 2;
+constexpr int NTHREADS = 256;
+
+struct Args {
+  const float* A;
+  const float* B;
+  float* C;
+  float* C2;
+  const float* R;
+  const float* bias;
+  int lda, ldb, ldc;
+  int M, N, K;
+  int k_split;      // K elements per blockIdx.z (multiple of BK)
+  long long c_zstride;  // floats between the partial outputs of successive splits (0 = none)
+};
+
+// Loads one K-slab of an operand into registers (4 float4 per thread) and later stores it to
+// LDS in [k][row] order. `rows` is M (for A) or N (for B).
+//  trans == false: operand stored (rows, K) row-major: thread -> (row = tid/8 + 32i, k4 = tid%8)
+//  trans == true : operand stored (K, rows):          thread -> (k = tid/32 + 8i, r4 = tid%32)
+template <bool TRANS>
+struct SlabLoader {
+  f32x4 v[4];
+
+  __device__ __forceinline__ void load(const float* __restrict__ P, int ld, int row0, int rows,
+                                       int k0, int kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (!TRANS) {
+        int r = row0 + tid / 8 + 32 * i;
+        int k = k0 + 4 * (tid % 8);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (r < rows && k < kend) {
+          x = *reinterpret_cast<const f32x4*>(P + (long long)r * ld + k);
+          if (k + 3 >= kend) {
+            if (k + 1 >= kend) x[1] = 0.f;
+            if (k + 2 >= kend) x[2] = 0.f;
+            if (k + 3 >= kend) x[3] = 0.f;
+          }
+        }
+        v[i] = x;
+      } else {
+        int k = k0 + tid / 32 + 8 * i;
+        int r = row0 + 4 * (tid % 32);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (k < kend && r < rows) x = *reinterpret_cast<const f32x4*>(P + (long long)k * ld + r);
+        v[i] = x;
+      }
+    }
+  }
+
+  template <int LDS>
+  __device__ __forceinline__ void store(float (*S)[LDS], int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (!TRANS) {
+        int r = tid / 8 + 32 * i;
+        int k = 4 * (tid % 8);
+        S[k + 0][r] = v[i][0];
+        S[k + 1][r] = v[i][1];
+        S[k + 2][r] = v[i][2];
+        S[k + 3][r] = v[i][3];
+      } else {
+        int k = tid / 32 + 8 * i;
+        int r = 4 * (tid % 32);
+        *reinterpret_cast<f32x2*>(&S[k][r]) = f32x2{v[i][0], v[i][1]};
+        *reinterpret_cast<f32x2*>(&S[k][r + 2]) = f32x2{v[i][2], v[i][3]};
+      }
+    }
+  }
+};
+
+template <int EPI>
+__device__ __forceinline__ void epilogue_pair(const Args& g, float* C, int m, int n, float v0,
+                                              float v1) {
+  if (m >= g.M || n >= g.N) return;
+  const bool two = n + 1 < g.N;
+  long long off = (long long)m * g.ldc + n;
+  if (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
+    if (g.bias) {
+      v0 += g.bias[n];
+      if (two) v1 += g.bias[n + 1];
+    }
+  }
+  if (EPI == EPI_RESID) {
+    if (two) {
+      f32x2 r = *reinterpret_cast<const f32x2*>(g.R + off);
+      v0 += r[0];
+      v1 += r[1];
+    } else {
+      v0 += g.R[off];
+    }
+  }
+  if (EPI == EPI_ACCUM) {
+    if (two) {
+      f32x2 c = *reinterpret_cast<const f32x2*>(C + off);
+      v0 += c[0];
+      v1 += c[1];
+    } else {
+      v0 += C[off];
+    }
+  }
+  if (EPI == EPI_GELU_BWD) {
+    if (two) {
+      f32x2 r = *reinterpret_cast<const f32x2*>(g.R + off);
+      v0 *= gelu_bwd(r[0]);
+      v1 *= gelu_bwd(r[1]);
+    } else {
+      v0 *= gelu_bwd(g.R[off]);
+    }
+  }
+  if (two) {
+    *reinterpret_cast<f32x2*>(C + off) = f32x2{v0, v1};
+    if (EPI == EPI_GELU) *reinterpret_cast<f32x2*>(g.C2 + off) = f32x2{gelu_fwd(v0), gelu_fwd(v1)};
+  } else {
+    C[off] = v0;
+    if (EPI == EPI_GELU) g.C2[off] = gelu_fwd(v0);
+  }
+}
+
+template <bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
+  __shared__ float As[2][BK][LDSA];
+  __shared__ float Bs[2][BK][LDSB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int wm0 = (wave >> 1) * 64, wn0 = (wave & 1) * 64;
+
+  const int kbeg = blockIdx.z * g.k_split;
+  const int kend = min(g.K, kbeg + g.k_split);
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+
+  SlabLoader<AT> la;
+  SlabLoader<BT> lb;
+  if (ntiles > 0) {
+    la.load(g.A, g.lda, m0, g.M, kbeg, kend, tid);
+    lb.load(g.B, g.ldb, n0, g.N, kbeg, kend, tid);
+    la.template store<LDSA>(As[0], tid);
+    lb.template store<LDSB>(Bs[0], tid);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; kt++) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < ntiles;
+    if (more) {
+      const int k0 = kbeg + (kt + 1) * BK;
+      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
+      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+    }
+#pragma unroll
+    for (int kk2 = 0; kk2 < BK / 2; kk2++) {
+      const int kk = 2 * kk2 + h;
+      f32x2 a = *reinterpret_cast<const f32x2*>(&As[cur][kk][wm0 + 2 * r]);
+      f32x2 b = *reinterpret_cast<const f32x2*>(&Bs[cur][kk][wn0 + 2 * r]);
+      acc[0][0] = mfma32x32x2(a[0], b[0], acc[0][0]);
+      acc[0][1] = mfma32x32x2(a[0], b[1], acc[0][1]);
+      acc[1][0] = mfma32x32x2(a[1], b[0], acc[1][0]);
+      acc[1][1] = mfma32x32x2(a[1], b[1], acc[1][1]);
+    }
+    if (more) {
+      la.template store<LDSA>(As[cur ^ 1], tid);
+      lb.template store<LDSB>(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  float* C = g.C + (long long)blockIdx.z * g.c_zstride;
+#pragma unroll
+  for (int bm = 0; bm < 2; bm++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int row = 8 * (i / 4) + 4 * h + (i % 4);
+      const int m = m0 + wm0 + 2 * row + bm;
+      const int n = n0 + wn0 + 2 * r;
+      epilogue_pair<EPI>(g, C, m, n, acc[bm][0][i], acc[bm][1][i]);
+    }
+}
+
+// Sums `splits` partial results (each M x N, row stride wld) into C with the epilogue `EPI`
+// (only EPI_STORE-with-bias, EPI_ACCUM and EPI_GELU_BWD are used with splits), adding the
+// partials in split order.
+template <int EPI>
+__global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int splits, int wld) {
+  const long long total = (long long)g.M * g.N;
+  const long long zstride = (long long)g.M * wld;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int m = (int)(idx / g.N), n = (int)(idx % g.N);
+    const long long widx = (long long)m * wld + n;
+    float s = 0.f;
+    for (int z = 0; z < splits; z++) s += ws[(long long)z * zstride + widx];
+    const long long off = (long long)m * g.ldc + n;
+    if (EPI == EPI_ACCUM) {
+      g.C[off] += s;
+    } else if (EPI == EPI_GELU_BWD) {
+      g.C[off] = s * gelu_bwd(g.R[off]);
+    } else {
+      g.C[off] = s + (g.bias ? g.bias[n] : 0.f);
+    }
+  }
+}
+
+template <bool AT, bool BT>
+void launch_tn(const Args& a, int epi, dim3 grid, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: gemm_kernel<AT, BT, EPI_STORE><<<grid, NTHREADS, 0, s>>>(a); break;
+    case EPI_GELU: gemm_kernel<AT, BT, EPI_GELU><<<grid, NTHREADS, 0, s>>>(a); break;
+    case EPI_RESID: gemm_kernel<AT, BT, EPI_RESID><<<grid, NTHREADS, 0, s>>>(a); break;
+    case EPI_ACCUM: gemm_kernel<AT, BT, EPI_ACCUM><<<grid, NTHREADS, 0, s>>>(a); break;
+    case EPI_GELU_BWD: gemm_kernel<AT, BT, EPI_GELU_BWD><<<grid, NTHREADS, 0, s>>>(a); break;
+  }
+}
+
+void launch(const Args& a, bool at, bool bt, int epi, dim3 grid, hipStream_t s) {
+  if (!at && !bt) launch_tn<false, false>(a, epi, grid, s);
+  else if (!at && bt) launch_tn<false, true>(a, epi, grid, s);
+  else if (at && bt) launch_tn<true, true>(a, epi, grid, s);
+  else launch_tn<true, false>(a, epi, grid, s);
+}
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Number of K splits for a problem: enough workgroups to give every CU about two, and each
+// split at least 4 K-slabs deep.
+int choose_splits(const Gemm& g) {
+  const long long tiles = (long long)ceil_div(g.M, BM) * ceil_div(g.N, BN);
+  const long long target = 2 * 256;
+  if (tiles >= target) return 1;
+  int s = (int)((target + tiles - 1) / tiles);
+  const int max_by_k = g.K / (4 * BK);
+  if (s > max_by_k) s = max_by_k;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+// partial results of a split GEMM are stored with an even row stride (8-byte stores)
+int split_ld(int N) { return (N + 1) & ~1; }
+
+size_t gemm_workspace_floats(const Gemm& g) {
+  if (g.epi == EPI_GELU || g.epi == EPI_RESID) return 0;
+  int s = choose_splits(g);
+  return s > 1 ? (size_t)s * g.M * split_ld(g.N) : 0;
+}
+
+int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) {
+    set_global_error("gemm: non-positive size M=%d N=%d K=%d", g.M, g.N, g.K);
+    return -1;
+  }
+  // float4 operand loads: 16-byte aligned bases and leading dimensions that are multiples
+  // of 4 (which also keeps the last float4 of a row inside the row's storage)
+  const int a_cols = g.a_trans ? g.M : g.K, b_cols = g.b_trans ? g.N : g.K;
+  if (!aligned16(g.A) || !aligned16(g.B) || !aligned16(g.C) || g.lda % 4 || g.ldb % 4 ||
+      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N) {
+    set_global_error("gemm: unsupported alignment or leading dimension (lda=%d ldb=%d ldc=%d)",
+                     g.lda, g.ldb, g.ldc);
+    return -1;
+  }
+  if ((g.epi == EPI_GELU && !g.C2) || ((g.epi == EPI_RESID || g.epi == EPI_GELU_BWD) && !g.R)) {
+    set_global_error("gemm: epilogue %d is missing an operand", (int)g.epi);
+    return -1;
+  }
+  Args a;
+  a.A = g.A;
+  a.B = g.B;
+  a.C = g.C;
+  a.C2 = g.C2;
+  a.R = g.R;
+  a.bias = g.bias;
+  a.lda = g.lda;
+  a.ldb = g.ldb;
+  a.ldc = g.ldc;
+  a.M = g.M;
+  a.N = g.N;
+  a.K = g.K;
+  a.c_zstride = 0;
+
+  int splits = (g.epi == EPI_GELU || g.epi == EPI_RESID) ? 1 : choose_splits(g);
+  if (splits > 1 && (!workspace || ws_floats < (size_t)splits * g.M * split_ld(g.N))) splits = 1;
+  const int kt = ceil_div(g.K, BK);
+  const int kt_per = ceil_div(kt, splits);
+  splits = ceil_div(kt, kt_per);
+  a.k_split = kt_per * BK;
+
+  const double MN = (double)g.M * g.N;
+  const double flop = 2.0 * MN * g.K;
+  const double in_bytes = 4.0 * ((double)g.M * g.K + (double)g.N * g.K);
+  // output traffic of an epilogue: stores, plus the extra tensor it reads or writes
+  const double out_factor = g.epi == EPI_STORE ? 1.0 : 2.0;
+  char name[64];
+  if (splits == 1) {
+    dim3 grid(ceil_div(g.N, BN), ceil_div(g.M, BM), 1);
+    snprintf(name, sizeof(name), "gemm_kernel<%d,%d,%d>", (int)g.a_trans, (int)g.b_trans,
+             (int)g.epi);
+    ProfScope ps(name, flop, in_bytes + 4.0 * MN * out_factor, stream);
+    launch(a, g.a_trans, g.b_trans, g.epi, grid, stream);
+  } else {
+    Args p = a;
+    p.C = workspace;
+    p.ldc = split_ld(g.N);
+    p.c_zstride = (long long)g.M * p.ldc;
+    p.bias = nullptr;
+    dim3 grid(ceil_div(g.N, BN), ceil_div(g.M, BM), splits);
+    snprintf(name, sizeof(name), "gemm_kernel<%d,%d,0>", (int)g.a_trans, (int)g.b_trans);
+    {
+      ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
+      launch(p, g.a_trans, g.b_trans, EPI_STORE, grid, stream);
+    }
+    const long long total = (long long)g.M * g.N;
+    int blocks = (int)((total + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    snprintf(name, sizeof(name), "split_reduce_kernel<%d>", (int)g.epi);
+    ProfScope ps(name, 0.0, 4.0 * MN * (splits + out_factor), stream);
+    switch (g.epi) {
+      case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+      case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+      default: split_reduce_kernel<EPI_STORE><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+    }
+  }
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+// ----- bias gradients: deterministic column sums -----------------------------------------
+namespace {
+constexpr int COLSUM_ROWS = 256;  // rows summed per workgroup before the second pass
+
+// partial[blockIdx.y][c] = sum of x[r][c] for r in this workgroup's row chunk (ascending)
+__global__ void colsum_partial_kernel(float* __restrict__ partial, const float* __restrict__ x,
+                                      int N, int C, int ld) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  const int r0 = blockIdx.y * COLSUM_ROWS;
+  const int r1 = min(N, r0 + COLSUM_ROWS);
+  float s = 0.f;
+  for (int r = r0; r < r1; r++) s += x[(long long)r * ld + c];
+  partial[(long long)blockIdx.y * C + c] = s;
+}
+
+__global__ void colsum_final_kernel(float* __restrict__ out, const float* __restrict__ partial,
+                                    int chunks, int C) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int k = 0; k < chunks; k++) s += partial[(long long)k * C + c];
+  out[c] += s;
+}
+}  // namespace
+
+size_t colsum_partial_floats(int N, int C) {
+  return (size_t)((N + COLSUM_ROWS - 1) / COLSUM_ROWS) * C;
+}
+
+int colsum_accumulate(float* out, const float* x, int N, int C, int ld, float* partial,
+                      hipStream_t stream) {
+  if (N <= 0 || C <= 0) return -1;
+  const int chunks = (N + COLSUM_ROWS - 1) / COLSUM_ROWS;
+  dim3 g1((C + 255) / 256, chunks);
+  {
+    ProfScope ps("colsum_partial_kernel", (double)N * C, 4.0 * ((double)N * C + (double)chunks * C),
+                 stream);
+    colsum_partial_kernel<<<g1, 256, 0, stream>>>(partial, x, N, C, ld);
+  }
+  ProfScope ps("colsum_final_kernel", (double)chunks * C, 4.0 * ((double)chunks * C + 2.0 * C),
+               stream);
+  colsum_final_kernel<<<(C + 255) / 256, 256, 0, stream>>>(out, partial, chunks, C);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+}  // namespace gpt2

@@ -1,0 +1,91 @@
+// kernels.h -- launchers of the gfx950 kernels, shared by the model driver and the C ABI.
+// Each returns 0 or a negative GPT2_ERR_* code; they only enqueue work on `stream`.
+#pragma once
+
+#include "common.h"
+
+namespace gpt2 {
+
+// ----- launch profiler (model.hip) --------------------------------------------------------
+// When enabled (gpt2_profile_enable), every kernel launch made through a launcher below is
+// bracketed by two HIP events on its stream and tagged with the kernel's name and the
+// algorithmic flops and HBM bytes of that launch. Not thread-safe (one caller at a time).
+bool profiling_on();
+struct ProfScope {
+  ProfScope(const char* name, double flop, double bytes, hipStream_t s);
+  ~ProfScope();
+  int rec = -1;
+  hipStream_t stream;
+};
+
+// ----- GEMM (gemm.hip) ------------------------------------------------------------------
+enum Epilogue {
+  EPI_STORE = 0,     // C = acc (+ bias)
+  EPI_GELU = 1,      // C = acc + bias; C2 = gelu(C)
+  EPI_RESID = 2,     // C = R + acc + bias
+  EPI_ACCUM = 3,     // C += acc
+  EPI_GELU_BWD = 4,  // C = acc * gelu'(R)
+};
+
+struct Gemm {
+  // logical C(M,N) = A(M,K) . B(K,N)
+  const float* A = nullptr;
+  int lda = 0;
+  bool a_trans = false;  // false: A stored (M,K) row-major; true: stored (K,M)
+  const float* B = nullptr;
+  int ldb = 0;
+  bool b_trans = false;  // false: B stored (N,K) (a weight (out,in)); true: stored (K,N)
+  float* C = nullptr;
+  int ldc = 0;
+  float* C2 = nullptr;        // EPI_GELU
+  const float* R = nullptr;   // EPI_RESID (residual) / EPI_GELU_BWD (pre-activation), ldc
+  const float* bias = nullptr;
+  int M = 0, N = 0, K = 0;
+  Epilogue epi = EPI_STORE;
+};
+
+// Runs the GEMM; `workspace` (device, `ws_floats` floats) enables a deterministic split of
+// K for grids too small to fill the chip (partials reduced in a fixed order). Pass
+// nullptr/0 to disable splitting.
+int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream);
+// floats of workspace gemm() may use for this problem (0 if it will not split)
+size_t gemm_workspace_floats(const Gemm& g);
+
+// column sums of x (N rows, C cols, row stride ld) added to out (C), fixed order;
+// `partial` needs colsum_partial_floats(N, C) floats.
+int colsum_accumulate(float* out, const float* x, int N, int C, int ld, float* partial,
+                      hipStream_t stream);
+size_t colsum_partial_floats(int N, int C);
+
+// ----- attention (attention.hip) --------------------------------------------------------
+int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                      hipStream_t stream);
+// `dscratch` needs B*NH*T floats (row dot products of dout and out)
+int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
+                       const float* lse, float* dscratch, int B, int T, int C, int NH,
+                       hipStream_t stream);
+
+// ----- memory-bound kernels (stream_ops.hip) ---------------------------------------------
+int encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe, int B,
+                    int T, int C, int V, int32_t* err_flag, hipStream_t stream);
+// sorted-token scratch: encoder_sort_scratch_ints(B*T, V) ints
+size_t encoder_sort_scratch_ints(int BT, int V);
+int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok, int B,
+                     int T, int C, int V, int32_t* scratch, hipStream_t stream);
+int layernorm_forward(float* out, float* mean, float* rstd, const float* x, const float* w,
+                      const float* b, int N, int C, hipStream_t stream);
+// `accumulate_dx`: dx += (true) or dx = (false). `partial` needs
+// layernorm_partial_floats(N, C) floats.
+int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const float* x,
+                       const float* w, const float* mean, const float* rstd, int N, int C,
+                       bool accumulate_dx, float* partial, hipStream_t stream);
+size_t layernorm_partial_floats(int N, int C);
+int crossentropy_forward(float* losses, float* lse, const float* logits, const int32_t* targets,
+                         int N, int V, int ld, int32_t* err_flag, hipStream_t stream);
+int crossentropy_backward(float* logits, const float* lse, const int32_t* targets, float dloss,
+                          int N, int V, int ld, hipStream_t stream);
+int mean_reduce(float* out, const float* x, int n, hipStream_t stream);
+int adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float beta1,
+          float beta2, float eps, float wd, int t, hipStream_t stream);
+
+}  // namespace gpt2

@@ -1,0 +1,911 @@
+// model.hip -- the GPT-2 model object and the C ABI declared in include/gpt2.h.
+//
+// Memory: parameters, gradients and the two AdamW moments live in one flat device block
+// (4 x num_params floats), and every activation, activation gradient and scratch buffer in
+// a second flat block sized once for (B, T) -- the "allocate everything up front" design of
+// "llm.c 的中文注解-20240421" (sections 1.17 and 1.19). The 16 parameter tensors keep that
+// page's order and shapes (section 1.16), so a flat fp32 parameter vector is portable.
+//
+// Launch sequence: gpt2_forward follows section 1.23, gpt2_backward section 1.25 (in
+// reverse layer order), gpt2_adamw_step section 1.26. Every launch goes to the model's one
+// stream; the only host synchronisation is the optional 4-byte loss readback.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gpt2.h"
+#include "kernels.h"
+
+namespace gpt2 {
+static char g_err[512] = "";
+static std::mutex g_err_mu;
+void set_global_error(const char* fmt, ...) {
+  std::lock_guard<std::mutex> lk(g_err_mu);
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+// ----- launch profiler -------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  std::string name;
+  double flop, bytes;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;  // events reused across profiling sessions
+size_t g_event_next = 0;
+
+hipEvent_t next_event() {
+  if (g_event_next == g_event_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_event_pool.push_back(e);
+  }
+  return g_event_pool[g_event_next++];
+}
+}  // namespace
+
+bool profiling_on() { return g_prof_on; }
+
+ProfScope::ProfScope(const char* name, double flop, double bytes, hipStream_t s) : stream(s) {
+  if (!g_prof_on) return;
+  hipEvent_t a = next_event(), b = next_event();
+  if (!a || !b) return;
+  if (hipEventRecord(a, s) != hipSuccess) return;
+  g_prof.push_back(ProfRec{name, flop, bytes, a, b});
+  rec = (int)g_prof.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (rec >= 0) (void)hipEventRecord(g_prof[rec].b, stream);
+}
+}  // namespace gpt2
+
+using namespace gpt2;
+
+struct gpt2_model {
+  int L = 0, C = 0, NH = 0, V = 0, maxT = 0, Vp = 0;
+  int device = 0;
+  hipStream_t stream = nullptr;  // NULL = the null stream
+  size_t nparams = 0;
+  size_t poff[16] = {}, plen[16] = {};
+  float* pbuf = nullptr;
+  float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
+
+  int B = 0, T = 0;
+  char* abuf = nullptr;
+  // forward activations (per layer where noted)
+  float *encoded, *ln1, *ln1_mean, *ln1_rstd, *qkv, *atty, *attn_lse, *res2, *ln2, *ln2_mean,
+      *ln2_rstd, *fch, *fchg, *res3, *lnf, *lnf_mean, *lnf_rstd, *logits, *losses, *xent_lse;
+  // backward buffers and scratch
+  float *dres, *dbuf4, *dln, *datty, *dqkv, *attn_D, *gemm_ws, *colsum_ws, *ln_ws, *d_loss;
+  size_t gemm_ws_floats = 0;
+  int32_t *tok, *tgt, *sort_scratch, *d_err;
+
+  bool fwd_targets = false;  // last forward had targets
+  bool logits_valid = false; // logits buffer holds logits (not their gradient)
+  bool has_grads = false;    // a backward or set_grads happened since build
+  char err[512] = "";
+};
+
+namespace {
+
+enum { P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB, P_LN2W, P_LN2B,
+       P_FCW, P_FCB, P_FCPROJW, P_FCPROJB, P_LNFW, P_LNFB };
+
+int fail(gpt2_model* md, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (md) snprintf(md->err, sizeof(md->err), "%s", buf);
+  set_global_error("%s", buf);
+  return code;
+}
+
+// propagate a kernel-launcher error code, copying the launcher's message into the model
+int chk(gpt2_model* md, int rc) {
+  if (rc) {
+    std::lock_guard<std::mutex> lk(g_err_mu);
+    snprintf(md->err, sizeof(md->err), "%s", g_err);
+  }
+  return rc;
+}
+#define CHK(expr)                    \
+  do {                               \
+    int rc_ = chk(md, (expr));       \
+    if (rc_) return rc_;             \
+  } while (0)
+#define HIPCHK(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(md, GPT2_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));                \
+  } while (0)
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+float* P(gpt2_model* md, int k) { return md->params + md->poff[k]; }
+float* G(gpt2_model* md, int k) { return md->grads + md->poff[k]; }
+
+// Carves the activation block for (B, T); with base == nullptr it only measures.
+size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
+  const size_t L = md->L, C = md->C, NH = md->NH, BT = (size_t)B * T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes, 256);
+    return p;
+  };
+  auto F = [&](size_t n) { return reinterpret_cast<float*>(take(n * sizeof(float))); };
+  md->encoded = F(BT * C);
+  md->ln1 = F(L * BT * C);
+  md->ln1_mean = F(L * BT);
+  md->ln1_rstd = F(L * BT);
+  md->qkv = F(L * BT * 3 * C);
+  md->atty = F(L * BT * C);
+  md->attn_lse = F(L * NH * BT);
+  md->res2 = F(L * BT * C);
+  md->ln2 = F(L * BT * C);
+  md->ln2_mean = F(L * BT);
+  md->ln2_rstd = F(L * BT);
+  md->fch = F(L * BT * 4 * C);
+  md->fchg = F(L * BT * 4 * C);
+  md->res3 = F(L * BT * C);
+  md->lnf = F(BT * C);
+  md->lnf_mean = F(BT);
+  md->lnf_rstd = F(BT);
+  md->logits = F(BT * md->Vp);
+  md->losses = F(BT);
+  md->xent_lse = F(BT);
+  md->dres = F(BT * C);
+  md->dbuf4 = F(BT * 4 * C);
+  md->dln = F(BT * C);
+  md->datty = F(BT * C);
+  md->dqkv = F(BT * 3 * C);
+  md->attn_D = F(NH * BT);
+  // split-K workspace: the largest any GEMM of the step asks for
+  size_t ws = 0;
+  {
+    const int iBT = (int)BT, iC = (int)C, iV = md->V;
+    const int oc[4] = {3 * iC, iC, 4 * iC, iC};
+    const int in[4] = {iC, iC, iC, 4 * iC};
+    for (int k = 0; k < 4; k++) {
+      Gemm g;
+      g.M = oc[k];
+      g.N = in[k];
+      g.K = iBT;
+      g.epi = EPI_ACCUM;
+      ws = std::max(ws, gemm_workspace_floats(g));
+      Gemm d;
+      d.M = iBT;
+      d.N = in[k];
+      d.K = oc[k];
+      d.epi = EPI_STORE;
+      ws = std::max(ws, gemm_workspace_floats(d));
+    }
+    Gemm d;
+    d.M = iBT;
+    d.N = iC;
+    d.K = iV;
+    ws = std::max(ws, gemm_workspace_floats(d));
+    Gemm w;
+    w.M = iV;
+    w.N = iC;
+    w.K = iBT;
+    w.epi = EPI_ACCUM;
+    ws = std::max(ws, gemm_workspace_floats(w));
+  }
+  md->gemm_ws_floats = ws;
+  md->gemm_ws = F(ws ? ws : 1);
+  md->colsum_ws = F(colsum_partial_floats((int)BT, 4 * (int)C));
+  md->ln_ws = F(layernorm_partial_floats((int)BT, (int)C));
+  md->d_loss = F(1);
+  md->tok = reinterpret_cast<int32_t*>(take(BT * sizeof(int32_t)));
+  md->tgt = reinterpret_cast<int32_t*>(take(BT * sizeof(int32_t)));
+  md->sort_scratch =
+      reinterpret_cast<int32_t*>(take(encoder_sort_scratch_ints((int)BT, md->V) * sizeof(int32_t)));
+  md->d_err = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  return off;
+}
+
+int alloc_activations(gpt2_model* md, int B, int T) {
+  const size_t bytes = carve_activations(md, nullptr, B, T);
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return fail(md, GPT2_ERR_OOM, "cannot allocate %zu bytes of activations for B=%d T=%d",
+                bytes, B, T);
+  }
+  md->abuf = static_cast<char*>(p);
+  carve_activations(md, md->abuf, B, T);
+  md->B = B;
+  md->T = T;
+  HIPCHK(hipMemsetAsync(md->d_err, 0, sizeof(int32_t), md->stream));
+  return GPT2_OK;
+}
+
+int copy_floats(gpt2_model* md, float* dst, const float* src, size_t n, hipMemcpyKind kind) {
+  HIPCHK(hipMemcpyAsync(dst, src, n * sizeof(float), kind, md->stream));
+  if (kind == hipMemcpyDeviceToHost || kind == hipMemcpyHostToDevice)
+    HIPCHK(hipStreamSynchronize(md->stream));
+  return GPT2_OK;
+}
+
+int check_err_flag(gpt2_model* md) {
+  int32_t e = 0;
+  HIPCHK(hipMemcpyAsync(&e, md->d_err, sizeof(e), hipMemcpyDeviceToHost, md->stream));
+  HIPCHK(hipStreamSynchronize(md->stream));
+  if (e) {
+    HIPCHK(hipMemsetAsync(md->d_err, 0, sizeof(int32_t), md->stream));
+    return fail(md, GPT2_ERR_TOKEN, "a token or target was outside [0, %d)", md->V);
+  }
+  return GPT2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt2_profile_enable(int on) {
+  g_prof.clear();
+  g_event_next = 0;
+  g_prof_on = on != 0;
+  return GPT2_OK;
+}
+
+int gpt2_profile_summary(char* buf, size_t len) {
+  if (!buf || len == 0) return fail(nullptr, GPT2_ERR_ARG, "gpt2_profile_summary: no buffer");
+  struct Agg {
+    long long n = 0;
+    double ms = 0, flop = 0, bytes = 0;
+  };
+  std::map<std::string, Agg> agg;
+  for (auto& r : g_prof) {
+    if (hipEventSynchronize(r.b) != hipSuccess)
+      return fail(nullptr, GPT2_ERR_HIP, "gpt2_profile_summary: event wait failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return fail(nullptr, GPT2_ERR_HIP, "gpt2_profile_summary: elapsed time failed");
+    Agg& a = agg[r.name];
+    a.n++;
+    a.ms += ms;
+    a.flop += r.flop;
+    a.bytes += r.bytes;
+  }
+  size_t off = 0;
+  buf[0] = 0;
+  for (auto& kv : agg) {
+    int w = snprintf(buf + off, len - off, "%s\t%lld\t%.6f\t%.6e\t%.6e\n", kv.first.c_str(),
+                     kv.second.n, kv.second.ms, kv.second.flop, kv.second.bytes);
+    if (w < 0 || (size_t)w >= len - off)
+      return fail(nullptr, GPT2_ERR_ARG, "gpt2_profile_summary: buffer too small");
+    off += (size_t)w;
+  }
+  return GPT2_OK;
+}
+
+const char* gpt2_version(void) { return "gpt2-mi355x 0.1 (gfx950, fp32 MFMA)"; }
+
+const char* gpt2_last_error(const gpt2_model* md) { return md ? md->err : gpt2::g_err; }
+
+const char* gpt2_last_global_error(void) { return gpt2::g_err; }
+
+int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dtype, int maxB,
+                  int maxTseq, void* stream) {
+  if (!out) return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: out is NULL");
+  *out = nullptr;
+  if (L < 1 || C < 1 || H < 1 || V < 1 || maxT < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: sizes must be >= 1");
+  if (C % H || C % 4 || (C / H) % 4 || C / H > 128)
+    return fail(nullptr, GPT2_ERR_ARG,
+                "gpt2_build: need C %% H == 0, C %% 4 == 0, head size %% 4 == 0 and <= 128 "
+                "(C=%d H=%d)", C, H);
+  if ((C / 4 + 63) / 64 > 8)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: C=%d above the supported 2048", C);
+  if (dtype != GPT2_DTYPE_FP32)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: dtype %d is not supported", dtype);
+  if ((maxB > 0) != (maxTseq > 0) || maxTseq > maxT)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: bad preallocation shape");
+
+  gpt2_model* md = new gpt2_model();
+  md->L = L;
+  md->C = C;
+  md->NH = H;
+  md->V = V;
+  md->maxT = maxT;
+  md->Vp = (int)align_up((size_t)V, 64);
+  if (hipGetDevice(&md->device) != hipSuccess) {
+    delete md;
+    return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: no HIP device");
+  }
+  const size_t c = C, l = L;
+  const size_t sizes[16] = {(size_t)V * c, (size_t)maxT * c, l * c, l * c, l * 3 * c * c,
+                            l * 3 * c, l * c * c, l * c, l * c, l * c, l * 4 * c * c, l * 4 * c,
+                            l * c * 4 * c, l * c, c, c};
+  size_t o = 0;
+  for (int k = 0; k < 16; k++) {
+    md->poff[k] = o;
+    md->plen[k] = sizes[k];
+    o += sizes[k];
+  }
+  md->nparams = o;
+  // every tensor offset must keep 16-byte alignment for the float4 kernels
+  for (int k = 0; k < 16; k++)
+    if (md->poff[k] % 4) {
+      delete md;
+      return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: tensor %d misaligned", k);
+    }
+  const size_t stride = align_up(md->nparams, 64);
+  void* p = nullptr;
+  if (hipMalloc(&p, 4 * stride * sizeof(float)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    delete md;
+    return fail(nullptr, GPT2_ERR_OOM, "gpt2_build: cannot allocate %zu parameter floats",
+                4 * stride);
+  }
+  md->pbuf = static_cast<float*>(p);
+  md->params = md->pbuf;
+  md->grads = md->pbuf + stride;
+  md->m = md->pbuf + 2 * stride;
+  md->v = md->pbuf + 3 * stride;
+  md->stream = static_cast<hipStream_t>(stream);  // NULL: the null stream
+  if (hipMemsetAsync(md->pbuf, 0, 4 * stride * sizeof(float), md->stream) != hipSuccess) {
+    gpt2_free(md);
+    return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: memset failed");
+  }
+  if (maxB > 0) {
+    int rc = alloc_activations(md, maxB, maxTseq);
+    if (rc) {
+      gpt2_free(md);
+      return rc;
+    }
+  }
+  if (hipStreamSynchronize(md->stream) != hipSuccess) {
+    gpt2_free(md);
+    return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: synchronize failed");
+  }
+  *out = md;
+  return GPT2_OK;
+}
+
+int gpt2_build(gpt2_model** out, int L, int C, int H, int V, int maxT) {
+  return gpt2_build_ex(out, L, C, H, V, maxT, GPT2_DTYPE_FP32, 0, 0, nullptr);
+}
+
+void gpt2_free(gpt2_model* md) {
+  if (!md) return;
+  if (md->stream) (void)hipStreamSynchronize(md->stream);
+  if (md->abuf) (void)hipFree(md->abuf);
+  if (md->pbuf) (void)hipFree(md->pbuf);
+  delete md;
+}
+
+int gpt2_set_stream(gpt2_model* md, void* stream) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  HIPCHK(hipStreamSynchronize(md->stream));
+  md->stream = static_cast<hipStream_t>(stream);
+  return GPT2_OK;
+}
+
+int gpt2_synchronize(gpt2_model* md) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  HIPCHK(hipStreamSynchronize(md->stream));
+  if (md->abuf) return check_err_flag(md);
+  return GPT2_OK;
+}
+
+size_t gpt2_num_params(const gpt2_model* md) { return md ? md->nparams : 0; }
+
+int gpt2_param_layout(const gpt2_model* md, size_t off[16], size_t len[16]) {
+  if (!md || !off || !len) return fail(nullptr, GPT2_ERR_ARG, "gpt2_param_layout: NULL");
+  for (int k = 0; k < 16; k++) {
+    off[k] = md->poff[k];
+    len[k] = md->plen[k];
+  }
+  return GPT2_OK;
+}
+
+static int xfer(gpt2_model* md, float* dev, const float* src, float* dst, int is_device) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (src) return copy_floats(md, dev, src, md->nparams,
+                              is_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice);
+  if (!dst) return fail(md, GPT2_ERR_ARG, "NULL buffer");
+  return copy_floats(md, dst, dev, md->nparams,
+                     is_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost);
+}
+
+int gpt2_set_params(gpt2_model* md, const float* src, int src_is_device) {
+  if (md && !src) return fail(md, GPT2_ERR_ARG, "gpt2_set_params: NULL source");
+  return xfer(md, md ? md->params : nullptr, src, nullptr, src_is_device);
+}
+int gpt2_get_params(gpt2_model* md, float* dst, int dst_is_device) {
+  return xfer(md, md ? md->params : nullptr, nullptr, dst, dst_is_device);
+}
+int gpt2_get_grads(gpt2_model* md, float* dst, int dst_is_device) {
+  return xfer(md, md ? md->grads : nullptr, nullptr, dst, dst_is_device);
+}
+int gpt2_set_grads(gpt2_model* md, const float* src, int src_is_device) {
+  if (md && !src) return fail(md, GPT2_ERR_ARG, "gpt2_set_grads: NULL source");
+  int rc = xfer(md, md ? md->grads : nullptr, src, nullptr, src_is_device);
+  if (!rc) md->has_grads = true;
+  return rc;
+}
+int gpt2_get_adam_state(gpt2_model* md, float* m, float* v, int dst_is_device) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (m) {
+    int rc = xfer(md, md->m, nullptr, m, dst_is_device);
+    if (rc) return rc;
+  }
+  if (v) return xfer(md, md->v, nullptr, v, dst_is_device);
+  return GPT2_OK;
+}
+
+int gpt2_get_losses(gpt2_model* md, float* dst, int dst_is_device) {
+  if (!md || !dst) return fail(md, GPT2_ERR_ARG, "gpt2_get_losses: NULL");
+  if (!md->fwd_targets) return fail(md, GPT2_ERR_STATE, "no forward with targets yet");
+  return copy_floats(md, dst, md->losses, (size_t)md->B * md->T,
+                     dst_is_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost);
+}
+
+int gpt2_get_logits(gpt2_model* md, float* dst, int dst_is_device) {
+  if (!md || !dst) return fail(md, GPT2_ERR_ARG, "gpt2_get_logits: NULL");
+  if (!md->logits_valid) return fail(md, GPT2_ERR_STATE, "logits are not available");
+  HIPCHK(hipMemcpy2DAsync(dst, (size_t)md->V * sizeof(float), md->logits,
+                          (size_t)md->Vp * sizeof(float), (size_t)md->V * sizeof(float),
+                          (size_t)md->B * md->T,
+                          dst_is_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost,
+                          md->stream));
+  HIPCHK(hipStreamSynchronize(md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B, int T,
+                 float* mean_loss) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (!tokens) return fail(md, GPT2_ERR_ARG, "gpt2_forward: tokens is NULL");
+  if (B < 1 || T < 1 || T > md->maxT)
+    return fail(md, GPT2_ERR_ARG, "gpt2_forward: need B >= 1 and 1 <= T <= %d (B=%d T=%d)",
+                md->maxT, B, T);
+  if (!md->abuf) {
+    int rc = alloc_activations(md, B, T);
+    if (rc) return rc;
+  } else if (B != md->B || T != md->T) {
+    return fail(md, GPT2_ERR_SHAPE, "gpt2_forward: model is sized for B=%d T=%d, got B=%d T=%d",
+                md->B, md->T, B, T);
+  }
+  const int L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T;
+  const size_t NC = (size_t)BT * C;
+  hipStream_t s = md->stream;
+  md->fwd_targets = false;
+  md->logits_valid = false;
+  HIPCHK(hipMemcpyAsync(md->tok, tokens, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  if (targets)
+    HIPCHK(hipMemcpyAsync(md->tgt, targets, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+
+  CHK(encoder_forward(md->encoded, md->tok, P(md, P_WTE), P(md, P_WPE), B, T, C, V, md->d_err, s));
+  for (int l = 0; l < L; l++) {
+    const float* x = l == 0 ? md->encoded : md->res3 + (l - 1) * NC;
+    float* ln1 = md->ln1 + l * NC;
+    float* qkv = md->qkv + l * 3 * NC;
+    float* atty = md->atty + l * NC;
+    float* res2 = md->res2 + l * NC;
+    float* ln2 = md->ln2 + l * NC;
+    float* fch = md->fch + l * 4 * NC;
+    float* fchg = md->fchg + l * 4 * NC;
+    float* res3 = md->res3 + l * NC;
+    CHK(layernorm_forward(ln1, md->ln1_mean + (size_t)l * BT, md->ln1_rstd + (size_t)l * BT, x,
+                          P(md, P_LN1W) + l * C, P(md, P_LN1B) + l * C, BT, C, s));
+    Gemm g;
+    g.A = ln1;
+    g.lda = C;
+    g.B = P(md, P_QKVW) + (size_t)l * 3 * C * C;
+    g.ldb = C;
+    g.C = qkv;
+    g.ldc = 3 * C;
+    g.bias = P(md, P_QKVB) + (size_t)l * 3 * C;
+    g.M = BT;
+    g.N = 3 * C;
+    g.K = C;
+    CHK(gemm(g, nullptr, 0, s));
+    CHK(attention_forward(atty, md->attn_lse + (size_t)l * NH * BT, qkv, B, T, C, NH, s));
+    Gemm pj;
+    pj.A = atty;
+    pj.lda = C;
+    pj.B = P(md, P_ATTPROJW) + (size_t)l * C * C;
+    pj.ldb = C;
+    pj.C = res2;
+    pj.ldc = C;
+    pj.R = x;
+    pj.bias = P(md, P_ATTPROJB) + (size_t)l * C;
+    pj.M = BT;
+    pj.N = C;
+    pj.K = C;
+    pj.epi = EPI_RESID;
+    CHK(gemm(pj, nullptr, 0, s));
+    CHK(layernorm_forward(ln2, md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, res2,
+                          P(md, P_LN2W) + l * C, P(md, P_LN2B) + l * C, BT, C, s));
+    Gemm fc;
+    fc.A = ln2;
+    fc.lda = C;
+    fc.B = P(md, P_FCW) + (size_t)l * 4 * C * C;
+    fc.ldb = C;
+    fc.C = fch;
+    fc.C2 = fchg;
+    fc.ldc = 4 * C;
+    fc.bias = P(md, P_FCB) + (size_t)l * 4 * C;
+    fc.M = BT;
+    fc.N = 4 * C;
+    fc.K = C;
+    fc.epi = EPI_GELU;
+    CHK(gemm(fc, nullptr, 0, s));
+    Gemm fp;
+    fp.A = fchg;
+    fp.lda = 4 * C;
+    fp.B = P(md, P_FCPROJW) + (size_t)l * 4 * C * C;
+    fp.ldb = 4 * C;
+    fp.C = res3;
+    fp.ldc = C;
+    fp.R = res2;
+    fp.bias = P(md, P_FCPROJB) + (size_t)l * C;
+    fp.M = BT;
+    fp.N = C;
+    fp.K = 4 * C;
+    fp.epi = EPI_RESID;
+    CHK(gemm(fp, nullptr, 0, s));
+  }
+  CHK(layernorm_forward(md->lnf, md->lnf_mean, md->lnf_rstd, md->res3 + (L - 1) * NC,
+                        P(md, P_LNFW), P(md, P_LNFB), BT, C, s));
+  // tied lm_head: logits = lnf . wte^T, no bias (rows padded to Vp floats)
+  Gemm lm;
+  lm.A = md->lnf;
+  lm.lda = C;
+  lm.B = P(md, P_WTE);
+  lm.ldb = C;
+  lm.C = md->logits;
+  lm.ldc = md->Vp;
+  lm.M = BT;
+  lm.N = V;
+  lm.K = C;
+  CHK(gemm(lm, nullptr, 0, s));
+  md->logits_valid = true;
+
+  if (targets) {
+    CHK(crossentropy_forward(md->losses, md->xent_lse, md->logits, md->tgt, BT, V, md->Vp,
+                             md->d_err, s));
+    CHK(mean_reduce(md->d_loss, md->losses, BT, s));
+    md->fwd_targets = true;
+  }
+  if (mean_loss) {
+    float host = -1.0f;
+    if (targets) {
+      HIPCHK(hipMemcpyAsync(&host, md->d_loss, sizeof(float), hipMemcpyDeviceToHost, s));
+    }
+    int rc = check_err_flag(md);  // synchronises the stream
+    if (rc) {
+      md->fwd_targets = false;
+      return rc;
+    }
+    *mean_loss = host;
+  }
+  return GPT2_OK;
+}
+
+int gpt2_zero_grad(gpt2_model* md) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  HIPCHK(hipMemsetAsync(md->grads, 0, md->nparams * sizeof(float), md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_backward(gpt2_model* md) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (!md->fwd_targets || !md->logits_valid)
+    return fail(md, GPT2_ERR_STATE, "gpt2_backward: needs a forward with targets first");
+  const int B = md->B, T = md->T, L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T;
+  const size_t NC = (size_t)BT * C;
+  hipStream_t s = md->stream;
+  float* ws = md->gemm_ws;
+  const size_t wsn = md->gemm_ws_floats;
+
+  // d(mean loss)/d(loss_bt) = 1/(B*T), through softmax + cross-entropy, in place
+  CHK(crossentropy_backward(md->logits, md->xent_lse, md->tgt, 1.0f / (float)BT, BT, V, md->Vp,
+                            s));
+  md->logits_valid = false;
+  {
+    Gemm d;  // dlnf = dlogits . wte
+    d.A = md->logits;
+    d.lda = md->Vp;
+    d.B = P(md, P_WTE);
+    d.ldb = C;
+    d.b_trans = true;
+    d.C = md->dln;
+    d.ldc = C;
+    d.M = BT;
+    d.N = C;
+    d.K = V;
+    CHK(gemm(d, ws, wsn, s));
+    Gemm w;  // dwte += dlogits^T . lnf
+    w.A = md->logits;
+    w.lda = md->Vp;
+    w.a_trans = true;
+    w.B = md->lnf;
+    w.ldb = C;
+    w.b_trans = true;
+    w.C = G(md, P_WTE);
+    w.ldc = C;
+    w.M = V;
+    w.N = C;
+    w.K = BT;
+    w.epi = EPI_ACCUM;
+    CHK(gemm(w, ws, wsn, s));
+  }
+  CHK(layernorm_backward(md->dres, G(md, P_LNFW), G(md, P_LNFB), md->dln, md->res3 + (L - 1) * NC,
+                         P(md, P_LNFW), md->lnf_mean, md->lnf_rstd, BT, C, false, md->ln_ws, s));
+
+  // one linear layer's backward: dinp = dout . W (optionally times gelu'(pre)),
+  // dW += dout^T . inp, db += column sums of dout
+  auto linear_bwd = [&](float* dinp, const float* gelu_pre, float* dW, float* db,
+                        const float* dout, const float* inp, const float* W, int in,
+                        int out) -> int {
+    Gemm d;
+    d.A = dout;
+    d.lda = out;
+    d.B = W;
+    d.ldb = in;
+    d.b_trans = true;
+    d.C = dinp;
+    d.ldc = in;
+    d.M = BT;
+    d.N = in;
+    d.K = out;
+    if (gelu_pre) {
+      d.epi = EPI_GELU_BWD;
+      d.R = gelu_pre;
+    }
+    int rc = gemm(d, ws, wsn, s);
+    if (rc) return rc;
+    Gemm w;
+    w.A = dout;
+    w.lda = out;
+    w.a_trans = true;
+    w.B = inp;
+    w.ldb = in;
+    w.b_trans = true;
+    w.C = dW;
+    w.ldc = in;
+    w.M = out;
+    w.N = in;
+    w.K = BT;
+    w.epi = EPI_ACCUM;
+    rc = gemm(w, ws, wsn, s);
+    if (rc) return rc;
+    return colsum_accumulate(db, dout, BT, out, out, md->colsum_ws, s);
+  };
+
+  for (int l = L - 1; l >= 0; l--) {
+    const float* x = l == 0 ? md->encoded : md->res3 + (l - 1) * NC;
+    // MLP: residual3 = residual2 + fcproj(gelu(fc(ln2(residual2))))
+    CHK(linear_bwd(md->dbuf4, md->fch + l * 4 * NC, G(md, P_FCPROJW) + (size_t)l * 4 * C * C,
+                   G(md, P_FCPROJB) + (size_t)l * C, md->dres, md->fchg + l * 4 * NC,
+                   P(md, P_FCPROJW) + (size_t)l * 4 * C * C, 4 * C, C));
+    CHK(linear_bwd(md->dln, nullptr, G(md, P_FCW) + (size_t)l * 4 * C * C,
+                   G(md, P_FCB) + (size_t)l * 4 * C, md->dbuf4, md->ln2 + l * NC,
+                   P(md, P_FCW) + (size_t)l * 4 * C * C, C, 4 * C));
+    CHK(layernorm_backward(md->dres, G(md, P_LN2W) + (size_t)l * C, G(md, P_LN2B) + (size_t)l * C,
+                           md->dln, md->res2 + l * NC, P(md, P_LN2W) + (size_t)l * C,
+                           md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, BT, C,
+                           true, md->ln_ws, s));
+    // attention: residual2 = x + attproj(attention(qkv(ln1(x))))
+    CHK(linear_bwd(md->datty, nullptr, G(md, P_ATTPROJW) + (size_t)l * C * C,
+                   G(md, P_ATTPROJB) + (size_t)l * C, md->dres, md->atty + l * NC,
+                   P(md, P_ATTPROJW) + (size_t)l * C * C, C, C));
+    CHK(attention_backward(md->dqkv, md->datty, md->qkv + l * 3 * NC, md->atty + l * NC,
+                           md->attn_lse + (size_t)l * NH * BT, md->attn_D, B, T, C, NH, s));
+    CHK(linear_bwd(md->dln, nullptr, G(md, P_QKVW) + (size_t)l * 3 * C * C,
+                   G(md, P_QKVB) + (size_t)l * 3 * C, md->dqkv, md->ln1 + l * NC,
+                   P(md, P_QKVW) + (size_t)l * 3 * C * C, C, 3 * C));
+    CHK(layernorm_backward(md->dres, G(md, P_LN1W) + (size_t)l * C, G(md, P_LN1B) + (size_t)l * C,
+                           md->dln, x, P(md, P_LN1W) + (size_t)l * C,
+                           md->ln1_mean + (size_t)l * BT, md->ln1_rstd + (size_t)l * BT, BT, C,
+                           true, md->ln_ws, s));
+  }
+  CHK(encoder_backward(G(md, P_WTE), G(md, P_WPE), md->dres, md->tok, B, T, C, V,
+                       md->sort_scratch, s));
+  md->has_grads = true;
+  return GPT2_OK;
+}
+
+int gpt2_adamw_step(gpt2_model* md, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, int t) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (t < 1) return fail(md, GPT2_ERR_ARG, "gpt2_adamw_step: t must be >= 1 (got %d)", t);
+  if (!md->has_grads) return fail(md, GPT2_ERR_STATE, "gpt2_adamw_step: no gradients yet");
+  CHK(adamw(md->params, md->grads, md->m, md->v, md->nparams, lr, beta1, beta2, eps,
+            weight_decay, t, md->stream));
+  return GPT2_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// per-kernel entry points
+// ---------------------------------------------------------------------------------------
+#define KCHK(expr)                                                                          \
+  do {                                                                                      \
+    int rc_ = (expr);                                                                       \
+    if (rc_) return rc_;                                                                    \
+  } while (0)
+
+static hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int gpt2_k_encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe,
+                           int B, int T, int C, int V, int32_t* err_flag, void* stream) {
+  if (!out || !tok || !wte || !wpe) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return encoder_forward(out, tok, wte, wpe, B, T, C, V, err_flag, as_stream(stream));
+}
+
+int gpt2_k_encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
+                            int B, int T, int C, int V, void* stream) {
+  if (!dwte || !dwpe || !dout || !tok || B < 1 || T < 1 || V < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  int32_t* scratch = nullptr;
+  if (hipMalloc(&scratch, encoder_sort_scratch_ints(B * T, V) * sizeof(int32_t)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = encoder_backward(dwte, dwpe, dout, tok, B, T, C, V, scratch, s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(scratch);
+  return rc;
+}
+
+int gpt2_k_layernorm_forward(float* out, float* mean, float* rstd, const float* x,
+                             const float* w, const float* b, int N, int C, void* stream) {
+  if (!out || !x || !w || !b) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return layernorm_forward(out, mean, rstd, x, w, b, N, C, as_stream(stream));
+}
+
+int gpt2_k_layernorm_backward(float* dx, float* dw, float* db, const float* dout,
+                              const float* x, const float* w, const float* mean,
+                              const float* rstd, int N, int C, void* stream) {
+  if (!dx || !dw || !db || !dout || !x || !w || !mean || !rstd || N < 1 || C < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  float* partial = nullptr;
+  if (hipMalloc(&partial, layernorm_partial_floats(N, C) * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = layernorm_backward(dx, dw, db, dout, x, w, mean, rstd, N, C, true, partial, s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(partial);
+  return rc;
+}
+
+int gpt2_k_matmul_forward(float* out, float* out2, const float* resid, const float* inp,
+                          const float* W, const float* bias, int N, int C, int OC, int ld_out,
+                          int epilogue, void* stream) {
+  if (!out || !inp || !W || N < 1 || C < 1 || OC < 1 || ld_out < OC)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  Gemm g;
+  g.A = inp;
+  g.lda = C;
+  g.B = W;
+  g.ldb = C;
+  g.C = out;
+  g.ldc = ld_out;
+  g.bias = bias;
+  g.M = N;
+  g.N = OC;
+  g.K = C;
+  if (epilogue == 1) {
+    g.epi = EPI_GELU;
+    g.C2 = out2;
+  } else if (epilogue == 2) {
+    g.epi = EPI_RESID;
+    g.R = resid;
+  } else if (epilogue != 0) {
+    return fail(nullptr, GPT2_ERR_ARG, "unknown epilogue %d", epilogue);
+  }
+  return gemm(g, nullptr, 0, as_stream(stream));
+}
+
+int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* dout,
+                           const float* inp, const float* W, const float* gelu_pre, int N, int C,
+                           int OC, int ld_dout, void* stream) {
+  if (!dout || N < 1 || C < 1 || OC < 1 || ld_dout < OC || (dinp && !W) || (dW && !inp))
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  Gemm d;
+  d.A = dout;
+  d.lda = ld_dout;
+  d.B = W;
+  d.ldb = C;
+  d.b_trans = true;
+  d.C = dinp;
+  d.ldc = C;
+  d.M = N;
+  d.N = C;
+  d.K = OC;
+  if (gelu_pre) {
+    d.epi = EPI_GELU_BWD;
+    d.R = gelu_pre;
+  }
+  Gemm w;
+  w.A = dout;
+  w.lda = ld_dout;
+  w.a_trans = true;
+  w.B = inp;
+  w.ldb = C;
+  w.b_trans = true;
+  w.C = dW;
+  w.ldc = C;
+  w.M = OC;
+  w.N = C;
+  w.K = N;
+  w.epi = EPI_ACCUM;
+  size_t ws = std::max(dinp ? gemm_workspace_floats(d) : 0, dW ? gemm_workspace_floats(w) : 0);
+  ws = std::max(ws, colsum_partial_floats(N, OC));
+  float* buf = nullptr;
+  if (hipMalloc(&buf, (ws ? ws : 1) * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = 0;
+  if (dinp) rc = gemm(d, buf, ws, s);
+  if (!rc && dW) rc = gemm(w, buf, ws, s);
+  if (!rc && dbias) rc = colsum_accumulate(dbias, dout, N, OC, ld_dout, buf, s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(buf);
+  return rc;
+}
+
+int gpt2_k_attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C,
+                             int NH, void* stream) {
+  if (!out || !lse || !qkv) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return attention_forward(out, lse, qkv, B, T, C, NH, as_stream(stream));
+}
+
+int gpt2_k_attention_backward(float* dqkv, const float* dout, const float* qkv,
+                              const float* out, const float* lse, int B, int T, int C, int NH,
+                              void* stream) {
+  if (!dqkv || !dout || !qkv || !out || !lse || B < 1 || T < 1 || NH < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  float* D = nullptr;
+  if (hipMalloc(&D, (size_t)B * NH * T * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = attention_backward(dqkv, dout, qkv, out, lse, D, B, T, C, NH, s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(D);
+  return rc;
+}
+
+int gpt2_k_crossentropy_forward(float* losses, float* lse, const float* logits,
+                                const int32_t* targets, int N, int V, int ld, int32_t* err_flag,
+                                void* stream) {
+  if (!losses || !lse || !logits || !targets) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return crossentropy_forward(losses, lse, logits, targets, N, V, ld, err_flag, as_stream(stream));
+}
+
+int gpt2_k_crossentropy_backward(float* logits, const float* lse, const int32_t* targets,
+                                 float dloss, int N, int V, int ld, void* stream) {
+  if (!logits || !lse || !targets) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return crossentropy_backward(logits, lse, targets, dloss, N, V, ld, as_stream(stream));
+}
+
+int gpt2_k_mean(float* out, const float* x, int n, void* stream) {
+  if (!out || !x) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return mean_reduce(out, x, n, as_stream(stream));
+}
+
+int gpt2_k_adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float beta1,
+                 float beta2, float eps, float weight_decay, int t, void* stream) {
+  if (!p || !g || !m || !v) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, t, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,571 @@
+// stream_ops.hip -- the memory-bound kernels of the training step: embedding gather and
+// scatter, LayerNorm forward/backward, softmax cross-entropy forward/backward, the mean
+// loss and AdamW. Each streams its tensors once with 16-byte accesses; row reductions use
+// wave64 shuffles, column reductions are split into fixed-order partial sums so results do
+// not depend on scheduling.
+//
+// Definitions follow "llm.c 的中文注解-20240421": 1.1 encoder_forward, 1.2 encoder_backward,
+// 1.3 layernorm_forward, 1.4 layernorm_backward, 1.13 softmax_forward, 1.14
+// crossentropy_forward, 1.15 crossentropy_softmax_backward, 1.26 gpt2_update (AdamW).
+#include <cmath>
+
+#include "kernels.h"
+
+namespace gpt2 {
+namespace {
+
+GPT2_DEVICE_INLINE f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+GPT2_DEVICE_INLINE void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+// tokens outside [0, V) were reported by the forward; here they read as 0 so that no
+// index leaves its buffer
+GPT2_DEVICE_INLINE int clamp_tok(int v, int V) { return (v < 0 || v >= V) ? 0 : v; }
+
+int blocks_for(long long n, int per_block, int cap) {
+  long long b = (n + per_block - 1) / per_block;
+  if (b > cap) b = cap;
+  return b < 1 ? 1 : (int)b;
+}
+
+// ---------------------------------------------------------------------------------------
+// encoder
+// ---------------------------------------------------------------------------------------
+__global__ void encoder_fwd_kernel(float* __restrict__ out, const int32_t* __restrict__ tok,
+                                   const float* __restrict__ wte, const float* __restrict__ wpe,
+                                   int BT, int T, int C, int V, int32_t* err) {
+  const int C4 = C / 4;
+  const long long total = (long long)BT * C4;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int row = (int)(idx / C4), c = 4 * (int)(idx % C4);
+    int v = tok[row];
+    if (v < 0 || v >= V) {
+      if (err) *err = 1;
+      v = 0;
+    }
+    const int t = row % T;
+    f32x4 a = ld4(wte + (long long)v * C + c), p = ld4(wpe + (long long)t * C + c);
+    st4(out + (long long)row * C + c, a + p);
+  }
+}
+
+// dwpe[t] += sum over b of dout[b, t] (b ascending)
+__global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const float* __restrict__ dout,
+                                       int B, int T, int C) {
+  const int C4 = C / 4;
+  const long long total = (long long)T * C4;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(idx / C4), c = 4 * (int)(idx % C4);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < B; b++) s += ld4(dout + ((long long)b * T + t) * C + c);
+    float* p = dwpe + (long long)t * C + c;
+    st4(p, ld4(p) + s);
+  }
+}
+
+// Stable sort of positions by token, in one workgroup of 1024 threads:
+// count[v] = occurrences (integer atomics: the counts do not depend on order);
+// offset = exclusive prefix sum of count; then positions are placed chunk by chunk
+// (1024 at a time, in order), each at offset[v] + (earlier occurrences of v), so within a
+// token positions stay ascending. scratch: count[V], offset[V]; out: sorted[BT].
+constexpr int SORT_THREADS = 1024;
+__global__ __launch_bounds__(SORT_THREADS) void token_sort_kernel(int32_t* __restrict__ sorted,
+                                                                  int32_t* __restrict__ count,
+                                                                  int32_t* __restrict__ offset,
+                                                                  const int32_t* __restrict__ tok,
+                                                                  int BT, int V) {
+  __shared__ int32_t part[SORT_THREADS];
+  __shared__ int32_t chunk_tok[SORT_THREADS];
+  const int tid = threadIdx.x;
+  for (int v = tid; v < V; v += SORT_THREADS) count[v] = 0;
+  __syncthreads();
+  for (int i = tid; i < BT; i += SORT_THREADS) atomicAdd(&count[clamp_tok(tok[i], V)], 1);
+  __threadfence_block();
+  __syncthreads();
+  // exclusive scan: each thread owns a contiguous segment of the vocabulary
+  const int seg = (V + SORT_THREADS - 1) / SORT_THREADS;
+  const int v0 = min(V, tid * seg), v1 = min(V, v0 + seg);
+  int s = 0;
+  for (int v = v0; v < v1; v++) s += count[v];
+  part[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < SORT_THREADS; o <<= 1) {  // inclusive Hillis-Steele scan
+    int add = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int v = v0; v < v1; v++) {
+    offset[v] = run;
+    run += count[v];
+  }
+  __threadfence_block();
+  __syncthreads();
+  // place positions; offset[v] is advanced past each chunk's occurrences of v
+  for (int c0 = 0; c0 < BT; c0 += SORT_THREADS) {
+    const int i = c0 + tid;
+    const int n = min(SORT_THREADS, BT - c0);
+    const int v = i < BT ? clamp_tok(tok[i], V) : -1;
+    chunk_tok[tid] = v;
+    __syncthreads();
+    int before = 0, total = 0;
+    if (i < BT) {
+      for (int j = 0; j < n; j++) {
+        const int same = chunk_tok[j] == v;
+        total += same;
+        before += same & (j < tid);
+      }
+      sorted[offset[v] + before] = i;
+    }
+    __threadfence_block();
+    __syncthreads();
+    if (i < BT && before == 0) offset[v] += total;
+    __threadfence_block();
+    __syncthreads();
+  }
+}
+
+// One wave per sorted index j; the wave that starts a run of equal tokens adds the run's
+// rows (in ascending position order) to that token's dwte row.
+__global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, const float* __restrict__ dout,
+                                       const int32_t* __restrict__ tok,
+                                       const int32_t* __restrict__ sorted, int BT, int C,
+                                       int V) {
+  const int j = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= BT) return;
+  const int v = clamp_tok(tok[sorted[j]], V);
+  if (j > 0 && clamp_tok(tok[sorted[j - 1]], V) == v) return;
+  float* dst = dwte + (long long)v * C;
+  for (int c = 4 * lane; c < C; c += 256) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k = j; k < BT && clamp_tok(tok[sorted[k]], V) == v; k++)
+      s += ld4(dout + (long long)sorted[k] * C + c);
+    st4(dst + c, ld4(dst + c) + s);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// LayerNorm: one wave per row, VPL float4 per lane held in registers
+// ---------------------------------------------------------------------------------------
+template <int VPL>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(float* __restrict__ out,
+                                                            float* __restrict__ mean,
+                                                            float* __restrict__ rstd,
+                                                            const float* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ bias,
+                                                            int N, int C) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const int C4 = C / 4;
+  const float* xr = x + (long long)row * C;
+  f32x4 v[VPL];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const int c4 = lane + 64 * i;
+    v[i] = c4 < C4 ? ld4(xr + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  }
+  const float m = warp_sum(s) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    if (lane + 64 * i < C4) {
+      f32x4 d = v[i] - m;
+      ss += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+    }
+  }
+  const float rs = 1.0f / sqrtf(warp_sum(ss) / C + 1e-5f);
+  float* orow = out + (long long)row * C;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const int c4 = lane + 64 * i;
+    if (c4 < C4) st4(orow + 4 * c4, (v[i] - m) * rs * ld4(w + 4 * c4) + ld4(bias + 4 * c4));
+  }
+  if (lane == 0) {
+    if (mean) mean[row] = m;
+    if (rstd) rstd[row] = rs;
+  }
+}
+
+constexpr int LNB_ROWS = 32;  // rows per workgroup in the backward
+
+// dx (+)= rstd * (g - mean(g) - n * mean(g*n)), g = w * dout, n = (x - mean) * rstd;
+// per workgroup, partial[blk][0][:] = sum of n*dout, partial[blk][1][:] = sum of dout over
+// its rows (each wave sums its rows in order, then the four waves are added in order).
+template <int VPL>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(
+    float* __restrict__ dx, float* __restrict__ partial, const float* __restrict__ dout,
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ mean,
+    const float* __restrict__ rstd, int N, int C, int accumulate) {
+  extern __shared__ float red[];  // [4 waves][2][C]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C4 = C / 4;
+  f32x4 wv[VPL], dw[VPL], db[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const int c4 = lane + 64 * i;
+    wv[i] = c4 < C4 ? ld4(w + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    dw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    db[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int r0 = blockIdx.x * LNB_ROWS;
+  const int r1 = min(N, r0 + LNB_ROWS);
+  for (int row = r0 + wave; row < r1; row += 4) {
+    const float mu = mean[row], rs = rstd[row];
+    const float* dyr = dout + (long long)row * C;
+    const float* xr = x + (long long)row * C;
+    f32x4 dy[VPL], nv[VPL];
+    float sg = 0.f, sgn = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+      const int c4 = lane + 64 * i;
+      if (c4 < C4) {
+        dy[i] = ld4(dyr + 4 * c4);
+        nv[i] = (ld4(xr + 4 * c4) - mu) * rs;
+        f32x4 g = wv[i] * dy[i];
+        sg += (g[0] + g[1]) + (g[2] + g[3]);
+        f32x4 gn = g * nv[i];
+        sgn += (gn[0] + gn[1]) + (gn[2] + gn[3]);
+      } else {
+        dy[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        nv[i] = dy[i];
+      }
+    }
+    const float mg = warp_sum(sg) / C, mgn = warp_sum(sgn) / C;
+    float* dxr = dx + (long long)row * C;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+      const int c4 = lane + 64 * i;
+      if (c4 < C4) {
+        f32x4 d = (wv[i] * dy[i] - mg - nv[i] * mgn) * rs;
+        if (accumulate) d += ld4(dxr + 4 * c4);
+        st4(dxr + 4 * c4, d);
+        dw[i] += nv[i] * dy[i];
+        db[i] += dy[i];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const int c4 = lane + 64 * i;
+    if (c4 < C4) {
+      st4(red + (wave * 2 + 0) * C + 4 * c4, dw[i]);
+      st4(red + (wave * 2 + 1) * C + 4 * c4, db[i]);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < 2 * C; c += 256) {
+    const int which = c / C, cc = c % C;
+    float s = red[(0 * 2 + which) * C + cc];
+    s += red[(1 * 2 + which) * C + cc];
+    s += red[(2 * 2 + which) * C + cc];
+    s += red[(3 * 2 + which) * C + cc];
+    partial[((long long)blockIdx.x * 2 + which) * C + cc] = s;
+  }
+}
+
+__global__ void layernorm_bwd_final_kernel(float* __restrict__ dw, float* __restrict__ db,
+                                           const float* __restrict__ partial, int blocks, int C) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= 2 * C) return;
+  const int which = c / C, cc = c % C;
+  float s = 0.f;
+  for (int k = 0; k < blocks; k++) s += partial[((long long)k * 2 + which) * C + cc];
+  if (which == 0) dw[cc] += s;
+  else db[cc] += s;
+}
+
+// ---------------------------------------------------------------------------------------
+// softmax cross-entropy over the vocabulary: one workgroup per row
+// ---------------------------------------------------------------------------------------
+GPT2_DEVICE_INLINE void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+__global__ __launch_bounds__(256) void xent_fwd_kernel(float* __restrict__ losses,
+                                                       float* __restrict__ lse_out,
+                                                       const float* __restrict__ logits,
+                                                       const int32_t* __restrict__ targets,
+                                                       int N, int V, int ld, int32_t* err) {
+  __shared__ float sm[4], ss[4];
+  const int row = blockIdx.x;
+  const float* z = logits + (long long)row * ld;
+  float m = -INFINITY, s = 0.f;
+  const int V4 = (V + 3) / 4;
+  for (int c4 = threadIdx.x; c4 < V4; c4 += 256) {
+    f32x4 v = ld4(z + 4 * c4);
+    const int c = 4 * c4;
+    if (c + 3 >= V) {
+      if (c + 1 >= V) v[1] = -INFINITY;
+      if (c + 2 >= V) v[2] = -INFINITY;
+      if (c + 3 >= V) v[3] = -INFINITY;
+    }
+    const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    if (mx > m) {
+      s *= __expf(m - mx);
+      m = mx;
+    }
+    s += (__expf(v[0] - m) + __expf(v[1] - m)) + (__expf(v[2] - m) + __expf(v[3] - m));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    lse_merge(m, s, m2, s2);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], S = ss[0];
+    for (int k = 1; k < 4; k++) lse_merge(M, S, sm[k], ss[k]);
+    const float lse = M + logf(S);
+    int y = targets[row];
+    if (y < 0 || y >= V) {
+      if (err) *err = 1;
+      y = 0;
+    }
+    losses[row] = lse - z[y];
+    lse_out[row] = lse;
+  }
+}
+
+// in place: logits[r, v] <- (softmax - onehot(target)) * dloss for v < V, 0 on the padding
+__global__ __launch_bounds__(256) void xent_bwd_kernel(float* __restrict__ logits,
+                                                       const float* __restrict__ lse,
+                                                       const int32_t* __restrict__ targets,
+                                                       float dloss, int N, int V, int ld) {
+  const int row = blockIdx.x;
+  float* z = logits + (long long)row * ld;
+  const float l = lse[row];
+  int y = targets[row];
+  if (y < 0 || y >= V) y = 0;
+  const int L4 = ld / 4;
+  for (int c4 = threadIdx.x; c4 < L4; c4 += 256) {
+    f32x4 v = ld4(z + 4 * c4);
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int c = 4 * c4 + j;
+      o[j] = c < V ? (__expf(v[j] - l) - (c == y ? 1.f : 0.f)) * dloss : 0.f;
+    }
+    st4(z + 4 * c4, o);
+  }
+}
+
+// mean of n values by one workgroup, in a fixed order
+__global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
+                                                    const float* __restrict__ x, int n) {
+  __shared__ float part[16];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += 1024) s += x[i];
+  s = warp_sum(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int k = 0; k < 16; k++) t += part[k];
+    *out = t / n;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// AdamW
+// ---------------------------------------------------------------------------------------
+__global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
+                             float* __restrict__ m, float* __restrict__ v, long long n4,
+                             long long n, float lr, float b1, float b2, float eps, float wd,
+                             float inv_c1, float inv_c2) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    f32x4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      mm[j] = b1 * mm[j] + (1.f - b1) * gg[j];
+      vv[j] = b2 * vv[j] + (1.f - b2) * gg[j] * gg[j];
+      const float mh = mm[j] * inv_c1, vh = vv[j] * inv_c2;
+      pp[j] -= lr * (mh / (sqrtf(vh) + eps) + wd * pp[j]);
+    }
+    st4(p + 4 * i, pp);
+    st4(m + 4 * i, mm);
+    st4(v + 4 * i, vv);
+  }
+  // scalar tail (n not a multiple of 4)
+  if (blockIdx.x == 0 && threadIdx.x < (n - 4 * n4)) {
+    const long long i = 4 * n4 + threadIdx.x;
+    const float gg = g[i];
+    const float mm = b1 * m[i] + (1.f - b1) * gg;
+    const float vv = b2 * v[i] + (1.f - b2) * gg * gg;
+    m[i] = mm;
+    v[i] = vv;
+    p[i] -= lr * ((mm * inv_c1) / (sqrtf(vv * inv_c2) + eps) + wd * p[i]);
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+int encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe, int B,
+                    int T, int C, int V, int32_t* err_flag, hipStream_t stream) {
+  if (B < 1 || T < 1 || C < 4 || C % 4 || V < 1 || !aligned16(out) || !aligned16(wte) ||
+      !aligned16(wpe)) {
+    set_global_error("encoder_forward: bad arguments");
+    return -1;
+  }
+  const long long n = (long long)B * T * (C / 4);
+  ProfScope ps("encoder_fwd_kernel", (double)B * T * C, 4.0 * (3.0 * B * T * C + B * T), stream);
+  encoder_fwd_kernel<<<blocks_for(n, 256, 8192), 256, 0, stream>>>(out, tok, wte, wpe, B * T, T,
+                                                                  C, V, err_flag);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+size_t encoder_sort_scratch_ints(int BT, int V) { return (size_t)2 * V + BT; }
+
+int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok, int B,
+                     int T, int C, int V, int32_t* scratch, hipStream_t stream) {
+  if (B < 1 || T < 1 || C < 4 || C % 4 || V < 1) {
+    set_global_error("encoder_backward: bad arguments");
+    return -1;
+  }
+  const int BT = B * T;
+  int32_t* count = scratch;
+  int32_t* offset = scratch + V;
+  int32_t* sorted = scratch + 2 * (size_t)V;
+  {
+    ProfScope ps("encoder_bwd_wpe_kernel", (double)BT * C, 4.0 * ((double)BT * C + 2.0 * T * C),
+                 stream);
+    encoder_bwd_wpe_kernel<<<blocks_for((long long)T * (C / 4), 256, 8192), 256, 0, stream>>>(
+        dwpe, dout, B, T, C);
+  }
+  {
+    ProfScope ps("token_sort_kernel", 0.0, 4.0 * (3.0 * BT + 3.0 * V), stream);
+    token_sort_kernel<<<1, SORT_THREADS, 0, stream>>>(sorted, count, offset, tok, BT, V);
+  }
+  ProfScope ps("encoder_bwd_wte_kernel", (double)BT * C, 4.0 * (3.0 * BT * C + 2.0 * BT), stream);
+  encoder_bwd_wte_kernel<<<(BT + 3) / 4, 256, 0, stream>>>(dwte, dout, tok, sorted, BT, C, V);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+#define GPT2_LN_DISPATCH(VPLV, ...) \
+  switch (VPLV) {                   \
+    case 1: __VA_ARGS__(1); break;  \
+    case 2: __VA_ARGS__(2); break;  \
+    case 3: __VA_ARGS__(3); break;  \
+    case 4: __VA_ARGS__(4); break;  \
+    case 5: __VA_ARGS__(5); break;  \
+    case 6: __VA_ARGS__(6); break;  \
+    case 7: __VA_ARGS__(7); break;  \
+    case 8: __VA_ARGS__(8); break;  \
+    default: break;                 \
+  }
+
+int layernorm_forward(float* out, float* mean, float* rstd, const float* x, const float* w,
+                      const float* b, int N, int C, hipStream_t stream) {
+  const int vpl = (C / 4 + 63) / 64;
+  if (N < 1 || C < 4 || C % 4 || vpl > 8 || !aligned16(out) || !aligned16(x)) {
+    set_global_error("layernorm_forward: unsupported N=%d C=%d", N, C);
+    return -1;
+  }
+  const int grid = (N + 3) / 4;
+  ProfScope ps("layernorm_fwd_kernel", 8.0 * N * C, 4.0 * (2.0 * N * C + 2.0 * N + 2.0 * C), stream);
+#define GPT2_LNF(V) layernorm_fwd_kernel<V><<<grid, 256, 0, stream>>>(out, mean, rstd, x, w, b, N, C)
+  GPT2_LN_DISPATCH(vpl, GPT2_LNF)
+#undef GPT2_LNF
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+size_t layernorm_partial_floats(int N, int C) {
+  return (size_t)((N + LNB_ROWS - 1) / LNB_ROWS) * 2 * C;
+}
+
+int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const float* x,
+                       const float* w, const float* mean, const float* rstd, int N, int C,
+                       bool accumulate_dx, float* partial, hipStream_t stream) {
+  const int vpl = (C / 4 + 63) / 64;
+  if (N < 1 || C < 4 || C % 4 || vpl > 8) {
+    set_global_error("layernorm_backward: unsupported N=%d C=%d", N, C);
+    return -1;
+  }
+  const int blocks = (N + LNB_ROWS - 1) / LNB_ROWS;
+  const size_t lds = (size_t)8 * C * sizeof(float);
+  {
+  ProfScope ps("layernorm_bwd_kernel", 14.0 * N * C,
+               4.0 * ((accumulate_dx ? 4.0 : 3.0) * N * C + 2.0 * N + (double)blocks * 2 * C),
+               stream);
+#define GPT2_LNB(V)                                                                        \
+  layernorm_bwd_kernel<V><<<blocks, 256, lds, stream>>>(dx, partial, dout, x, w, mean, rstd, N, \
+                                                        C, accumulate_dx ? 1 : 0)
+  GPT2_LN_DISPATCH(vpl, GPT2_LNB)
+#undef GPT2_LNB
+  }
+  ProfScope ps("layernorm_bwd_final_kernel", 2.0 * blocks * C, 4.0 * (2.0 * blocks * C + 4.0 * C),
+               stream);
+  layernorm_bwd_final_kernel<<<(2 * C + 255) / 256, 256, 0, stream>>>(dw, db, partial, blocks, C);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int crossentropy_forward(float* losses, float* lse, const float* logits, const int32_t* targets,
+                         int N, int V, int ld, int32_t* err_flag, hipStream_t stream) {
+  if (N < 1 || V < 1 || ld < V || ld % 4 || !aligned16(logits)) {
+    set_global_error("crossentropy_forward: bad arguments");
+    return -1;
+  }
+  ProfScope ps("xent_fwd_kernel", 3.0 * N * V, 4.0 * ((double)N * V + 3.0 * N), stream);
+  xent_fwd_kernel<<<N, 256, 0, stream>>>(losses, lse, logits, targets, N, V, ld, err_flag);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int crossentropy_backward(float* logits, const float* lse, const int32_t* targets, float dloss,
+                          int N, int V, int ld, hipStream_t stream) {
+  if (N < 1 || V < 1 || ld < V || ld % 4 || !aligned16(logits)) {
+    set_global_error("crossentropy_backward: bad arguments");
+    return -1;
+  }
+  ProfScope ps("xent_bwd_kernel", 3.0 * N * V, 4.0 * (2.0 * N * ld + 2.0 * N), stream);
+  xent_bwd_kernel<<<N, 256, 0, stream>>>(logits, lse, targets, dloss, N, V, ld);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int mean_reduce(float* out, const float* x, int n, hipStream_t stream) {
+  if (n < 1) return -1;
+  ProfScope ps("mean_kernel", (double)n, 4.0 * (n + 1.0), stream);
+  mean_kernel<<<1, 1024, 0, stream>>>(out, x, n);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float beta1,
+          float beta2, float eps, float wd, int t, hipStream_t stream) {
+  if (t < 1 || !aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v)) {
+    set_global_error("adamw: bad arguments (t=%d)", t);
+    return -1;
+  }
+  const long long n4 = (long long)(n / 4);
+  const float inv_c1 = (float)(1.0 / (1.0 - pow((double)beta1, t)));
+  const float inv_c2 = (float)(1.0 / (1.0 - pow((double)beta2, t)));
+  ProfScope ps("adamw_kernel", 12.0 * n, 28.0 * n, stream);
+  adamw_kernel<<<blocks_for(n4, 256, 16384), 256, 0, stream>>>(p, g, m, v, n4, (long long)n, lr,
+                                                               beta1, beta2, eps, wd, inv_c1,
+                                                               inv_c2);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+}  // namespace gpt2

@@ -1,0 +1,224 @@
+/* gpt2.h -- C ABI of the MI355X (gfx950) GPT-2 training-step library, libgpt2_mi355x.so.
+ *
+ * One GPT-2-style decoder-only training step: token + position embedding gather,
+ * pre-LayerNorm blocks (causal multi-head self-attention, GELU MLP, residuals), final
+ * LayerNorm, tied lm_head with softmax cross-entropy, full backward, AdamW.
+ * The operations follow "llm.c 的中文注解-20240421" (an annotated copy of llm.c's
+ * train_gpt2.c; cited below as [llm.c] with its section numbers) and "高能技巧！60 行
+ * NumPy 代码实现一个 GPT" (GPT in 60 lines of NumPy; cited as [np60] with its section
+ * names).
+ *
+ * Conventions for every entry point:
+ *  - All tensors are fp32, row-major, unless stated. "(B,T,C)" means C is contiguous.
+ *  - Pointers documented as "device" must be HIP device (or managed) memory; "host" means
+ *    ordinary host memory. Arguments named *_is_device select between the two.
+ *  - Work is enqueued on the model's HIP stream (or the stream argument of the per-kernel
+ *    entry points); a NULL stream means the null (default) stream. Calls return once the
+ *    work is enqueued unless they read a result back to the host, which synchronises that
+ *    stream.
+ *  - Return value: GPT2_OK (0) or a negative GPT2_ERR_* code. Errors never abort the
+ *    process; gpt2_last_error() gives a message for the model's last failure, and
+ *    gpt2_last_global_error() for failures with no model (build, per-kernel calls).
+ *  - A model is bound to one device and one stream and is not re-entrant: do not call
+ *    into the same model from two threads at once.
+ */
+#ifndef GPT2_MI355X_H
+#define GPT2_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gpt2_model gpt2_model; /* opaque; owns every device buffer of one model */
+
+enum {
+  GPT2_OK = 0,
+  GPT2_ERR_ARG = -1,   /* invalid argument: null pointer, non-positive or unsupported size */
+  GPT2_ERR_SHAPE = -2, /* B,T differ from the shape the activations were sized for */
+  GPT2_ERR_TOKEN = -3, /* a token or target outside [0, V) */
+  GPT2_ERR_STATE = -4, /* call out of order (backward before a forward with targets, ...) */
+  GPT2_ERR_OOM = -5,   /* device allocation failed */
+  GPT2_ERR_HIP = -6    /* a HIP runtime call failed */
+};
+
+enum { GPT2_DTYPE_FP32 = 0 };
+
+/* ---------------------------------------------------------------------------------------
+ * Model lifetime and parameters
+ * ------------------------------------------------------------------------------------- */
+
+/* Create a model with L layers, C channels, H heads, vocabulary V and maximum sequence
+ * length maxT ([llm.c] 1.20 GPT2Config). Allocates, on the current HIP device, one flat
+ * block holding parameters, gradients and the two AdamW moments (4 x num_params fp32),
+ * all zero. Activations are allocated as one flat block at the first gpt2_forward, for
+ * that call's B and T ([llm.c] 1.23 allocates lazily; 1.19 one allocation).
+ * Requires C % H == 0, C % 4 == 0 and (C/H) % 4 == 0 with C/H <= 128; all sizes >= 1.
+ * *out receives the handle, or NULL on error. */
+int gpt2_build(gpt2_model** out, int L, int C, int H, int V, int maxT);
+
+/* As gpt2_build, plus: dtype (GPT2_DTYPE_FP32 only); if maxB > 0 and maxTseq > 0 the
+ * activation block is allocated now for exactly B = maxB, T = maxTseq; stream is the
+ * hipStream_t the model enqueues all its work on (NULL = the null stream). */
+int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dtype,
+                  int maxB, int maxTseq, void* stream);
+
+/* Release every device buffer and the handle ([llm.c] 1.27 gpt2_free). NULL is a no-op. */
+void gpt2_free(gpt2_model* model);
+
+/* Rebind the model to another hipStream_t (NULL = the null stream), after waiting for the
+ * work already enqueued on the current one. */
+int gpt2_set_stream(gpt2_model* model, void* stream);
+
+/* Block until all work enqueued on the model's stream has finished. Reports
+ * GPT2_ERR_TOKEN if a forward since the last check saw an out-of-range token. */
+int gpt2_synchronize(gpt2_model* model);
+
+/* Number of fp32 parameters: the sum of the 16 tensor sizes of [llm.c] 1.22. */
+size_t gpt2_num_params(const gpt2_model* model);
+
+/* Offsets and lengths (in floats) of the 16 parameter tensors inside the flat buffer, in
+ * the order of [llm.c] 1.16 ParameterTensors: wte (V,C), wpe (maxT,C), ln1w (L,C), ln1b
+ * (L,C), qkvw (L,3C,C), qkvb (L,3C), attprojw (L,C,C), attprojb (L,C), ln2w (L,C), ln2b
+ * (L,C), fcw (L,4C,C), fcb (L,4C), fcprojw (L,C,4C), fcprojb (L,C), lnfw (C), lnfb (C).
+ * Weight matrices are (out, in) and are applied as x . W^T ([llm.c] 1.5). */
+int gpt2_param_layout(const gpt2_model* model, size_t off[16], size_t len[16]);
+
+/* Copy num_params floats in the flat layout above into / out of the model. */
+int gpt2_set_params(gpt2_model* model, const float* src, int src_is_device);
+int gpt2_get_params(gpt2_model* model, float* dst, int dst_is_device);
+/* Parameter gradients (flat layout) as accumulated by gpt2_backward. */
+int gpt2_get_grads(gpt2_model* model, float* dst, int dst_is_device);
+/* Overwrite the gradients (flat layout); lets a caller run gpt2_adamw_step on given grads. */
+int gpt2_set_grads(gpt2_model* model, const float* src, int src_is_device);
+/* AdamW first and second moments (flat layout); either pointer may be NULL. */
+int gpt2_get_adam_state(gpt2_model* model, float* m, float* v, int dst_is_device);
+
+/* ---------------------------------------------------------------------------------------
+ * Training step: gpt2_zero_grad -> gpt2_forward(targets) -> gpt2_backward -> gpt2_adamw_step
+ * ------------------------------------------------------------------------------------- */
+
+/* Forward pass ([llm.c] 1.23 gpt2_forward). tokens and targets: device int32 (B,T),
+ * caller-owned; they are copied into the model, so they may be reused once this returns.
+ * targets may be NULL (no loss; backward is then refused). mean_loss: host float or NULL.
+ * If non-NULL the call waits for the step and stores the mean cross-entropy over the B*T
+ * positions, or -1 when targets is NULL; it also reports GPT2_ERR_TOKEN for a token or
+ * target outside [0, V) (such entries are read as 0 so no access goes out of bounds).
+ * If NULL nothing is waited for; the loss stays on the device (gpt2_get_losses).
+ * Errors: ERR_ARG (T > maxT, B or T < 1), ERR_SHAPE (B,T differ from the allocation). */
+int gpt2_forward(gpt2_model* model, const int32_t* tokens, const int32_t* targets, int B,
+                 int T, float* mean_loss);
+
+/* Per-position losses (B,T) and the logits (B,T,V) of the last forward. The logits buffer
+ * is reused for their gradient by gpt2_backward, so gpt2_get_logits is valid only
+ * between a forward and the next backward (else ERR_STATE). */
+int gpt2_get_losses(gpt2_model* model, float* dst, int dst_is_device);
+int gpt2_get_logits(gpt2_model* model, float* dst, int dst_is_device);
+
+/* Set all parameter gradients to zero ([llm.c] 1.24 gpt2_zero_grad). The library writes,
+ * rather than accumulates, every activation gradient, so only parameter gradients need
+ * zeroing. */
+int gpt2_zero_grad(gpt2_model* model);
+
+/* Backward pass ([llm.c] 1.25 gpt2_backward) of the mean loss of the last forward, which
+ * must have had targets (else ERR_STATE). Adds d(mean loss)/d(param) to the gradients. */
+int gpt2_backward(gpt2_model* model);
+
+/* One AdamW update of every parameter ([llm.c] 1.26 gpt2_update): m = b1 m + (1-b1) g;
+ * v = b2 v + (1-b2) g^2; p -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd p).
+ * t is the 1-based step count (ERR_ARG if t < 1). */
+int gpt2_adamw_step(gpt2_model* model, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, int t);
+
+/* Launch profiler. gpt2_profile_enable(1) clears the record and from then on brackets every
+ * kernel launch of the library with two HIP events on the launch's stream, tagged with the
+ * kernel's name and that launch's algorithmic flops and HBM bytes; (0) stops recording.
+ * gpt2_profile_summary waits for the recorded events and writes one line per kernel name,
+ * "name<TAB>launches<TAB>total_ms<TAB>total_flop<TAB>total_bytes", into buf (ERR_ARG if
+ * len is too small). Process-wide state; not thread-safe. */
+int gpt2_profile_enable(int on);
+int gpt2_profile_summary(char* buf, size_t len);
+
+const char* gpt2_last_error(const gpt2_model* model);
+const char* gpt2_last_global_error(void);
+const char* gpt2_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Per-kernel entry points: the production kernels on caller device buffers, enqueued on
+ * `stream` (hipStream_t, NULL = null stream). They exist so each kernel can be checked
+ * against a reference on its own. All pointers are device pointers unless stated.
+ * ------------------------------------------------------------------------------------- */
+
+/* [llm.c] 1.1: out (B,T,C) = wte[tok] + wpe[t]. tok (B,T) int32; entries outside [0,V)
+ * read row 0 and set *err_flag (device int, may be NULL) to 1. */
+int gpt2_k_encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe,
+                           int B, int T, int C, int V, int32_t* err_flag, void* stream);
+
+/* [llm.c] 1.2: dwte[tok[b,t]] += dout[b,t]; dwpe[t] += sum_b dout[b,t]. Deterministic:
+ * rows of one token are summed in ascending (b,t) order. Tokens must be in [0,V). */
+int gpt2_k_encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
+                            int B, int T, int C, int V, void* stream);
+
+/* [llm.c] 1.3, [np60] Layer Norm: per row of x (N,C), out = (x-mean)*rstd*w + b with the
+ * biased variance and rstd = 1/sqrt(var + 1e-5); mean, rstd (N) may be NULL. */
+int gpt2_k_layernorm_forward(float* out, float* mean, float* rstd, const float* x,
+                             const float* w, const float* b, int N, int C, void* stream);
+
+/* [llm.c] 1.4: dx (N,C) += LN backward; dw, db (C) += column sums. Deterministic. */
+int gpt2_k_layernorm_backward(float* dx, float* dw, float* db, const float* dout,
+                              const float* x, const float* w, const float* mean,
+                              const float* rstd, int N, int C, void* stream);
+
+/* [llm.c] 1.5 (+1.9, 1.11 fused): out (N,OC) = inp (N,C) . W(OC,C)^T + bias (bias may be
+ * NULL), then by `epilogue`: 0 store; 1 also out2 = gelu(out) (tanh form, [llm.c] 1.9);
+ * 2 out = resid + result (resid (N,OC) may alias out). ld_out >= OC is out's row stride. */
+int gpt2_k_matmul_forward(float* out, float* out2, const float* resid, const float* inp,
+                          const float* W, const float* bias, int N, int C, int OC,
+                          int ld_out, int epilogue, void* stream);
+
+/* [llm.c] 1.6 (+1.10 fused): dinp (N,C) = dout (N,OC) . W (OC,C) -- written, not
+ * accumulated; if gelu_pre != NULL, dinp = gelu'(gelu_pre) * (dout . W) (gelu_pre (N,C));
+ * dW (OC,C) += dout^T . inp; dbias (OC) += column sums of dout (may be NULL).
+ * ld_dout >= OC is dout's row stride. dinp may be NULL (skip), as may dW. */
+int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* dout,
+                           const float* inp, const float* W, const float* gelu_pre, int N,
+                           int C, int OC, int ld_dout, void* stream);
+
+/* [llm.c] 1.7, [np60] Attention: qkv (B,T,3C) -> out (B,T,C), causal softmax attention
+ * per head with scale 1/sqrt(C/NH). lse (B,NH,T) receives each query row's log-sum-exp
+ * of the scaled scores (what the backward needs instead of the (B,NH,T,T) matrices). */
+int gpt2_k_attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C,
+                             int NH, void* stream);
+
+/* [llm.c] 1.8: dqkv (B,T,3C) = gradient of the attention output w.r.t. qkv (written),
+ * given dout (B,T,C), the forward's qkv, out and lse. */
+int gpt2_k_attention_backward(float* dqkv, const float* dout, const float* qkv,
+                              const float* out, const float* lse, int B, int T, int C,
+                              int NH, void* stream);
+
+/* [llm.c] 1.13 + 1.14: per row of logits (N rows of V, row stride ld >= V):
+ * lse = logsumexp(row); loss = lse - row[target]. Writes losses (N) and lse (N); sets
+ * *err_flag (may be NULL) to 1 for a target outside [0,V) and treats it as 0. */
+int gpt2_k_crossentropy_forward(float* losses, float* lse, const float* logits,
+                                const int32_t* targets, int N, int V, int ld,
+                                int32_t* err_flag, void* stream);
+
+/* [llm.c] 1.15: in place, logits[r,v] <- (exp(logits[r,v] - lse[r]) - [v == target[r]]) *
+ * dloss for v < V, and 0 for V <= v < ld. */
+int gpt2_k_crossentropy_backward(float* logits, const float* lse, const int32_t* targets,
+                                 float dloss, int N, int V, int ld, void* stream);
+
+/* Mean of n floats into *out (device float), summed in a fixed order. */
+int gpt2_k_mean(float* out, const float* x, int n, void* stream);
+
+/* [llm.c] 1.26: AdamW over n elements of p, g, m, v (see gpt2_adamw_step). */
+int gpt2_k_adamw(float* p, const float* g, float* m, float* v, size_t n, float lr,
+                 float beta1, float beta2, float eps, float weight_decay, int t, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_MI355X_H */

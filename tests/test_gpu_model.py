@@ -1,0 +1,221 @@
+"""Whole training steps through the C ABI (gpt2_build / forward / backward / adamw_step)
+against the fp64 oracle on the same seeded parameters and tokens.
+
+- tiny model (L1 C16 H4 V27, B4 T16): 1 step element by element, then 10 steps;
+- a small multi-layer model with ragged tiles (L2 C64 H4 V1000, B3 T100): 3 steps;
+- GPT-2 124M shape at B4 T64: one full step element by element (the oracle runs one
+  single-threaded instance per batch row in parallel threads; the batch gradient is the
+  mean of the row gradients because every row has T positions);
+- GPT-2 124M shape at B16 T1024, in the launch configuration the benchmark times: the
+  oracle checks sampled outputs (by causality the loss and logits of positions 0..63 of a
+  row depend only on that row's first 64 tokens), plus properties that hold at any size;
+- error paths of the ABI.
+"""
+import concurrent.futures as cf
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from decoder_only_transformer_05_amd import synth
+from parity import assert_close, assert_loss, stats, PARAM_ATOL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from decoder_only_transformer_05_amd import binding as gb  # noqa: E402
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def dev_i32(a):
+    return torch.tensor(np.ascontiguousarray(a, dtype=np.int32), device="cuda")
+
+
+def make_model(shape, B=0, T=0):
+    return gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, B, T)
+
+
+def oracle_rows(shape, params64, tok, tgt, want_logits=False, workers=8):
+    """Oracle forward+backward of a batch as independent single-row runs (threads)."""
+    B = tok.shape[0]
+    with cf.ThreadPoolExecutor(max_workers=min(B, workers)) as ex:
+        rows = list(ex.map(lambda b: oracle.gpt2_step(shape, params64, tok[b:b + 1],
+                                                      tgt[b:b + 1], want_logits=want_logits),
+                           range(B)))
+    out = {"loss": sum(r["loss"] for r in rows) / B,
+           "grads": sum(r["grads"] for r in rows) / B}
+    if want_logits:
+        out["logits"] = np.concatenate([r["logits"] for r in rows])
+    return out
+
+
+def compare_grads(shape, got, ref, BT):
+    """allclose per parameter tensor, plus the same after scaling by B*T (see parity.py)."""
+    sizes = synth.param_sizes(shape.L, shape.C, shape.V, shape.maxT)
+    off = 0
+    for name, n in zip(synth.PARAM_NAMES, sizes):
+        a, o = got[off:off + n], ref[off:off + n]
+        assert_close(f"grad {name}", a, o)
+        assert_close(f"grad {name} x BT", a.astype(np.float64) * BT, o * BT, atol=1e-6)
+        off += n
+
+
+def run_steps(shape, wl_seed, B, T, steps, token_mode, scale_residual, check_every=True):
+    p0 = synth.init_params(shape, wl_seed, scale_residual)
+    m = make_model(shape)
+    m.set_params(p0)
+    rp, rm, rv = p0.astype(np.float64), np.zeros(p0.size), np.zeros(p0.size)
+    for step in range(steps):
+        tok, tgt = synth.batch(wl_seed, B, T, shape.V, step=step, mode=token_mode)
+        m.zero_grad()
+        loss = m.forward(dev_i32(tok), dev_i32(tgt))
+        if check_every or step == 0:
+            logits = np.empty((B, T, shape.V), np.float32)
+            m.get_logits(logits)
+        m.backward()
+        grads = m.get_grads()
+        m.adamw_step(t=step + 1, **HP)
+        ref = oracle.gpt2_step(shape, rp, tok, tgt, want_logits=True)
+        assert_loss(loss, ref["loss"])
+        if check_every or step == 0:
+            assert_close("logits", logits, ref["logits"])
+            compare_grads(shape, grads, ref["grads"], B * T)
+        rp, rm, rv = oracle.adamw(rp, ref["grads"], rm, rv, HP["lr"], HP["beta1"], HP["beta2"],
+                                  HP["eps"], HP["weight_decay"], step + 1)
+    got = m.get_params()
+    err = np.abs(got - rp).max()
+    assert err <= PARAM_ATOL, err
+    mg, vg = m.get_adam_state()
+    assert_close("adam m", mg, rm, atol=1e-9)
+    m.close()
+
+
+def test_tiny_one_step_and_ten_steps():
+    w = synth.WORKLOADS["tiny"]
+    run_steps(w.shape, w.seed, w.B, w.T, 1, w.token_mode, w.scale_residual)
+    run_steps(w.shape, w.seed, w.B, w.T, 10, w.token_mode, w.scale_residual)
+
+
+def test_small_multilayer_ragged_three_steps():
+    shape = synth.ModelShape(L=2, C=64, H=4, V=1000, maxT=128)
+    run_steps(shape, 4242, 3, 100, 3, "stream", True)
+
+
+def test_gpt2_124m_b4_t64_one_step():
+    w = synth.WORKLOADS["gpt2_124m_b4_t64"]
+    shape = w.shape
+    p0 = synth.init_params(shape, w.seed, w.scale_residual)
+    tok, tgt = synth.batch(w.seed, w.B, w.T, shape.V, mode=w.token_mode)
+    m = make_model(shape, w.B, w.T)
+    m.set_params(p0)
+    m.zero_grad()
+    loss = m.forward(dev_i32(tok), dev_i32(tgt))
+    logits = np.empty((w.B, w.T, shape.V), np.float32)
+    m.get_logits(logits)
+    m.backward()
+    grads = m.get_grads()
+    m.adamw_step(t=1, **HP)
+    params = m.get_params()
+    m.close()
+
+    p64 = p0.astype(np.float64)
+    ref = oracle_rows(shape, p64, tok, tgt, want_logits=True)
+    assert_loss(loss, ref["loss"])
+    s = assert_close("logits", logits, ref["logits"])
+    print("logits", s)
+    compare_grads(shape, grads, ref["grads"], w.B * w.T)
+    rp, _, _ = oracle.adamw(p64, ref["grads"], np.zeros(p0.size), np.zeros(p0.size), HP["lr"],
+                            HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], 1)
+    # the first AdamW step moves each parameter by about lr * sign(g); elements whose
+    # gradient is below eps are sensitive to its last bits, so the GPU's own fp32 gradient
+    # is also fed to the oracle update to check the rule by itself
+    rp_own, _, _ = oracle.adamw(p64, grads, np.zeros(p0.size), np.zeros(p0.size), HP["lr"],
+                                HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], 1)
+    assert np.abs(params - rp_own).max() <= 1e-6
+    assert np.abs(params - rp).max() <= PARAM_ATOL
+
+
+def test_gpt2_124m_b16_t1024_sampled_and_properties():
+    w = synth.WORKLOADS["gpt2_124m_b16_t1024"]
+    shape = w.shape
+    B, T, V = w.B, w.T, shape.V
+    p0 = synth.init_params(shape, w.seed, w.scale_residual)
+    tok, tgt = synth.batch(w.seed, B, T, V, mode=w.token_mode)
+    m = make_model(shape, B, T)
+    m.set_params(p0)
+    m.zero_grad()
+    loss = m.forward(dev_i32(tok), dev_i32(tgt))
+    losses = torch.empty((B, T), device="cuda")
+    m.get_losses(losses)
+    logits = torch.empty((B, T, V), device="cuda")
+    m.get_logits(logits)
+    rows, P = [0, 7, 15], 64
+    got_logits = logits[rows, :P].cpu().numpy()
+    got_losses = losses[rows, :P].cpu().numpy()
+    del logits
+    m.backward()
+    g1 = torch.empty(m.num_params, device="cuda")
+    m.get_grads(g1)
+    # the same step again from zeroed gradients is bitwise identical (no atomics anywhere)
+    m.zero_grad()
+    assert m.forward(dev_i32(tok), dev_i32(tgt)) == loss
+    m.backward()
+    g2 = torch.empty(m.num_params, device="cuda")
+    m.get_grads(g2)
+    assert torch.equal(g1, g2)
+    assert bool(torch.isfinite(g1).all())
+    m.adamw_step(t=1, **HP)
+    m.close()
+
+    # sampled outputs against the oracle: positions 0..63 of three rows
+    ref = oracle.gpt2_step(shape, p0.astype(np.float64), tok[rows, :P], tgt[rows, :P],
+                           want_logits=True, want_losses=True, want_grads=False)
+    assert_close("sampled logits", got_logits, ref["logits"])
+    assert_close("sampled losses", got_losses, ref["losses"], rtol=1e-5, atol=1e-5)
+    # loss at init: ln V + C*sigma^2/2 within a few standard errors
+    expect = math.log(V) + shape.C * 0.02 ** 2 / 2
+    assert abs(loss - expect) < 0.05, (loss, expect)
+
+
+def test_abi_error_paths():
+    shape = synth.WORKLOADS["tiny"].shape
+    m = make_model(shape)
+    m.set_params(synth.init_params(shape, 1, False))
+    tok = dev_i32(np.zeros((2, 8), np.int32))
+    with pytest.raises(gb.GPT2Error) as e:
+        m.backward()
+    assert e.value.code == -4
+    with pytest.raises(gb.GPT2Error) as e:
+        m.adamw_step(t=1)
+    assert e.value.code == -4
+    with pytest.raises(gb.GPT2Error) as e:
+        m.forward(dev_i32(np.zeros((1, shape.maxT + 1), np.int32)))
+    assert e.value.code == -1
+    assert m.forward(tok) == -1.0  # no targets: no loss
+    with pytest.raises(gb.GPT2Error) as e:
+        m.backward()
+    assert e.value.code == -4
+    with pytest.raises(gb.GPT2Error) as e:
+        m.forward(dev_i32(np.zeros((3, 8), np.int32)))
+    assert e.value.code == -2
+    bad = np.zeros((2, 8), np.int32)
+    bad[1, 3] = shape.V
+    with pytest.raises(gb.GPT2Error) as e:
+        m.forward(dev_i32(bad), tok)
+    assert e.value.code == -3
+    with pytest.raises(gb.GPT2Error) as e:
+        m.forward(tok, dev_i32(bad))
+    assert e.value.code == -3
+    loss = m.forward(tok, tok)
+    assert math.isfinite(loss)
+    m.backward()
+    with pytest.raises(gb.GPT2Error) as e:
+        m.get_logits(np.empty((2, 8, shape.V), np.float32))
+    assert e.value.code == -4
+    with pytest.raises(gb.GPT2Error) as e:
+        m.adamw_step(t=0)
+    assert e.value.code == -1
+    m.adamw_step(t=1)
+    m.close()
