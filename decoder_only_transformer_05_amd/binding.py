@@ -108,15 +108,23 @@ def current_stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _ptr(t) -> int | None:
-    """Device pointer of a torch tensor (contiguous), or None."""
+def _ptr(t, kind: str = "f32") -> int | None:
+    """Device pointer of a contiguous torch tensor of the expected dtype, or None."""
     if t is None:
         return None
+    torch = _torch()
+    want = torch.float32 if kind == "f32" else torch.int32
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
+    if t.dtype != want:
+        raise ValueError(f"expected a {want} tensor, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     return t.data_ptr()
+
+
+def _iptr(t) -> int | None:
+    return _ptr(t, "i32")
 
 
 def _host_or_device(buf):
@@ -204,7 +212,7 @@ class GPT2:
         B = tokens.shape[0] if B is None else B
         T = tokens.shape[1] if T is None else T
         loss = _f(0.0)
-        self._c(lib().gpt2_forward(self.h, _ptr(tokens), _ptr(targets), B, T,
+        self._c(lib().gpt2_forward(self.h, _iptr(tokens), _iptr(targets), B, T,
                                    ctypes.byref(loss) if want_loss else None))
         return float(loss.value) if want_loss else None
 
@@ -246,12 +254,12 @@ def profile_summary() -> dict:
 
 # ---- per-kernel entry points (device tensors; torch's current stream) --------------------
 def k_encoder_forward(out, tok, wte, wpe, B, T, C, V, err_flag=None):
-    _check(lib().gpt2_k_encoder_forward(_ptr(out), _ptr(tok), _ptr(wte), _ptr(wpe), B, T, C, V,
-                                        _ptr(err_flag), current_stream()))
+    _check(lib().gpt2_k_encoder_forward(_ptr(out), _iptr(tok), _ptr(wte), _ptr(wpe), B, T, C, V,
+                                        _iptr(err_flag), current_stream()))
 
 
 def k_encoder_backward(dwte, dwpe, dout, tok, B, T, C, V):
-    _check(lib().gpt2_k_encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(dout), _ptr(tok), B, T, C,
+    _check(lib().gpt2_k_encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(dout), _iptr(tok), B, T, C,
                                          V, current_stream()))
 
 
@@ -291,12 +299,12 @@ def k_attention_backward(dqkv, dout, qkv, out, lse, B, T, C, NH):
 
 def k_crossentropy_forward(losses, lse, logits, targets, N, V, ld, err_flag=None):
     _check(lib().gpt2_k_crossentropy_forward(_ptr(losses), _ptr(lse), _ptr(logits),
-                                             _ptr(targets), N, V, ld, _ptr(err_flag),
+                                             _iptr(targets), N, V, ld, _iptr(err_flag),
                                              current_stream()))
 
 
 def k_crossentropy_backward(logits, lse, targets, dloss, N, V, ld):
-    _check(lib().gpt2_k_crossentropy_backward(_ptr(logits), _ptr(lse), _ptr(targets), dloss, N, V,
+    _check(lib().gpt2_k_crossentropy_backward(_ptr(logits), _ptr(lse), _iptr(targets), dloss, N, V,
                                               ld, current_stream()))
 
 

@@ -30,17 +30,26 @@ GPT2_DEVICE_INLINE float warp_max(float v) {
   return v;
 }
 
-// tanh-form GELU ("llm.c 的中文注解", section 1.9; "60 行 NumPy 代码实现一个 GPT", GELU).
-// tanh(u) is evaluated as 1 - 2/(exp(2u)+1), which saturates correctly for large |u|.
+// tanh-form GELU ("llm.c 的中文注解", sections 1.9 and 1.10; "60 行 NumPy 代码实现一个 GPT",
+// GELU): gelu(x) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// Evaluated through s = sigmoid(2u), using 1 + tanh(u) = 2s and sech^2(u) = 4 s (1 - s), so
+// neither the function nor its derivative subtracts nearly equal numbers for negative x
+// (1 + tanh(u) computed directly loses all its bits there). u is clamped to +-30, where s
+// is 0 or 1 to fp32 precision, so exp cannot overflow.
 #define GPT2_GELU_S 0.7978845608028654f  // sqrt(2/pi)
-GPT2_DEVICE_INLINE float gelu_tanh_arg(float x) { return GPT2_GELU_S * (x + 0.044715f * x * x * x); }
-GPT2_DEVICE_INLINE float fast_tanh(float u) { return 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f); }
-GPT2_DEVICE_INLINE float gelu_fwd(float x) { return 0.5f * x * (1.0f + fast_tanh(gelu_tanh_arg(x))); }
-// derivative of the tanh form (section 1.10), with sech^2 = 1 - tanh^2
+GPT2_DEVICE_INLINE float gelu_u(float x) {
+  return fminf(fmaxf(GPT2_GELU_S * (x + 0.044715f * x * x * x), -30.f), 30.f);
+}
+GPT2_DEVICE_INLINE float gelu_fwd(float x) {
+  const float s = 1.0f / (1.0f + __expf(-2.0f * gelu_u(x)));
+  return x * s;
+}
+// d gelu / dx = s + 2 x s (1 - s) u'(x), u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2)
 GPT2_DEVICE_INLINE float gelu_bwd(float x) {
-  float th = fast_tanh(gelu_tanh_arg(x));
-  return 0.5f * (1.0f + th) +
-         0.5f * x * (1.0f - th * th) * GPT2_GELU_S * (1.0f + 3.0f * 0.044715f * x * x);
+  const float e = __expf(-2.0f * gelu_u(x));
+  const float s = 1.0f / (1.0f + e);
+  const float one_minus_s = e * s;
+  return s + 2.0f * x * s * one_minus_s * GPT2_GELU_S * (1.0f + 3.0f * 0.044715f * x * x);
 }
 
 // Error reporting shared by the translation units of the library.
