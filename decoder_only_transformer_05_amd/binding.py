@@ -236,8 +236,8 @@ class GPT2:
         return out
 
 
-def profile_enable(on: bool = True):
-    _check(lib().gpt2_profile_enable(1 if on else 0))
+def profile_enable(on: bool = True, shapes: bool = False):
+    _check(lib().gpt2_profile_enable((2 if shapes else 1) if on else 0))
 
 
 def profile_summary() -> dict:

@@ -32,8 +32,24 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int TILE = 64;    // queries per workgroup / keys per LDS tile
 constexpr int NTHR = 128;   // two waves, 32 queries (or keys) each
 
-GPT2_DEVICE_INLINE f32x4 load4_masked(const float* p, bool ok) {
-  return ok ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+// Loads 4 floats of row t, columns d..d+3 (row stride ld) without a branch: the address is
+// clamped into the tensor (t <= T-1, d <= hs-4) and out-of-range values are replaced by 0.
+GPT2_DEVICE_INLINE f32x4 load4_rowcol(const float* base, long long ld, int t, int d, int T,
+                                      int hs) {
+  const int tc = min(t, T - 1), dc = min(d, hs - 4);
+  const f32x4 x = *reinterpret_cast<const f32x4*>(base + (long long)tc * ld + dc);
+  return (t < T && d < hs) ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// 1-D grid over (tile, head, batch) with the tile index fastest; logical ids are made
+// XCD-local, so all tiles of one (batch, head) -- which share its K and V -- run on the same
+// XCD and its L2.
+GPT2_DEVICE_INLINE void tile_of_block(int ntiles, int NH, int* tile, int* head, int* b) {
+  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  *tile = lid % ntiles;
+  const int bh = lid / ntiles;
+  *head = bh % NH;
+  *b = bh / NH;
 }
 
 // Cooperative load of `rows` x HSP values starting at row `row0` of a strided tensor
@@ -48,8 +64,7 @@ GPT2_DEVICE_INLINE void load_tile(float (*S)[HSP + 4], const float* base, long l
     const int f = tid + NTHR * i;
     const int row = f / F4, d = 4 * (f % F4);
     const int t = row0 + row;
-    *reinterpret_cast<f32x4*>(&S[row][d]) =
-        load4_masked(base + (long long)t * ld + d, t < T && d < hs);
+    *reinterpret_cast<f32x4*>(&S[row][d]) = load4_rowcol(base, ld, t, d, T, hs);
   }
 }
 
@@ -67,8 +82,9 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
   __shared__ float Vs[TILE][LD];
 
   const int nqt = (T + TILE - 1) / TILE;
-  const int qt = nqt - 1 - blockIdx.x;  // longest rows first
-  const int head = blockIdx.y, b = blockIdx.z;
+  int qt, head, b;
+  tile_of_block(nqt, NH, &qt, &head, &b);
+  qt = nqt - 1 - qt;  // longest rows first
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
@@ -80,7 +96,7 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
 #pragma unroll
   for (int g = 0; g < HSP / 8; g++) {
     const int d = 8 * g + 4 * hf;
-    f32x4 v = load4_masked(base + (long long)qm * C3 + d, d < hs);
+    f32x4 v = load4_rowcol(base, C3, qm, d, T, hs);
 #pragma unroll
     for (int j = 0; j < 4; j++) qf[4 * g + j] = v[j] * scale_log2;
   }
@@ -202,8 +218,8 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
   __shared__ float Ds[TILE];
 
   const int nkt = (T + TILE - 1) / TILE;
-  const int kt = nkt - 1 - blockIdx.x;  // ordering only; every tile is independent
-  const int head = blockIdx.y, b = blockIdx.z;
+  int kt, head, b;
+  tile_of_block(nkt, NH, &kt, &head, &b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
@@ -218,8 +234,8 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
 #pragma unroll
   for (int g = 0; g < HSP / 8; g++) {
     const int d = 8 * g + 4 * hf;
-    f32x4 kv = load4_masked(base + (long long)km * C3 + C + d, d < hs);
-    f32x4 vv = load4_masked(base + (long long)km * C3 + 2 * C + d, d < hs);
+    f32x4 kv = load4_rowcol(base + C, C3, km, d, T, hs);
+    f32x4 vv = load4_rowcol(base + 2 * C, C3, km, d, T, hs);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       kf[4 * g + j] = kv[j];
@@ -318,8 +334,9 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(
   __shared__ float Vs[TILE][LD];
 
   const int nqt = (T + TILE - 1) / TILE;
-  const int qt = nqt - 1 - blockIdx.x;
-  const int head = blockIdx.y, b = blockIdx.z;
+  int qt, head, b;
+  tile_of_block(nqt, NH, &qt, &head, &b);
+  qt = nqt - 1 - qt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
@@ -334,8 +351,8 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int g = 0; g < HSP / 8; g++) {
     const int d = 8 * g + 4 * hf;
-    f32x4 qv = load4_masked(base + (long long)qm * C3 + d, d < hs);
-    f32x4 ov = load4_masked(dobase + (long long)qm * C + d, d < hs);
+    f32x4 qv = load4_rowcol(base, C3, qm, d, T, hs);
+    f32x4 ov = load4_rowcol(dobase, C, qm, d, T, hs);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       qf[4 * g + j] = qv[j];
@@ -426,7 +443,7 @@ int attention_forward(float* out, float* lse, const float* qkv, int B, int T, in
   }
   const int hs = C / NH;
   const float scale_log2 = kLog2e / sqrtf((float)hs);
-  dim3 grid((T + TILE - 1) / TILE, NH, B);
+  dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   const double tri = (double)T * (T + 1) / 2.0;  // causal (query, key) pairs per head
   ProfScope ps("attn_fwd_kernel", 4.0 * B * NH * hs * tri,
                4.0 * ((double)B * T * 3 * C + (double)B * T * C + (double)B * NH * T), stream);
@@ -455,7 +472,7 @@ int attention_backward(float* dqkv, const float* dout, const float* qkv, const f
     attn_bwd_rowdot_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
         dscratch, dout, out, B, T, C, NH, hs);
   }
-  dim3 grid((T + TILE - 1) / TILE, NH, B);
+  dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
     ProfScope ps("attn_bwd_dkdv_kernel", 6.0 * B * NH * hs * tri,
                  4.0 * (3.0 * BTC + BTC + 2.0 * rows + 2.0 * BTC), stream);

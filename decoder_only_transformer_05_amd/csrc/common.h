@@ -19,6 +19,16 @@ GPT2_DEVICE_INLINE f32x16 mfma32x32x2(float a, float b, f32x16 acc) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
 }
 
+// Workgroups of a launch are dealt to the 8 XCDs of the chip round-robin (hardware block i
+// runs on XCD i % 8), and each XCD has its own L2. This maps the hardware block id to a
+// logical id such that logical ids [x*n/8, (x+1)*n/8) all run on XCD x, so neighbouring
+// logical tiles (which read the same operand panels) share one L2.
+GPT2_DEVICE_INLINE int xcd_logical_block(int bid, int nblocks) {
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nblocks >> 3, rem = nblocks & 7;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
 GPT2_DEVICE_INLINE float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -16,6 +16,7 @@
 // MFMA blocks along M take adjacent rows m = 2r and 2r+1, so one 8-byte LDS read feeds two
 // MFMAs, and the results are un-interleaved in the epilogue.
 #include <cstdio>
+#include <cstring>
 
 #include "kernels.h"
 
@@ -35,41 +36,43 @@ struct Args {
   const float* bias;
   int lda, ldb, ldc;
   int M, N, K;
-  int k_split;      // K elements per blockIdx.z (multiple of BK)
-  long long c_zstride;  // floats between the partial outputs of successive splits (0 = none)
+  float* colsum;     // see Gemm::colsum (or its per-split partials)
+  int k_split;       // K elements per split (multiple of BK)
+  int splits;
+  long long c_zstride;       // floats between the partial outputs of successive splits
+  long long colsum_zstride;  // floats between per-split colsum partials (0: accumulate)
 };
+
+constexpr int GROUP_M = 8;  // m-tiles that sweep the n-tiles together (L2 reuse of A and B)
 
 // Loads one K-slab of an operand into registers (4 float4 per thread) and later stores it to
 // LDS in [k][row] order. `rows` is M (for A) or N (for B).
 //  trans == false: operand stored (rows, K) row-major: thread -> (row = tid/8 + 32i, k4 = tid%8)
 //  trans == true : operand stored (K, rows):          thread -> (k = tid/32 + 8i, r4 = tid%32)
+// The loads carry no branches and no use of their values before the LDS store, so all eight
+// of a thread's loads stay in flight across the MFMAs of the current slab. Addresses are
+// clamped into the operand: a row past `rows` reads the last row (its products only reach
+// outputs that are never stored), and K indices past `kend` read a valid element whose value
+// is replaced by zero when the slab is written to LDS.
 template <bool TRANS>
 struct SlabLoader {
   f32x4 v[4];
+  int k0, kend;
 
   __device__ __forceinline__ void load(const float* __restrict__ P, int ld, int row0, int rows,
-                                       int k0, int kend, int tid) {
+                                       int k0_, int kend_, int tid) {
+    k0 = k0_;
+    kend = kend_;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       if (!TRANS) {
-        int r = row0 + tid / 8 + 32 * i;
-        int k = k0 + 4 * (tid % 8);
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (r < rows && k < kend) {
-          x = *reinterpret_cast<const f32x4*>(P + (long long)r * ld + k);
-          if (k + 3 >= kend) {
-            if (k + 1 >= kend) x[1] = 0.f;
-            if (k + 2 >= kend) x[2] = 0.f;
-            if (k + 3 >= kend) x[3] = 0.f;
-          }
-        }
-        v[i] = x;
+        const int r = min(row0 + tid / 8 + 32 * i, rows - 1);
+        const int k = min(k0 + 4 * (tid % 8), (kend - 1) & ~3);
+        v[i] = *reinterpret_cast<const f32x4*>(P + (long long)r * ld + k);
       } else {
-        int k = k0 + tid / 32 + 8 * i;
-        int r = row0 + 4 * (tid % 32);
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (k < kend && r < rows) x = *reinterpret_cast<const f32x4*>(P + (long long)k * ld + r);
-        v[i] = x;
+        const int k = min(k0 + tid / 32 + 8 * i, kend - 1);
+        const int r = min(row0 + 4 * (tid % 32), (rows - 1) & ~3);
+        v[i] = *reinterpret_cast<const f32x4*>(P + (long long)k * ld + r);
       }
     }
   }
@@ -79,17 +82,17 @@ struct SlabLoader {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       if (!TRANS) {
-        int r = tid / 8 + 32 * i;
-        int k = 4 * (tid % 8);
-        S[k + 0][r] = v[i][0];
-        S[k + 1][r] = v[i][1];
-        S[k + 2][r] = v[i][2];
-        S[k + 3][r] = v[i][3];
+        const int r = tid / 8 + 32 * i;
+        const int k = 4 * (tid % 8);
+        const int kg = k0 + k;  // global K index of element 0
+#pragma unroll
+        for (int j = 0; j < 4; j++) S[k + j][r] = kg + j < kend ? v[i][j] : 0.f;
       } else {
-        int k = tid / 32 + 8 * i;
-        int r = 4 * (tid % 32);
-        *reinterpret_cast<f32x2*>(&S[k][r]) = f32x2{v[i][0], v[i][1]};
-        *reinterpret_cast<f32x2*>(&S[k][r + 2]) = f32x2{v[i][2], v[i][3]};
+        const int k = tid / 32 + 8 * i;
+        const int r = 4 * (tid % 32);
+        const bool ok = k0 + k < kend;
+        *reinterpret_cast<f32x2*>(&S[k][r]) = ok ? f32x2{v[i][0], v[i][1]} : f32x2{0.f, 0.f};
+        *reinterpret_cast<f32x2*>(&S[k][r + 2]) = ok ? f32x2{v[i][2], v[i][3]} : f32x2{0.f, 0.f};
       }
     }
   }
@@ -151,12 +154,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // 1-D grid: logical block -> (split z, m-tile, n-tile), XCD-local and grouped
+  const int nM = (g.M + BM - 1) / BM, nN = (g.N + BN - 1) / BN;
+  const int tiles = nM * nN;
+  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int z = lid / tiles;
+  const int t = lid - z * tiles;
+  const int group = t / (GROUP_M * nN);
+  const int first_m = group * GROUP_M;
+  const int gsz = min(nM - first_m, GROUP_M);
+  const int tin = t - group * GROUP_M * nN;
+  const int mt = first_m + tin % gsz, nt = tin / gsz;
+  const int m0 = mt * BM, n0 = nt * BN;
   const int wm0 = (wave >> 1) * 64, wn0 = (wave & 1) * 64;
+  const bool do_colsum = AT && g.colsum != nullptr && nt == 0;  // uniform per workgroup
+  float csum = 0.f;
 
-  const int kbeg = blockIdx.z * g.k_split;
+  const int kbeg = z * g.k_split;
   const int kend = min(g.K, kbeg + g.k_split);
-  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int klen = kend > kbeg ? kend - kbeg : 0;
+  const int ntiles = (klen + BK - 1) / BK;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -168,9 +185,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
 
   SlabLoader<AT> la;
   SlabLoader<BT> lb;
+  auto load_slab = [&](int kt) {
+    const int k0 = kbeg + kt * BK;
+    la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
+    lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+  };
   if (ntiles > 0) {
-    la.load(g.A, g.lda, m0, g.M, kbeg, kend, tid);
-    lb.load(g.B, g.ldb, n0, g.N, kbeg, kend, tid);
+    load_slab(0);
     la.template store<LDSA>(As[0], tid);
     lb.template store<LDSB>(Bs[0], tid);
   }
@@ -179,20 +200,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
   for (int kt = 0; kt < ntiles; kt++) {
     const int cur = kt & 1;
     const bool more = kt + 1 < ntiles;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
-      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
-    }
+    if (more) load_slab(kt + 1);
+    // all of this slab's fragments first, then its 64 MFMAs
+    f32x2 af[BK / 2], bf[BK / 2];
 #pragma unroll
     for (int kk2 = 0; kk2 < BK / 2; kk2++) {
       const int kk = 2 * kk2 + h;
-      f32x2 a = *reinterpret_cast<const f32x2*>(&As[cur][kk][wm0 + 2 * r]);
-      f32x2 b = *reinterpret_cast<const f32x2*>(&Bs[cur][kk][wn0 + 2 * r]);
-      acc[0][0] = mfma32x32x2(a[0], b[0], acc[0][0]);
-      acc[0][1] = mfma32x32x2(a[0], b[1], acc[0][1]);
-      acc[1][0] = mfma32x32x2(a[1], b[0], acc[1][0]);
-      acc[1][1] = mfma32x32x2(a[1], b[1], acc[1][1]);
+      af[kk2] = *reinterpret_cast<const f32x2*>(&As[cur][kk][wm0 + 2 * r]);
+      bf[kk2] = *reinterpret_cast<const f32x2*>(&Bs[cur][kk][wn0 + 2 * r]);
+    }
+#pragma unroll
+    for (int kk2 = 0; kk2 < BK / 2; kk2++) {
+      acc[0][0] = mfma32x32x2(af[kk2][0], bf[kk2][0], acc[0][0]);
+      acc[0][1] = mfma32x32x2(af[kk2][0], bf[kk2][1], acc[0][1]);
+      acc[1][0] = mfma32x32x2(af[kk2][1], bf[kk2][0], acc[1][0]);
+      acc[1][1] = mfma32x32x2(af[kk2][1], bf[kk2][1], acc[1][1]);
+    }
+    if (do_colsum) {  // column c of the A tile: rows 16*half .. 16*half+15 of this slab
+      const int c = tid & (BM - 1), half = tid >> 7;
+#pragma unroll
+      for (int kk = 0; kk < BK / 2; kk++) csum += As[cur][half * (BK / 2) + kk][c];
     }
     if (more) {
       la.template store<LDSA>(As[cur ^ 1], tid);
@@ -201,7 +228,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
     __syncthreads();
   }
 
-  float* C = g.C + (long long)blockIdx.z * g.c_zstride;
+  if (do_colsum) {
+    float* red = &As[0][0][0];
+    if (tid >= BM) red[tid - BM] = csum;
+    __syncthreads();
+    if (tid < BM && m0 + tid < g.M) {
+      const float total = csum + red[tid];
+      if (g.colsum_zstride) g.colsum[(long long)z * g.colsum_zstride + m0 + tid] = total;
+      else g.colsum[m0 + tid] += total;
+    }
+  }
+
+  float* C = g.C + (long long)z * g.c_zstride;
 #pragma unroll
   for (int bm = 0; bm < 2; bm++)
 #pragma unroll
@@ -280,8 +318,21 @@ int split_ld(int N) { return (N + 1) & ~1; }
 size_t gemm_workspace_floats(const Gemm& g) {
   if (g.epi == EPI_GELU || g.epi == EPI_RESID) return 0;
   int s = choose_splits(g);
-  return s > 1 ? (size_t)s * g.M * split_ld(g.N) : 0;
+  if (s <= 1) return 0;
+  return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
 }
+
+namespace {
+// colsum[m] += sum over splits of the per-split column sums (split order)
+__global__ void colsum_split_reduce_kernel(float* __restrict__ colsum,
+                                           const float* __restrict__ part, int splits, int M) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; z++) s += part[(long long)z * M + m];
+  colsum[m] += s;
+}
+}  // namespace
 
 int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0) {
@@ -297,7 +348,8 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
                      g.lda, g.ldb, g.ldc);
     return -1;
   }
-  if ((g.epi == EPI_GELU && !g.C2) || ((g.epi == EPI_RESID || g.epi == EPI_GELU_BWD) && !g.R)) {
+  if ((g.epi == EPI_GELU && !g.C2) || ((g.epi == EPI_RESID || g.epi == EPI_GELU_BWD) && !g.R) ||
+      (g.colsum && !g.a_trans)) {
     set_global_error("gemm: epilogue %d is missing an operand", (int)g.epi);
     return -1;
   }
@@ -308,6 +360,7 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   a.C2 = g.C2;
   a.R = g.R;
   a.bias = g.bias;
+  a.colsum = g.colsum;
   a.lda = g.lda;
   a.ldb = g.ldb;
   a.ldc = g.ldc;
@@ -315,13 +368,16 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   a.N = g.N;
   a.K = g.K;
   a.c_zstride = 0;
+  a.colsum_zstride = 0;
 
   int splits = (g.epi == EPI_GELU || g.epi == EPI_RESID) ? 1 : choose_splits(g);
-  if (splits > 1 && (!workspace || ws_floats < (size_t)splits * g.M * split_ld(g.N))) splits = 1;
+  if (splits > 1 && (!workspace || ws_floats < gemm_workspace_floats(g))) splits = 1;
   const int kt = ceil_div(g.K, BK);
   const int kt_per = ceil_div(kt, splits);
   splits = ceil_div(kt, kt_per);
   a.k_split = kt_per * BK;
+  a.splits = splits;
+  const int tiles = ceil_div(g.M, BM) * ceil_div(g.N, BN);
 
   const double MN = (double)g.M * g.N;
   const double flop = 2.0 * MN * g.K;
@@ -330,32 +386,48 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   const double out_factor = g.epi == EPI_STORE ? 1.0 : 2.0;
   char name[64];
   if (splits == 1) {
-    dim3 grid(ceil_div(g.N, BN), ceil_div(g.M, BM), 1);
     snprintf(name, sizeof(name), "gemm_kernel<%d,%d,%d>", (int)g.a_trans, (int)g.b_trans,
              (int)g.epi);
+    if (profiling_detail())
+      snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d", g.M, g.N, g.K);
     ProfScope ps(name, flop, in_bytes + 4.0 * MN * out_factor, stream);
-    launch(a, g.a_trans, g.b_trans, g.epi, grid, stream);
+    launch(a, g.a_trans, g.b_trans, g.epi, dim3(tiles), stream);
   } else {
     Args p = a;
     p.C = workspace;
     p.ldc = split_ld(g.N);
     p.c_zstride = (long long)g.M * p.ldc;
     p.bias = nullptr;
-    dim3 grid(ceil_div(g.N, BN), ceil_div(g.M, BM), splits);
+    float* colsum_part = workspace + (size_t)splits * g.M * p.ldc;
+    if (g.colsum) {
+      p.colsum = colsum_part;
+      p.colsum_zstride = g.M;
+    }
     snprintf(name, sizeof(name), "gemm_kernel<%d,%d,0>", (int)g.a_trans, (int)g.b_trans);
+    if (profiling_detail())
+      snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d/%d", g.M, g.N, g.K,
+               splits);
     {
       ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
-      launch(p, g.a_trans, g.b_trans, EPI_STORE, grid, stream);
+      launch(p, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
     }
     const long long total = (long long)g.M * g.N;
     int blocks = (int)((total + 255) / 256);
     if (blocks > 4096) blocks = 4096;
     snprintf(name, sizeof(name), "split_reduce_kernel<%d>", (int)g.epi);
-    ProfScope ps(name, 0.0, 4.0 * MN * (splits + out_factor), stream);
-    switch (g.epi) {
-      case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-      case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-      default: split_reduce_kernel<EPI_STORE><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+    {
+      ProfScope ps(name, 0.0, 4.0 * MN * (splits + out_factor), stream);
+      switch (g.epi) {
+        case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+        case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+        default: split_reduce_kernel<EPI_STORE><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+      }
+    }
+    if (g.colsum) {
+      ProfScope ps("colsum_split_reduce_kernel", (double)splits * g.M,
+                   4.0 * ((double)splits * g.M + 2.0 * g.M), stream);
+      colsum_split_reduce_kernel<<<ceil_div(g.M, 256), 256, 0, stream>>>(g.colsum, colsum_part,
+                                                                        splits, g.M);
     }
   }
   GPT2_HIP_OK(hipGetLastError());

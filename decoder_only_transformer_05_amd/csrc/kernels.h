@@ -11,6 +11,7 @@ namespace gpt2 {
 // bracketed by two HIP events on its stream and tagged with the kernel's name and the
 // algorithmic flops and HBM bytes of that launch. Not thread-safe (one caller at a time).
 bool profiling_on();
+bool profiling_detail();  // names also carry the problem shape (gpt2_profile_enable(2))
 struct ProfScope {
   ProfScope(const char* name, double flop, double bytes, hipStream_t s);
   ~ProfScope();
@@ -40,6 +41,10 @@ struct Gemm {
   float* C2 = nullptr;        // EPI_GELU
   const float* R = nullptr;   // EPI_RESID (residual) / EPI_GELU_BWD (pre-activation), ldc
   const float* bias = nullptr;
+  // optional, only with a_trans: colsum[m] += sum over k of A(m, k), i.e. the column sums
+  // of the stored (K, M) operand -- the bias gradient of a weight-gradient GEMM, computed
+  // from the A tiles already staged in LDS
+  float* colsum = nullptr;
   int M = 0, N = 0, K = 0;
   Epilogue epi = EPI_STORE;
 };

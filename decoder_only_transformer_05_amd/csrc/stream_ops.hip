@@ -269,15 +269,29 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   }
 }
 
-__global__ void layernorm_bwd_final_kernel(float* __restrict__ dw, float* __restrict__ db,
-                                           const float* __restrict__ partial, int blocks, int C) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= 2 * C) return;
-  const int which = c / C, cc = c % C;
+// dw[c] += sum_k partial[k][0][c], db[c] += sum_k partial[k][1][c]. A workgroup owns 32 of
+// the 2C columns; its 8 thread groups each sum every 8th partial (in order), and the 8
+// group sums are then added in group order.
+__global__ __launch_bounds__(256) void layernorm_bwd_final_kernel(float* __restrict__ dw,
+                                                                  float* __restrict__ db,
+                                                                  const float* __restrict__ partial,
+                                                                  int blocks, int C) {
+  __shared__ float red[8][32];
+  const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
+  const int which = c / C, cc = c - which * C;
   float s = 0.f;
-  for (int k = 0; k < blocks; k++) s += partial[((long long)k * 2 + which) * C + cc];
-  if (which == 0) dw[cc] += s;
-  else db[cc] += s;
+  if (c < 2 * C)
+    for (int k = grp; k < blocks; k += 8) s += partial[((long long)k * 2 + which) * C + cc];
+  red[grp][cl] = s;
+  __syncthreads();
+  if (grp == 0 && c < 2 * C) {
+    float t = red[0][cl];
+#pragma unroll
+    for (int k = 1; k < 8; k++) t += red[k][cl];
+    if (which == 0) dw[cc] += t;
+    else db[cc] += t;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -514,7 +528,7 @@ int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const
   }
   ProfScope ps("layernorm_bwd_final_kernel", 2.0 * blocks * C, 4.0 * (2.0 * blocks * C + 4.0 * C),
                stream);
-  layernorm_bwd_final_kernel<<<(2 * C + 255) / 256, 256, 0, stream>>>(dw, db, partial, blocks, C);
+  layernorm_bwd_final_kernel<<<(2 * C + 31) / 32, 256, 0, stream>>>(dw, db, partial, blocks, C);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }

@@ -134,7 +134,8 @@ int gpt2_adamw_step(gpt2_model* model, float lr, float beta1, float beta2, float
 
 /* Launch profiler. gpt2_profile_enable(1) clears the record and from then on brackets every
  * kernel launch of the library with two HIP events on the launch's stream, tagged with the
- * kernel's name and that launch's algorithmic flops and HBM bytes; (0) stops recording.
+ * kernel's name and that launch's algorithmic flops and HBM bytes; (2) does the same with
+ * the problem shape appended to GEMM names; (0) stops recording.
  * gpt2_profile_summary waits for the recorded events and writes one line per kernel name,
  * "name<TAB>launches<TAB>total_ms<TAB>total_flop<TAB>total_bytes", into buf (ERR_ARG if
  * len is too small). Process-wide state; not thread-safe. */
