@@ -295,17 +295,33 @@ void launch(const Args& a, bool at, bool bt, int epi, dim3 grid, hipStream_t s) 
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Number of K splits for a problem: enough workgroups to give every CU about two, and each
-// split at least 4 K-slabs deep.
+// Number of K splits for a problem, from a small cost model in units of one K-slab of one
+// workgroup: two 256-thread workgroups fit on each of the 256 CUs; a CU running one
+// workgroup instead of two finishes it about twice as fast, so the work of a launch costs
+// (slabs per split) x ceil(workgroups / 256) / 2; a split adds the partial results'
+// round trip through HBM (written once, read once) at ~4 TB/s against ~5 us per slab.
 int choose_splits(const Gemm& g) {
   const long long tiles = (long long)ceil_div(g.M, BM) * ceil_div(g.N, BN);
-  const long long target = 2 * 256;
-  if (tiles >= target) return 1;
-  int s = (int)((target + tiles - 1) / tiles);
-  const int max_by_k = g.K / (4 * BK);
-  if (s > max_by_k) s = max_by_k;
-  if (s > 16) s = 16;
-  return s < 1 ? 1 : s;
+  const int kt = ceil_div(g.K, BK);
+  double best = 1e30;
+  int best_s = 1;
+  for (int s = 1; s <= 32; s++) {
+    const int kper = ceil_div(kt, s);
+    if (s > 1 && kper < 4) break;
+    const int s_eff = ceil_div(kt, kper);
+    if (s > 1 && s_eff != s) continue;
+    const double halves = (double)ceil_div(tiles * s, 256);
+    double cost = kper * halves / 2.0;
+    if (s > 1) {
+      const double bytes = 4.0 * (2.0 * s * g.M * (double)g.N + 2.0 * g.M * (double)g.N);
+      cost += bytes / 4e12 / 5e-6;
+    }
+    if (cost < best * 0.9) {  // prefer fewer splits unless clearly cheaper
+      best = cost;
+      best_s = s;
+    }
+  }
+  return best_s;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
