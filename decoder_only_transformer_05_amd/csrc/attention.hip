@@ -187,22 +187,48 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
 // ---------------------------------------------------------------------------------------
 // backward: D = rowsum(dO * O) per (b, head, query)
 // ---------------------------------------------------------------------------------------
-__global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const float* __restrict__ dout,
-                                       const float* __restrict__ out, int B, int T, int C,
-                                       int NH, int hs) {
+// Head sizes that are not 4 times a power of two: one thread per (b, q, head) segment.
+__global__ void attn_bwd_rowdot_generic_kernel(float* __restrict__ D,
+                                               const float* __restrict__ dout,
+                                               const float* __restrict__ out, int B, int T,
+                                               int C, int NH, int hs) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)B * NH * T) return;
-  const int q = (int)(idx % T);
-  const int head = (int)((idx / T) % NH);
-  const int b = (int)(idx / ((long long)T * NH));
-  const long long off = ((long long)b * T + q) * C + (long long)head * hs;
+  const int head = (int)(idx % NH);
+  const long long bq = idx / NH;
+  const int q = (int)(bq % T), b = (int)(bq / T);
+  const long long off = bq * C + (long long)head * hs;
   float s = 0.f;
   for (int d = 0; d < hs; d += 4) {
     f32x4 a = *reinterpret_cast<const f32x4*>(dout + off + d);
     f32x4 o = *reinterpret_cast<const f32x4*>(out + off + d);
     s += a[0] * o[0] + a[1] * o[1] + a[2] * o[2] + a[3] * o[3];
   }
-  D[idx] = s;
+  D[((long long)b * NH + head) * T + q] = s;
+}
+
+// One float4 per thread, threads of a (b, q, head) segment adjacent: loads are contiguous
+// across the wave, and the HS4 = hs/4 partial sums of a segment are combined with shuffles
+// (HS4 a power of two up to 32). D is (B, NH, T).
+template <int HS4>
+__global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const float* __restrict__ dout,
+                                       const float* __restrict__ out, int B, int T, int C,
+                                       int NH) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long n4 = (long long)B * T * (C / 4);
+  const bool ok = idx < n4;
+  const long long i4 = ok ? idx : 0;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(dout + 4 * i4);
+  const f32x4 o = *reinterpret_cast<const f32x4*>(out + 4 * i4);
+  float s = (a[0] * o[0] + a[1] * o[1]) + (a[2] * o[2] + a[3] * o[3]);
+#pragma unroll
+  for (int w = HS4 / 2; w > 0; w >>= 1) s += __shfl_xor(s, w, 64);
+  if (ok && (threadIdx.x % HS4) == 0) {
+    const long long bq = i4 / (C / 4);
+    const int head = (int)((i4 % (C / 4)) / HS4);
+    const int q = (int)(bq % T), b = (int)(bq / T);
+    D[((long long)b * NH + head) * T + q] = s;
+  }
 }
 
 // dK, dV for a tile of 64 keys (32 per wave), looping over query tiles from the diagonal.
@@ -469,8 +495,19 @@ int attention_backward(float* dqkv, const float* dout, const float* qkv, const f
   const double BTC = (double)B * T * C, tri = (double)T * (T + 1) / 2.0;
   {
     ProfScope ps("attn_bwd_rowdot_kernel", 2.0 * BTC, 4.0 * (2.0 * BTC + rows), stream);
-    attn_bwd_rowdot_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
-        dscratch, dout, out, B, T, C, NH, hs);
+    const long long n4 = (long long)B * T * (C / 4);
+    const unsigned blocks = (unsigned)((n4 + 255) / 256);
+    switch (hs / 4) {
+      case 1: attn_bwd_rowdot_kernel<1><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 2: attn_bwd_rowdot_kernel<2><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 4: attn_bwd_rowdot_kernel<4><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 8: attn_bwd_rowdot_kernel<8><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 16: attn_bwd_rowdot_kernel<16><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 32: attn_bwd_rowdot_kernel<32><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      default:
+        attn_bwd_rowdot_generic_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+            dscratch, dout, out, B, T, C, NH, hs);
+    }
   }
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)

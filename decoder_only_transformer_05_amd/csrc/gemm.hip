@@ -15,7 +15,9 @@
 // LDS holds both operands K-major ([k][m] and [k][n], row stride 130 floats): a lane's two
 // MFMA blocks along M take adjacent rows m = 2r and 2r+1, so one 8-byte LDS read feeds two
 // MFMAs, and the results are un-interleaved in the epilogue.
+#include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -23,7 +25,10 @@
 namespace gpt2 {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
+#ifndef GPT2_GEMM_BK
+#define GPT2_GEMM_BK 16
+#endif
+constexpr int BM = 128, BN = 128, BK = GPT2_GEMM_BK;
 constexpr int LDSA = BM + 2, LDSB = BN + 2;
 constexpr int NTHREADS = 256;
 
@@ -56,7 +61,12 @@ constexpr int GROUP_M = 8;  // m-tiles that sweep the n-tiles together (L2 reuse
 // is replaced by zero when the slab is written to LDS.
 template <bool TRANS>
 struct SlabLoader {
-  f32x4 v[4];
+  // float4 loads per thread per slab: 128 x BK floats / (256 threads x 4)
+  static constexpr int NV = BM * BK / (4 * NTHREADS);
+  static constexpr int F4_PER_ROW = BK / 4;              // !TRANS: float4s along K per row
+  static constexpr int ROWS_PER_PASS = NTHREADS / F4_PER_ROW;
+  static constexpr int K_PER_PASS = NTHREADS / (BM / 4);  // TRANS: K rows per pass (8)
+  f32x4 v[NV];
   int k0, kend;
 
   __device__ __forceinline__ void load(const float* __restrict__ P, int ld, int row0, int rows,
@@ -64,14 +74,14 @@ struct SlabLoader {
     k0 = k0_;
     kend = kend_;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < NV; i++) {
       if (!TRANS) {
-        const int r = min(row0 + tid / 8 + 32 * i, rows - 1);
-        const int k = min(k0 + 4 * (tid % 8), (kend - 1) & ~3);
+        const int r = min(row0 + tid / F4_PER_ROW + ROWS_PER_PASS * i, rows - 1);
+        const int k = min(k0 + 4 * (tid % F4_PER_ROW), (kend - 1) & ~3);
         v[i] = *reinterpret_cast<const f32x4*>(P + (long long)r * ld + k);
       } else {
-        const int k = min(k0 + tid / 32 + 8 * i, kend - 1);
-        const int r = min(row0 + 4 * (tid % 32), (rows - 1) & ~3);
+        const int k = min(k0 + tid / (BM / 4) + K_PER_PASS * i, kend - 1);
+        const int r = min(row0 + 4 * (tid % (BM / 4)), (rows - 1) & ~3);
         v[i] = *reinterpret_cast<const f32x4*>(P + (long long)k * ld + r);
       }
     }
@@ -80,16 +90,16 @@ struct SlabLoader {
   template <int LDS>
   __device__ __forceinline__ void store(float (*S)[LDS], int tid) const {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < NV; i++) {
       if (!TRANS) {
-        const int r = tid / 8 + 32 * i;
-        const int k = 4 * (tid % 8);
+        const int r = tid / F4_PER_ROW + ROWS_PER_PASS * i;
+        const int k = 4 * (tid % F4_PER_ROW);
         const int kg = k0 + k;  // global K index of element 0
 #pragma unroll
         for (int j = 0; j < 4; j++) S[k + j][r] = kg + j < kend ? v[i][j] : 0.f;
       } else {
-        const int k = tid / 32 + 8 * i;
-        const int r = 4 * (tid % 32);
+        const int k = tid / (BM / 4) + K_PER_PASS * i;
+        const int r = 4 * (tid % (BM / 4));
         const bool ok = k0 + k < kend;
         *reinterpret_cast<f32x2*>(&S[k][r]) = ok ? f32x2{v[i][0], v[i][1]} : f32x2{0.f, 0.f};
         *reinterpret_cast<f32x2*>(&S[k][r + 2]) = ok ? f32x2{v[i][2], v[i][3]} : f32x2{0.f, 0.f};
@@ -255,22 +265,52 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
 // (only EPI_STORE-with-bias, EPI_ACCUM and EPI_GELU_BWD are used with splits), adding the
 // partials in split order.
 template <int EPI>
+__device__ __forceinline__ float split_epilogue(const Args& g, long long off, int n, float s) {
+  if (EPI == EPI_ACCUM) return g.C[off] + s;
+  if (EPI == EPI_GELU_BWD) return s * gelu_bwd(g.R[off]);
+  s += g.bias ? g.bias[n] : 0.f;
+  if (EPI == EPI_RESID) s += g.R[off];
+  return s;
+}
+
+// Sums `splits` partial results (each M x N, row stride wld) into C with the epilogue `EPI`,
+// adding the partials in split order; four consecutive columns per thread, with all of a
+// group's partial loads issued before the adds.
+template <int EPI>
 __global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int splits, int wld) {
-  const long long total = (long long)g.M * g.N;
+  const int N4 = (g.N + 3) / 4;
+  const long long total = (long long)g.M * N4;
   const long long zstride = (long long)g.M * wld;
   for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (long long)gridDim.x * blockDim.x) {
-    const int m = (int)(idx / g.N), n = (int)(idx % g.N);
-    const long long widx = (long long)m * wld + n;
-    float s = 0.f;
-    for (int z = 0; z < splits; z++) s += ws[(long long)z * zstride + widx];
-    const long long off = (long long)m * g.ldc + n;
-    if (EPI == EPI_ACCUM) {
-      g.C[off] += s;
-    } else if (EPI == EPI_GELU_BWD) {
-      g.C[off] = s * gelu_bwd(g.R[off]);
+    const int m = (int)(idx / N4), n = 4 * (int)(idx % N4);
+    const float* src = ws + (long long)m * wld + n;
+    const bool full = n + 3 < g.N;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    int z = 0;
+    if (full) {
+      for (; z + 4 <= splits; z += 4) {
+        f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (long long)(z + 0) * zstride);
+        f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (long long)(z + 1) * zstride);
+        f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (long long)(z + 2) * zstride);
+        f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (long long)(z + 3) * zstride);
+        s += p0;
+        s += p1;
+        s += p2;
+        s += p3;
+      }
+      for (; z < splits; z++) s += *reinterpret_cast<const f32x4*>(src + (long long)z * zstride);
     } else {
-      g.C[off] = s + (g.bias ? g.bias[n] : 0.f);
+      for (; z < splits; z++)
+        for (int j = 0; j < 4 && n + j < g.N; j++) s[j] += src[(long long)z * zstride + j];
+    }
+    const long long off = (long long)m * g.ldc + n;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (n + j >= g.N) break;
+      const float v = split_epilogue<EPI>(g, off + j, n + j, s[j]);
+      g.C[off + j] = v;
+      if (EPI == EPI_GELU) g.C2[off + j] = gelu_fwd(v);
     }
   }
 }
@@ -295,28 +335,32 @@ void launch(const Args& a, bool at, bool bt, int epi, dim3 grid, hipStream_t s) 
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Number of K splits for a problem, from a small cost model in units of one K-slab of one
-// workgroup: two 256-thread workgroups fit on each of the 256 CUs; a CU running one
-// workgroup instead of two finishes it about twice as fast, so the work of a launch costs
-// (slabs per split) x ceil(workgroups / 256) / 2; a split adds the partial results'
-// round trip through HBM (written once, read once) at ~4 TB/s against ~5 us per slab.
+// Number of K splits for a problem, from a cost model fitted to measurements on MI355X.
+// Four 256-thread workgroups fit on each of the 256 CUs (1024 slots). A launch of n
+// workgroups runs ceil(n/1024) rounds of the same length, so relative to perfectly packed
+// work it costs q = ceil(n/1024) / (n/1024); splitting K multiplies n by the split count and
+// adds a pass that reads the partials and applies the epilogue (the partials themselves are
+// written while the GEMM computes).
+// Compute time is estimated at 90% of the fp32 MFMA peak, memory at 5 TB/s.
 int choose_splits(const Gemm& g) {
-  const long long tiles = (long long)ceil_div(g.M, BM) * ceil_div(g.N, BN);
+#ifdef GPT2_SPLIT_OVERRIDE
+  if (const char* e = getenv("GPT2_SPLITS")) return atoi(e);
+#endif
+  const double tiles = (double)ceil_div(g.M, BM) * ceil_div(g.N, BN);
   const int kt = ceil_div(g.K, BK);
+  const double mn = (double)g.M * g.N;
+  const double t_mfma = 2.0 * mn * g.K / (0.9 * 157.3e12);
   double best = 1e30;
   int best_s = 1;
   for (int s = 1; s <= 32; s++) {
     const int kper = ceil_div(kt, s);
     if (s > 1 && kper < 4) break;
-    const int s_eff = ceil_div(kt, kper);
-    if (s > 1 && s_eff != s) continue;
-    const double halves = (double)ceil_div(tiles * s, 256);
-    double cost = kper * halves / 2.0;
-    if (s > 1) {
-      const double bytes = 4.0 * (2.0 * s * g.M * (double)g.N + 2.0 * g.M * (double)g.N);
-      cost += bytes / 4e12 / 5e-6;
-    }
-    if (cost < best * 0.9) {  // prefer fewer splits unless clearly cheaper
+    if (s > 1 && ceil_div(kt, kper) != s) continue;
+    const double rounds = tiles * s / 1024.0;
+    const double q = std::ceil(rounds) / rounds;
+    double cost = t_mfma * q;
+    if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;  // partials are written during the GEMM
+    if (cost < best * 0.95) {  // prefer fewer splits unless clearly cheaper
       best = cost;
       best_s = s;
     }
@@ -328,11 +372,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-// partial results of a split GEMM are stored with an even row stride (8-byte stores)
-int split_ld(int N) { return (N + 1) & ~1; }
+// partial results of a split GEMM are stored with a row stride that is a multiple of 4
+// (16-byte loads in the reduction)
+int split_ld(int N) { return (N + 3) & ~3; }
 
 size_t gemm_workspace_floats(const Gemm& g) {
-  if (g.epi == EPI_GELU || g.epi == EPI_RESID) return 0;
   int s = choose_splits(g);
   if (s <= 1) return 0;
   return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
@@ -386,7 +430,7 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   a.c_zstride = 0;
   a.colsum_zstride = 0;
 
-  int splits = (g.epi == EPI_GELU || g.epi == EPI_RESID) ? 1 : choose_splits(g);
+  int splits = choose_splits(g);
   if (splits > 1 && (!workspace || ws_floats < gemm_workspace_floats(g))) splits = 1;
   const int kt = ceil_div(g.K, BK);
   const int kt_per = ceil_div(kt, splits);
@@ -427,15 +471,17 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
       ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
       launch(p, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
     }
-    const long long total = (long long)g.M * g.N;
+    const long long total = (long long)g.M * ((g.N + 3) / 4);
     int blocks = (int)((total + 255) / 256);
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 8192) blocks = 8192;
     snprintf(name, sizeof(name), "split_reduce_kernel<%d>", (int)g.epi);
     {
       ProfScope ps(name, 0.0, 4.0 * MN * (splits + out_factor), stream);
       switch (g.epi) {
         case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
         case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+        case EPI_GELU: split_reduce_kernel<EPI_GELU><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+        case EPI_RESID: split_reduce_kernel<EPI_RESID><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
         default: split_reduce_kernel<EPI_STORE><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
       }
     }

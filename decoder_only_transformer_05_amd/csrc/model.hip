@@ -198,6 +198,16 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
       d.epi = EPI_STORE;
       ws = std::max(ws, gemm_workspace_floats(d));
     }
+    // forward: qkv, attproj, fc, fcproj, lm_head (out = M x N with K = in)
+    const int fn[5] = {3 * iC, iC, 4 * iC, iC, iV};
+    const int fk[5] = {iC, iC, iC, 4 * iC, iC};
+    for (int k = 0; k < 5; k++) {
+      Gemm f;
+      f.M = iBT;
+      f.N = fn[k];
+      f.K = fk[k];
+      ws = std::max(ws, gemm_workspace_floats(f));
+    }
     Gemm d;
     d.M = iBT;
     d.N = iC;
@@ -521,7 +531,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     g.M = BT;
     g.N = 3 * C;
     g.K = C;
-    CHK(gemm(g, nullptr, 0, s));
+    CHK(gemm(g, md->gemm_ws, md->gemm_ws_floats, s));
     CHK(attention_forward(atty, md->attn_lse + (size_t)l * NH * BT, qkv, B, T, C, NH, s));
     Gemm pj;
     pj.A = atty;
@@ -536,7 +546,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     pj.N = C;
     pj.K = C;
     pj.epi = EPI_RESID;
-    CHK(gemm(pj, nullptr, 0, s));
+    CHK(gemm(pj, md->gemm_ws, md->gemm_ws_floats, s));
     CHK(layernorm_forward(ln2, md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, res2,
                           P(md, P_LN2W) + l * C, P(md, P_LN2B) + l * C, BT, C, s));
     Gemm fc;
@@ -552,7 +562,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     fc.N = 4 * C;
     fc.K = C;
     fc.epi = EPI_GELU;
-    CHK(gemm(fc, nullptr, 0, s));
+    CHK(gemm(fc, md->gemm_ws, md->gemm_ws_floats, s));
     Gemm fp;
     fp.A = fchg;
     fp.lda = 4 * C;
@@ -566,7 +576,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     fp.N = C;
     fp.K = 4 * C;
     fp.epi = EPI_RESID;
-    CHK(gemm(fp, nullptr, 0, s));
+    CHK(gemm(fp, md->gemm_ws, md->gemm_ws_floats, s));
   }
   CHK(layernorm_forward(md->lnf, md->lnf_mean, md->lnf_rstd, md->res3 + (L - 1) * NC,
                         P(md, P_LNFW), P(md, P_LNFB), BT, C, s));
@@ -581,7 +591,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   lm.M = BT;
   lm.N = V;
   lm.K = C;
-  CHK(gemm(lm, nullptr, 0, s));
+  CHK(gemm(lm, md->gemm_ws, md->gemm_ws_floats, s));
   md->logits_valid = true;
 
   if (targets) {

@@ -281,8 +281,20 @@ __global__ __launch_bounds__(256) void layernorm_bwd_final_kernel(float* __restr
   const int c = blockIdx.x * 32 + cl;
   const int which = c / C, cc = c - which * C;
   float s = 0.f;
-  if (c < 2 * C)
-    for (int k = grp; k < blocks; k += 8) s += partial[((long long)k * 2 + which) * C + cc];
+  if (c < 2 * C) {
+    const float* p = partial + (long long)which * C + cc;
+    const long long st = 2LL * C;  // between consecutive partials
+    int k = grp;
+    for (; k + 24 < blocks; k += 32) {  // four independent loads in flight, added in order
+      const float a0 = p[(long long)k * st], a1 = p[(long long)(k + 8) * st];
+      const float a2 = p[(long long)(k + 16) * st], a3 = p[(long long)(k + 24) * st];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; k < blocks; k += 8) s += p[(long long)k * st];
+  }
   red[grp][cl] = s;
   __syncthreads();
   if (grp == 0 && c < 2 * C) {

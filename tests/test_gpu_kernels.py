@@ -120,7 +120,7 @@ def test_layernorm_forward_backward(N, C):
 
 
 @pytest.mark.parametrize("B,T,C,NH", [(2, 100, 128, 2), (4, 16, 16, 4), (1, 200, 96, 3),
-                                      (1, 130, 512, 4), (2, 64, 768, 12), (1, 1, 64, 1),
+                                      (1, 130, 512, 4), (2, 64, 768, 12), (1, 1, 64, 1), (2, 40, 48, 4),
                                       (3, 257, 64, 1)])
 def test_attention_forward_backward(B, T, C, NH):
     r = rng(B * T + C + NH)
