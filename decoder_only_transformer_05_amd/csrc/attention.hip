@@ -10,8 +10,10 @@
 // are never stored. The forward keeps a running max and sum per query row over 64-key
 // tiles (online softmax) and saves only the row log-sum-exp; the backward recomputes P
 // from Q, K and that log-sum-exp, and uses rowsum(P*dP) = rowsum(dO*O) (precomputed per
-// row). dK/dV and dQ come from two kernels that each own their outputs, so nothing is
-// accumulated with atomics and results are deterministic.
+// row). dK/dV come from one kernel per key tile, which also writes dS of each causal
+// 64x64 tile to a scratch buffer; dQ = dS K is then a second kernel per query tile. Each
+// kernel owns its outputs, so nothing is accumulated with atomics and results are
+// deterministic.
 //
 // MFMA layout trick: S is computed transposed (keys down the rows, one query per lane
 // column), so the softmax statistics of a query live in a single lane (plus its partner
@@ -231,12 +233,19 @@ __global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const float* __res
   }
 }
 
+// Causal 64x64 tiles (qt, kt), kt <= qt, of one (b, head), stored row after row:
+// tile (qt, kt) is number qt(qt+1)/2 + kt.
+GPT2_DEVICE_INLINE long long tri_index(int qt, int kt) { return (long long)qt * (qt + 1) / 2 + kt; }
+GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 2; }
+
 // dK, dV for a tile of 64 keys (32 per wave), looping over query tiles from the diagonal.
+// It also writes dS = P * (dP - D) of every causal tile it visits to `dsbuf`, from which
+// attn_bwd_dq_kernel forms dQ = dS K without recomputing P and dP.
 template <int HSP>
 __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Drow, int T, int C, int NH,
-    int hs, float scale, float scale_log2) {
+    float* __restrict__ dqkv, float* __restrict__ dsbuf, const float* __restrict__ dout,
+    const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Drow,
+    int T, int C, int NH, int hs, float scale, float scale_log2) {
   constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
   __shared__ float Qs[TILE][LD];
   __shared__ float dOs[TILE][LD];
@@ -289,10 +298,20 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
       Ds[tid] = t < T ? drow[t] : 0.f;
     }
     __syncthreads();
+    // dS tile (qt, kt) of this (b, head): 64 x 64 floats, [query][key]
+    float* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
+                             (TILE * TILE);
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
-      // skip sub-blocks that lie entirely above the diagonal for this wave's keys
-      if (q0 + 32 * qb + 31 < kt * TILE + wave * 32) continue;
+      // sub-blocks entirely above the diagonal for this wave's keys: dS is zero
+      if (q0 + 32 * qb + 31 < kt * TILE + wave * 32) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
+          dst[ql * TILE + wave * 32 + r] = 0.f;
+        }
+        continue;
+      }
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
@@ -318,6 +337,7 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
         const float p = ok ? exp2f(s[i] * scale_log2 - Ls[ql]) : 0.f;
         s[i] = p;
         dp[i] = p * (dp[i] - Ds[ql]);
+        dst[ql * TILE + wave * 32 + r] = dp[i];  // 32 lanes store 32 consecutive keys
       }
 #pragma unroll
       for (int db = 0; db < ND; db++)
@@ -349,15 +369,16 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
   }
 }
 
-// dQ for a tile of 64 queries (32 per wave), looping over key tiles up to the diagonal.
+// dQ = scale * dS K for a tile of 64 queries (32 per wave), over key tiles 0 .. qt, reading
+// the dS tiles written by attn_bwd_dkdv_kernel. M = queries, N = head dim, K = keys.
 template <int HSP>
-__global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Drow, int T, int C, int NH,
-    int hs, float scale, float scale_log2) {
-  constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
+__global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(float* __restrict__ dqkv,
+                                                           const float* __restrict__ qkv,
+                                                           const float* __restrict__ dsbuf, int T,
+                                                           int C, int NH, int hs, float scale) {
+  constexpr int LD = HSP + 4, ND = HSP / 32, LDSS = TILE + 4;
   __shared__ float Ks[TILE][LD];
-  __shared__ float Vs[TILE][LD];
+  __shared__ float Ss[TILE][LDSS];
 
   const int nqt = (T + TILE - 1) / TILE;
   int qt, head, b;
@@ -366,84 +387,49 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
-  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
-  const float* dobase = dout + (long long)b * T * C + (long long)head * hs;
-  const int q = qt * TILE + wave * 32 + r;
-  const int qm = min(q, T - 1);
-  const float lq = lse[((long long)b * NH + head) * T + qm] * kLog2e;
-  const float Dq = Drow[((long long)b * NH + head) * T + qm];
+  const float* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
+  const float* src = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, 0)) *
+                                 (TILE * TILE);
 
-  float qf[NS], of[NS];
-#pragma unroll
-  for (int g = 0; g < HSP / 8; g++) {
-    const int d = 8 * g + 4 * hf;
-    f32x4 qv = load4_rowcol(base, C3, qm, d, T, hs);
-    f32x4 ov = load4_rowcol(dobase, C, qm, d, T, hs);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      qf[4 * g + j] = qv[j];
-      of[4 * g + j] = ov[j];
-    }
-  }
-  f32x16 dqacc[ND];
+  f32x16 acc[ND];
 #pragma unroll
   for (int db = 0; db < ND; db++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) dqacc[db][i] = 0.f;
+    for (int i = 0; i < 16; i++) acc[db][i] = 0.f;
 
   for (int kt = 0; kt <= qt; kt++) {
-    const int key0 = kt * TILE;
     __syncthreads();
-    load_tile<HSP>(Ks, base + C, C3, key0, T, hs, tid);
-    load_tile<HSP>(Vs, base + 2 * C, C3, key0, T, hs, tid);
+    load_tile<HSP>(Ks, kbase, C3, kt * TILE, T, hs, tid);
+    const float* ts = src + (long long)kt * TILE * TILE;
+#pragma unroll
+    for (int i = 0; i < TILE * TILE / 4 / NTHR; i++) {
+      const int f = tid + NTHR * i;
+      const int row = f / (TILE / 4), c4 = f % (TILE / 4);
+      *reinterpret_cast<f32x4*>(&Ss[row][4 * c4]) =
+          *reinterpret_cast<const f32x4*>(ts + row * TILE + 4 * c4);
+    }
     __syncthreads();
+    // 32 steps of two keys; at step s = 4g + j this half of the wave takes key 8g + 4hf + j
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      if (key0 + 32 * kb > qt * TILE + wave * 32 + 31) continue;  // all keys above diagonal
-      f32x16 s, dp;
+    for (int g = 0; g < TILE / 8; g++) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(&Ss[32 * wave + r][8 * g + 4 * hf]);
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
+      for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int g = 0; g < HSP / 8; g++) {
-        f32x4 kv = *reinterpret_cast<const f32x4*>(&Ks[32 * kb + r][8 * g + 4 * hf]);
-        f32x4 vv = *reinterpret_cast<const f32x4*>(&Vs[32 * kb + r][8 * g + 4 * hf]);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          s = mfma32x32x2(kv[j], qf[4 * g + j], s);
-          dp = mfma32x32x2(vv[j], of[4 * g + j], dp);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * hf + (i % 4);
-        const bool ok = key <= qm && key < T;
-        const float p = ok ? exp2f(s[i] * scale_log2 - lq) : 0.f;
-        dp[i] = p * (dp[i] - Dq);
-      }
-#pragma unroll
-      for (int db = 0; db < ND; db++)
-#pragma unroll
-        for (int st = 0; st < 16; st++) {
-          const int kl = 32 * kb + 8 * (st / 4) + 4 * hf + (st % 4);
-          dqacc[db] = mfma32x32x2(Ks[kl][32 * db + r], dp[st], dqacc[db]);
-        }
+        for (int db = 0; db < ND; db++)
+          acc[db] = mfma32x32x2(sv[j], Ks[8 * g + 4 * hf + j][32 * db + r], acc[db]);
     }
   }
-  if (q < T) {
-    float* dq = dqkv + ((long long)b * T + q) * C3 + (long long)head * hs;
+  // acc[db][i]: query 32*wave + 8(i/4) + 4hf + i%4 of the tile, head dim 32*db + r
 #pragma unroll
-    for (int db = 0; db < ND; db++)
+  for (int db = 0; db < ND; db++) {
+    const int d = 32 * db + r;
+    if (d >= hs) continue;
 #pragma unroll
-      for (int ig = 0; ig < 4; ig++) {
-        const int d = 32 * db + 8 * ig + 4 * hf;
-        if (d < hs)
-          *reinterpret_cast<f32x4*>(dq + d) =
-              f32x4{dqacc[db][4 * ig] * scale, dqacc[db][4 * ig + 1] * scale,
-                    dqacc[db][4 * ig + 2] * scale, dqacc[db][4 * ig + 3] * scale};
-      }
+    for (int i = 0; i < 16; i++) {
+      const int q = qt * TILE + 32 * wave + 8 * (i / 4) + 4 * hf + (i % 4);
+      if (q < T) dqkv[((long long)b * T + q) * C3 + (long long)head * hs + d] = acc[db][i] * scale;
+    }
   }
 }
 
@@ -480,9 +466,14 @@ int attention_forward(float* out, float* lse, const float* qkv, int B, int T, in
   return 0;
 }
 
+size_t attention_ds_scratch_floats(int B, int T, int NH) {
+  const long long nt = (T + TILE - 1) / TILE;
+  return (size_t)B * NH * (nt * (nt + 1) / 2) * TILE * TILE;
+}
+
 int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
-                       const float* lse, float* dscratch, int B, int T, int C, int NH,
-                       hipStream_t stream) {
+                       const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
+                       int NH, hipStream_t stream) {
   int hsp;
   if (!check_shape(B, T, C, NH, &hsp)) {
     set_global_error("attention: unsupported shape B=%d T=%d C=%d NH=%d", B, T, C, NH);
@@ -512,17 +503,17 @@ int attention_backward(float* dqkv, const float* dout, const float* qkv, const f
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
     ProfScope ps("attn_bwd_dkdv_kernel", 6.0 * B * NH * hs * tri,
-                 4.0 * (3.0 * BTC + BTC + 2.0 * rows + 2.0 * BTC), stream);
-    if (hsp == 32) attn_bwd_dkdv_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else if (hsp == 64) attn_bwd_dkdv_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else attn_bwd_dkdv_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+                 4.0 * (3.0 * BTC + BTC + 2.0 * rows + 2.0 * BTC + B * NH * tri), stream);
+    if (hsp == 32) attn_bwd_dkdv_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hsp == 64) attn_bwd_dkdv_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dkdv_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
   }
   {  // dQ = dS K
     ProfScope ps("attn_bwd_dq_kernel", 2.0 * B * NH * hs * tri,
-                 4.0 * (3.0 * BTC + BTC + 2.0 * rows + BTC), stream);
-    if (hsp == 32) attn_bwd_dq_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else if (hsp == 64) attn_bwd_dq_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else attn_bwd_dq_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+                 4.0 * (B * NH * tri + 2.0 * BTC), stream);
+    if (hsp == 32) attn_bwd_dq_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+    else if (hsp == 64) attn_bwd_dq_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+    else attn_bwd_dq_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
   }
   GPT2_HIP_OK(hipGetLastError());
   return 0;

@@ -65,10 +65,12 @@ size_t colsum_partial_floats(int N, int C);
 // ----- attention (attention.hip) --------------------------------------------------------
 int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
                       hipStream_t stream);
-// `dscratch` needs B*NH*T floats (row dot products of dout and out)
+// `dscratch` needs B*NH*T floats (row dot products of dout and out); `ds_scratch` needs
+// attention_ds_scratch_floats(B, T, NH) floats (the causal 64x64 tiles of dS)
+size_t attention_ds_scratch_floats(int B, int T, int NH);
 int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
-                       const float* lse, float* dscratch, int B, int T, int C, int NH,
-                       hipStream_t stream);
+                       const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
+                       int NH, hipStream_t stream);
 
 // ----- memory-bound kernels (stream_ops.hip) ---------------------------------------------
 int encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe, int B,

@@ -89,7 +89,7 @@ struct gpt2_model {
   float *encoded, *ln1, *ln1_mean, *ln1_rstd, *qkv, *atty, *attn_lse, *res2, *ln2, *ln2_mean,
       *ln2_rstd, *fch, *fchg, *res3, *lnf, *lnf_mean, *lnf_rstd, *logits, *losses, *xent_lse;
   // backward buffers and scratch
-  float *dres, *dbuf4, *dln, *datty, *dqkv, *attn_D, *gemm_ws, *ln_ws, *d_loss;
+  float *dres, *dbuf4, *dln, *datty, *dqkv, *attn_D, *attn_dS, *gemm_ws, *ln_ws, *d_loss;
   size_t gemm_ws_floats = 0;
   int32_t *tok, *tgt, *sort_scratch, *d_err;
 
@@ -176,6 +176,7 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
   md->datty = F(BT * C);
   md->dqkv = F(BT * 3 * C);
   md->attn_D = F(NH * BT);
+  md->attn_dS = F(attention_ds_scratch_floats(B, T, (int)NH));
   // split-K workspace: the largest any GEMM of the step asks for
   size_t ws = 0;
   {
@@ -723,7 +724,8 @@ int gpt2_backward(gpt2_model* md) {
                    G(md, P_ATTPROJB) + (size_t)l * C, md->dres, md->atty + l * NC,
                    P(md, P_ATTPROJW) + (size_t)l * C * C, C, C));
     CHK(attention_backward(md->dqkv, md->datty, md->qkv + l * 3 * NC, md->atty + l * NC,
-                           md->attn_lse + (size_t)l * NH * BT, md->attn_D, B, T, C, NH, s));
+                           md->attn_lse + (size_t)l * NH * BT, md->attn_D, md->attn_dS, B, T, C,
+                           NH, s));
     CHK(linear_bwd(md->dln, nullptr, G(md, P_QKVW) + (size_t)l * 3 * C * C,
                    G(md, P_QKVB) + (size_t)l * 3 * C, md->dqkv, md->ln1 + l * NC,
                    P(md, P_QKVW) + (size_t)l * 3 * C * C, C, 3 * C));
@@ -890,9 +892,10 @@ int gpt2_k_attention_backward(float* dqkv, const float* dout, const float* qkv,
     return fail(nullptr, GPT2_ERR_ARG, "bad argument");
   hipStream_t s = as_stream(stream);
   float* D = nullptr;
-  if (hipMalloc(&D, (size_t)B * NH * T * sizeof(float)) != hipSuccess)
+  const size_t nD = (size_t)B * NH * T, nS = attention_ds_scratch_floats(B, T, NH);
+  if (hipMalloc(&D, (nD + nS) * sizeof(float)) != hipSuccess)
     return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
-  int rc = attention_backward(dqkv, dout, qkv, out, lse, D, B, T, C, NH, s);
+  int rc = attention_backward(dqkv, dout, qkv, out, lse, D, D + nD, B, T, C, NH, s);
   (void)hipStreamSynchronize(s);
   (void)hipFree(D);
   return rc;
