@@ -24,7 +24,9 @@ section 1.22):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -91,6 +93,7 @@ def init_params(shape: ModelShape, seed: int, scale_residual: bool,
     sizes = param_sizes(shape.L, shape.C, shape.V, shape.maxT)
     out = np.empty(sum(sizes), dtype=np.float32)
     resid_std = std / math.sqrt(2.0 * shape.L) if scale_residual else std
+    jobs = []  # (first flat element, count, std) of each chunk of normal draws
     off = 0
     for name, n in zip(PARAM_NAMES, sizes):
         if name in ("ln1w", "ln2w", "lnfw"):
@@ -99,10 +102,16 @@ def init_params(shape: ModelShape, seed: int, scale_residual: bool,
             out[off:off + n] = 0.0
         else:
             s = resid_std if name in ("attprojw", "fcprojw") else std
-            for c0 in range(0, n, chunk):
-                c1 = min(n, c0 + chunk)
-                out[off + c0:off + c1] = (normal(seed, off + c0, c1 - c0) * s).astype(np.float32)
+            jobs += [(off + c0, min(chunk, n - c0), s) for c0 in range(0, n, chunk)]
         off += n
+
+    def fill(job):
+        start, count, s = job
+        out[start:start + count] = (normal(seed, start, count) * s).astype(np.float32)
+
+    # chunks are independent slices of the counter-based stream; numpy releases the GIL
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, jobs))
     return out
 
 

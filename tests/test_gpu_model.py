@@ -9,6 +9,8 @@ against the fp64 oracle on the same seeded parameters and tokens.
 - GPT-2 124M shape at B16 T1024, in the launch configuration the benchmark times: the
   oracle checks sampled outputs (by causality the loss and logits of positions 0..63 of a
   row depend only on that row's first 64 tokens), plus properties that hold at any size;
+- GPT-2 350M shape (L24 C1024 H16): every gradient of one step at B1 T32, then the B8 T1024
+  forward on sampled positions;
 - error paths of the ABI.
 """
 import concurrent.futures as cf
@@ -184,6 +186,58 @@ def test_gpt2_124m_b16_t1024_sampled_and_properties():
     assert np.all(err <= 1e-5 * np.abs(ref["losses"])), err.max()
     # loss at init: ln V + C*sigma^2/2 within a few standard errors
     expect = math.log(V) + shape.C * 0.02 ** 2 / 2
+    assert abs(loss - expect) < 0.05, (loss, expect)
+
+
+def test_gpt2_350m_b1_grads_and_b8_t1024_sampled():
+    w = synth.WORKLOADS["gpt2_350m_b8_t1024"]
+    shape = w.shape
+    p0 = synth.init_params(shape, w.seed, w.scale_residual)
+    p64 = p0.astype(np.float64)
+    with cf.ThreadPoolExecutor(max_workers=3) as ex:
+        # the oracle runs on the host while the GPU works
+        tok1, tgt1 = synth.batch(w.seed, 1, 32, shape.V, mode=w.token_mode)
+        ref1 = ex.submit(oracle.gpt2_step, shape, p64, tok1, tgt1)
+        tok, tgt = synth.batch(w.seed, w.B, w.T, shape.V, mode=w.token_mode)
+        rows, P = [0, 5], 64
+        refs = [ex.submit(oracle.gpt2_step, shape, p64, tok[r:r + 1, :P], tgt[r:r + 1, :P],
+                          want_logits=True, want_losses=True, want_grads=False) for r in rows]
+
+        m = make_model(shape)
+        m.set_params(p0)
+        m.zero_grad()
+        loss1 = m.forward(dev_i32(tok1), dev_i32(tgt1))
+        m.backward()
+        grads = m.get_grads()
+        m.adamw_step(t=1, **HP)
+        params = m.get_params()
+        m.close()
+
+        m = make_model(shape, w.B, w.T)
+        m.set_params(p0)
+        loss = m.forward(dev_i32(tok), dev_i32(tgt))
+        losses = torch.empty((w.B, w.T), device="cuda")
+        m.get_losses(losses)
+        logits = torch.empty((w.B, w.T, shape.V), device="cuda")
+        m.get_logits(logits)
+        got_logits = logits[rows, :P].cpu().numpy()
+        got_losses = losses[rows, :P].cpu().numpy()
+        del logits
+        m.close()
+
+        ref1 = ref1.result()
+        refs = [f.result() for f in refs]
+    assert_loss(loss1, ref1["loss"])
+    compare_grads(shape, grads, ref1["grads"])
+    rp_own, _, _ = oracle.adamw(p64, grads, np.zeros(p0.size), np.zeros(p0.size), HP["lr"],
+                                HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], 1)
+    assert np.abs(params - rp_own).max() <= 1e-6
+    ref_logits = np.concatenate([r["logits"] for r in refs])
+    ref_losses = np.concatenate([r["losses"] for r in refs])
+    print("sampled logits", assert_tensor_close("sampled logits", got_logits, ref_logits))
+    err = np.abs(got_losses - ref_losses)
+    assert np.all(err <= 1e-5 * np.abs(ref_losses)), err.max()
+    expect = math.log(shape.V) + shape.C * 0.02 ** 2 / 2
     assert abs(loss - expect) < 0.05, (loss, expect)
 
 
