@@ -65,7 +65,24 @@ SIGNATURES = {
     "gpt2_k_crossentropy_backward": (_int, [_vp, _vp, _vp, _f, _int, _int, _int, _vp]),
     "gpt2_k_mean": (_int, [_vp, _vp, _int, _vp]),
     "gpt2_k_adamw": (_int, [_vp, _vp, _vp, _vp, _sz, _f, _f, _f, _f, _f, _int, _vp]),
+    "gpt2_k_gemm_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                                _int, _int, _int, _int, _vp]),
+    "gpt2_k_encoder_forward_bf16": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
+                                           _vp]),
+    "gpt2_k_layernorm_forward_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp]),
+    "gpt2_k_layernorm_backward_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int,
+                                              _int, _vp]),
+    "gpt2_k_attention_forward_bf16": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "gpt2_k_attention_backward_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                                              _vp]),
+    "gpt2_k_crossentropy_forward_bf16": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _vp,
+                                                _vp]),
+    "gpt2_k_crossentropy_backward_bf16": (_int, [_vp, _vp, _vp, _f, _int, _int, _int, _vp]),
+    "gpt2_k_adamw_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _f, _f, _f, _f, _f, _int, _vp]),
+    "gpt2_k_cast_bf16": (_int, [_vp, _vp, _sz, _vp]),
 }
+
+DTYPES = {"fp32": 0, "bf16": 1}
 
 _lib = None
 
@@ -113,7 +130,7 @@ def _ptr(t, kind: str = "f32") -> int | None:
     if t is None:
         return None
     torch = _torch()
-    want = torch.float32 if kind == "f32" else torch.int32
+    want = {"f32": torch.float32, "i32": torch.int32, "bf16": torch.bfloat16}[kind]
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
     if t.dtype != want:
@@ -125,6 +142,10 @@ def _ptr(t, kind: str = "f32") -> int | None:
 
 def _iptr(t) -> int | None:
     return _ptr(t, "i32")
+
+
+def _hptr(t) -> int | None:
+    return _ptr(t, "bf16")
 
 
 def _host_or_device(buf):
@@ -143,11 +164,12 @@ class GPT2:
     """One model on the current device (see include/gpt2.h for the semantics)."""
 
     def __init__(self, L: int, C: int, H: int, V: int, maxT: int, B: int = 0, T: int = 0,
-                 stream: int | None = None):
+                 stream: int | None = None, dtype: str = "fp32"):
         h = _vp()
         st = current_stream() if stream is None else stream
-        _check(lib().gpt2_build_ex(ctypes.byref(h), L, C, H, V, maxT, 0, B, T, st))
+        _check(lib().gpt2_build_ex(ctypes.byref(h), L, C, H, V, maxT, DTYPES[dtype], B, T, st))
         self.h = h
+        self.dtype = dtype
         self.L, self.C, self.H, self.V, self.maxT = L, C, H, V, maxT
         self.num_params = int(lib().gpt2_num_params(h))
 
@@ -315,3 +337,60 @@ def k_mean(out, x, n):
 def k_adamw(p, g, m, v, n, lr, beta1, beta2, eps, wd, t):
     _check(lib().gpt2_k_adamw(_ptr(p), _ptr(g), _ptr(m), _ptr(v), n, lr, beta1, beta2, eps, wd,
                               t, current_stream()))
+
+
+# ---- bf16 forms (bf16 tensors are torch.bfloat16) ------------------------------------------
+def k_gemm_bf16(C, A, B, M, N, K, lda, ldb, ldc, a_trans=False, b_trans=False, epilogue=0,
+                bias=None, C2=None, R=None, colsum=None):
+    """C (bf16, or fp32 for epilogue 3) = op(A) . op(B) with the fused epilogue."""
+    c_ptr = _ptr(C) if epilogue == 3 else _hptr(C)
+    _check(lib().gpt2_k_gemm_bf16(c_ptr, _hptr(C2), _hptr(R), _hptr(A), _hptr(B), _ptr(bias),
+                                  _ptr(colsum), M, N, K, lda, ldb, ldc, int(a_trans),
+                                  int(b_trans), epilogue, current_stream()))
+
+
+def k_encoder_forward_bf16(out, tok, wte, wpe, B, T, C, V, err_flag=None):
+    _check(lib().gpt2_k_encoder_forward_bf16(_hptr(out), _iptr(tok), _ptr(wte), _ptr(wpe), B, T,
+                                             C, V, _iptr(err_flag), current_stream()))
+
+
+def k_layernorm_forward_bf16(out, mean, rstd, x, w, b, N, C):
+    _check(lib().gpt2_k_layernorm_forward_bf16(_hptr(out), _ptr(mean), _ptr(rstd), _hptr(x),
+                                               _ptr(w), _ptr(b), N, C, current_stream()))
+
+
+def k_layernorm_backward_bf16(dx, dx_copy, dw, db, dout, x, w, mean, rstd, N, C):
+    _check(lib().gpt2_k_layernorm_backward_bf16(_ptr(dx), _hptr(dx_copy), _ptr(dw), _ptr(db),
+                                                _hptr(dout), _hptr(x), _ptr(w), _ptr(mean),
+                                                _ptr(rstd), N, C, current_stream()))
+
+
+def k_attention_forward_bf16(out, lse, qkv, B, T, C, NH):
+    _check(lib().gpt2_k_attention_forward_bf16(_hptr(out), _ptr(lse), _hptr(qkv), B, T, C, NH,
+                                               current_stream()))
+
+
+def k_attention_backward_bf16(dqkv, dout, qkv, out, lse, B, T, C, NH):
+    _check(lib().gpt2_k_attention_backward_bf16(_hptr(dqkv), _hptr(dout), _hptr(qkv),
+                                                _hptr(out), _ptr(lse), B, T, C, NH,
+                                                current_stream()))
+
+
+def k_crossentropy_forward_bf16(losses, lse, logits, targets, N, V, ld, err_flag=None):
+    _check(lib().gpt2_k_crossentropy_forward_bf16(_ptr(losses), _ptr(lse), _hptr(logits),
+                                                  _iptr(targets), N, V, ld, _iptr(err_flag),
+                                                  current_stream()))
+
+
+def k_crossentropy_backward_bf16(logits, lse, targets, dloss, N, V, ld):
+    _check(lib().gpt2_k_crossentropy_backward_bf16(_hptr(logits), _ptr(lse), _iptr(targets),
+                                                   dloss, N, V, ld, current_stream()))
+
+
+def k_adamw_bf16(p, p_bf16, g, m, v, n, lr, beta1, beta2, eps, wd, t):
+    _check(lib().gpt2_k_adamw_bf16(_ptr(p), _hptr(p_bf16), _ptr(g), _ptr(m), _ptr(v), n, lr,
+                                   beta1, beta2, eps, wd, t, current_stream()))
+
+
+def k_cast_bf16(dst, src, n):
+    _check(lib().gpt2_k_cast_bf16(_hptr(dst), _ptr(src), n, current_stream()))

@@ -36,11 +36,12 @@ constexpr int NTHR = 128;   // two waves, 32 queries (or keys) each
 
 // Loads 4 floats of row t, columns d..d+3 (row stride ld) without a branch: the address is
 // clamped into the tensor (t <= T-1, d <= hs-4) and out-of-range values are replaced by 0.
-GPT2_DEVICE_INLINE f32x4 load4_rowcol(const float* base, long long ld, int t, int d, int T,
+template <typename T>
+GPT2_DEVICE_INLINE f32x4 load4_rowcol(const T* base, long long ld, int t, int d, int Tn,
                                       int hs) {
-  const int tc = min(t, T - 1), dc = min(d, hs - 4);
-  const f32x4 x = *reinterpret_cast<const f32x4*>(base + (long long)tc * ld + dc);
-  return (t < T && d < hs) ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tc = min(t, Tn - 1), dc = min(d, hs - 4);
+  const f32x4 x = ld4(base + (long long)tc * ld + dc);
+  return (t < Tn && d < hs) ? x : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // 1-D grid over (tile, head, batch) with the tile index fastest; logical ids are made
@@ -57,8 +58,8 @@ GPT2_DEVICE_INLINE void tile_of_block(int ntiles, int NH, int* tile, int* head, 
 // Cooperative load of `rows` x HSP values starting at row `row0` of a strided tensor
 // (row stride `ld`, column offset already applied) into S[TILE][HSP+4]; rows >= T and
 // columns >= hs are zero.
-template <int HSP>
-GPT2_DEVICE_INLINE void load_tile(float (*S)[HSP + 4], const float* base, long long ld,
+template <int HSP, typename TS>
+GPT2_DEVICE_INLINE void load_tile(float (*S)[HSP + 4], const TS* base, long long ld,
                                   int row0, int T, int hs, int tid) {
   constexpr int F4 = HSP / 4;
 #pragma unroll
@@ -73,10 +74,10 @@ GPT2_DEVICE_INLINE void load_tile(float (*S)[HSP + 4], const float* base, long l
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
-template <int HSP>
-__global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
+template <int HSP, typename TS>
+__global__ __launch_bounds__(NTHR) void attn_fwd_kernel(TS* __restrict__ out,
                                                         float* __restrict__ lse,
-                                                        const float* __restrict__ qkv, int T,
+                                                        const TS* __restrict__ qkv, int T,
                                                         int C, int NH, int hs,
                                                         float scale_log2) {
   constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
-  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const TS* base = qkv + (long long)b * T * C3 + (long long)head * hs;
   const int q = qt * TILE + wave * 32 + r;
   const int qm = min(q, T - 1);  // lanes past the end mask as the last row; never stored
 
@@ -171,16 +172,15 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
   if (q < T) {
-    float* o = out + ((long long)b * T + q) * C + (long long)head * hs;
+    TS* o = out + ((long long)b * T + q) * C + (long long)head * hs;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
       for (int ig = 0; ig < 4; ig++) {
         const int d = 32 * db + 8 * ig + 4 * hf;
         if (d < hs)
-          *reinterpret_cast<f32x4*>(o + d) =
-              f32x4{oacc[db][4 * ig] * inv, oacc[db][4 * ig + 1] * inv,
-                    oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv};
+          st4(o + d, f32x4{oacc[db][4 * ig] * inv, oacc[db][4 * ig + 1] * inv,
+                           oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv});
       }
     if (hf == 0) lse[((long long)b * NH + head) * T + q] = (m_run + log2f(l_tot)) * kLn2;
   }
@@ -190,9 +190,10 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(float* __restrict__ out,
 // backward: D = rowsum(dO * O) per (b, head, query)
 // ---------------------------------------------------------------------------------------
 // Head sizes that are not 4 times a power of two: one thread per (b, q, head) segment.
+template <typename TS>
 __global__ void attn_bwd_rowdot_generic_kernel(float* __restrict__ D,
-                                               const float* __restrict__ dout,
-                                               const float* __restrict__ out, int B, int T,
+                                               const TS* __restrict__ dout,
+                                               const TS* __restrict__ out, int B, int T,
                                                int C, int NH, int hs) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)B * NH * T) return;
@@ -202,8 +203,8 @@ __global__ void attn_bwd_rowdot_generic_kernel(float* __restrict__ D,
   const long long off = bq * C + (long long)head * hs;
   float s = 0.f;
   for (int d = 0; d < hs; d += 4) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(dout + off + d);
-    f32x4 o = *reinterpret_cast<const f32x4*>(out + off + d);
+    f32x4 a = ld4(dout + off + d);
+    f32x4 o = ld4(out + off + d);
     s += a[0] * o[0] + a[1] * o[1] + a[2] * o[2] + a[3] * o[3];
   }
   D[((long long)b * NH + head) * T + q] = s;
@@ -212,16 +213,16 @@ __global__ void attn_bwd_rowdot_generic_kernel(float* __restrict__ D,
 // One float4 per thread, threads of a (b, q, head) segment adjacent: loads are contiguous
 // across the wave, and the HS4 = hs/4 partial sums of a segment are combined with shuffles
 // (HS4 a power of two up to 32). D is (B, NH, T).
-template <int HS4>
-__global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const float* __restrict__ dout,
-                                       const float* __restrict__ out, int B, int T, int C,
+template <int HS4, typename TS>
+__global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const TS* __restrict__ dout,
+                                       const TS* __restrict__ out, int B, int T, int C,
                                        int NH) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long n4 = (long long)B * T * (C / 4);
   const bool ok = idx < n4;
   const long long i4 = ok ? idx : 0;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(dout + 4 * i4);
-  const f32x4 o = *reinterpret_cast<const f32x4*>(out + 4 * i4);
+  const f32x4 a = ld4(dout + 4 * i4);
+  const f32x4 o = ld4(out + 4 * i4);
   float s = (a[0] * o[0] + a[1] * o[1]) + (a[2] * o[2] + a[3] * o[3]);
 #pragma unroll
   for (int w = HS4 / 2; w > 0; w >>= 1) s += __shfl_xor(s, w, 64);
@@ -241,10 +242,10 @@ GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 
 // dK, dV for a tile of 64 keys (32 per wave), looping over query tiles from the diagonal.
 // It also writes dS = P * (dP - D) of every causal tile it visits to `dsbuf`, from which
 // attn_bwd_dq_kernel forms dQ = dS K without recomputing P and dP.
-template <int HSP>
+template <int HSP, typename TS>
 __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
-    float* __restrict__ dqkv, float* __restrict__ dsbuf, const float* __restrict__ dout,
-    const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Drow,
+    TS* __restrict__ dqkv, float* __restrict__ dsbuf, const TS* __restrict__ dout,
+    const TS* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Drow,
     int T, int C, int NH, int hs, float scale, float scale_log2) {
   constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
   __shared__ float Qs[TILE][LD];
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
-  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
-  const float* dobase = dout + (long long)b * T * C + (long long)head * hs;
+  const TS* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const TS* dobase = dout + (long long)b * T * C + (long long)head * hs;
   const float* lrow = lse + ((long long)b * NH + head) * T;
   const float* drow = Drow + ((long long)b * NH + head) * T;
   const int key = kt * TILE + wave * 32 + r;
@@ -350,20 +351,18 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
     }
   }
   if (key < T) {
-    float* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
-    float* dv = dk + C;
+    TS* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
+    TS* dv = dk + C;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
       for (int ig = 0; ig < 4; ig++) {
         const int d = 32 * db + 8 * ig + 4 * hf;
         if (d < hs) {
-          *reinterpret_cast<f32x4*>(dk + d) =
-              f32x4{dkacc[db][4 * ig] * scale, dkacc[db][4 * ig + 1] * scale,
-                    dkacc[db][4 * ig + 2] * scale, dkacc[db][4 * ig + 3] * scale};
-          *reinterpret_cast<f32x4*>(dv + d) =
-              f32x4{dvacc[db][4 * ig], dvacc[db][4 * ig + 1], dvacc[db][4 * ig + 2],
-                    dvacc[db][4 * ig + 3]};
+          st4(dk + d, f32x4{dkacc[db][4 * ig] * scale, dkacc[db][4 * ig + 1] * scale,
+                            dkacc[db][4 * ig + 2] * scale, dkacc[db][4 * ig + 3] * scale});
+          st4(dv + d, f32x4{dvacc[db][4 * ig], dvacc[db][4 * ig + 1], dvacc[db][4 * ig + 2],
+                            dvacc[db][4 * ig + 3]});
         }
       }
   }
@@ -371,9 +370,9 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
 
 // dQ = scale * dS K for a tile of 64 queries (32 per wave), over key tiles 0 .. qt, reading
 // the dS tiles written by attn_bwd_dkdv_kernel. M = queries, N = head dim, K = keys.
-template <int HSP>
-__global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(float* __restrict__ dqkv,
-                                                           const float* __restrict__ qkv,
+template <int HSP, typename TS>
+__global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(TS* __restrict__ dqkv,
+                                                           const TS* __restrict__ qkv,
                                                            const float* __restrict__ dsbuf, int T,
                                                            int C, int NH, int hs, float scale) {
   constexpr int LD = HSP + 4, ND = HSP / 32, LDSS = TILE + 4;
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(float* __restrict__ d
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
-  const float* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
+  const TS* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
   const float* src = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, 0)) *
                                  (TILE * TILE);
 
@@ -428,7 +427,7 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(float* __restrict__ d
 #pragma unroll
     for (int i = 0; i < 16; i++) {
       const int q = qt * TILE + 32 * wave + 8 * (i / 4) + 4 * hf + (i % 4);
-      if (q < T) dqkv[((long long)b * T + q) * C3 + (long long)head * hs + d] = acc[db][i] * scale;
+      if (q < T) st1(dqkv + ((long long)b * T + q) * C3 + (long long)head * hs + d, acc[db][i] * scale);
     }
   }
 }
@@ -444,10 +443,10 @@ bool check_shape(int B, int T, int C, int NH, int* hsp) {
   return true;
 }
 
-}  // namespace
 
-int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
-                      hipStream_t stream) {
+template <typename TS>
+int attention_forward_t(TS* out, float* lse, const TS* qkv, int B, int T, int C, int NH,
+                        hipStream_t stream) {
   int hsp;
   if (!check_shape(B, T, C, NH, &hsp)) {
     set_global_error("attention: unsupported shape B=%d T=%d C=%d NH=%d", B, T, C, NH);
@@ -457,66 +456,99 @@ int attention_forward(float* out, float* lse, const float* qkv, int B, int T, in
   const float scale_log2 = kLog2e / sqrtf((float)hs);
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   const double tri = (double)T * (T + 1) / 2.0;  // causal (query, key) pairs per head
-  ProfScope ps("attn_fwd_kernel", 4.0 * B * NH * hs * tri,
-               4.0 * ((double)B * T * 3 * C + (double)B * T * C + (double)B * NH * T), stream);
-  if (hsp == 32) attn_fwd_kernel<32><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
-  else if (hsp == 64) attn_fwd_kernel<64><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
-  else attn_fwd_kernel<128><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  const double es = sizeof(TS);
+  ProfScope ps(sizeof(TS) == 4 ? "attn_fwd_kernel" : "attn_fwd_bf16_kernel",
+               4.0 * B * NH * hs * tri,
+               es * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
+  if (hsp == 32) attn_fwd_kernel<32, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else if (hsp == 64) attn_fwd_kernel<64, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else attn_fwd_kernel<128, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
+
+}  // namespace
 
 size_t attention_ds_scratch_floats(int B, int T, int NH) {
   const long long nt = (T + TILE - 1) / TILE;
   return (size_t)B * NH * (nt * (nt + 1) / 2) * TILE * TILE;
 }
 
-int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
-                       const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
-                       int NH, hipStream_t stream) {
+namespace {
+template <typename TS>
+int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
+                         const float* lse, float* dscratch, float* ds_scratch, int B, int T,
+                         int C, int NH, hipStream_t stream) {
   int hsp;
   if (!check_shape(B, T, C, NH, &hsp)) {
     set_global_error("attention: unsupported shape B=%d T=%d C=%d NH=%d", B, T, C, NH);
     return -1;
   }
+  const bool f32 = sizeof(TS) == 4;
+  const double es = sizeof(TS);
   const int hs = C / NH;
   const float scale = 1.0f / sqrtf((float)hs);
   const float scale_log2 = scale * kLog2e;
   const long long rows = (long long)B * NH * T;
   const double BTC = (double)B * T * C, tri = (double)T * (T + 1) / 2.0;
   {
-    ProfScope ps("attn_bwd_rowdot_kernel", 2.0 * BTC, 4.0 * (2.0 * BTC + rows), stream);
+    ProfScope ps(f32 ? "attn_bwd_rowdot_kernel" : "attn_bwd_rowdot_bf16_kernel", 2.0 * BTC,
+                 es * 2.0 * BTC + 4.0 * rows, stream);
     const long long n4 = (long long)B * T * (C / 4);
     const unsigned blocks = (unsigned)((n4 + 255) / 256);
     switch (hs / 4) {
-      case 1: attn_bwd_rowdot_kernel<1><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 2: attn_bwd_rowdot_kernel<2><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 4: attn_bwd_rowdot_kernel<4><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 8: attn_bwd_rowdot_kernel<8><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 16: attn_bwd_rowdot_kernel<16><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 32: attn_bwd_rowdot_kernel<32><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 1: attn_bwd_rowdot_kernel<1, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 2: attn_bwd_rowdot_kernel<2, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 4: attn_bwd_rowdot_kernel<4, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 8: attn_bwd_rowdot_kernel<8, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 16: attn_bwd_rowdot_kernel<16, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
+      case 32: attn_bwd_rowdot_kernel<32, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
       default:
-        attn_bwd_rowdot_generic_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+        attn_bwd_rowdot_generic_kernel<TS><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
             dscratch, dout, out, B, T, C, NH, hs);
     }
   }
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
-    ProfScope ps("attn_bwd_dkdv_kernel", 6.0 * B * NH * hs * tri,
-                 4.0 * (3.0 * BTC + BTC + 2.0 * rows + 2.0 * BTC + B * NH * tri), stream);
-    if (hsp == 32) attn_bwd_dkdv_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else if (hsp == 64) attn_bwd_dkdv_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else attn_bwd_dkdv_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    ProfScope ps(f32 ? "attn_bwd_dkdv_kernel" : "attn_bwd_dkdv_bf16_kernel",
+                 6.0 * B * NH * hs * tri,
+                 es * (3.0 * BTC + BTC + 2.0 * BTC) + 4.0 * (2.0 * rows + B * NH * tri), stream);
+    if (hsp == 32) attn_bwd_dkdv_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hsp == 64) attn_bwd_dkdv_kernel<64, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dkdv_kernel<128, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
   }
   {  // dQ = dS K
-    ProfScope ps("attn_bwd_dq_kernel", 2.0 * B * NH * hs * tri,
-                 4.0 * (B * NH * tri + 2.0 * BTC), stream);
-    if (hsp == 32) attn_bwd_dq_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
-    else if (hsp == 64) attn_bwd_dq_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
-    else attn_bwd_dq_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+    ProfScope ps(f32 ? "attn_bwd_dq_kernel" : "attn_bwd_dq_bf16_kernel", 2.0 * B * NH * hs * tri,
+                 4.0 * B * NH * tri + es * 2.0 * BTC, stream);
+    if (hsp == 32) attn_bwd_dq_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+    else if (hsp == 64) attn_bwd_dq_kernel<64, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+    else attn_bwd_dq_kernel<128, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
   }
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+
+}  // namespace
+
+int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                      hipStream_t stream) {
+  return attention_forward_t(out, lse, qkv, B, T, C, NH, stream);
+}
+int attention_forward(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C, int NH,
+                      hipStream_t stream) {
+  return attention_forward_t(out, lse, qkv, B, T, C, NH, stream);
+}
+int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
+                       const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
+                       int NH, hipStream_t stream) {
+  return attention_backward_t(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C, NH,
+                              stream);
+}
+int attention_backward(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv, const bf16_t* out,
+                       const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
+                       int NH, hipStream_t stream) {
+  return attention_backward_t(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C, NH,
+                              stream);
 }
 
 }  // namespace gpt2

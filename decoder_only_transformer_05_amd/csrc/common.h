@@ -12,6 +12,32 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define GPT2_DEVICE_INLINE __device__ __forceinline__
 
+// bf16 storage: the upper 16 bits of an IEEE fp32 value. Conversion to bf16 rounds to
+// nearest, ties to even (v_cvt_pk_bf16_f32 on gfx950).
+typedef uint16_t bf16_t;
+GPT2_DEVICE_INLINE float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+GPT2_DEVICE_INLINE bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// Four consecutive elements of an activation tensor, fp32 or bf16 storage, as fp32
+// (16- or 8-byte aligned accesses).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+GPT2_DEVICE_INLINE f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+GPT2_DEVICE_INLINE f32x4 ld4(const bf16_t* p) {
+  const u32x2_t u = *reinterpret_cast<const u32x2_t*>(p);
+  return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
+               __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};
+}
+GPT2_DEVICE_INLINE void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+GPT2_DEVICE_INLINE void st4(bf16_t* p, f32x4 v) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
+}
+GPT2_DEVICE_INLINE float ld1(const float* p) { return *p; }
+GPT2_DEVICE_INLINE float ld1(const bf16_t* p) { return bf16_to_f32(*p); }
+GPT2_DEVICE_INLINE void st1(float* p, float v) { *p = v; }
+GPT2_DEVICE_INLINE void st1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
 // One wave64 MFMA: acc(32x32) += A(32x2) * B(2x32), fp32 in and out.
 // Operand layout: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32].
 // Result layout: acc[i] of lane l is element (row 8*(i/4) + 4*(l/32) + i%4, col l % 32).

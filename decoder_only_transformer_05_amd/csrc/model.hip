@@ -76,20 +76,25 @@ using namespace gpt2;
 
 struct gpt2_model {
   int L = 0, C = 0, NH = 0, V = 0, maxT = 0, Vp = 0;
+  int dtype = GPT2_DTYPE_FP32;
   int device = 0;
   hipStream_t stream = nullptr;  // NULL = the null stream
   size_t nparams = 0;
   size_t poff[16] = {}, plen[16] = {};
   float* pbuf = nullptr;
   float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
+  bf16_t* pbf = nullptr;  // GPT2_DTYPE_BF16: bf16 copy of params (GEMM operands)
 
   int B = 0, T = 0;
   char* abuf = nullptr;
-  // forward activations (per layer where noted)
-  float *encoded, *ln1, *ln1_mean, *ln1_rstd, *qkv, *atty, *attn_lse, *res2, *ln2, *ln2_mean,
-      *ln2_rstd, *fch, *fchg, *res3, *lnf, *lnf_mean, *lnf_rstd, *logits, *losses, *xent_lse;
-  // backward buffers and scratch
-  float *dres, *dbuf4, *dln, *datty, *dqkv, *attn_D, *attn_dS, *gemm_ws, *ln_ws, *d_loss;
+  // activation tensors: fp32 or bf16 storage by dtype (per layer where noted)
+  void *encoded, *ln1, *qkv, *atty, *res2, *ln2, *fch, *fchg, *res3, *lnf, *logits;
+  void *dbuf4, *dln, *datty, *dqkv;
+  // fp32 in both modes: statistics, losses, the residual-stream gradient, scratch
+  float *ln1_mean, *ln1_rstd, *attn_lse, *ln2_mean, *ln2_rstd, *lnf_mean, *lnf_rstd, *losses,
+      *xent_lse;
+  float *dres, *attn_D, *attn_dS, *gemm_ws, *ln_ws, *d_loss;
+  bf16_t* dres_h = nullptr;  // GPT2_DTYPE_BF16: dres rounded to bf16 (a GEMM operand)
   size_t gemm_ws_floats = 0;
   int32_t *tok, *tgt, *sort_scratch, *d_err;
 
@@ -140,6 +145,71 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 float* P(gpt2_model* md, int k) { return md->params + md->poff[k]; }
 float* G(gpt2_model* md, int k) { return md->grads + md->poff[k]; }
 
+// storage of the weights that GEMMs read: the fp32 parameters, or their bf16 copy
+template <typename T> const T* W(gpt2_model* md, int k);
+template <> const float* W<float>(gpt2_model* md, int k) { return md->params + md->poff[k]; }
+template <> const bf16_t* W<bf16_t>(gpt2_model* md, int k) { return md->pbf + md->poff[k]; }
+
+template <typename T> T* act(void* p) { return static_cast<T*>(p); }
+
+template <typename T> struct GemmOf;
+template <> struct GemmOf<float> { using type = Gemm; };
+template <> struct GemmOf<bf16_t> { using type = GemmBf16; };
+
+size_t ws_floats(const Gemm& g) { return gemm_workspace_floats(g); }
+size_t ws_floats(const GemmBf16& g) { return gemm_bf16_workspace_floats(g); }
+int run_gemm(gpt2_model* md, const Gemm& g) {
+  return gemm(g, md->gemm_ws, md->gemm_ws_floats, md->stream);
+}
+int run_gemm(gpt2_model* md, const GemmBf16& g) {
+  return gemm_bf16(g, md->gemm_ws, md->gemm_ws_floats, md->stream);
+}
+
+// the largest split-K workspace any GEMM of a step asks for
+template <typename T>
+size_t step_gemm_workspace(int BT, int C, int V) {
+  using GT = typename GemmOf<T>::type;
+  size_t ws = 0;
+  const int oc[4] = {3 * C, C, 4 * C, C};
+  const int in[4] = {C, C, C, 4 * C};
+  for (int k = 0; k < 4; k++) {
+    GT w;  // weight gradient (bias gradient fused)
+    w.M = oc[k];
+    w.N = in[k];
+    w.K = BT;
+    w.epi = EPI_ACCUM;
+    w.a_trans = true;
+    w.colsum = reinterpret_cast<float*>(16);  // only its presence matters when measuring
+    ws = std::max(ws, ws_floats(w));
+    GT d;  // input gradient
+    d.M = BT;
+    d.N = in[k];
+    d.K = oc[k];
+    ws = std::max(ws, ws_floats(d));
+  }
+  const int fn[5] = {3 * C, C, 4 * C, C, V};  // forward: qkv, attproj, fc, fcproj, lm_head
+  const int fk[5] = {C, C, C, 4 * C, C};
+  for (int k = 0; k < 5; k++) {
+    GT f;
+    f.M = BT;
+    f.N = fn[k];
+    f.K = fk[k];
+    ws = std::max(ws, ws_floats(f));
+  }
+  GT d;  // dlnf = dlogits . wte
+  d.M = BT;
+  d.N = C;
+  d.K = V;
+  ws = std::max(ws, ws_floats(d));
+  GT w;  // dwte += dlogits^T . lnf
+  w.M = V;
+  w.N = C;
+  w.K = BT;
+  w.epi = EPI_ACCUM;
+  ws = std::max(ws, ws_floats(w));
+  return ws;
+}
+
 // Carves the activation block for (B, T); with base == nullptr it only measures.
 size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
   const size_t L = md->L, C = md->C, NH = md->NH, BT = (size_t)B * T;
@@ -150,77 +220,41 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
     return p;
   };
   auto F = [&](size_t n) { return reinterpret_cast<float*>(take(n * sizeof(float))); };
-  md->encoded = F(BT * C);
-  md->ln1 = F(L * BT * C);
+  const size_t es = md->dtype == GPT2_DTYPE_BF16 ? 2 : 4;  // activation element size
+  auto A = [&](size_t n) { return static_cast<void*>(take(n * es)); };
+  md->encoded = A(BT * C);
+  md->ln1 = A(L * BT * C);
   md->ln1_mean = F(L * BT);
   md->ln1_rstd = F(L * BT);
-  md->qkv = F(L * BT * 3 * C);
-  md->atty = F(L * BT * C);
+  md->qkv = A(L * BT * 3 * C);
+  md->atty = A(L * BT * C);
   md->attn_lse = F(L * NH * BT);
-  md->res2 = F(L * BT * C);
-  md->ln2 = F(L * BT * C);
+  md->res2 = A(L * BT * C);
+  md->ln2 = A(L * BT * C);
   md->ln2_mean = F(L * BT);
   md->ln2_rstd = F(L * BT);
-  md->fch = F(L * BT * 4 * C);
-  md->fchg = F(L * BT * 4 * C);
-  md->res3 = F(L * BT * C);
-  md->lnf = F(BT * C);
+  md->fch = A(L * BT * 4 * C);
+  md->fchg = A(L * BT * 4 * C);
+  md->res3 = A(L * BT * C);
+  md->lnf = A(BT * C);
   md->lnf_mean = F(BT);
   md->lnf_rstd = F(BT);
-  md->logits = F(BT * md->Vp);
+  md->logits = A(BT * md->Vp);
   md->losses = F(BT);
   md->xent_lse = F(BT);
   md->dres = F(BT * C);
-  md->dbuf4 = F(BT * 4 * C);
-  md->dln = F(BT * C);
-  md->datty = F(BT * C);
-  md->dqkv = F(BT * 3 * C);
+  md->dres_h = md->dtype == GPT2_DTYPE_BF16
+                   ? reinterpret_cast<bf16_t*>(take(BT * C * sizeof(bf16_t)))
+                   : nullptr;
+  md->dbuf4 = A(BT * 4 * C);
+  md->dln = A(BT * C);
+  md->datty = A(BT * C);
+  md->dqkv = A(BT * 3 * C);
   md->attn_D = F(NH * BT);
   md->attn_dS = F(attention_ds_scratch_floats(B, T, (int)NH));
-  // split-K workspace: the largest any GEMM of the step asks for
-  size_t ws = 0;
-  {
-    const int iBT = (int)BT, iC = (int)C, iV = md->V;
-    const int oc[4] = {3 * iC, iC, 4 * iC, iC};
-    const int in[4] = {iC, iC, iC, 4 * iC};
-    for (int k = 0; k < 4; k++) {
-      Gemm g;
-      g.M = oc[k];
-      g.N = in[k];
-      g.K = iBT;
-      g.epi = EPI_ACCUM;
-      g.a_trans = true;
-      g.colsum = reinterpret_cast<float*>(16);  // only its presence matters when measuring
-      ws = std::max(ws, gemm_workspace_floats(g));
-      Gemm d;
-      d.M = iBT;
-      d.N = in[k];
-      d.K = oc[k];
-      d.epi = EPI_STORE;
-      ws = std::max(ws, gemm_workspace_floats(d));
-    }
-    // forward: qkv, attproj, fc, fcproj, lm_head (out = M x N with K = in)
-    const int fn[5] = {3 * iC, iC, 4 * iC, iC, iV};
-    const int fk[5] = {iC, iC, iC, 4 * iC, iC};
-    for (int k = 0; k < 5; k++) {
-      Gemm f;
-      f.M = iBT;
-      f.N = fn[k];
-      f.K = fk[k];
-      ws = std::max(ws, gemm_workspace_floats(f));
-    }
-    Gemm d;
-    d.M = iBT;
-    d.N = iC;
-    d.K = iV;
-    ws = std::max(ws, gemm_workspace_floats(d));
-    Gemm w;
-    w.M = iV;
-    w.N = iC;
-    w.K = iBT;
-    w.epi = EPI_ACCUM;
-    ws = std::max(ws, gemm_workspace_floats(w));
-  }
+  const size_t ws = md->dtype == GPT2_DTYPE_BF16
+                        ? step_gemm_workspace<bf16_t>((int)BT, (int)C, md->V)
+                        : step_gemm_workspace<float>((int)BT, (int)C, md->V);
   md->gemm_ws_floats = ws;
   md->gemm_ws = F(ws ? ws : 1);
   md->ln_ws = F(layernorm_partial_floats((int)BT, (int)C));
@@ -267,6 +301,245 @@ int check_err_flag(gpt2_model* md) {
   return GPT2_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+// the training step, for fp32 (T = float) or bf16 (T = bf16_t) activations
+// ---------------------------------------------------------------------------------------
+int ln_backward(gpt2_model* md, float* dx, float* dw, float* db, const float* dout,
+                const float* x, const float* w, const float* mean, const float* rstd, int BT,
+                bool acc) {
+  return layernorm_backward(dx, dw, db, dout, x, w, mean, rstd, BT, md->C, acc, md->ln_ws,
+                            md->stream);
+}
+int ln_backward(gpt2_model* md, float* dx, float* dw, float* db, const bf16_t* dout,
+                const bf16_t* x, const float* w, const float* mean, const float* rstd, int BT,
+                bool acc) {
+  return layernorm_backward(dx, md->dres_h, dw, db, dout, x, w, mean, rstd, BT, md->C, acc,
+                            md->ln_ws, md->stream);
+}
+// the residual-stream gradient as a GEMM operand
+template <typename T> const T* dres_operand(gpt2_model* md);
+template <> const float* dres_operand<float>(gpt2_model* md) { return md->dres; }
+template <> const bf16_t* dres_operand<bf16_t>(gpt2_model* md) { return md->dres_h; }
+
+// "llm.c 的中文注解-20240421" section 1.23 (gpt2_forward), on md->tok / md->tgt
+template <typename T>
+int forward_impl(gpt2_model* md, bool with_targets) {
+  using GT = typename GemmOf<T>::type;
+  const int B = md->B, T_ = md->T, L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T_;
+  const size_t NC = (size_t)BT * C;
+  hipStream_t s = md->stream;
+  T* encoded = act<T>(md->encoded);
+  CHK(encoder_forward(encoded, md->tok, P(md, P_WTE), P(md, P_WPE), B, T_, C, V, md->d_err, s));
+  for (int l = 0; l < L; l++) {
+    const T* x = l == 0 ? encoded : act<T>(md->res3) + (l - 1) * NC;
+    T* ln1 = act<T>(md->ln1) + l * NC;
+    T* qkv = act<T>(md->qkv) + l * 3 * NC;
+    T* atty = act<T>(md->atty) + l * NC;
+    T* res2 = act<T>(md->res2) + l * NC;
+    T* ln2 = act<T>(md->ln2) + l * NC;
+    T* fch = act<T>(md->fch) + l * 4 * NC;
+    T* fchg = act<T>(md->fchg) + l * 4 * NC;
+    T* res3 = act<T>(md->res3) + l * NC;
+    CHK(layernorm_forward(ln1, md->ln1_mean + (size_t)l * BT, md->ln1_rstd + (size_t)l * BT, x,
+                          P(md, P_LN1W) + l * C, P(md, P_LN1B) + l * C, BT, C, s));
+    GT g;  // qkv = ln1 . Wqkv^T + b
+    g.A = ln1;
+    g.lda = C;
+    g.B = W<T>(md, P_QKVW) + (size_t)l * 3 * C * C;
+    g.ldb = C;
+    g.C = qkv;
+    g.ldc = 3 * C;
+    g.bias = P(md, P_QKVB) + (size_t)l * 3 * C;
+    g.M = BT;
+    g.N = 3 * C;
+    g.K = C;
+    CHK(run_gemm(md, g));
+    CHK(attention_forward(atty, md->attn_lse + (size_t)l * NH * BT, qkv, B, T_, C, NH, s));
+    GT pj;  // res2 = x + atty . Wproj^T + b
+    pj.A = atty;
+    pj.lda = C;
+    pj.B = W<T>(md, P_ATTPROJW) + (size_t)l * C * C;
+    pj.ldb = C;
+    pj.C = res2;
+    pj.ldc = C;
+    pj.R = x;
+    pj.bias = P(md, P_ATTPROJB) + (size_t)l * C;
+    pj.M = BT;
+    pj.N = C;
+    pj.K = C;
+    pj.epi = EPI_RESID;
+    CHK(run_gemm(md, pj));
+    CHK(layernorm_forward(ln2, md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, res2,
+                          P(md, P_LN2W) + l * C, P(md, P_LN2B) + l * C, BT, C, s));
+    GT fc;  // fch = ln2 . Wfc^T + b, fchg = gelu(fch)
+    fc.A = ln2;
+    fc.lda = C;
+    fc.B = W<T>(md, P_FCW) + (size_t)l * 4 * C * C;
+    fc.ldb = C;
+    fc.C = fch;
+    fc.C2 = fchg;
+    fc.ldc = 4 * C;
+    fc.bias = P(md, P_FCB) + (size_t)l * 4 * C;
+    fc.M = BT;
+    fc.N = 4 * C;
+    fc.K = C;
+    fc.epi = EPI_GELU;
+    CHK(run_gemm(md, fc));
+    GT fp;  // res3 = res2 + fchg . Wfcproj^T + b
+    fp.A = fchg;
+    fp.lda = 4 * C;
+    fp.B = W<T>(md, P_FCPROJW) + (size_t)l * 4 * C * C;
+    fp.ldb = 4 * C;
+    fp.C = res3;
+    fp.ldc = C;
+    fp.R = res2;
+    fp.bias = P(md, P_FCPROJB) + (size_t)l * C;
+    fp.M = BT;
+    fp.N = C;
+    fp.K = 4 * C;
+    fp.epi = EPI_RESID;
+    CHK(run_gemm(md, fp));
+  }
+  T* lnf = act<T>(md->lnf);
+  CHK(layernorm_forward(lnf, md->lnf_mean, md->lnf_rstd, act<T>(md->res3) + (L - 1) * NC,
+                        P(md, P_LNFW), P(md, P_LNFB), BT, C, s));
+  // tied lm_head: logits = lnf . wte^T, no bias (rows padded to Vp)
+  T* logits = act<T>(md->logits);
+  GT lm;
+  lm.A = lnf;
+  lm.lda = C;
+  lm.B = W<T>(md, P_WTE);
+  lm.ldb = C;
+  lm.C = logits;
+  lm.ldc = md->Vp;
+  lm.M = BT;
+  lm.N = V;
+  lm.K = C;
+  CHK(run_gemm(md, lm));
+  if (with_targets) {
+    CHK(crossentropy_forward(md->losses, md->xent_lse, logits, md->tgt, BT, V, md->Vp,
+                             md->d_err, s));
+    CHK(mean_reduce(md->d_loss, md->losses, BT, s));
+  }
+  return GPT2_OK;
+}
+
+// section 1.25 (gpt2_backward): layers in reverse order; parameter gradients accumulate
+template <typename T>
+int backward_impl(gpt2_model* md) {
+  using GT = typename GemmOf<T>::type;
+  const int B = md->B, T_ = md->T, L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T_;
+  const size_t NC = (size_t)BT * C;
+  hipStream_t s = md->stream;
+  T* logits = act<T>(md->logits);
+  T* dln = act<T>(md->dln);
+  // d(mean loss)/d(loss_bt) = 1/(B*T), through softmax + cross-entropy, in place
+  CHK(crossentropy_backward(logits, md->xent_lse, md->tgt, 1.0f / (float)BT, BT, V, md->Vp, s));
+  {
+    GT d;  // dlnf = dlogits . wte
+    d.A = logits;
+    d.lda = md->Vp;
+    d.B = W<T>(md, P_WTE);
+    d.ldb = C;
+    d.b_trans = true;
+    d.C = dln;
+    d.ldc = C;
+    d.M = BT;
+    d.N = C;
+    d.K = V;
+    CHK(run_gemm(md, d));
+    GT w;  // dwte += dlogits^T . lnf
+    w.A = logits;
+    w.lda = md->Vp;
+    w.a_trans = true;
+    w.B = act<T>(md->lnf);
+    w.ldb = C;
+    w.b_trans = true;
+    w.C = G(md, P_WTE);
+    w.ldc = C;
+    w.M = V;
+    w.N = C;
+    w.K = BT;
+    w.epi = EPI_ACCUM;
+    CHK(run_gemm(md, w));
+  }
+  CHK(ln_backward(md, md->dres, G(md, P_LNFW), G(md, P_LNFB), dln,
+                  act<T>(md->res3) + (L - 1) * NC, P(md, P_LNFW), md->lnf_mean, md->lnf_rstd, BT,
+                  false));
+
+  // one linear layer's backward: dinp = dout . W (optionally times gelu'(pre)),
+  // dW += dout^T . inp, and db += column sums of dout inside the same weight-gradient GEMM
+  auto linear_bwd = [&](T* dinp, const T* gelu_pre, float* dW, float* db, const T* dout,
+                        const T* inp, const T* Wt, int in, int out) -> int {
+    GT d;
+    d.A = dout;
+    d.lda = out;
+    d.B = Wt;
+    d.ldb = in;
+    d.b_trans = true;
+    d.C = dinp;
+    d.ldc = in;
+    d.M = BT;
+    d.N = in;
+    d.K = out;
+    if (gelu_pre) {
+      d.epi = EPI_GELU_BWD;
+      d.R = gelu_pre;
+    }
+    int rc = run_gemm(md, d);
+    if (rc) return rc;
+    GT w;
+    w.A = dout;
+    w.lda = out;
+    w.a_trans = true;
+    w.B = inp;
+    w.ldb = in;
+    w.b_trans = true;
+    w.C = dW;
+    w.ldc = in;
+    w.M = out;
+    w.N = in;
+    w.K = BT;
+    w.epi = EPI_ACCUM;
+    w.colsum = db;
+    return run_gemm(md, w);
+  };
+
+  T* dbuf4 = act<T>(md->dbuf4);
+  T* datty = act<T>(md->datty);
+  T* dqkv = act<T>(md->dqkv);
+  const T* dres = dres_operand<T>(md);
+  for (int l = L - 1; l >= 0; l--) {
+    const T* x = l == 0 ? act<T>(md->encoded) : act<T>(md->res3) + (l - 1) * NC;
+    // MLP: residual3 = residual2 + fcproj(gelu(fc(ln2(residual2))))
+    CHK(linear_bwd(dbuf4, act<T>(md->fch) + l * 4 * NC, G(md, P_FCPROJW) + (size_t)l * 4 * C * C,
+                   G(md, P_FCPROJB) + (size_t)l * C, dres, act<T>(md->fchg) + l * 4 * NC,
+                   W<T>(md, P_FCPROJW) + (size_t)l * 4 * C * C, 4 * C, C));
+    CHK(linear_bwd(dln, nullptr, G(md, P_FCW) + (size_t)l * 4 * C * C,
+                   G(md, P_FCB) + (size_t)l * 4 * C, dbuf4, act<T>(md->ln2) + l * NC,
+                   W<T>(md, P_FCW) + (size_t)l * 4 * C * C, C, 4 * C));
+    CHK(ln_backward(md, md->dres, G(md, P_LN2W) + (size_t)l * C, G(md, P_LN2B) + (size_t)l * C,
+                    dln, act<T>(md->res2) + l * NC, P(md, P_LN2W) + (size_t)l * C,
+                    md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, BT, true));
+    // attention: residual2 = x + attproj(attention(qkv(ln1(x))))
+    CHK(linear_bwd(datty, nullptr, G(md, P_ATTPROJW) + (size_t)l * C * C,
+                   G(md, P_ATTPROJB) + (size_t)l * C, dres, act<T>(md->atty) + l * NC,
+                   W<T>(md, P_ATTPROJW) + (size_t)l * C * C, C, C));
+    CHK(attention_backward(dqkv, datty, act<T>(md->qkv) + l * 3 * NC, act<T>(md->atty) + l * NC,
+                           md->attn_lse + (size_t)l * NH * BT, md->attn_D, md->attn_dS, B, T_, C,
+                           NH, s));
+    CHK(linear_bwd(dln, nullptr, G(md, P_QKVW) + (size_t)l * 3 * C * C,
+                   G(md, P_QKVB) + (size_t)l * 3 * C, dqkv, act<T>(md->ln1) + l * NC,
+                   W<T>(md, P_QKVW) + (size_t)l * 3 * C * C, C, 3 * C));
+    CHK(ln_backward(md, md->dres, G(md, P_LN1W) + (size_t)l * C, G(md, P_LN1B) + (size_t)l * C,
+                    dln, x, P(md, P_LN1W) + (size_t)l * C, md->ln1_mean + (size_t)l * BT,
+                    md->ln1_rstd + (size_t)l * BT, BT, true));
+  }
+  CHK(encoder_backward(G(md, P_WTE), G(md, P_WPE), md->dres, md->tok, B, T_, C, V,
+                       md->sort_scratch, s));
+  return GPT2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,7 +583,7 @@ int gpt2_profile_summary(char* buf, size_t len) {
   return GPT2_OK;
 }
 
-const char* gpt2_version(void) { return "gpt2-mi355x 0.1 (gfx950, fp32 MFMA)"; }
+const char* gpt2_version(void) { return "gpt2-mi355x 0.2 (gfx950, fp32 and bf16 MFMA)"; }
 
 const char* gpt2_last_error(const gpt2_model* md) { return md ? md->err : gpt2::g_err; }
 
@@ -328,12 +601,13 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
                 "(C=%d H=%d)", C, H);
   if ((C / 4 + 63) / 64 > 8)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: C=%d above the supported 2048", C);
-  if (dtype != GPT2_DTYPE_FP32)
+  if (dtype != GPT2_DTYPE_FP32 && dtype != GPT2_DTYPE_BF16)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: dtype %d is not supported", dtype);
   if ((maxB > 0) != (maxTseq > 0) || maxTseq > maxT)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: bad preallocation shape");
 
   gpt2_model* md = new gpt2_model();
+  md->dtype = dtype;
   md->L = L;
   md->C = C;
   md->NH = H;
@@ -355,9 +629,11 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
     o += sizes[k];
   }
   md->nparams = o;
-  // every tensor offset must keep 16-byte alignment for the float4 kernels
+  // every tensor offset must keep 16-byte alignment for the vector kernels (fp32 params;
+  // bf16 weight copy in mixed precision)
+  const size_t align = dtype == GPT2_DTYPE_BF16 ? 8 : 4;
   for (int k = 0; k < 16; k++)
-    if (md->poff[k] % 4) {
+    if (md->poff[k] % align) {
       delete md;
       return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: tensor %d misaligned", k);
     }
@@ -375,6 +651,19 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
   md->m = md->pbuf + 2 * stride;
   md->v = md->pbuf + 3 * stride;
   md->stream = static_cast<hipStream_t>(stream);  // NULL: the null stream
+  if (dtype == GPT2_DTYPE_BF16) {
+    void* q = nullptr;
+    if (hipMalloc(&q, stride * sizeof(bf16_t)) != hipSuccess || !q) {
+      (void)hipGetLastError();
+      gpt2_free(md);
+      return fail(nullptr, GPT2_ERR_OOM, "gpt2_build: cannot allocate the bf16 weight copy");
+    }
+    md->pbf = static_cast<bf16_t*>(q);
+    if (hipMemsetAsync(md->pbf, 0, stride * sizeof(bf16_t), md->stream) != hipSuccess) {
+      gpt2_free(md);
+      return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: memset failed");
+    }
+  }
   if (hipMemsetAsync(md->pbuf, 0, 4 * stride * sizeof(float), md->stream) != hipSuccess) {
     gpt2_free(md);
     return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: memset failed");
@@ -403,6 +692,7 @@ void gpt2_free(gpt2_model* md) {
   if (md->stream) (void)hipStreamSynchronize(md->stream);
   if (md->abuf) (void)hipFree(md->abuf);
   if (md->pbuf) (void)hipFree(md->pbuf);
+  if (md->pbf) (void)hipFree(md->pbf);
   delete md;
 }
 
@@ -442,7 +732,9 @@ static int xfer(gpt2_model* md, float* dev, const float* src, float* dst, int is
 
 int gpt2_set_params(gpt2_model* md, const float* src, int src_is_device) {
   if (md && !src) return fail(md, GPT2_ERR_ARG, "gpt2_set_params: NULL source");
-  return xfer(md, md ? md->params : nullptr, src, nullptr, src_is_device);
+  int rc = xfer(md, md ? md->params : nullptr, src, nullptr, src_is_device);
+  if (!rc && md->pbf) CHK(cast_f32_to_bf16(md->pbf, md->params, md->nparams, md->stream));
+  return rc;
 }
 int gpt2_get_params(gpt2_model* md, float* dst, int dst_is_device) {
   return xfer(md, md ? md->params : nullptr, nullptr, dst, dst_is_device);
@@ -476,6 +768,28 @@ int gpt2_get_losses(gpt2_model* md, float* dst, int dst_is_device) {
 int gpt2_get_logits(gpt2_model* md, float* dst, int dst_is_device) {
   if (!md || !dst) return fail(md, GPT2_ERR_ARG, "gpt2_get_logits: NULL");
   if (!md->logits_valid) return fail(md, GPT2_ERR_STATE, "logits are not available");
+  if (md->dtype == GPT2_DTYPE_BF16) {  // widen the bf16 logits through a temporary
+    const size_t n = (size_t)md->B * md->T * md->Vp;
+    float* tmp = nullptr;
+    if (hipMalloc(&tmp, n * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(md, GPT2_ERR_OOM, "gpt2_get_logits: no memory to widen the logits");
+    }
+    int rc = chk(md, cast_bf16_to_f32(tmp, static_cast<const bf16_t*>(md->logits), n,
+                                      md->stream));
+    hipError_t e = rc ? hipSuccess
+                      : hipMemcpy2DAsync(dst, (size_t)md->V * sizeof(float), tmp,
+                                         (size_t)md->Vp * sizeof(float),
+                                         (size_t)md->V * sizeof(float), (size_t)md->B * md->T,
+                                         dst_is_device ? hipMemcpyDeviceToDevice
+                                                       : hipMemcpyDeviceToHost,
+                                         md->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(md->stream);
+    (void)hipFree(tmp);
+    if (rc) return rc;
+    if (e != hipSuccess) return fail(md, GPT2_ERR_HIP, "gpt2_get_logits: %s", hipGetErrorString(e));
+    return GPT2_OK;
+  }
   HIPCHK(hipMemcpy2DAsync(dst, (size_t)md->V * sizeof(float), md->logits,
                           (size_t)md->Vp * sizeof(float), (size_t)md->V * sizeof(float),
                           (size_t)md->B * md->T,
@@ -499,108 +813,17 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     return fail(md, GPT2_ERR_SHAPE, "gpt2_forward: model is sized for B=%d T=%d, got B=%d T=%d",
                 md->B, md->T, B, T);
   }
-  const int L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T;
-  const size_t NC = (size_t)BT * C;
+  const int BT = B * T;
   hipStream_t s = md->stream;
   md->fwd_targets = false;
   md->logits_valid = false;
   HIPCHK(hipMemcpyAsync(md->tok, tokens, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
   if (targets)
     HIPCHK(hipMemcpyAsync(md->tgt, targets, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
-
-  CHK(encoder_forward(md->encoded, md->tok, P(md, P_WTE), P(md, P_WPE), B, T, C, V, md->d_err, s));
-  for (int l = 0; l < L; l++) {
-    const float* x = l == 0 ? md->encoded : md->res3 + (l - 1) * NC;
-    float* ln1 = md->ln1 + l * NC;
-    float* qkv = md->qkv + l * 3 * NC;
-    float* atty = md->atty + l * NC;
-    float* res2 = md->res2 + l * NC;
-    float* ln2 = md->ln2 + l * NC;
-    float* fch = md->fch + l * 4 * NC;
-    float* fchg = md->fchg + l * 4 * NC;
-    float* res3 = md->res3 + l * NC;
-    CHK(layernorm_forward(ln1, md->ln1_mean + (size_t)l * BT, md->ln1_rstd + (size_t)l * BT, x,
-                          P(md, P_LN1W) + l * C, P(md, P_LN1B) + l * C, BT, C, s));
-    Gemm g;
-    g.A = ln1;
-    g.lda = C;
-    g.B = P(md, P_QKVW) + (size_t)l * 3 * C * C;
-    g.ldb = C;
-    g.C = qkv;
-    g.ldc = 3 * C;
-    g.bias = P(md, P_QKVB) + (size_t)l * 3 * C;
-    g.M = BT;
-    g.N = 3 * C;
-    g.K = C;
-    CHK(gemm(g, md->gemm_ws, md->gemm_ws_floats, s));
-    CHK(attention_forward(atty, md->attn_lse + (size_t)l * NH * BT, qkv, B, T, C, NH, s));
-    Gemm pj;
-    pj.A = atty;
-    pj.lda = C;
-    pj.B = P(md, P_ATTPROJW) + (size_t)l * C * C;
-    pj.ldb = C;
-    pj.C = res2;
-    pj.ldc = C;
-    pj.R = x;
-    pj.bias = P(md, P_ATTPROJB) + (size_t)l * C;
-    pj.M = BT;
-    pj.N = C;
-    pj.K = C;
-    pj.epi = EPI_RESID;
-    CHK(gemm(pj, md->gemm_ws, md->gemm_ws_floats, s));
-    CHK(layernorm_forward(ln2, md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, res2,
-                          P(md, P_LN2W) + l * C, P(md, P_LN2B) + l * C, BT, C, s));
-    Gemm fc;
-    fc.A = ln2;
-    fc.lda = C;
-    fc.B = P(md, P_FCW) + (size_t)l * 4 * C * C;
-    fc.ldb = C;
-    fc.C = fch;
-    fc.C2 = fchg;
-    fc.ldc = 4 * C;
-    fc.bias = P(md, P_FCB) + (size_t)l * 4 * C;
-    fc.M = BT;
-    fc.N = 4 * C;
-    fc.K = C;
-    fc.epi = EPI_GELU;
-    CHK(gemm(fc, md->gemm_ws, md->gemm_ws_floats, s));
-    Gemm fp;
-    fp.A = fchg;
-    fp.lda = 4 * C;
-    fp.B = P(md, P_FCPROJW) + (size_t)l * 4 * C * C;
-    fp.ldb = 4 * C;
-    fp.C = res3;
-    fp.ldc = C;
-    fp.R = res2;
-    fp.bias = P(md, P_FCPROJB) + (size_t)l * C;
-    fp.M = BT;
-    fp.N = C;
-    fp.K = 4 * C;
-    fp.epi = EPI_RESID;
-    CHK(gemm(fp, md->gemm_ws, md->gemm_ws_floats, s));
-  }
-  CHK(layernorm_forward(md->lnf, md->lnf_mean, md->lnf_rstd, md->res3 + (L - 1) * NC,
-                        P(md, P_LNFW), P(md, P_LNFB), BT, C, s));
-  // tied lm_head: logits = lnf . wte^T, no bias (rows padded to Vp floats)
-  Gemm lm;
-  lm.A = md->lnf;
-  lm.lda = C;
-  lm.B = P(md, P_WTE);
-  lm.ldb = C;
-  lm.C = md->logits;
-  lm.ldc = md->Vp;
-  lm.M = BT;
-  lm.N = V;
-  lm.K = C;
-  CHK(gemm(lm, md->gemm_ws, md->gemm_ws_floats, s));
+  if (md->dtype == GPT2_DTYPE_BF16) CHK(forward_impl<bf16_t>(md, targets != nullptr));
+  else CHK(forward_impl<float>(md, targets != nullptr));
   md->logits_valid = true;
-
-  if (targets) {
-    CHK(crossentropy_forward(md->losses, md->xent_lse, md->logits, md->tgt, BT, V, md->Vp,
-                             md->d_err, s));
-    CHK(mean_reduce(md->d_loss, md->losses, BT, s));
-    md->fwd_targets = true;
-  }
+  if (targets) md->fwd_targets = true;
   if (mean_loss) {
     float host = -1.0f;
     if (targets) {
@@ -626,116 +849,9 @@ int gpt2_backward(gpt2_model* md) {
   if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
   if (!md->fwd_targets || !md->logits_valid)
     return fail(md, GPT2_ERR_STATE, "gpt2_backward: needs a forward with targets first");
-  const int B = md->B, T = md->T, L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T;
-  const size_t NC = (size_t)BT * C;
-  hipStream_t s = md->stream;
-  float* ws = md->gemm_ws;
-  const size_t wsn = md->gemm_ws_floats;
-
-  // d(mean loss)/d(loss_bt) = 1/(B*T), through softmax + cross-entropy, in place
-  CHK(crossentropy_backward(md->logits, md->xent_lse, md->tgt, 1.0f / (float)BT, BT, V, md->Vp,
-                            s));
   md->logits_valid = false;
-  {
-    Gemm d;  // dlnf = dlogits . wte
-    d.A = md->logits;
-    d.lda = md->Vp;
-    d.B = P(md, P_WTE);
-    d.ldb = C;
-    d.b_trans = true;
-    d.C = md->dln;
-    d.ldc = C;
-    d.M = BT;
-    d.N = C;
-    d.K = V;
-    CHK(gemm(d, ws, wsn, s));
-    Gemm w;  // dwte += dlogits^T . lnf
-    w.A = md->logits;
-    w.lda = md->Vp;
-    w.a_trans = true;
-    w.B = md->lnf;
-    w.ldb = C;
-    w.b_trans = true;
-    w.C = G(md, P_WTE);
-    w.ldc = C;
-    w.M = V;
-    w.N = C;
-    w.K = BT;
-    w.epi = EPI_ACCUM;
-    CHK(gemm(w, ws, wsn, s));
-  }
-  CHK(layernorm_backward(md->dres, G(md, P_LNFW), G(md, P_LNFB), md->dln, md->res3 + (L - 1) * NC,
-                         P(md, P_LNFW), md->lnf_mean, md->lnf_rstd, BT, C, false, md->ln_ws, s));
-
-  // one linear layer's backward: dinp = dout . W (optionally times gelu'(pre)),
-  // dW += dout^T . inp, and db += column sums of dout inside the same weight-gradient GEMM
-  auto linear_bwd = [&](float* dinp, const float* gelu_pre, float* dW, float* db,
-                        const float* dout, const float* inp, const float* W, int in,
-                        int out) -> int {
-    Gemm d;
-    d.A = dout;
-    d.lda = out;
-    d.B = W;
-    d.ldb = in;
-    d.b_trans = true;
-    d.C = dinp;
-    d.ldc = in;
-    d.M = BT;
-    d.N = in;
-    d.K = out;
-    if (gelu_pre) {
-      d.epi = EPI_GELU_BWD;
-      d.R = gelu_pre;
-    }
-    int rc = gemm(d, ws, wsn, s);
-    if (rc) return rc;
-    Gemm w;
-    w.A = dout;
-    w.lda = out;
-    w.a_trans = true;
-    w.B = inp;
-    w.ldb = in;
-    w.b_trans = true;
-    w.C = dW;
-    w.ldc = in;
-    w.M = out;
-    w.N = in;
-    w.K = BT;
-    w.epi = EPI_ACCUM;
-    w.colsum = db;
-    return gemm(w, ws, wsn, s);
-  };
-
-  for (int l = L - 1; l >= 0; l--) {
-    const float* x = l == 0 ? md->encoded : md->res3 + (l - 1) * NC;
-    // MLP: residual3 = residual2 + fcproj(gelu(fc(ln2(residual2))))
-    CHK(linear_bwd(md->dbuf4, md->fch + l * 4 * NC, G(md, P_FCPROJW) + (size_t)l * 4 * C * C,
-                   G(md, P_FCPROJB) + (size_t)l * C, md->dres, md->fchg + l * 4 * NC,
-                   P(md, P_FCPROJW) + (size_t)l * 4 * C * C, 4 * C, C));
-    CHK(linear_bwd(md->dln, nullptr, G(md, P_FCW) + (size_t)l * 4 * C * C,
-                   G(md, P_FCB) + (size_t)l * 4 * C, md->dbuf4, md->ln2 + l * NC,
-                   P(md, P_FCW) + (size_t)l * 4 * C * C, C, 4 * C));
-    CHK(layernorm_backward(md->dres, G(md, P_LN2W) + (size_t)l * C, G(md, P_LN2B) + (size_t)l * C,
-                           md->dln, md->res2 + l * NC, P(md, P_LN2W) + (size_t)l * C,
-                           md->ln2_mean + (size_t)l * BT, md->ln2_rstd + (size_t)l * BT, BT, C,
-                           true, md->ln_ws, s));
-    // attention: residual2 = x + attproj(attention(qkv(ln1(x))))
-    CHK(linear_bwd(md->datty, nullptr, G(md, P_ATTPROJW) + (size_t)l * C * C,
-                   G(md, P_ATTPROJB) + (size_t)l * C, md->dres, md->atty + l * NC,
-                   P(md, P_ATTPROJW) + (size_t)l * C * C, C, C));
-    CHK(attention_backward(md->dqkv, md->datty, md->qkv + l * 3 * NC, md->atty + l * NC,
-                           md->attn_lse + (size_t)l * NH * BT, md->attn_D, md->attn_dS, B, T, C,
-                           NH, s));
-    CHK(linear_bwd(md->dln, nullptr, G(md, P_QKVW) + (size_t)l * 3 * C * C,
-                   G(md, P_QKVB) + (size_t)l * 3 * C, md->dqkv, md->ln1 + l * NC,
-                   P(md, P_QKVW) + (size_t)l * 3 * C * C, C, 3 * C));
-    CHK(layernorm_backward(md->dres, G(md, P_LN1W) + (size_t)l * C, G(md, P_LN1B) + (size_t)l * C,
-                           md->dln, x, P(md, P_LN1W) + (size_t)l * C,
-                           md->ln1_mean + (size_t)l * BT, md->ln1_rstd + (size_t)l * BT, BT, C,
-                           true, md->ln_ws, s));
-  }
-  CHK(encoder_backward(G(md, P_WTE), G(md, P_WPE), md->dres, md->tok, B, T, C, V,
-                       md->sort_scratch, s));
+  if (md->dtype == GPT2_DTYPE_BF16) CHK(backward_impl<bf16_t>(md));
+  else CHK(backward_impl<float>(md));
   md->has_grads = true;
   return GPT2_OK;
 }
@@ -745,7 +861,7 @@ int gpt2_adamw_step(gpt2_model* md, float lr, float beta1, float beta2, float ep
   if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
   if (t < 1) return fail(md, GPT2_ERR_ARG, "gpt2_adamw_step: t must be >= 1 (got %d)", t);
   if (!md->has_grads) return fail(md, GPT2_ERR_STATE, "gpt2_adamw_step: no gradients yet");
-  CHK(adamw(md->params, md->grads, md->m, md->v, md->nparams, lr, beta1, beta2, eps,
+  CHK(adamw(md->params, md->grads, md->m, md->v, md->pbf, md->nparams, lr, beta1, beta2, eps,
             weight_decay, t, md->stream));
   return GPT2_OK;
 }
@@ -919,10 +1035,126 @@ int gpt2_k_mean(float* out, const float* x, int n, void* stream) {
   return mean_reduce(out, x, n, as_stream(stream));
 }
 
+int gpt2_k_gemm_bf16(void* C, uint16_t* C2, const uint16_t* R, const uint16_t* A,
+                     const uint16_t* B, const float* bias, float* colsum, int M, int N, int K,
+                     int lda, int ldb, int ldc, int a_trans, int b_trans, int epilogue,
+                     void* stream) {
+  if (!C || !A || !B || epilogue < 0 || epilogue > 4)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_k_gemm_bf16: bad argument");
+  GemmBf16 g;
+  g.A = A;
+  g.lda = lda;
+  g.a_trans = a_trans != 0;
+  g.B = B;
+  g.ldb = ldb;
+  g.b_trans = b_trans != 0;
+  g.C = C;
+  g.ldc = ldc;
+  g.C2 = C2;
+  g.R = R;
+  g.bias = bias;
+  g.colsum = colsum;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi = static_cast<Epilogue>(epilogue);
+  hipStream_t s = as_stream(stream);
+  const size_t ws = M > 0 && N > 0 && K > 0 ? gemm_bf16_workspace_floats(g) : 0;
+  float* buf = nullptr;
+  if (ws && hipMalloc(&buf, ws * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = gemm_bf16(g, buf, ws, s);
+  if (buf) {
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(buf);
+  }
+  return rc;
+}
+
+int gpt2_k_encoder_forward_bf16(uint16_t* out, const int32_t* tok, const float* wte,
+                                const float* wpe, int B, int T, int C, int V, int32_t* err_flag,
+                                void* stream) {
+  if (!out || !tok || !wte || !wpe) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return encoder_forward(out, tok, wte, wpe, B, T, C, V, err_flag, as_stream(stream));
+}
+
+int gpt2_k_layernorm_forward_bf16(uint16_t* out, float* mean, float* rstd, const uint16_t* x,
+                                  const float* w, const float* b, int N, int C, void* stream) {
+  if (!out || !x || !w || !b) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return layernorm_forward(out, mean, rstd, x, w, b, N, C, as_stream(stream));
+}
+
+int gpt2_k_layernorm_backward_bf16(float* dx, uint16_t* dx_copy, float* dw, float* db,
+                                   const uint16_t* dout, const uint16_t* x, const float* w,
+                                   const float* mean, const float* rstd, int N, int C,
+                                   void* stream) {
+  if (!dx || !dw || !db || !dout || !x || !w || !mean || !rstd || N < 1 || C < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  float* partial = nullptr;
+  if (hipMalloc(&partial, layernorm_partial_floats(N, C) * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = layernorm_backward(dx, dx_copy, dw, db, dout, x, w, mean, rstd, N, C, true, partial,
+                              s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(partial);
+  return rc;
+}
+
+int gpt2_k_attention_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
+                                  int C, int NH, void* stream) {
+  if (!out || !lse || !qkv) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return attention_forward(out, lse, qkv, B, T, C, NH, as_stream(stream));
+}
+
+int gpt2_k_attention_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                                   const uint16_t* out, const float* lse, int B, int T, int C,
+                                   int NH, void* stream) {
+  if (!dqkv || !dout || !qkv || !out || !lse || B < 1 || T < 1 || NH < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  float* D = nullptr;
+  const size_t nD = (size_t)B * NH * T, nS = attention_ds_scratch_floats(B, T, NH);
+  if (hipMalloc(&D, (nD + nS) * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = attention_backward(dqkv, dout, qkv, out, lse, D, D + nD, B, T, C, NH, s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(D);
+  return rc;
+}
+
+int gpt2_k_crossentropy_forward_bf16(float* losses, float* lse, const uint16_t* logits,
+                                     const int32_t* targets, int N, int V, int ld,
+                                     int32_t* err_flag, void* stream) {
+  if (!losses || !lse || !logits || !targets) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return crossentropy_forward(losses, lse, logits, targets, N, V, ld, err_flag, as_stream(stream));
+}
+
+int gpt2_k_crossentropy_backward_bf16(uint16_t* logits, const float* lse,
+                                      const int32_t* targets, float dloss, int N, int V, int ld,
+                                      void* stream) {
+  if (!logits || !lse || !targets) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return crossentropy_backward(logits, lse, targets, dloss, N, V, ld, as_stream(stream));
+}
+
+int gpt2_k_adamw_bf16(float* p, uint16_t* p_bf16, const float* g, float* m, float* v, size_t n,
+                      float lr, float beta1, float beta2, float eps, float weight_decay, int t,
+                      void* stream) {
+  if (!p || !p_bf16 || !g || !m || !v) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return adamw(p, g, m, v, p_bf16, n, lr, beta1, beta2, eps, weight_decay, t,
+               as_stream(stream));
+}
+
+int gpt2_k_cast_bf16(uint16_t* dst, const float* src, size_t n, void* stream) {
+  if (!dst || !src) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return cast_f32_to_bf16(dst, src, n, as_stream(stream));
+}
+
 int gpt2_k_adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float beta1,
                  float beta2, float eps, float weight_decay, int t, void* stream) {
   if (!p || !g || !m || !v) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
-  return adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, t, as_stream(stream));
+  return adamw(p, g, m, v, nullptr, n, lr, beta1, beta2, eps, weight_decay, t,
+               as_stream(stream));
 }
 
 }  // extern "C"

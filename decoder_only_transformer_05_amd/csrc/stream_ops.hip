@@ -14,8 +14,6 @@
 namespace gpt2 {
 namespace {
 
-GPT2_DEVICE_INLINE f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-GPT2_DEVICE_INLINE void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 // tokens outside [0, V) were reported by the forward; here they read as 0 so that no
 // index leaves its buffer
 GPT2_DEVICE_INLINE int clamp_tok(int v, int V) { return (v < 0 || v >= V) ? 0 : v; }
@@ -29,7 +27,8 @@ int blocks_for(long long n, int per_block, int cap) {
 // ---------------------------------------------------------------------------------------
 // encoder
 // ---------------------------------------------------------------------------------------
-__global__ void encoder_fwd_kernel(float* __restrict__ out, const int32_t* __restrict__ tok,
+template <typename TO>
+__global__ void encoder_fwd_kernel(TO* __restrict__ out, const int32_t* __restrict__ tok,
                                    const float* __restrict__ wte, const float* __restrict__ wpe,
                                    int BT, int T, int C, int V, int32_t* err) {
   const int C4 = C / 4;
@@ -149,11 +148,11 @@ __global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, const float* __
 // ---------------------------------------------------------------------------------------
 // LayerNorm: one wave per row, VPL float4 per lane held in registers
 // ---------------------------------------------------------------------------------------
-template <int VPL>
-__global__ __launch_bounds__(256) void layernorm_fwd_kernel(float* __restrict__ out,
+template <int VPL, typename T>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
                                                             float* __restrict__ mean,
                                                             float* __restrict__ rstd,
-                                                            const float* __restrict__ x,
+                                                            const T* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
                                                             int N, int C) {
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(float* __restrict__ 
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
   const int C4 = C / 4;
-  const float* xr = x + (long long)row * C;
+  const T* xr = x + (long long)row * C;
   f32x4 v[VPL];
   float s = 0.f;
 #pragma unroll
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(float* __restrict__ 
     }
   }
   const float rs = 1.0f / sqrtf(warp_sum(ss) / C + 1e-5f);
-  float* orow = out + (long long)row * C;
+  T* orow = out + (long long)row * C;
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
     const int c4 = lane + 64 * i;
@@ -197,11 +196,13 @@ constexpr int LNB_ROWS = 32;  // rows per workgroup in the backward
 // dx (+)= rstd * (g - mean(g) - n * mean(g*n)), g = w * dout, n = (x - mean) * rstd;
 // per workgroup, partial[blk][0][:] = sum of n*dout, partial[blk][1][:] = sum of dout over
 // its rows (each wave sums its rows in order, then the four waves are added in order).
-template <int VPL>
+// dx is fp32; with bf16 activations dx_copy (if not null) receives dx rounded to bf16.
+template <int VPL, typename T>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
-    float* __restrict__ dx, float* __restrict__ partial, const float* __restrict__ dout,
-    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ mean,
-    const float* __restrict__ rstd, int N, int C, int accumulate) {
+    float* __restrict__ dx, bf16_t* __restrict__ dx_copy, float* __restrict__ partial,
+    const T* __restrict__ dout, const T* __restrict__ x, const float* __restrict__ w,
+    const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C,
+    int accumulate) {
   extern __shared__ float red[];  // [4 waves][2][C]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C4 = C / 4;
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   const int r1 = min(N, r0 + LNB_ROWS);
   for (int row = r0 + wave; row < r1; row += 4) {
     const float mu = mean[row], rs = rstd[row];
-    const float* dyr = dout + (long long)row * C;
-    const float* xr = x + (long long)row * C;
+    const T* dyr = dout + (long long)row * C;
+    const T* xr = x + (long long)row * C;
     f32x4 dy[VPL], nv[VPL];
     float sg = 0.f, sgn = 0.f;
 #pragma unroll
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
         f32x4 d = (wv[i] * dy[i] - mg - nv[i] * mgn) * rs;
         if (accumulate) d += ld4(dxr + 4 * c4);
         st4(dxr + 4 * c4, d);
+        if (dx_copy) st4(dx_copy + (long long)row * C + 4 * c4, d);
         dw[i] += nv[i] * dy[i];
         db[i] += dy[i];
       }
@@ -316,14 +318,15 @@ GPT2_DEVICE_INLINE void lse_merge(float& m, float& s, float m2, float s2) {
   m = mn;
 }
 
+template <typename T>
 __global__ __launch_bounds__(256) void xent_fwd_kernel(float* __restrict__ losses,
                                                        float* __restrict__ lse_out,
-                                                       const float* __restrict__ logits,
+                                                       const T* __restrict__ logits,
                                                        const int32_t* __restrict__ targets,
                                                        int N, int V, int ld, int32_t* err) {
   __shared__ float sm[4], ss[4];
   const int row = blockIdx.x;
-  const float* z = logits + (long long)row * ld;
+  const T* z = logits + (long long)row * ld;
   float m = -INFINITY, s = 0.f;
   const int V4 = (V + 3) / 4;
   for (int c4 = threadIdx.x; c4 < V4; c4 += 256) {
@@ -361,18 +364,19 @@ __global__ __launch_bounds__(256) void xent_fwd_kernel(float* __restrict__ losse
       if (err) *err = 1;
       y = 0;
     }
-    losses[row] = lse - z[y];
+    losses[row] = lse - ld1(z + y);
     lse_out[row] = lse;
   }
 }
 
 // in place: logits[r, v] <- (softmax - onehot(target)) * dloss for v < V, 0 on the padding
-__global__ __launch_bounds__(256) void xent_bwd_kernel(float* __restrict__ logits,
+template <typename T>
+__global__ __launch_bounds__(256) void xent_bwd_kernel(T* __restrict__ logits,
                                                        const float* __restrict__ lse,
                                                        const int32_t* __restrict__ targets,
                                                        float dloss, int N, int V, int ld) {
   const int row = blockIdx.x;
-  float* z = logits + (long long)row * ld;
+  T* z = logits + (long long)row * ld;
   const float l = lse[row];
   int y = targets[row];
   if (y < 0 || y >= V) y = 0;
@@ -408,10 +412,12 @@ __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
 // ---------------------------------------------------------------------------------------
 // AdamW
 // ---------------------------------------------------------------------------------------
+// pbf (if not null) receives the updated parameters rounded to bf16
 __global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
-                             float* __restrict__ m, float* __restrict__ v, long long n4,
-                             long long n, float lr, float b1, float b2, float eps, float wd,
-                             float inv_c1, float inv_c2) {
+                             float* __restrict__ m, float* __restrict__ v,
+                             bf16_t* __restrict__ pbf, long long n4, long long n, float lr,
+                             float b1, float b2, float eps, float wd, float inv_c1,
+                             float inv_c2) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
        i += (long long)gridDim.x * blockDim.x) {
     f32x4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
@@ -425,6 +431,7 @@ __global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
     st4(p + 4 * i, pp);
     st4(m + 4 * i, mm);
     st4(v + 4 * i, vv);
+    if (pbf) st4(pbf + 4 * i, pp);
   }
   // scalar tail (n not a multiple of 4)
   if (blockIdx.x == 0 && threadIdx.x < (n - 4 * n4)) {
@@ -435,6 +442,20 @@ __global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
     m[i] = mm;
     v[i] = vv;
     p[i] -= lr * ((mm * inv_c1) / (sqrtf(vv * inv_c2) + eps) + wd * p[i]);
+    if (pbf) pbf[i] = f32_to_bf16(p[i]);
+  }
+}
+
+// fp32 <-> bf16 copies (round to nearest even)
+template <typename TD, typename TS>
+__global__ void cast_kernel(TD* __restrict__ dst, const TS* __restrict__ src, long long n) {
+  const long long n4 = n / 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x)
+    st4(dst + 4 * i, ld4(src + 4 * i));
+  if (blockIdx.x == 0 && threadIdx.x < n - 4 * n4) {
+    const long long i = 4 * n4 + threadIdx.x;
+    st1(dst + i, ld1(src + i));
   }
 }
 
@@ -442,19 +463,33 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-int encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe, int B,
-                    int T, int C, int V, int32_t* err_flag, hipStream_t stream) {
+namespace {
+template <typename TO>
+int encoder_forward_t(TO* out, const int32_t* tok, const float* wte, const float* wpe, int B,
+                      int T, int C, int V, int32_t* err_flag, hipStream_t stream,
+                      const char* name) {
   if (B < 1 || T < 1 || C < 4 || C % 4 || V < 1 || !aligned16(out) || !aligned16(wte) ||
       !aligned16(wpe)) {
     set_global_error("encoder_forward: bad arguments");
     return -1;
   }
   const long long n = (long long)B * T * (C / 4);
-  ProfScope ps("encoder_fwd_kernel", (double)B * T * C, 4.0 * (3.0 * B * T * C + B * T), stream);
-  encoder_fwd_kernel<<<blocks_for(n, 256, 8192), 256, 0, stream>>>(out, tok, wte, wpe, B * T, T,
-                                                                  C, V, err_flag);
+  ProfScope ps(name, (double)B * T * C, (8.0 + sizeof(TO)) * B * T * C + 4.0 * B * T, stream);
+  encoder_fwd_kernel<TO><<<blocks_for(n, 256, 8192), 256, 0, stream>>>(out, tok, wte, wpe, B * T,
+                                                                      T, C, V, err_flag);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+}  // namespace
+
+int encoder_forward(float* out, const int32_t* tok, const float* wte, const float* wpe, int B,
+                    int T, int C, int V, int32_t* err_flag, hipStream_t stream) {
+  return encoder_forward_t(out, tok, wte, wpe, B, T, C, V, err_flag, stream, "encoder_fwd_kernel");
+}
+int encoder_forward(bf16_t* out, const int32_t* tok, const float* wte, const float* wpe, int B,
+                    int T, int C, int V, int32_t* err_flag, hipStream_t stream) {
+  return encoder_forward_t(out, tok, wte, wpe, B, T, C, V, err_flag, stream,
+                           "encoder_fwd_bf16_kernel");
 }
 
 size_t encoder_sort_scratch_ints(int BT, int V) { return (size_t)2 * V + BT; }
@@ -498,29 +533,46 @@ int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t*
     default: break;                 \
   }
 
-int layernorm_forward(float* out, float* mean, float* rstd, const float* x, const float* w,
-                      const float* b, int N, int C, hipStream_t stream) {
+namespace {
+template <typename T>
+int layernorm_forward_t(T* out, float* mean, float* rstd, const T* x, const float* w,
+                        const float* b, int N, int C, hipStream_t stream, const char* name) {
   const int vpl = (C / 4 + 63) / 64;
   if (N < 1 || C < 4 || C % 4 || vpl > 8 || !aligned16(out) || !aligned16(x)) {
     set_global_error("layernorm_forward: unsupported N=%d C=%d", N, C);
     return -1;
   }
   const int grid = (N + 3) / 4;
-  ProfScope ps("layernorm_fwd_kernel", 8.0 * N * C, 4.0 * (2.0 * N * C + 2.0 * N + 2.0 * C), stream);
-#define GPT2_LNF(V) layernorm_fwd_kernel<V><<<grid, 256, 0, stream>>>(out, mean, rstd, x, w, b, N, C)
+  ProfScope ps(name, 8.0 * N * C, 2.0 * sizeof(T) * N * C + 8.0 * N + 8.0 * C, stream);
+#define GPT2_LNF(V) \
+  layernorm_fwd_kernel<V, T><<<grid, 256, 0, stream>>>(out, mean, rstd, x, w, b, N, C)
   GPT2_LN_DISPATCH(vpl, GPT2_LNF)
 #undef GPT2_LNF
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+}  // namespace
+
+int layernorm_forward(float* out, float* mean, float* rstd, const float* x, const float* w,
+                      const float* b, int N, int C, hipStream_t stream) {
+  return layernorm_forward_t(out, mean, rstd, x, w, b, N, C, stream, "layernorm_fwd_kernel");
+}
+int layernorm_forward(bf16_t* out, float* mean, float* rstd, const bf16_t* x, const float* w,
+                      const float* b, int N, int C, hipStream_t stream) {
+  return layernorm_forward_t(out, mean, rstd, x, w, b, N, C, stream,
+                             "layernorm_fwd_bf16_kernel");
 }
 
 size_t layernorm_partial_floats(int N, int C) {
   return (size_t)((N + LNB_ROWS - 1) / LNB_ROWS) * 2 * C;
 }
 
-int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const float* x,
-                       const float* w, const float* mean, const float* rstd, int N, int C,
-                       bool accumulate_dx, float* partial, hipStream_t stream) {
+namespace {
+template <typename T>
+int layernorm_backward_t(float* dx, bf16_t* dx_copy, float* dw, float* db, const T* dout,
+                         const T* x, const float* w, const float* mean, const float* rstd, int N,
+                         int C, bool accumulate_dx, float* partial, hipStream_t stream,
+                         const char* name) {
   const int vpl = (C / 4 + 63) / 64;
   if (N < 1 || C < 4 || C % 4 || vpl > 8) {
     set_global_error("layernorm_backward: unsupported N=%d C=%d", N, C);
@@ -529,13 +581,14 @@ int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const
   const int blocks = (N + LNB_ROWS - 1) / LNB_ROWS;
   const size_t lds = (size_t)8 * C * sizeof(float);
   {
-  ProfScope ps("layernorm_bwd_kernel", 14.0 * N * C,
-               4.0 * ((accumulate_dx ? 4.0 : 3.0) * N * C + 2.0 * N + (double)blocks * 2 * C),
-               stream);
-#define GPT2_LNB(V)                                                                        \
-  layernorm_bwd_kernel<V><<<blocks, 256, lds, stream>>>(dx, partial, dout, x, w, mean, rstd, N, \
-                                                        C, accumulate_dx ? 1 : 0)
-  GPT2_LN_DISPATCH(vpl, GPT2_LNB)
+    ProfScope ps(name, 14.0 * N * C,
+                 (2.0 * sizeof(T) + (accumulate_dx ? 8.0 : 4.0) + (dx_copy ? 2.0 : 0.0)) * N * C +
+                     8.0 * N + 8.0 * blocks * C,
+                 stream);
+#define GPT2_LNB(V)                                                                          \
+  layernorm_bwd_kernel<V, T><<<blocks, 256, lds, stream>>>(dx, dx_copy, partial, dout, x, w,   \
+                                                           mean, rstd, N, C, accumulate_dx ? 1 : 0)
+    GPT2_LN_DISPATCH(vpl, GPT2_LNB)
 #undef GPT2_LNB
   }
   ProfScope ps("layernorm_bwd_final_kernel", 2.0 * blocks * C, 4.0 * (2.0 * blocks * C + 4.0 * C),
@@ -544,29 +597,69 @@ int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
+}  // namespace
 
-int crossentropy_forward(float* losses, float* lse, const float* logits, const int32_t* targets,
-                         int N, int V, int ld, int32_t* err_flag, hipStream_t stream) {
+int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const float* x,
+                       const float* w, const float* mean, const float* rstd, int N, int C,
+                       bool accumulate_dx, float* partial, hipStream_t stream) {
+  return layernorm_backward_t(dx, (bf16_t*)nullptr, dw, db, dout, x, w, mean, rstd, N, C,
+                              accumulate_dx, partial, stream, "layernorm_bwd_kernel");
+}
+int layernorm_backward(float* dx, bf16_t* dx_copy, float* dw, float* db, const bf16_t* dout,
+                       const bf16_t* x, const float* w, const float* mean, const float* rstd,
+                       int N, int C, bool accumulate_dx, float* partial, hipStream_t stream) {
+  return layernorm_backward_t(dx, dx_copy, dw, db, dout, x, w, mean, rstd, N, C, accumulate_dx,
+                              partial, stream, "layernorm_bwd_bf16_kernel");
+}
+
+namespace {
+template <typename T>
+int crossentropy_forward_t(float* losses, float* lse, const T* logits, const int32_t* targets,
+                           int N, int V, int ld, int32_t* err_flag, hipStream_t stream,
+                           const char* name) {
   if (N < 1 || V < 1 || ld < V || ld % 4 || !aligned16(logits)) {
     set_global_error("crossentropy_forward: bad arguments");
     return -1;
   }
-  ProfScope ps("xent_fwd_kernel", 3.0 * N * V, 4.0 * ((double)N * V + 3.0 * N), stream);
-  xent_fwd_kernel<<<N, 256, 0, stream>>>(losses, lse, logits, targets, N, V, ld, err_flag);
+  ProfScope ps(name, 3.0 * N * V, (double)sizeof(T) * N * V + 12.0 * N, stream);
+  xent_fwd_kernel<T><<<N, 256, 0, stream>>>(losses, lse, logits, targets, N, V, ld, err_flag);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
 
-int crossentropy_backward(float* logits, const float* lse, const int32_t* targets, float dloss,
-                          int N, int V, int ld, hipStream_t stream) {
+template <typename T>
+int crossentropy_backward_t(T* logits, const float* lse, const int32_t* targets, float dloss,
+                            int N, int V, int ld, hipStream_t stream, const char* name) {
   if (N < 1 || V < 1 || ld < V || ld % 4 || !aligned16(logits)) {
     set_global_error("crossentropy_backward: bad arguments");
     return -1;
   }
-  ProfScope ps("xent_bwd_kernel", 3.0 * N * V, 4.0 * (2.0 * N * ld + 2.0 * N), stream);
-  xent_bwd_kernel<<<N, 256, 0, stream>>>(logits, lse, targets, dloss, N, V, ld);
+  ProfScope ps(name, 3.0 * N * V, 2.0 * sizeof(T) * N * ld + 8.0 * N, stream);
+  xent_bwd_kernel<T><<<N, 256, 0, stream>>>(logits, lse, targets, dloss, N, V, ld);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+}  // namespace
+
+int crossentropy_forward(float* losses, float* lse, const float* logits, const int32_t* targets,
+                         int N, int V, int ld, int32_t* err_flag, hipStream_t stream) {
+  return crossentropy_forward_t(losses, lse, logits, targets, N, V, ld, err_flag, stream,
+                                "xent_fwd_kernel");
+}
+int crossentropy_forward(float* losses, float* lse, const bf16_t* logits, const int32_t* targets,
+                         int N, int V, int ld, int32_t* err_flag, hipStream_t stream) {
+  return crossentropy_forward_t(losses, lse, logits, targets, N, V, ld, err_flag, stream,
+                                "xent_fwd_bf16_kernel");
+}
+int crossentropy_backward(float* logits, const float* lse, const int32_t* targets, float dloss,
+                          int N, int V, int ld, hipStream_t stream) {
+  return crossentropy_backward_t(logits, lse, targets, dloss, N, V, ld, stream,
+                                 "xent_bwd_kernel");
+}
+int crossentropy_backward(bf16_t* logits, const float* lse, const int32_t* targets, float dloss,
+                          int N, int V, int ld, hipStream_t stream) {
+  return crossentropy_backward_t(logits, lse, targets, dloss, N, V, ld, stream,
+                                 "xent_bwd_bf16_kernel");
 }
 
 int mean_reduce(float* out, const float* x, int n, hipStream_t stream) {
@@ -577,19 +670,46 @@ int mean_reduce(float* out, const float* x, int n, hipStream_t stream) {
   return 0;
 }
 
-int adamw(float* p, const float* g, float* m, float* v, size_t n, float lr, float beta1,
-          float beta2, float eps, float wd, int t, hipStream_t stream) {
-  if (t < 1 || !aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v)) {
+int adamw(float* p, const float* g, float* m, float* v, bf16_t* pbf, size_t n, float lr,
+          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream) {
+  if (t < 1 || !aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v) ||
+      (pbf && ((uintptr_t)pbf & 7))) {
     set_global_error("adamw: bad arguments (t=%d)", t);
     return -1;
   }
   const long long n4 = (long long)(n / 4);
   const float inv_c1 = (float)(1.0 / (1.0 - pow((double)beta1, t)));
   const float inv_c2 = (float)(1.0 / (1.0 - pow((double)beta2, t)));
-  ProfScope ps("adamw_kernel", 12.0 * n, 28.0 * n, stream);
-  adamw_kernel<<<blocks_for(n4, 256, 16384), 256, 0, stream>>>(p, g, m, v, n4, (long long)n, lr,
-                                                               beta1, beta2, eps, wd, inv_c1,
+  ProfScope ps("adamw_kernel", 12.0 * n, (pbf ? 30.0 : 28.0) * n, stream);
+  adamw_kernel<<<blocks_for(n4, 256, 16384), 256, 0, stream>>>(p, g, m, v, pbf, n4, (long long)n,
+                                                               lr, beta1, beta2, eps, wd, inv_c1,
                                                                inv_c2);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int cast_f32_to_bf16(bf16_t* dst, const float* src, size_t n, hipStream_t stream) {
+  if (((uintptr_t)dst & 7) || !aligned16(src)) {
+    set_global_error("cast: misaligned buffers");
+    return -1;
+  }
+  if (n == 0) return 0;
+  ProfScope ps("cast_kernel", 0.0, 6.0 * n, stream);
+  cast_kernel<<<blocks_for((long long)n / 4 + 1, 256, 16384), 256, 0, stream>>>(dst, src,
+                                                                                 (long long)n);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int cast_bf16_to_f32(float* dst, const bf16_t* src, size_t n, hipStream_t stream) {
+  if (!aligned16(dst) || ((uintptr_t)src & 7)) {
+    set_global_error("cast: misaligned buffers");
+    return -1;
+  }
+  if (n == 0) return 0;
+  ProfScope ps("cast_kernel", 0.0, 6.0 * n, stream);
+  cast_kernel<<<blocks_for((long long)n / 4 + 1, 256, 16384), 256, 0, stream>>>(dst, src,
+                                                                                 (long long)n);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }

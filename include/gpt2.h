@@ -44,7 +44,17 @@ enum {
   GPT2_ERR_HIP = -6    /* a HIP runtime call failed */
 };
 
-enum { GPT2_DTYPE_FP32 = 0 };
+/* Arithmetic of the training step.
+ * GPT2_DTYPE_FP32: every tensor fp32, GEMMs on fp32 MFMA.
+ * GPT2_DTYPE_BF16: mixed precision, the extension to "fp16 or lower" that the llm.c
+ *   overview names as a next step: GEMM operands (a bf16 copy of the weights, refreshed
+ *   by every gpt2_set_params and gpt2_adamw_step) and all activation tensors are stored
+ *   as bf16 (round to nearest even) and multiplied on bf16 MFMA with fp32 accumulation;
+ *   LayerNorm statistics, softmax and cross-entropy reductions, the losses, the residual-
+ *   stream gradient, the parameter gradients, the master parameters and the AdamW moments
+ *   stay fp32. The ABI is unchanged: parameters, gradients, logits and losses are read
+ *   and written as fp32. */
+enum { GPT2_DTYPE_FP32 = 0, GPT2_DTYPE_BF16 = 1 };
 
 /* ---------------------------------------------------------------------------------------
  * Model lifetime and parameters
@@ -59,7 +69,8 @@ enum { GPT2_DTYPE_FP32 = 0 };
  * *out receives the handle, or NULL on error. */
 int gpt2_build(gpt2_model** out, int L, int C, int H, int V, int maxT);
 
-/* As gpt2_build, plus: dtype (GPT2_DTYPE_FP32 only); if maxB > 0 and maxTseq > 0 the
+/* As gpt2_build, plus: dtype (GPT2_DTYPE_FP32 or GPT2_DTYPE_BF16; bf16 also needs every
+ * parameter tensor to start at a multiple of 8 elements); if maxB > 0 and maxTseq > 0 the
  * activation block is allocated now for exactly B = maxB, T = maxTseq; stream is the
  * hipStream_t the model enqueues all its work on (NULL = the null stream). */
 int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dtype,
@@ -217,6 +228,68 @@ int gpt2_k_mean(float* out, const float* x, int n, void* stream);
 /* [llm.c] 1.26: AdamW over n elements of p, g, m, v (see gpt2_adamw_step). */
 int gpt2_k_adamw(float* p, const float* g, float* m, float* v, size_t n, float lr,
                  float beta1, float beta2, float eps, float weight_decay, int t, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * bf16 forms of the kernels used by GPT2_DTYPE_BF16. Tensors named bf16 are arrays of
+ * uint16_t holding the upper half of an IEEE fp32 value; results rounded to bf16 use
+ * round to nearest even. Statistics, losses, lse and gradients of parameters stay fp32.
+ * ------------------------------------------------------------------------------------- */
+
+/* [llm.c] 1.5, 1.6 (+1.9, 1.10, 1.11 fused) on bf16 operands with fp32 accumulation:
+ * C (M,N) = op(A) . op(B). a_trans = 0: A stored (M,K) row-major (row stride lda);
+ * 1: A stored (K,M). b_trans = 0: B stored (N,K) (a weight (out,in)); 1: B stored (K,N).
+ * epilogue: 0 C = acc + bias; 1 C = acc + bias and C2 = gelu(acc + bias) (tanh form);
+ * 2 C = R + acc + bias; 3 C += acc with C fp32 (gradient accumulation); 4 C = acc *
+ * gelu'(R). C, C2 and R are bf16 with row stride ldc except for epilogue 3. bias (N, fp32)
+ * may be NULL. colsum (M, fp32, may be NULL, needs a_trans) += sums over k of op(A)(m,k).
+ * All pointers device, 16-byte aligned; lda, ldb multiples of 8; ldc a multiple of 8 (4
+ * for epilogue 3). */
+int gpt2_k_gemm_bf16(void* C, uint16_t* C2, const uint16_t* R, const uint16_t* A,
+                     const uint16_t* B, const float* bias, float* colsum, int M, int N, int K,
+                     int lda, int ldb, int ldc, int a_trans, int b_trans, int epilogue,
+                     void* stream);
+
+/* [llm.c] 1.1 with a bf16 result: out (B,T,C) bf16 = wte[tok] + wpe[t] (fp32 tables). */
+int gpt2_k_encoder_forward_bf16(uint16_t* out, const int32_t* tok, const float* wte,
+                                const float* wpe, int B, int T, int C, int V,
+                                int32_t* err_flag, void* stream);
+
+/* [llm.c] 1.3 on bf16 rows: x, out (N,C) bf16; w, b, mean, rstd fp32 (mean, rstd may be
+ * NULL); statistics in fp32. */
+int gpt2_k_layernorm_forward_bf16(uint16_t* out, float* mean, float* rstd, const uint16_t* x,
+                                  const float* w, const float* b, int N, int C, void* stream);
+
+/* [llm.c] 1.4 with bf16 dout and x: dx (N,C) fp32 += the LN backward, dx_copy (N,C) bf16
+ * (may be NULL) receives the new dx rounded to bf16; dw, db (C) fp32 +=. */
+int gpt2_k_layernorm_backward_bf16(float* dx, uint16_t* dx_copy, float* dw, float* db,
+                                   const uint16_t* dout, const uint16_t* x, const float* w,
+                                   const float* mean, const float* rstd, int N, int C,
+                                   void* stream);
+
+/* [llm.c] 1.7, 1.8 with bf16 qkv, out, dout and dqkv (lse fp32); products in fp32. */
+int gpt2_k_attention_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
+                                  int C, int NH, void* stream);
+int gpt2_k_attention_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                                   const uint16_t* out, const float* lse, int B, int T, int C,
+                                   int NH, void* stream);
+
+/* [llm.c] 1.13 - 1.15 on bf16 logits (row stride ld, a multiple of 4); losses, lse fp32;
+ * the backward writes bf16 dlogits in place. */
+int gpt2_k_crossentropy_forward_bf16(float* losses, float* lse, const uint16_t* logits,
+                                     const int32_t* targets, int N, int V, int ld,
+                                     int32_t* err_flag, void* stream);
+int gpt2_k_crossentropy_backward_bf16(uint16_t* logits, const float* lse,
+                                      const int32_t* targets, float dloss, int N, int V, int ld,
+                                      void* stream);
+
+/* AdamW as gpt2_k_adamw, also writing the updated parameters rounded to bf16 into p_bf16
+ * (n elements, 8-byte aligned). */
+int gpt2_k_adamw_bf16(float* p, uint16_t* p_bf16, const float* g, float* m, float* v, size_t n,
+                      float lr, float beta1, float beta2, float eps, float weight_decay, int t,
+                      void* stream);
+
+/* dst (n, bf16) = src (n, fp32) rounded to nearest even. */
+int gpt2_k_cast_bf16(uint16_t* dst, const float* src, size_t n, void* stream);
 
 #ifdef __cplusplus
 }
