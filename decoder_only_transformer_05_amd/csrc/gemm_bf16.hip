@@ -10,7 +10,7 @@
 // master gradients, GELU backward), computed in fp32 and rounded once to bf16 on store.
 //
 // Tiling: 256-thread workgroups own 128x128 tiles of C, each wave a 64x64 sub-tile (2x2
-// MFMA blocks of 32x32); K advances 64 at a time through two LDS buffers per operand. Both
+// MFMA blocks of 32x32); K advances 64 at a time through one LDS buffer per operand. Both
 // operands sit in LDS as [row][k] with k contiguous (128-byte rows), because each lane of
 // the bf16 MFMA supplies 8 consecutive k of one row. Operands stored with K contiguous are
 // copied in 16-byte pieces; operands stored (K, rows) are transposed on the way: a thread
@@ -94,7 +94,8 @@ struct SlabLoader {
     }
   }
 
-  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+  // `tail`: this slab reaches past kend (the same for the whole workgroup)
+  __device__ __forceinline__ void store(bf16_t* S, int tid, bool tail) const {
     if (!TRANS) {
       const int c = tid & 7;
       const int kg = k0 + 8 * c;
@@ -102,7 +103,7 @@ struct SlabLoader {
       for (int i = 0; i < 4; i++) {
         const int row = (tid >> 3) + 32 * i;
         u32x4 x = v[i];
-        if (kg + 8 > kend) {
+        if (tail) {
 #pragma unroll
           for (int q = 0; q < 4; q++) x[q] = mask_pair(x[q], kg + 2 * q, kend);
         }
@@ -113,7 +114,7 @@ struct SlabLoader {
       const int kg = k0 + 4 * kq;
       u32x4 x[4];
 #pragma unroll
-      for (int j = 0; j < 4; j++) x[j] = kg + j < kend ? v[j] : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; j++) x[j] = (!tail || kg + j < kend) ? v[j] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         const int q = e >> 1;
@@ -183,9 +184,9 @@ __device__ __forceinline__ void epilogue4(const Args& g, void* Cv, int m, int n,
 }
 
 template <bool AT, bool BT, bool CF32, int EPI>
-__global__ __launch_bounds__(NTHREADS, 2) void gemm_bf16_kernel(Args g) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BK];
+__global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[1][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[1][BN * BK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -218,54 +219,63 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_bf16_kernel(Args g) {
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
+  // One LDS buffer (32 KB), so three workgroups fit on a CU: the next slab's global loads
+  // are issued into registers before the current slab's MFMAs and written to LDS after a
+  // barrier.
   SlabLoader<AT> la;
   SlabLoader<BT> lb;
-  if (nslabs > 0) {
-    la.load(g.A, g.lda, m0, g.M, kbeg, kend, tid);
-    lb.load(g.B, g.ldb, n0, g.N, kbeg, kend, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nslabs; kt++) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nslabs;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
-      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
-    }
+  auto compute = [&]() {
+    // all of this slab's fragments first, then its 16 MFMAs
+    bf16x8 af[BK / 16][2], bfr[BK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ks++) {
       const int c = 2 * ks + h;
-      bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int q = 0; q < 2; q++) {
-        af[q] = *reinterpret_cast<const bf16x8*>(&As[cur][lds_off(wm0 + 32 * q + r, c)]);
-        bfr[q] = *reinterpret_cast<const bf16x8*>(&Bs[cur][lds_off(wn0 + 32 * q + r, c)]);
+        af[ks][q] = *reinterpret_cast<const bf16x8*>(&As[0][lds_off(wm0 + 32 * q + r, c)]);
+        bfr[ks][q] = *reinterpret_cast<const bf16x8*>(&Bs[0][lds_off(wn0 + 32 * q + r, c)]);
       }
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++)
 #pragma unroll
       for (int tm = 0; tm < 2; tm++)
 #pragma unroll
         for (int tn = 0; tn < 2; tn++)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn], 0, 0, 0);
-    }
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][tn], af[ks][tm],
+                                                                acc[tm][tn], 0, 0, 0);
     if (do_colsum) {  // row m of the A tile, k chunks 4*half .. 4*half+3 of this slab
       const int m = tid & (BM - 1), half = tid >> 7;
 #pragma unroll
       for (int cc = 0; cc < 4; cc++) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&As[cur][lds_off(m, 4 * half + cc)]);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&As[0][lds_off(m, 4 * half + cc)]);
 #pragma unroll
         for (int q = 0; q < 4; q++)
           csum += __uint_as_float(x[q] << 16) + __uint_as_float(x[q] & 0xFFFF0000u);
       }
     }
+  };
+  if (nslabs > 0) {
+    la.load(g.A, g.lda, m0, g.M, kbeg, kend, tid);
+    lb.load(g.B, g.ldb, n0, g.N, kbeg, kend, tid);
+    la.store(As[0], tid, kbeg + BK > kend);
+    lb.store(Bs[0], tid, kbeg + BK > kend);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nslabs; kt++) {
+    const bool more = kt + 1 < nslabs;
     if (more) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+      la.load(g.A, g.lda, m0, g.M, kbeg + (kt + 1) * BK, kend, tid);
+      lb.load(g.B, g.ldb, n0, g.N, kbeg + (kt + 1) * BK, kend, tid);
     }
+    compute();
     __syncthreads();
+    if (more) {
+      const bool tail = kbeg + (kt + 2) * BK > kend;
+      la.store(As[0], tid, tail);
+      lb.store(Bs[0], tid, tail);
+      __syncthreads();
+    }
   }
 
   if (do_colsum) {
@@ -364,7 +374,7 @@ void launch(const Args& a, bool at, bool bt, int epi, bool cf32, dim3 grid, hipS
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// K splits from a wave-quantisation cost model (two 256-thread workgroups per CU, 512
+// K splits from a wave-quantisation cost model (three 256-thread workgroups per CU, 768
 // slots), compute at half the bf16 MFMA peak, split partials and their reduction at 5 TB/s.
 int choose_splits(const GemmBf16& g) {
   const double tiles = (double)ceil_div(g.M, BM) * ceil_div(g.N, BN);
@@ -377,7 +387,7 @@ int choose_splits(const GemmBf16& g) {
     const int kper = ceil_div(kt, s);
     if (s > 1 && kper < 4) break;
     if (s > 1 && ceil_div(kt, kper) != s) continue;
-    const double rounds = tiles * s / 512.0;
+    const double rounds = tiles * s / 768.0;
     const double q = std::ceil(rounds) / rounds;
     double cost = t_mfma * q;
     if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;
