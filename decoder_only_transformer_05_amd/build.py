@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libgpt2_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["gemm.hip", "gemm_bf16.hip", "attention.hip", "stream_ops.hip", "model.hip"]
+SOURCES = ["gemm.hip", "gemm_bf16.hip", "attention.hip", "attention_bf16.hip", "stream_ops.hip",
+           "model.hip"]
 ARCH = os.environ.get("GPT2_OFFLOAD_ARCH", "gfx950")
 
 

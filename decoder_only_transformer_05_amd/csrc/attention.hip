@@ -475,6 +475,32 @@ size_t attention_ds_scratch_floats(int B, int T, int NH) {
 }
 
 namespace {
+// D = rowsum(dout * out) per (b, head, query), fp32, into D (B, NH, T)
+template <typename TS>
+int rowdot_t(float* D, const TS* dout, const TS* out, int B, int T, int C, int NH,
+             hipStream_t stream) {
+  const int hs = C / NH;
+  const long long rows = (long long)B * NH * T;
+  const double BTC = (double)B * T * C;
+  ProfScope ps(sizeof(TS) == 4 ? "attn_bwd_rowdot_kernel" : "attn_bwd_rowdot_bf16_kernel",
+               2.0 * BTC, (double)sizeof(TS) * 2.0 * BTC + 4.0 * rows, stream);
+  const long long n4 = (long long)B * T * (C / 4);
+  const unsigned blocks = (unsigned)((n4 + 255) / 256);
+  switch (hs / 4) {
+    case 1: attn_bwd_rowdot_kernel<1, TS><<<blocks, 256, 0, stream>>>(D, dout, out, B, T, C, NH); break;
+    case 2: attn_bwd_rowdot_kernel<2, TS><<<blocks, 256, 0, stream>>>(D, dout, out, B, T, C, NH); break;
+    case 4: attn_bwd_rowdot_kernel<4, TS><<<blocks, 256, 0, stream>>>(D, dout, out, B, T, C, NH); break;
+    case 8: attn_bwd_rowdot_kernel<8, TS><<<blocks, 256, 0, stream>>>(D, dout, out, B, T, C, NH); break;
+    case 16: attn_bwd_rowdot_kernel<16, TS><<<blocks, 256, 0, stream>>>(D, dout, out, B, T, C, NH); break;
+    case 32: attn_bwd_rowdot_kernel<32, TS><<<blocks, 256, 0, stream>>>(D, dout, out, B, T, C, NH); break;
+    default:
+      attn_bwd_rowdot_generic_kernel<TS><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+          D, dout, out, B, T, C, NH, hs);
+  }
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
 template <typename TS>
 int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
                          const float* lse, float* dscratch, float* ds_scratch, int B, int T,
@@ -491,23 +517,8 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
   const float scale_log2 = scale * kLog2e;
   const long long rows = (long long)B * NH * T;
   const double BTC = (double)B * T * C, tri = (double)T * (T + 1) / 2.0;
-  {
-    ProfScope ps(f32 ? "attn_bwd_rowdot_kernel" : "attn_bwd_rowdot_bf16_kernel", 2.0 * BTC,
-                 es * 2.0 * BTC + 4.0 * rows, stream);
-    const long long n4 = (long long)B * T * (C / 4);
-    const unsigned blocks = (unsigned)((n4 + 255) / 256);
-    switch (hs / 4) {
-      case 1: attn_bwd_rowdot_kernel<1, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 2: attn_bwd_rowdot_kernel<2, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 4: attn_bwd_rowdot_kernel<4, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 8: attn_bwd_rowdot_kernel<8, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 16: attn_bwd_rowdot_kernel<16, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      case 32: attn_bwd_rowdot_kernel<32, TS><<<blocks, 256, 0, stream>>>(dscratch, dout, out, B, T, C, NH); break;
-      default:
-        attn_bwd_rowdot_generic_kernel<TS><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
-            dscratch, dout, out, B, T, C, NH, hs);
-    }
-  }
+  const int rc = rowdot_t(dscratch, dout, out, B, T, C, NH, stream);
+  if (rc) return rc;
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
     ProfScope ps(f32 ? "attn_bwd_dkdv_kernel" : "attn_bwd_dkdv_bf16_kernel",
@@ -536,6 +547,9 @@ int attention_forward(float* out, float* lse, const float* qkv, int B, int T, in
 }
 int attention_forward(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C, int NH,
                       hipStream_t stream) {
+  // head sizes that are multiples of 8 use the bf16-MFMA kernel; others multiply in fp32
+  if (C % NH == 0 && attention_bf16_mma_supported(C, NH))
+    return attention_forward_bf16_mma(out, lse, qkv, B, T, C, NH, stream);
   return attention_forward_t(out, lse, qkv, B, T, C, NH, stream);
 }
 int attention_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
@@ -547,8 +561,15 @@ int attention_backward(float* dqkv, const float* dout, const float* qkv, const f
 int attention_backward(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv, const bf16_t* out,
                        const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
                        int NH, hipStream_t stream) {
+  if (C % NH == 0 && attention_bf16_mma_supported(C, NH))
+    return attention_backward_bf16_mma(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C,
+                                       NH, stream);
   return attention_backward_t(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C, NH,
                               stream);
+}
+int attention_rowdot(float* D, const bf16_t* dout, const bf16_t* out, int B, int T, int C,
+                     int NH, hipStream_t stream) {
+  return rowdot_t(D, dout, out, B, T, C, NH, stream);
 }
 
 }  // namespace gpt2

@@ -1,0 +1,510 @@
+// attention_bf16.hip -- causal attention of the mixed-precision step on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// Same computation as attention.hip ("llm.c 的中文注解-20240421" sections 1.7 and 1.8;
+// flash-style: online softmax forward keeping only the row log-sum-exp, recomputation in
+// the backward), for bf16 Q, K, V, O, dO and dQKV. The score products take bf16 operands
+// with exact products and fp32 sums, as in fp32 arithmetic on the same inputs; the
+// probabilities P and the score gradients dS are rounded to bf16 where they become MFMA
+// operands. Softmax statistics, lse, rowsum(dO*O) and the dS scratch tiles stay fp32.
+//
+// Register layouts. Each lane of the bf16 MFMA supplies 8 consecutive k of one row of A and
+// of one column of B; the result tile gives lane l the column l % 32 and the rows
+// 8*(i/4) + 4*(l/32) + i%4 of acc[i]. Scores are computed transposed (keys down the rows,
+// one query per lane column), so for a 16-wide k step the 16 accumulator entries
+// 8h .. 8h+7 of lanes l and l+32 together hold 16 consecutive keys of the lane's query:
+// lane l < 32 keys 16h + {0..3, 8..11}, lane l+32 keys 16h + {4..7, 12..15}. That is
+// directly the B operand of the next product if the other operand orders its keys the same
+// way, which V^T (and, in the backward, dO^T and Q^T) do by being stored in LDS at the
+// permuted key position kpos() below: each lane's 8 keys are then one 16-byte read.
+#include <cmath>
+
+#include "kernels.h"
+
+namespace gpt2 {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int TILE = 64;   // queries per workgroup, keys per tile
+constexpr int NTHR = 128;  // two waves of 32 queries (or keys)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// position of key k (0..63 within a tile) in a permuted row: groups of 4 keys stay
+// together, and lane-half lh of k step (kb, h) finds its 8 keys at 32kb + 16h + 8lh .. +7
+GPT2_DEVICE_INLINE int kpos(int k) {
+  const int r = k & 15;
+  return (k & ~15) + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
+}
+
+// LDS tiles of ROWS rows x COLS bf16 (COLS a multiple of 8): 16-byte chunk c of row r is
+// stored at chunk c ^ swz(r), which spreads 32 rows read at the same chunk, and rows 8
+// apart written at the same chunk, over the banks.
+template <int COLS>
+GPT2_DEVICE_INLINE int loff(int row, int c) {
+  constexpr int CPR = COLS / 8;
+  return row * COLS + ((c ^ ((row ^ (row >> 3)) & (CPR - 1))) << 3);
+}
+
+GPT2_DEVICE_INLINE uint32_t pack2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// 16 bytes (8 bf16) of row t, columns d..d+7 of a strided tensor; rows past the end and
+// columns past hs read as zero (addresses clamped into the tensor)
+GPT2_DEVICE_INLINE u32x4 load8(const bf16_t* base, long long ld, int t, int d, int T, int hs) {
+  const int tc = min(t, T - 1), dc = min(d, hs - 8);
+  const u32x4 x = *reinterpret_cast<const u32x4*>(base + (long long)tc * ld + dc);
+  return (t < T && d < hs) ? x : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Natural tile: rows row0 .. row0+63 of the tensor -> S[row][d] (HSP columns).
+template <int HSP>
+GPT2_DEVICE_INLINE void tile_rows(bf16_t* S, const bf16_t* base, long long ld, int row0, int T,
+                                  int hs, int tid) {
+  constexpr int CPR = HSP / 8;
+#pragma unroll
+  for (int i = 0; i < TILE * CPR / NTHR; i++) {
+    const int f = tid + NTHR * i;
+    const int row = f / CPR, c = f % CPR;
+    *reinterpret_cast<u32x4*>(S + loff<HSP>(row, c)) = load8(base, ld, row0 + row, 8 * c, T, hs);
+  }
+}
+
+// Transposed tile: rows row0 .. row0+63 of the tensor -> S[d][kpos(row)] (64 columns). A
+// thread moves a block of 4 rows x 8 columns: four 16-byte loads, eight 8-byte stores.
+template <int HSP>
+GPT2_DEVICE_INLINE void tile_cols(bf16_t* S, const bf16_t* base, long long ld, int row0, int T,
+                                  int hs, int tid) {
+  constexpr int DG = HSP / 8;               // 8-column groups
+  constexpr int BLOCKS = (TILE / 4) * DG;   // 4x8 blocks in the tile
+#pragma unroll
+  for (int i = 0; i < (BLOCKS + NTHR - 1) / NTHR; i++) {
+    const int b = tid + NTHR * i;
+    if (BLOCKS % NTHR && b >= BLOCKS) break;
+    const int dg = b % DG, rq = b / DG;  // columns 8dg .. +7, rows 4rq .. +3
+    u32x4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) x[j] = load8(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs);
+    const int p = kpos(4 * rq);  // a multiple of 4: the 4 rows stay consecutive
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int q = e >> 1;
+      uint32_t lo, hi;
+      if ((e & 1) == 0) {
+        lo = (x[0][q] & 0xFFFFu) | (x[1][q] << 16);
+        hi = (x[2][q] & 0xFFFFu) | (x[3][q] << 16);
+      } else {
+        lo = (x[0][q] >> 16) | (x[1][q] & 0xFFFF0000u);
+        hi = (x[2][q] >> 16) | (x[3][q] & 0xFFFF0000u);
+      }
+      *reinterpret_cast<u32x2*>(S + loff<TILE>(8 * dg + e, p >> 3) + (p & 7)) = u32x2{lo, hi};
+    }
+  }
+}
+
+GPT2_DEVICE_INLINE void tile_of_block(int ntiles, int NH, int* tile, int* head, int* b) {
+  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  *tile = lid % ntiles;
+  const int bh = lid / ntiles;
+  *head = bh % NH;
+  *b = bh / NH;
+}
+
+// ---------------------------------------------------------------------------------------
+// forward: a workgroup owns 64 queries (32 per wave) of one (batch, head)
+// ---------------------------------------------------------------------------------------
+template <int HSP>
+__global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restrict__ out,
+                                                                float* __restrict__ lse,
+                                                                const bf16_t* __restrict__ qkv,
+                                                                int T, int C, int NH, int hs,
+                                                                float scale_log2) {
+  constexpr int KS = HSP / 16, ND = HSP / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[TILE * HSP];   // [key][d]
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[HSP * TILE];   // [d][kpos(key)]
+
+  const int nqt = (T + TILE - 1) / TILE;
+  int qt, head, b;
+  tile_of_block(nqt, NH, &qt, &head, &b);
+  qt = nqt - 1 - qt;  // longest rows first
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, lh = lane >> 5;
+  const long long C3 = 3LL * C;
+  const bf16_t* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const int q = qt * TILE + wave * 32 + r;
+  const int qm = min(q, T - 1);  // lanes past the end mask as the last row; never stored
+
+  // this lane's query, d = 16ks + 8lh .. +7 for each k step
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++)
+    qf[ks] = __builtin_bit_cast(bf16x8, load8(base, C3, qm, 16 * ks + 8 * lh, T, hs));
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // in units of the scaled log2 domain
+
+  const int ntiles = (min(T, (qt + 1) * TILE) + TILE - 1) / TILE;
+  for (int kt = 0; kt < ntiles; kt++) {
+    const int key0 = kt * TILE;
+    __syncthreads();
+    tile_rows<HSP>(Ks, base + C, C3, key0, T, hs, tid);
+    tile_cols<HSP>(Vt, base + 2 * C, C3, key0, T, hs, tid);
+    __syncthreads();
+
+    // S^T for 2 x 32 keys: s[kb][i] = score of key 32kb + 8(i/4) + 4lh + i%4
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&Ks[loff<HSP>(32 * kb + r, 2 * ks + lh)]);
+        s[kb] = mfma_bf16(kf, qf[ks], s[kb]);
+      }
+    }
+    const bool diag = key0 + TILE > qt * TILE;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * lh + (i % 4);
+        if (diag && key > qm) s[kb][i] = -INFINITY;
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);  // key0 = 0 <= qm: finite
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+    bf16x8 pf[2][2];  // P as the B operand of k step (kb, h)
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float p0 = exp2f(fmaf(s[kb][8 * hh + 2 * j], scale_log2, -m_new));
+          const float p1 = exp2f(fmaf(s[kb][8 * hh + 2 * j + 1], scale_log2, -m_new));
+          l_run += p0 + p1;
+          w[j] = pack2(p0, p1);
+        }
+        pf[kb][hh] = __builtin_bit_cast(bf16x8, w);
+      }
+    m_run = m_new;
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+              &Vt[loff<TILE>(32 * db + r, 4 * kb + 2 * hh + lh)]);
+          oacc[db] = mfma_bf16(vf, pf[kb][hh], oacc[db]);
+        }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (q < T) {
+    bf16_t* o = out + ((long long)b * T + q) * C + (long long)head * hs;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * lh;
+        if (d < hs)
+          st4(o + d, f32x4{oacc[db][4 * ig] * inv, oacc[db][4 * ig + 1] * inv,
+                           oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv});
+      }
+    if (lh == 0) lse[((long long)b * NH + head) * T + q] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+
+// ---------------------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------------------
+GPT2_DEVICE_INLINE long long tri_index(int qt, int kt) { return (long long)qt * (qt + 1) / 2 + kt; }
+GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 2; }
+
+// dK, dV for 64 keys (32 per wave), over the query tiles from the diagonal down. Per query
+// tile, S and dP are computed with queries down the rows and this lane's key as the column;
+// P and dS are then the B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A operands are
+// the transposed tiles dO^T and Q^T in LDS. dS^T of each causal 64x64 tile is written (bf16,
+// [key][query]) for the dQ kernel.
+template <int HSP>
+__global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
+    bf16_t* __restrict__ dqkv, bf16_t* __restrict__ dsbuf, const bf16_t* __restrict__ dout,
+    const bf16_t* __restrict__ qkv, const float* __restrict__ lse,
+    const float* __restrict__ Drow, int T, int C, int NH, int hs, float scale,
+    float scale_log2) {
+  constexpr int KS = HSP / 16, ND = HSP / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[TILE * HSP];   // [q][d]
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[HSP * TILE];   // [d][kpos(q)]
+  __shared__ __attribute__((aligned(16))) bf16_t dOs[TILE * HSP];  // [q][d]
+  __shared__ __attribute__((aligned(16))) bf16_t dOt[HSP * TILE];  // [d][kpos(q)]
+  __shared__ float Ls[TILE], Ds[TILE];
+
+  const int nkt = (T + TILE - 1) / TILE;
+  int kt, head, b;
+  tile_of_block(nkt, NH, &kt, &head, &b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, lh = lane >> 5;
+  const long long C3 = 3LL * C;
+  const bf16_t* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const bf16_t* dobase = dout + (long long)b * T * C + (long long)head * hs;
+  const float* lrow = lse + ((long long)b * NH + head) * T;
+  const float* drow = Drow + ((long long)b * NH + head) * T;
+  const int key = kt * TILE + wave * 32 + r;
+  const int km = min(key, T - 1);
+
+  bf16x8 kf[KS], vf[KS];  // this lane's key and value, d = 16ks + 8lh .. +7
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    kf[ks] = __builtin_bit_cast(bf16x8, load8(base + C, C3, km, 16 * ks + 8 * lh, T, hs));
+    vf[ks] = __builtin_bit_cast(bf16x8, load8(base + 2 * C, C3, km, 16 * ks + 8 * lh, T, hs));
+  }
+  f32x16 dvacc[ND], dkacc[ND];  // [d][key]
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      dvacc[db][i] = 0.f;
+      dkacc[db][i] = 0.f;
+    }
+
+  const int nqt = nkt;
+  for (int qt = kt; qt < nqt; qt++) {
+    const int q0 = qt * TILE;
+    __syncthreads();
+    tile_rows<HSP>(Qs, base, C3, q0, T, hs, tid);
+    tile_cols<HSP>(Qt, base, C3, q0, T, hs, tid);
+    tile_rows<HSP>(dOs, dobase, C, q0, T, hs, tid);
+    tile_cols<HSP>(dOt, dobase, C, q0, T, hs, tid);
+    if (tid < TILE) {
+      const int t = q0 + tid;
+      Ls[tid] = t < T ? lrow[t] * kLog2e : 0.f;
+      Ds[tid] = t < T ? drow[t] : 0.f;
+    }
+    __syncthreads();
+    // dS^T tile (kt, qt) of this (b, head): [key][query], 64 x 64 bf16
+    bf16_t* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
+                              (TILE * TILE) + (long long)(wave * 32 + r) * TILE;
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      u32x4 pw[2], sw[2];  // P and dS (bf16 pairs) as B operands of k step h
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[loff<HSP>(32 * qb + r, 2 * ks + lh)]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOs[loff<HSP>(32 * qb + r, 2 * ks + lh)]);
+        s = mfma_bf16(qa, kf[ks], s);
+        dp = mfma_bf16(oa, vf[ks], dp);
+      }
+      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int i = 4 * g4 + j;
+          const int ql = 32 * qb + 8 * g4 + 4 * lh + j;
+          const int qa = q0 + ql;
+          const bool ok = qa < T && qa >= key;
+          const float p = ok ? exp2f(fmaf(s[i], scale_log2, -Ls[ql])) : 0.f;
+          pv[j] = p;
+          dsv[j] = p * (dp[i] - Ds[ql]);
+        }
+        const int hh = g4 >> 1, w = 2 * (g4 & 1);  // acc entries 8hh .. 8hh+7 form k step hh
+        pw[hh][w] = pack2(pv[0], pv[1]);
+        pw[hh][w + 1] = pack2(pv[2], pv[3]);
+        const uint32_t d01 = pack2(dsv[0], dsv[1]), d23 = pack2(dsv[2], dsv[3]);
+        sw[hh][w] = d01;
+        sw[hh][w + 1] = d23;
+        // 4 consecutive queries of this key: one 8-byte store
+        *reinterpret_cast<u32x2*>(dst + 32 * qb + 8 * g4 + 4 * lh) = u32x2{d01, d23};
+      }
+#pragma unroll
+      for (int db = 0; db < ND; db++)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const int c = 4 * qb + 2 * hh + lh;
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOt[loff<TILE>(32 * db + r, c)]);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[loff<TILE>(32 * db + r, c)]);
+          dvacc[db] = mfma_bf16(oa, __builtin_bit_cast(bf16x8, pw[hh]), dvacc[db]);
+          dkacc[db] = mfma_bf16(qa, __builtin_bit_cast(bf16x8, sw[hh]), dkacc[db]);
+        }
+    }
+  }
+  if (key < T) {
+    bf16_t* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
+    bf16_t* dv = dk + C;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * lh;
+        if (d < hs) {
+          st4(dk + d, f32x4{dkacc[db][4 * ig] * scale, dkacc[db][4 * ig + 1] * scale,
+                            dkacc[db][4 * ig + 2] * scale, dkacc[db][4 * ig + 3] * scale});
+          st4(dv + d, f32x4{dvacc[db][4 * ig], dvacc[db][4 * ig + 1], dvacc[db][4 * ig + 2],
+                            dvacc[db][4 * ig + 3]});
+        }
+      }
+  }
+}
+
+// dQ^T[d][q] = scale * K^T[d][key] dS^T[key][q] for 64 queries (32 per wave), over key
+// tiles 0 .. qt, reading the dS^T tiles of the dK/dV kernel transposed into LDS.
+template <int HSP>
+__global__ __launch_bounds__(NTHR) void attn_bwd_dq_bf16mma_kernel(
+    bf16_t* __restrict__ dqkv, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dsbuf,
+    int T, int C, int NH, int hs, float scale) {
+  constexpr int ND = HSP / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[HSP * TILE];   // [d][kpos(key)]
+  __shared__ __attribute__((aligned(16))) bf16_t Sq[TILE * TILE];  // [q][kpos(key)]
+
+  const int nqt = (T + TILE - 1) / TILE;
+  int qt, head, b;
+  tile_of_block(nqt, NH, &qt, &head, &b);
+  qt = nqt - 1 - qt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, lh = lane >> 5;
+  const long long C3 = 3LL * C;
+  const bf16_t* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
+  const bf16_t* src = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, 0)) *
+                                  (TILE * TILE);
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[db][i] = 0.f;
+
+  for (int kt = 0; kt <= qt; kt++) {
+    __syncthreads();
+    tile_cols<HSP>(Kt, kbase, C3, kt * TILE, T, hs, tid);
+    // the stored tile is [key][query] (64 x 64, rows of 64): as rows of a tensor with
+    // T = 64 and hs = 64 it transposes into [query][kpos(key)]
+    tile_cols<TILE>(Sq, src + (long long)kt * TILE * TILE, TILE, 0, TILE, TILE, tid);
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const int c = 4 * kb + 2 * hh + lh;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[loff<TILE>(32 * db + r, c)]);
+          const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&Sq[loff<TILE>(32 * wave + r, c)]);
+          acc[db] = mfma_bf16(ka, sb, acc[db]);
+        }
+  }
+  // acc[db][i]: d = 32db + 8(i/4) + 4lh + i%4, query 32 wave + r of the tile
+  const int q = qt * TILE + 32 * wave + r;
+  if (q < T) {
+    bf16_t* o = dqkv + ((long long)b * T + q) * C3 + (long long)head * hs;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * lh;
+        if (d < hs)
+          st4(o + d, f32x4{acc[db][4 * ig] * scale, acc[db][4 * ig + 1] * scale,
+                           acc[db][4 * ig + 2] * scale, acc[db][4 * ig + 3] * scale});
+      }
+  }
+}
+
+}  // namespace
+
+bool attention_bf16_mma_supported(int C, int NH) {
+  const int hs = C / NH;
+  return hs % 8 == 0 && hs <= 128;
+}
+
+int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
+                               int NH, hipStream_t stream) {
+  if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_bf16_mma_supported(C, NH)) {
+    set_global_error("attention (bf16 MFMA): unsupported shape B=%d T=%d C=%d NH=%d", B, T, C,
+                     NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale_log2 = kLog2e / sqrtf((float)hs);
+  dim3 grid(((T + TILE - 1) / TILE) * NH * B);
+  const double tri = (double)T * (T + 1) / 2.0;
+  ProfScope ps("attn_fwd_bf16mma_kernel", 4.0 * B * NH * hs * tri,
+               2.0 * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
+  if (hs <= 32) attn_fwd_bf16mma_kernel<32><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else if (hs <= 64) attn_fwd_bf16mma_kernel<64><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else attn_fwd_bf16mma_kernel<128><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+}  // namespace gpt2
+
+namespace gpt2 {
+int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,
+                                const bf16_t* out, const float* lse, float* dscratch,
+                                float* ds_scratch, int B, int T, int C, int NH,
+                                hipStream_t stream) {
+  if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_bf16_mma_supported(C, NH)) {
+    set_global_error("attention (bf16 MFMA): unsupported shape B=%d T=%d C=%d NH=%d", B, T, C,
+                     NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale = 1.0f / sqrtf((float)hs);
+  const float scale_log2 = scale * kLog2e;
+  const double BTC = (double)B * T * C, tri = (double)T * (T + 1) / 2.0;
+  const long long rows = (long long)B * NH * T;
+  const int rc = attention_rowdot(dscratch, dout, out, B, T, C, NH, stream);
+  if (rc) return rc;
+  bf16_t* ds = reinterpret_cast<bf16_t*>(ds_scratch);
+  dim3 grid(((T + TILE - 1) / TILE) * NH * B);
+  {
+    ProfScope ps("attn_bwd_dkdv_bf16mma_kernel", 6.0 * B * NH * hs * tri,
+                 2.0 * (3.0 * BTC + BTC + 2.0 * BTC) + 4.0 * 2.0 * rows + 2.0 * B * NH * tri,
+                 stream);
+    if (hs <= 32) attn_bwd_dkdv_bf16mma_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hs <= 64) attn_bwd_dkdv_bf16mma_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dkdv_bf16mma_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+  }
+  {
+    ProfScope ps("attn_bwd_dq_bf16mma_kernel", 2.0 * B * NH * hs * tri,
+                 2.0 * B * NH * tri + 2.0 * 2.0 * BTC, stream);
+    if (hs <= 32) attn_bwd_dq_bf16mma_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
+    else if (hs <= 64) attn_bwd_dq_bf16mma_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
+    else attn_bwd_dq_bf16mma_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
+  }
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+}  // namespace gpt2

@@ -92,6 +92,18 @@ int attention_forward(float* out, float* lse, const float* qkv, int B, int T, in
                       hipStream_t stream);
 int attention_forward(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C, int NH,
                       hipStream_t stream);
+// bf16-MFMA attention (attention_bf16.hip), used by the bf16 overloads when the head size
+// is a multiple of 8 (at most 128)
+bool attention_bf16_mma_supported(int C, int NH);
+int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
+                               int NH, hipStream_t stream);
+int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,
+                                const bf16_t* out, const float* lse, float* dscratch,
+                                float* ds_scratch, int B, int T, int C, int NH,
+                                hipStream_t stream);
+// D (B, NH, T) = rowsum over each head's columns of dout * out (fp32 sums)
+int attention_rowdot(float* D, const bf16_t* dout, const bf16_t* out, int B, int T, int C,
+                     int NH, hipStream_t stream);
 // `dscratch` needs B*NH*T floats (row dot products of dout and out); `ds_scratch` needs
 // attention_ds_scratch_floats(B, T, NH) floats (the causal 64x64 tiles of dS)
 size_t attention_ds_scratch_floats(int B, int T, int NH);

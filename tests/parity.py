@@ -66,18 +66,20 @@ def assert_tensor_close(name, a, o, rtol=RTOL, floor=ATOL, elem_rms=1e-4):
 U32 = 2.0 ** -24  # fp32 unit roundoff
 
 
-def assert_close_mag(name, a, o, mag, K, rtol=RTOL, atol=ATOL):
+def assert_close_mag(name, a, o, mag, K, rtol=RTOL, atol=ATOL, operand_u=0.0):
     """allclose with an extra absolute term from the arithmetic of a K-term fp32 sum.
 
     ``mag`` is the same sum taken over absolute values (sum_k |x_k y_k|); rounding in a
     K-term fp32 accumulation is below K*u*mag in the worst case and about sqrt(K)*u*mag in
     practice, so cancellation (|o| << mag) is allowed 4*sqrt(K)*u*mag of absolute error.
+    ``operand_u``: unit roundoff of an operand the kernel rounds before the products (bf16:
+    2^-9), which moves the sum by at most operand_u * mag.
     """
     a = np.asarray(a, dtype=np.float64).ravel()
     o = np.asarray(o, dtype=np.float64).ravel()
     mag = np.asarray(mag, dtype=np.float64).ravel()
     err = np.abs(a - o)
-    bound = rtol * np.abs(o) + atol + 4.0 * np.sqrt(K) * U32 * mag
+    bound = rtol * np.abs(o) + atol + (4.0 * np.sqrt(K) * U32 + operand_u) * mag
     bad = err > bound
     if bad.any():
         i = int(np.argmax(err - bound))

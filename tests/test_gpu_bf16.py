@@ -166,7 +166,8 @@ def test_layernorm_bf16(N, C):
 
 
 @pytest.mark.parametrize("B,T,C,NH", [(2, 100, 128, 2), (4, 16, 16, 4), (2, 64, 768, 12),
-                                      (1, 1, 64, 1), (3, 257, 64, 1)])
+                                      (1, 1, 64, 1), (3, 257, 64, 1), (2, 130, 48, 2),
+                                      (1, 200, 256, 2), (2, 77, 96, 3), (1, 1024, 1280, 20)])
 def test_attention_bf16(B, T, C, NH):
     r = rng(B * T + C + NH + 5)
     qkv = bf16_values(r.normal(0, 1.0, (B, T, 3 * C)))
@@ -178,7 +179,12 @@ def test_attention_bf16(B, T, C, NH):
     qabs = qkv.copy()
     qabs[:, :, 2 * C:] = np.abs(qabs[:, :, 2 * C:])
     mag, _ = oracle.attention_forward(qabs, NH)
-    assert_close_mag("attn out", host(out), ro, mag, T + C // NH, rtol=BF)
+    # with a head size that is a multiple of 8 the product P V takes P rounded to bf16 (as
+    # an MFMA operand): that changes out by up to 2^-9 sum_k P|v| = 2^-9 mag; the bound
+    # allows twice that, like the BF allowance for a rounded result
+    hs = C // NH
+    assert_close_mag("attn out", host(out), ro, mag, T + hs, rtol=BF,
+                     operand_u=BF if hs % 8 == 0 else 0.0)
     dqkv = torch.full((B, T, 3 * C), float("nan"), device="cuda").to(torch.bfloat16)
     gb.k_attention_backward_bf16(dqkv, dev_bf16(dy), dev_bf16(qkv), out, lse, B, T, C, NH)
     rd = oracle.attention_backward(dy, qkv, ratt, NH)
