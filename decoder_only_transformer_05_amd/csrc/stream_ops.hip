@@ -191,7 +191,13 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
   }
 }
 
-constexpr int LNB_ROWS = 32;  // rows per workgroup in the backward
+// rows per workgroup in the backward: 32, halved (down to 4) until there are at least 1024
+// workgroups, so short batches still fill the chip
+int lnb_rows(int N) {
+  int rows = 32;
+  while (rows > 4 && (N + rows - 1) / rows < 1024) rows /= 2;
+  return rows;
+}
 
 // dx (+)= rstd * (g - mean(g) - n * mean(g*n)), g = w * dout, n = (x - mean) * rstd;
 // per workgroup, partial[blk][0][:] = sum of n*dout, partial[blk][1][:] = sum of dout over
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     float* __restrict__ dx, bf16_t* __restrict__ dx_copy, float* __restrict__ partial,
     const T* __restrict__ dout, const T* __restrict__ x, const float* __restrict__ w,
     const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C,
-    int accumulate) {
+    int accumulate, int rows_per_block) {
   extern __shared__ float red[];  // [4 waves][2][C]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C4 = C / 4;
@@ -214,8 +220,8 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     dw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     db[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int r0 = blockIdx.x * LNB_ROWS;
-  const int r1 = min(N, r0 + LNB_ROWS);
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(N, r0 + rows_per_block);
   for (int row = r0 + wave; row < r1; row += 4) {
     const float mu = mean[row], rs = rstd[row];
     const T* dyr = dout + (long long)row * C;
@@ -564,7 +570,8 @@ int layernorm_forward(bf16_t* out, float* mean, float* rstd, const bf16_t* x, co
 }
 
 size_t layernorm_partial_floats(int N, int C) {
-  return (size_t)((N + LNB_ROWS - 1) / LNB_ROWS) * 2 * C;
+  const int rows = lnb_rows(N);
+  return (size_t)((N + rows - 1) / rows) * 2 * C;
 }
 
 namespace {
@@ -578,7 +585,8 @@ int layernorm_backward_t(float* dx, bf16_t* dx_copy, float* dw, float* db, const
     set_global_error("layernorm_backward: unsupported N=%d C=%d", N, C);
     return -1;
   }
-  const int blocks = (N + LNB_ROWS - 1) / LNB_ROWS;
+  const int rows = lnb_rows(N);
+  const int blocks = (N + rows - 1) / rows;
   const size_t lds = (size_t)8 * C * sizeof(float);
   {
     ProfScope ps(name, 14.0 * N * C,
@@ -587,7 +595,8 @@ int layernorm_backward_t(float* dx, bf16_t* dx_copy, float* dw, float* db, const
                  stream);
 #define GPT2_LNB(V)                                                                          \
   layernorm_bwd_kernel<V, T><<<blocks, 256, lds, stream>>>(dx, dx_copy, partial, dout, x, w,   \
-                                                           mean, rstd, N, C, accumulate_dx ? 1 : 0)
+                                                           mean, rstd, N, C, accumulate_dx ? 1 : 0, \
+                                                           rows)
     GPT2_LN_DISPATCH(vpl, GPT2_LNB)
 #undef GPT2_LNB
   }

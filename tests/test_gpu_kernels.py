@@ -115,8 +115,11 @@ def test_layernorm_forward_backward(N, C):
     gb.k_layernorm_backward(dx, dw, db, dev(dy), dev(x), dev(w), mean, rstd, N, C)
     rdx, rdw, rdb = oracle.layernorm_backward(dy, x, w, rm, rr)
     assert_close("ln dx", host(dx), dx0 + rdx)
-    assert_close("ln dw", host(dw), dw0 + rdw)
-    assert_close("ln db", host(db), db0 + rdb)
+    # dw, db are N-term column sums added to the existing values: fp32 bound on their
+    # magnitude sums (n = normalised x)
+    nrm = (x - rm[:, None]) * rr[:, None]
+    assert_close_mag("ln dw", host(dw), dw0 + rdw, np.abs(dw0) + np.abs(nrm * dy).sum(0), N)
+    assert_close_mag("ln db", host(db), db0 + rdb, np.abs(db0) + np.abs(dy).sum(0), N)
 
 
 @pytest.mark.parametrize("B,T,C,NH", [(2, 100, 128, 2), (4, 16, 16, 4), (1, 200, 96, 3),
