@@ -275,14 +275,28 @@ __device__ __forceinline__ float split_epilogue(const Args& g, long long off, in
 
 // Sums `splits` partial results (each M x N, row stride wld) into C with the epilogue `EPI`,
 // adding the partials in split order; four consecutive columns per thread, with all of a
-// group's partial loads issued before the adds.
+// group's partial loads issued before the adds. With colsum_part, the last workgroups instead
+// add the per-split column sums (split order) into g.colsum.
 template <int EPI>
-__global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int splits, int wld) {
+__global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int splits, int wld,
+                                    const float* __restrict__ colsum_part) {
+  // the last ceil(M / blockDim) workgroups reduce the column sums, one m per thread
+  const int ncs = colsum_part ? (g.M + blockDim.x - 1) / blockDim.x : 0;
+  const int nb = gridDim.x - ncs;
+  if ((int)blockIdx.x >= nb) {
+    const int m = (blockIdx.x - nb) * blockDim.x + threadIdx.x;
+    if (m < g.M) {
+      float cs = 0.f;
+      for (int z = 0; z < splits; z++) cs += colsum_part[(long long)z * g.M + m];
+      g.colsum[m] += cs;
+    }
+    return;
+  }
   const int N4 = (g.N + 3) / 4;
   const long long total = (long long)g.M * N4;
   const long long zstride = (long long)g.M * wld;
   for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (long long)gridDim.x * blockDim.x) {
+       idx += (long long)nb * blockDim.x) {
     const int m = (int)(idx / N4), n = 4 * (int)(idx % N4);
     const float* src = ws + (long long)m * wld + n;
     const bool full = n + 3 < g.N;
@@ -382,17 +396,6 @@ size_t gemm_workspace_floats(const Gemm& g) {
   return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
 }
 
-namespace {
-// colsum[m] += sum over splits of the per-split column sums (split order)
-__global__ void colsum_split_reduce_kernel(float* __restrict__ colsum,
-                                           const float* __restrict__ part, int splits, int M) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  float s = 0.f;
-  for (int z = 0; z < splits; z++) s += part[(long long)z * M + m];
-  colsum[m] += s;
-}
-}  // namespace
 
 int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0) {
@@ -476,20 +479,18 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
     if (blocks > 8192) blocks = 8192;
     snprintf(name, sizeof(name), "split_reduce_kernel<%d>", (int)g.epi);
     {
-      ProfScope ps(name, 0.0, 4.0 * MN * (splits + out_factor), stream);
+      const float* cp = g.colsum ? colsum_part : nullptr;
+      const int nblk = blocks + (cp ? ceil_div(g.M, 256) : 0);
+      ProfScope ps(name, 0.0,
+                   4.0 * MN * (splits + out_factor) + (cp ? 4.0 * (splits + 2.0) * g.M : 0.0),
+                   stream);
       switch (g.epi) {
-        case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        case EPI_GELU: split_reduce_kernel<EPI_GELU><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        case EPI_RESID: split_reduce_kernel<EPI_RESID><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        default: split_reduce_kernel<EPI_STORE><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
+        case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+        case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+        case EPI_GELU: split_reduce_kernel<EPI_GELU><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+        case EPI_RESID: split_reduce_kernel<EPI_RESID><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+        default: split_reduce_kernel<EPI_STORE><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
       }
-    }
-    if (g.colsum) {
-      ProfScope ps("colsum_split_reduce_kernel", (double)splits * g.M,
-                   4.0 * ((double)splits * g.M + 2.0 * g.M), stream);
-      colsum_split_reduce_kernel<<<ceil_div(g.M, 256), 256, 0, stream>>>(g.colsum, colsum_part,
-                                                                        splits, g.M);
     }
   }
   GPT2_HIP_OK(hipGetLastError());

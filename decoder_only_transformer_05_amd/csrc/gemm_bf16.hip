@@ -311,14 +311,28 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
 
 // Adds `splits` fp32 partials (each M x N, row stride wld) in split order, then applies the
 // epilogue into the real output; four consecutive columns per thread.
+// With colsum_part, the last workgroups instead add the per-split column sums (split order)
+// into g.colsum.
 template <int EPI, bool CF32>
 __global__ void split_reduce_bf16_kernel(Args g, const float* __restrict__ ws, int splits,
-                                         int wld) {
+                                         int wld, const float* __restrict__ colsum_part) {
+  // the last ceil(M / blockDim) workgroups reduce the column sums, one m per thread
+  const int ncs = colsum_part ? (g.M + blockDim.x - 1) / blockDim.x : 0;
+  const int nb = gridDim.x - ncs;
+  if ((int)blockIdx.x >= nb) {
+    const int m = (blockIdx.x - nb) * blockDim.x + threadIdx.x;
+    if (m < g.M) {
+      float cs = 0.f;
+      for (int z = 0; z < splits; z++) cs += colsum_part[(long long)z * g.M + m];
+      g.colsum[m] += cs;
+    }
+    return;
+  }
   const int N4 = (g.N + 3) / 4;
   const long long total = (long long)g.M * N4;
   const long long zstride = (long long)g.M * wld;
   for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (long long)gridDim.x * blockDim.x) {
+       idx += (long long)nb * blockDim.x) {
     const int m = (int)(idx / N4), n = 4 * (int)(idx % N4);
     const float* src = ws + (long long)m * wld + n;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -338,15 +352,6 @@ __global__ void split_reduce_bf16_kernel(Args g, const float* __restrict__ ws, i
   }
 }
 
-__global__ void colsum_split_reduce_bf16_kernel(float* __restrict__ colsum,
-                                                const float* __restrict__ part, int splits,
-                                                int M) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  float s = 0.f;
-  for (int z = 0; z < splits; z++) s += part[(long long)z * M + m];
-  colsum[m] += s;
-}
 
 template <bool AT, bool BT, bool CF32>
 void launch_epi(const Args& a, int epi, dim3 grid, hipStream_t s) {
@@ -494,21 +499,16 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
     int blocks = (int)((total + 255) / 256);
     if (blocks > 8192) blocks = 8192;
     snprintf(name, sizeof(name), "split_reduce_bf16_kernel<%d>", (int)g.epi);
-    {
-      ProfScope ps(name, 0.0, 4.0 * MN * splits + out_bytes, stream);
-      switch (g.epi) {
-        case EPI_ACCUM: split_reduce_bf16_kernel<EPI_ACCUM, true><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        case EPI_GELU_BWD: split_reduce_bf16_kernel<EPI_GELU_BWD, false><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        case EPI_GELU: split_reduce_bf16_kernel<EPI_GELU, false><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        case EPI_RESID: split_reduce_bf16_kernel<EPI_RESID, false><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-        default: split_reduce_bf16_kernel<EPI_STORE, false><<<blocks, 256, 0, stream>>>(a, workspace, splits, p.ldc); break;
-      }
-    }
-    if (g.colsum) {
-      ProfScope ps("colsum_split_reduce_kernel", (double)splits * g.M,
-                   4.0 * ((double)splits * g.M + 2.0 * g.M), stream);
-      colsum_split_reduce_bf16_kernel<<<ceil_div(g.M, 256), 256, 0, stream>>>(
-          g.colsum, colsum_part, splits, g.M);
+    const float* cp = g.colsum ? colsum_part : nullptr;
+    const int nblk = blocks + (cp ? ceil_div(g.M, 256) : 0);
+    ProfScope ps(name, 0.0, 4.0 * MN * splits + out_bytes + (cp ? 4.0 * (splits + 2.0) * g.M : 0.0),
+                 stream);
+    switch (g.epi) {
+      case EPI_ACCUM: split_reduce_bf16_kernel<EPI_ACCUM, true><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_GELU_BWD: split_reduce_bf16_kernel<EPI_GELU_BWD, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_GELU: split_reduce_bf16_kernel<EPI_GELU, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_RESID: split_reduce_bf16_kernel<EPI_RESID, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      default: split_reduce_bf16_kernel<EPI_STORE, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
     }
   }
   GPT2_HIP_OK(hipGetLastError());

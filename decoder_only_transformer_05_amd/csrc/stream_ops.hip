@@ -101,25 +101,47 @@ __global__ __launch_bounds__(SORT_THREADS) void token_sort_kernel(int32_t* __res
   }
   __threadfence_block();
   __syncthreads();
-  // place positions; offset[v] is advanced past each chunk's occurrences of v
+  // place positions, 1024 at a time: the chunk is sorted by (token, position) with a
+  // bitonic network in LDS, so each position's rank among the chunk's occurrences of its
+  // token is its distance from the start of its run; offset[v] then advances by the run
   for (int c0 = 0; c0 < BT; c0 += SORT_THREADS) {
     const int i = c0 + tid;
-    const int n = min(SORT_THREADS, BT - c0);
-    const int v = i < BT ? clamp_tok(tok[i], V) : -1;
-    chunk_tok[tid] = v;
+    // key: token in the high bits, position within the chunk in the low 10 bits
+    chunk_tok[tid] = i < BT ? (clamp_tok(tok[i], V) << 10) | tid : 0x7FFFFFFF;
     __syncthreads();
-    int before = 0, total = 0;
-    if (i < BT) {
-      for (int j = 0; j < n; j++) {
-        const int same = chunk_tok[j] == v;
-        total += same;
-        before += same & (j < tid);
+    for (int k = 2; k <= SORT_THREADS; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const int partner = tid ^ j;
+        if (partner > tid) {
+          const int a = chunk_tok[tid], b = chunk_tok[partner];
+          const bool up = (tid & k) == 0;
+          if ((a > b) == up) {
+            chunk_tok[tid] = b;
+            chunk_tok[partner] = a;
+          }
+        }
+        __syncthreads();
       }
-      sorted[offset[v] + before] = i;
     }
-    __threadfence_block();
+    // run starts: part[x] = x where the token changes, then a max-scan gives each slot
+    // the start of its run
+    const int key = chunk_tok[tid];
+    const int v = key >> 10;
+    const bool valid = key != 0x7FFFFFFF;
+    part[tid] = (tid == 0 || (chunk_tok[tid - 1] >> 10) != v) ? tid : 0;
     __syncthreads();
-    if (i < BT && before == 0) offset[v] += total;
+    for (int o = 1; o < SORT_THREADS; o <<= 1) {
+      const int other = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] = max(part[tid], other);
+      __syncthreads();
+    }
+    const int start = part[tid];
+    const bool last = valid && (tid == SORT_THREADS - 1 || (chunk_tok[tid + 1] >> 10) != v);
+    if (valid) sorted[offset[v] + (tid - start)] = c0 + (key & 1023);
+    __threadfence_block();
+    __syncthreads();  // every slot of a run has read offset[v]
+    if (last) offset[v] += tid - start + 1;
     __threadfence_block();
     __syncthreads();
   }
@@ -277,38 +299,40 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   }
 }
 
-// dw[c] += sum_k partial[k][0][c], db[c] += sum_k partial[k][1][c]. A workgroup owns 32 of
-// the 2C columns; its 8 thread groups each sum every 8th partial (in order), and the 8
-// group sums are then added in group order.
+// dw[c] += sum_k partial[k][0][c], db[c] += sum_k partial[k][1][c]. A workgroup owns 16 of
+// the 2C columns; its 16 thread groups each sum every 16th partial (in order, four loads in
+// flight), and the 16 group sums are then added in group order.
+constexpr int LNF_COLS = 16, LNF_GROUPS = 16;
 __global__ __launch_bounds__(256) void layernorm_bwd_final_kernel(float* __restrict__ dw,
                                                                   float* __restrict__ db,
                                                                   const float* __restrict__ partial,
                                                                   int blocks, int C) {
-  __shared__ float red[8][32];
-  const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
-  const int c = blockIdx.x * 32 + cl;
+  __shared__ float red[LNF_GROUPS][LNF_COLS];
+  const int cl = threadIdx.x % LNF_COLS, grp = threadIdx.x / LNF_COLS;
+  const int c = blockIdx.x * LNF_COLS + cl;
   const int which = c / C, cc = c - which * C;
   float s = 0.f;
   if (c < 2 * C) {
     const float* p = partial + (long long)which * C + cc;
     const long long st = 2LL * C;  // between consecutive partials
+    constexpr int G = LNF_GROUPS;
     int k = grp;
-    for (; k + 24 < blocks; k += 32) {  // four independent loads in flight, added in order
-      const float a0 = p[(long long)k * st], a1 = p[(long long)(k + 8) * st];
-      const float a2 = p[(long long)(k + 16) * st], a3 = p[(long long)(k + 24) * st];
+    for (; k + 3 * G < blocks; k += 4 * G) {
+      const float a0 = p[(long long)k * st], a1 = p[(long long)(k + G) * st];
+      const float a2 = p[(long long)(k + 2 * G) * st], a3 = p[(long long)(k + 3 * G) * st];
       s += a0;
       s += a1;
       s += a2;
       s += a3;
     }
-    for (; k < blocks; k += 8) s += p[(long long)k * st];
+    for (; k < blocks; k += G) s += p[(long long)k * st];
   }
   red[grp][cl] = s;
   __syncthreads();
   if (grp == 0 && c < 2 * C) {
     float t = red[0][cl];
 #pragma unroll
-    for (int k = 1; k < 8; k++) t += red[k][cl];
+    for (int k = 1; k < LNF_GROUPS; k++) t += red[k][cl];
     if (which == 0) dw[cc] += t;
     else db[cc] += t;
   }
@@ -602,7 +626,8 @@ int layernorm_backward_t(float* dx, bf16_t* dx_copy, float* dw, float* db, const
   }
   ProfScope ps("layernorm_bwd_final_kernel", 2.0 * blocks * C, 4.0 * (2.0 * blocks * C + 4.0 * C),
                stream);
-  layernorm_bwd_final_kernel<<<(2 * C + 31) / 32, 256, 0, stream>>>(dw, db, partial, blocks, C);
+  layernorm_bwd_final_kernel<<<(2 * C + LNF_COLS - 1) / LNF_COLS, 256, 0, stream>>>(dw, db, partial,
+                                                                                  blocks, C);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
