@@ -287,67 +287,97 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
       dkacc[db][i] = 0.f;
     }
 
+  // The next query tile's Q, dO, lse and D are loaded into registers while this tile is
+  // computed (one wave per SIMD leaves room), and written to LDS after it.
+  constexpr int F4 = HSP / 4, NV = TILE * F4 / NTHR;
+  f32x4 pq[NV], po[NV];
+  float pl = 0.f, pd = 0.f;
+  auto fetch = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int f = tid + NTHR * i;
+      const int row = f / F4, d = 4 * (f % F4);
+      pq[i] = load4_rowcol(base, C3, q0 + row, d, T, hs);
+      po[i] = load4_rowcol(dobase, C, q0 + row, d, T, hs);
+    }
+    if (tid < TILE) {
+      const int t = min(q0 + tid, T - 1);
+      pl = lrow[t];
+      pd = drow[t];
+    }
+  };
+  auto commit = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int f = tid + NTHR * i;
+      const int row = f / F4, d = 4 * (f % F4);
+      *reinterpret_cast<f32x4*>(&Qs[row][d]) = pq[i];
+      *reinterpret_cast<f32x4*>(&dOs[row][d]) = po[i];
+    }
+    if (tid < TILE) {
+      const bool ok = q0 + tid < T;
+      Ls[tid] = ok ? pl * kLog2e : 0.f;
+      Ds[tid] = ok ? pd : 0.f;
+    }
+  };
+
   const int nqt = (T + TILE - 1) / TILE;
+  fetch(kt * TILE);
+  commit(kt * TILE);
+  __syncthreads();
   for (int qt = kt; qt < nqt; qt++) {
     const int q0 = qt * TILE;
-    __syncthreads();
-    load_tile<HSP>(Qs, base, C3, q0, T, hs, tid);
-    load_tile<HSP>(dOs, dobase, C, q0, T, hs, tid);
-    if (tid < TILE) {
-      const int t = q0 + tid;
-      Ls[tid] = t < T ? lrow[t] * kLog2e : 0.f;
-      Ds[tid] = t < T ? drow[t] : 0.f;
-    }
-    __syncthreads();
+    if (qt + 1 < nqt) fetch(q0 + TILE);
     // dS tile (qt, kt) of this (b, head): 64 x 64 floats, [query][key]
     float* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
                              (TILE * TILE);
+    // S and dP of both 32-query sub-blocks first (four independent MFMA chains)
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
-      // sub-blocks entirely above the diagonal for this wave's keys: dS is zero
-      if (q0 + 32 * qb + 31 < kt * TILE + wave * 32) {
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
-          dst[ql * TILE + wave * 32 + r] = 0.f;
-        }
-        continue;
-      }
-      f32x16 s, dp;
+    for (int qb = 0; qb < 2; qb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
+        s[qb][i] = 0.f;
+        dp[qb][i] = 0.f;
       }
 #pragma unroll
-      for (int g = 0; g < HSP / 8; g++) {
+    for (int g = 0; g < HSP / 8; g++)
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
         f32x4 qv = *reinterpret_cast<const f32x4*>(&Qs[32 * qb + r][8 * g + 4 * hf]);
         f32x4 ov = *reinterpret_cast<const f32x4*>(&dOs[32 * qb + r][8 * g + 4 * hf]);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          s = mfma32x32x2(qv[j], kf[4 * g + j], s);
-          dp = mfma32x32x2(ov[j], vf[4 * g + j], dp);
+          s[qb] = mfma32x32x2(qv[j], kf[4 * g + j], s[qb]);
+          dp[qb] = mfma32x32x2(ov[j], vf[4 * g + j], dp[qb]);
         }
       }
-      // s[i], dp[i]: query row ql = 32qb + 8(i/4) + 4hf + i%4, key column = this lane's key
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      // s[qb][i], dp[qb][i]: query row ql = 32qb + 8(i/4) + 4hf + i%4, key = this lane's
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
         const int qa = q0 + ql;
         const bool ok = qa < T && qa >= key;
-        const float p = ok ? exp2f(s[i] * scale_log2 - Ls[ql]) : 0.f;
-        s[i] = p;
-        dp[i] = p * (dp[i] - Ds[ql]);
-        dst[ql * TILE + wave * 32 + r] = dp[i];  // 32 lanes store 32 consecutive keys
+        const float p = ok ? exp2f(s[qb][i] * scale_log2 - Ls[ql]) : 0.f;
+        s[qb][i] = p;
+        dp[qb][i] = p * (dp[qb][i] - Ds[ql]);
+        dst[ql * TILE + wave * 32 + r] = dp[qb][i];  // 32 lanes store 32 consecutive keys
       }
 #pragma unroll
       for (int db = 0; db < ND; db++)
 #pragma unroll
         for (int st = 0; st < 16; st++) {
           const int ql = 32 * qb + 8 * (st / 4) + 4 * hf + (st % 4);
-          dvacc[db] = mfma32x32x2(dOs[ql][32 * db + r], s[st], dvacc[db]);
-          dkacc[db] = mfma32x32x2(Qs[ql][32 * db + r], dp[st], dkacc[db]);
+          dvacc[db] = mfma32x32x2(dOs[ql][32 * db + r], s[qb][st], dvacc[db]);
+          dkacc[db] = mfma32x32x2(Qs[ql][32 * db + r], dp[qb][st], dkacc[db]);
         }
+    }
+    __syncthreads();
+    if (qt + 1 < nqt) {
+      commit(q0 + TILE);
+      __syncthreads();
     }
   }
   if (key < T) {
