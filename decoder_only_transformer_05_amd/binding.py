@@ -47,6 +47,7 @@ SIGNATURES = {
     "gpt2_adamw_step": (_int, [_vp, _f, _f, _f, _f, _f, _int]),
     "gpt2_profile_enable": (_int, [_int]),
     "gpt2_profile_summary": (_int, [ctypes.c_char_p, _sz]),
+    "gpt2_profile_only": (_int, [ctypes.c_char_p]),
     "gpt2_last_error": (ctypes.c_char_p, [_vp]),
     "gpt2_last_global_error": (ctypes.c_char_p, []),
     "gpt2_version": (ctypes.c_char_p, []),
@@ -260,6 +261,11 @@ class GPT2:
 
 def profile_enable(on: bool = True, shapes: bool = False):
     _check(lib().gpt2_profile_enable((2 if shapes else 1) if on else 0))
+
+
+def profile_only(name: str | None):
+    """Record only launches named `name` (None: all)."""
+    _check(lib().gpt2_profile_only(None if not name else name.encode()))
 
 
 def profile_summary() -> dict:

@@ -225,25 +225,22 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
   SlabLoader<AT> la;
   SlabLoader<BT> lb;
   auto compute = [&]() {
-    // all of this slab's fragments first, then its 16 MFMAs
-    bf16x8 af[BK / 16][2], bfr[BK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ks++) {
       const int c = 2 * ks + h;
+      bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int q = 0; q < 2; q++) {
-        af[ks][q] = *reinterpret_cast<const bf16x8*>(&As[0][lds_off(wm0 + 32 * q + r, c)]);
-        bfr[ks][q] = *reinterpret_cast<const bf16x8*>(&Bs[0][lds_off(wn0 + 32 * q + r, c)]);
+        af[q] = *reinterpret_cast<const bf16x8*>(&As[0][lds_off(wm0 + 32 * q + r, c)]);
+        bfr[q] = *reinterpret_cast<const bf16x8*>(&Bs[0][lds_off(wn0 + 32 * q + r, c)]);
       }
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++)
 #pragma unroll
       for (int tm = 0; tm < 2; tm++)
 #pragma unroll
         for (int tn = 0; tn < 2; tn++)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][tn], af[ks][tm],
-                                                                acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn],
+                                                                0, 0, 0);
+    }
     if (do_colsum) {  // row m of the A tile, k chunks 4*half .. 4*half+3 of this slab
       const int m = tid & (BM - 1), half = tid >> 7;
 #pragma unroll

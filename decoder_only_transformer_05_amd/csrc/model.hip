@@ -41,6 +41,7 @@ struct ProfRec {
 };
 bool g_prof_on = false;
 bool g_prof_detail = false;
+std::string g_prof_only;  // record only launches of this name (empty: all)
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;  // events reused across profiling sessions
 size_t g_event_next = 0;
@@ -60,6 +61,7 @@ bool profiling_detail() { return g_prof_detail; }
 
 ProfScope::ProfScope(const char* name, double flop, double bytes, hipStream_t s) : stream(s) {
   if (!g_prof_on) return;
+  if (!g_prof_only.empty() && g_prof_only != name) return;
   hipEvent_t a = next_event(), b = next_event();
   if (!a || !b) return;
   if (hipEventRecord(a, s) != hipSuccess) return;
@@ -549,6 +551,11 @@ int gpt2_profile_enable(int on) {
   g_event_next = 0;
   g_prof_on = on != 0;
   g_prof_detail = on == 2;
+  return GPT2_OK;
+}
+
+int gpt2_profile_only(const char* name) {
+  g_prof_only = name ? name : "";
   return GPT2_OK;
 }
 

@@ -152,6 +152,9 @@ int gpt2_adamw_step(gpt2_model* model, float lr, float beta1, float beta2, float
  * len is too small). Process-wide state; not thread-safe. */
 int gpt2_profile_enable(int on);
 int gpt2_profile_summary(char* buf, size_t len);
+/* Restrict the profiler to launches whose recorded name equals `name` (a copy is kept);
+ * NULL or "" records every launch again. Fewer events perturb the timed work less. */
+int gpt2_profile_only(const char* name);
 
 const char* gpt2_last_error(const gpt2_model* model);
 const char* gpt2_last_global_error(void);
