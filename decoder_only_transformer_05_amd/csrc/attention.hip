@@ -426,18 +426,37 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(TS* __restrict__ dqkv
 #pragma unroll
     for (int i = 0; i < 16; i++) acc[db][i] = 0.f;
 
-  for (int kt = 0; kt <= qt; kt++) {
-    __syncthreads();
-    load_tile<HSP>(Ks, kbase, C3, kt * TILE, T, hs, tid);
+  // the next key tile's K and dS are loaded into registers while this one is used
+  constexpr int F4 = HSP / 4, NK = TILE * F4 / NTHR, NS4 = TILE * TILE / 4 / NTHR;
+  f32x4 pk[NK], ps[NS4];
+  auto fetch = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+      const int f = tid + NTHR * i;
+      pk[i] = load4_rowcol(kbase, C3, kt * TILE + f / F4, 4 * (f % F4), T, hs);
+    }
     const float* ts = src + (long long)kt * TILE * TILE;
 #pragma unroll
-    for (int i = 0; i < TILE * TILE / 4 / NTHR; i++) {
+    for (int i = 0; i < NS4; i++) {
       const int f = tid + NTHR * i;
-      const int row = f / (TILE / 4), c4 = f % (TILE / 4);
-      *reinterpret_cast<f32x4*>(&Ss[row][4 * c4]) =
-          *reinterpret_cast<const f32x4*>(ts + row * TILE + 4 * c4);
+      ps[i] = *reinterpret_cast<const f32x4*>(ts + 4 * f);
+    }
+  };
+  fetch(0);
+  for (int kt = 0; kt <= qt; kt++) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+      const int f = tid + NTHR * i;
+      *reinterpret_cast<f32x4*>(&Ks[f / F4][4 * (f % F4)]) = pk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NS4; i++) {
+      const int f = tid + NTHR * i;
+      *reinterpret_cast<f32x4*>(&Ss[f / (TILE / 4)][4 * (f % (TILE / 4))]) = ps[i];
     }
     __syncthreads();
+    if (kt < qt) fetch(kt + 1);
     // 32 steps of two keys; at step s = 4g + j this half of the wave takes key 8g + 4hf + j
 #pragma unroll
     for (int g = 0; g < TILE / 8; g++) {
