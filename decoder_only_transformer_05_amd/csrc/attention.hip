@@ -132,33 +132,43 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(TS* __restrict__ out,
         for (int j = 0; j < 4; j++) s[kb] = mfma32x32x2(kv[j], qf[4 * g + j], s[kb]);
       }
     }
+    if (key0 + TILE > qt * TILE) {  // the diagonal tile (uniform): mask keys after the query
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * hf + (i % 4);
+          if (key > qm) s[kb][i] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
-    const bool diag = key0 + TILE > qt * TILE;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * hf + (i % 4);
-        if (diag && key > qm) s[kb][i] = -INFINITY;
-        mx = fmaxf(mx, s[kb][i]);
-      }
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[kb][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);  // finite: key0 = 0 <= qm is in the first tile
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
+    // The running max only moves when a tile's max exceeds it by more than 8 (the
+    // exponentials then stay below 2^8, harmless in fp32), so most tiles skip rescaling
+    // oacc and l; O = oacc / l is unchanged by the choice of reference. The first tile
+    // always moves it (m_run = -inf; key 0 <= qm is never masked, so mx is finite).
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < ND; db++)
+      for (int db = 0; db < ND; db++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        const float p = exp2f(s[kb][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_run);
         s[kb][i] = p;
         l_run += p;
       }
-    m_run = m_new;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
         const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
         const int qa = q0 + ql;
         const bool ok = qa < T && qa >= key;
-        const float p = ok ? exp2f(s[qb][i] * scale_log2 - Ls[ql]) : 0.f;
+        const float p = ok ? __builtin_amdgcn_exp2f(s[qb][i] * scale_log2 - Ls[ql]) : 0.f;
         s[qb][i] = p;
         dp[qb][i] = p * (dp[qb][i] - Ds[ql]);
         dst[ql * TILE + wave * 32 + r] = dp[qb][i];  // 32 lanes store 32 consecutive keys

@@ -65,49 +65,86 @@ GPT2_DEVICE_INLINE u32x4 load8(const bf16_t* base, long long ld, int t, int d, i
   return (t < T && d < hs) ? x : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Natural tile: rows row0 .. row0+63 of the tensor -> S[row][d] (HSP columns).
+// Natural tile: rows row0 .. row0+63 of the tensor -> S[row][d] (HSP columns). load()
+// fills registers, store() writes them, so a tile can be fetched ahead of its use.
+template <int HSP>
+struct RowsTile {
+  static constexpr int CPR = HSP / 8, NI = TILE * CPR / NTHR;
+  u32x4 v[NI];
+  __device__ __forceinline__ void load(const bf16_t* base, long long ld, int row0, int T,
+                                       int hs, int tid) {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int f = tid + NTHR * i;
+      v[i] = load8(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int f = tid + NTHR * i;
+      *reinterpret_cast<u32x4*>(S + loff<HSP>(f / CPR, f % CPR)) = v[i];
+    }
+  }
+};
+
+// Transposed tile: rows row0 .. row0+63 of the tensor -> S[d][kpos(row)] (64 columns). A
+// thread moves blocks of 4 rows x 8 columns: four 16-byte loads, eight 8-byte stores.
+template <int HSP>
+struct ColsTile {
+  static constexpr int DG = HSP / 8;             // 8-column groups
+  static constexpr int BLOCKS = (TILE / 4) * DG;  // 4x8 blocks in the tile
+  static constexpr int NI = (BLOCKS + NTHR - 1) / NTHR;
+  u32x4 x[NI][4];
+  __device__ __forceinline__ void load(const bf16_t* base, long long ld, int row0, int T,
+                                       int hs, int tid) {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int b = tid + NTHR * i;
+      if (BLOCKS % NTHR && b >= BLOCKS) break;
+      const int dg = b % DG, rq = b / DG;  // columns 8dg .. +7, rows 4rq .. +3
+#pragma unroll
+      for (int j = 0; j < 4; j++) x[i][j] = load8(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int b = tid + NTHR * i;
+      if (BLOCKS % NTHR && b >= BLOCKS) break;
+      const int dg = b % DG, rq = b / DG;
+      const int p = kpos(4 * rq);  // a multiple of 4: the 4 rows stay consecutive
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int q = e >> 1;
+        uint32_t lo, hi;
+        if ((e & 1) == 0) {
+          lo = (x[i][0][q] & 0xFFFFu) | (x[i][1][q] << 16);
+          hi = (x[i][2][q] & 0xFFFFu) | (x[i][3][q] << 16);
+        } else {
+          lo = (x[i][0][q] >> 16) | (x[i][1][q] & 0xFFFF0000u);
+          hi = (x[i][2][q] >> 16) | (x[i][3][q] & 0xFFFF0000u);
+        }
+        *reinterpret_cast<u32x2*>(S + loff<TILE>(8 * dg + e, p >> 3) + (p & 7)) = u32x2{lo, hi};
+      }
+    }
+  }
+};
+
 template <int HSP>
 GPT2_DEVICE_INLINE void tile_rows(bf16_t* S, const bf16_t* base, long long ld, int row0, int T,
                                   int hs, int tid) {
-  constexpr int CPR = HSP / 8;
-#pragma unroll
-  for (int i = 0; i < TILE * CPR / NTHR; i++) {
-    const int f = tid + NTHR * i;
-    const int row = f / CPR, c = f % CPR;
-    *reinterpret_cast<u32x4*>(S + loff<HSP>(row, c)) = load8(base, ld, row0 + row, 8 * c, T, hs);
-  }
+  RowsTile<HSP> t;
+  t.load(base, ld, row0, T, hs, tid);
+  t.store(S, tid);
 }
 
-// Transposed tile: rows row0 .. row0+63 of the tensor -> S[d][kpos(row)] (64 columns). A
-// thread moves a block of 4 rows x 8 columns: four 16-byte loads, eight 8-byte stores.
 template <int HSP>
 GPT2_DEVICE_INLINE void tile_cols(bf16_t* S, const bf16_t* base, long long ld, int row0, int T,
                                   int hs, int tid) {
-  constexpr int DG = HSP / 8;               // 8-column groups
-  constexpr int BLOCKS = (TILE / 4) * DG;   // 4x8 blocks in the tile
-#pragma unroll
-  for (int i = 0; i < (BLOCKS + NTHR - 1) / NTHR; i++) {
-    const int b = tid + NTHR * i;
-    if (BLOCKS % NTHR && b >= BLOCKS) break;
-    const int dg = b % DG, rq = b / DG;  // columns 8dg .. +7, rows 4rq .. +3
-    u32x4 x[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) x[j] = load8(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs);
-    const int p = kpos(4 * rq);  // a multiple of 4: the 4 rows stay consecutive
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const int q = e >> 1;
-      uint32_t lo, hi;
-      if ((e & 1) == 0) {
-        lo = (x[0][q] & 0xFFFFu) | (x[1][q] << 16);
-        hi = (x[2][q] & 0xFFFFu) | (x[3][q] << 16);
-      } else {
-        lo = (x[0][q] >> 16) | (x[1][q] & 0xFFFF0000u);
-        hi = (x[2][q] >> 16) | (x[3][q] & 0xFFFF0000u);
-      }
-      *reinterpret_cast<u32x2*>(S + loff<TILE>(8 * dg + e, p >> 3) + (p & 7)) = u32x2{lo, hi};
-    }
-  }
+  ColsTile<HSP> t;
+  t.load(base, ld, row0, T, hs, tid);
+  t.store(S, tid);
 }
 
 GPT2_DEVICE_INLINE void tile_of_block(int ntiles, int NH, int* tile, int* head, int* b) {
@@ -156,12 +193,21 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
   float m_run = -INFINITY, l_run = 0.f;  // in units of the scaled log2 domain
 
   const int ntiles = (min(T, (qt + 1) * TILE) + TILE - 1) / TILE;
+  // the next key tile is loaded into registers while this one is used
+  RowsTile<HSP> kn;
+  ColsTile<HSP> vn;
+  kn.load(base + C, C3, 0, T, hs, tid);
+  vn.load(base + 2 * C, C3, 0, T, hs, tid);
   for (int kt = 0; kt < ntiles; kt++) {
     const int key0 = kt * TILE;
     __syncthreads();
-    tile_rows<HSP>(Ks, base + C, C3, key0, T, hs, tid);
-    tile_cols<HSP>(Vt, base + 2 * C, C3, key0, T, hs, tid);
+    kn.store(Ks, tid);
+    vn.store(Vt, tid);
     __syncthreads();
+    if (kt + 1 < ntiles) {
+      kn.load(base + C, C3, key0 + TILE, T, hs, tid);
+      vn.load(base + 2 * C, C3, key0 + TILE, T, hs, tid);
+    }
 
     // S^T for 2 x 32 keys: s[kb][i] = score of key 32kb + 8(i/4) + 4lh + i%4
     f32x16 s[2];
@@ -176,24 +222,33 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
         s[kb] = mfma_bf16(kf, qf[ks], s[kb]);
       }
     }
-    const bool diag = key0 + TILE > qt * TILE;
+    if (key0 + TILE > qt * TILE) {  // the diagonal tile (uniform): mask keys after the query
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * lh + (i % 4);
+          if (key > qm) s[kb][i] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * lh + (i % 4);
-        if (diag && key > qm) s[kb][i] = -INFINITY;
-        mx = fmaxf(mx, s[kb][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);  // key0 = 0 <= qm: finite
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    // the running max moves only by more than 8 (see attention.hip): most tiles skip the
+    // rescale; the first always moves it (key 0 <= qm is never masked)
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < ND; db++)
+      for (int db = 0; db < ND; db++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
     bf16x8 pf[2][2];  // P as the B operand of k step (kb, h)
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
@@ -202,14 +257,13 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const float p0 = exp2f(fmaf(s[kb][8 * hh + 2 * j], scale_log2, -m_new));
-          const float p1 = exp2f(fmaf(s[kb][8 * hh + 2 * j + 1], scale_log2, -m_new));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hh + 2 * j], scale_log2, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hh + 2 * j + 1], scale_log2, -m_run));
           l_run += p0 + p1;
           w[j] = pack2(p0, p1);
         }
         pf[kb][hh] = __builtin_bit_cast(bf16x8, w);
       }
-    m_run = m_new;
     // O^T[d][q] += V^T[d][key] P^T[key][q]
 #pragma unroll
     for (int db = 0; db < ND; db++)
@@ -336,7 +390,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
           const int ql = 32 * qb + 8 * g4 + 4 * lh + j;
           const int qa = q0 + ql;
           const bool ok = qa < T && qa >= key;
-          const float p = ok ? exp2f(fmaf(s[i], scale_log2, -Ls[ql])) : 0.f;
+          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -Ls[ql])) : 0.f;
           pv[j] = p;
           dsv[j] = p * (dp[i] - Ds[ql]);
         }
@@ -406,13 +460,22 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_bf16mma_kernel(
 #pragma unroll
     for (int i = 0; i < 16; i++) acc[db][i] = 0.f;
 
+  // the stored dS^T tile is [key][query] (64 x 64, rows of 64): as rows of a tensor with
+  // T = 64 and hs = 64 it transposes into [query][kpos(key)]. The next key tile is loaded
+  // into registers while this one is used.
+  ColsTile<HSP> kn;
+  ColsTile<TILE> sn;
+  kn.load(kbase, C3, 0, T, hs, tid);
+  sn.load(src, TILE, 0, TILE, TILE, tid);
   for (int kt = 0; kt <= qt; kt++) {
     __syncthreads();
-    tile_cols<HSP>(Kt, kbase, C3, kt * TILE, T, hs, tid);
-    // the stored tile is [key][query] (64 x 64, rows of 64): as rows of a tensor with
-    // T = 64 and hs = 64 it transposes into [query][kpos(key)]
-    tile_cols<TILE>(Sq, src + (long long)kt * TILE * TILE, TILE, 0, TILE, TILE, tid);
+    kn.store(Kt, tid);
+    sn.store(Sq, tid);
     __syncthreads();
+    if (kt < qt) {
+      kn.load(kbase, C3, (kt + 1) * TILE, T, hs, tid);
+      sn.load(src + (long long)(kt + 1) * TILE * TILE, TILE, 0, TILE, TILE, tid);
+    }
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
