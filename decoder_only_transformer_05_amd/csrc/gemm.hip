@@ -261,9 +261,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
     }
 }
 
-// Sums `splits` partial results (each M x N, row stride wld) into C with the epilogue `EPI`
-// (only EPI_STORE-with-bias, EPI_ACCUM and EPI_GELU_BWD are used with splits), adding the
-// partials in split order.
+// The epilogue `EPI` of one output element of a split-K GEMM (only EPI_STORE-with-bias,
+// EPI_ACCUM and EPI_GELU_BWD are used with splits) applied to the sum s of its partials.
 template <int EPI>
 __device__ __forceinline__ float split_epilogue(const Args& g, long long off, int n, float s) {
   if (EPI == EPI_ACCUM) return g.C[off] + s;
@@ -275,11 +274,15 @@ __device__ __forceinline__ float split_epilogue(const Args& g, long long off, in
 
 // Sums `splits` partial results (each M x N, row stride wld) into C with the epilogue `EPI`,
 // adding the partials in split order; four consecutive columns per thread, with all of a
-// group's partial loads issued before the adds. With colsum_part, the last workgroups instead
-// add the per-split column sums (split order) into g.colsum.
+// group's partial loads issued before the adds. With vec4 (ldc a multiple of 4, every output
+// and epilogue operand 16-byte aligned) the epilogue reads and writes whole float4s. With
+// colsum_part, the last workgroups instead add the per-split column sums (split order) into
+// g.colsum. The host keeps M * ceil(N / 4) below 2^31.
 template <int EPI>
-__global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int splits, int wld,
-                                    const float* __restrict__ colsum_part) {
+__global__ __launch_bounds__(256) void split_reduce_kernel(Args g, const float* __restrict__ ws,
+                                                           int splits, int wld,
+                                                           const float* __restrict__ colsum_part,
+                                                           int vec4) {
   // the last ceil(M / blockDim) workgroups reduce the column sums, one m per thread
   const int ncs = colsum_part ? (g.M + blockDim.x - 1) / blockDim.x : 0;
   const int nb = gridDim.x - ncs;
@@ -293,11 +296,10 @@ __global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int sp
     return;
   }
   const int N4 = (g.N + 3) / 4;
-  const long long total = (long long)g.M * N4;
+  const int total = g.M * N4;
   const long long zstride = (long long)g.M * wld;
-  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (long long)nb * blockDim.x) {
-    const int m = (int)(idx / N4), n = 4 * (int)(idx % N4);
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += nb * blockDim.x) {
+    const int m = idx / N4, n = 4 * (idx - m * N4);
     const float* src = ws + (long long)m * wld + n;
     const bool full = n + 3 < g.N;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -319,12 +321,34 @@ __global__ void split_reduce_kernel(Args g, const float* __restrict__ ws, int sp
         for (int j = 0; j < 4 && n + j < g.N; j++) s[j] += src[(long long)z * zstride + j];
     }
     const long long off = (long long)m * g.ldc + n;
+    if (full && vec4) {
+      f32x4 v;
+      if (EPI == EPI_ACCUM) {
+        v = ld4(g.C + off) + s;
+      } else if (EPI == EPI_GELU_BWD) {
+        const f32x4 r = ld4(g.R + off);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (n + j >= g.N) break;
-      const float v = split_epilogue<EPI>(g, off + j, n + j, s[j]);
-      g.C[off + j] = v;
-      if (EPI == EPI_GELU) g.C2[off + j] = gelu_fwd(v);
+        for (int j = 0; j < 4; j++) v[j] = s[j] * gelu_bwd(r[j]);
+      } else {
+        v = s;
+        if (g.bias) v += ld4(g.bias + n);
+        if (EPI == EPI_RESID) v += ld4(g.R + off);
+      }
+      st4(g.C + off, v);
+      if (EPI == EPI_GELU) {
+        f32x4 gv;
+#pragma unroll
+        for (int j = 0; j < 4; j++) gv[j] = gelu_fwd(v[j]);
+        st4(g.C2 + off, gv);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (n + j >= g.N) break;
+        const float v = split_epilogue<EPI>(g, off + j, n + j, s[j]);
+        g.C[off + j] = v;
+        if (EPI == EPI_GELU) g.C2[off + j] = gelu_fwd(v);
+      }
     }
   }
 }
@@ -456,6 +480,12 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
     ProfScope ps(name, flop, in_bytes + 4.0 * MN * out_factor, stream);
     launch(a, g.a_trans, g.b_trans, g.epi, dim3(tiles), stream);
   } else {
+    // the reduction indexes the M x ceil(N/4) output groups with 32-bit integers
+    const long long total = (long long)g.M * ((g.N + 3) / 4);
+    if (total >= (1LL << 31) - 65536LL * 256) {
+      set_global_error("gemm: split-K output too large (%d x %d)", g.M, g.N);
+      return -1;
+    }
     Args p = a;
     p.C = workspace;
     p.ldc = split_ld(g.N);
@@ -474,9 +504,11 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
       ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
       launch(p, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
     }
-    const long long total = (long long)g.M * ((g.N + 3) / 4);
     int blocks = (int)((total + 255) / 256);
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > 65536) blocks = 65536;
+    auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    const int vec4 = g.ldc % 4 == 0 && al(g.C) && (!g.C2 || al(g.C2)) && (!g.R || al(g.R)) &&
+                     (!g.bias || al(g.bias));
     snprintf(name, sizeof(name), "split_reduce_kernel<%d>", (int)g.epi);
     {
       const float* cp = g.colsum ? colsum_part : nullptr;
@@ -485,11 +517,11 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
                    4.0 * MN * (splits + out_factor) + (cp ? 4.0 * (splits + 2.0) * g.M : 0.0),
                    stream);
       switch (g.epi) {
-        case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-        case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-        case EPI_GELU: split_reduce_kernel<EPI_GELU><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-        case EPI_RESID: split_reduce_kernel<EPI_RESID><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-        default: split_reduce_kernel<EPI_STORE><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+        case EPI_ACCUM: split_reduce_kernel<EPI_ACCUM><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp, vec4); break;
+        case EPI_GELU_BWD: split_reduce_kernel<EPI_GELU_BWD><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp, vec4); break;
+        case EPI_GELU: split_reduce_kernel<EPI_GELU><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp, vec4); break;
+        case EPI_RESID: split_reduce_kernel<EPI_RESID><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp, vec4); break;
+        default: split_reduce_kernel<EPI_STORE><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp, vec4); break;
       }
     }
   }

@@ -221,9 +221,27 @@ int lnb_rows(int N) {
   return rows;
 }
 
+// one row's operands of the LayerNorm backward, held in registers (zeros past C)
+template <int VPL, typename T>
+GPT2_DEVICE_INLINE void lnb_fetch(f32x4 (&dy)[VPL], f32x4 (&xv)[VPL], f32x4 (&dxo)[VPL],
+                                  const T* dout, const T* x, const float* dx, int row, int C,
+                                  int lane, int accumulate) {
+  const int C4 = C / 4;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const int c4 = lane + 64 * i;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const long long o = (long long)row * C + 4 * c4;
+    dy[i] = c4 < C4 ? ld4(dout + o) : zero;
+    xv[i] = c4 < C4 ? ld4(x + o) : zero;
+    dxo[i] = c4 < C4 && accumulate ? ld4(dx + o) : zero;
+  }
+}
+
 // dx (+)= rstd * (g - mean(g) - n * mean(g*n)), g = w * dout, n = (x - mean) * rstd;
 // per workgroup, partial[blk][0][:] = sum of n*dout, partial[blk][1][:] = sum of dout over
-// its rows (each wave sums its rows in order, then the four waves are added in order).
+// its rows (each wave sums its rows in order, then the four waves are added in order). A
+// wave's next row is loaded while the current one is computed.
 // dx is fp32; with bf16 activations dx_copy (if not null) receives dx rounded to bf16.
 template <int VPL, typename T>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
@@ -244,25 +262,39 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   }
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(N, r0 + rows_per_block);
-  for (int row = r0 + wave; row < r1; row += 4) {
-    const float mu = mean[row], rs = rstd[row];
-    const T* dyr = dout + (long long)row * C;
-    const T* xr = x + (long long)row * C;
-    f32x4 dy[VPL], nv[VPL];
+  f32x4 dyn[VPL], xn[VPL], dxn[VPL];
+  float mun = 0.f, rsn = 0.f;
+  int row = r0 + wave;
+  if (row < r1) {
+    lnb_fetch<VPL>(dyn, xn, dxn, dout, x, dx, row, C, lane, accumulate);
+    mun = mean[row];
+    rsn = rstd[row];
+  }
+  for (; row < r1; row += 4) {
+    f32x4 dy[VPL], nv[VPL], dxo[VPL];
+    const float mu = mun, rs = rsn;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+      dy[i] = dyn[i];
+      nv[i] = xn[i];
+      dxo[i] = dxn[i];
+    }
+    if (row + 4 < r1) {
+      lnb_fetch<VPL>(dyn, xn, dxn, dout, x, dx, row + 4, C, lane, accumulate);
+      mun = mean[row + 4];
+      rsn = rstd[row + 4];
+    }
     float sg = 0.f, sgn = 0.f;
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
-      const int c4 = lane + 64 * i;
-      if (c4 < C4) {
-        dy[i] = ld4(dyr + 4 * c4);
-        nv[i] = (ld4(xr + 4 * c4) - mu) * rs;
+      if (lane + 64 * i < C4) {
+        nv[i] = (nv[i] - mu) * rs;
         f32x4 g = wv[i] * dy[i];
         sg += (g[0] + g[1]) + (g[2] + g[3]);
         f32x4 gn = g * nv[i];
         sgn += (gn[0] + gn[1]) + (gn[2] + gn[3]);
       } else {
-        dy[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        nv[i] = dy[i];
+        nv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     const float mg = warp_sum(sg) / C, mgn = warp_sum(sgn) / C;
@@ -272,7 +304,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
       const int c4 = lane + 64 * i;
       if (c4 < C4) {
         f32x4 d = (wv[i] * dy[i] - mg - nv[i] * mgn) * rs;
-        if (accumulate) d += ld4(dxr + 4 * c4);
+        if (accumulate) d += dxo[i];
         st4(dxr + 4 * c4, d);
         if (dx_copy) st4(dx_copy + (long long)row * C + 4 * c4, d);
         dw[i] += nv[i] * dy[i];
@@ -399,27 +431,35 @@ __global__ __launch_bounds__(256) void xent_fwd_kernel(float* __restrict__ losse
   }
 }
 
-// in place: logits[r, v] <- (softmax - onehot(target)) * dloss for v < V, 0 on the padding
+// in place: logits[r, v] <- (softmax - onehot(target)) * dloss for v < V, 0 on the padding.
+// One 16-byte vector per thread over a flat grid: a workgroup covers 256 vectors of one row
+// (`chunks` workgroups per row), so the whole matrix streams in address order.
 template <typename T>
 __global__ __launch_bounds__(256) void xent_bwd_kernel(T* __restrict__ logits,
                                                        const float* __restrict__ lse,
                                                        const int32_t* __restrict__ targets,
-                                                       float dloss, int N, int V, int ld) {
-  const int row = blockIdx.x;
+                                                       float dloss, int V, int ld, int chunks) {
+  constexpr int G = 16 / (4 * sizeof(T));  // groups of 4 elements per thread
+  const int row = blockIdx.x / chunks;
+  const int c0 = ((blockIdx.x - row * chunks) * 256 + threadIdx.x) * 4 * G;
+  if (c0 >= ld) return;
   T* z = logits + (long long)row * ld;
   const float l = lse[row];
   int y = targets[row];
   if (y < 0 || y >= V) y = 0;
-  const int L4 = ld / 4;
-  for (int c4 = threadIdx.x; c4 < L4; c4 += 256) {
-    f32x4 v = ld4(z + 4 * c4);
+  f32x4 v[G];
+#pragma unroll
+  for (int k = 0; k < G; k++)
+    if (c0 + 4 * k < ld) v[k] = ld4(z + c0 + 4 * k);
+#pragma unroll
+  for (int k = 0; k < G; k++) {
+    const int c = c0 + 4 * k;
+    if (c >= ld) break;
     f32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int c = 4 * c4 + j;
-      o[j] = c < V ? (__expf(v[j] - l) - (c == y ? 1.f : 0.f)) * dloss : 0.f;
-    }
-    st4(z + 4 * c4, o);
+    for (int j = 0; j < 4; j++)
+      o[j] = c + j < V ? (__expf(v[k][j] - l) - (c + j == y ? 1.f : 0.f)) * dloss : 0.f;
+    st4(z + c, o);
   }
 }
 
@@ -442,37 +482,49 @@ __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
 // ---------------------------------------------------------------------------------------
 // AdamW
 // ---------------------------------------------------------------------------------------
-// pbf (if not null) receives the updated parameters rounded to bf16
-__global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
-                             float* __restrict__ m, float* __restrict__ v,
-                             bf16_t* __restrict__ pbf, long long n4, long long n, float lr,
-                             float b1, float b2, float eps, float wd, float inv_c1,
-                             float inv_c2) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (long long)gridDim.x * blockDim.x) {
+// One float4 of parameters per thread over a flat grid (streams HBM faster than a
+// grid-stride loop); threads n4 ... n4 + (n % 4) - 1 take the scalar tail. pbf (if not null)
+// receives the updated parameters rounded to bf16.
+GPT2_DEVICE_INLINE float adamw_one(float& p, float g, float& m, float& v, float lr, float b1,
+                                   float b2, float eps, float wd, float inv_c1, float inv_c2) {
+  m = b1 * m + (1.f - b1) * g;
+  v = b2 * v + (1.f - b2) * g * g;
+  const float mh = m * inv_c1, vh = v * inv_c2;
+  p -= lr * (mh / (sqrtf(vh) + eps) + wd * p);
+  return p;
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
+                                                    const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    bf16_t* __restrict__ pbf, long long n4,
+                                                    long long n, float lr, float b1, float b2,
+                                                    float eps, float wd, float inv_c1,
+                                                    float inv_c2) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) {
     f32x4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      mm[j] = b1 * mm[j] + (1.f - b1) * gg[j];
-      vv[j] = b2 * vv[j] + (1.f - b2) * gg[j] * gg[j];
-      const float mh = mm[j] * inv_c1, vh = vv[j] * inv_c2;
-      pp[j] -= lr * (mh / (sqrtf(vh) + eps) + wd * pp[j]);
+      float pj = pp[j], mj = mm[j], vj = vv[j];
+      adamw_one(pj, gg[j], mj, vj, lr, b1, b2, eps, wd, inv_c1, inv_c2);
+      pp[j] = pj;
+      mm[j] = mj;
+      vv[j] = vj;
     }
     st4(p + 4 * i, pp);
     st4(m + 4 * i, mm);
     st4(v + 4 * i, vv);
     if (pbf) st4(pbf + 4 * i, pp);
-  }
-  // scalar tail (n not a multiple of 4)
-  if (blockIdx.x == 0 && threadIdx.x < (n - 4 * n4)) {
-    const long long i = 4 * n4 + threadIdx.x;
-    const float gg = g[i];
-    const float mm = b1 * m[i] + (1.f - b1) * gg;
-    const float vv = b2 * v[i] + (1.f - b2) * gg * gg;
-    m[i] = mm;
-    v[i] = vv;
-    p[i] -= lr * ((mm * inv_c1) / (sqrtf(vv * inv_c2) + eps) + wd * p[i]);
-    if (pbf) pbf[i] = f32_to_bf16(p[i]);
+  } else {
+    const long long e = 4 * n4 + (i - n4);
+    if (e >= n) return;
+    float pe = p[e], me = m[e], ve = v[e];
+    adamw_one(pe, g[e], me, ve, lr, b1, b2, eps, wd, inv_c1, inv_c2);
+    p[e] = pe;
+    m[e] = me;
+    v[e] = ve;
+    if (pbf) pbf[e] = f32_to_bf16(pe);
   }
 }
 
@@ -668,8 +720,14 @@ int crossentropy_backward_t(T* logits, const float* lse, const int32_t* targets,
     set_global_error("crossentropy_backward: bad arguments");
     return -1;
   }
+  const int per_block = 256 * 16 / (int)sizeof(T);  // elements one workgroup covers
+  const int chunks = (ld + per_block - 1) / per_block;
+  if ((long long)N * chunks >= (1LL << 31)) {
+    set_global_error("crossentropy_backward: too many rows");
+    return -1;
+  }
   ProfScope ps(name, 3.0 * N * V, 2.0 * sizeof(T) * N * ld + 8.0 * N, stream);
-  xent_bwd_kernel<T><<<N, 256, 0, stream>>>(logits, lse, targets, dloss, N, V, ld);
+  xent_bwd_kernel<T><<<N * chunks, 256, 0, stream>>>(logits, lse, targets, dloss, V, ld, chunks);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
@@ -715,9 +773,10 @@ int adamw(float* p, const float* g, float* m, float* v, bf16_t* pbf, size_t n, f
   const float inv_c1 = (float)(1.0 / (1.0 - pow((double)beta1, t)));
   const float inv_c2 = (float)(1.0 / (1.0 - pow((double)beta2, t)));
   ProfScope ps("adamw_kernel", 12.0 * n, (pbf ? 30.0 : 28.0) * n, stream);
-  adamw_kernel<<<blocks_for(n4, 256, 16384), 256, 0, stream>>>(p, g, m, v, pbf, n4, (long long)n,
-                                                               lr, beta1, beta2, eps, wd, inv_c1,
-                                                               inv_c2);
+  const long long threads = n4 + (long long)(n - 4 * n4);
+  if (threads == 0) return 0;
+  adamw_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
+      p, g, m, v, pbf, n4, (long long)n, lr, beta1, beta2, eps, wd, inv_c1, inv_c2);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
