@@ -249,23 +249,55 @@ __global__ void attn_bwd_rowdot_kernel(float* __restrict__ D, const TS* __restri
 GPT2_DEVICE_INLINE long long tri_index(int qt, int kt) { return (long long)qt * (qt + 1) / 2 + kt; }
 GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 2; }
 
-// dK, dV for a tile of 64 keys (32 per wave), looping over query tiles from the diagonal.
-// It also writes dS = P * (dP - D) of every causal tile it visits to `dsbuf`, from which
-// attn_bwd_dq_kernel forms dQ = dS K without recomputing P and dP.
+// dK, dV for a block of 128 keys (32 per wave, four waves), looping over 64-query tiles from
+// the diagonal. It also writes dS = P * (dP - D) of every causal 64x64 tile it visits to
+// `dsbuf`, from which attn_bwd_dq_kernel forms dQ = dS K without recomputing P and dP.
+// The query tile is held in LDS twice: row-major for S = Q K^T and dP = dO V^T (a lane reads
+// four consecutive head dims of its query), and transposed for dV^T = dO^T P^T and
+// dK^T = Q^T dS^T (a lane reads four consecutive queries of its head dim), so every MFMA
+// operand comes from a 16-byte LDS read. With 64-dim heads this fits two waves per SIMD.
+constexpr int DK_KEYS = 128, DK_THR = 256;
+
+// Block order of the dK/dV grid: XCD-local (as tile_of_block), and inside each XCD's share
+// all first key blocks (the most query tiles) before all second ones, and so on, so the
+// longest blocks start first. Falls back to the plain XCD-local order when the grid does not
+// split evenly.
+GPT2_DEVICE_INLINE void dkdv_block(int nkb, int NH, int* kb, int* head, int* b) {
+  const int n = gridDim.x;
+  const int per = n >> 3;
+  int bh, k;
+  if ((n & 7) == 0 && per % nkb == 0) {
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int groups = per / nkb;  // (batch, head) pairs on this XCD
+    k = idx / groups;
+    bh = xcd * groups + idx % groups;
+  } else {
+    const int lid = xcd_logical_block(blockIdx.x, n);
+    k = lid % nkb;
+    bh = lid / nkb;
+  }
+  *kb = k;
+  *head = bh % NH;
+  *b = bh / NH;
+}
+
 template <int HSP, typename TS>
-__global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
-    TS* __restrict__ dqkv, float* __restrict__ dsbuf, const TS* __restrict__ dout,
-    const TS* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Drow,
-    int T, int C, int NH, int hs, float scale, float scale_log2) {
-  constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
+__global__ __launch_bounds__(DK_THR) __attribute__((amdgpu_waves_per_eu(HSP <= 64 ? 2 : 1)))
+void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
+                          const TS* __restrict__ dout, const TS* __restrict__ qkv,
+                          const float* __restrict__ lse, const float* __restrict__ Drow, int T,
+                          int C, int NH, int hs, float scale, float scale_log2) {
+  constexpr int LD = HSP + 4, LDT = TILE + 4, NS = HSP / 2, ND = HSP / 32;
   __shared__ float Qs[TILE][LD];
   __shared__ float dOs[TILE][LD];
+  __shared__ float QT[HSP][LDT];
+  __shared__ float dOT[HSP][LDT];
   __shared__ float Ls[TILE];
   __shared__ float Ds[TILE];
 
-  const int nkt = (T + TILE - 1) / TILE;
-  int kt, head, b;
-  tile_of_block(nkt, NH, &kt, &head, &b);
+  const int nkb = (T + DK_KEYS - 1) / DK_KEYS;
+  int kb, head, b;
+  dkdv_block(nkb, NH, &kb, &head, &b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
@@ -273,8 +305,11 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
   const TS* dobase = dout + (long long)b * T * C + (long long)head * hs;
   const float* lrow = lse + ((long long)b * NH + head) * T;
   const float* drow = Drow + ((long long)b * NH + head) * T;
-  const int key = kt * TILE + wave * 32 + r;
+  const int key0 = kb * DK_KEYS + wave * 32;  // first key of this wave
+  const int key = key0 + r;
   const int km = min(key, T - 1);
+  const int kt = key0 / TILE;             // this wave's 64-key tile in the dS layout
+  const int kcol = key0 - kt * TILE + r;  // this lane's column in that tile
 
   float kf[NS], vf[NS];
 #pragma unroll
@@ -297,97 +332,80 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dkdv_kernel(
       dkacc[db][i] = 0.f;
     }
 
-  // The next query tile's Q, dO, lse and D are loaded into registers while this tile is
-  // computed (one wave per SIMD leaves room), and written to LDS after it.
-  constexpr int F4 = HSP / 4, NV = TILE * F4 / NTHR;
-  f32x4 pq[NV], po[NV];
-  float pl = 0.f, pd = 0.f;
-  auto fetch = [&](int q0) __attribute__((always_inline)) {
+  const int nqt = (T + TILE - 1) / TILE;
+  for (int qt = kb * DK_KEYS / TILE; qt < nqt; qt++) {
+    const int q0 = qt * TILE;
+    __syncthreads();
+    constexpr int F4 = HSP / 4;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-      const int f = tid + NTHR * i;
+    for (int i = 0; i < TILE * F4 / DK_THR; i++) {
+      const int f = tid + DK_THR * i;
       const int row = f / F4, d = 4 * (f % F4);
-      pq[i] = load4_rowcol(base, C3, q0 + row, d, T, hs);
-      po[i] = load4_rowcol(dobase, C, q0 + row, d, T, hs);
-    }
-    if (tid < TILE) {
-      const int t = min(q0 + tid, T - 1);
-      pl = lrow[t];
-      pd = drow[t];
-    }
-  };
-  auto commit = [&](int q0) __attribute__((always_inline)) {
+      const f32x4 qv = load4_rowcol(base, C3, q0 + row, d, T, hs);
+      const f32x4 ov = load4_rowcol(dobase, C, q0 + row, d, T, hs);
+      *reinterpret_cast<f32x4*>(&Qs[row][d]) = qv;
+      *reinterpret_cast<f32x4*>(&dOs[row][d]) = ov;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-      const int f = tid + NTHR * i;
-      const int row = f / F4, d = 4 * (f % F4);
-      *reinterpret_cast<f32x4*>(&Qs[row][d]) = pq[i];
-      *reinterpret_cast<f32x4*>(&dOs[row][d]) = po[i];
+      for (int j = 0; j < 4; j++) {
+        QT[d + j][row] = qv[j];
+        dOT[d + j][row] = ov[j];
+      }
     }
     if (tid < TILE) {
       const bool ok = q0 + tid < T;
-      Ls[tid] = ok ? pl * kLog2e : 0.f;
-      Ds[tid] = ok ? pd : 0.f;
+      const int t = min(q0 + tid, T - 1);
+      Ls[tid] = ok ? lrow[t] * kLog2e : 0.f;
+      Ds[tid] = ok ? drow[t] : 0.f;
     }
-  };
-
-  const int nqt = (T + TILE - 1) / TILE;
-  fetch(kt * TILE);
-  commit(kt * TILE);
-  __syncthreads();
-  for (int qt = kt; qt < nqt; qt++) {
-    const int q0 = qt * TILE;
-    if (qt + 1 < nqt) fetch(q0 + TILE);
+    __syncthreads();
+    if (qt < kt) continue;  // every query of this tile precedes this wave's keys
     // dS tile (qt, kt) of this (b, head): 64 x 64 floats, [query][key]
     float* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
                              (TILE * TILE);
-    // S and dP of both 32-query sub-blocks first (four independent MFMA chains)
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; qb++)
+#pragma unroll 1
+    for (int qb = 0; qb < 2; qb++) {
+      f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        s[qb][i] = 0.f;
-        dp[qb][i] = 0.f;
+        s[i] = 0.f;
+        dp[i] = 0.f;
       }
 #pragma unroll
-    for (int g = 0; g < HSP / 8; g++)
-#pragma unroll
-      for (int qb = 0; qb < 2; qb++) {
-        f32x4 qv = *reinterpret_cast<const f32x4*>(&Qs[32 * qb + r][8 * g + 4 * hf]);
-        f32x4 ov = *reinterpret_cast<const f32x4*>(&dOs[32 * qb + r][8 * g + 4 * hf]);
+      for (int g = 0; g < HSP / 8; g++) {
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(&Qs[32 * qb + r][8 * g + 4 * hf]);
+        const f32x4 ov = *reinterpret_cast<const f32x4*>(&dOs[32 * qb + r][8 * g + 4 * hf]);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          s[qb] = mfma32x32x2(qv[j], kf[4 * g + j], s[qb]);
-          dp[qb] = mfma32x32x2(ov[j], vf[4 * g + j], dp[qb]);
+          s = mfma32x32x2(qv[j], kf[4 * g + j], s);
+          dp = mfma32x32x2(ov[j], vf[4 * g + j], dp);
         }
       }
-#pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
-      // s[qb][i], dp[qb][i]: query row ql = 32qb + 8(i/4) + 4hf + i%4, key = this lane's
+      // s[i], dp[i]: query ql = 32qb + 8(i/4) + 4hf + i%4, key = this lane's
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
         const int qa = q0 + ql;
         const bool ok = qa < T && qa >= key;
-        const float p = ok ? __builtin_amdgcn_exp2f(s[qb][i] * scale_log2 - Ls[ql]) : 0.f;
-        s[qb][i] = p;
-        dp[qb][i] = p * (dp[qb][i] - Ds[ql]);
-        dst[ql * TILE + wave * 32 + r] = dp[qb][i];  // 32 lanes store 32 consecutive keys
+        const float p = ok ? __builtin_amdgcn_exp2f(s[i] * scale_log2 - Ls[ql]) : 0.f;
+        s[i] = p;
+        dp[i] = p * (dp[i] - Ds[ql]);
+        dst[ql * TILE + kcol] = dp[i];  // 32 lanes store 32 consecutive keys
       }
+      // dV^T[d][key] += dO[q][d] P[q][key] and dK^T[d][key] += Q[q][d] dS[q][key] over this
+      // sub-block's queries; entries 4sg .. 4sg+3 of s and dp are four consecutive queries
 #pragma unroll
       for (int db = 0; db < ND; db++)
 #pragma unroll
-        for (int st = 0; st < 16; st++) {
-          const int ql = 32 * qb + 8 * (st / 4) + 4 * hf + (st % 4);
-          dvacc[db] = mfma32x32x2(dOs[ql][32 * db + r], s[qb][st], dvacc[db]);
-          dkacc[db] = mfma32x32x2(Qs[ql][32 * db + r], dp[qb][st], dkacc[db]);
+        for (int sg = 0; sg < 4; sg++) {
+          const int ql0 = 32 * qb + 8 * sg + 4 * hf;
+          const f32x4 ot = *reinterpret_cast<const f32x4*>(&dOT[32 * db + r][ql0]);
+          const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&QT[32 * db + r][ql0]);
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            dvacc[db] = mfma32x32x2(ot[j], s[4 * sg + j], dvacc[db]);
+            dkacc[db] = mfma32x32x2(qt4[j], dp[4 * sg + j], dkacc[db]);
+          }
         }
-    }
-    __syncthreads();
-    if (qt + 1 < nqt) {
-      commit(q0 + TILE);
-      __syncthreads();
     }
   }
   if (key < T) {
@@ -583,9 +601,10 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
     ProfScope ps(f32 ? "attn_bwd_dkdv_kernel" : "attn_bwd_dkdv_bf16_kernel",
                  6.0 * B * NH * hs * tri,
                  es * (3.0 * BTC + BTC + 2.0 * BTC) + 4.0 * (2.0 * rows + B * NH * tri), stream);
-    if (hsp == 32) attn_bwd_dkdv_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else if (hsp == 64) attn_bwd_dkdv_kernel<64, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else attn_bwd_dkdv_kernel<128, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    const dim3 gk(((T + DK_KEYS - 1) / DK_KEYS) * NH * B);
+    if (hsp == 32) attn_bwd_dkdv_kernel<32, TS><<<gk, DK_THR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hsp == 64) attn_bwd_dkdv_kernel<64, TS><<<gk, DK_THR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dkdv_kernel<128, TS><<<gk, DK_THR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
   }
   {  // dQ = dS K
     ProfScope ps(f32 ? "attn_bwd_dq_kernel" : "attn_bwd_dq_bf16_kernel", 2.0 * B * NH * hs * tri,

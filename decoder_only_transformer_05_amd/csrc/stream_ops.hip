@@ -213,11 +213,12 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* __restrict__ out,
   }
 }
 
-// rows per workgroup in the backward: 32, halved (down to 4) until there are at least 1024
-// workgroups, so short batches still fill the chip
+// rows per workgroup in the backward: 32, halved (down to 4) until there are at least 512
+// workgroups, so short batches still fill the chip (fewer workgroups, fewer partial sums
+// for the column reduction)
 int lnb_rows(int N) {
   int rows = 32;
-  while (rows > 4 && (N + rows - 1) / rows < 1024) rows /= 2;
+  while (rows > 4 && (N + rows - 1) / rows < 512) rows /= 2;
   return rows;
 }
 
@@ -331,10 +332,10 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   }
 }
 
-// dw[c] += sum_k partial[k][0][c], db[c] += sum_k partial[k][1][c]. A workgroup owns 16 of
-// the 2C columns; its 16 thread groups each sum every 16th partial (in order, four loads in
-// flight), and the 16 group sums are then added in group order.
-constexpr int LNF_COLS = 16, LNF_GROUPS = 16;
+// dw[c] += sum_k partial[k][0][c], db[c] += sum_k partial[k][1][c]. A workgroup owns 8 of
+// the 2C columns; its 32 thread groups each sum every 32nd partial (in order, four loads in
+// flight), and the 32 group sums are then added in group order.
+constexpr int LNF_COLS = 8, LNF_GROUPS = 32;
 __global__ __launch_bounds__(256) void layernorm_bwd_final_kernel(float* __restrict__ dw,
                                                                   float* __restrict__ db,
                                                                   const float* __restrict__ partial,
