@@ -222,11 +222,10 @@ int lnb_rows(int N) {
   return rows;
 }
 
-// one row's operands of the LayerNorm backward, held in registers (zeros past C)
+// one row's dout and x for the LayerNorm backward, held in registers (zeros past C)
 template <int VPL, typename T>
-GPT2_DEVICE_INLINE void lnb_fetch(f32x4 (&dy)[VPL], f32x4 (&xv)[VPL], f32x4 (&dxo)[VPL],
-                                  const T* dout, const T* x, const float* dx, int row, int C,
-                                  int lane, int accumulate) {
+GPT2_DEVICE_INLINE void lnb_fetch(f32x4 (&dy)[VPL], f32x4 (&xv)[VPL], const T* dout,
+                                  const T* x, int row, int C, int lane) {
   const int C4 = C / 4;
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
@@ -235,14 +234,15 @@ GPT2_DEVICE_INLINE void lnb_fetch(f32x4 (&dy)[VPL], f32x4 (&xv)[VPL], f32x4 (&dx
     const long long o = (long long)row * C + 4 * c4;
     dy[i] = c4 < C4 ? ld4(dout + o) : zero;
     xv[i] = c4 < C4 ? ld4(x + o) : zero;
-    dxo[i] = c4 < C4 && accumulate ? ld4(dx + o) : zero;
   }
 }
 
 // dx (+)= rstd * (g - mean(g) - n * mean(g*n)), g = w * dout, n = (x - mean) * rstd;
 // per workgroup, partial[blk][0][:] = sum of n*dout, partial[blk][1][:] = sum of dout over
-// its rows (each wave sums its rows in order, then the four waves are added in order). A
-// wave's next row is loaded while the current one is computed.
+// its rows. Each wave sums its rows in order into its own LDS slice (so the column sums
+// take no registers across rows), then the four slices are added in wave order. A wave's
+// next row of dout and x is loaded while the current one is computed; the dx being
+// accumulated into is loaded at the start of its row and used after the two row sums.
 // dx is fp32; with bf16 activations dx_copy (if not null) receives dx rounded to bf16.
 template <int VPL, typename T>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
@@ -253,21 +253,25 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   extern __shared__ float red[];  // [4 waves][2][C]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C4 = C / 4;
-  f32x4 wv[VPL], dw[VPL], db[VPL];
+  float* rdw = red + (wave * 2 + 0) * C;
+  float* rdb = red + (wave * 2 + 1) * C;
+  f32x4 wv[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
     const int c4 = lane + 64 * i;
     wv[i] = c4 < C4 ? ld4(w + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    dw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    db[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c4 < C4) {
+      st4(rdw + 4 * c4, f32x4{0.f, 0.f, 0.f, 0.f});
+      st4(rdb + 4 * c4, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
   }
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(N, r0 + rows_per_block);
-  f32x4 dyn[VPL], xn[VPL], dxn[VPL];
+  f32x4 dyn[VPL], xn[VPL];
   float mun = 0.f, rsn = 0.f;
   int row = r0 + wave;
   if (row < r1) {
-    lnb_fetch<VPL>(dyn, xn, dxn, dout, x, dx, row, C, lane, accumulate);
+    lnb_fetch<VPL>(dyn, xn, dout, x, row, C, lane);
     mun = mean[row];
     rsn = rstd[row];
   }
@@ -278,10 +282,15 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     for (int i = 0; i < VPL; i++) {
       dy[i] = dyn[i];
       nv[i] = xn[i];
-      dxo[i] = dxn[i];
+    }
+    float* dxr = dx + (long long)row * C;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+      const int c4 = lane + 64 * i;
+      dxo[i] = c4 < C4 && accumulate ? ld4(dxr + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (row + 4 < r1) {
-      lnb_fetch<VPL>(dyn, xn, dxn, dout, x, dx, row + 4, C, lane, accumulate);
+      lnb_fetch<VPL>(dyn, xn, dout, x, row + 4, C, lane);
       mun = mean[row + 4];
       rsn = rstd[row + 4];
     }
@@ -299,7 +308,6 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
       }
     }
     const float mg = warp_sum(sg) / C, mgn = warp_sum(sgn) / C;
-    float* dxr = dx + (long long)row * C;
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
       const int c4 = lane + 64 * i;
@@ -308,17 +316,9 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
         if (accumulate) d += dxo[i];
         st4(dxr + 4 * c4, d);
         if (dx_copy) st4(dx_copy + (long long)row * C + 4 * c4, d);
-        dw[i] += nv[i] * dy[i];
-        db[i] += dy[i];
+        st4(rdw + 4 * c4, ld4(rdw + 4 * c4) + nv[i] * dy[i]);
+        st4(rdb + 4 * c4, ld4(rdb + 4 * c4) + dy[i]);
       }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < VPL; i++) {
-    const int c4 = lane + 64 * i;
-    if (c4 < C4) {
-      st4(red + (wave * 2 + 0) * C + 4 * c4, dw[i]);
-      st4(red + (wave * 2 + 1) * C + 4 * c4, db[i]);
     }
   }
   __syncthreads();
