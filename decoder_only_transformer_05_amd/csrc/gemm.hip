@@ -9,7 +9,7 @@
 // accumulate, and the GELU backward (section 1.10).
 //
 // Tiling: a 256-thread workgroup owns a 128x128 tile of C; its four waves own 64x64
-// sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances 32 at a time through two LDS
+// sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances 16 at a time through two LDS
 // buffers: global loads for the next K-slab are issued before the MFMAs of the current one
 // and written to the other buffer afterwards, so one barrier per slab suffices.
 // LDS holds both operands K-major ([k][m] and [k][n], row stride 130 floats): a lane's two
