@@ -225,6 +225,10 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
   SlabLoader<AT> la;
   SlabLoader<BT> lb;
   auto compute = [&]() {
+    // the compiler's MFMA / LDS-read interleaving strategy 1 (measured 1% faster per step
+    // than its default schedule on the 774M shapes; strategy 0 and explicit prefetch depth
+    // 2 or 3 were slower)
+    __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ks++) {
       const int c = 2 * ks + h;
