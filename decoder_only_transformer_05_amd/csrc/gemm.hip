@@ -57,8 +57,11 @@ constexpr int GROUP_M = 8;  // m-tiles that sweep the n-tiles together (L2 reuse
 // The loads carry no branches and no use of their values before the LDS store, so all eight
 // of a thread's loads stay in flight across the MFMAs of the current slab. Addresses are
 // clamped into the operand: a row past `rows` reads the last row (its products only reach
-// outputs that are never stored), and K indices past `kend` read a valid element whose value
-// is replaced by zero when the slab is written to LDS.
+// outputs that are never stored). A slab that lies wholly below `kend` is loaded from a
+// uniform per-slab base plus per-thread byte offsets computed once (`init`), with no clamps
+// or masks; only a slab that reaches past `kend` clamps its K indices (to a valid element
+// whose value is replaced by zero when the slab is written to LDS). The host keeps the byte
+// offsets below 2^32.
 template <bool TRANS>
 struct SlabLoader {
   // float4 loads per thread per slab: 128 x BK floats / (256 threads x 4)
@@ -68,6 +71,36 @@ struct SlabLoader {
   static constexpr int K_PER_PASS = NTHREADS / (BM / 4);  // TRANS: K rows per pass (8)
   f32x4 v[NV];
   int k0, kend;
+  uint32_t voff[NV];  // byte offsets of this thread's float4s from the slab base
+  const float* base0;  // !TRANS: row row0 of the operand; TRANS: the operand itself
+  int ld;
+
+  __device__ __forceinline__ void init(const float* __restrict__ P, int ld_, int row0, int rows,
+                                       int tid) {
+    ld = ld_;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      if (!TRANS) {
+        const int r = min(row0 + tid / F4_PER_ROW + ROWS_PER_PASS * i, rows - 1) - row0;
+        voff[i] = (uint32_t)(r * ld + 4 * (tid % F4_PER_ROW)) * 4u;
+      } else {
+        const int k = tid / (BM / 4) + K_PER_PASS * i;
+        const int r = min(row0 + 4 * (tid % (BM / 4)), (rows - 1) & ~3);
+        voff[i] = (uint32_t)(k * ld + r) * 4u;
+      }
+    }
+    base0 = TRANS ? P : P + (long long)row0 * ld;
+  }
+
+  // a slab wholly below kend
+  __device__ __forceinline__ void load_full(int k0_, int kend_) {
+    k0 = k0_;
+    kend = kend_;
+    const char* b = reinterpret_cast<const char*>(TRANS ? base0 + (long long)k0 * ld
+                                                          : base0 + k0);
+#pragma unroll
+    for (int i = 0; i < NV; i++) v[i] = *reinterpret_cast<const f32x4*>(b + voff[i]);
+  }
 
   __device__ __forceinline__ void load(const float* __restrict__ P, int ld, int row0, int rows,
                                        int k0_, int kend_, int tid) {
@@ -89,6 +122,23 @@ struct SlabLoader {
 
   template <int LDS>
   __device__ __forceinline__ void store(float (*S)[LDS], int tid) const {
+    if (k0 + BK <= kend) {  // full slab (uniform): no masks
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        if (!TRANS) {
+          const int r = tid / F4_PER_ROW + ROWS_PER_PASS * i;
+          const int k = 4 * (tid % F4_PER_ROW);
+#pragma unroll
+          for (int j = 0; j < 4; j++) S[k + j][r] = v[i][j];
+        } else {
+          const int k = tid / (BM / 4) + K_PER_PASS * i;
+          const int r = 4 * (tid % (BM / 4));
+          *reinterpret_cast<f32x2*>(&S[k][r]) = f32x2{v[i][0], v[i][1]};
+          *reinterpret_cast<f32x2*>(&S[k][r + 2]) = f32x2{v[i][2], v[i][3]};
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NV; i++) {
       if (!TRANS) {
@@ -195,10 +245,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
 
   SlabLoader<AT> la;
   SlabLoader<BT> lb;
+  la.init(g.A, g.lda, m0, g.M, tid);
+  lb.init(g.B, g.ldb, n0, g.N, tid);
   auto load_slab = [&](int kt) {
     const int k0 = kbeg + kt * BK;
-    la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
-    lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+    if (k0 + BK <= kend) {  // uniform
+      la.load_full(k0, kend);
+      lb.load_full(k0, kend);
+    } else {
+      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
+      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+    }
   };
   if (ntiles > 0) {
     load_slab(0);
@@ -428,9 +485,11 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   }
   // float4 operand loads: 16-byte aligned bases and leading dimensions that are multiples
   // of 4 (which also keeps the last float4 of a row inside the row's storage)
+  // (and leading dimensions below 2^23, so a slab's per-thread byte offsets fit 32 bits)
   const int a_cols = g.a_trans ? g.M : g.K, b_cols = g.b_trans ? g.N : g.K;
   if (!aligned16(g.A) || !aligned16(g.B) || !aligned16(g.C) || g.lda % 4 || g.ldb % 4 ||
-      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N) {
+      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N || g.lda >= (1 << 23) ||
+      g.ldb >= (1 << 23)) {
     set_global_error("gemm: unsupported alignment or leading dimension (lda=%d ldb=%d ldc=%d)",
                      g.lda, g.ldb, g.ldc);
     return -1;
