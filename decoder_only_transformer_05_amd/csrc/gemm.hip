@@ -49,6 +49,8 @@ struct Args {
 };
 
 constexpr int GROUP_M = 8;  // m-tiles that sweep the n-tiles together (L2 reuse of A and B)
+// word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family GPUs
+constexpr int kBufferFlags = 0x00020000;
 
 // Loads one K-slab of an operand into registers (4 float4 per thread) and later stores it to
 // LDS in [k][row] order. `rows` is M (for A) or N (for B).
@@ -92,14 +94,17 @@ struct SlabLoader {
     base0 = TRANS ? P : P + (long long)row0 * ld;
   }
 
-  // a slab wholly below kend
+  // a slab wholly below kend: buffer loads from a scalar base (the slab's buffer resource)
+  // plus this thread's 32-bit offsets, so the loop spends no vector ALU on addresses
   __device__ __forceinline__ void load_full(int k0_, int kend_) {
     k0 = k0_;
     kend = kend_;
-    const char* b = reinterpret_cast<const char*>(TRANS ? base0 + (long long)k0 * ld
-                                                          : base0 + k0);
+    const float* b = TRANS ? base0 + (long long)k0 * ld : base0 + k0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(b), (short)0, -1, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < NV; i++) v[i] = *reinterpret_cast<const f32x4*>(b + voff[i]);
+    for (int i = 0; i < NV; i++)
+      v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0));
   }
 
   __device__ __forceinline__ void load(const float* __restrict__ P, int ld, int row0, int rows,
