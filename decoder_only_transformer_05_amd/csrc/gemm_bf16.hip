@@ -64,10 +64,42 @@ GPT2_DEVICE_INLINE uint32_t mask_pair(uint32_t x, int k, int kend) {
   return x & (lo | hi);
 }
 
+// word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family GPUs
+constexpr int kBufferFlags = 0x00020000;
+
+// A slab of an interior tile (no row past the operand's edge) wholly below kend is loaded
+// with buffer loads from a scalar per-slab base: a per-thread 32-bit byte offset computed
+// once (`init`) plus a uniform offset per load, so no vector ALU goes to addresses. Other
+// slabs take `load`, which clamps their indices. The host keeps the byte offsets below 2^32.
 template <bool TRANS>
 struct SlabLoader {
   u32x4 v[4];
   int k0, kend;
+  uint32_t voff;        // byte offset of this thread's first piece from the slab base
+  const bf16_t* base0;  // !TRANS: row row0 of the operand; TRANS: column row0
+  int ld;
+
+  __device__ __forceinline__ void init(const bf16_t* __restrict__ P, int ld_, int row0,
+                                       int tid) {
+    ld = ld_;
+    if (!TRANS) voff = (uint32_t)((tid >> 3) * ld + 8 * (tid & 7)) * 2u;
+    else voff = (uint32_t)(4 * (tid >> 4) * ld + 8 * (tid & 15)) * 2u;
+    base0 = TRANS ? P + row0 : P + (long long)row0 * ld;
+  }
+
+  __device__ __forceinline__ void load_full(int k0_, int kend_) {
+    k0 = k0_;
+    kend = kend_;
+    const bf16_t* b = TRANS ? base0 + (long long)k0 * ld : base0 + k0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b), (short)0, -1, kBufferFlags);
+    // !TRANS: piece i is 32 rows further; TRANS: piece j is one k row further
+    const int step = TRANS ? ld * 2 : 64 * ld;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      v[i] = __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * step, 0));
+  }
 
   // !TRANS: operand stored (rows, K): thread -> rows tid/8 + 32i, k chunk tid%8 (8 k)
   //  TRANS: operand stored (K, rows): thread -> k rows 4*(tid/16) .. +3, rows 8*(tid%16) .. +7
@@ -224,6 +256,18 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
   // barrier.
   SlabLoader<AT> la;
   SlabLoader<BT> lb;
+  la.init(g.A, g.lda, m0, tid);
+  lb.init(g.B, g.ldb, n0, tid);
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;  // uniform
+  auto load_slab = [&](int k0) {
+    if (interior && k0 + BK <= kend) {  // uniform
+      la.load_full(k0, kend);
+      lb.load_full(k0, kend);
+    } else {
+      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
+      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+    }
+  };
   auto compute = [&]() {
     // the compiler's MFMA / LDS-read interleaving strategy 1 (measured 1% faster per step
     // than its default schedule on the 774M shapes; strategy 0 and explicit prefetch depth
@@ -257,18 +301,14 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
     }
   };
   if (nslabs > 0) {
-    la.load(g.A, g.lda, m0, g.M, kbeg, kend, tid);
-    lb.load(g.B, g.ldb, n0, g.N, kbeg, kend, tid);
+    load_slab(kbeg);
     la.store(As[0], tid, kbeg + BK > kend);
     lb.store(Bs[0], tid, kbeg + BK > kend);
   }
   __syncthreads();
   for (int kt = 0; kt < nslabs; kt++) {
     const bool more = kt + 1 < nslabs;
-    if (more) {
-      la.load(g.A, g.lda, m0, g.M, kbeg + (kt + 1) * BK, kend, tid);
-      lb.load(g.B, g.ldb, n0, g.N, kbeg + (kt + 1) * BK, kend, tid);
-    }
+    if (more) load_slab(kbeg + (kt + 1) * BK);
     compute();
     __syncthreads();
     if (more) {
@@ -426,9 +466,10 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
   // multiples of 8 elements; the epilogue's vector stores need ldc % 8 (bf16) or % 4 (fp32)
   const bool cf32 = g.epi == EPI_ACCUM;
   const int a_cols = g.a_trans ? g.M : g.K, b_cols = g.b_trans ? g.N : g.K;
+  // (and leading dimensions below 2^24, so a slab's per-thread byte offsets fit 32 bits)
   if (!aligned16(g.A) || !aligned16(g.B) || !aligned16(g.C) || g.lda % 8 || g.ldb % 8 ||
       g.ldc % (cf32 ? 4 : 8) || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N ||
-      (g.bias && !aligned16(g.bias))) {
+      (g.bias && !aligned16(g.bias)) || g.lda >= (1 << 24) || g.ldb >= (1 << 24)) {
     set_global_error("gemm_bf16: unsupported alignment or leading dimension (lda=%d ldb=%d "
                      "ldc=%d)", g.lda, g.ldb, g.ldc);
     return -1;
