@@ -292,8 +292,8 @@ void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
   __shared__ float dOs[TILE][LD];
   __shared__ float QT[HSP][LDT];
   __shared__ float dOT[HSP][LDT];
-  __shared__ float Ls[TILE];
-  __shared__ float Ds[TILE];
+  __shared__ __attribute__((aligned(16))) float Ls[TILE];
+  __shared__ __attribute__((aligned(16))) float Ds[TILE];
 
   const int nkb = (T + DK_KEYS - 1) / DK_KEYS;
   int kb, head, b;
@@ -359,11 +359,20 @@ void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
     }
     __syncthreads();
     if (qt < kt) continue;  // every query of this tile precedes this wave's keys
-    // dS tile (qt, kt) of this (b, head): 64 x 64 floats, [query][key]
+    // dS tile (qt, kt) of this (b, head): 64 x 64 floats, [query][key]; this lane writes
+    // column kcol of rows 4hf + (32qb + 8(i/4) + i%4)
     float* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
-                             (TILE * TILE);
+                             (TILE * TILE) + 4 * hf * TILE + kcol;
 #pragma unroll 1
     for (int qb = 0; qb < 2; qb++) {
+      // the lse and D of this lane's 16 queries (four runs of four consecutive rows), read
+      // before the products so their latency is hidden
+      f32x4 lq[4], dq[4];
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        lq[gq] = *reinterpret_cast<const f32x4*>(&Ls[32 * qb + 8 * gq + 4 * hf]);
+        dq[gq] = *reinterpret_cast<const f32x4*>(&Ds[32 * qb + 8 * gq + 4 * hf]);
+      }
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
@@ -380,16 +389,18 @@ void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
           dp = mfma32x32x2(ov[j], vf[4 * g + j], dp);
         }
       }
-      // s[i], dp[i]: query ql = 32qb + 8(i/4) + 4hf + i%4, key = this lane's
+      // s[i], dp[i]: query ql = 32qb + 8(i/4) + 4hf + i%4, key = this lane's. The
+      // exponential is taken for every entry and masked after (no branch per entry).
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        const int ql = 32 * qb + 8 * (i / 4) + 4 * hf + (i % 4);
-        const int qa = q0 + ql;
+        const int qo = 32 * qb + 8 * (i / 4) + (i % 4);  // ql - 4hf
+        const int qa = q0 + qo + 4 * hf;
         const bool ok = qa < T && qa >= key;
-        const float p = ok ? __builtin_amdgcn_exp2f(s[i] * scale_log2 - Ls[ql]) : 0.f;
+        const float e = __builtin_amdgcn_exp2f(s[i] * scale_log2 - lq[i / 4][i % 4]);
+        const float p = ok ? e : 0.f;
         s[i] = p;
-        dp[i] = p * (dp[i] - Ds[ql]);
-        dst[ql * TILE + kcol] = dp[i];  // 32 lanes store 32 consecutive keys
+        dp[i] = p * (dp[i] - dq[i / 4][i % 4]);
+        dst[qo * TILE] = dp[i];  // 32 lanes store 32 consecutive keys
       }
       // dV^T[d][key] += dO[q][d] P[q][key] and dK^T[d][key] += Q[q][d] dS[q][key] over this
       // sub-block's queries; entries 4sg .. 4sg+3 of s and dp are four consecutive queries
