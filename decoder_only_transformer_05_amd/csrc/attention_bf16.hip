@@ -317,7 +317,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t Qt[HSP * TILE];   // [d][kpos(q)]
   __shared__ __attribute__((aligned(16))) bf16_t dOs[TILE * HSP];  // [q][d]
   __shared__ __attribute__((aligned(16))) bf16_t dOt[HSP * TILE];  // [d][kpos(q)]
-  __shared__ float Ls[TILE], Ds[TILE];
+  __shared__ __attribute__((aligned(16))) float Ls[TILE];
+  __shared__ __attribute__((aligned(16))) float Ds[TILE];
 
   const int nkt = (T + TILE - 1) / TILE;
   int kt, head, b;
@@ -366,6 +367,14 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
                               (TILE * TILE) + (long long)(wave * 32 + r) * TILE;
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
+      // the lse and D of this lane's 16 queries (four runs of four consecutive rows), read
+      // before the products so their latency is hidden
+      f32x4 lq[4], dq[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        lq[g4] = *reinterpret_cast<const f32x4*>(&Ls[32 * qb + 8 * g4 + 4 * lh]);
+        dq[g4] = *reinterpret_cast<const f32x4*>(&Ds[32 * qb + 8 * g4 + 4 * lh]);
+      }
       u32x4 pw[2], sw[2];  // P and dS (bf16 pairs) as B operands of k step h
       f32x16 s, dp;
 #pragma unroll
@@ -380,20 +389,30 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
         s = mfma_bf16(qa, kf[ks], s);
         dp = mfma_bf16(oa, vf[ks], dp);
       }
-      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's
+      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's. The
+      // exponential is taken for every entry and masked after (no branch per entry); a
+      // sub-block whose 32 queries all follow the wave's 32 keys and lie before T needs no
+      // mask (uniform test).
+      const bool nomask = q0 + 32 * qb >= kt * TILE + wave * 32 + 31 && q0 + 32 * qb + 32 <= T;
 #pragma unroll
       for (int g4 = 0; g4 < 4; g4++) {
         float pv[4], dsv[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const int i = 4 * g4 + j;
-          const int ql = 32 * qb + 8 * g4 + 4 * lh + j;
-          const int qa = q0 + ql;
-          const bool ok = qa < T && qa >= key;
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -Ls[ql])) : 0.f;
-          pv[j] = p;
-          dsv[j] = p * (dp[i] - Ds[ql]);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lq[g4][j]));
+          pv[j] = e;
+          dsv[j] = dp[i] - dq[g4][j];
         }
+        if (!nomask) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const int qa = q0 + 32 * qb + 8 * g4 + 4 * lh + j;
+            if (!(qa < T && qa >= key)) pv[j] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) dsv[j] *= pv[j];
         const int hh = g4 >> 1, w = 2 * (g4 & 1);  // acc entries 8hh .. 8hh+7 form k step hh
         pw[hh][w] = pack2(pv[0], pv[1]);
         pw[hh][w + 1] = pack2(pv[2], pv[3]);
