@@ -27,6 +27,18 @@ GPT2_DEVICE_INLINE f32x4 ld4(const bf16_t* p) {
   return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
                __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};
 }
+// The same four elements kept as stored (fp32: 16 bytes, bf16: 8 bytes) until widened, so a
+// prefetched bf16 row takes half the registers.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { typedef f32x4 type; };
+template <> struct Raw4<bf16_t> { typedef u32x2_t type; };
+GPT2_DEVICE_INLINE f32x4 raw4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+GPT2_DEVICE_INLINE u32x2_t raw4(const bf16_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+GPT2_DEVICE_INLINE f32x4 widen4(f32x4 v) { return v; }
+GPT2_DEVICE_INLINE f32x4 widen4(u32x2_t u) {
+  return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
+               __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};
+}
 GPT2_DEVICE_INLINE void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 GPT2_DEVICE_INLINE void st4(bf16_t* p, f32x4 v) {
   const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);

@@ -222,18 +222,17 @@ int lnb_rows(int N) {
   return rows;
 }
 
-// one row's dout and x for the LayerNorm backward, held in registers (zeros past C)
-template <int VPL, typename T>
-GPT2_DEVICE_INLINE void lnb_fetch(f32x4 (&dy)[VPL], f32x4 (&xv)[VPL], const T* dout,
-                                  const T* x, int row, int C, int lane) {
+// one row's dout and x for the LayerNorm backward, held in registers as stored (zeros past C)
+template <int VPL, typename T, typename R>
+GPT2_DEVICE_INLINE void lnb_fetch(R (&dy)[VPL], R (&xv)[VPL], const T* dout, const T* x,
+                                  int row, int C, int lane) {
   const int C4 = C / 4;
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
     const int c4 = lane + 64 * i;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const long long o = (long long)row * C + 4 * c4;
-    dy[i] = c4 < C4 ? ld4(dout + o) : zero;
-    xv[i] = c4 < C4 ? ld4(x + o) : zero;
+    dy[i] = c4 < C4 ? raw4(dout + o) : R{};
+    xv[i] = c4 < C4 ? raw4(x + o) : R{};
   }
 }
 
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   }
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(N, r0 + rows_per_block);
-  f32x4 dyn[VPL], xn[VPL];
+  typename Raw4<T>::type dyn[VPL], xn[VPL];  // the next row, as stored
   float mun = 0.f, rsn = 0.f;
   int row = r0 + wave;
   if (row < r1) {
@@ -280,8 +279,8 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     const float mu = mun, rs = rsn;
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
-      dy[i] = dyn[i];
-      nv[i] = xn[i];
+      dy[i] = widen4(dyn[i]);
+      nv[i] = widen4(xn[i]);
     }
     float* dxr = dx + (long long)row * C;
 #pragma unroll
