@@ -74,15 +74,27 @@ GPT2_DEVICE_INLINE void load_tile(float (*S)[HSP + 4], const TS* base, long long
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
-template <int HSP, typename TS>
+// 16 bytes from global memory straight into LDS: lane l writes lds + 16 l (the LDS address is
+// the same for the whole wave). Kept out of the kernel bodies: clang's host pass drops the
+// launch stub of a kernel that calls this builtin directly.
+GPT2_DEVICE_INLINE void lds_copy16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// DIRECT (fp32 storage, hs == HSP == 64): the K and V tiles are copied from global memory
+// straight into LDS (global_load_lds_dwordx4: no registers), one 1 KB run of four rows per
+// wave instruction, so the tiles are unpadded; a key's 16-byte chunk c is stored at chunk
+// c ^ (key & 15), chosen on the global side, which spreads the K reads over the banks.
+template <int HSP, typename TS, bool DIRECT = false>
 __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(TS* __restrict__ out,
                                                         float* __restrict__ lse,
                                                         const TS* __restrict__ qkv, int T,
                                                         int C, int NH, int hs,
                                                         float scale_log2) {
-  constexpr int LD = HSP + 4, NS = HSP / 2, ND = HSP / 32;
-  __shared__ float Ks[TILE][LD];
-  __shared__ float Vs[TILE][LD];
+  static_assert(!DIRECT || HSP == 64, "direct tile copies assume 64-dim rows");
+  constexpr int LD = DIRECT ? HSP : HSP + 4, NS = HSP / 2, ND = HSP / 32;
+  __shared__ __attribute__((aligned(16))) float Ks[TILE][LD];
+  __shared__ __attribute__((aligned(16))) float Vs[TILE][LD];
 
   const int nqt = (T + TILE - 1) / TILE;
   int qt, head, b;
@@ -116,8 +128,24 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(TS* __restrict__ out,
   for (int kt = 0; kt < ntiles; kt++) {
     const int key0 = kt * TILE;
     __syncthreads();
-    load_tile<HSP>(Ks, base + C, C3, key0, T, hs, tid);
-    load_tile<HSP>(Vs, base + 2 * C, C3, key0, T, hs, tid);
+    if constexpr (DIRECT) {
+      // 16 wave instructions per tile (two waves, eight each): lane l of instruction j
+      // fills row 4j + l/16, stored chunk l%16; rows past T read the last row (those keys
+      // are masked and their V rows weigh 0)
+#pragma unroll
+      for (int jj = 0; jj < TILE / 8; jj++) {
+        const int j = 2 * jj + wave;
+        const int row = 4 * j + (lane >> 4);
+        const long long t = min(key0 + row, T - 1);
+        const int cs = lane & 15;
+        lds_copy16(base + C + t * C3 + 4 * (cs ^ (row & 15)), &Ks[4 * j][0]);
+        lds_copy16(base + 2 * C + t * C3 + 4 * cs, &Vs[4 * j][0]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      load_tile<HSP>(Ks, base + C, C3, key0, T, hs, tid);
+      load_tile<HSP>(Vs, base + 2 * C, C3, key0, T, hs, tid);
+    }
     __syncthreads();
 
     f32x16 s[2];
@@ -127,7 +155,9 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(TS* __restrict__ out,
       for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
 #pragma unroll
       for (int g = 0; g < HSP / 8; g++) {
-        f32x4 kv = *reinterpret_cast<const f32x4*>(&Ks[32 * kb + r][8 * g + 4 * hf]);
+        const int krow = 32 * kb + r, kc = 2 * g + hf;  // chunk of 4 head dims
+        f32x4 kv = *reinterpret_cast<const f32x4*>(
+            &Ks[krow][4 * (DIRECT ? kc ^ (krow & 15) : kc)]);
 #pragma unroll
         for (int j = 0; j < 4; j++) s[kb] = mfma32x32x2(kv[j], qf[4 * g + j], s[kb]);
       }
@@ -532,6 +562,19 @@ bool check_shape(int B, int T, int C, int NH, int* hsp) {
 }
 
 
+// the direct-to-LDS forward exists for fp32 storage only
+template <typename TS>
+bool launch_fwd_direct(dim3, hipStream_t, TS*, float*, const TS*, int, int, int, int, float) {
+  return false;
+}
+template <>
+bool launch_fwd_direct<float>(dim3 grid, hipStream_t stream, float* out, float* lse,
+                              const float* qkv, int T, int C, int NH, int hs, float scale_log2) {
+  attn_fwd_kernel<64, float, true><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs,
+                                                               scale_log2);
+  return true;
+}
+
 template <typename TS>
 int attention_forward_t(TS* out, float* lse, const TS* qkv, int B, int T, int C, int NH,
                         hipStream_t stream) {
@@ -548,7 +591,8 @@ int attention_forward_t(TS* out, float* lse, const TS* qkv, int B, int T, int C,
   ProfScope ps(sizeof(TS) == 4 ? "attn_fwd_kernel" : "attn_fwd_bf16_kernel",
                4.0 * B * NH * hs * tri,
                es * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
-  if (hsp == 32) attn_fwd_kernel<32, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  if (hsp == 64 && hs == 64 && launch_fwd_direct(grid, stream, out, lse, qkv, T, C, NH, hs, scale_log2)) {
+  } else if (hsp == 32) attn_fwd_kernel<32, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   else if (hsp == 64) attn_fwd_kernel<64, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   else attn_fwd_kernel<128, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   GPT2_HIP_OK(hipGetLastError());
