@@ -9,34 +9,55 @@
 // and the same fused epilogues (bias, bias+GELU, bias+residual, fp32 accumulate into the
 // master gradients, GELU backward), computed in fp32 and rounded once to bf16 on store.
 //
-// Tiling: 256-thread workgroups own 128x128 tiles of C, each wave a 64x64 sub-tile (2x2
-// MFMA blocks of 32x32); K advances 64 at a time through one LDS buffer per operand. Both
-// operands sit in LDS as [row][k] with k contiguous (128-byte rows), because each lane of
-// the bf16 MFMA supplies 8 consecutive k of one row. Operands stored with K contiguous are
-// copied in 16-byte pieces; operands stored (K, rows) are transposed on the way: a thread
-// loads 4 k-rows of 8 consecutive row elements and writes 8 rows of 4 k (8 bytes each).
-// The 16-byte chunks of row r are placed at chunk c ^ ((r ^ r/8) & 7), which keeps both the
-// fragment reads (32 rows, same chunk) and the transposing writes (rows 8 apart) spread
-// over the LDS banks.
+// Tiling: workgroups own 256x256 tiles of C (8 waves of 128x64) or, for grids too small to
+// fill the chip, 128x128 tiles (4 waves of 64x64); each wave holds WM x WN blocks of 32x32
+// accumulators. K advances in slabs that go from global memory straight into LDS (buffer
+// loads with the LDS as destination, no staging registers), several slabs in flight, one
+// LDS object per pipeline stage. Each lane of the bf16 MFMA supplies 8 consecutive k of one
+// row: an operand stored with K contiguous is kept [row][k] in LDS and read with 16-byte
+// loads; an operand stored (K, rows) is kept as stored, [k][row], and read with the
+// transposing LDS load of gfx950 (ds_read_b64_tr_b16), so no thread transposes anything.
+// XOR swizzles of the 16-byte chunks (applied on the global side of the copy) keep both
+// kinds of fragment read free of LDS bank conflicts.
 // The MFMA takes the B tile as its first operand, so a lane ends up holding four runs of 4
 // consecutive output columns of one row: epilogue loads and stores are 8- or 16-byte
 // vectors.
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "kernels.h"
 
 namespace gpt2 {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int NTHREADS = 256;
-constexpr int GROUP_M = 8;
+// Tile shapes: BM x BN per workgroup of WGM x WGN waves (each wave WM x WN blocks of 32 x 32),
+// slabs of BK k, NSTAGE slabs in LDS, OCC workgroups per CU.
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int NSTAGE_, int OCC_, int GROUP_M_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, GROUP_M = GROUP_M_;
+  static constexpr int NWAVES = WGM * WGN, NT = 64 * NWAVES;
+  static constexpr int WM = BM / 32 / WGM, WN = BN / 32 / WGN;
+  static constexpr int NSTAGE = NSTAGE_, OCC = OCC_;
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5, "two to five LDS stages");
+  static_assert(BK == 32 || BK == 64, "slab depth");
+};
+// 128 x 128: 4 waves of 64 x 64, slabs of 32 k, 3 stages of 16 KB, three workgroups per CU
+// (small grids: more workgroups than the large tile)
+typedef TileCfg<128, 128, 32, 2, 2, 3, 3, 8> Tile128;
+// 256 x 256: 8 waves of 128 x 64, slabs of 64 k (128-byte pieces of rows stored with K
+// contiguous), 2 stages of 64 KB, one workgroup per CU: half the operand bytes per flop of
+// the 128 x 128 tile
+typedef TileCfg<256, 256, 64, 2, 4, 2, 1, 8> Tile256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 struct Args {
   const bf16_t* A;
@@ -54,116 +75,105 @@ struct Args {
   long long colsum_zstride;
 };
 
-GPT2_DEVICE_INLINE int swz(int row) { return (row ^ (row >> 3)) & 7; }
-// bf16 offset of the 16-byte chunk c (8 k values) of LDS row `row`
-GPT2_DEVICE_INLINE int lds_off(int row, int c) { return row * BK + ((c ^ swz(row)) << 3); }
-
-// zero the 16-bit halves of x whose k index (k0 + 2*i + half) is >= kend
-GPT2_DEVICE_INLINE uint32_t mask_pair(uint32_t x, int k, int kend) {
-  const uint32_t lo = k < kend ? 0xFFFFu : 0u, hi = k + 1 < kend ? 0xFFFF0000u : 0u;
-  return x & (lo | hi);
+// LDS placement. An operand stored with K contiguous sits in LDS as [row][k] (rows of BK k);
+// the 16-byte chunk c of row r holds the row's chunk c ^ kswz(r), which spreads the 16-byte
+// fragment reads (consecutive rows, one chunk) over all banks. An operand stored
+// (K, rows) keeps that layout in LDS, [k][row] (R elements per k); chunk c of k-row k holds
+// chunk c ^ rswz(k % 4), so the four k-rows that one transposing read touches fall on
+// different banks.
+template <int BK>
+GPT2_DEVICE_INLINE int kswz(int row) {
+  return BK == 32 ? ((row >> 1) ^ (row >> 3)) & 3 : (row ^ (row >> 3)) & 7;
 }
+GPT2_DEVICE_INLINE int rswz(int j) { return (0xAC60 >> (4 * j)) & 15; }  // 0, 6, 12, 10
 
 // word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family GPUs
 constexpr int kBufferFlags = 0x00020000;
 
-// A slab of an interior tile (no row past the operand's edge) wholly below kend is loaded
-// with buffer loads from a scalar per-slab base: a per-thread 32-bit byte offset computed
-// once (`init`) plus a uniform offset per load, so no vector ALU goes to addresses. Other
-// slabs take `load`, which clamps their indices. The host keeps the byte offsets below 2^32.
-template <bool TRANS>
-struct SlabLoader {
-  u32x4 v[4];
-  int k0, kend;
-  uint32_t voff;        // byte offset of this thread's first piece from the slab base
-  const bf16_t* base0;  // !TRANS: row row0 of the operand; TRANS: column row0
-  int ld;
+// 16 bytes per lane from a buffer into LDS (lane l writes lds + 16 l); `lds` is wave-uniform
+GPT2_DEVICE_INLINE void copy_to_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
 
-  __device__ __forceinline__ void init(const bf16_t* __restrict__ P, int ld_, int row0,
-                                       int tid) {
-    ld = ld_;
-    if (!TRANS) voff = (uint32_t)((tid >> 3) * ld + 8 * (tid & 7)) * 2u;
-    else voff = (uint32_t)(4 * (tid >> 4) * ld + 8 * (tid & 15)) * 2u;
-    base0 = TRANS ? P + row0 : P + (long long)row0 * ld;
-  }
+// One operand's share of the slab pipeline: a slab (BK k x R rows, 2 R BK bytes) is copied
+// from global memory straight into LDS, 1 KB per wave-wide buffer load (lane l fills bytes
+// 16 l .. 16 l + 15 of the KB), without passing through registers. The buffer resource of a
+// slab ends where the operand ends, so rows past its last row (and, for an operand stored
+// (K, rows), k past K) read as zero. Per-lane byte offsets are computed once.
+template <bool TRANS, int R, int NWAVES, int BK>
+struct SlabCopy {
+  static constexpr int PER_WAVE = R * BK * 2 / 1024 / NWAVES;
+  static_assert(PER_WAVE * NWAVES * 1024 == R * BK * 2, "whole 1 KB copies per wave");
+  const char* tile;     // operand at this tile's first row (!TRANS) or column (TRANS), k = 0
+  long long step;       // bytes between consecutive slabs
+  long long remain;     // bytes from `tile` to the end of the operand
+  uint32_t voff[PER_WAVE];
 
-  __device__ __forceinline__ void load_full(int k0_, int kend_) {
-    k0 = k0_;
-    kend = kend_;
-    const bf16_t* b = TRANS ? base0 + (long long)k0 * ld : base0 + k0;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b), (short)0, -1, kBufferFlags);
-    // !TRANS: piece i is 32 rows further; TRANS: piece j is one k row further
-    const int step = TRANS ? ld * 2 : 64 * ld;
+  __device__ __forceinline__ void init(const bf16_t* P, int ld, int row0, long long total,
+                                       int wave, int lane) {
+    const long long at = TRANS ? (long long)row0 : (long long)row0 * ld;
+    tile = reinterpret_cast<const char*>(P + at);
+    remain = 2 * (total - at);
+    step = TRANS ? 2LL * BK * ld : 2LL * BK;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      v[i] = __builtin_bit_cast(u32x4,
-                                __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * step, 0));
-  }
-
-  // !TRANS: operand stored (rows, K): thread -> rows tid/8 + 32i, k chunk tid%8 (8 k)
-  //  TRANS: operand stored (K, rows): thread -> k rows 4*(tid/16) .. +3, rows 8*(tid%16) .. +7
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ P, int ld, int row0,
-                                       int rows, int k0_, int kend_, int tid) {
-    k0 = k0_;
-    kend = kend_;
-    if (!TRANS) {
-      const int c = tid & 7;
-      const int kc = min(k0 + 8 * c, (kend - 1) & ~7);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = min(row0 + (tid >> 3) + 32 * i, rows - 1);
-        v[i] = *reinterpret_cast<const u32x4*>(P + (long long)r * ld + kc);
-      }
-    } else {
-      const int rg = tid & 15, kq = tid >> 4;
-      const int r = min(row0 + 8 * rg, (rows - 1) & ~7);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int k = min(k0 + 4 * kq + j, kend - 1);
-        v[j] = *reinterpret_cast<const u32x4*>(P + (long long)k * ld + r);
+    for (int j = 0; j < PER_WAVE; j++) {
+      const int b = (j * NWAVES + wave) * 1024 + 16 * lane;  // LDS byte within the slab
+      if (!TRANS) {
+        const int row = b / (2 * BK), p = (b % (2 * BK)) >> 4;
+        voff[j] = (uint32_t)(row * ld + 8 * (p ^ kswz<BK>(row))) * 2u;
+      } else {
+        const int k = b / (2 * R), p = (b % (2 * R)) >> 4;
+        voff[j] = (uint32_t)(k * ld + 8 * (p ^ rswz(k & 3))) * 2u;
       }
     }
   }
 
-  // `tail`: this slab reaches past kend (the same for the whole workgroup)
-  __device__ __forceinline__ void store(bf16_t* S, int tid, bool tail) const {
-    if (!TRANS) {
-      const int c = tid & 7;
-      const int kg = k0 + 8 * c;
+  // `live` false: a copy past the last slab, given an empty range (it reads nothing and
+  // writes zeros), so that every pipeline step issues the same number of copies
+  __device__ __forceinline__ void issue(int kt, bool live, bf16_t* lds, int wave) const {
+    const long long off = live ? (long long)kt * step : 0;
+    const long long left = live ? remain - off : 0;
+    const int nrec = (int)(uint32_t)(left > 0xFFFFFFFFLL ? 0xFFFFFFFFLL : left > 0 ? left : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tile + off), (short)0, nrec, kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int row = (tid >> 3) + 32 * i;
-        u32x4 x = v[i];
-        if (tail) {
-#pragma unroll
-          for (int q = 0; q < 4; q++) x[q] = mask_pair(x[q], kg + 2 * q, kend);
-        }
-        *reinterpret_cast<u32x4*>(S + lds_off(row, c)) = x;
-      }
-    } else {
-      const int rg = tid & 15, kq = tid >> 4;
-      const int kg = k0 + 4 * kq;
-      u32x4 x[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++) x[j] = (!tail || kg + j < kend) ? v[j] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int q = e >> 1;
-        uint32_t lo, hi;
-        if ((e & 1) == 0) {
-          lo = (x[0][q] & 0xFFFFu) | (x[1][q] << 16);
-          hi = (x[2][q] & 0xFFFFu) | (x[3][q] << 16);
-        } else {
-          lo = (x[0][q] >> 16) | (x[1][q] & 0xFFFF0000u);
-          hi = (x[2][q] >> 16) | (x[3][q] & 0xFFFF0000u);
-        }
-        const int row = 8 * rg + e;
-        *reinterpret_cast<u32x2*>(S + lds_off(row, kq >> 1) + 4 * (kq & 1)) = u32x2{lo, hi};
-      }
-    }
+    for (int j = 0; j < PER_WAVE; j++)
+      copy_to_lds16(rs, reinterpret_cast<char*>(lds) + (j * NWAVES + wave) * 1024, voff[j]);
   }
 };
+
+// Fragment of the bf16 MFMA for a lane: row r = lane % 32 of a 32-row block, k = 8 h .. 8 h + 7
+// with h = lane / 32 (within a 16-k step).
+// Operand stored with K contiguous: one 16-byte read. `rd` = byte of (row base + r, chunk of
+// step 0); step 1 is the chunk 2 further, which the swizzle maps to rd ^ 32 within the row.
+// Operand stored (K, rows): two transposing 8-byte reads (ds_read_b64_tr_b16). In each
+// 16-lane group, lane i receives column i of the 4 x 16 block whose k-row j is read by lanes
+// 4j .. 4j + 3 (4 columns each), so a group covers 16 columns x 4 k.
+GPT2_DEVICE_INLINE bf16x8 frag_tr(const char* p, int kstride4) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + kstride4));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// zero the k values of a fragment at or past `lim` (its first element being k = 0)
+GPT2_DEVICE_INLINE bf16x8 kmask(bf16x8 v, int lim) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    u[q] &= (2 * q < lim ? 0xFFFFu : 0u) | (2 * q + 1 < lim ? 0xFFFF0000u : 0u);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// workgroup barrier without a memory fence: the slab copies still in flight must not be
+// waited for here (the fence of __syncthreads would wait for all of them); the clobber keeps
+// the compiler from moving LDS accesses across it
+GPT2_DEVICE_INLINE void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// wait until at most n vector-memory operations of this wave are outstanding (n < 16)
+template <int n>
+GPT2_DEVICE_INLINE void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);  // expcnt and lgkmcnt at their no-wait maxima
+}
 
 // Epilogue of four consecutive columns n..n+3 of row m (n % 4 == 0, m < M, n < N).
 template <int EPI, bool CF32>
@@ -215,10 +225,19 @@ __device__ __forceinline__ void epilogue4(const Args& g, void* Cv, int m, int n,
   }
 }
 
-template <bool AT, bool BT, bool CF32, int EPI>
-__global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[1][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[1][BN * BK];
+template <class CFG, bool AT, bool BT, bool CF32, int EPI>
+__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
+  constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, WM = CFG::WM, WN = CFG::WN;
+  constexpr int NT = CFG::NT;
+  constexpr int NSTAGE = CFG::NSTAGE, NWAVES = CFG::NWAVES;
+  // one LDS object per pipeline stage, so the compiler can tell which copies a read waits for
+  // (stages past NSTAGE are 16-byte placeholders)
+  constexpr int SA = BM * BK, SB = BN * BK;
+  constexpr int SA3 = NSTAGE > 3 ? SA : 8, SB3 = NSTAGE > 3 ? SB : 8;
+  constexpr int SA4 = NSTAGE > 4 ? SA : 8, SB4 = NSTAGE > 4 ? SB : 8;
+  __shared__ __attribute__((aligned(1024))) bf16_t As0[SA], As1[SA], As2[SA];
+  __shared__ __attribute__((aligned(1024))) bf16_t Bs0[SB], Bs1[SB], Bs2[SB];
+  __shared__ __attribute__((aligned(16))) bf16_t As3[SA3], Bs3[SB3], As4[SA4], Bs4[SB4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -228,103 +247,159 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
   const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
   const int z = lid / tiles;
   const int t = lid - z * tiles;
+  constexpr int GROUP_M = CFG::GROUP_M;
   const int group = t / (GROUP_M * nN);
   const int first_m = group * GROUP_M;
   const int gsz = min(nM - first_m, GROUP_M);
   const int tin = t - group * GROUP_M * nN;
   const int mt = first_m + tin % gsz, nt = tin / gsz;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int wm0 = (wave >> 1) * 64, wn0 = (wave & 1) * 64;
+  const int wm0 = (wave / CFG::WGN) * 32 * WM, wn0 = (wave % CFG::WGN) * 32 * WN;
   const bool do_colsum = AT && g.colsum != nullptr && nt == 0;  // uniform per workgroup
-  float csum = 0.f;
+  // column sums: thread -> 8 consecutive m (chunk tid % CHUNKS) of every KG-th k-row
+  constexpr int CHUNKS = BM / 8, KG = NT / CHUNKS;
+  static_assert(BK % KG == 0 && KG * BM * 4 <= SA * 2, "column-sum layout");
+  float csum[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) csum[e] = 0.f;
 
   const int kbeg = z * g.k_split;
   const int kend = min(g.K, kbeg + g.k_split);
   const int klen = kend > kbeg ? kend - kbeg : 0;
   const int nslabs = (klen + BK - 1) / BK;
 
-  f32x16 acc[2][2];
+  f32x16 acc[WM][WN];
 #pragma unroll
-  for (int a = 0; a < 2; a++)
+  for (int a = 0; a < WM; a++)
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int b = 0; b < WN; b++)
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-  // One LDS buffer (32 KB), so three workgroups fit on a CU: the next slab's global loads
-  // are issued into registers before the current slab's MFMAs and written to LDS after a
-  // barrier.
-  SlabLoader<AT> la;
-  SlabLoader<BT> lb;
-  la.init(g.A, g.lda, m0, tid);
-  lb.init(g.B, g.ldb, n0, tid);
-  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;  // uniform
-  auto load_slab = [&](int k0) {
-    if (interior && k0 + BK <= kend) {  // uniform
-      la.load_full(k0, kend);
-      lb.load_full(k0, kend);
-    } else {
-      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
-      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+  SlabCopy<AT, BM, NWAVES, BK> ca;
+  SlabCopy<BT, BN, NWAVES, BK> cb;
+  ca.init(g.A + (AT ? (long long)kbeg * g.lda : kbeg), g.lda, m0,
+          AT ? (long long)(g.K - kbeg) * g.lda : (long long)g.M * g.lda - kbeg, wave, lane);
+  cb.init(g.B + (BT ? (long long)kbeg * g.ldb : kbeg), g.ldb, n0,
+          BT ? (long long)(g.K - kbeg) * g.ldb : (long long)g.N * g.ldb - kbeg, wave, lane);
+
+  // per-lane fragment read offsets (bytes within a stage)
+  const int g16 = lane >> 4, i16 = lane & 15;
+  int rda[WM], rdb[WN];
+#pragma unroll
+  for (int q = 0; q < WM; q++) {
+    if (!AT) rda[q] = (wm0 + 32 * q + r) * 2 * BK + 16 * (h ^ kswz<BK>(wm0 + 32 * q + r));
+    else {
+      const int n = wm0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
+      rda[q] = (8 * h + (i16 >> 2)) * 2 * BM + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
     }
-  };
-  auto compute = [&]() {
-    // the compiler's MFMA / LDS-read interleaving strategy 1 (measured 1% faster per step
-    // than its default schedule on the 774M shapes; strategy 0 and explicit prefetch depth
-    // 2 or 3 were slower)
-    __builtin_amdgcn_iglp_opt(1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-      const int c = 2 * ks + h;
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int q = 0; q < 2; q++) {
-        af[q] = *reinterpret_cast<const bf16x8*>(&As[0][lds_off(wm0 + 32 * q + r, c)]);
-        bfr[q] = *reinterpret_cast<const bf16x8*>(&Bs[0][lds_off(wn0 + 32 * q + r, c)]);
-      }
-#pragma unroll
-      for (int tm = 0; tm < 2; tm++)
-#pragma unroll
-        for (int tn = 0; tn < 2; tn++)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn],
-                                                                0, 0, 0);
-    }
-    if (do_colsum) {  // row m of the A tile, k chunks 4*half .. 4*half+3 of this slab
-      const int m = tid & (BM - 1), half = tid >> 7;
-#pragma unroll
-      for (int cc = 0; cc < 4; cc++) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&As[0][lds_off(m, 4 * half + cc)]);
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          csum += __uint_as_float(x[q] << 16) + __uint_as_float(x[q] & 0xFFFF0000u);
-      }
-    }
-  };
-  if (nslabs > 0) {
-    load_slab(kbeg);
-    la.store(As[0], tid, kbeg + BK > kend);
-    lb.store(Bs[0], tid, kbeg + BK > kend);
   }
-  __syncthreads();
-  for (int kt = 0; kt < nslabs; kt++) {
-    const bool more = kt + 1 < nslabs;
-    if (more) load_slab(kbeg + (kt + 1) * BK);
-    compute();
-    __syncthreads();
-    if (more) {
-      const bool tail = kbeg + (kt + 2) * BK > kend;
-      la.store(As[0], tid, tail);
-      lb.store(Bs[0], tid, tail);
-      __syncthreads();
+#pragma unroll
+  for (int q = 0; q < WN; q++) {
+    if (!BT) rdb[q] = (wn0 + 32 * q + r) * 2 * BK + 16 * (h ^ kswz<BK>(wn0 + 32 * q + r));
+    else {
+      const int n = wn0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
+      rdb[q] = (8 * h + (i16 >> 2)) * 2 * BN + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
     }
   }
 
+  auto stage_a = [&](int s) -> bf16_t* {
+    return s == 0 ? As0 : s == 1 ? As1 : s == 2 ? As2 : s == 3 ? As3 : As4;
+  };
+  auto stage_b = [&](int s) -> bf16_t* {
+    return s == 0 ? Bs0 : s == 1 ? Bs1 : s == 2 ? Bs2 : s == 3 ? Bs3 : Bs4;
+  };
+  auto issue = [&](int kt, int s) {
+    ca.issue(kt, kt < nslabs, stage_a(s), wave);
+    cb.issue(kt, kt < nslabs, stage_b(s), wave);
+  };
+  auto compute = [&](const bf16_t* As, const bf16_t* Bs, int kt) {
+    const char* pa = reinterpret_cast<const char*>(As);
+    const char* pb = reinterpret_cast<const char*>(Bs);
+    const int k0 = kbeg + kt * BK;
+    const bool tail = k0 + BK > kend;  // uniform
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++) {
+      bf16x8 af[WM], bfr[WN];
+#pragma unroll
+      for (int q = 0; q < WM; q++) {
+        if (!AT) af[q] = *reinterpret_cast<const bf16x8*>(pa + (rda[q] ^ (32 * ks)));
+        else af[q] = frag_tr(pa + rda[q] + 16 * ks * 2 * BM, 4 * 2 * BM);
+      }
+#pragma unroll
+      for (int q = 0; q < WN; q++) {
+        if (!BT) bfr[q] = *reinterpret_cast<const bf16x8*>(pb + (rdb[q] ^ (32 * ks)));
+        else bfr[q] = frag_tr(pb + rdb[q] + 16 * ks * 2 * BN, 4 * 2 * BN);
+      }
+      if (tail) {
+        const int lim = kend - (k0 + 16 * ks + 8 * h);
+#pragma unroll
+        for (int q = 0; q < WM; q++) af[q] = kmask(af[q], lim);
+#pragma unroll
+        for (int q = 0; q < WN; q++) bfr[q] = kmask(bfr[q], lim);
+      }
+#pragma unroll
+      for (int tm = 0; tm < WM; tm++)
+#pragma unroll
+        for (int tn = 0; tn < WN; tn++)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn],
+                                                                0, 0, 0);
+    }
+    if (do_colsum) {
+      // A is stored (K, M): LDS [k][m] (k past K reads as zero: the copy stops at the
+      // operand's end)
+#pragma unroll
+      for (int j = 0; j < BK / KG; j++) {
+        const int k = tid / CHUNKS + KG * j, mc = tid % CHUNKS;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(pa + k * 2 * BM +
+                                                         16 * (mc ^ rswz(k & 3)));
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          csum[2 * q] += __uint_as_float(x[q] << 16);
+          csum[2 * q + 1] += __uint_as_float(x[q] & 0xFFFF0000u);
+        }
+      }
+    }
+  };
+  // Stage of slab kt: kt % NSTAGE. Slab kt + NSTAGE - 1 is issued while slab kt is used. The
+  // loop is unrolled by NSTAGE so every LDS access names its stage statically, and every step
+  // issues the same copies (empty ones past the last slab).
+  constexpr int COPIES =
+      SlabCopy<AT, BM, NWAVES, BK>::PER_WAVE + SlabCopy<BT, BN, NWAVES, BK>::PER_WAVE;
+  auto step = [&](int s, int kt) {  // s: a constant at every call
+    // this wave's copies of slab kt have landed (those of the NSTAGE - 2 later slabs may not)
+    wait_vmcnt<COPIES * (NSTAGE - 2)>();
+    lds_barrier();  // so have every wave's; and every wave is done with slab kt - 1
+    issue(kt + NSTAGE - 1, (s + NSTAGE - 1) % NSTAGE);
+    compute(stage_a(s), stage_b(s), kt);
+  };
+  if (nslabs > 0) {
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; s++) issue(s, s);
+    // whole groups of NSTAGE steps in the loop: every path round the loop issues the same
+    // copies in the same order, so the compiler's waits before reading a stage need only that
+    // stage's copies; the remaining steps follow the loop
+    int kt = 0;
+    for (; kt + NSTAGE <= nslabs; kt += NSTAGE) {
+#pragma unroll
+      for (int s = 0; s < NSTAGE; s++) step(s, kt + s);
+    }
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; s++)
+      if (kt + s < nslabs) step(s, kt + s);
+    wait_vmcnt<0>();  // the empty copies past the end still write their zeros
+  }
+
   if (do_colsum) {
-    float* red = reinterpret_cast<float*>(&As[0][0]);
-    if (tid >= BM) red[tid - BM] = csum;
+    // reduce the KG k-row groups of each m through LDS (stage 0 of A: KG x BM floats)
+    float* red = reinterpret_cast<float*>(As0);
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < 8; e++) red[(tid / CHUNKS) * BM + 8 * (tid % CHUNKS) + e] = csum[e];
     __syncthreads();
     if (tid < BM && m0 + tid < g.M) {
-      const float total = csum + red[tid];
+      float total = 0.f;
+      for (int j = 0; j < KG; j++) total += red[j * BM + tid];
       if (g.colsum_zstride) g.colsum[(long long)z * g.colsum_zstride + m0 + tid] = total;
       else g.colsum[m0 + tid] += total;
     }
@@ -334,11 +409,11 @@ __global__ __launch_bounds__(NTHREADS, 3) void gemm_bf16_kernel(Args g) {
                  : g.C;
   // acc[tm][tn][4q + j]: row m = m0 + wm0 + 32 tm + r, column n = n0 + wn0 + 32 tn + 8q + 4h + j
 #pragma unroll
-  for (int tm = 0; tm < 2; tm++) {
+  for (int tm = 0; tm < WM; tm++) {
     const int m = m0 + wm0 + 32 * tm + r;
     if (m >= g.M) continue;
 #pragma unroll
-    for (int tn = 0; tn < 2; tn++)
+    for (int tn = 0; tn < WN; tn++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
@@ -394,55 +469,81 @@ __global__ void split_reduce_bf16_kernel(Args g, const float* __restrict__ ws, i
 }
 
 
-template <bool AT, bool BT, bool CF32>
+template <class CFG, bool AT, bool BT, bool CF32>
 void launch_epi(const Args& a, int epi, dim3 grid, hipStream_t s) {
+  constexpr int NT = CFG::NT;
   switch (epi) {
-    case EPI_STORE: gemm_bf16_kernel<AT, BT, CF32, EPI_STORE><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_GELU: gemm_bf16_kernel<AT, BT, false, EPI_GELU><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_RESID: gemm_bf16_kernel<AT, BT, false, EPI_RESID><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_ACCUM: gemm_bf16_kernel<AT, BT, true, EPI_ACCUM><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_GELU_BWD: gemm_bf16_kernel<AT, BT, false, EPI_GELU_BWD><<<grid, NTHREADS, 0, s>>>(a); break;
+    case EPI_STORE: gemm_bf16_kernel<CFG, AT, BT, CF32, EPI_STORE><<<grid, NT, 0, s>>>(a); break;
+    case EPI_GELU: gemm_bf16_kernel<CFG, AT, BT, false, EPI_GELU><<<grid, NT, 0, s>>>(a); break;
+    case EPI_RESID: gemm_bf16_kernel<CFG, AT, BT, false, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
+    case EPI_ACCUM: gemm_bf16_kernel<CFG, AT, BT, true, EPI_ACCUM><<<grid, NT, 0, s>>>(a); break;
+    case EPI_GELU_BWD: gemm_bf16_kernel<CFG, AT, BT, false, EPI_GELU_BWD><<<grid, NT, 0, s>>>(a); break;
   }
 }
 
-template <bool AT, bool BT>
+template <class CFG, bool AT, bool BT>
 void launch_c(const Args& a, int epi, bool cf32, dim3 grid, hipStream_t s) {
-  if (cf32) launch_epi<AT, BT, true>(a, epi, grid, s);
-  else launch_epi<AT, BT, false>(a, epi, grid, s);
+  if (cf32) launch_epi<CFG, AT, BT, true>(a, epi, grid, s);
+  else launch_epi<CFG, AT, BT, false>(a, epi, grid, s);
 }
 
+template <class CFG>
 void launch(const Args& a, bool at, bool bt, int epi, bool cf32, dim3 grid, hipStream_t s) {
-  if (!at && !bt) launch_c<false, false>(a, epi, cf32, grid, s);
-  else if (!at && bt) launch_c<false, true>(a, epi, cf32, grid, s);
-  else if (at && bt) launch_c<true, true>(a, epi, cf32, grid, s);
-  else launch_c<true, false>(a, epi, cf32, grid, s);
+  if (!at && !bt) launch_c<CFG, false, false>(a, epi, cf32, grid, s);
+  else if (!at && bt) launch_c<CFG, false, true>(a, epi, cf32, grid, s);
+  else if (at && bt) launch_c<CFG, true, true>(a, epi, cf32, grid, s);
+  else launch_c<CFG, true, false>(a, epi, cf32, grid, s);
 }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// K splits from a wave-quantisation cost model (three 256-thread workgroups per CU, 768
-// slots), compute at half the bf16 MFMA peak, split partials and their reduction at 5 TB/s.
-int choose_splits(const GemmBf16& g) {
-  const double tiles = (double)ceil_div(g.M, BM) * ceil_div(g.N, BN);
-  const int kt = ceil_div(g.K, BK);
+// Tile shape and K splits from a wave-quantisation cost model: each shape's workgroups run
+// in rounds of OCC per CU (256 CUs) at that shape's measured fraction of the bf16 MFMA peak;
+// split partials and their reduction move at 5 TB/s.
+enum TileKind { T128 = 1, T256 = 2 };
+struct Plan {
+  int tile;    // TileKind
+  int splits;
+};
+struct TileInfo {
+  int bm, bn, bk, occ;
+  double eff;  // measured fraction of the peak on the 774M shapes
+};
+TileInfo tile_info(int t) {
+  if (t == T128) return {Tile128::BM, Tile128::BN, Tile128::BK, Tile128::OCC, 0.26};
+  return {Tile256::BM, Tile256::BN, Tile256::BK, Tile256::OCC, 0.34};
+}
+// GPT2_GEMM_BF16_TILE=1 (128 x 128) or 2 (256 x 256) in the environment pins the tile shape
+// (tests of both kernels, measurements); anything else leaves the choice to the model
+int forced_tile() {
+  const char* e = getenv("GPT2_GEMM_BF16_TILE");
+  const int v = e ? atoi(e) : 0;
+  return v == T128 || v == T256 ? v : 0;
+}
+Plan choose_plan(const GemmBf16& g) {
   const double mn = (double)g.M * g.N;
-  const double t_mfma = 2.0 * mn * g.K / (0.5 * 2516.6e12);
+  Plan best_p{T128, 1};
   double best = 1e30;
-  int best_s = 1;
-  for (int s = 1; s <= 16; s++) {
-    const int kper = ceil_div(kt, s);
-    if (s > 1 && kper < 4) break;
-    if (s > 1 && ceil_div(kt, kper) != s) continue;
-    const double rounds = tiles * s / 768.0;
-    const double q = std::ceil(rounds) / rounds;
-    double cost = t_mfma * q;
-    if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;
-    if (cost < best * 0.95) {
-      best = cost;
-      best_s = s;
+  for (int t = T128; t <= T256; t++) {
+    if (forced_tile() && t != forced_tile()) continue;
+    const TileInfo ti = tile_info(t);
+    const int kt = ceil_div(g.K, ti.bk);
+    const double tiles = (double)ceil_div(g.M, ti.bm) * ceil_div(g.N, ti.bn);
+    for (int s = 1; s <= 16; s++) {
+      const int kper = ceil_div(kt, s);
+      if (s > 1 && kper * ti.bk < 128) break;
+      if (s > 1 && ceil_div(kt, kper) != s) continue;
+      const double rounds = std::ceil(tiles * s / (256.0 * ti.occ));
+      double cost = rounds * ti.occ * 2.0 * ti.bm * ti.bn * (double)kper * ti.bk /
+                    (ti.eff * 2516.6e12 / 256);
+      if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;
+      if (cost < best * 0.97) {
+        best = cost;
+        best_p = Plan{t, s};
+      }
     }
   }
-  return best_s;
+  return best_p;
 }
 
 int split_ld(int N) { return (N + 3) & ~3; }
@@ -452,7 +553,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 size_t gemm_bf16_workspace_floats(const GemmBf16& g) {
-  const int s = choose_splits(g);
+  const int s = choose_plan(g).splits;
   if (s <= 1) return 0;
   return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
 }
@@ -466,10 +567,13 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
   // multiples of 8 elements; the epilogue's vector stores need ldc % 8 (bf16) or % 4 (fp32)
   const bool cf32 = g.epi == EPI_ACCUM;
   const int a_cols = g.a_trans ? g.M : g.K, b_cols = g.b_trans ? g.N : g.K;
-  // (and leading dimensions below 2^24, so a slab's per-thread byte offsets fit 32 bits)
+  // (and leading dimensions below 2^24 and operands below 4 GiB, so the byte offsets and
+  // the extent of a slab's buffer resource fit 32 bits)
   if (!aligned16(g.A) || !aligned16(g.B) || !aligned16(g.C) || g.lda % 8 || g.ldb % 8 ||
       g.ldc % (cf32 ? 4 : 8) || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N ||
-      (g.bias && !aligned16(g.bias)) || g.lda >= (1 << 24) || g.ldb >= (1 << 24)) {
+      (g.bias && !aligned16(g.bias)) || g.lda >= (1 << 24) || g.ldb >= (1 << 24) ||
+      2.0 * (g.a_trans ? g.K : g.M) * g.lda >= 4294967295.0 ||
+      2.0 * (g.b_trans ? g.K : g.N) * g.ldb >= 4294967295.0) {
     set_global_error("gemm_bf16: unsupported alignment or leading dimension (lda=%d ldb=%d "
                      "ldc=%d)", g.lda, g.ldb, g.ldc);
     return -1;
@@ -496,14 +600,21 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
   a.c_zstride = 0;
   a.colsum_zstride = 0;
 
-  int splits = choose_splits(g);
+  const Plan plan = choose_plan(g);
+  const TileInfo ti = tile_info(plan.tile);
+  int splits = plan.splits;
   if (splits > 1 && (!workspace || ws_floats < gemm_bf16_workspace_floats(g))) splits = 1;
-  const int kt = ceil_div(g.K, BK);
+  const int kt = ceil_div(g.K, ti.bk);
   const int kt_per = ceil_div(kt, splits);
   splits = ceil_div(kt, kt_per);
-  a.k_split = kt_per * BK;
+  a.k_split = kt_per * ti.bk;
   a.splits = splits;
-  const int tiles = ceil_div(g.M, BM) * ceil_div(g.N, BN);
+  const int tiles = ceil_div(g.M, ti.bm) * ceil_div(g.N, ti.bn);
+  auto run = [&](const Args& x, int epi, bool f32out, int grid) {
+    const bool at = g.a_trans, bt = g.b_trans;
+    if (plan.tile == T128) launch<Tile128>(x, at, bt, epi, f32out, dim3(grid), stream);
+    else launch<Tile256>(x, at, bt, epi, f32out, dim3(grid), stream);
+  };
 
   const double MN = (double)g.M * g.N;
   const double flop = 2.0 * MN * g.K;
@@ -517,7 +628,7 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d", g.M, g.N, g.K);
     ProfScope ps(name, flop, in_bytes + out_bytes, stream);
-    launch(a, g.a_trans, g.b_trans, g.epi, cf32, dim3(tiles), stream);
+    run(a, g.epi, cf32, tiles);
   } else {
     Args p = a;
     p.C = workspace;
@@ -535,7 +646,7 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
                splits);
     {
       ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
-      launch(p, g.a_trans, g.b_trans, EPI_STORE, true, dim3(tiles * splits), stream);
+      run(p, EPI_STORE, true, tiles * splits);
     }
     const long long total = (long long)g.M * ((g.N + 3) / 4);
     int blocks = (int)((total + 255) / 256);

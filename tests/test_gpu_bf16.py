@@ -64,7 +64,7 @@ CASES = [
     (300, 96, 200, 0, 1), (64, 80, 50257, 0, 1), (128, 128, 4096, 0, 1),  # grad input (NN)
     (200, 96, 300, 1, 1), (50257, 64, 64, 1, 1), (128, 256, 8192, 1, 1),  # grad weight (TN)
     (136, 72, 130, 1, 0),
-    # at least 256 tiles of 256 x 256: the 512-thread kernel, with ragged edges
+    # more tiles than CUs (both tile shapes), with ragged edges
     (4100, 4104, 136, 0, 0), (4100, 4104, 200, 0, 1), (4104, 4100, 72, 1, 1),
 ]
 
@@ -80,9 +80,14 @@ def stored(op, trans, ld_pad=0):
     return buf, ld
 
 
+@pytest.mark.parametrize("tile", ["1", "2"])
 @pytest.mark.parametrize("M,N,K,at,bt", CASES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
-def test_gemm_bf16(M, N, K, at, bt, epi):
+def test_gemm_bf16(M, N, K, at, bt, epi, tile, monkeypatch):
+    """Both tile shapes of the bf16 GEMM: 128 x 128 tiles with 32-deep K slabs and 256 x 256
+    tiles with 64-deep slabs (the library picks one per shape; the environment variable pins
+    it)."""
+    monkeypatch.setenv("GPT2_GEMM_BF16_TILE", tile)
     if K > 1000 and epi in (1, 2):
         pytest.skip("long-K shapes run with the epilogues the step uses with them")
     if at and epi in (1, 2) and M * N > 4_000_000:
