@@ -9,12 +9,14 @@
 // accumulate, and the GELU backward (section 1.10).
 //
 // Tiling: a 256-thread workgroup owns a 128x128 tile of C; its four waves own 64x64
-// sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances 16 at a time through two LDS
-// buffers: global loads for the next K-slab are issued before the MFMAs of the current one
-// and written to the other buffer afterwards, so one barrier per slab suffices.
-// LDS holds both operands K-major ([k][m] and [k][n], row stride 130 floats): a lane's two
-// MFMA blocks along M take adjacent rows m = 2r and 2r+1, so one 8-byte LDS read feeds two
-// MFMAs, and the results are un-interleaved in the epilogue.
+// sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances in slabs of 16 that go from global
+// memory straight into LDS (buffer loads with the LDS as destination, no staging registers),
+// the next slab in flight while the current one is used, one LDS object per stage. An
+// operand stored with K contiguous is kept [row][k] in LDS and read 16 bytes (four k) per
+// lane, feeding four MFMAs: the products take the K order in which lane half h supplies
+// k = 8h + s at step s. An operand stored (K, rows) is kept as stored, [k][row], and read 4
+// bytes per lane. The MFMA takes the B fragment as its first operand, so a lane ends up
+// holding runs of 4 consecutive output columns of one row: the epilogue works on float4s.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -25,12 +27,15 @@
 namespace gpt2 {
 namespace {
 
-#ifndef GPT2_GEMM_BK
-#define GPT2_GEMM_BK 16
+constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int NTHREADS = 256, NWAVES = NTHREADS / 64;
+#ifndef GPT2_GEMM_STAGES
+#define GPT2_GEMM_STAGES 2
 #endif
-constexpr int BM = 128, BN = 128, BK = GPT2_GEMM_BK;
-constexpr int LDSA = BM + 2, LDSB = BN + 2;
-constexpr int NTHREADS = 256;
+// LDS slabs per workgroup (16 KB each); four workgroups per CU with two, three with three
+constexpr int NSTAGE = GPT2_GEMM_STAGES;
+constexpr int OCC = NSTAGE == 2 ? 4 : 3;
+static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
 
 struct Args {
   const float* A;
@@ -52,169 +57,141 @@ constexpr int GROUP_M = 8;  // m-tiles that sweep the n-tiles together (L2 reuse
 // word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family GPUs
 constexpr int kBufferFlags = 0x00020000;
 
-// Loads one K-slab of an operand into registers (4 float4 per thread) and later stores it to
-// LDS in [k][row] order. `rows` is M (for A) or N (for B).
-//  trans == false: operand stored (rows, K) row-major: thread -> (row = tid/8 + 32i, k4 = tid%8)
-//  trans == true : operand stored (K, rows):          thread -> (k = tid/32 + 8i, r4 = tid%32)
-// The loads carry no branches and no use of their values before the LDS store, so all eight
-// of a thread's loads stay in flight across the MFMAs of the current slab. Addresses are
-// clamped into the operand: a row past `rows` reads the last row (its products only reach
-// outputs that are never stored). A slab that lies wholly below `kend` is loaded from a
-// uniform per-slab base plus per-thread byte offsets computed once (`init`), with no clamps
-// or masks; only a slab that reaches past `kend` clamps its K indices (to a valid element
-// whose value is replaced by zero when the slab is written to LDS). The host keeps the byte
-// offsets below 2^32.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from a buffer into LDS (lane l writes lds + 16 l); `lds` is wave-uniform
+GPT2_DEVICE_INLINE void copy_to_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
+// LDS placement of an operand stored with K contiguous: [row][k], 64-byte rows of BK = 16 k;
+// the 16-byte chunk c of row r holds the row's chunk c ^ kswz(r), which spreads the 16-byte
+// fragment reads (32 consecutive rows, one chunk) over all banks. An operand stored
+// (K, rows) keeps that layout, [k][row] (512-byte k-rows), and is read 4 bytes per lane
+// from consecutive rows (no conflicts, no swizzle).
+GPT2_DEVICE_INLINE int kswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// One operand's share of the slab pipeline: a slab (BK k x 128 rows, 8 KB) is copied from
+// global memory straight into LDS, 1 KB per wave-wide buffer load (lane l fills bytes
+// 16 l .. 16 l + 15 of the KB), without passing through registers; two copies per wave. The
+// buffer resource of a slab ends where the operand ends, so rows past its last row (and,
+// for an operand stored (K, rows), k past K) read as zero; a K tail inside a row is masked
+// in the fragments. The extent is clamped to 32 bits: only a slab whose extent is small
+// (the last rows or the last k) ever reaches past the operand. Per-lane byte offsets are
+// computed once; the host keeps them below 2^32.
 template <bool TRANS>
-struct SlabLoader {
-  // float4 loads per thread per slab: 128 x BK floats / (256 threads x 4)
-  static constexpr int NV = BM * BK / (4 * NTHREADS);
-  static constexpr int F4_PER_ROW = BK / 4;              // !TRANS: float4s along K per row
-  static constexpr int ROWS_PER_PASS = NTHREADS / F4_PER_ROW;
-  static constexpr int K_PER_PASS = NTHREADS / (BM / 4);  // TRANS: K rows per pass (8)
-  f32x4 v[NV];
-  int k0, kend;
-  uint32_t voff[NV];  // byte offsets of this thread's float4s from the slab base
-  const float* base0;  // !TRANS: row row0 of the operand; TRANS: the operand itself
-  int ld;
+struct SlabCopy {
+  static constexpr int PER_WAVE = BM * BK * 4 / 1024 / NWAVES;
+  static_assert(PER_WAVE * NWAVES * 1024 == BM * BK * 4, "whole 1 KB copies per wave");
+  const char* tile;  // operand at this tile's first row (!TRANS) or column (TRANS), k = kbeg
+  long long step;    // bytes between consecutive slabs
+  long long remain;  // bytes from `tile` to the end of the operand
+  uint32_t voff[PER_WAVE];
 
-  __device__ __forceinline__ void init(const float* __restrict__ P, int ld_, int row0, int rows,
-                                       int tid) {
-    ld = ld_;
+  __device__ __forceinline__ void init(const float* P, int ld, int row0, long long total,
+                                       int wave, int lane) {
+    const long long at = TRANS ? (long long)row0 : (long long)row0 * ld;
+    tile = reinterpret_cast<const char*>(P + at);
+    remain = 4 * (total - at);
+    step = TRANS ? 4LL * BK * ld : 4LL * BK;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
+    for (int j = 0; j < PER_WAVE; j++) {
+      const int b = (j * NWAVES + wave) * 1024 + 16 * lane;  // LDS byte within the slab
       if (!TRANS) {
-        const int r = min(row0 + tid / F4_PER_ROW + ROWS_PER_PASS * i, rows - 1) - row0;
-        voff[i] = (uint32_t)(r * ld + 4 * (tid % F4_PER_ROW)) * 4u;
+        const int row = b >> 6, p = (b >> 4) & 3;
+        voff[j] = (uint32_t)(row * ld + 4 * (p ^ kswz(row))) * 4u;
       } else {
-        const int k = tid / (BM / 4) + K_PER_PASS * i;
-        const int r = min(row0 + 4 * (tid % (BM / 4)), (rows - 1) & ~3);
-        voff[i] = (uint32_t)(k * ld + r) * 4u;
-      }
-    }
-    base0 = TRANS ? P : P + (long long)row0 * ld;
-  }
-
-  // a slab wholly below kend: buffer loads from a scalar base (the slab's buffer resource)
-  // plus this thread's 32-bit offsets, so the loop spends no vector ALU on addresses
-  __device__ __forceinline__ void load_full(int k0_, int kend_) {
-    k0 = k0_;
-    kend = kend_;
-    const float* b = TRANS ? base0 + (long long)k0 * ld : base0 + k0;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(b), (short)0, -1, kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < NV; i++)
-      v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0));
-  }
-
-  __device__ __forceinline__ void load(const float* __restrict__ P, int ld, int row0, int rows,
-                                       int k0_, int kend_, int tid) {
-    k0 = k0_;
-    kend = kend_;
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-      if (!TRANS) {
-        const int r = min(row0 + tid / F4_PER_ROW + ROWS_PER_PASS * i, rows - 1);
-        const int k = min(k0 + 4 * (tid % F4_PER_ROW), (kend - 1) & ~3);
-        v[i] = *reinterpret_cast<const f32x4*>(P + (long long)r * ld + k);
-      } else {
-        const int k = min(k0 + tid / (BM / 4) + K_PER_PASS * i, kend - 1);
-        const int r = min(row0 + 4 * (tid % (BM / 4)), (rows - 1) & ~3);
-        v[i] = *reinterpret_cast<const f32x4*>(P + (long long)k * ld + r);
+        const int k = b >> 9, p = (b & 511) >> 4;
+        voff[j] = (uint32_t)(k * ld + 4 * p) * 4u;
       }
     }
   }
 
-  template <int LDS>
-  __device__ __forceinline__ void store(float (*S)[LDS], int tid) const {
-    if (k0 + BK <= kend) {  // full slab (uniform): no masks
+  // `live` false: a copy past the last slab, given an empty range (it reads nothing and
+  // writes zeros), so that every pipeline step issues the same number of copies
+  __device__ __forceinline__ void issue(int kt, bool live, float* lds, int wave) const {
+    const long long off = live ? (long long)kt * step : 0;
+    const long long left = live ? remain - off : 0;
+    const int nrec = (int)(uint32_t)(left > 0xFFFFFFFFLL ? 0xFFFFFFFFLL : left > 0 ? left : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tile + off), (short)0, nrec, kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < NV; i++) {
-        if (!TRANS) {
-          const int r = tid / F4_PER_ROW + ROWS_PER_PASS * i;
-          const int k = 4 * (tid % F4_PER_ROW);
-#pragma unroll
-          for (int j = 0; j < 4; j++) S[k + j][r] = v[i][j];
-        } else {
-          const int k = tid / (BM / 4) + K_PER_PASS * i;
-          const int r = 4 * (tid % (BM / 4));
-          *reinterpret_cast<f32x2*>(&S[k][r]) = f32x2{v[i][0], v[i][1]};
-          *reinterpret_cast<f32x2*>(&S[k][r + 2]) = f32x2{v[i][2], v[i][3]};
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-      if (!TRANS) {
-        const int r = tid / F4_PER_ROW + ROWS_PER_PASS * i;
-        const int k = 4 * (tid % F4_PER_ROW);
-        const int kg = k0 + k;  // global K index of element 0
-#pragma unroll
-        for (int j = 0; j < 4; j++) S[k + j][r] = kg + j < kend ? v[i][j] : 0.f;
-      } else {
-        const int k = tid / (BM / 4) + K_PER_PASS * i;
-        const int r = 4 * (tid % (BM / 4));
-        const bool ok = k0 + k < kend;
-        *reinterpret_cast<f32x2*>(&S[k][r]) = ok ? f32x2{v[i][0], v[i][1]} : f32x2{0.f, 0.f};
-        *reinterpret_cast<f32x2*>(&S[k][r + 2]) = ok ? f32x2{v[i][2], v[i][3]} : f32x2{0.f, 0.f};
-      }
-    }
+    for (int j = 0; j < PER_WAVE; j++)
+      copy_to_lds16(rs, reinterpret_cast<char*>(lds) + (j * NWAVES + wave) * 1024, voff[j]);
   }
 };
 
+// workgroup barrier without a memory fence: the slab copies still in flight must not be
+// waited for here (the fence of __syncthreads would wait for all of them); the clobber keeps
+// the compiler from moving LDS accesses across it
+GPT2_DEVICE_INLINE void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// wait until at most n vector-memory operations of this wave are outstanding (n < 16)
+template <int n>
+GPT2_DEVICE_INLINE void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);  // expcnt and lgkmcnt at their no-wait maxima
+}
+
+// Epilogue of four consecutive columns n..n+3 of row m (n % 4 == 0, m < M, n < N): bias,
+// GELU, residual, accumulate or GELU backward, then the store (16-byte vectors when the
+// row stride keeps them aligned).
 template <int EPI>
-__device__ __forceinline__ void epilogue_pair(const Args& g, float* C, int m, int n, float v0,
-                                              float v1) {
-  if (m >= g.M || n >= g.N) return;
-  const bool two = n + 1 < g.N;
-  long long off = (long long)m * g.ldc + n;
+__device__ __forceinline__ void epilogue4(const Args& g, float* C, int m, int n, f32x4 v) {
+  const long long off = (long long)m * g.ldc + n;
+  const int cnt = min(4, g.N - n);
+  const bool vec = cnt == 4 && (g.ldc & 3) == 0;
   if (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
     if (g.bias) {
-      v0 += g.bias[n];
-      if (two) v1 += g.bias[n + 1];
+      if (cnt == 4) v += *reinterpret_cast<const f32x4*>(g.bias + n);
+      else
+        for (int j = 0; j < cnt; j++) v[j] += g.bias[n + j];
     }
   }
-  if (EPI == EPI_RESID) {
-    if (two) {
-      f32x2 r = *reinterpret_cast<const f32x2*>(g.R + off);
-      v0 += r[0];
-      v1 += r[1];
+  if (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_ACCUM) {
+    const float* src = EPI == EPI_ACCUM ? C : g.R;
+    f32x4 r;
+    if (vec) r = *reinterpret_cast<const f32x4*>(src + off);
+    else
+      for (int j = 0; j < 4; j++) r[j] = j < cnt ? src[off + j] : 0.f;
+    if (EPI == EPI_GELU_BWD) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) v[j] *= gelu_bwd(r[j]);
     } else {
-      v0 += g.R[off];
+      v += r;
     }
   }
-  if (EPI == EPI_ACCUM) {
-    if (two) {
-      f32x2 c = *reinterpret_cast<const f32x2*>(C + off);
-      v0 += c[0];
-      v1 += c[1];
-    } else {
-      v0 += C[off];
-    }
-  }
-  if (EPI == EPI_GELU_BWD) {
-    if (two) {
-      f32x2 r = *reinterpret_cast<const f32x2*>(g.R + off);
-      v0 *= gelu_bwd(r[0]);
-      v1 *= gelu_bwd(r[1]);
-    } else {
-      v0 *= gelu_bwd(g.R[off]);
-    }
-  }
-  if (two) {
-    *reinterpret_cast<f32x2*>(C + off) = f32x2{v0, v1};
-    if (EPI == EPI_GELU) *reinterpret_cast<f32x2*>(g.C2 + off) = f32x2{gelu_fwd(v0), gelu_fwd(v1)};
+  if (vec) {
+    *reinterpret_cast<f32x4*>(C + off) = v;
+    if (EPI == EPI_GELU)
+      *reinterpret_cast<f32x4*>(g.C2 + off) =
+          f32x4{gelu_fwd(v[0]), gelu_fwd(v[1]), gelu_fwd(v[2]), gelu_fwd(v[3])};
   } else {
-    C[off] = v0;
-    if (EPI == EPI_GELU) g.C2[off] = gelu_fwd(v0);
+    for (int j = 0; j < cnt; j++) {
+      C[off + j] = v[j];
+      if (EPI == EPI_GELU) g.C2[off + j] = gelu_fwd(v[j]);
+    }
   }
 }
 
+// zero the elements of a 4-k fragment at or past `lim` (its first element being k = 0)
+GPT2_DEVICE_INLINE f32x4 kmask4(f32x4 v, int lim) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) v[e] = e < lim ? v[e] : 0.f;
+  return v;
+}
+
+// K order of the products: at MFMA step s (0..7) of a slab, lane half h supplies k = 8h + s
+// for both operands (each lane supplies one k per 32x32x2 MFMA; any bijection contracts the
+// same sum), so a lane's four consecutive k of a row stored with K contiguous are one
+// 16-byte LDS read feeding four MFMAs.
 template <bool AT, bool BT, int EPI>
-__global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
-  __shared__ float As[2][BK][LDSA];
-  __shared__ float Bs[2][BK][LDSB];
+__global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
+  // one LDS object per pipeline stage, so the compiler can tell which copies a read waits
+  // for (the third is a placeholder with two stages)
+  constexpr int S3 = NSTAGE > 2 ? BM * BK : 4;
+  __shared__ __attribute__((aligned(1024))) float As0[BM * BK], As1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) float Bs0[BN * BK], Bs1[BN * BK];
+  __shared__ __attribute__((aligned(16))) float As2[S3], Bs2[S3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -238,7 +215,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
   const int kbeg = z * g.k_split;
   const int kend = min(g.K, kbeg + g.k_split);
   const int klen = kend > kbeg ? kend - kbeg : 0;
-  const int ntiles = (klen + BK - 1) / BK;
+  const int nslabs = (klen + BK - 1) / BK;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -248,60 +225,101 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-  SlabLoader<AT> la;
-  SlabLoader<BT> lb;
-  la.init(g.A, g.lda, m0, g.M, tid);
-  lb.init(g.B, g.ldb, n0, g.N, tid);
-  auto load_slab = [&](int kt) {
+  SlabCopy<AT> ca;
+  SlabCopy<BT> cb;
+  ca.init(g.A + (AT ? (long long)kbeg * g.lda : kbeg), g.lda, m0,
+          AT ? (long long)(g.K - kbeg) * g.lda : (long long)g.M * g.lda - kbeg, wave, lane);
+  cb.init(g.B + (BT ? (long long)kbeg * g.ldb : kbeg), g.ldb, n0,
+          BT ? (long long)(g.K - kbeg) * g.ldb : (long long)g.N * g.ldb - kbeg, wave, lane);
+
+  // per-lane fragment read offsets (bytes within a stage): K-contiguous operands, the chunk
+  // of k = 8h .. 8h + 3 (the next four k: offset ^ 16); (K, rows) operands, k-row 8h
+  int rda[2], rdb[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int ra = wm0 + 32 * q + r, rb = wn0 + 32 * q + r;
+    rda[q] = AT ? (8 * h * BM + ra) * 4 : ra * 64 + 16 * ((2 * h) ^ kswz(ra));
+    rdb[q] = BT ? (8 * h * BN + rb) * 4 : rb * 64 + 16 * ((2 * h) ^ kswz(rb));
+  }
+
+  auto stage_a = [&](int s) -> float* { return s == 0 ? As0 : s == 1 ? As1 : As2; };
+  auto stage_b = [&](int s) -> float* { return s == 0 ? Bs0 : s == 1 ? Bs1 : Bs2; };
+  auto issue = [&](int kt, int s) {
+    ca.issue(kt, kt < nslabs, stage_a(s), wave);
+    cb.issue(kt, kt < nslabs, stage_b(s), wave);
+  };
+  auto frag = [&](const char* p, int rd, int j, bool trans, int rows) -> f32x4 {
+    if (!trans) return *reinterpret_cast<const f32x4*>(p + (rd ^ (16 * j)));
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      v[e] = *reinterpret_cast<const float*>(p + rd + (4 * j + e) * rows * 4);
+    return v;
+  };
+  auto compute = [&](const float* As, const float* Bs, int kt) {
+    const char* pa = reinterpret_cast<const char*>(As);
+    const char* pb = reinterpret_cast<const char*>(Bs);
     const int k0 = kbeg + kt * BK;
-    if (k0 + BK <= kend) {  // uniform
-      la.load_full(k0, kend);
-      lb.load_full(k0, kend);
-    } else {
-      la.load(g.A, g.lda, m0, g.M, k0, kend, tid);
-      lb.load(g.B, g.ldb, n0, g.N, k0, kend, tid);
+    const bool tail = k0 + BK > kend;  // uniform
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      f32x4 af[2], bfr[2];
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        af[q] = frag(pa, rda[q], j, AT, BM);
+        bfr[q] = frag(pb, rdb[q], j, BT, BN);
+      }
+      if (tail) {
+        const int lim = kend - (k0 + 8 * h + 4 * j);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+          af[q] = kmask4(af[q], lim);
+          bfr[q] = kmask4(bfr[q], lim);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+#pragma unroll
+        for (int tm = 0; tm < 2; tm++)
+#pragma unroll
+          for (int tn = 0; tn < 2; tn++)
+            acc[tm][tn] = mfma32x32x2(bfr[tn][e], af[tm][e], acc[tm][tn]);
+    }
+    if (do_colsum) {  // column m of the A tile ([k][m] in LDS), k-rows 8 half .. 8 half + 7
+      const int m = tid & (BM - 1), half = tid >> 7;
+#pragma unroll
+      for (int kk = 0; kk < BK / 2; kk++) csum += As[(half * (BK / 2) + kk) * BM + m];
     }
   };
-  if (ntiles > 0) {
-    load_slab(0);
-    la.template store<LDSA>(As[0], tid);
-    lb.template store<LDSB>(Bs[0], tid);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; kt++) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) load_slab(kt + 1);
-    // all of this slab's fragments first, then its 64 MFMAs
-    f32x2 af[BK / 2], bf[BK / 2];
+  // Stage of slab kt: kt % NSTAGE; slab kt + NSTAGE - 1 is issued while slab kt is used. The
+  // loop is unrolled by NSTAGE so every LDS access names its stage statically, and every
+  // step issues the same copies (empty ones past the last slab): the compiler's own waits
+  // for the copies then follow them exactly.
+  constexpr int COPIES = SlabCopy<AT>::PER_WAVE + SlabCopy<BT>::PER_WAVE;
+  auto step = [&](int s, int kt) {  // s: a constant at every call
+    // this wave's copies of slab kt have landed (those of the NSTAGE - 2 later slabs may not)
+    wait_vmcnt<COPIES * (NSTAGE - 2)>();
+    lds_barrier();  // so have every wave's; and every wave is done with slab kt - 1
+    issue(kt + NSTAGE - 1, (s + NSTAGE - 1) % NSTAGE);
+    compute(stage_a(s), stage_b(s), kt);
+  };
+  if (nslabs > 0) {
 #pragma unroll
-    for (int kk2 = 0; kk2 < BK / 2; kk2++) {
-      const int kk = 2 * kk2 + h;
-      af[kk2] = *reinterpret_cast<const f32x2*>(&As[cur][kk][wm0 + 2 * r]);
-      bf[kk2] = *reinterpret_cast<const f32x2*>(&Bs[cur][kk][wn0 + 2 * r]);
+    for (int s = 0; s < NSTAGE - 1; s++) issue(s, s);
+    int kt = 0;
+    for (; kt + NSTAGE <= nslabs; kt += NSTAGE) {
+#pragma unroll
+      for (int s = 0; s < NSTAGE; s++) step(s, kt + s);
     }
 #pragma unroll
-    for (int kk2 = 0; kk2 < BK / 2; kk2++) {
-      acc[0][0] = mfma32x32x2(af[kk2][0], bf[kk2][0], acc[0][0]);
-      acc[0][1] = mfma32x32x2(af[kk2][0], bf[kk2][1], acc[0][1]);
-      acc[1][0] = mfma32x32x2(af[kk2][1], bf[kk2][0], acc[1][0]);
-      acc[1][1] = mfma32x32x2(af[kk2][1], bf[kk2][1], acc[1][1]);
-    }
-    if (do_colsum) {  // column c of the A tile: rows 16*half .. 16*half+15 of this slab
-      const int c = tid & (BM - 1), half = tid >> 7;
-#pragma unroll
-      for (int kk = 0; kk < BK / 2; kk++) csum += As[cur][half * (BK / 2) + kk][c];
-    }
-    if (more) {
-      la.template store<LDSA>(As[cur ^ 1], tid);
-      lb.template store<LDSB>(Bs[cur ^ 1], tid);
-    }
-    __syncthreads();
+    for (int s = 0; s < NSTAGE - 1; s++)
+      if (kt + s < nslabs) step(s, kt + s);
+    wait_vmcnt<0>();  // the empty copies past the end still write their zeros
   }
 
   if (do_colsum) {
-    float* red = &As[0][0][0];
+    float* red = As0;
+    lds_barrier();
     if (tid >= BM) red[tid - BM] = csum;
     __syncthreads();
     if (tid < BM && m0 + tid < g.M) {
@@ -312,15 +330,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(Args g) {
   }
 
   float* C = g.C + (long long)z * g.c_zstride;
+  // acc[tm][tn][4q + j]: row m = m0 + wm0 + 32 tm + r, column n = n0 + wn0 + 32 tn + 8q + 4h + j
 #pragma unroll
-  for (int bm = 0; bm < 2; bm++)
+  for (int tm = 0; tm < 2; tm++) {
+    const int m = m0 + wm0 + 32 * tm + r;
+    if (m >= g.M) continue;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int row = 8 * (i / 4) + 4 * h + (i % 4);
-      const int m = m0 + wm0 + 2 * row + bm;
-      const int n = n0 + wn0 + 2 * r;
-      epilogue_pair<EPI>(g, C, m, n, acc[bm][0][i], acc[bm][1][i]);
-    }
+    for (int tn = 0; tn < 2; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
+        if (n >= g.N) continue;
+        epilogue4<EPI>(g, C, m, n,
+                       f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                             acc[tm][tn][4 * q + 3]});
+      }
+  }
 }
 
 // The epilogue `EPI` of one output element of a split-K GEMM (only EPI_STORE-with-bias,
@@ -436,9 +461,9 @@ void launch(const Args& a, bool at, bool bt, int epi, dim3 grid, hipStream_t s) 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // Number of K splits for a problem, from a cost model fitted to measurements on MI355X.
-// Four 256-thread workgroups fit on each of the 256 CUs (1024 slots). A launch of n
-// workgroups runs ceil(n/1024) rounds of the same length, so relative to perfectly packed
-// work it costs q = ceil(n/1024) / (n/1024); splitting K multiplies n by the split count and
+// OCC 256-thread workgroups fit on each of the 256 CUs (256 OCC slots). A launch of n
+// workgroups runs ceil(n/slots) rounds of the same length, so relative to perfectly packed
+// work it costs q = ceil(n/slots) / (n/slots); splitting K multiplies n by the split count and
 // adds a pass that reads the partials and applies the epilogue (the partials themselves are
 // written while the GEMM computes).
 // Compute time is estimated at 90% of the fp32 MFMA peak, memory at 5 TB/s.
@@ -456,7 +481,7 @@ int choose_splits(const Gemm& g) {
     const int kper = ceil_div(kt, s);
     if (s > 1 && kper < 4) break;
     if (s > 1 && ceil_div(kt, kper) != s) continue;
-    const double rounds = tiles * s / 1024.0;
+    const double rounds = tiles * s / (256.0 * OCC);
     const double q = std::ceil(rounds) / rounds;
     double cost = t_mfma * q;
     if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;  // partials are written during the GEMM
