@@ -366,19 +366,37 @@ void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
   for (int qt = kb * DK_KEYS / TILE; qt < nqt; qt++) {
     const int q0 = qt * TILE;
     __syncthreads();
-    constexpr int F4 = HSP / 4;
+    // A thread takes a 4 x 4 block (rows 4a .. 4a+3, head dims 4dg .. 4dg+3), consecutive
+    // threads consecutive row groups, and writes it row-major and, transposed in registers,
+    // head-dim-major, all as 16-byte vectors: the transposed rows of eight consecutive
+    // threads then fall on different banks, and the row-major rows are written in a
+    // per-thread rotated order (row 4a + (w + a) % 4 at step w), which halves their
+    // conflicts.
+    constexpr int RG = TILE / 4, DG = HSP / 4;
 #pragma unroll
-    for (int i = 0; i < TILE * F4 / DK_THR; i++) {
-      const int f = tid + DK_THR * i;
-      const int row = f / F4, d = 4 * (f % F4);
-      const f32x4 qv = load4_rowcol(base, C3, q0 + row, d, T, hs);
-      const f32x4 ov = load4_rowcol(dobase, C, q0 + row, d, T, hs);
-      *reinterpret_cast<f32x4*>(&Qs[row][d]) = qv;
-      *reinterpret_cast<f32x4*>(&dOs[row][d]) = ov;
+    for (int blk = 0; blk < (RG * DG + DK_THR - 1) / DK_THR; blk++) {
+      const int f = tid + DK_THR * blk;
+      if (RG * DG % DK_THR != 0 && f >= RG * DG) break;
+      const int a = f % RG, d = 4 * (f / RG);
+      f32x4 qv[4], ov[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        qv[i] = load4_rowcol(base, C3, q0 + 4 * a + i, d, T, hs);
+        ov[i] = load4_rowcol(dobase, C, q0 + 4 * a + i, d, T, hs);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const int i = (w + a) & 3;
+        const f32x4 qr = i == 0 ? qv[0] : i == 1 ? qv[1] : i == 2 ? qv[2] : qv[3];
+        const f32x4 orow = i == 0 ? ov[0] : i == 1 ? ov[1] : i == 2 ? ov[2] : ov[3];
+        *reinterpret_cast<f32x4*>(&Qs[4 * a + i][d]) = qr;
+        *reinterpret_cast<f32x4*>(&dOs[4 * a + i][d]) = orow;
+      }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        QT[d + j][row] = qv[j];
-        dOT[d + j][row] = ov[j];
+        *reinterpret_cast<f32x4*>(&QT[d + j][4 * a]) = f32x4{qv[0][j], qv[1][j], qv[2][j], qv[3][j]};
+        *reinterpret_cast<f32x4*>(&dOT[d + j][4 * a]) =
+            f32x4{ov[0][j], ov[1][j], ov[2][j], ov[3][j]};
       }
     }
     if (tid < TILE) {

@@ -27,14 +27,18 @@
 namespace gpt2 {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16;
-constexpr int NTHREADS = 256, NWAVES = NTHREADS / 64;
+#ifndef GPT2_GEMM_BM
+#define GPT2_GEMM_BM 128
+#endif
+// BM x 128 tiles; waves of 64 x 64 (BM / 64 x 2 of them)
+constexpr int BM = GPT2_GEMM_BM, BN = 128, BK = 16;
+constexpr int NTHREADS = 2 * BM, NWAVES = NTHREADS / 64;
 #ifndef GPT2_GEMM_STAGES
 #define GPT2_GEMM_STAGES 2
 #endif
 // LDS slabs per workgroup (16 KB each); four workgroups per CU with two, three with three
 constexpr int NSTAGE = GPT2_GEMM_STAGES;
-constexpr int OCC = NSTAGE == 2 ? 4 : 3;
+constexpr int OCC = (NSTAGE == 2 ? 4 : 3) * 128 / BM;
 static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
 
 struct Args {
@@ -79,10 +83,10 @@ GPT2_DEVICE_INLINE int kswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 // in the fragments. The extent is clamped to 32 bits: only a slab whose extent is small
 // (the last rows or the last k) ever reaches past the operand. Per-lane byte offsets are
 // computed once; the host keeps them below 2^32.
-template <bool TRANS>
+template <bool TRANS, int R>
 struct SlabCopy {
-  static constexpr int PER_WAVE = BM * BK * 4 / 1024 / NWAVES;
-  static_assert(PER_WAVE * NWAVES * 1024 == BM * BK * 4, "whole 1 KB copies per wave");
+  static constexpr int PER_WAVE = R * BK * 4 / 1024 / NWAVES;
+  static_assert(PER_WAVE * NWAVES * 1024 == R * BK * 4, "whole 1 KB copies per wave");
   const char* tile;  // operand at this tile's first row (!TRANS) or column (TRANS), k = kbeg
   long long step;    // bytes between consecutive slabs
   long long remain;  // bytes from `tile` to the end of the operand
@@ -101,7 +105,7 @@ struct SlabCopy {
         const int row = b >> 6, p = (b >> 4) & 3;
         voff[j] = (uint32_t)(row * ld + 4 * (p ^ kswz(row))) * 4u;
       } else {
-        const int k = b >> 9, p = (b & 511) >> 4;
+        const int k = b / (4 * R), p = (b % (4 * R)) >> 4;
         voff[j] = (uint32_t)(k * ld + 4 * p) * 4u;
       }
     }
@@ -188,10 +192,10 @@ template <bool AT, bool BT, int EPI>
 __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   // one LDS object per pipeline stage, so the compiler can tell which copies a read waits
   // for (the third is a placeholder with two stages)
-  constexpr int S3 = NSTAGE > 2 ? BM * BK : 4;
+  constexpr int SA3 = NSTAGE > 2 ? BM * BK : 4, SB3 = NSTAGE > 2 ? BN * BK : 4;
   __shared__ __attribute__((aligned(1024))) float As0[BM * BK], As1[BM * BK];
   __shared__ __attribute__((aligned(1024))) float Bs0[BN * BK], Bs1[BN * BK];
-  __shared__ __attribute__((aligned(16))) float As2[S3], Bs2[S3];
+  __shared__ __attribute__((aligned(16))) float As2[SA3], Bs2[SB3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -216,6 +220,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   const int kend = min(g.K, kbeg + g.k_split);
   const int klen = kend > kbeg ? kend - kbeg : 0;
   const int nslabs = (klen + BK - 1) / BK;
+  static_assert(NTHREADS == 2 * BM, "column sums: two threads per m");
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -225,8 +230,8 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-  SlabCopy<AT> ca;
-  SlabCopy<BT> cb;
+  SlabCopy<AT, BM> ca;
+  SlabCopy<BT, BN> cb;
   ca.init(g.A + (AT ? (long long)kbeg * g.lda : kbeg), g.lda, m0,
           AT ? (long long)(g.K - kbeg) * g.lda : (long long)g.M * g.lda - kbeg, wave, lane);
   cb.init(g.B + (BT ? (long long)kbeg * g.ldb : kbeg), g.ldb, n0,
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
             acc[tm][tn] = mfma32x32x2(bfr[tn][e], af[tm][e], acc[tm][tn]);
     }
     if (do_colsum) {  // column m of the A tile ([k][m] in LDS), k-rows 8 half .. 8 half + 7
-      const int m = tid & (BM - 1), half = tid >> 7;
+      const int m = tid % BM, half = tid / BM;
 #pragma unroll
       for (int kk = 0; kk < BK / 2; kk++) csum += As[(half * (BK / 2) + kk) * BM + m];
     }
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   // loop is unrolled by NSTAGE so every LDS access names its stage statically, and every
   // step issues the same copies (empty ones past the last slab): the compiler's own waits
   // for the copies then follow them exactly.
-  constexpr int COPIES = SlabCopy<AT>::PER_WAVE + SlabCopy<BT>::PER_WAVE;
+  constexpr int COPIES = SlabCopy<AT, BM>::PER_WAVE + SlabCopy<BT, BN>::PER_WAVE;
   auto step = [&](int s, int kt) {  // s: a constant at every call
     // this wave's copies of slab kt have landed (those of the NSTAGE - 2 later slabs may not)
     wait_vmcnt<COPIES * (NSTAGE - 2)>();
@@ -515,11 +520,11 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   }
   // float4 operand loads: 16-byte aligned bases and leading dimensions that are multiples
   // of 4 (which also keeps the last float4 of a row inside the row's storage)
-  // (and leading dimensions below 2^23, so a slab's per-thread byte offsets fit 32 bits)
+  // (and leading dimensions below 2^22, so a slab's per-thread byte offsets fit 32 bits)
   const int a_cols = g.a_trans ? g.M : g.K, b_cols = g.b_trans ? g.N : g.K;
   if (!aligned16(g.A) || !aligned16(g.B) || !aligned16(g.C) || g.lda % 4 || g.ldb % 4 ||
-      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N || g.lda >= (1 << 23) ||
-      g.ldb >= (1 << 23)) {
+      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N || g.lda >= (1 << 22) ||
+      g.ldb >= (1 << 22)) {
     set_global_error("gemm: unsupported alignment or leading dimension (lda=%d ldb=%d ldc=%d)",
                      g.lda, g.ldb, g.ldc);
     return -1;
