@@ -31,14 +31,19 @@ namespace {
 #define GPT2_GEMM_BM 128
 #endif
 // BM x 128 tiles; waves of 64 x 64 (BM / 64 x 2 of them)
-constexpr int BM = GPT2_GEMM_BM, BN = 128, BK = 16;
+#ifndef GPT2_GEMM_BK
+#define GPT2_GEMM_BK 16
+#endif
+constexpr int BM = GPT2_GEMM_BM, BN = 128, BK = GPT2_GEMM_BK;
+static_assert(BK == 16 || BK == 32, "slab depth");
+constexpr int HALF = BK / 2;  // k per lane half in a slab
 constexpr int NTHREADS = 2 * BM, NWAVES = NTHREADS / 64;
 #ifndef GPT2_GEMM_STAGES
 #define GPT2_GEMM_STAGES 2
 #endif
 // LDS slabs per workgroup (16 KB each); four workgroups per CU with two, three with three
 constexpr int NSTAGE = GPT2_GEMM_STAGES;
-constexpr int OCC = (NSTAGE == 2 ? 4 : 3) * 128 / BM;
+constexpr int OCC = (NSTAGE == 2 ? 4 : 3) * 128 / BM * 16 / BK;
 static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
 
 struct Args {
@@ -68,12 +73,14 @@ GPT2_DEVICE_INLINE void copy_to_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-// LDS placement of an operand stored with K contiguous: [row][k], 64-byte rows of BK = 16 k;
-// the 16-byte chunk c of row r holds the row's chunk c ^ kswz(r), which spreads the 16-byte
-// fragment reads (32 consecutive rows, one chunk) over all banks. An operand stored
-// (K, rows) keeps that layout, [k][row] (512-byte k-rows), and is read 4 bytes per lane
-// from consecutive rows (no conflicts, no swizzle).
-GPT2_DEVICE_INLINE int kswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// LDS placement of an operand stored with K contiguous: [row][k], rows of BK k (64 or 128
+// bytes); the 16-byte chunk c of row r holds the row's chunk c ^ kswz(r), which spreads the
+// 16-byte fragment reads (32 consecutive rows, one chunk) over all banks. An operand stored
+// (K, rows) keeps that layout, [k][row], and is read 4 bytes per lane from consecutive rows
+// (no conflicts, no swizzle).
+GPT2_DEVICE_INLINE int kswz(int row) {
+  return BK == 16 ? ((row >> 1) ^ (row >> 3)) & 3 : (row ^ (row >> 3)) & 7;
+}
 
 // One operand's share of the slab pipeline: a slab (BK k x 128 rows, 8 KB) is copied from
 // global memory straight into LDS, 1 KB per wave-wide buffer load (lane l fills bytes
@@ -102,7 +109,7 @@ struct SlabCopy {
     for (int j = 0; j < PER_WAVE; j++) {
       const int b = (j * NWAVES + wave) * 1024 + 16 * lane;  // LDS byte within the slab
       if (!TRANS) {
-        const int row = b >> 6, p = (b >> 4) & 3;
+        const int row = b / (4 * BK), p = (b % (4 * BK)) >> 4;
         voff[j] = (uint32_t)(row * ld + 4 * (p ^ kswz(row))) * 4u;
       } else {
         const int k = b / (4 * R), p = (b % (4 * R)) >> 4;
@@ -184,7 +191,7 @@ GPT2_DEVICE_INLINE f32x4 kmask4(f32x4 v, int lim) {
   return v;
 }
 
-// K order of the products: at MFMA step s (0..7) of a slab, lane half h supplies k = 8h + s
+// K order of the products: at MFMA step s (0..BK/2-1) of a slab, lane half h supplies k = (BK/2) h + s
 // for both operands (each lane supplies one k per 32x32x2 MFMA; any bijection contracts the
 // same sum), so a lane's four consecutive k of a row stored with K contiguous are one
 // 16-byte LDS read feeding four MFMAs.
@@ -238,13 +245,14 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
           BT ? (long long)(g.K - kbeg) * g.ldb : (long long)g.N * g.ldb - kbeg, wave, lane);
 
   // per-lane fragment read offsets (bytes within a stage): K-contiguous operands, the chunk
-  // of k = 8h .. 8h + 3 (the next four k: offset ^ 16); (K, rows) operands, k-row 8h
+  // of k = HALF h .. HALF h + 3 (the j-th next four k: offset ^ 16 j); (K, rows) operands,
+  // k-row HALF h
   int rda[2], rdb[2];
 #pragma unroll
   for (int q = 0; q < 2; q++) {
     const int ra = wm0 + 32 * q + r, rb = wn0 + 32 * q + r;
-    rda[q] = AT ? (8 * h * BM + ra) * 4 : ra * 64 + 16 * ((2 * h) ^ kswz(ra));
-    rdb[q] = BT ? (8 * h * BN + rb) * 4 : rb * 64 + 16 * ((2 * h) ^ kswz(rb));
+    rda[q] = AT ? (HALF * h * BM + ra) * 4 : ra * 4 * BK + 16 * (((HALF / 4) * h) ^ kswz(ra));
+    rdb[q] = BT ? (HALF * h * BN + rb) * 4 : rb * 4 * BK + 16 * (((HALF / 4) * h) ^ kswz(rb));
   }
 
   auto stage_a = [&](int s) -> float* { return s == 0 ? As0 : s == 1 ? As1 : As2; };
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
     const int k0 = kbeg + kt * BK;
     const bool tail = k0 + BK > kend;  // uniform
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < HALF / 4; j++) {
       f32x4 af[2], bfr[2];
 #pragma unroll
       for (int q = 0; q < 2; q++) {
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
         bfr[q] = frag(pb, rdb[q], j, BT, BN);
       }
       if (tail) {
-        const int lim = kend - (k0 + 8 * h + 4 * j);
+        const int lim = kend - (k0 + HALF * h + 4 * j);
 #pragma unroll
         for (int q = 0; q < 2; q++) {
           af[q] = kmask4(af[q], lim);
