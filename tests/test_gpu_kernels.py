@@ -36,6 +36,7 @@ def rng(seed):
 
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("N,C,OC,ld", [(300, 96, 200, 200), (64, 16, 48, 48), (130, 772, 130, 132),
+                                       (130, 772, 130, 130),  # rows 8-byte aligned: scalar epilogue
                                        (64, 768, 50257, 50304), (1024, 768, 2304, 2304)])
 @pytest.mark.parametrize("epi", [0, 1, 2])
 def test_matmul_forward(N, C, OC, ld, epi):
