@@ -1,4 +1,4 @@
-// gemm.hip -- fp32 GEMMs of the training step on gfx950 MFMA (v_mfma_f32_32x32x2_f32).
+// gemm.hip -- fp32 GEMMs of the training step on gfx950 MFMA.
 //
 // Every linear layer of "llm.c 的中文注解-20240421" (section 1.5 matmul_forward,
 // section 1.6 matmul_backward) is one of three storage patterns of C = A . B:
@@ -8,15 +8,23 @@
 // with fused epilogues: bias, bias+GELU (section 1.9), bias+residual (section 1.11),
 // accumulate, and the GELU backward (section 1.10).
 //
-// Tiling: a 256-thread workgroup owns a 128x128 tile of C; its four waves own 64x64
-// sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances in slabs of 16 that go from global
-// memory straight into LDS (buffer loads with the LDS as destination, no staging registers),
-// the next slab in flight while the current one is used, one LDS object per stage. An
-// operand stored with K contiguous is kept [row][k] in LDS and read 16 bytes (four k) per
-// lane, feeding four MFMAs: the products take the K order in which lane half h supplies
-// k = 8h + s at step s. An operand stored (K, rows) is kept as stored, [k][row], and read 4
-// bytes per lane. The MFMA takes the B fragment as its first operand, so a lane ends up
-// holding runs of 4 consecutive output columns of one row: the epilogue works on float4s.
+// Two kernels compute them, with the same epilogues and split-K planning:
+// - gemm_x6_kernel (used by default): fp32 operands and fp32 accumulation, the products
+//   formed on bf16 MFMA (v_mfma_f32_32x32x16_bf16) from an exact three-way bf16 split of each
+//   operand value, six partial products per fp32 product, which keeps each product within
+//   2^-23 of its exact value (fp32 accuracy) at 16/6 times the fp32 MFMA rate. 256x256 tiles;
+//   each slab of 16 k is loaded through registers, split once per workgroup and written to
+//   LDS as three bf16 planes per operand.
+// - gemm_kernel: fp32 MFMA (v_mfma_f32_32x32x2_f32). A 256-thread workgroup owns a 128x128
+//   tile of C; its four waves own 64x64 sub-tiles, i.e. 2x2 MFMA blocks of 32x32. K advances
+//   in slabs of 16 that go from global memory straight into LDS (buffer loads with the LDS as
+//   destination, no staging registers), the next slab in flight while the current one is
+//   used, one LDS object per stage. An operand stored with K contiguous is kept [row][k] in
+//   LDS and read 16 bytes (four k) per lane, feeding four MFMAs: the products take the K
+//   order in which lane half h supplies k = 8h + s at step s. An operand stored (K, rows) is
+//   kept as stored, [k][row], and read 4 bytes per lane.
+// In both the MFMA takes the B fragment as its first operand, so a lane ends up holding runs
+// of 4 consecutive output columns of one row: the epilogue works on float4s.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -27,25 +35,54 @@
 namespace gpt2 {
 namespace {
 
-#ifndef GPT2_GEMM_BM
-#define GPT2_GEMM_BM 128
-#endif
-// BM x 128 tiles; waves of 64 x 64 (BM / 64 x 2 of them)
+// Slab depth (build option): K advances BK at a time through LDS.
 #ifndef GPT2_GEMM_BK
 #define GPT2_GEMM_BK 16
 #endif
-constexpr int BM = GPT2_GEMM_BM, BN = 128, BK = GPT2_GEMM_BK;
+constexpr int BK = GPT2_GEMM_BK;
 static_assert(BK == 16 || BK == 32, "slab depth");
 constexpr int HALF = BK / 2;  // k per lane half in a slab
-constexpr int NTHREADS = 2 * BM, NWAVES = NTHREADS / 64;
+
+// Shape of one GEMM kernel: a workgroup owns BM x BN outputs; WAVES_M x WAVES_N waves own
+// (BM / WAVES_M) x (BN / WAVES_N) each, i.e. TM x TN MFMA blocks of 32x32; at least OCC
+// waves per SIMD (the register budget). X6 false: fp32 MFMA products, NSTAGE fp32 slabs in
+// LDS. X6 true: split-operand bf16 MFMA products (see gemm_x6s_body), two LDS buffers of
+// three bf16 planes per operand (NSTAGE must be 2). WG_PER_CU workgroups fit on a CU; RATE
+// is the throughput (flop/s) the split planner assumes for the kernel.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_, int OCC_, bool X6_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N, NTHREADS = 64 * NWAVES;
+  static constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;
+  static constexpr int NSTAGE = NSTAGE_, OCC = OCC_;
+  static constexpr bool X6 = X6_;
+  static constexpr int LDS_BYTES = X6 ? 2 * 3 * (BM + BN) * BK * 2 : NSTAGE * (BM + BN) * BK * 4;
+  static constexpr int WG_PER_CU = (OCC * 4 / NWAVES) < (160 * 1024 / LDS_BYTES)
+                                       ? OCC * 4 / NWAVES : 160 * 1024 / LDS_BYTES;
+  static constexpr double RATE = X6 ? 0.4 * 2.5e15 / 6 : 0.9 * 157.3e12;
+  static_assert(TM * WAVES_M * 32 == BM && TN * WAVES_N * 32 == BN, "whole MFMA blocks");
+  static_assert(NSTAGE == 2 || (NSTAGE == 3 && !X6), "two or three LDS stages");
+  static_assert(NTHREADS == BM || NTHREADS == 2 * BM, "column sums: one or two threads per m");
+  static_assert(WG_PER_CU >= 1, "fits a CU");
+};
+
+// fp32 MFMA kernel: BM x 128 tiles (BM a build option), waves of 64 x 64, two LDS stages
+// (16 KB each at BM 128) and four workgroups per CU, or three stages and three.
+#ifndef GPT2_GEMM_BM
+#define GPT2_GEMM_BM 128
+#endif
 #ifndef GPT2_GEMM_STAGES
 #define GPT2_GEMM_STAGES 2
 #endif
-// LDS slabs per workgroup (16 KB each); four workgroups per CU with two, three with three
-constexpr int NSTAGE = GPT2_GEMM_STAGES;
-constexpr int OCC = (NSTAGE == 2 ? 4 : 3) * 128 / BM * 16 / BK;
-static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
-
+typedef Cfg<GPT2_GEMM_BM, 128, GPT2_GEMM_BM / 64, 2, GPT2_GEMM_STAGES,
+            (GPT2_GEMM_STAGES == 2 ? 4 : 3) * 128 / GPT2_GEMM_BM * 16 / BK, false>
+    CfgF32;
+// split-operand kernel (shape a build option): 256 x 256 tiles, eight waves of 128 x 64,
+// 96 KB of LDS, one workgroup per CU (two waves per SIMD)
+#ifndef GPT2_GEMM_X6_SHAPE
+#define GPT2_GEMM_X6_SHAPE 256, 256, 2, 4, 2, 2
+#endif
+typedef Cfg<GPT2_GEMM_X6_SHAPE, true> CfgX6;
 struct Args {
   const float* A;
   const float* B;
@@ -82,15 +119,15 @@ GPT2_DEVICE_INLINE int kswz(int row) {
   return BK == 16 ? ((row >> 1) ^ (row >> 3)) & 3 : (row ^ (row >> 3)) & 7;
 }
 
-// One operand's share of the slab pipeline: a slab (BK k x 128 rows, 8 KB) is copied from
-// global memory straight into LDS, 1 KB per wave-wide buffer load (lane l fills bytes
-// 16 l .. 16 l + 15 of the KB), without passing through registers; two copies per wave. The
+// One operand's share of the slab pipeline: a slab (BK k x R rows) is copied from global
+// memory straight into LDS, 1 KB per wave-wide buffer load (lane l fills bytes
+// 16 l .. 16 l + 15 of the KB), without passing through registers, shared among NWAVES. The
 // buffer resource of a slab ends where the operand ends, so rows past its last row (and,
 // for an operand stored (K, rows), k past K) read as zero; a K tail inside a row is masked
 // in the fragments. The extent is clamped to 32 bits: only a slab whose extent is small
 // (the last rows or the last k) ever reaches past the operand. Per-lane byte offsets are
 // computed once; the host keeps them below 2^32.
-template <bool TRANS, int R>
+template <bool TRANS, int R, int NWAVES>
 struct SlabCopy {
   static constexpr int PER_WAVE = R * BK * 4 / 1024 / NWAVES;
   static_assert(PER_WAVE * NWAVES * 1024 == R * BK * 4, "whole 1 KB copies per wave");
@@ -191,18 +228,20 @@ GPT2_DEVICE_INLINE f32x4 kmask4(f32x4 v, int lim) {
   return v;
 }
 
-// K order of the products: at MFMA step s (0..BK/2-1) of a slab, lane half h supplies k = (BK/2) h + s
-// for both operands (each lane supplies one k per 32x32x2 MFMA; any bijection contracts the
-// same sum), so a lane's four consecutive k of a row stored with K contiguous are one
-// 16-byte LDS read feeding four MFMAs.
-template <bool AT, bool BT, int EPI>
-__global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
+// fp32 MFMA kernel body. K order of the products: at MFMA step s (0..BK/2-1) of a slab, lane
+// half h supplies k = (BK/2) h + s for both operands (each lane supplies one k per 32x32x2
+// MFMA; any bijection contracts the same sum), so a lane's four consecutive k of a row
+// stored with K contiguous are one 16-byte LDS read feeding four MFMAs.
+template <class CFG, bool AT, bool BT, int EPI>
+__device__ __forceinline__ void gemm_body(const Args& g) {
+  constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
+  constexpr int NSTAGE = CFG::NSTAGE, NWAVES = CFG::NWAVES;
   // one LDS object per pipeline stage, so the compiler can tell which copies a read waits
   // for (the third is a placeholder with two stages)
   constexpr int SA3 = NSTAGE > 2 ? BM * BK : 4, SB3 = NSTAGE > 2 ? BN * BK : 4;
   __shared__ __attribute__((aligned(1024))) float As0[BM * BK], As1[BM * BK];
   __shared__ __attribute__((aligned(1024))) float Bs0[BN * BK], Bs1[BN * BK];
-  __shared__ __attribute__((aligned(16))) float As2[SA3], Bs2[SB3];
+  __shared__ __attribute__((aligned(1024))) float As2[SA3], Bs2[SB3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -219,7 +258,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   const int tin = t - group * GROUP_M * nN;
   const int mt = first_m + tin % gsz, nt = tin / gsz;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int wm0 = (wave >> 1) * 64, wn0 = (wave & 1) * 64;
+  const int wm0 = (wave / CFG::WAVES_N) * (32 * TM), wn0 = (wave % CFG::WAVES_N) * (32 * TN);
   const bool do_colsum = AT && g.colsum != nullptr && nt == 0;  // uniform per workgroup
   float csum = 0.f;
 
@@ -227,18 +266,17 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   const int kend = min(g.K, kbeg + g.k_split);
   const int klen = kend > kbeg ? kend - kbeg : 0;
   const int nslabs = (klen + BK - 1) / BK;
-  static_assert(NTHREADS == 2 * BM, "column sums: two threads per m");
 
-  f32x16 acc[2][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int a = 0; a < 2; a++)
+  for (int a = 0; a < TM; a++)
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int b = 0; b < TN; b++)
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-  SlabCopy<AT, BM> ca;
-  SlabCopy<BT, BN> cb;
+  SlabCopy<AT, BM, NWAVES> ca;
+  SlabCopy<BT, BN, NWAVES> cb;
   ca.init(g.A + (AT ? (long long)kbeg * g.lda : kbeg), g.lda, m0,
           AT ? (long long)(g.K - kbeg) * g.lda : (long long)g.M * g.lda - kbeg, wave, lane);
   cb.init(g.B + (BT ? (long long)kbeg * g.ldb : kbeg), g.ldb, n0,
@@ -247,11 +285,15 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   // per-lane fragment read offsets (bytes within a stage): K-contiguous operands, the chunk
   // of k = HALF h .. HALF h + 3 (the j-th next four k: offset ^ 16 j); (K, rows) operands,
   // k-row HALF h
-  int rda[2], rdb[2];
+  int rda[TM], rdb[TN];
 #pragma unroll
-  for (int q = 0; q < 2; q++) {
-    const int ra = wm0 + 32 * q + r, rb = wn0 + 32 * q + r;
+  for (int q = 0; q < TM; q++) {
+    const int ra = wm0 + 32 * q + r;
     rda[q] = AT ? (HALF * h * BM + ra) * 4 : ra * 4 * BK + 16 * (((HALF / 4) * h) ^ kswz(ra));
+  }
+#pragma unroll
+  for (int q = 0; q < TN; q++) {
+    const int rb = wn0 + 32 * q + r;
     rdb[q] = BT ? (HALF * h * BN + rb) * 4 : rb * 4 * BK + 16 * (((HALF / 4) * h) ^ kswz(rb));
   }
 
@@ -274,41 +316,43 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
     const char* pb = reinterpret_cast<const char*>(Bs);
     const int k0 = kbeg + kt * BK;
     const bool tail = k0 + BK > kend;  // uniform
+    f32x4 af[HALF / 4][TM], bfr[HALF / 4][TN];
 #pragma unroll
     for (int j = 0; j < HALF / 4; j++) {
-      f32x4 af[2], bfr[2];
 #pragma unroll
-      for (int q = 0; q < 2; q++) {
-        af[q] = frag(pa, rda[q], j, AT, BM);
-        bfr[q] = frag(pb, rdb[q], j, BT, BN);
-      }
+      for (int q = 0; q < TM; q++) af[j][q] = frag(pa, rda[q], j, AT, BM);
+#pragma unroll
+      for (int q = 0; q < TN; q++) bfr[j][q] = frag(pb, rdb[q], j, BT, BN);
       if (tail) {
         const int lim = kend - (k0 + HALF * h + 4 * j);
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
-          af[q] = kmask4(af[q], lim);
-          bfr[q] = kmask4(bfr[q], lim);
-        }
+        for (int q = 0; q < TM; q++) af[j][q] = kmask4(af[j][q], lim);
+#pragma unroll
+        for (int q = 0; q < TN; q++) bfr[j][q] = kmask4(bfr[j][q], lim);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < HALF / 4; j++)
 #pragma unroll
       for (int e = 0; e < 4; e++)
 #pragma unroll
-        for (int tm = 0; tm < 2; tm++)
+        for (int tm = 0; tm < TM; tm++)
 #pragma unroll
-          for (int tn = 0; tn < 2; tn++)
-            acc[tm][tn] = mfma32x32x2(bfr[tn][e], af[tm][e], acc[tm][tn]);
-    }
-    if (do_colsum) {  // column m of the A tile ([k][m] in LDS), k-rows 8 half .. 8 half + 7
-      const int m = tid % BM, half = tid / BM;
+          for (int tn = 0; tn < TN; tn++)
+            acc[tm][tn] = mfma32x32x2(bfr[j][tn][e], af[j][tm][e], acc[tm][tn]);
+    if (do_colsum) {  // column m of the A tile ([k][m] in LDS): this thread's share of k
+      constexpr int KP = BK * BM / CFG::NTHREADS;
+      const int m = tid % BM, part = tid / BM;
 #pragma unroll
-      for (int kk = 0; kk < BK / 2; kk++) csum += As[(half * (BK / 2) + kk) * BM + m];
+      for (int kk = 0; kk < KP; kk++) csum += As[(part * KP + kk) * BM + m];
     }
   };
   // Stage of slab kt: kt % NSTAGE; slab kt + NSTAGE - 1 is issued while slab kt is used. The
   // loop is unrolled by NSTAGE so every LDS access names its stage statically, and every
   // step issues the same copies (empty ones past the last slab): the compiler's own waits
   // for the copies then follow them exactly.
-  constexpr int COPIES = SlabCopy<AT, BM>::PER_WAVE + SlabCopy<BT, BN>::PER_WAVE;
+  constexpr int COPIES =
+      SlabCopy<AT, BM, NWAVES>::PER_WAVE + SlabCopy<BT, BN, NWAVES>::PER_WAVE;
   auto step = [&](int s, int kt) {  // s: a constant at every call
     // this wave's copies of slab kt have landed (those of the NSTAGE - 2 later slabs may not)
     wait_vmcnt<COPIES * (NSTAGE - 2)>();
@@ -332,11 +376,13 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
 
   if (do_colsum) {
     float* red = As0;
-    lds_barrier();
-    if (tid >= BM) red[tid - BM] = csum;
-    __syncthreads();
+    if (CFG::NTHREADS == 2 * BM) {  // the second thread of each m hands its share over
+      lds_barrier();
+      if (tid >= BM) red[tid - BM] = csum;
+      __syncthreads();
+    }
     if (tid < BM && m0 + tid < g.M) {
-      const float total = csum + red[tid];
+      const float total = CFG::NTHREADS == 2 * BM ? csum + red[tid] : csum;
       if (g.colsum_zstride) g.colsum[(long long)z * g.colsum_zstride + m0 + tid] = total;
       else g.colsum[m0 + tid] += total;
     }
@@ -345,11 +391,11 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
   float* C = g.C + (long long)z * g.c_zstride;
   // acc[tm][tn][4q + j]: row m = m0 + wm0 + 32 tm + r, column n = n0 + wn0 + 32 tn + 8q + 4h + j
 #pragma unroll
-  for (int tm = 0; tm < 2; tm++) {
+  for (int tm = 0; tm < TM; tm++) {
     const int m = m0 + wm0 + 32 * tm + r;
     if (m >= g.M) continue;
 #pragma unroll
-    for (int tn = 0; tn < 2; tn++)
+    for (int tn = 0; tn < TN; tn++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
@@ -360,6 +406,331 @@ __global__ __launch_bounds__(NTHREADS, OCC) void gemm_kernel(Args g) {
       }
   }
 }
+
+// ---- split-operand kernel ----------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One wave64 bf16 MFMA: acc(32x32) += A(32x16) * B(16x32), fp32 accumulation. Lane l
+// supplies A[l % 32][8 (l / 32) .. + 7] and B[8 (l / 32) .. + 7][l % 32]; the result layout
+// is that of mfma32x32x2.
+GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+// Exact split of fp32 values into three bf16 parts, x = hi + mid + lo: hi is x rounded to
+// bf16 (8 significand bits), mid the remainder x - hi rounded to bf16, lo what remains.
+// x - hi is exact in fp32 (hi is within a factor 2 of x) and, being a multiple of the last
+// significand bit of x below 2^-8 |x|, has at most 16 significant bits; after mid at most 8
+// are left, so lo is that remainder exactly (down to |x| ~ 2^-110, where lo leaves the
+// normal bf16 range). |mid| <= 2^-8 |x| and |lo| <= 2^-16 |x|.
+GPT2_DEVICE_INLINE uint32_t bf16_pair(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+GPT2_DEVICE_INLINE void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_pair(x0, x1);
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+  mid = bf16_pair(r0, r1);
+  const float s0 = r0 - __uint_as_float(mid << 16), s1 = r1 - __uint_as_float(mid & 0xFFFF0000u);
+  lo = bf16_pair(s0, s1);
+}
+// the eight k of a lane's fragment (two float4s) as the three bf16x8 operands
+GPT2_DEVICE_INLINE void split3(f32x4 x, f32x4 y, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  uint32_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
+  split2(x[0], x[1], h0, m0, l0);
+  split2(x[2], x[3], h1, m1, l1);
+  split2(y[0], y[1], h2, m2, l2);
+  split2(y[2], y[3], h3, m3, l3);
+  hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+  mid = __builtin_bit_cast(bf16x8, u32x4{m0, m1, m2, m3});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
+}
+
+// Products: with a = ah + am + al and b = bh + bm + bl as above,
+// a b = ah bh + (ah bm + am bh) + (ah bl + al bh + am bm) + (am bl + al bm) + al bl; the six
+// terms of the first three groups are formed on bf16 MFMA (each exact, 8 x 8 significand
+// bits, accumulated in fp32) and the last three dropped, which changes a b by at most
+// 2^-23 |a b|, the size of one or two fp32 roundings of the product. The fp32 accumulation
+// of the K-term sum then dominates the error, as it does with fp32 products. The MFMA's 16-k
+// step takes, in lane half h, the k 8h .. 8h + 7 of a 16-k slab.
+//
+// The workgroup stages each slab through registers: every thread loads 8 consecutive fp32
+// values of each operand (two 16-byte buffer loads; rows or k past the operand's end read
+// as zero), splits them into their bf16 parts and writes the three parts to three LDS
+// planes, so each value is split once rather than once per wave that reads it. Planes are
+// double-buffered (slab kt + 1 is written while slab kt is read) with one barrier per slab,
+// and the global loads of slab kt + 3 are in flight during the products of slabs kt + 1 and
+// kt + 2 (two register sets).
+// Plane layouts (bf16): an operand stored with K contiguous as [row][16 k], 32-byte rows,
+// chunk c (8 k) of row r at chunk c ^ ((r >> 3) & 1), so the 16-byte fragment reads of 32
+// consecutive rows cover all banks; an operand stored (K, rows) as [k][row], chunk c (8 rows)
+// of k-row k at chunk c ^ rswz(k % 4), read with transposing reads.
+GPT2_DEVICE_INLINE int rswz(int j) { return (0xAC60 >> (4 * j)) & 15; }  // 0, 6, 12, 10
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Fragment of an operand stored (K, rows): two transposing 8-byte reads
+// (ds_read_b64_tr_b16). In each 16-lane group, lane i receives column i of the 4 x 16 block
+// whose k-row j is read by lanes 4j .. 4j + 3 (4 columns each).
+GPT2_DEVICE_INLINE bf16x8 frag_tr(const char* p, int kstride4) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + kstride4));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One operand's staging: thread t holds 8 values, for an operand stored with K contiguous
+// row t / 2 at k 8 (t % 2) .. + 7 of the slab, for one stored (K, rows) k-row t / (R / 8) at
+// rows 8 (t % (R / 8)) .. + 7. The buffer resource of a slab ends where the operand ends.
+template <bool TRANS, int R>
+struct StageX6 {
+  static constexpr int CPR = R / 8;  // 8-row chunks per k-row (TRANS)
+  const char* tile;                  // operand at this tile's first row / column, k = kbeg
+  long long step;                    // bytes between consecutive slabs
+  long long remain;                  // bytes from `tile` to the end of the operand
+  uint32_t voff;                     // this thread's byte offset within a slab
+  int kofs;                          // k (first k) of this thread's values within a slab
+  int lds_off;                       // byte offset of its 16-byte chunk within a plane
+
+  __device__ __forceinline__ void init(const float* P, int ld, int row0, long long total,
+                                       int tid) {
+    const long long at = TRANS ? (long long)row0 : (long long)row0 * ld;
+    tile = reinterpret_cast<const char*>(P + at);
+    remain = 4 * (total - at);
+    step = TRANS ? 4LL * BK * ld : 4LL * BK;
+    if (!TRANS) {
+      const int row = tid >> 1, c = tid & 1;
+      voff = (uint32_t)(row * ld + 8 * c) * 4u;
+      kofs = 8 * c;
+      lds_off = row * 2 * BK + 16 * (c ^ ((row >> 3) & 1));
+    } else {
+      const int kk = tid / CPR, c = tid % CPR;
+      voff = (uint32_t)(kk * ld + 8 * c) * 4u;
+      kofs = kk;
+      lds_off = kk * 2 * R + 16 * (c ^ rswz(kk & 3));
+    }
+  }
+  __device__ __forceinline__ void load(int kt, f32x4* v) const {
+    const long long off = (long long)kt * step;
+    const long long left = remain - off;
+    const int nrec = (int)(uint32_t)(left > 0xFFFFFFFFLL ? 0xFFFFFFFFLL : left > 0 ? left : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tile + off), (short)0, nrec, kBufferFlags);
+    v[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+    v[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, 0, 0));
+  }
+  // mask k at or past kend (k0: first k of the slab), add the values to cs (column sums of
+  // an operand stored (K, rows)), split, and write the three parts
+  template <bool COLSUM>
+  __device__ __forceinline__ void store(const f32x4* v, char* planes, int k0, int kend,
+                                        float* cs) const {
+    constexpr int PLANE = R * BK * 2;
+    f32x4 a = v[0], b = v[1];
+    if (!TRANS) {
+      const int lim = kend - (k0 + kofs);
+      a = kmask4(a, lim);
+      b = kmask4(b, lim - 4);
+    } else if (k0 + kofs >= kend) {
+      a = f32x4{0.f, 0.f, 0.f, 0.f};
+      b = a;
+    }
+    if (COLSUM) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        cs[e] += a[e];
+        cs[4 + e] += b[e];
+      }
+    }
+    bf16x8 hi, mid, lo;
+    split3(a, b, hi, mid, lo);
+    *reinterpret_cast<bf16x8*>(planes + lds_off) = hi;
+    *reinterpret_cast<bf16x8*>(planes + PLANE + lds_off) = mid;
+    *reinterpret_cast<bf16x8*>(planes + 2 * PLANE + lds_off) = lo;
+  }
+};
+
+template <class CFG, bool AT, bool BT, int EPI>
+__device__ __forceinline__ void gemm_x6s_body(const Args& g) {
+  constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
+  constexpr int NT = CFG::NTHREADS;
+  static_assert(BK == 16, "one bf16 MFMA step per slab");
+  static_assert(BM * BK == 8 * NT && BN * BK == 8 * NT, "eight values of each operand per thread");
+  constexpr int PA = BM * BK * 2, PB = BN * BK * 2;  // bytes of one plane
+  constexpr int BUF = 3 * (PA + PB);
+  __shared__ __attribute__((aligned(1024))) char lds[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int nM = (g.M + BM - 1) / BM, nN = (g.N + BN - 1) / BN;
+  const int tiles = nM * nN;
+  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int z = lid / tiles;
+  const int t = lid - z * tiles;
+  const int group = t / (GROUP_M * nN);
+  const int first_m = group * GROUP_M;
+  const int gsz = min(nM - first_m, GROUP_M);
+  const int tin = t - group * GROUP_M * nN;
+  const int mt = first_m + tin % gsz, nt = tin / gsz;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wm0 = (wave / CFG::WAVES_N) * (32 * TM), wn0 = (wave % CFG::WAVES_N) * (32 * TN);
+  const bool do_colsum = AT && g.colsum != nullptr && nt == 0;  // uniform per workgroup
+
+  const int kbeg = z * g.k_split;
+  const int kend = min(g.K, kbeg + g.k_split);
+  const int klen = kend > kbeg ? kend - kbeg : 0;
+  const int nslabs = (klen + BK - 1) / BK;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; a++)
+#pragma unroll
+    for (int b = 0; b < TN; b++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+  StageX6<AT, BM> sa;
+  StageX6<BT, BN> sb;
+  sa.init(g.A + (AT ? (long long)kbeg * g.lda : kbeg), g.lda, m0,
+          AT ? (long long)(g.K - kbeg) * g.lda : (long long)g.M * g.lda - kbeg, tid);
+  sb.init(g.B + (BT ? (long long)kbeg * g.ldb : kbeg), g.ldb, n0,
+          BT ? (long long)(g.K - kbeg) * g.ldb : (long long)g.N * g.ldb - kbeg, tid);
+
+  // per-lane fragment read offsets within a plane
+  const int g16 = lane >> 4, i16 = lane & 15;
+  int rda[TM], rdb[TN];
+#pragma unroll
+  for (int q = 0; q < TM; q++) {
+    const int row = wm0 + 32 * q + r;
+    const int n = wm0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
+    rda[q] = !AT ? row * 2 * BK + 16 * (h ^ ((row >> 3) & 1))
+                 : (8 * h + (i16 >> 2)) * 2 * BM + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
+  }
+#pragma unroll
+  for (int q = 0; q < TN; q++) {
+    const int row = wn0 + 32 * q + r;
+    const int n = wn0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
+    rdb[q] = !BT ? row * 2 * BK + 16 * (h ^ ((row >> 3) & 1))
+                 : (8 * h + (i16 >> 2)) * 2 * BN + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
+  }
+  auto fa = [&](const char* pl, int q) -> bf16x8 {
+    if (!AT) return *reinterpret_cast<const bf16x8*>(pl + rda[q]);
+    return frag_tr(pl + rda[q], 4 * 2 * BM);
+  };
+  auto fb = [&](const char* pl, int q) -> bf16x8 {
+    if (!BT) return *reinterpret_cast<const bf16x8*>(pl + rdb[q]);
+    return frag_tr(pl + rdb[q], 4 * 2 * BN);
+  };
+  f32x4 va[2][2], vb[2][2];  // two register sets of staged values
+  auto load = [&](int kt, int set) {
+    sa.load(kt, va[set]);
+    sb.load(kt, vb[set]);
+  };
+  auto stage = [&](int set, char* buf, int kt) {
+    const int k0 = kbeg + kt * BK;
+    if (do_colsum) sa.template store<true>(va[set], buf, k0, kend, cs);
+    else sa.template store<false>(va[set], buf, k0, kend, cs);
+    sb.template store<false>(vb[set], buf + 3 * PA, k0, kend, cs);
+  };
+  auto compute = [&](const char* buf) {
+    const char* pa = buf;
+    const char* pb = buf + 3 * PA;
+    bf16x8 bh[TN], bm[TN], bl[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++) {
+      bh[tn] = fb(pb, tn);
+      bm[tn] = fb(pb + PB, tn);
+      bl[tn] = fb(pb + 2 * PB, tn);
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) {
+      const bf16x8 ah = fa(pa, tm), am = fa(pa + PA, tm), al = fa(pa + 2 * PA, tm);
+      // the B fragment is the MFMA's first operand (a lane then holds runs of 4
+      // consecutive output columns); the smaller terms go first
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) acc[tm][tn] = mfma_bf16(bm[tn], am, acc[tm][tn]);
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) acc[tm][tn] = mfma_bf16(bl[tn], ah, acc[tm][tn]);
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) acc[tm][tn] = mfma_bf16(bh[tn], al, acc[tm][tn]);
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) acc[tm][tn] = mfma_bf16(bm[tn], ah, acc[tm][tn]);
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) acc[tm][tn] = mfma_bf16(bh[tn], am, acc[tm][tn]);
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) acc[tm][tn] = mfma_bf16(bh[tn], ah, acc[tm][tn]);
+    }
+  };
+
+  // Slab kt is read from plane buffer kt % 2; its values arrive in register set kt % 2. The
+  // loop is unrolled by two so that both name their buffer and set statically.
+  char* const buf0 = lds;
+  char* const buf1 = lds + BUF;
+  if (nslabs > 0) {
+    load(0, 0);
+    if (nslabs > 1) load(1, 1);
+    stage(0, buf0, 0);
+    if (nslabs > 2) load(2, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= nslabs; kt += 2) {
+      compute(buf0);  // slab kt
+      if (kt + 1 < nslabs) stage(1, buf1, kt + 1);
+      __syncthreads();  // slab kt + 1 is written; every wave is done with slab kt
+      if (kt + 3 < nslabs) load(kt + 3, 1);
+      compute(buf1);  // slab kt + 1
+      if (kt + 2 < nslabs) stage(0, buf0, kt + 2);
+      __syncthreads();
+      if (kt + 4 < nslabs) load(kt + 4, 0);
+    }
+    if (kt < nslabs) compute(buf0);  // an odd last slab
+  }
+
+  if (do_colsum) {  // the 16 k-row partial sums of each m, added in k-row order
+    float* red = reinterpret_cast<float*>(lds);
+    constexpr int CPR = BM / 8;
+    const int kk = tid / CPR, c = tid % CPR;
+    __syncthreads();  // every wave is done reading the planes (an odd last slab has no barrier)
+#pragma unroll
+    for (int e = 0; e < 8; e++) red[kk * BM + 8 * c + e] = cs[e];
+    __syncthreads();
+    if (tid < BM && m0 + tid < g.M) {
+      float total = 0.f;
+      for (int j = 0; j < NT / CPR; j++) total += red[j * BM + tid];
+      if (g.colsum_zstride) g.colsum[(long long)z * g.colsum_zstride + m0 + tid] = total;
+      else g.colsum[m0 + tid] += total;
+    }
+  }
+
+  float* C = g.C + (long long)z * g.c_zstride;
+#pragma unroll
+  for (int tm = 0; tm < TM; tm++) {
+    const int m = m0 + wm0 + 32 * tm + r;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
+        if (n >= g.N) continue;
+        epilogue4<EPI>(g, C, m, n,
+                       f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                             acc[tm][tn][4 * q + 3]});
+      }
+  }
+}
+
+// the two GEMM kernels: fp32 MFMA products, and split-operand bf16 MFMA products
+template <bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(CfgF32::NTHREADS, CfgF32::OCC) void gemm_kernel(Args g) {
+  gemm_body<CfgF32, AT, BT, EPI>(g);
+}
+template <bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(CfgX6::NTHREADS, CfgX6::OCC) void gemm_x6_kernel(Args g) {
+  gemm_x6s_body<CfgX6, AT, BT, EPI>(g);
+}
+
 
 // The epilogue `EPI` of one output element of a split-K GEMM (only EPI_STORE-with-bias,
 // EPI_ACCUM and EPI_GELU_BWD are used with splits) applied to the sum s of its partials.
@@ -453,48 +824,72 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Args g, const float* 
   }
 }
 
+template <bool AT, bool BT, int EPI>
+void launch_e(const Args& a, bool x6, dim3 grid, hipStream_t s) {
+  if (x6) gemm_x6_kernel<AT, BT, EPI><<<grid, CfgX6::NTHREADS, 0, s>>>(a);
+  else gemm_kernel<AT, BT, EPI><<<grid, CfgF32::NTHREADS, 0, s>>>(a);
+}
+
 template <bool AT, bool BT>
-void launch_tn(const Args& a, int epi, dim3 grid, hipStream_t s) {
+void launch_tn(const Args& a, bool x6, int epi, dim3 grid, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: gemm_kernel<AT, BT, EPI_STORE><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_GELU: gemm_kernel<AT, BT, EPI_GELU><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_RESID: gemm_kernel<AT, BT, EPI_RESID><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_ACCUM: gemm_kernel<AT, BT, EPI_ACCUM><<<grid, NTHREADS, 0, s>>>(a); break;
-    case EPI_GELU_BWD: gemm_kernel<AT, BT, EPI_GELU_BWD><<<grid, NTHREADS, 0, s>>>(a); break;
+    case EPI_STORE: launch_e<AT, BT, EPI_STORE>(a, x6, grid, s); break;
+    case EPI_GELU: launch_e<AT, BT, EPI_GELU>(a, x6, grid, s); break;
+    case EPI_RESID: launch_e<AT, BT, EPI_RESID>(a, x6, grid, s); break;
+    case EPI_ACCUM: launch_e<AT, BT, EPI_ACCUM>(a, x6, grid, s); break;
+    case EPI_GELU_BWD: launch_e<AT, BT, EPI_GELU_BWD>(a, x6, grid, s); break;
   }
 }
 
-void launch(const Args& a, bool at, bool bt, int epi, dim3 grid, hipStream_t s) {
-  if (!at && !bt) launch_tn<false, false>(a, epi, grid, s);
-  else if (!at && bt) launch_tn<false, true>(a, epi, grid, s);
-  else if (at && bt) launch_tn<true, true>(a, epi, grid, s);
-  else launch_tn<true, false>(a, epi, grid, s);
+void launch(const Args& a, bool x6, bool at, bool bt, int epi, dim3 grid, hipStream_t s) {
+  if (!at && !bt) launch_tn<false, false>(a, x6, epi, grid, s);
+  else if (!at && bt) launch_tn<false, true>(a, x6, epi, grid, s);
+  else if (at && bt) launch_tn<true, true>(a, x6, epi, grid, s);
+  else launch_tn<true, false>(a, x6, epi, grid, s);
 }
+
+// The kernel for the fp32 GEMMs: the split-operand bf16 kernel, unless the environment
+// variable GPT2_GEMM_F32_PRODUCTS is "fp32" (the fp32 MFMA kernel, kept for comparison).
+bool use_x6() {
+  const char* e = getenv("GPT2_GEMM_F32_PRODUCTS");
+  return !(e && strcmp(e, "fp32") == 0);
+}
+
+// tile shape, workgroups per CU and planning rate of the kernel in use
+struct KernelShape {
+  int bm, bn, wg_per_cu;
+  double rate;
+};
+template <class CFG>
+KernelShape shape_of() {
+  return KernelShape{CFG::BM, CFG::BN, CFG::WG_PER_CU, CFG::RATE};
+}
+KernelShape kernel_shape(bool x6) { return x6 ? shape_of<CfgX6>() : shape_of<CfgF32>(); }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // Number of K splits for a problem, from a cost model fitted to measurements on MI355X.
-// OCC 256-thread workgroups fit on each of the 256 CUs (256 OCC slots). A launch of n
-// workgroups runs ceil(n/slots) rounds of the same length, so relative to perfectly packed
-// work it costs q = ceil(n/slots) / (n/slots); splitting K multiplies n by the split count and
-// adds a pass that reads the partials and applies the epilogue (the partials themselves are
-// written while the GEMM computes).
-// Compute time is estimated at 90% of the fp32 MFMA peak, memory at 5 TB/s.
-int choose_splits(const Gemm& g) {
+// wg_per_cu workgroups fit on each of the 256 CUs. A launch of n workgroups runs
+// ceil(n/slots) rounds of the same length, so relative to perfectly packed work it costs
+// q = ceil(n/slots) / (n/slots); splitting K multiplies n by the split count and adds a pass
+// that reads the partials and applies the epilogue (the partials themselves are written
+// while the GEMM computes). Compute time is estimated at the kernel's planning rate,
+// memory at 5 TB/s.
+int choose_splits(const Gemm& g, const KernelShape& ks) {
 #ifdef GPT2_SPLIT_OVERRIDE
   if (const char* e = getenv("GPT2_SPLITS")) return atoi(e);
 #endif
-  const double tiles = (double)ceil_div(g.M, BM) * ceil_div(g.N, BN);
+  const double tiles = (double)ceil_div(g.M, ks.bm) * ceil_div(g.N, ks.bn);
   const int kt = ceil_div(g.K, BK);
   const double mn = (double)g.M * g.N;
-  const double t_mfma = 2.0 * mn * g.K / (0.9 * 157.3e12);
+  const double t_mfma = 2.0 * mn * g.K / ks.rate;
   double best = 1e30;
   int best_s = 1;
   for (int s = 1; s <= 32; s++) {
     const int kper = ceil_div(kt, s);
     if (s > 1 && kper < 4) break;
     if (s > 1 && ceil_div(kt, kper) != s) continue;
-    const double rounds = tiles * s / (256.0 * OCC);
+    const double rounds = tiles * s / (256.0 * ks.wg_per_cu);
     const double q = std::ceil(rounds) / rounds;
     double cost = t_mfma * q;
     if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;  // partials are written during the GEMM
@@ -515,7 +910,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int split_ld(int N) { return (N + 3) & ~3; }
 
 size_t gemm_workspace_floats(const Gemm& g) {
-  int s = choose_splits(g);
+  int s = choose_splits(g, kernel_shape(use_x6()));
   if (s <= 1) return 0;
   return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
 }
@@ -528,11 +923,12 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   }
   // float4 operand loads: 16-byte aligned bases and leading dimensions that are multiples
   // of 4 (which also keeps the last float4 of a row inside the row's storage)
-  // (and leading dimensions below 2^22, so a slab's per-thread byte offsets fit 32 bits)
+  // (and leading dimensions below 2^21, so the per-thread byte offsets within a slab of
+  // 256 rows fit 32 bits)
   const int a_cols = g.a_trans ? g.M : g.K, b_cols = g.b_trans ? g.N : g.K;
   if (!aligned16(g.A) || !aligned16(g.B) || !aligned16(g.C) || g.lda % 4 || g.ldb % 4 ||
-      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N || g.lda >= (1 << 22) ||
-      g.ldb >= (1 << 22)) {
+      g.ldc % 2 || g.lda < a_cols || g.ldb < b_cols || g.ldc < g.N || g.lda >= (1 << 21) ||
+      g.ldb >= (1 << 21)) {
     set_global_error("gemm: unsupported alignment or leading dimension (lda=%d ldb=%d ldc=%d)",
                      g.lda, g.ldb, g.ldc);
     return -1;
@@ -559,14 +955,17 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   a.c_zstride = 0;
   a.colsum_zstride = 0;
 
-  int splits = choose_splits(g);
+  const bool x6 = use_x6();
+  const KernelShape ks = kernel_shape(x6);
+  int splits = choose_splits(g, ks);
   if (splits > 1 && (!workspace || ws_floats < gemm_workspace_floats(g))) splits = 1;
   const int kt = ceil_div(g.K, BK);
   const int kt_per = ceil_div(kt, splits);
   splits = ceil_div(kt, kt_per);
   a.k_split = kt_per * BK;
   a.splits = splits;
-  const int tiles = ceil_div(g.M, BM) * ceil_div(g.N, BN);
+  const int tiles = ceil_div(g.M, ks.bm) * ceil_div(g.N, ks.bn);
+  const char* kname = x6 ? "gemm_x6_kernel" : "gemm_kernel";
 
   const double MN = (double)g.M * g.N;
   const double flop = 2.0 * MN * g.K;
@@ -575,12 +974,12 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   const double out_factor = g.epi == EPI_STORE ? 1.0 : 2.0;
   char name[64];
   if (splits == 1) {
-    snprintf(name, sizeof(name), "gemm_kernel<%d,%d,%d>", (int)g.a_trans, (int)g.b_trans,
+    snprintf(name, sizeof(name), "%s<%d,%d,%d>", kname, (int)g.a_trans, (int)g.b_trans,
              (int)g.epi);
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d", g.M, g.N, g.K);
     ProfScope ps(name, flop, in_bytes + 4.0 * MN * out_factor, stream);
-    launch(a, g.a_trans, g.b_trans, g.epi, dim3(tiles), stream);
+    launch(a, x6, g.a_trans, g.b_trans, g.epi, dim3(tiles), stream);
   } else {
     // the reduction indexes the M x ceil(N/4) output groups with 32-bit integers
     const long long total = (long long)g.M * ((g.N + 3) / 4);
@@ -598,13 +997,13 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
       p.colsum = colsum_part;
       p.colsum_zstride = g.M;
     }
-    snprintf(name, sizeof(name), "gemm_kernel<%d,%d,0>", (int)g.a_trans, (int)g.b_trans);
+    snprintf(name, sizeof(name), "%s<%d,%d,0>", kname, (int)g.a_trans, (int)g.b_trans);
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d/%d", g.M, g.N, g.K,
                splits);
     {
       ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
-      launch(p, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
+      launch(p, x6, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
     }
     int blocks = (int)((total + 255) / 256);
     if (blocks > 65536) blocks = 65536;

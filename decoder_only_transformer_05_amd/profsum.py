@@ -29,6 +29,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # translation unit (plus the headers every kernel includes) that defines each kernel
 KERNEL_SOURCES = {
     "gemm_kernel": ["csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h"],
+    "gemm_x6_kernel": ["csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h"],
     "attn_": ["csrc/attention.hip", "csrc/common.h", "csrc/kernels.h"],
 }
 

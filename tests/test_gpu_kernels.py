@@ -34,12 +34,22 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
+@pytest.fixture(params=["x6", "fp32"])
+def f32_products(request, monkeypatch):
+    """Both fp32 GEMM kernels: split-operand bf16 products (the default) and fp32 MFMA."""
+    if request.param == "fp32":
+        monkeypatch.setenv("GPT2_GEMM_F32_PRODUCTS", "fp32")
+    else:
+        monkeypatch.delenv("GPT2_GEMM_F32_PRODUCTS", raising=False)
+    return request.param
+
+
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("N,C,OC,ld", [(300, 96, 200, 200), (64, 16, 48, 48), (130, 772, 130, 132),
                                        (130, 772, 130, 130),  # rows 8-byte aligned: scalar epilogue
                                        (64, 768, 50257, 50304), (1024, 768, 2304, 2304)])
 @pytest.mark.parametrize("epi", [0, 1, 2])
-def test_matmul_forward(N, C, OC, ld, epi):
+def test_matmul_forward(N, C, OC, ld, epi, f32_products):
     if OC == 50257 and epi:
         pytest.skip("lm_head shape is used without bias or fused epilogue")
     r = rng(N + C + OC + epi)
@@ -66,9 +76,12 @@ def test_matmul_forward(N, C, OC, ld, epi):
         assert np.all(np.isnan(host(out)[:, OC:]))
 
 
-@pytest.mark.parametrize("N,C,OC", [(300, 96, 200), (4096, 64, 96), (256, 64, 8192), (77, 16, 28)])
+@pytest.mark.parametrize("N,C,OC", [(300, 96, 200), (4096, 64, 96), (256, 64, 8192), (77, 16, 28),
+                                    (16384, 256, 384)])
 @pytest.mark.parametrize("with_gelu", [False, True])
-def test_matmul_backward(N, C, OC, with_gelu):
+def test_matmul_backward(N, C, OC, with_gelu, f32_products):
+    # (16384, 256, 384): the weight gradient reduces over all 16384 tokens of a 16 x 1024
+    # batch, split along the tokens into partial sums
     r = rng(N * 7 + C + OC + with_gelu)
     x, W = f32(r.normal(size=(N, C))), f32(r.normal(0, 0.05, (OC, C)))
     dy = f32(r.normal(size=(N, OC)))
@@ -86,6 +99,41 @@ def test_matmul_backward(N, C, OC, with_gelu):
     assert_close_mag("dinp", host(dinp), rdinp, mdinp, OC)
     assert_close_mag("dW", host(dW), dW0 + rdW, np.abs(dW0) + mdW, N)
     assert_close_mag("db", host(db), db0 + rdb, np.abs(db0) + mdb, N)
+
+
+@pytest.mark.parametrize("N,C,OC,dist", [(512, 3072, 768, "normal"), (300, 768, 200, "positive"),
+                                         (256, 16384, 64, "normal")])
+def test_matmul_fp32_error_model(N, C, OC, dist):
+    """fp32 accuracy of both GEMM kernels with no relative slack: every output within
+    (4 sqrt(K) + 2) u sum_k |x_k w_k| of the exact sum (u = 2^-24). The fp32 K-term
+    accumulation accounts for the first term; the second covers the products the
+    split-operand kernel drops (at most 2^-23 |x w| each). Also, the split-operand kernel's
+    rms error is no larger than 1.5 times the fp32 MFMA kernel's on the same inputs."""
+    r = rng(N + C + OC)
+    if dist == "normal":
+        x, W = f32(r.normal(size=(N, C))), f32(r.normal(size=(OC, C)))
+    else:
+        x, W = f32(r.lognormal(0, 1, (N, C))), f32(r.lognormal(0, 1, (OC, C)))
+    ref = oracle.matmul_forward(x, W, None)
+    mag = oracle.matmul_forward(np.abs(x), np.abs(W), None)
+    rms = {}
+    for mode in ("x6", "fp32"):
+        mp = pytest.MonkeyPatch()
+        if mode == "fp32":
+            mp.setenv("GPT2_GEMM_F32_PRODUCTS", "fp32")
+        else:
+            mp.delenv("GPT2_GEMM_F32_PRODUCTS", raising=False)
+        try:
+            out = torch.full((N, OC), float("nan"), device="cuda")
+            gb.k_matmul_forward(out, dev(x), dev(W), None, N, C, OC, OC, 0, None, None)
+            got = host(out)
+        finally:
+            mp.undo()
+        err = np.abs(got - ref)
+        bound = (4.0 * np.sqrt(C) + 2.0) * 2.0 ** -24 * mag
+        assert np.all(err <= bound), (mode, float((err / bound).max()))
+        rms[mode] = float(np.sqrt(np.mean(err ** 2)))
+    assert rms["x6"] <= 1.5 * rms["fp32"], rms
 
 
 def test_matmul_rejects_unaligned_leading_dimension():
@@ -125,8 +173,10 @@ def test_layernorm_forward_backward(N, C):
 
 @pytest.mark.parametrize("B,T,C,NH", [(2, 100, 128, 2), (4, 16, 16, 4), (1, 200, 96, 3),
                                       (1, 130, 512, 4), (2, 64, 768, 12), (1, 1, 64, 1), (2, 40, 48, 4),
-                                      (3, 257, 64, 1)])
+                                      (3, 257, 64, 1), (2, 1024, 768, 12)])
 def test_attention_forward_backward(B, T, C, NH):
+    # (2, 1024, 768, 12): the trained model's head layout at its full context, whose dK/dV
+    # grid (24 heads x 8 key blocks) takes the longest-first block order
     r = rng(B * T + C + NH)
     qkv = f32(r.normal(0, 1.0, (B, T, 3 * C)))
     dy = f32(r.normal(size=(B, T, C)))
