@@ -77,12 +77,11 @@ struct Cfg {
 typedef Cfg<GPT2_GEMM_BM, 128, GPT2_GEMM_BM / 64, 2, GPT2_GEMM_STAGES,
             (GPT2_GEMM_STAGES == 2 ? 4 : 3) * 128 / GPT2_GEMM_BM * 16 / BK, false>
     CfgF32;
-// split-operand kernel (shape a build option): 256 x 256 tiles, eight waves of 128 x 64,
-// 96 KB of LDS, one workgroup per CU (two waves per SIMD)
-#ifndef GPT2_GEMM_X6_SHAPE
-#define GPT2_GEMM_X6_SHAPE 256, 256, 2, 4, 2, 2
-#endif
-typedef Cfg<GPT2_GEMM_X6_SHAPE, true> CfgX6;
+// split-operand kernel: 256 x 256 tiles of eight waves of 128 x 64 (96 KB of LDS), or
+// 256 x 192 tiles of eight waves of 64 x 96 (84 KB; for output widths that 192 divides and
+// 256 does not), one workgroup per CU (two waves per SIMD)
+typedef Cfg<256, 256, 2, 4, 2, 2, true> CfgX6W;
+typedef Cfg<256, 192, 4, 2, 2, 2, true> CfgX6N;
 struct Args {
   const float* A;
   const float* B;
@@ -464,8 +463,15 @@ GPT2_DEVICE_INLINE void split3(f32x4 x, f32x4 y, bf16x8& hi, bf16x8& mid, bf16x8
 // Plane layouts (bf16): an operand stored with K contiguous as [row][16 k], 32-byte rows,
 // chunk c (8 k) of row r at chunk c ^ ((r >> 3) & 1), so the 16-byte fragment reads of 32
 // consecutive rows cover all banks; an operand stored (K, rows) as [k][row], chunk c (8 rows)
-// of k-row k at chunk c ^ rswz(k % 4), read with transposing reads.
-GPT2_DEVICE_INLINE int rswz(int j) { return (0xAC60 >> (4 * j)) & 15; }  // 0, 6, 12, 10
+// of k-row k at chunk c ^ rswz<R>(k % 4), read with transposing reads, whose four k-rows
+// then fall on disjoint banks: with R = 256 (512-byte k-rows) the XOR moves them by 0, 96,
+// 192 and 160 bytes, with R = 192 (384-byte k-rows, every other one 128 bytes on) by 0, 0,
+// 32 and 32 (the XOR stays inside the row's 24 chunks).
+template <int R>
+GPT2_DEVICE_INLINE int rswz(int j) {
+  static_assert(R == 256 || R == 192, "k-row length");
+  return R == 256 ? (0xAC60 >> (4 * j)) & 15 : (0x2200 >> (4 * j)) & 15;
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
@@ -479,12 +485,14 @@ GPT2_DEVICE_INLINE bf16x8 frag_tr(const char* p, int kstride4) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One operand's staging: thread t holds 8 values, for an operand stored with K contiguous
-// row t / 2 at k 8 (t % 2) .. + 7 of the slab, for one stored (K, rows) k-row t / (R / 8) at
-// rows 8 (t % (R / 8)) .. + 7. The buffer resource of a slab ends where the operand ends.
+// One operand's staging: thread t < R BK / 8 holds 8 values, for an operand stored with K
+// contiguous row t / 2 at k 8 (t % 2) .. + 7 of the slab, for one stored (K, rows) k-row
+// t / (R / 8) at rows 8 (t % (R / 8)) .. + 7. The buffer resource of a slab ends where the
+// operand ends.
 template <bool TRANS, int R>
 struct StageX6 {
-  static constexpr int CPR = R / 8;  // 8-row chunks per k-row (TRANS)
+  static constexpr int CPR = R / 8;        // 8-row chunks per k-row (TRANS)
+  static constexpr int NCH = R * BK / 8;   // threads that stage this operand
   const char* tile;                  // operand at this tile's first row / column, k = kbeg
   long long step;                    // bytes between consecutive slabs
   long long remain;                  // bytes from `tile` to the end of the operand
@@ -507,10 +515,11 @@ struct StageX6 {
       const int kk = tid / CPR, c = tid % CPR;
       voff = (uint32_t)(kk * ld + 8 * c) * 4u;
       kofs = kk;
-      lds_off = kk * 2 * R + 16 * (c ^ rswz(kk & 3));
+      lds_off = kk * 2 * R + 16 * (c ^ rswz<R>(kk & 3));
     }
   }
-  __device__ __forceinline__ void load(int kt, f32x4* v) const {
+  __device__ __forceinline__ void load(int kt, f32x4* v, int tid) const {
+    if (NCH % 64 == 0 && tid >= NCH) return;  // (wave-uniform)
     const long long off = (long long)kt * step;
     const long long left = remain - off;
     const int nrec = (int)(uint32_t)(left > 0xFFFFFFFFLL ? 0xFFFFFFFFLL : left > 0 ? left : 0);
@@ -523,8 +532,9 @@ struct StageX6 {
   // an operand stored (K, rows)), split, and write the three parts
   template <bool COLSUM>
   __device__ __forceinline__ void store(const f32x4* v, char* planes, int k0, int kend,
-                                        float* cs) const {
+                                        float* cs, int tid) const {
     constexpr int PLANE = R * BK * 2;
+    if (tid >= NCH) return;
     f32x4 a = v[0], b = v[1];
     if (!TRANS) {
       const int lim = kend - (k0 + kofs);
@@ -554,7 +564,8 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   constexpr int NT = CFG::NTHREADS;
   static_assert(BK == 16, "one bf16 MFMA step per slab");
-  static_assert(BM * BK == 8 * NT && BN * BK == 8 * NT, "eight values of each operand per thread");
+  static_assert(BM * BK == 8 * NT && BN * BK <= 8 * NT && BN * BK % 512 == 0,
+                "eight values per thread: of A for all, of B for whole waves");
   constexpr int PA = BM * BK * 2, PB = BN * BK * 2;  // bytes of one plane
   constexpr int BUF = 3 * (PA + PB);
   __shared__ __attribute__((aligned(1024))) char lds[2 * BUF];
@@ -605,14 +616,16 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
     const int row = wm0 + 32 * q + r;
     const int n = wm0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
     rda[q] = !AT ? row * 2 * BK + 16 * (h ^ ((row >> 3) & 1))
-                 : (8 * h + (i16 >> 2)) * 2 * BM + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
+                 : (8 * h + (i16 >> 2)) * 2 * BM + 16 * ((n >> 3) ^ rswz<BM>(i16 >> 2)) +
+                       8 * (i16 & 1);
   }
 #pragma unroll
   for (int q = 0; q < TN; q++) {
     const int row = wn0 + 32 * q + r;
     const int n = wn0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
     rdb[q] = !BT ? row * 2 * BK + 16 * (h ^ ((row >> 3) & 1))
-                 : (8 * h + (i16 >> 2)) * 2 * BN + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
+                 : (8 * h + (i16 >> 2)) * 2 * BN + 16 * ((n >> 3) ^ rswz<BN>(i16 >> 2)) +
+                       8 * (i16 & 1);
   }
   auto fa = [&](const char* pl, int q) -> bf16x8 {
     if (!AT) return *reinterpret_cast<const bf16x8*>(pl + rda[q]);
@@ -624,14 +637,14 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
   };
   f32x4 va[2][2], vb[2][2];  // two register sets of staged values
   auto load = [&](int kt, int set) {
-    sa.load(kt, va[set]);
-    sb.load(kt, vb[set]);
+    sa.load(kt, va[set], tid);
+    sb.load(kt, vb[set], tid);
   };
   auto stage = [&](int set, char* buf, int kt) {
     const int k0 = kbeg + kt * BK;
-    if (do_colsum) sa.template store<true>(va[set], buf, k0, kend, cs);
-    else sa.template store<false>(va[set], buf, k0, kend, cs);
-    sb.template store<false>(vb[set], buf + 3 * PA, k0, kend, cs);
+    if (do_colsum) sa.template store<true>(va[set], buf, k0, kend, cs, tid);
+    else sa.template store<false>(va[set], buf, k0, kend, cs, tid);
+    sb.template store<false>(vb[set], buf + 3 * PA, k0, kend, cs, tid);
   };
   auto compute = [&](const char* buf) {
     const char* pa = buf;
@@ -726,9 +739,12 @@ template <bool AT, bool BT, int EPI>
 __global__ __launch_bounds__(CfgF32::NTHREADS, CfgF32::OCC) void gemm_kernel(Args g) {
   gemm_body<CfgF32, AT, BT, EPI>(g);
 }
-template <bool AT, bool BT, int EPI>
-__global__ __launch_bounds__(CfgX6::NTHREADS, CfgX6::OCC) void gemm_x6_kernel(Args g) {
-  gemm_x6s_body<CfgX6, AT, BT, EPI>(g);
+template <int BNX, bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(512, 2) void gemm_x6_kernel(Args g) {
+  static_assert(CfgX6W::NTHREADS == 512 && CfgX6N::NTHREADS == 512 && CfgX6W::OCC == 2 &&
+                CfgX6N::OCC == 2, "launch bounds");
+  if constexpr (BNX == 256) gemm_x6s_body<CfgX6W, AT, BT, EPI>(g);
+  else gemm_x6s_body<CfgX6N, AT, BT, EPI>(g);
 }
 
 
@@ -824,81 +840,106 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Args g, const float* 
   }
 }
 
+// the kernels and tile shapes a GEMM can run with
+enum GemmKind { KIND_F32 = 0, KIND_X6W = 1, KIND_X6N = 2 };
+
 template <bool AT, bool BT, int EPI>
-void launch_e(const Args& a, bool x6, dim3 grid, hipStream_t s) {
-  if (x6) gemm_x6_kernel<AT, BT, EPI><<<grid, CfgX6::NTHREADS, 0, s>>>(a);
+void launch_e(const Args& a, int kind, dim3 grid, hipStream_t s) {
+  if (kind == KIND_X6W) gemm_x6_kernel<256, AT, BT, EPI><<<grid, 512, 0, s>>>(a);
+  else if (kind == KIND_X6N) gemm_x6_kernel<192, AT, BT, EPI><<<grid, 512, 0, s>>>(a);
   else gemm_kernel<AT, BT, EPI><<<grid, CfgF32::NTHREADS, 0, s>>>(a);
 }
 
 template <bool AT, bool BT>
-void launch_tn(const Args& a, bool x6, int epi, dim3 grid, hipStream_t s) {
+void launch_tn(const Args& a, int kind, int epi, dim3 grid, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: launch_e<AT, BT, EPI_STORE>(a, x6, grid, s); break;
-    case EPI_GELU: launch_e<AT, BT, EPI_GELU>(a, x6, grid, s); break;
-    case EPI_RESID: launch_e<AT, BT, EPI_RESID>(a, x6, grid, s); break;
-    case EPI_ACCUM: launch_e<AT, BT, EPI_ACCUM>(a, x6, grid, s); break;
-    case EPI_GELU_BWD: launch_e<AT, BT, EPI_GELU_BWD>(a, x6, grid, s); break;
+    case EPI_STORE: launch_e<AT, BT, EPI_STORE>(a, kind, grid, s); break;
+    case EPI_GELU: launch_e<AT, BT, EPI_GELU>(a, kind, grid, s); break;
+    case EPI_RESID: launch_e<AT, BT, EPI_RESID>(a, kind, grid, s); break;
+    case EPI_ACCUM: launch_e<AT, BT, EPI_ACCUM>(a, kind, grid, s); break;
+    case EPI_GELU_BWD: launch_e<AT, BT, EPI_GELU_BWD>(a, kind, grid, s); break;
   }
 }
 
-void launch(const Args& a, bool x6, bool at, bool bt, int epi, dim3 grid, hipStream_t s) {
-  if (!at && !bt) launch_tn<false, false>(a, x6, epi, grid, s);
-  else if (!at && bt) launch_tn<false, true>(a, x6, epi, grid, s);
-  else if (at && bt) launch_tn<true, true>(a, x6, epi, grid, s);
-  else launch_tn<true, false>(a, x6, epi, grid, s);
+void launch(const Args& a, int kind, bool at, bool bt, int epi, dim3 grid, hipStream_t s) {
+  if (!at && !bt) launch_tn<false, false>(a, kind, epi, grid, s);
+  else if (!at && bt) launch_tn<false, true>(a, kind, epi, grid, s);
+  else if (at && bt) launch_tn<true, true>(a, kind, epi, grid, s);
+  else launch_tn<true, false>(a, kind, epi, grid, s);
 }
 
-// The kernel for the fp32 GEMMs: the split-operand bf16 kernel, unless the environment
-// variable GPT2_GEMM_F32_PRODUCTS is "fp32" (the fp32 MFMA kernel, kept for comparison).
+// The kernels for the fp32 GEMMs: the split-operand bf16 kernel, unless the environment
+// variable GPT2_GEMM_F32_PRODUCTS is "fp32" (the fp32 MFMA kernel, kept for comparison);
+// GPT2_GEMM_X6_TILE = 256 or 192 restricts it to one tile width (for tests).
 bool use_x6() {
   const char* e = getenv("GPT2_GEMM_F32_PRODUCTS");
   return !(e && strcmp(e, "fp32") == 0);
 }
+int forced_x6_width() {
+  const char* e = getenv("GPT2_GEMM_X6_TILE");
+  const int v = e ? atoi(e) : 0;
+  return v == 256 || v == 192 ? v : 0;
+}
 
-// tile shape, workgroups per CU and planning rate of the kernel in use
+// tile shape, workgroups per CU and planning rate of a kernel
 struct KernelShape {
   int bm, bn, wg_per_cu;
   double rate;
 };
 template <class CFG>
-KernelShape shape_of() {
-  return KernelShape{CFG::BM, CFG::BN, CFG::WG_PER_CU, CFG::RATE};
+KernelShape shape_of(double derate = 1.0) {
+  return KernelShape{CFG::BM, CFG::BN, CFG::WG_PER_CU, CFG::RATE * derate};
 }
-KernelShape kernel_shape(bool x6) { return x6 ? shape_of<CfgX6>() : shape_of<CfgF32>(); }
+// the narrower split-operand tile reads more LDS per product: planned at 95% of the rate
+KernelShape kernel_shape(int kind) {
+  return kind == KIND_X6W ? shape_of<CfgX6W>()
+                          : kind == KIND_X6N ? shape_of<CfgX6N>(0.95) : shape_of<CfgF32>();
+}
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Number of K splits for a problem, from a cost model fitted to measurements on MI355X.
-// wg_per_cu workgroups fit on each of the 256 CUs. A launch of n workgroups runs
-// ceil(n/slots) rounds of the same length, so relative to perfectly packed work it costs
-// q = ceil(n/slots) / (n/slots); splitting K multiplies n by the split count and adds a pass
-// that reads the partials and applies the epilogue (the partials themselves are written
-// while the GEMM computes). Compute time is estimated at the kernel's planning rate,
-// memory at 5 TB/s.
-int choose_splits(const Gemm& g, const KernelShape& ks) {
-#ifdef GPT2_SPLIT_OVERRIDE
-  if (const char* e = getenv("GPT2_SPLITS")) return atoi(e);
-#endif
-  const double tiles = (double)ceil_div(g.M, ks.bm) * ceil_div(g.N, ks.bn);
+// Kernel, tile shape and number of K splits for a problem, from a cost model fitted to
+// measurements on MI355X. wg_per_cu workgroups of a kernel fit on each of the 256 CUs; a
+// launch of n workgroups runs ceil(n / slots) rounds, each as long as one tile's products at
+// the kernel's planning rate (tiles padded to whole tiles). Splitting K multiplies n by the
+// split count and adds a pass that reads the partials and applies the epilogue (the
+// partials themselves are written while the GEMM computes), costed at 5 TB/s. More splits,
+// or the narrower tile, only when clearly (5%) cheaper.
+struct Plan {
+  int kind, splits;
+};
+Plan choose_plan(const Gemm& g) {
+  int kinds[2] = {use_x6() ? (int)KIND_X6W : (int)KIND_F32, (int)KIND_X6N};
+  int nkinds = use_x6() ? 2 : 1;
+  if (use_x6() && forced_x6_width()) {
+    kinds[0] = forced_x6_width() == 256 ? KIND_X6W : KIND_X6N;
+    nkinds = 1;
+  }
   const int kt = ceil_div(g.K, BK);
   const double mn = (double)g.M * g.N;
-  const double t_mfma = 2.0 * mn * g.K / ks.rate;
   double best = 1e30;
-  int best_s = 1;
-  for (int s = 1; s <= 32; s++) {
-    const int kper = ceil_div(kt, s);
-    if (s > 1 && kper < 4) break;
-    if (s > 1 && ceil_div(kt, kper) != s) continue;
-    const double rounds = tiles * s / (256.0 * ks.wg_per_cu);
-    const double q = std::ceil(rounds) / rounds;
-    double cost = t_mfma * q;
-    if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;  // partials are written during the GEMM
-    if (cost < best * 0.95) {  // prefer fewer splits unless clearly cheaper
-      best = cost;
-      best_s = s;
+  Plan plan{kinds[0], 1};
+  for (int ki = 0; ki < nkinds; ki++) {
+    const KernelShape ks = kernel_shape(kinds[ki]);
+    const double tiles = (double)ceil_div(g.M, ks.bm) * ceil_div(g.N, ks.bn);
+    const double slots = 256.0 * ks.wg_per_cu;
+    for (int s = 1; s <= 32; s++) {
+      const int kper = ceil_div(kt, s);
+      if (s > 1 && kper < 4) break;
+      if (s > 1 && ceil_div(kt, kper) != s) continue;
+      double cost = std::ceil(tiles * s / slots) * 2.0 * ks.bm * ks.bn * (double)kper * BK *
+                    slots / ks.rate;
+      if (s > 1) cost += 4.0 * mn * (s + 2.0) / 5e12;
+      if (cost < best * 0.95) {
+        best = cost;
+        plan = Plan{kinds[ki], s};
+      }
     }
   }
-  return best_s;
+#ifdef GPT2_SPLIT_OVERRIDE
+  if (const char* e = getenv("GPT2_SPLITS")) plan.splits = atoi(e);
+#endif
+  return plan;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -910,7 +951,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int split_ld(int N) { return (N + 3) & ~3; }
 
 size_t gemm_workspace_floats(const Gemm& g) {
-  int s = choose_splits(g, kernel_shape(use_x6()));
+  const int s = choose_plan(g).splits;
   if (s <= 1) return 0;
   return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
 }
@@ -955,9 +996,9 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   a.c_zstride = 0;
   a.colsum_zstride = 0;
 
-  const bool x6 = use_x6();
-  const KernelShape ks = kernel_shape(x6);
-  int splits = choose_splits(g, ks);
+  const Plan plan = choose_plan(g);
+  const KernelShape ks = kernel_shape(plan.kind);
+  int splits = plan.splits;
   if (splits > 1 && (!workspace || ws_floats < gemm_workspace_floats(g))) splits = 1;
   const int kt = ceil_div(g.K, BK);
   const int kt_per = ceil_div(kt, splits);
@@ -965,7 +1006,11 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   a.k_split = kt_per * BK;
   a.splits = splits;
   const int tiles = ceil_div(g.M, ks.bm) * ceil_div(g.N, ks.bn);
-  const char* kname = x6 ? "gemm_x6_kernel" : "gemm_kernel";
+  // kernel name as profilers show it (template arguments: tile width for the split-operand
+  // kernel, then the operand layouts)
+  char kname[32];
+  if (plan.kind == KIND_F32) snprintf(kname, sizeof(kname), "gemm_kernel<");
+  else snprintf(kname, sizeof(kname), "gemm_x6_kernel<%d,", ks.bn);
 
   const double MN = (double)g.M * g.N;
   const double flop = 2.0 * MN * g.K;
@@ -974,12 +1019,12 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
   const double out_factor = g.epi == EPI_STORE ? 1.0 : 2.0;
   char name[64];
   if (splits == 1) {
-    snprintf(name, sizeof(name), "%s<%d,%d,%d>", kname, (int)g.a_trans, (int)g.b_trans,
+    snprintf(name, sizeof(name), "%s%d,%d,%d>", kname, (int)g.a_trans, (int)g.b_trans,
              (int)g.epi);
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d", g.M, g.N, g.K);
     ProfScope ps(name, flop, in_bytes + 4.0 * MN * out_factor, stream);
-    launch(a, x6, g.a_trans, g.b_trans, g.epi, dim3(tiles), stream);
+    launch(a, plan.kind, g.a_trans, g.b_trans, g.epi, dim3(tiles), stream);
   } else {
     // the reduction indexes the M x ceil(N/4) output groups with 32-bit integers
     const long long total = (long long)g.M * ((g.N + 3) / 4);
@@ -997,13 +1042,13 @@ int gemm(const Gemm& g, float* workspace, size_t ws_floats, hipStream_t stream) 
       p.colsum = colsum_part;
       p.colsum_zstride = g.M;
     }
-    snprintf(name, sizeof(name), "%s<%d,%d,0>", kname, (int)g.a_trans, (int)g.b_trans);
+    snprintf(name, sizeof(name), "%s%d,%d,0>", kname, (int)g.a_trans, (int)g.b_trans);
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d/%d", g.M, g.N, g.K,
                splits);
     {
       ProfScope ps(name, flop, in_bytes + 4.0 * MN * splits, stream);
-      launch(p, x6, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
+      launch(p, plan.kind, g.a_trans, g.b_trans, EPI_STORE, dim3(tiles * splits), stream);
     }
     int blocks = (int)((total + 255) / 256);
     if (blocks > 65536) blocks = 65536;

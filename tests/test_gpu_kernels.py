@@ -34,13 +34,16 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
-@pytest.fixture(params=["x6", "fp32"])
+@pytest.fixture(params=["x6w", "x6n", "fp32"])
 def f32_products(request, monkeypatch):
-    """Both fp32 GEMM kernels: split-operand bf16 products (the default) and fp32 MFMA."""
+    """Both fp32 GEMM kernels: split-operand bf16 products (the default; both tile widths,
+    256 and 192) and fp32 MFMA."""
+    monkeypatch.delenv("GPT2_GEMM_F32_PRODUCTS", raising=False)
+    monkeypatch.delenv("GPT2_GEMM_X6_TILE", raising=False)
     if request.param == "fp32":
         monkeypatch.setenv("GPT2_GEMM_F32_PRODUCTS", "fp32")
     else:
-        monkeypatch.delenv("GPT2_GEMM_F32_PRODUCTS", raising=False)
+        monkeypatch.setenv("GPT2_GEMM_X6_TILE", "256" if request.param == "x6w" else "192")
     return request.param
 
 
@@ -117,12 +120,14 @@ def test_matmul_fp32_error_model(N, C, OC, dist):
     ref = oracle.matmul_forward(x, W, None)
     mag = oracle.matmul_forward(np.abs(x), np.abs(W), None)
     rms = {}
-    for mode in ("x6", "fp32"):
+    for mode in ("x6w", "x6n", "fp32"):
         mp = pytest.MonkeyPatch()
+        mp.delenv("GPT2_GEMM_F32_PRODUCTS", raising=False)
+        mp.delenv("GPT2_GEMM_X6_TILE", raising=False)
         if mode == "fp32":
             mp.setenv("GPT2_GEMM_F32_PRODUCTS", "fp32")
         else:
-            mp.delenv("GPT2_GEMM_F32_PRODUCTS", raising=False)
+            mp.setenv("GPT2_GEMM_X6_TILE", "256" if mode == "x6w" else "192")
         try:
             out = torch.full((N, OC), float("nan"), device="cuda")
             gb.k_matmul_forward(out, dev(x), dev(W), None, N, C, OC, OC, 0, None, None)
@@ -133,7 +138,7 @@ def test_matmul_fp32_error_model(N, C, OC, dist):
         bound = (4.0 * np.sqrt(C) + 2.0) * 2.0 ** -24 * mag
         assert np.all(err <= bound), (mode, float((err / bound).max()))
         rms[mode] = float(np.sqrt(np.mean(err ** 2)))
-    assert rms["x6"] <= 1.5 * rms["fp32"], rms
+    assert max(rms["x6w"], rms["x6n"]) <= 1.5 * rms["fp32"], rms
 
 
 def test_matmul_rejects_unaligned_leading_dimension():
