@@ -423,8 +423,10 @@ GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 acc) {
 // significand bit of x below 2^-8 |x|, has at most 16 significant bits; after mid at most 8
 // are left, so lo is that remainder exactly (down to |x| ~ 2^-110, where lo leaves the
 // normal bf16 range). |mid| <= 2^-8 |x| and |lo| <= 2^-16 |x|.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two values rounded to bf16 by one v_cvt_pk_bf16_f32 (a in the low half)
 GPT2_DEVICE_INLINE uint32_t bf16_pair(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 GPT2_DEVICE_INLINE void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   hi = bf16_pair(x0, x1);
@@ -485,20 +487,27 @@ GPT2_DEVICE_INLINE bf16x8 frag_tr(const char* p, int kstride4) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One operand's staging: thread t < R BK / 8 holds 8 values, for an operand stored with K
-// contiguous row t / 2 at k 8 (t % 2) .. + 7 of the slab, for one stored (K, rows) k-row
-// t / (R / 8) at rows 8 (t % (R / 8)) .. + 7. The buffer resource of a slab ends where the
-// operand ends.
-template <bool TRANS, int R>
+// One operand's staging. The slab is cut into R BK / 8 chunks of 8 values; chunk f is, for
+// an operand stored with K contiguous, row f / 2 at k 8 (f % 2) .. + 7 of the slab, for one
+// stored (K, rows), k-row f / (R / 8) at rows 8 (f % (R / 8)) .. + 7. Thread t stages chunks
+// t, t + NT, ... below R BK / 8 (whole waves take part or skip). The buffer resource of a
+// slab ends where the operand ends.
+template <bool TRANS, int R, int NT>
 struct StageX6 {
-  static constexpr int CPR = R / 8;        // 8-row chunks per k-row (TRANS)
-  static constexpr int NCH = R * BK / 8;   // threads that stage this operand
-  const char* tile;                  // operand at this tile's first row / column, k = kbeg
-  long long step;                    // bytes between consecutive slabs
-  long long remain;                  // bytes from `tile` to the end of the operand
-  uint32_t voff;                     // this thread's byte offset within a slab
-  int kofs;                          // k (first k) of this thread's values within a slab
-  int lds_off;                       // byte offset of its 16-byte chunk within a plane
+  static constexpr int CPR = R / 8;                  // 8-row chunks per k-row (TRANS)
+  static constexpr int NCH = R * BK / 8;             // chunks per slab
+  static constexpr int CH = (NCH + NT - 1) / NT;     // chunks per thread (at most)
+  static_assert(NCH % 64 == 0, "whole waves");
+  // whether chunk i of thread tid exists (wave-uniform)
+  static __device__ __forceinline__ bool live(int i, int tid) {
+    return NCH % NT == 0 || tid + NT * i < NCH;
+  }
+  const char* tile;     // operand at this tile's first row / column, k = kbeg
+  long long step;       // bytes between consecutive slabs
+  long long remain;     // bytes from `tile` to the end of the operand
+  uint32_t voff[CH];    // byte offsets of this thread's chunks within a slab
+  int kofs[CH];         // k (first k) of each chunk within a slab
+  int lds_off[CH];      // byte offset of each chunk within a plane
 
   __device__ __forceinline__ void init(const float* P, int ld, int row0, long long total,
                                        int tid) {
@@ -506,56 +515,70 @@ struct StageX6 {
     tile = reinterpret_cast<const char*>(P + at);
     remain = 4 * (total - at);
     step = TRANS ? 4LL * BK * ld : 4LL * BK;
-    if (!TRANS) {
-      const int row = tid >> 1, c = tid & 1;
-      voff = (uint32_t)(row * ld + 8 * c) * 4u;
-      kofs = 8 * c;
-      lds_off = row * 2 * BK + 16 * (c ^ ((row >> 3) & 1));
-    } else {
-      const int kk = tid / CPR, c = tid % CPR;
-      voff = (uint32_t)(kk * ld + 8 * c) * 4u;
-      kofs = kk;
-      lds_off = kk * 2 * R + 16 * (c ^ rswz<R>(kk & 3));
+#pragma unroll
+    for (int i = 0; i < CH; i++) {
+      const int f = tid + NT * i;
+      if (!TRANS) {
+        const int row = f >> 1, c = f & 1;
+        voff[i] = (uint32_t)(row * ld + 8 * c) * 4u;
+        kofs[i] = 8 * c;
+        lds_off[i] = row * 2 * BK + 16 * (c ^ ((row >> 3) & 1));
+      } else {
+        const int kk = f / CPR, c = f % CPR;
+        voff[i] = (uint32_t)(kk * ld + 8 * c) * 4u;
+        kofs[i] = kk;
+        lds_off[i] = kk * 2 * R + 16 * (c ^ rswz<R>(kk & 3));
+      }
     }
   }
+  // v: 2 CH float4s
   __device__ __forceinline__ void load(int kt, f32x4* v, int tid) const {
-    if (NCH % 64 == 0 && tid >= NCH) return;  // (wave-uniform)
     const long long off = (long long)kt * step;
     const long long left = remain - off;
     const int nrec = (int)(uint32_t)(left > 0xFFFFFFFFLL ? 0xFFFFFFFFLL : left > 0 ? left : 0);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(tile + off), (short)0, nrec, kBufferFlags);
-    v[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
-    v[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, 0, 0));
+#pragma unroll
+    for (int i = 0; i < CH; i++) {
+      if (!live(i, tid)) break;
+      v[2 * i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0));
+      v[2 * i + 1] =
+          __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + 16, 0, 0));
+    }
   }
   // mask k at or past kend (k0: first k of the slab), add the values to cs (column sums of
-  // an operand stored (K, rows)), split, and write the three parts
+  // an operand stored (K, rows); 8 per chunk), split, and write the three parts
   template <bool COLSUM>
   __device__ __forceinline__ void store(const f32x4* v, char* planes, int k0, int kend,
                                         float* cs, int tid) const {
     constexpr int PLANE = R * BK * 2;
-    if (tid >= NCH) return;
-    f32x4 a = v[0], b = v[1];
-    if (!TRANS) {
-      const int lim = kend - (k0 + kofs);
-      a = kmask4(a, lim);
-      b = kmask4(b, lim - 4);
-    } else if (k0 + kofs >= kend) {
-      a = f32x4{0.f, 0.f, 0.f, 0.f};
-      b = a;
-    }
-    if (COLSUM) {
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        cs[e] += a[e];
-        cs[4 + e] += b[e];
+    for (int i = 0; i < CH; i++) {
+      if (!live(i, tid)) break;
+      f32x4 a = v[2 * i], b = v[2 * i + 1];
+      if (!TRANS) {
+        if (k0 + BK > kend) {  // the slab reaches past kend (uniform)
+          const int lim = kend - (k0 + kofs[i]);
+          a = kmask4(a, lim);
+          b = kmask4(b, lim - 4);
+        }
+      } else if (k0 + kofs[i] >= kend) {
+        a = f32x4{0.f, 0.f, 0.f, 0.f};
+        b = a;
       }
+      if (COLSUM) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          cs[8 * i + e] += a[e];
+          cs[8 * i + 4 + e] += b[e];
+        }
+      }
+      bf16x8 hi, mid, lo;
+      split3(a, b, hi, mid, lo);
+      *reinterpret_cast<bf16x8*>(planes + lds_off[i]) = hi;
+      *reinterpret_cast<bf16x8*>(planes + PLANE + lds_off[i]) = mid;
+      *reinterpret_cast<bf16x8*>(planes + 2 * PLANE + lds_off[i]) = lo;
     }
-    bf16x8 hi, mid, lo;
-    split3(a, b, hi, mid, lo);
-    *reinterpret_cast<bf16x8*>(planes + lds_off) = hi;
-    *reinterpret_cast<bf16x8*>(planes + PLANE + lds_off) = mid;
-    *reinterpret_cast<bf16x8*>(planes + 2 * PLANE + lds_off) = lo;
   }
 };
 
@@ -564,8 +587,7 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   constexpr int NT = CFG::NTHREADS;
   static_assert(BK == 16, "one bf16 MFMA step per slab");
-  static_assert(BM * BK == 8 * NT && BN * BK <= 8 * NT && BN * BK % 512 == 0,
-                "eight values per thread: of A for all, of B for whole waves");
+  static_assert(BM * BK >= 8 * NT, "every thread stages A (its column sums)");
   constexpr int PA = BM * BK * 2, PB = BN * BK * 2;  // bytes of one plane
   constexpr int BUF = 3 * (PA + PB);
   __shared__ __attribute__((aligned(1024))) char lds[2 * BUF];
@@ -599,10 +621,12 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
     for (int b = 0; b < TN; b++)
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
-  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-
-  StageX6<AT, BM> sa;
-  StageX6<BT, BN> sb;
+  StageX6<AT, BM, NT> sa;
+  StageX6<BT, BN, NT> sb;
+  constexpr int CHA = StageX6<AT, BM, NT>::CH, CHB = StageX6<BT, BN, NT>::CH;
+  float cs[8 * CHA];
+#pragma unroll
+  for (int i = 0; i < 8 * CHA; i++) cs[i] = 0.f;
   sa.init(g.A + (AT ? (long long)kbeg * g.lda : kbeg), g.lda, m0,
           AT ? (long long)(g.K - kbeg) * g.lda : (long long)g.M * g.lda - kbeg, tid);
   sb.init(g.B + (BT ? (long long)kbeg * g.ldb : kbeg), g.ldb, n0,
@@ -635,7 +659,7 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
     if (!BT) return *reinterpret_cast<const bf16x8*>(pl + rdb[q]);
     return frag_tr(pl + rdb[q], 4 * 2 * BN);
   };
-  f32x4 va[2][2], vb[2][2];  // two register sets of staged values
+  f32x4 va[2][2 * CHA], vb[2][2 * CHB];  // two register sets of staged values
   auto load = [&](int kt, int set) {
     sa.load(kt, va[set], tid);
     sb.load(kt, vb[set], tid);
@@ -700,19 +724,23 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
     if (kt < nslabs) compute(buf0);  // an odd last slab
   }
 
-  if (do_colsum) {  // the 16 k-row partial sums of each m, added in k-row order
+  if (do_colsum) {  // the BK k-row partial sums of each m, added in k-row order
     float* red = reinterpret_cast<float*>(lds);
     constexpr int CPR = BM / 8;
-    const int kk = tid / CPR, c = tid % CPR;
     __syncthreads();  // every wave is done reading the planes (an odd last slab has no barrier)
 #pragma unroll
-    for (int e = 0; e < 8; e++) red[kk * BM + 8 * c + e] = cs[e];
+    for (int i = 0; i < CHA; i++) {
+      const int f = tid + NT * i, kk = f / CPR, c = f % CPR;
+#pragma unroll
+      for (int e = 0; e < 8; e++) red[kk * BM + 8 * c + e] = cs[8 * i + e];
+    }
     __syncthreads();
-    if (tid < BM && m0 + tid < g.M) {
+    for (int m = tid; m < BM; m += NT) {
+      if (m0 + m >= g.M) break;
       float total = 0.f;
-      for (int j = 0; j < NT / CPR; j++) total += red[j * BM + tid];
-      if (g.colsum_zstride) g.colsum[(long long)z * g.colsum_zstride + m0 + tid] = total;
-      else g.colsum[m0 + tid] += total;
+      for (int j = 0; j < BK; j++) total += red[j * BM + m];
+      if (g.colsum_zstride) g.colsum[(long long)z * g.colsum_zstride + m0 + m] = total;
+      else g.colsum[m0 + m] += total;
     }
   }
 
