@@ -27,6 +27,7 @@
 // of 4 consecutive output columns of one row: the epilogue works on float4s.
 #include <cmath>
 #include <cstdio>
+#include <type_traits>
 #include <cstdlib>
 #include <cstring>
 
@@ -546,9 +547,10 @@ struct StageX6 {
           __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + 16, 0, 0));
     }
   }
-  // mask k at or past kend (k0: first k of the slab), add the values to cs (column sums of
-  // an operand stored (K, rows); 8 per chunk), split, and write the three parts
-  template <bool COLSUM>
+  // with MASKED, zero k at or past kend (k0: first k of the slab); with COLSUM, add the
+  // values to cs (column sums of an operand stored (K, rows); 8 per chunk); split, and write
+  // the three parts
+  template <bool COLSUM, bool MASKED>
   __device__ __forceinline__ void store(const f32x4* v, char* planes, int k0, int kend,
                                         float* cs, int tid) const {
     constexpr int PLANE = R * BK * 2;
@@ -556,13 +558,11 @@ struct StageX6 {
     for (int i = 0; i < CH; i++) {
       if (!live(i, tid)) break;
       f32x4 a = v[2 * i], b = v[2 * i + 1];
-      if (!TRANS) {
-        if (k0 + BK > kend) {  // the slab reaches past kend (uniform)
-          const int lim = kend - (k0 + kofs[i]);
-          a = kmask4(a, lim);
-          b = kmask4(b, lim - 4);
-        }
-      } else if (k0 + kofs[i] >= kend) {
+      if (MASKED && !TRANS) {
+        const int lim = kend - (k0 + kofs[i]);
+        a = kmask4(a, lim);
+        b = kmask4(b, lim - 4);
+      } else if (MASKED && k0 + kofs[i] >= kend) {
         a = f32x4{0.f, 0.f, 0.f, 0.f};
         b = a;
       }
@@ -664,11 +664,12 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
     sa.load(kt, va[set], tid);
     sb.load(kt, vb[set], tid);
   };
-  auto stage = [&](int set, char* buf, int kt) {
+  // COLSUM: column sums of A wanted; MASKED: the last slab ends before BK (a K tail)
+  auto stage = [&](auto colsum, auto masked, int set, char* buf, int kt) {
+    constexpr bool COLSUM = decltype(colsum)::value, MASKED = decltype(masked)::value;
     const int k0 = kbeg + kt * BK;
-    if (do_colsum) sa.template store<true>(va[set], buf, k0, kend, cs, tid);
-    else sa.template store<false>(va[set], buf, k0, kend, cs, tid);
-    sb.template store<false>(vb[set], buf + 3 * PA, k0, kend, cs, tid);
+    sa.template store<COLSUM, MASKED>(va[set], buf, k0, kend, cs, tid);
+    sb.template store<false, MASKED>(vb[set], buf + 3 * PA, k0, kend, cs, tid);
   };
   auto compute = [&](const char* buf) {
     const char* pa = buf;
@@ -701,27 +702,52 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
   };
 
   // Slab kt is read from plane buffer kt % 2; its values arrive in register set kt % 2. The
-  // loop is unrolled by two so that both name their buffer and set statically.
+  // loop is unrolled by two so that both name their buffer and set statically, and its
+  // steady state (every step stages and loads) has no conditions, so the products, the
+  // splitting and the LDS traffic of a step form one block the compiler can interleave.
+  // Masking and column sums are compile-time choices of the loop (both uniform).
   char* const buf0 = lds;
   char* const buf1 = lds + BUF;
-  if (nslabs > 0) {
+  auto run = [&](auto colsum, auto masked) {
     load(0, 0);
     if (nslabs > 1) load(1, 1);
-    stage(0, buf0, 0);
+    stage(colsum, masked, 0, buf0, 0);
     if (nslabs > 2) load(2, 0);
     __syncthreads();
     int kt = 0;
-    for (; kt + 2 <= nslabs; kt += 2) {
+    for (; kt + 5 <= nslabs; kt += 2) {
       compute(buf0);  // slab kt
-      if (kt + 1 < nslabs) stage(1, buf1, kt + 1);
+      stage(colsum, masked, 1, buf1, kt + 1);
       __syncthreads();  // slab kt + 1 is written; every wave is done with slab kt
-      if (kt + 3 < nslabs) load(kt + 3, 1);
+      load(kt + 3, 1);
       compute(buf1);  // slab kt + 1
-      if (kt + 2 < nslabs) stage(0, buf0, kt + 2);
+      stage(colsum, masked, 0, buf0, kt + 2);
+      __syncthreads();
+      load(kt + 4, 0);
+    }
+    for (; kt + 2 <= nslabs; kt += 2) {
+      compute(buf0);
+      stage(colsum, masked, 1, buf1, kt + 1);
+      __syncthreads();
+      if (kt + 3 < nslabs) load(kt + 3, 1);
+      compute(buf1);
+      if (kt + 2 < nslabs) stage(colsum, masked, 0, buf0, kt + 2);
       __syncthreads();
       if (kt + 4 < nslabs) load(kt + 4, 0);
     }
     if (kt < nslabs) compute(buf0);  // an odd last slab
+  };
+  typedef std::integral_constant<bool, true> yes;
+  typedef std::integral_constant<bool, false> no;
+  if (nslabs > 0) {
+    const bool tail = klen % BK != 0;
+    if (AT && do_colsum) {
+      if (tail) run(yes{}, yes{});
+      else run(yes{}, no{});
+    } else {
+      if (tail) run(no{}, yes{});
+      else run(no{}, no{});
+    }
   }
 
   if (do_colsum) {  // the BK k-row partial sums of each m, added in k-row order
