@@ -188,7 +188,12 @@ int gpt2_k_layernorm_backward(float* dx, float* dw, float* db, const float* dout
 
 /* [llm.c] 1.5 (+1.9, 1.11 fused): out (N,OC) = inp (N,C) . W(OC,C)^T + bias (bias may be
  * NULL), then by `epilogue`: 0 store; 1 also out2 = gelu(out) (tanh form, [llm.c] 1.9);
- * 2 out = resid + result (resid (N,OC) may alias out). ld_out >= OC is out's row stride. */
+ * 2 out = resid + result (resid (N,OC) may alias out). ld_out >= OC is out's row stride.
+ * The fp32 GEMMs here and in gpt2_k_matmul_backward form each fp32 product as six bf16
+ * MFMA products of an exact three-way bf16 split of the operands (within 2^-23 of the
+ * exact product) with fp32 accumulation; the environment variable
+ * GPT2_GEMM_F32_PRODUCTS=fp32 selects fp32 MFMA products instead. Leading dimensions must
+ * be below 2^21 and multiples of 4 (-1 otherwise). */
 int gpt2_k_matmul_forward(float* out, float* out2, const float* resid, const float* inp,
                           const float* W, const float* bias, int N, int C, int OC,
                           int ld_out, int epilogue, void* stream);
