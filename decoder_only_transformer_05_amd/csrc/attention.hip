@@ -23,6 +23,8 @@
 // d(s, half) = 8*(s/4) + 4*half + s%4, which lets one 16-byte LDS read feed four MFMAs;
 // both operands use the same order, so the dot products are unchanged.
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 #include "kernels.h"
 
@@ -694,6 +696,12 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
 
 int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
                       hipStream_t stream) {
+  // head sizes that are multiples of 8 use split-operand products on bf16 MFMA unless
+  // GPT2_ATTN_F32_PRODUCTS is "fp32"; others (and that setting) multiply on fp32 MFMA
+  const char* e = getenv("GPT2_ATTN_F32_PRODUCTS");
+  const bool x6 = !(e && strcmp(e, "fp32") == 0);
+  if (x6 && C % NH == 0 && attention_bf16_mma_supported(C, NH))
+    return attention_forward_x6(out, lse, qkv, B, T, C, NH, stream);
   return attention_forward_t(out, lse, qkv, B, T, C, NH, stream);
 }
 int attention_forward(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C, int NH,

@@ -294,6 +294,287 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// forward on fp32 tensors with split-operand products: each fp32 value of Q, K, V and P is
+// split exactly into three bf16 parts (x = hi + mid + lo, |mid| <= 2^-8 |x|,
+// |lo| <= 2^-16 |x|) and every fp32 product becomes the six bf16 MFMA products of parts at
+// or above 2^-16 of it (within 2^-23 of the exact product), accumulated in fp32. The
+// structure is that of attn_fwd_bf16mma_kernel, with three LDS planes per K and V tile.
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+GPT2_DEVICE_INLINE uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// x0, x1 -> packed (hi, mid, lo) pairs
+GPT2_DEVICE_INLINE void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_pair(x0, x1);
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+  mid = bf16_pair(r0, r1);
+  const float s0 = r0 - __uint_as_float(mid << 16), s1 = r1 - __uint_as_float(mid & 0xFFFF0000u);
+  lo = bf16_pair(s0, s1);
+}
+// eight values (two float4s) -> the three parts as u32x4 (8 bf16 each)
+GPT2_DEVICE_INLINE void split8(f32x4 x, f32x4 y, u32x4& hi, u32x4& mid, u32x4& lo) {
+  uint32_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
+  split2(x[0], x[1], h0, m0, l0);
+  split2(x[2], x[3], h1, m1, l1);
+  split2(y[0], y[1], h2, m2, l2);
+  split2(y[2], y[3], h3, m3, l3);
+  hi = u32x4{h0, h1, h2, h3};
+  mid = u32x4{m0, m1, m2, m3};
+  lo = u32x4{l0, l1, l2, l3};
+}
+// acc += the six products of a (ah, am, al) x b (bh, bm, bl), smaller terms first
+GPT2_DEVICE_INLINE f32x16 mfma_x6(bf16x8 ah, bf16x8 am, bf16x8 al, bf16x8 bh, bf16x8 bm,
+                                  bf16x8 bl, f32x16 acc) {
+  acc = mfma_bf16(am, bm, acc);
+  acc = mfma_bf16(al, bh, acc);
+  acc = mfma_bf16(ah, bl, acc);
+  acc = mfma_bf16(am, bh, acc);
+  acc = mfma_bf16(ah, bm, acc);
+  return mfma_bf16(ah, bh, acc);
+}
+
+// 8 fp32 values of row t, columns d..d+7 (hs a multiple of 8); rows past T and columns
+// past hs read as zero (addresses clamped into the tensor)
+GPT2_DEVICE_INLINE void load8f(const float* base, long long ld, int t, int d, int T, int hs,
+                               f32x4& x, f32x4& y) {
+  const int tc = min(t, T - 1), dc = min(d, hs - 8);
+  const float* p = base + (long long)tc * ld + dc;
+  x = *reinterpret_cast<const f32x4*>(p);
+  y = *reinterpret_cast<const f32x4*>(p + 4);
+  if (!(t < T && d < hs)) {
+    x = f32x4{0.f, 0.f, 0.f, 0.f};
+    y = x;
+  }
+}
+
+// Natural tile of fp32 rows -> three bf16 planes S[p][row][d] (HSP columns each, loff layout)
+template <int HSP>
+struct RowsTileX6 {
+  static constexpr int CPR = HSP / 8, NI = TILE * CPR / NTHR;
+  f32x4 v[NI][2];
+  __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
+                                       int hs, int tid) {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int f = tid + NTHR * i;
+      load8f(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs, v[i][0], v[i][1]);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int f = tid + NTHR * i;
+      u32x4 h, m, l;
+      split8(v[i][0], v[i][1], h, m, l);
+      const int o = loff<HSP>(f / CPR, f % CPR);
+      *reinterpret_cast<u32x4*>(S + o) = h;
+      *reinterpret_cast<u32x4*>(S + TILE * HSP + o) = m;
+      *reinterpret_cast<u32x4*>(S + 2 * TILE * HSP + o) = l;
+    }
+  }
+};
+
+// Transposed tile of fp32 rows -> three bf16 planes S[p][d][kpos(row)] (64 columns each): a
+// thread moves blocks of 4 rows x 8 columns, split per row, then transposed per plane
+template <int HSP>
+struct ColsTileX6 {
+  static constexpr int DG = HSP / 8;
+  static constexpr int BLOCKS = (TILE / 4) * DG;
+  static constexpr int NI = (BLOCKS + NTHR - 1) / NTHR;
+  f32x4 v[NI][4][2];
+  __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
+                                       int hs, int tid) {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int b = tid + NTHR * i;
+      if (BLOCKS % NTHR && b >= BLOCKS) break;
+      const int dg = b % DG, rq = b / DG;
+#pragma unroll
+      for (int j = 0; j < 4; j++) load8f(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs, v[i][j][0], v[i][j][1]);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int b = tid + NTHR * i;
+      if (BLOCKS % NTHR && b >= BLOCKS) break;
+      const int dg = b % DG, rq = b / DG;
+      const int p = kpos(4 * rq);
+      u32x4 x[3][4];  // [plane][row]
+#pragma unroll
+      for (int j = 0; j < 4; j++) split8(v[i][j][0], v[i][j][1], x[0][j], x[1][j], x[2][j]);
+#pragma unroll
+      for (int pl = 0; pl < 3; pl++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int q = e >> 1;
+          uint32_t lo, hi;
+          if ((e & 1) == 0) {
+            lo = (x[pl][0][q] & 0xFFFFu) | (x[pl][1][q] << 16);
+            hi = (x[pl][2][q] & 0xFFFFu) | (x[pl][3][q] << 16);
+          } else {
+            lo = (x[pl][0][q] >> 16) | (x[pl][1][q] & 0xFFFF0000u);
+            hi = (x[pl][2][q] >> 16) | (x[pl][3][q] & 0xFFFF0000u);
+          }
+          *reinterpret_cast<u32x2*>(S + pl * HSP * TILE + loff<TILE>(8 * dg + e, p >> 3) +
+                                    (p & 7)) = u32x2{lo, hi};
+        }
+    }
+  }
+};
+
+template <int HSP>
+__global__ __launch_bounds__(NTHR, 2) void attn_fwd_x6_kernel(float* __restrict__ out,
+                                                              float* __restrict__ lse,
+                                                              const float* __restrict__ qkv,
+                                                              int T, int C, int NH, int hs,
+                                                              float scale_log2) {
+  constexpr int KS = HSP / 16, ND = HSP / 32;
+  constexpr int PK = TILE * HSP, PV = HSP * TILE;  // elements of one plane
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[3 * PK];  // [plane][key][d]
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[3 * PV];  // [plane][d][kpos(key)]
+
+  const int nqt = (T + TILE - 1) / TILE;
+  int qt, head, b;
+  tile_of_block(nqt, NH, &qt, &head, &b);
+  qt = nqt - 1 - qt;  // longest rows first
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, lh = lane >> 5;
+  const long long C3 = 3LL * C;
+  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const int q = qt * TILE + wave * 32 + r;
+  const int qm = min(q, T - 1);  // lanes past the end mask as the last row; never stored
+
+  // this lane's query, d = 16ks + 8lh .. +7 for each k step, as three parts
+  bf16x8 qh[KS], qmid[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    f32x4 x, y;
+    load8f(base, C3, qm, 16 * ks + 8 * lh, T, hs, x, y);
+    u32x4 h, m, l;
+    split8(x, y, h, m, l);
+    qh[ks] = __builtin_bit_cast(bf16x8, h);
+    qmid[ks] = __builtin_bit_cast(bf16x8, m);
+    ql[ks] = __builtin_bit_cast(bf16x8, l);
+  }
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // in units of the scaled log2 domain
+
+  const int ntiles = (min(T, (qt + 1) * TILE) + TILE - 1) / TILE;
+  RowsTileX6<HSP> kn;
+  ColsTileX6<HSP> vn;
+  kn.load(base + C, C3, 0, T, hs, tid);
+  vn.load(base + 2 * C, C3, 0, T, hs, tid);
+  for (int kt = 0; kt < ntiles; kt++) {
+    const int key0 = kt * TILE;
+    __syncthreads();
+    kn.store(Ks, tid);
+    vn.store(Vt, tid);
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      kn.load(base + C, C3, key0 + TILE, T, hs, tid);
+      vn.load(base + 2 * C, C3, key0 + TILE, T, hs, tid);
+    }
+
+    // S^T for 2 x 32 keys: s[kb][i] = score of key 32kb + 8(i/4) + 4lh + i%4
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const int o = loff<HSP>(32 * kb + r, 2 * ks + lh);
+        s[kb] = mfma_x6(*reinterpret_cast<const bf16x8*>(&Ks[o]),
+                        *reinterpret_cast<const bf16x8*>(&Ks[PK + o]),
+                        *reinterpret_cast<const bf16x8*>(&Ks[2 * PK + o]), qh[ks], qmid[ks],
+                        ql[ks], s[kb]);
+      }
+    }
+    if (key0 + TILE > qt * TILE) {  // the diagonal tile (uniform): mask keys after the query
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * lh + (i % 4);
+          if (key > qm) s[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    // the running max moves only by more than 8 (see attention.hip): most tiles skip the
+    // rescale; the first always moves it (key 0 <= qm is never masked)
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; db++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    // P as the B operand of k step (kb, hh), in three parts
+    bf16x8 ph[2][2], pm[2][2], pl[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          pv[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hh + j], scale_log2, -m_run));
+          l_run += pv[j];
+        }
+        u32x4 wh, wm, wl;
+        split8(f32x4{pv[0], pv[1], pv[2], pv[3]}, f32x4{pv[4], pv[5], pv[6], pv[7]}, wh, wm, wl);
+        ph[kb][hh] = __builtin_bit_cast(bf16x8, wh);
+        pm[kb][hh] = __builtin_bit_cast(bf16x8, wm);
+        pl[kb][hh] = __builtin_bit_cast(bf16x8, wl);
+      }
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const int o = loff<TILE>(32 * db + r, 4 * kb + 2 * hh + lh);
+          oacc[db] = mfma_x6(*reinterpret_cast<const bf16x8*>(&Vt[o]),
+                             *reinterpret_cast<const bf16x8*>(&Vt[PV + o]),
+                             *reinterpret_cast<const bf16x8*>(&Vt[2 * PV + o]), ph[kb][hh],
+                             pm[kb][hh], pl[kb][hh], oacc[db]);
+        }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (q < T) {
+    float* o = out + ((long long)b * T + q) * C + (long long)head * hs;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * lh;
+        if (d < hs)
+          st4(o + d, f32x4{oacc[db][4 * ig] * inv, oacc[db][4 * ig + 1] * inv,
+                           oacc[db][4 * ig + 2] * inv, oacc[db][4 * ig + 3] * inv});
+      }
+    if (lh == 0) lse[((long long)b * NH + head) * T + q] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
 
 // ---------------------------------------------------------------------------------------
 // backward
@@ -524,6 +805,26 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_bf16mma_kernel(
 }
 
 }  // namespace
+
+int attention_forward_x6(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                         hipStream_t stream) {
+  if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_bf16_mma_supported(C, NH)) {
+    set_global_error("attention (split operands): unsupported shape B=%d T=%d C=%d NH=%d", B,
+                     T, C, NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale_log2 = kLog2e / sqrtf((float)hs);
+  dim3 grid(((T + TILE - 1) / TILE) * NH * B);
+  const double tri = (double)T * (T + 1) / 2.0;
+  ProfScope ps("attn_fwd_x6_kernel", 4.0 * B * NH * hs * tri,
+               4.0 * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
+  if (hs <= 32) attn_fwd_x6_kernel<32><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else if (hs <= 64) attn_fwd_x6_kernel<64><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else attn_fwd_x6_kernel<128><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
 
 bool attention_bf16_mma_supported(int C, int NH) {
   const int hs = C / NH;

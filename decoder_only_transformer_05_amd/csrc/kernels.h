@@ -95,6 +95,10 @@ int attention_forward(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, 
 // bf16-MFMA attention (attention_bf16.hip), used by the bf16 overloads when the head size
 // is a multiple of 8 (at most 128)
 bool attention_bf16_mma_supported(int C, int NH);
+// fp32 attention forward with split-operand products on bf16 MFMA (head size a multiple of
+// 8, at most 128); the fp32 attention_forward uses it unless GPT2_ATTN_F32_PRODUCTS=fp32
+int attention_forward_x6(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                         hipStream_t stream);
 int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
                                int NH, hipStream_t stream);
 int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,

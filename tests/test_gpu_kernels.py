@@ -179,9 +179,15 @@ def test_layernorm_forward_backward(N, C):
 @pytest.mark.parametrize("B,T,C,NH", [(2, 100, 128, 2), (4, 16, 16, 4), (1, 200, 96, 3),
                                       (1, 130, 512, 4), (2, 64, 768, 12), (1, 1, 64, 1), (2, 40, 48, 4),
                                       (3, 257, 64, 1), (2, 1024, 768, 12)])
-def test_attention_forward_backward(B, T, C, NH):
+@pytest.mark.parametrize("products", ["x6", "fp32"])
+def test_attention_forward_backward(B, T, C, NH, products, monkeypatch):
     # (2, 1024, 768, 12): the trained model's head layout at its full context, whose dK/dV
-    # grid (24 heads x 8 key blocks) takes the longest-first block order
+    # grid (24 heads x 8 key blocks) takes the longest-first block order. products: the
+    # forward's split-operand bf16 products (head sizes that are multiples of 8) or fp32 MFMA
+    if products == "fp32":
+        monkeypatch.setenv("GPT2_ATTN_F32_PRODUCTS", "fp32")
+    else:
+        monkeypatch.delenv("GPT2_ATTN_F32_PRODUCTS", raising=False)
     r = rng(B * T + C + NH)
     qkv = f32(r.normal(0, 1.0, (B, T, 3 * C)))
     dy = f32(r.normal(size=(B, T, C)))
