@@ -349,23 +349,25 @@ GPT2_DEVICE_INLINE void load8f(const float* base, long long ld, int t, int d, in
   }
 }
 
-// Natural tile of fp32 rows -> three bf16 planes S[p][row][d] (HSP columns each, loff layout)
-template <int HSP>
+// Natural tile of fp32 rows -> three bf16 planes S[p][row][d] (HSP columns each, loff
+// layout), staged by NT threads
+template <int HSP, int NT>
 struct RowsTileX6 {
-  static constexpr int CPR = HSP / 8, NI = TILE * CPR / NTHR;
+  static constexpr int CPR = HSP / 8, NI = TILE * CPR / NT;
+  static_assert(NI * NT == TILE * CPR, "whole chunks per thread");
   f32x4 v[NI][2];
   __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
                                        int hs, int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-      const int f = tid + NTHR * i;
+      const int f = tid + NT * i;
       load8f(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs, v[i][0], v[i][1]);
     }
   }
   __device__ __forceinline__ void store(bf16_t* S, int tid) const {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-      const int f = tid + NTHR * i;
+      const int f = tid + NT * i;
       u32x4 h, m, l;
       split8(v[i][0], v[i][1], h, m, l);
       const int o = loff<HSP>(f / CPR, f % CPR);
@@ -377,19 +379,19 @@ struct RowsTileX6 {
 };
 
 // Transposed tile of fp32 rows -> three bf16 planes S[p][d][kpos(row)] (64 columns each): a
-// thread moves blocks of 4 rows x 8 columns, split per row, then transposed per plane
-template <int HSP>
+// thread (of NT) moves blocks of 4 rows x 8 columns, split per row, then transposed per plane
+template <int HSP, int NT>
 struct ColsTileX6 {
   static constexpr int DG = HSP / 8;
   static constexpr int BLOCKS = (TILE / 4) * DG;
-  static constexpr int NI = (BLOCKS + NTHR - 1) / NTHR;
+  static constexpr int NI = (BLOCKS + NT - 1) / NT;
   f32x4 v[NI][4][2];
   __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
                                        int hs, int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-      const int b = tid + NTHR * i;
-      if (BLOCKS % NTHR && b >= BLOCKS) break;
+      const int b = tid + NT * i;
+      if (BLOCKS % NT && b >= BLOCKS) break;
       const int dg = b % DG, rq = b / DG;
 #pragma unroll
       for (int j = 0; j < 4; j++) load8f(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs, v[i][j][0], v[i][j][1]);
@@ -398,8 +400,8 @@ struct ColsTileX6 {
   __device__ __forceinline__ void store(bf16_t* S, int tid) const {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-      const int b = tid + NTHR * i;
-      if (BLOCKS % NTHR && b >= BLOCKS) break;
+      const int b = tid + NT * i;
+      if (BLOCKS % NT && b >= BLOCKS) break;
       const int dg = b % DG, rq = b / DG;
       const int p = kpos(4 * rq);
       u32x4 x[3][4];  // [plane][row]
@@ -425,18 +427,21 @@ struct ColsTileX6 {
   }
 };
 
+// A workgroup owns X6_QT = 128 queries (four waves of 32), so each split K and V tile
+// serves four waves.
+constexpr int X6_NW = 4, X6_NT = 64 * X6_NW, X6_QT = 32 * X6_NW;
 template <int HSP>
-__global__ __launch_bounds__(NTHR, 2) void attn_fwd_x6_kernel(float* __restrict__ out,
-                                                              float* __restrict__ lse,
-                                                              const float* __restrict__ qkv,
-                                                              int T, int C, int NH, int hs,
-                                                              float scale_log2) {
+__global__ __launch_bounds__(X6_NT, 2) void attn_fwd_x6_kernel(float* __restrict__ out,
+                                                               float* __restrict__ lse,
+                                                               const float* __restrict__ qkv,
+                                                               int T, int C, int NH, int hs,
+                                                               float scale_log2) {
   constexpr int KS = HSP / 16, ND = HSP / 32;
   constexpr int PK = TILE * HSP, PV = HSP * TILE;  // elements of one plane
   __shared__ __attribute__((aligned(16))) bf16_t Ks[3 * PK];  // [plane][key][d]
   __shared__ __attribute__((aligned(16))) bf16_t Vt[3 * PV];  // [plane][d][kpos(key)]
 
-  const int nqt = (T + TILE - 1) / TILE;
+  const int nqt = (T + X6_QT - 1) / X6_QT;
   int qt, head, b;
   tile_of_block(nqt, NH, &qt, &head, &b);
   qt = nqt - 1 - qt;  // longest rows first
@@ -444,8 +449,9 @@ __global__ __launch_bounds__(NTHR, 2) void attn_fwd_x6_kernel(float* __restrict_
   const int r = lane & 31, lh = lane >> 5;
   const long long C3 = 3LL * C;
   const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
-  const int q = qt * TILE + wave * 32 + r;
+  const int q = qt * X6_QT + wave * 32 + r;
   const int qm = min(q, T - 1);  // lanes past the end mask as the last row; never stored
+  const int wq_last = min(qt * X6_QT + wave * 32 + 31, T - 1);  // this wave's last query
 
   // this lane's query, d = 16ks + 8lh .. +7 for each k step, as three parts
   bf16x8 qh[KS], qmid[KS], ql[KS];
@@ -467,9 +473,9 @@ __global__ __launch_bounds__(NTHR, 2) void attn_fwd_x6_kernel(float* __restrict_
     for (int i = 0; i < 16; i++) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;  // in units of the scaled log2 domain
 
-  const int ntiles = (min(T, (qt + 1) * TILE) + TILE - 1) / TILE;
-  RowsTileX6<HSP> kn;
-  ColsTileX6<HSP> vn;
+  const int ntiles = (min(T, (qt + 1) * X6_QT) + TILE - 1) / TILE;
+  RowsTileX6<HSP, X6_NT> kn;
+  ColsTileX6<HSP, X6_NT> vn;
   kn.load(base + C, C3, 0, T, hs, tid);
   vn.load(base + 2 * C, C3, 0, T, hs, tid);
   for (int kt = 0; kt < ntiles; kt++) {
@@ -482,6 +488,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_fwd_x6_kernel(float* __restrict_
       kn.load(base + C, C3, key0 + TILE, T, hs, tid);
       vn.load(base + 2 * C, C3, key0 + TILE, T, hs, tid);
     }
+    if (key0 > wq_last) continue;  // every key of the tile follows this wave's queries
 
     // S^T for 2 x 32 keys: s[kb][i] = score of key 32kb + 8(i/4) + 4lh + i%4
     f32x16 s[2];
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_fwd_x6_kernel(float* __restrict_
                         ql[ks], s[kb]);
       }
     }
-    if (key0 + TILE > qt * TILE) {  // the diagonal tile (uniform): mask keys after the query
+    if (key0 + TILE > qt * X6_QT + wave * 32) {  // a diagonal tile (uniform): mask later keys
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
@@ -815,13 +822,13 @@ int attention_forward_x6(float* out, float* lse, const float* qkv, int B, int T,
   }
   const int hs = C / NH;
   const float scale_log2 = kLog2e / sqrtf((float)hs);
-  dim3 grid(((T + TILE - 1) / TILE) * NH * B);
+  dim3 grid(((T + X6_QT - 1) / X6_QT) * NH * B);
   const double tri = (double)T * (T + 1) / 2.0;
   ProfScope ps("attn_fwd_x6_kernel", 4.0 * B * NH * hs * tri,
                4.0 * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
-  if (hs <= 32) attn_fwd_x6_kernel<32><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
-  else if (hs <= 64) attn_fwd_x6_kernel<64><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
-  else attn_fwd_x6_kernel<128><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  if (hs <= 32) attn_fwd_x6_kernel<32><<<grid, X6_NT, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else if (hs <= 64) attn_fwd_x6_kernel<64><<<grid, X6_NT, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else attn_fwd_x6_kernel<128><<<grid, X6_NT, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
