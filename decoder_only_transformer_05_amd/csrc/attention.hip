@@ -653,6 +653,15 @@ int rowdot_t(float* D, const TS* dout, const TS* out, int B, int T, int C, int N
   return 0;
 }
 
+// fp32 attention with head sizes that are multiples of 8 forms its forward and dQ products
+// from split operands on bf16 MFMA unless GPT2_ATTN_F32_PRODUCTS is "fp32"; other head sizes
+// (and that setting) multiply on fp32 MFMA
+bool attn_x6(int C, int NH) {
+  const char* e = getenv("GPT2_ATTN_F32_PRODUCTS");
+  return !(e && strcmp(e, "fp32") == 0) && NH > 0 && C % NH == 0 &&
+         attention_bf16_mma_supported(C, NH);
+}
+
 template <typename TS>
 int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
                          const float* lse, float* dscratch, float* ds_scratch, int B, int T,
@@ -681,7 +690,12 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
     else if (hsp == 64) attn_bwd_dkdv_kernel<64, TS><<<gk, DK_THR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
     else attn_bwd_dkdv_kernel<128, TS><<<gk, DK_THR, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
   }
-  {  // dQ = dS K
+  if (f32 && attn_x6(C, NH)) {  // dQ = dS K with split-operand products
+    const int rq = attention_dq_x6(reinterpret_cast<float*>(dqkv),
+                                   reinterpret_cast<const float*>(qkv), ds_scratch, B, T, C, NH,
+                                   stream);
+    if (rq) return rq;
+  } else {  // dQ = dS K
     ProfScope ps(f32 ? "attn_bwd_dq_kernel" : "attn_bwd_dq_bf16_kernel", 2.0 * B * NH * hs * tri,
                  4.0 * B * NH * tri + es * 2.0 * BTC, stream);
     if (hsp == 32) attn_bwd_dq_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
@@ -696,12 +710,7 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
 
 int attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
                       hipStream_t stream) {
-  // head sizes that are multiples of 8 use split-operand products on bf16 MFMA unless
-  // GPT2_ATTN_F32_PRODUCTS is "fp32"; others (and that setting) multiply on fp32 MFMA
-  const char* e = getenv("GPT2_ATTN_F32_PRODUCTS");
-  const bool x6 = !(e && strcmp(e, "fp32") == 0);
-  if (x6 && C % NH == 0 && attention_bf16_mma_supported(C, NH))
-    return attention_forward_x6(out, lse, qkv, B, T, C, NH, stream);
+  if (attn_x6(C, NH)) return attention_forward_x6(out, lse, qkv, B, T, C, NH, stream);
   return attention_forward_t(out, lse, qkv, B, T, C, NH, stream);
 }
 int attention_forward(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C, int NH,

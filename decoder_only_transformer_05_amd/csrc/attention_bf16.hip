@@ -378,9 +378,10 @@ struct RowsTileX6 {
   }
 };
 
-// Transposed tile of fp32 rows -> three bf16 planes S[p][d][kpos(row)] (64 columns each): a
-// thread (of NT) moves blocks of 4 rows x 8 columns, split per row, then transposed per plane
-template <int HSP, int NT>
+// Transposed tile of fp32 rows -> three bf16 planes S[p][d][kpos(row)] (64 columns each; with
+// KPOS false S[p][d][row]): a thread (of NT) moves blocks of 4 rows x 8 columns, split per
+// row, then transposed per plane
+template <int HSP, int NT, bool KPOS = true>
 struct ColsTileX6 {
   static constexpr int DG = HSP / 8;
   static constexpr int BLOCKS = (TILE / 4) * DG;
@@ -403,7 +404,7 @@ struct ColsTileX6 {
       const int b = tid + NT * i;
       if (BLOCKS % NT && b >= BLOCKS) break;
       const int dg = b % DG, rq = b / DG;
-      const int p = kpos(4 * rq);
+      const int p = KPOS ? kpos(4 * rq) : 4 * rq;
       u32x4 x[3][4];  // [plane][row]
 #pragma unroll
       for (int j = 0; j < 4; j++) split8(v[i][j][0], v[i][j][1], x[0][j], x[1][j], x[2][j]);
@@ -582,12 +583,126 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_fwd_x6_kernel(float* __restrict
   }
 }
 
+// causal 64x64 tiles (qt, kt <= qt) of one (batch, head), stored in row order
+GPT2_DEVICE_INLINE long long tri_index(int qt, int kt) { return (long long)qt * (qt + 1) / 2 + kt; }
+GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 2; }
+
+// ---------------------------------------------------------------------------------------
+// dQ = dS K on fp32 tensors with split-operand products (as attn_fwd_x6_kernel): a workgroup
+// owns 128 queries (four waves of 32) and walks the 64-key tiles up to its diagonal; the
+// fp32 dS tiles written by attn_bwd_dkdv_kernel ([query][key], 64 x 64 per causal tile) and
+// the K tile are split into three bf16 planes each (dS [q][key], K transposed [d][key]).
+// dQ^T[d][q] accumulates so a lane stores four consecutive head dims of its query.
+// ---------------------------------------------------------------------------------------
+template <int HSP>
+__global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dq_x6_kernel(float* __restrict__ dqkv,
+                                                                  const float* __restrict__ qkv,
+                                                                  const float* __restrict__ dsbuf,
+                                                                  int T, int C, int NH, int hs,
+                                                                  float scale) {
+  constexpr int ND = HSP / 32, KS = TILE / 16;
+  constexpr int PK = HSP * TILE, PS = X6_QT * TILE;  // elements of one plane
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[3 * PK];  // [plane][d][key]
+  __shared__ __attribute__((aligned(16))) bf16_t Ss[3 * PS];  // [plane][q][key]
+
+  const int nq64 = (T + TILE - 1) / TILE;  // 64-query tiles of the dS store
+  const int nqt = (T + X6_QT - 1) / X6_QT;
+  int qt, head, b;
+  tile_of_block(nqt, NH, &qt, &head, &b);
+  qt = nqt - 1 - qt;  // longest rows first
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, lh = lane >> 5;
+  const long long C3 = 3LL * C;
+  const float* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
+  const float* sbase = dsbuf + ((long long)b * NH + head) * tri_tiles(nq64) * (TILE * TILE);
+  const int wq_last = min(qt * X6_QT + wave * 32 + 31, T - 1);
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[db][i] = 0.f;
+
+  // dS staging: 128 rows x 64 keys, chunks of 8 keys; thread t takes chunks t + X6_NT i
+  constexpr int SCH = X6_QT * TILE / 8 / X6_NT;
+  f32x4 sv[SCH][2];
+  auto load_ds = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < SCH; i++) {
+      const int f = tid + X6_NT * i, row = f / (TILE / 8), c = f % (TILE / 8);
+      const int q64 = 2 * qt + row / TILE;  // the 64-query tile of this row
+      if (q64 < nq64 && kt <= q64) {  // the causal tile (q64, kt) exists
+        const float* p = sbase + tri_index(q64, kt) * (TILE * TILE) + (row % TILE) * TILE + 8 * c;
+        sv[i][0] = *reinterpret_cast<const f32x4*>(p);
+        sv[i][1] = *reinterpret_cast<const f32x4*>(p + 4);
+      } else {
+        sv[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[i][1] = sv[i][0];
+      }
+    }
+  };
+  auto store_ds = [&]() {
+#pragma unroll
+    for (int i = 0; i < SCH; i++) {
+      const int f = tid + X6_NT * i, row = f / (TILE / 8), c = f % (TILE / 8);
+      u32x4 h, m, l;
+      split8(sv[i][0], sv[i][1], h, m, l);
+      const int o = loff<TILE>(row, c);
+      *reinterpret_cast<u32x4*>(Ss + o) = h;
+      *reinterpret_cast<u32x4*>(Ss + PS + o) = m;
+      *reinterpret_cast<u32x4*>(Ss + 2 * PS + o) = l;
+    }
+  };
+
+  const int nkt = (min(T, (qt + 1) * X6_QT) + TILE - 1) / TILE;
+  ColsTileX6<HSP, X6_NT, false> kn;
+  kn.load(kbase, C3, 0, T, hs, tid);
+  load_ds(0);
+  for (int kt = 0; kt < nkt; kt++) {
+    __syncthreads();
+    kn.store(Kt, tid);
+    store_ds();
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      kn.load(kbase, C3, (kt + 1) * TILE, T, hs, tid);
+      load_ds(kt + 1);
+    }
+    if (kt * TILE > wq_last) continue;  // the tile lies wholly after this wave's queries
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int os = loff<TILE>(32 * wave + r, 2 * ks + lh);
+      const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&Ss[os]);
+      const bf16x8 sm = *reinterpret_cast<const bf16x8*>(&Ss[PS + os]);
+      const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&Ss[2 * PS + os]);
+#pragma unroll
+      for (int db = 0; db < ND; db++) {
+        const int ok = loff<TILE>(32 * db + r, 2 * ks + lh);
+        acc[db] = mfma_x6(*reinterpret_cast<const bf16x8*>(&Kt[ok]),
+                          *reinterpret_cast<const bf16x8*>(&Kt[PK + ok]),
+                          *reinterpret_cast<const bf16x8*>(&Kt[2 * PK + ok]), sh, sm, sl, acc[db]);
+      }
+    }
+  }
+  // acc[db][i]: head dim 32db + 8(i/4) + 4lh + i%4 of query 32 wave + r of the tile
+  const int q = qt * X6_QT + 32 * wave + r;
+  if (q < T) {
+    float* dq = dqkv + ((long long)b * T + q) * C3 + (long long)head * hs;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * lh;
+        if (d < hs)
+          st4(dq + d, f32x4{acc[db][4 * ig] * scale, acc[db][4 * ig + 1] * scale,
+                            acc[db][4 * ig + 2] * scale, acc[db][4 * ig + 3] * scale});
+      }
+  }
+}
+
 
 // ---------------------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------------------
-GPT2_DEVICE_INLINE long long tri_index(int qt, int kt) { return (long long)qt * (qt + 1) / 2 + kt; }
-GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 2; }
 
 // dK, dV for 64 keys (32 per wave), over the query tiles from the diagonal down. Per query
 // tile, S and dP are computed with queries down the rows and this lane's key as the column;
@@ -829,6 +944,26 @@ int attention_forward_x6(float* out, float* lse, const float* qkv, int B, int T,
   if (hs <= 32) attn_fwd_x6_kernel<32><<<grid, X6_NT, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   else if (hs <= 64) attn_fwd_x6_kernel<64><<<grid, X6_NT, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   else attn_fwd_x6_kernel<128><<<grid, X6_NT, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int attention_dq_x6(float* dqkv, const float* qkv, const float* ds_scratch, int B, int T, int C,
+                    int NH, hipStream_t stream) {
+  if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_bf16_mma_supported(C, NH)) {
+    set_global_error("attention dQ (split operands): unsupported shape B=%d T=%d C=%d NH=%d", B,
+                     T, C, NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale = 1.0f / sqrtf((float)hs);
+  dim3 grid(((T + X6_QT - 1) / X6_QT) * NH * B);
+  const double tri = (double)T * (T + 1) / 2.0;
+  ProfScope ps("attn_bwd_dq_x6_kernel", 2.0 * B * NH * hs * tri,
+               4.0 * B * NH * tri + 4.0 * 2.0 * B * T * C, stream);
+  if (hs <= 32) attn_bwd_dq_x6_kernel<32><<<grid, X6_NT, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+  else if (hs <= 64) attn_bwd_dq_x6_kernel<64><<<grid, X6_NT, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
+  else attn_bwd_dq_x6_kernel<128><<<grid, X6_NT, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }

@@ -99,6 +99,10 @@ bool attention_bf16_mma_supported(int C, int NH);
 // 8, at most 128); the fp32 attention_forward uses it unless GPT2_ATTN_F32_PRODUCTS=fp32
 int attention_forward_x6(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
                          hipStream_t stream);
+// dQ = dS K of the fp32 attention backward from the fp32 dS tiles of attn_bwd_dkdv_kernel,
+// with split-operand products (same conditions and switch as attention_forward_x6)
+int attention_dq_x6(float* dqkv, const float* qkv, const float* ds_scratch, int B, int T, int C,
+                    int NH, hipStream_t stream);
 int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
                                int NH, hipStream_t stream);
 int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,
