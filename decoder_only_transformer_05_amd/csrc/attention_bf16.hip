@@ -30,7 +30,6 @@ constexpr int TILE = 64;   // queries per workgroup, keys per tile
 constexpr int NTHR = 128;  // two waves of 32 queries (or keys)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -296,34 +295,11 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
 
 // ---------------------------------------------------------------------------------------
 // forward on fp32 tensors with split-operand products: each fp32 value of Q, K, V and P is
-// split exactly into three bf16 parts (x = hi + mid + lo, |mid| <= 2^-8 |x|,
+// split exactly into three bf16 parts (split8, x = hi + mid + lo, |mid| <= 2^-8 |x|,
 // |lo| <= 2^-16 |x|) and every fp32 product becomes the six bf16 MFMA products of parts at
 // or above 2^-16 of it (within 2^-23 of the exact product), accumulated in fp32. The
 // structure is that of attn_fwd_bf16mma_kernel, with three LDS planes per K and V tile.
 // ---------------------------------------------------------------------------------------
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-GPT2_DEVICE_INLINE uint32_t bf16_pair(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-// x0, x1 -> packed (hi, mid, lo) pairs
-GPT2_DEVICE_INLINE void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = bf16_pair(x0, x1);
-  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
-  mid = bf16_pair(r0, r1);
-  const float s0 = r0 - __uint_as_float(mid << 16), s1 = r1 - __uint_as_float(mid & 0xFFFF0000u);
-  lo = bf16_pair(s0, s1);
-}
-// eight values (two float4s) -> the three parts as u32x4 (8 bf16 each)
-GPT2_DEVICE_INLINE void split8(f32x4 x, f32x4 y, u32x4& hi, u32x4& mid, u32x4& lo) {
-  uint32_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
-  split2(x[0], x[1], h0, m0, l0);
-  split2(x[2], x[3], h1, m1, l1);
-  split2(y[0], y[1], h2, m2, l2);
-  split2(y[2], y[3], h3, m3, l3);
-  hi = u32x4{h0, h1, h2, h3};
-  mid = u32x4{m0, m1, m2, m3};
-  lo = u32x4{l0, l1, l2, l3};
-}
 // acc += the six products of a (ah, am, al) x b (bh, bm, bl), smaller terms first
 GPT2_DEVICE_INLINE f32x16 mfma_x6(bf16x8 ah, bf16x8 am, bf16x8 al, bf16x8 bh, bf16x8 bm,
                                   bf16x8 bl, f32x16 acc) {

@@ -50,6 +50,39 @@ GPT2_DEVICE_INLINE float ld1(const bf16_t* p) { return bf16_to_f32(*p); }
 GPT2_DEVICE_INLINE void st1(float* p, float v) { *p = v; }
 GPT2_DEVICE_INLINE void st1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Exact split of fp32 values into three bf16 parts, x = hi + mid + lo: hi is x rounded to
+// bf16 (8 significand bits), mid the remainder x - hi rounded to bf16, lo what remains.
+// x - hi is exact in fp32 (hi is within a factor 2 of x) and, being a multiple of the last
+// significand bit of x below 2^-8 |x|, has at most 16 significant bits; after mid at most 8
+// are left, so lo is that remainder exactly (down to |x| ~ 2^-110, where lo leaves the
+// normal bf16 range). |mid| <= 2^-8 |x| and |lo| <= 2^-16 |x|. Used by the kernels that form
+// fp32 products as six bf16 MFMA products of the parts.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two values rounded to bf16 by one v_cvt_pk_bf16_f32 (a in the low half)
+GPT2_DEVICE_INLINE uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// x0, x1 -> their packed (hi, mid, lo) pairs
+GPT2_DEVICE_INLINE void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_pair(x0, x1);
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+  mid = bf16_pair(r0, r1);
+  const float s0 = r0 - __uint_as_float(mid << 16), s1 = r1 - __uint_as_float(mid & 0xFFFF0000u);
+  lo = bf16_pair(s0, s1);
+}
+// eight values (two float4s) -> the three parts, 8 bf16 each in value order
+GPT2_DEVICE_INLINE void split8(f32x4 x, f32x4 y, u32x4& hi, u32x4& mid, u32x4& lo) {
+  uint32_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
+  split2(x[0], x[1], h0, m0, l0);
+  split2(x[2], x[3], h1, m1, l1);
+  split2(y[0], y[1], h2, m2, l2);
+  split2(y[2], y[3], h3, m3, l3);
+  hi = u32x4{h0, h1, h2, h3};
+  mid = u32x4{m0, m1, m2, m3};
+  lo = u32x4{l0, l1, l2, l3};
+}
+
 // One wave64 MFMA: acc(32x32) += A(32x2) * B(2x32), fp32 in and out.
 // Operand layout: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32].
 // Result layout: acc[i] of lane l is element (row 8*(i/4) + 4*(l/32) + i%4, col l % 32).

@@ -409,7 +409,6 @@ __device__ __forceinline__ void gemm_body(const Args& g) {
 
 // ---- split-operand kernel ----------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One wave64 bf16 MFMA: acc(32x32) += A(32x16) * B(16x32), fp32 accumulation. Lane l
 // supplies A[l % 32][8 (l / 32) .. + 7] and B[8 (l / 32) .. + 7][l % 32]; the result layout
@@ -418,37 +417,8 @@ GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 acc) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
-// Exact split of fp32 values into three bf16 parts, x = hi + mid + lo: hi is x rounded to
-// bf16 (8 significand bits), mid the remainder x - hi rounded to bf16, lo what remains.
-// x - hi is exact in fp32 (hi is within a factor 2 of x) and, being a multiple of the last
-// significand bit of x below 2^-8 |x|, has at most 16 significant bits; after mid at most 8
-// are left, so lo is that remainder exactly (down to |x| ~ 2^-110, where lo leaves the
-// normal bf16 range). |mid| <= 2^-8 |x| and |lo| <= 2^-16 |x|.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// two values rounded to bf16 by one v_cvt_pk_bf16_f32 (a in the low half)
-GPT2_DEVICE_INLINE uint32_t bf16_pair(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-GPT2_DEVICE_INLINE void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = bf16_pair(x0, x1);
-  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
-  mid = bf16_pair(r0, r1);
-  const float s0 = r0 - __uint_as_float(mid << 16), s1 = r1 - __uint_as_float(mid & 0xFFFF0000u);
-  lo = bf16_pair(s0, s1);
-}
-// the eight k of a lane's fragment (two float4s) as the three bf16x8 operands
-GPT2_DEVICE_INLINE void split3(f32x4 x, f32x4 y, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
-  uint32_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
-  split2(x[0], x[1], h0, m0, l0);
-  split2(x[2], x[3], h1, m1, l1);
-  split2(y[0], y[1], h2, m2, l2);
-  split2(y[2], y[3], h3, m3, l3);
-  hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
-  mid = __builtin_bit_cast(bf16x8, u32x4{m0, m1, m2, m3});
-  lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
-}
 
-// Products: with a = ah + am + al and b = bh + bm + bl as above,
+// Products: with a = ah + am + al and b = bh + bm + bl (the exact split of common.h),
 // a b = ah bh + (ah bm + am bh) + (ah bl + al bh + am bm) + (am bl + al bm) + al bl; the six
 // terms of the first three groups are formed on bf16 MFMA (each exact, 8 x 8 significand
 // bits, accumulated in fp32) and the last three dropped, which changes a b by at most
@@ -573,11 +543,11 @@ struct StageX6 {
           cs[8 * i + 4 + e] += b[e];
         }
       }
-      bf16x8 hi, mid, lo;
-      split3(a, b, hi, mid, lo);
-      *reinterpret_cast<bf16x8*>(planes + lds_off[i]) = hi;
-      *reinterpret_cast<bf16x8*>(planes + PLANE + lds_off[i]) = mid;
-      *reinterpret_cast<bf16x8*>(planes + 2 * PLANE + lds_off[i]) = lo;
+      u32x4 hi, mid, lo;
+      split8(a, b, hi, mid, lo);
+      *reinterpret_cast<u32x4*>(planes + lds_off[i]) = hi;
+      *reinterpret_cast<u32x4*>(planes + PLANE + lds_off[i]) = mid;
+      *reinterpret_cast<u32x4*>(planes + 2 * PLANE + lds_off[i]) = lo;
     }
   }
 };
