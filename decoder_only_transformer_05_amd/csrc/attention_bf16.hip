@@ -606,7 +606,7 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dq_x6_kernel(float* __restr
 #pragma unroll
     for (int i = 0; i < SCH; i++) {
       const int f = tid + X6_NT * i, row = f / (TILE / 8), c = f % (TILE / 8);
-      const int q64 = 2 * qt + row / TILE;  // the 64-query tile of this row
+      const int q64 = (X6_QT / TILE) * qt + row / TILE;  // the 64-query tile of this row
       if (q64 < nq64 && kt <= q64) {  // the causal tile (q64, kt) exists
         const float* p = sbase + tri_index(q64, kt) * (TILE * TILE) + (row % TILE) * TILE + 8 * c;
         sv[i][0] = *reinterpret_cast<const f32x4*>(p);
