@@ -741,6 +741,8 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
   }
 
   float* C = g.C + (long long)z * g.c_zstride;
+  // GELU: the pre-activation and the activation are written in two passes over the tile
+  constexpr int EPI1 = EPI == EPI_GELU ? EPI_STORE : EPI;
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
     const int m = m0 + wm0 + 32 * tm + r;
@@ -751,10 +753,38 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
       for (int q = 0; q < 4; q++) {
         const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
         if (n >= g.N) continue;
-        epilogue4<EPI>(g, C, m, n,
-                       f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
-                             acc[tm][tn][4 * q + 3]});
+        epilogue4<EPI1>(g, C, m, n,
+                        f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                              acc[tm][tn][4 * q + 3]});
       }
+  }
+  if (EPI == EPI_GELU) {
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) {
+      const int m = m0 + wm0 + 32 * tm + r;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
+          if (n >= g.N) continue;
+          const long long off = (long long)m * g.ldc + n;
+          const int cnt = min(4, g.N - n);
+          f32x4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                     acc[tm][tn][4 * q + 3]};
+          if (g.bias) {
+            if (cnt == 4) v += *reinterpret_cast<const f32x4*>(g.bias + n);
+            else
+              for (int j = 0; j < cnt; j++) v[j] += g.bias[n + j];
+          }
+          if (cnt == 4 && (g.ldc & 3) == 0)
+            *reinterpret_cast<f32x4*>(g.C2 + off) =
+                f32x4{gelu_fwd(v[0]), gelu_fwd(v[1]), gelu_fwd(v[2]), gelu_fwd(v[3])};
+          else
+            for (int j = 0; j < cnt; j++) g.C2[off + j] = gelu_fwd(v[j]);
+        }
+    }
   }
 }
 
