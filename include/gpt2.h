@@ -208,7 +208,10 @@ int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* do
 
 /* [llm.c] 1.7, [np60] Attention: qkv (B,T,3C) -> out (B,T,C), causal softmax attention
  * per head with scale 1/sqrt(C/NH). lse (B,NH,T) receives each query row's log-sum-exp
- * of the scaled scores (what the backward needs instead of the (B,NH,T,T) matrices). */
+ * of the scaled scores (what the backward needs instead of the (B,NH,T,T) matrices).
+ * For head sizes that are multiples of 8 the forward and the dQ products of the backward
+ * are formed as six bf16 MFMA products of exact three-way operand splits (fp32 accuracy,
+ * as for the GEMMs); GPT2_ATTN_F32_PRODUCTS=fp32 selects fp32 MFMA products. */
 int gpt2_k_attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C,
                              int NH, void* stream);
 
