@@ -45,7 +45,12 @@ enum {
 };
 
 /* Arithmetic of the training step.
- * GPT2_DTYPE_FP32: every tensor fp32, GEMMs on fp32 MFMA.
+ * GPT2_DTYPE_FP32: every tensor fp32. Each fp32 product of the GEMMs, of the attention
+ *   forward and of the attention dQ is formed as six bf16 MFMA products of an exact
+ *   three-way bf16 split of its operands (within 2^-23 of the exact product) with fp32
+ *   accumulation; the attention dK/dV products run on fp32 MFMA (see
+ *   gpt2_k_matmul_forward and gpt2_k_attention_forward for the switches that select fp32
+ *   MFMA products throughout).
  * GPT2_DTYPE_BF16: mixed precision, the extension to "fp16 or lower" that the llm.c
  *   overview names as a next step: GEMM operands (a bf16 copy of the weights, refreshed
  *   by every gpt2_set_params and gpt2_adamw_step) and all activation tensors are stored
@@ -277,7 +282,11 @@ int gpt2_k_layernorm_backward_bf16(float* dx, uint16_t* dx_copy, float* dw, floa
                                    const float* mean, const float* rstd, int N, int C,
                                    void* stream);
 
-/* [llm.c] 1.7, 1.8 with bf16 qkv, out, dout and dqkv (lse fp32); products in fp32. */
+/* [llm.c] 1.7, 1.8 with bf16 qkv, out, dout and dqkv (lse fp32). For head sizes that are
+ * multiples of 8 (at most 128) the products run on bf16 MFMA with fp32 accumulation: Q, K,
+ * V and dO enter as stored, the probabilities P and the score gradients dS are rounded to
+ * bf16 where they become MFMA operands, and the softmax statistics stay fp32. Other head
+ * sizes widen the bf16 tensors and multiply on fp32 MFMA. */
 int gpt2_k_attention_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
                                   int C, int NH, void* stream);
 int gpt2_k_attention_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,

@@ -55,6 +55,8 @@ _SIGS = {
     "oracle_num_params": (_i64, [_int, _int, _int, _int]),
     "oracle_gpt2_step": (_int, [_int, _int, _int, _int, _int, _D, _I, _I, _int, _int, _D, _D,
                                 _D, _D]),
+    "oracle_gpt2_step_mag": (_int, [_int, _int, _int, _int, _int, _D, _I, _I, _int, _int, _D,
+                                    _D, _D, _D, _D, _D]),
 }
 
 
@@ -244,11 +246,13 @@ def num_params(L, C, V, maxT) -> int:
 
 
 def gpt2_step(shape, params, tokens, targets=None, want_logits=False, want_grads=True,
-              want_losses=False):
+              want_losses=False, want_mags=False):
     """Forward (+ backward) of the whole model. ``shape`` has L, C, H, V, maxT.
 
     Returns a dict with ``loss`` (float; -1 without targets) and, on request, ``logits``
-    (B,T,V), ``losses`` (B,T) and ``grads`` (flat, fp64).
+    (B,T,V), ``losses`` (B,T) and ``grads`` (flat, fp64). ``want_mags`` adds the magnitude
+    envelopes used by the parity gates: ``grad_mag`` (flat, with grads) and, with logits,
+    ``logit_mag`` (B,T,V) -- each entry's final sum taken over absolute values.
     """
     tokens = i32(tokens)
     B, T = tokens.shape
@@ -260,9 +264,11 @@ def gpt2_step(shape, params, tokens, targets=None, want_logits=False, want_grads
     logits = np.zeros((B, T, shape.V)) if want_logits else None
     losses = np.zeros((B, T)) if (want_losses and tg is not None) else None
     grads = np.zeros(P) if (want_grads and tg is not None) else None
-    rc = lib().oracle_gpt2_step(shape.L, shape.C, shape.H, shape.V, shape.maxT, _d(params),
-                                _i(tokens), _i(tg), B, T, _d(loss), _d(losses), _d(logits),
-                                _d(grads))
+    gmag = np.zeros(P) if (want_mags and grads is not None) else None
+    lmag = np.zeros((B, T, shape.V)) if (want_mags and want_logits) else None
+    rc = lib().oracle_gpt2_step_mag(shape.L, shape.C, shape.H, shape.V, shape.maxT, _d(params),
+                                    _i(tokens), _i(tg), B, T, _d(loss), _d(losses), _d(logits),
+                                    _d(grads), _d(gmag), _d(lmag))
     if rc:
         raise ValueError("oracle_gpt2_step rejected its arguments")
     out = {"loss": float(loss[0])}
@@ -272,4 +278,8 @@ def gpt2_step(shape, params, tokens, targets=None, want_logits=False, want_grads
         out["losses"] = losses
     if grads is not None:
         out["grads"] = grads
+    if gmag is not None:
+        out["grad_mag"] = gmag
+    if lmag is not None:
+        out["logit_mag"] = lmag
     return out

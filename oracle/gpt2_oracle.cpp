@@ -79,31 +79,32 @@ void layernorm_forward(double* out, double* mean, double* rstd, const double* x,
   }
 }
 
-// [llm.c] 1.4 layernorm_backward (accumulates into dx, dw, db). With n = (x-mean)*rstd and
-// g = w*dout: dx += rstd * (g - mean(g) - n * mean(g*n)); dw += n*dout; db += dout.
+// [llm.c] 1.4 layernorm_backward (accumulates into dx, dw, db), written from the
+// derivative of y = n * w + b with n = (x - mean) * rstd. Per row, with g = w * dout (the
+// gradient reaching n), the Jacobian of n with respect to x is rstd * (I - 1/C - n n^T / C),
+// so dx = rstd * (g - <g> - n <g n>), where <.> is the mean over the C channels. The
+// affine parameters collect dw = sum over rows of n * dout and db = sum of dout.
 void layernorm_backward(double* dx, double* dw, double* db, const double* dout,
                         const double* x, const double* w, const double* mean,
                         const double* rstd, int64_t N, int C) {
+  std::vector<double> nrm(C), g(C);
   for (int64_t r = 0; r < N; r++) {
-    const double* d = dout + r * C;
+    const double* dy = dout + r * C;
     const double* xr = x + r * C;
-    double m = mean[r], s = rstd[r];
-    double gmean = 0.0, gnmean = 0.0;
     for (int c = 0; c < C; c++) {
-      double n = (xr[c] - m) * s;
-      double g = w[c] * d[c];
-      gmean += g;
-      gnmean += g * n;
+      nrm[c] = (xr[c] - mean[r]) * rstd[r];
+      g[c] = w[c] * dy[c];
     }
-    gmean /= C;
-    gnmean /= C;
+    double g_avg = 0.0, gn_avg = 0.0;
+    for (int c = 0; c < C; c++) g_avg += g[c];
+    for (int c = 0; c < C; c++) gn_avg += g[c] * nrm[c];
+    g_avg /= C;
+    gn_avg /= C;
     double* dxr = dx + r * C;
+    for (int c = 0; c < C; c++) dxr[c] += rstd[r] * (g[c] - g_avg - nrm[c] * gn_avg);
     for (int c = 0; c < C; c++) {
-      double n = (xr[c] - m) * s;
-      double g = w[c] * d[c];
-      db[c] += d[c];
-      dw[c] += n * d[c];
-      dxr[c] += s * (g - gmean - n * gnmean);
+      dw[c] += nrm[c] * dy[c];
+      db[c] += dy[c];
     }
   }
 }
@@ -277,6 +278,44 @@ double logsumexp(const double* z, int V) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Magnitude envelopes for the parity gates: each parameter gradient is a sum over
+// positions of products; these helpers form the same sums over absolute values, which
+// bound how much rounding (and error in the summed factors) the sum can carry when its
+// terms cancel. They do not take part in the training step itself.
+// ---------------------------------------------------------------------------------------
+
+// linear layer ([llm.c] 1.6): dWmag[o,c] += sum_n |dout[n,o]| |inp[n,c]|,
+// dbmag[o] += sum_n |dout[n,o]| (dbmag may be null)
+void matmul_param_grad_mag(double* dWmag, double* dbmag, const double* dout, const double* inp,
+                           int64_t N, int C, int OC) {
+  const int P = 64;
+  for (int o0 = 0; o0 < OC; o0 += P) {
+    int o1 = o0 + P < OC ? o0 + P : OC;
+    for (int64_t n = 0; n < N; n++) {
+      const double* x = inp + n * C;
+      for (int o = o0; o < o1; o++) {
+        const double dd = std::fabs(dout[n * OC + o]);
+        if (dbmag) dbmag[o] += dd;
+        double* dwr = dWmag + (size_t)o * C;
+        for (int c = 0; c < C; c++) dwr[c] += dd * std::fabs(x[c]);
+      }
+    }
+  }
+}
+
+// LayerNorm affine parameters ([llm.c] 1.4): dwmag[c] += sum |n * dout|, dbmag[c] += sum |dout|
+void layernorm_param_grad_mag(double* dwmag, double* dbmag, const double* dout,
+                              const double* x, const double* mean, const double* rstd,
+                              int64_t N, int C) {
+  for (int64_t r = 0; r < N; r++)
+    for (int c = 0; c < C; c++) {
+      const double dy = dout[r * C + c];
+      dwmag[c] += std::fabs((x[r * C + c] - mean[r]) * rstd[r] * dy);
+      dbmag[c] += std::fabs(dy);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Model layout ([llm.c] 1.16 ParameterTensors, 1.22 sizes): 16 tensors in one flat buffer.
 // ---------------------------------------------------------------------------------------
 struct Sizes {
@@ -438,15 +477,20 @@ int64_t oracle_num_params(int L, int C, int V, int maxT) {
 // 1.25 gpt2_backward). params: flat fp64 in the 16-tensor order. tokens/targets: (B,T).
 // Outputs (each may be null): mean_loss, losses (B*T), logits (B*T*V), grads (flat,
 // overwritten, not accumulated). Returns 0, or 1 for bad shapes/tokens.
-int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params,
-                     const int* tokens, const int* targets, int B, int T, double* mean_loss,
-                     double* losses_out, double* logits_out, double* grads) {
+// grad_mag (flat, like grads) and logit_mag (B*T*V), each optional, receive the sums over
+// absolute values of the final contraction that forms each gradient entry and each logit
+// (see matmul_param_grad_mag); grad_mag needs grads.
+int oracle_gpt2_step_mag(int L, int C, int NH, int V, int maxT, const double* params,
+                         const int* tokens, const int* targets, int B, int T, double* mean_loss,
+                         double* losses_out, double* logits_out, double* grads,
+                         double* grad_mag, double* logit_mag) {
   if (L < 1 || C < 1 || NH < 1 || C % NH || V < 1 || B < 1 || T < 1 || T > maxT) return 1;
   for (int64_t i = 0; i < (int64_t)B * T; i++) {
     if (tokens[i] < 0 || tokens[i] >= V) return 1;
     if (targets && (targets[i] < 0 || targets[i] >= V)) return 1;
   }
   if (grads && !targets) return 1;
+  if (grad_mag && !grads) return 1;
   const Sizes S = param_sizes(L, C, V, maxT);
   const int64_t N = (int64_t)B * T, NC = N * C;
   auto P = [&](int k) { return params + S.off[k]; };
@@ -498,6 +542,12 @@ int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params
   // tied lm_head: logits = lnf . wte^T, no bias ([llm.c] 1.23; [np60] "x @ wte.T")
   matmul_forward(logits.data(), lnf.data(), P(WTE), nullptr, N, C, V);
   if (logits_out) std::memcpy(logits_out, logits.data(), sizeof(double) * N * V);
+  if (logit_mag) {
+    std::vector<double> alnf(NC), awte((size_t)V * C);
+    for (int64_t i = 0; i < NC; i++) alnf[i] = std::fabs(lnf[i]);
+    for (int64_t i = 0; i < (int64_t)V * C; i++) awte[i] = std::fabs(P(WTE)[i]);
+    matmul_forward(logit_mag, alnf.data(), awte.data(), nullptr, N, C, V);
+  }
 
   if (!targets) {
     if (mean_loss) *mean_loss = -1.0;  // [llm.c] 1.23: no targets, no loss
@@ -521,12 +571,20 @@ int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params
                                        N, V);
   std::vector<double> dlnf(NC, 0.0);
   matmul_backward(dlnf.data(), G(WTE), nullptr, dlogits.data(), lnf.data(), P(WTE), N, C, V);
+  double* M = grad_mag;  // envelopes, or null
+  if (M) {
+    std::memset(M, 0, sizeof(double) * S.total);
+    matmul_param_grad_mag(M + S.off[WTE], nullptr, dlogits.data(), lnf.data(), N, C, V);
+  }
   dlogits.clear();
   dlogits.shrink_to_fit();
   // dres holds d(loss)/d(residual stream) entering the layer being processed
   std::vector<double> dres(NC, 0.0);
   layernorm_backward(dres.data(), G(LNFW), G(LNFB), dlnf.data(), xL, P(LNFW), lnfm.data(),
                      lnfr.data(), N, C);
+  if (M)
+    layernorm_param_grad_mag(M + S.off[LNFW], M + S.off[LNFB], dlnf.data(), xL, lnfm.data(),
+                             lnfr.data(), N, C);
   std::vector<double> dfchg(4 * NC), dfch(4 * NC), dln(NC), datty(NC), dqkv(3 * NC);
   for (int l = L - 1; l >= 0; l--) {
     const double* x = l == 0 ? encoded.data() : res3.data() + (l - 1) * NC;
@@ -535,12 +593,23 @@ int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params
     matmul_backward(dfchg.data(), G(FCPROJW) + (int64_t)l * 4 * C * C, G(FCPROJB) + l * C,
                     dres.data(), fchg.data() + l * 4 * NC, P(FCPROJW) + (int64_t)l * 4 * C * C,
                     N, 4 * C, C);
+    if (M)
+      matmul_param_grad_mag(M + S.off[FCPROJW] + (int64_t)l * 4 * C * C,
+                            M + S.off[FCPROJB] + l * C, dres.data(), fchg.data() + l * 4 * NC,
+                            N, 4 * C, C);
     std::fill(dfch.begin(), dfch.end(), 0.0);
     oracle_gelu_backward(dfch.data(), fch.data() + l * 4 * NC, dfchg.data(), 4 * NC);
     std::fill(dln.begin(), dln.end(), 0.0);
     matmul_backward(dln.data(), G(FCW) + (int64_t)l * 4 * C * C, G(FCB) + l * 4 * C,
                     dfch.data(), ln2.data() + l * NC, P(FCW) + (int64_t)l * 4 * C * C, N, C,
                     4 * C);
+    if (M)
+      matmul_param_grad_mag(M + S.off[FCW] + (int64_t)l * 4 * C * C, M + S.off[FCB] + l * 4 * C,
+                            dfch.data(), ln2.data() + l * NC, N, C, 4 * C);
+    if (M)
+      layernorm_param_grad_mag(M + S.off[LN2W] + l * C, M + S.off[LN2B] + l * C, dln.data(),
+                               res2.data() + l * NC, ln2m.data() + l * N, ln2r.data() + l * N,
+                               N, C);
     // dres now also collects the ln2 branch: d residual2 = d residual3 + LN2 backward
     layernorm_backward(dres.data(), G(LN2W) + l * C, G(LN2B) + l * C, dln.data(),
                        res2.data() + l * NC, P(LN2W) + l * C, ln2m.data() + l * N,
@@ -550,6 +619,9 @@ int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params
     matmul_backward(datty.data(), G(ATTPROJW) + (int64_t)l * C * C, G(ATTPROJB) + l * C,
                     dres.data(), atty.data() + l * NC, P(ATTPROJW) + (int64_t)l * C * C, N, C,
                     C);
+    if (M)
+      matmul_param_grad_mag(M + S.off[ATTPROJW] + (int64_t)l * C * C, M + S.off[ATTPROJB] + l * C,
+                            dres.data(), atty.data() + l * NC, N, C, C);
     std::fill(dqkv.begin(), dqkv.end(), 0.0);
     attention_backward(dqkv.data(), datty.data(), qkv.data() + l * 3 * NC,
                        att.data() + (size_t)l * B * NH * T * T, B, T, C, NH);
@@ -557,12 +629,29 @@ int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params
     matmul_backward(dln.data(), G(QKVW) + (int64_t)l * 3 * C * C, G(QKVB) + l * 3 * C,
                     dqkv.data(), ln1.data() + l * NC, P(QKVW) + (int64_t)l * 3 * C * C, N, C,
                     3 * C);
+    if (M) {
+      matmul_param_grad_mag(M + S.off[QKVW] + (int64_t)l * 3 * C * C, M + S.off[QKVB] + l * 3 * C,
+                            dqkv.data(), ln1.data() + l * NC, N, C, 3 * C);
+      layernorm_param_grad_mag(M + S.off[LN1W] + l * C, M + S.off[LN1B] + l * C, dln.data(), x,
+                               ln1m.data() + l * N, ln1r.data() + l * N, N, C);
+    }
     layernorm_backward(dres.data(), G(LN1W) + l * C, G(LN1B) + l * C, dln.data(), x,
                        P(LN1W) + l * C, ln1m.data() + l * N, ln1r.data() + l * N, N, C);
   }
   // dres is now d(loss)/d(encoded); the encoder term adds to the lm_head term of dwte
   encoder_backward(G(WTE), G(WPE), dres.data(), tokens, B, T, C);
+  if (M) {
+    for (int64_t i = 0; i < NC; i++) dres[i] = std::fabs(dres[i]);
+    encoder_backward(M + S.off[WTE], M + S.off[WPE], dres.data(), tokens, B, T, C);
+  }
   return 0;
+}
+
+int oracle_gpt2_step(int L, int C, int NH, int V, int maxT, const double* params,
+                     const int* tokens, const int* targets, int B, int T, double* mean_loss,
+                     double* losses_out, double* logits_out, double* grads) {
+  return oracle_gpt2_step_mag(L, C, NH, V, maxT, params, tokens, targets, B, T, mean_loss,
+                              losses_out, logits_out, grads, nullptr, nullptr);
 }
 
 }  // extern "C"

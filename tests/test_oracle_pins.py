@@ -428,3 +428,67 @@ def test_model_rejects_bad_inputs():
         oracle.gpt2_step(shape, p, tok + shape.V, tok)
     with pytest.raises(ValueError):
         oracle.gpt2_step(shape, p, np.zeros((1, shape.maxT + 1), dtype=np.int32))
+
+
+# ---------------------------------------------------------------------------------------
+# Magnitude envelopes (sums over absolute values) that the parity gates scale with
+# ---------------------------------------------------------------------------------------
+def test_envelopes_of_a_single_position_equal_the_gradient_magnitude():
+    """With one position every parameter-gradient entry is a single product (or a single
+    term), so its envelope is exactly |g| -- except the wte row of the input token, which
+    sums the lm_head term and the embedding term (|a| + |b| >= |a + b|)."""
+    shape = SMALL
+    p = _params(shape, 31, bias_std=0.3)
+    tok = np.array([[7]], np.int32)
+    tgt = np.array([[12]], np.int32)
+    r = oracle.gpt2_step(shape, p, tok, tgt, want_mags=True)
+    g, m = r["grads"], r["grad_mag"]
+    sizes = synth.param_sizes(shape.L, shape.C, shape.V, shape.maxT)
+    wte_tok = slice(7 * shape.C, 8 * shape.C)
+    exact = np.ones(g.size, bool)
+    exact[wte_tok] = False
+    np.testing.assert_array_equal(m[exact], np.abs(g[exact]))
+    assert np.all(m[wte_tok] >= np.abs(g[wte_tok]))
+    # every tensor's envelope is non-trivial where its gradient is
+    off = 0
+    for name, n in zip(synth.PARAM_NAMES, sizes):
+        assert (m[off:off + n] > 0).any() == (g[off:off + n] != 0).any(), name
+        off += n
+
+
+def test_envelopes_of_a_batch_are_the_mean_of_its_rows():
+    """Rows of one position each: the batch gradient is the mean of the row gradients, and
+    scaling the loss by 1/B (a power of two) scales every backward product exactly, so the
+    batch envelope equals the mean of the row envelopes; the row envelopes are |g_row|
+    (previous test), so this also fixes the batch envelope from gradients alone."""
+    shape = SMALL
+    p = _params(shape, 32, bias_std=0.3)
+    tok = np.array([[3], [9], [3], [20]], np.int32)
+    tgt = np.array([[5], [1], [40], [5]], np.int32)
+    full = oracle.gpt2_step(shape, p, tok, tgt, want_mags=True)
+    rows = [oracle.gpt2_step(shape, p, tok[b:b + 1], tgt[b:b + 1], want_mags=True)
+            for b in range(4)]
+    np.testing.assert_allclose(full["grad_mag"], sum(r["grad_mag"] for r in rows) / 4,
+                               rtol=1e-14, atol=0)
+    # and for longer rows the envelope bounds the gradient (triangle inequality)
+    tok, tgt = synth.batch(33, 3, 11, shape.V, mode="independent")
+    r = oracle.gpt2_step(shape, p, tok, tgt, want_mags=True)
+    assert np.all(r["grad_mag"] >= np.abs(r["grads"]) * (1 - 1e-12))
+    assert (r["grad_mag"] > np.abs(r["grads"]) * (1 + 1e-6)).mean() > 0.5
+
+
+def test_logit_envelope_equals_logits_when_no_term_cancels():
+    """lnf = its bias when the final gain is 0; with a positive bias and |wte| every product
+    of the lm_head sum is non-negative, so the envelope equals the logits themselves."""
+    shape = SMALL
+    p = _params(shape, 34, bias_std=0.3)
+    prm = _unflatten(shape, p)
+    prm["wte"][:] = np.abs(prm["wte"])
+    prm["lnfw"][:] = 0.0
+    prm["lnfb"][:] = np.linspace(0.1, 2.0, shape.C)
+    tok, tgt = synth.batch(35, 2, 6, shape.V, mode="independent")
+    r = oracle.gpt2_step(shape, p, tok, tgt, want_logits=True, want_mags=True)
+    np.testing.assert_array_equal(r["logit_mag"], r["logits"])
+    p2 = _params(shape, 36, bias_std=0.3)
+    r2 = oracle.gpt2_step(shape, p2, tok, tgt, want_logits=True, want_mags=True)
+    assert np.all(r2["logit_mag"] >= np.abs(r2["logits"]) * (1 - 1e-12))
