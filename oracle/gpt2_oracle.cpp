@@ -109,12 +109,111 @@ void layernorm_backward(double* dx, double* dw, double* db, const double* dout,
   }
 }
 
+// Accumulating product used by the linear layers: for i < mi, j < nj,
+//   out[i*ldo + j] += sum over k = 0, 1, ..., K-1 of a(i, k) * b(k, j),
+// with a(i, k) = a[i*sa_i + k*sa_k] and b(k, j) = b[k*sb_k + j] (each |.| when ABS).
+// Every output adds its K terms one at a time in ascending k, starting from its current
+// value: the result is that of the plain triple loop. The outputs of a block (up to 4 x 8)
+// are kept in registers while k runs, which only changes how fast this goes.
+template <bool ABS>
+inline double mag_or_value(double x) { return ABS ? std::fabs(x) : x; }
+
+template <bool ABS, int MI, int NJ>
+void block_product_acc(double* out, int64_t ldo, const double* a, int64_t sa_i, int64_t sa_k,
+                       const double* b, int64_t sb_k, int64_t K) {
+  double acc[MI][NJ];
+  for (int i = 0; i < MI; i++)
+    for (int j = 0; j < NJ; j++) acc[i][j] = out[i * ldo + j];
+  for (int64_t k = 0; k < K; k++) {
+    const double* bk = b + k * sb_k;
+    for (int i = 0; i < MI; i++) {
+      const double ai = mag_or_value<ABS>(a[i * sa_i + k * sa_k]);
+      for (int j = 0; j < NJ; j++) acc[i][j] += ai * mag_or_value<ABS>(bk[j]);
+    }
+  }
+  for (int i = 0; i < MI; i++)
+    for (int j = 0; j < NJ; j++) out[i * ldo + j] = acc[i][j];
+}
+
+// The 4 x 8 block with the accumulators held as eight 4-wide vectors (GCC vector
+// extensions: element-wise IEEE multiply and add, so the same operations as above).
+typedef double f64x4 __attribute__((vector_size(32)));
+typedef long long i64x4 __attribute__((vector_size(32)));
+template <bool ABS>
+inline f64x4 load4(const double* p) {
+  f64x4 v;
+  std::memcpy(&v, p, sizeof(v));
+  if (ABS) {
+    i64x4 bits = (i64x4)v & (i64x4){INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX};
+    v = (f64x4)bits;
+  }
+  return v;
+}
+template <bool ABS>
+void block_product_acc_4x8(double* out, int64_t ldo, const double* a, int64_t sa_i,
+                           int64_t sa_k, const double* b, int64_t sb_k, int64_t K) {
+  f64x4 c00 = load4<false>(out), c01 = load4<false>(out + 4);
+  f64x4 c10 = load4<false>(out + ldo), c11 = load4<false>(out + ldo + 4);
+  f64x4 c20 = load4<false>(out + 2 * ldo), c21 = load4<false>(out + 2 * ldo + 4);
+  f64x4 c30 = load4<false>(out + 3 * ldo), c31 = load4<false>(out + 3 * ldo + 4);
+  for (int64_t k = 0; k < K; k++) {
+    const f64x4 b0 = load4<ABS>(b + k * sb_k), b1 = load4<ABS>(b + k * sb_k + 4);
+    const double* ak = a + k * sa_k;
+    const double a0 = mag_or_value<ABS>(ak[0]), a1 = mag_or_value<ABS>(ak[sa_i]),
+                 a2 = mag_or_value<ABS>(ak[2 * sa_i]), a3 = mag_or_value<ABS>(ak[3 * sa_i]);
+    c00 += a0 * b0;
+    c01 += a0 * b1;
+    c10 += a1 * b0;
+    c11 += a1 * b1;
+    c20 += a2 * b0;
+    c21 += a2 * b1;
+    c30 += a3 * b0;
+    c31 += a3 * b1;
+  }
+  std::memcpy(out, &c00, 32);
+  std::memcpy(out + 4, &c01, 32);
+  std::memcpy(out + ldo, &c10, 32);
+  std::memcpy(out + ldo + 4, &c11, 32);
+  std::memcpy(out + 2 * ldo, &c20, 32);
+  std::memcpy(out + 2 * ldo + 4, &c21, 32);
+  std::memcpy(out + 3 * ldo, &c30, 32);
+  std::memcpy(out + 3 * ldo + 4, &c31, 32);
+}
+
+// the same over an M x N output. k runs in ascending chunks of 256, and within a chunk the
+// outputs are visited in panels of 256 columns, blocks of 4 x 8 and single entries at the
+// edges, so the operand pieces in use stay in cache. Each output still receives its terms
+// in ascending k (a chunk continues from the value the previous chunk stored).
+template <bool ABS>
+void product_acc(double* out, int64_t ldo, const double* a, int64_t sa_i, int64_t sa_k,
+                 const double* b, int64_t sb_k, int64_t M, int64_t N, int64_t K) {
+  const int64_t KC = 256, NP = 256;
+  const int64_t M4 = M / 4 * 4;
+  for (int64_t k0 = 0; k0 < K; k0 += KC) {
+    const int64_t kn = K - k0 < KC ? K - k0 : KC;
+    const double* ak = a + k0 * sa_k;
+    const double* bk = b + k0 * sb_k;
+    for (int64_t j0 = 0; j0 < N; j0 += NP) {
+      const int64_t j1 = N - j0 < NP ? N : j0 + NP;
+      const int64_t j8 = j0 + (j1 - j0) / 8 * 8;
+      for (int64_t i = 0; i < M4; i += 4)
+        for (int64_t j = j0; j < j8; j += 8)
+          block_product_acc_4x8<ABS>(out + i * ldo + j, ldo, ak + i * sa_i, sa_i, sa_k,
+                                     bk + j, sb_k, kn);
+      for (int64_t i = 0; i < M; i++)
+        for (int64_t j = (i < M4 ? j8 : j0); j < j1; j++)
+          block_product_acc<ABS, 1, 1>(out + i * ldo + j, ldo, ak + i * sa_i, sa_i, sa_k,
+                                       bk + j, sb_k, kn);
+    }
+  }
+}
+
 // [llm.c] 1.5 matmul_forward, [np60] Linear: out(N,OC) = inp(N,C) . W(OC,C)^T + bias(OC).
 // W is stored (OC, C) row-major as on the llm.c page (the NumPy page stores [in, out];
 // same function). bias may be null. Each output is bias + sum over c in ascending order.
 void matmul_forward(double* out, const double* inp, const double* W, const double* bias,
                     int64_t N, int C, int OC) {
-  // W^T, so the innermost loop runs over contiguous output columns.
+  // W^T, so a block of outputs reads contiguous columns
   std::vector<double> WT((size_t)C * OC);
   for (int o = 0; o < OC; o++)
     for (int c = 0; c < C; c++) WT[(size_t)c * OC + o] = W[(size_t)o * C + c];
@@ -122,50 +221,22 @@ void matmul_forward(double* out, const double* inp, const double* W, const doubl
     double* orow = out + n * OC;
     for (int o = 0; o < OC; o++) orow[o] = bias ? bias[o] : 0.0;
   }
-  // column panels only keep a slice of W^T in cache; no sum is split or reordered
-  const int P = 512;
-  for (int o0 = 0; o0 < OC; o0 += P) {
-    int o1 = o0 + P < OC ? o0 + P : OC;
-    for (int64_t n = 0; n < N; n++) {
-      const double* x = inp + n * C;
-      double* orow = out + n * OC;
-      for (int c = 0; c < C; c++) {
-        const double xc = x[c];
-        const double* wt = WT.data() + (size_t)c * OC;
-        for (int o = o0; o < o1; o++) orow[o] += xc * wt[o];
-      }
-    }
-  }
+  // out[n][o] += sum_c inp[n][c] * WT[c][o]
+  product_acc<false>(out, OC, inp, C, 1, WT.data(), OC, N, OC, C);
 }
 
 // [llm.c] 1.6 matmul_backward (accumulates): dinp += dout . W; dW += dout^T . inp;
 // dbias += column sums of dout. dbias may be null. Every sum runs in ascending order of
-// its index (o for dinp, n for dW and dbias); the row panels below only keep a slice of W
-// (or of dW) in cache and do not split or reorder any sum.
+// its index (o for dinp, n for dW and dbias).
 void matmul_backward(double* dinp, double* dW, double* dbias, const double* dout,
                      const double* inp, const double* W, int64_t N, int C, int OC) {
-  const int P = 64;
-  for (int o0 = 0; o0 < OC; o0 += P) {
-    int o1 = o0 + P < OC ? o0 + P : OC;
-    for (int64_t n = 0; n < N; n++) {
-      const double* d = dout + n * OC;
-      double* di = dinp + n * C;
-      for (int o = o0; o < o1; o++) {
-        const double dd = d[o];
-        const double* wr = W + (size_t)o * C;
-        for (int c = 0; c < C; c++) di[c] += dd * wr[c];
-      }
-    }
-    for (int64_t n = 0; n < N; n++) {
-      const double* x = inp + n * C;
-      for (int o = o0; o < o1; o++) {
-        const double dd = dout[n * OC + o];
-        if (dbias) dbias[o] += dd;
-        double* dwr = dW + (size_t)o * C;
-        for (int c = 0; c < C; c++) dwr[c] += dd * x[c];
-      }
-    }
-  }
+  // dinp[n][c] += sum_o dout[n][o] * W[o][c]
+  product_acc<false>(dinp, C, dout, OC, 1, W, C, N, C, OC);
+  // dW[o][c] += sum_n dout[n][o] * inp[n][c]
+  product_acc<false>(dW, C, dout, 1, OC, inp, C, OC, C, N);
+  if (dbias)
+    for (int64_t n = 0; n < N; n++)
+      for (int o = 0; o < OC; o++) dbias[o] += dout[n * OC + o];
 }
 
 // [llm.c] 1.7 attention_forward, [np60] Attention + causal mask.
@@ -181,13 +252,22 @@ void attention_forward(double* out, double* att, const double* qkv, int B, int T
   const int64_t C3 = 3 * (int64_t)C;
   const double scale = 1.0 / std::sqrt((double)hs);
   std::vector<double> s(T), p(T);
+  // one head's q, k, v rows gathered into contiguous (T, hs) arrays (a copy, for locality)
+  std::vector<double> Q((size_t)T * hs), K((size_t)T * hs), Vv((size_t)T * hs);
   for (int b = 0; b < B; b++)
-    for (int h = 0; h < NH; h++)
+    for (int h = 0; h < NH; h++) {
+      for (int t = 0; t < T; t++)
+        for (int i = 0; i < hs; i++) {
+          const double* row = qkv + ((int64_t)b * T + t) * C3 + h * hs + i;
+          Q[(size_t)t * hs + i] = row[0];
+          K[(size_t)t * hs + i] = row[C];
+          Vv[(size_t)t * hs + i] = row[2 * C];
+        }
       for (int t = 0; t < T; t++) {
-        const double* q = qkv + ((int64_t)b * T + t) * C3 + h * hs;
+        const double* q = Q.data() + (size_t)t * hs;
         double mx = -INFINITY;
         for (int t2 = 0; t2 <= t; t2++) {
-          const double* k = qkv + ((int64_t)b * T + t2) * C3 + C + h * hs;
+          const double* k = K.data() + (size_t)t2 * hs;
           double dot = 0.0;
           for (int i = 0; i < hs; i++) dot += q[i] * k[i];
           s[t2] = dot * scale;
@@ -202,7 +282,7 @@ void attention_forward(double* out, double* att, const double* qkv, int B, int T
         double* o = out + ((int64_t)b * T + t) * C + h * hs;
         for (int i = 0; i < hs; i++) o[i] = 0.0;
         for (int t2 = 0; t2 <= t; t2++) {
-          const double* v = qkv + ((int64_t)b * T + t2) * C3 + 2 * C + h * hs;
+          const double* v = Vv.data() + (size_t)t2 * hs;
           for (int i = 0; i < hs; i++) o[i] += p[t2] * v[i];
         }
         if (att) {
@@ -210,6 +290,7 @@ void attention_forward(double* out, double* att, const double* qkv, int B, int T
           for (int t2 = 0; t2 < T; t2++) a[t2] = t2 <= t ? p[t2] : 0.0;
         }
       }
+    }
 }
 
 // [llm.c] 1.8 attention_backward (accumulates into dqkv), with the softmax Jacobian
@@ -223,17 +304,32 @@ void attention_backward(double* dqkv, const double* dout, const double* qkv, con
   const int64_t C3 = 3 * (int64_t)C;
   const double scale = 1.0 / std::sqrt((double)hs);
   std::vector<double> datt(T), dpre(T);
+  // one head's q, k, v and their gradients in contiguous (T, hs) arrays (gathered from and
+  // written back to qkv / dqkv, so every accumulation continues from dqkv's contents)
+  const size_t TH = (size_t)T * hs;
+  std::vector<double> Q(TH), K(TH), Vv(TH), dQ(TH), dK(TH), dV(TH);
   for (int b = 0; b < B; b++)
-    for (int h = 0; h < NH; h++)
+    for (int h = 0; h < NH; h++) {
+      for (int t = 0; t < T; t++)
+        for (int i = 0; i < hs; i++) {
+          const int64_t r = ((int64_t)b * T + t) * C3 + h * hs + i;
+          const size_t j = (size_t)t * hs + i;
+          Q[j] = qkv[r];
+          K[j] = qkv[r + C];
+          Vv[j] = qkv[r + 2 * C];
+          dQ[j] = dqkv[r];
+          dK[j] = dqkv[r + C];
+          dV[j] = dqkv[r + 2 * C];
+        }
       for (int t = 0; t < T; t++) {
         const double* a = att + (((int64_t)b * NH + h) * T + t) * T;
         const double* dO = dout + ((int64_t)b * T + t) * C + h * hs;
-        const double* q = qkv + ((int64_t)b * T + t) * C3 + h * hs;
-        double* dq = dqkv + ((int64_t)b * T + t) * C3 + h * hs;
+        const double* q = Q.data() + (size_t)t * hs;
+        double* dq = dQ.data() + (size_t)t * hs;
         double dot_ad = 0.0;
         for (int t2 = 0; t2 <= t; t2++) {
-          const double* v = qkv + ((int64_t)b * T + t2) * C3 + 2 * C + h * hs;
-          double* dv = dqkv + ((int64_t)b * T + t2) * C3 + 2 * C + h * hs;
+          const double* v = Vv.data() + (size_t)t2 * hs;
+          double* dv = dV.data() + (size_t)t2 * hs;
           double acc = 0.0;
           for (int i = 0; i < hs; i++) {
             acc += v[i] * dO[i];
@@ -244,14 +340,23 @@ void attention_backward(double* dqkv, const double* dout, const double* qkv, con
         }
         for (int t2 = 0; t2 <= t; t2++) dpre[t2] = a[t2] * (datt[t2] - dot_ad);
         for (int t2 = 0; t2 <= t; t2++) {
-          const double* k = qkv + ((int64_t)b * T + t2) * C3 + C + h * hs;
-          double* dk = dqkv + ((int64_t)b * T + t2) * C3 + C + h * hs;
+          const double* k = K.data() + (size_t)t2 * hs;
+          double* dk = dK.data() + (size_t)t2 * hs;
           for (int i = 0; i < hs; i++) {
             dq[i] += scale * dpre[t2] * k[i];
             dk[i] += scale * dpre[t2] * q[i];
           }
         }
       }
+      for (int t = 0; t < T; t++)
+        for (int i = 0; i < hs; i++) {
+          const int64_t r = ((int64_t)b * T + t) * C3 + h * hs + i;
+          const size_t j = (size_t)t * hs + i;
+          dqkv[r] = dQ[j];
+          dqkv[r + C] = dK[j];
+          dqkv[r + 2 * C] = dV[j];
+        }
+    }
 }
 
 // [llm.c] 1.9 gelu_forward, [np60] GELU: the tanh approximation
@@ -288,19 +393,10 @@ double logsumexp(const double* z, int V) {
 // dbmag[o] += sum_n |dout[n,o]| (dbmag may be null)
 void matmul_param_grad_mag(double* dWmag, double* dbmag, const double* dout, const double* inp,
                            int64_t N, int C, int OC) {
-  const int P = 64;
-  for (int o0 = 0; o0 < OC; o0 += P) {
-    int o1 = o0 + P < OC ? o0 + P : OC;
-    for (int64_t n = 0; n < N; n++) {
-      const double* x = inp + n * C;
-      for (int o = o0; o < o1; o++) {
-        const double dd = std::fabs(dout[n * OC + o]);
-        if (dbmag) dbmag[o] += dd;
-        double* dwr = dWmag + (size_t)o * C;
-        for (int c = 0; c < C; c++) dwr[c] += dd * std::fabs(x[c]);
-      }
-    }
-  }
+  product_acc<true>(dWmag, C, dout, 1, OC, inp, C, OC, C, N);
+  if (dbmag)
+    for (int64_t n = 0; n < N; n++)
+      for (int o = 0; o < OC; o++) dbmag[o] += std::fabs(dout[n * OC + o]);
 }
 
 // LayerNorm affine parameters ([llm.c] 1.4): dwmag[c] += sum |n * dout|, dbmag[c] += sum |dout|

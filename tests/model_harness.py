@@ -1,0 +1,169 @@
+"""Whole-model parity harness: the oracle run as independent single-row instances, and the
+gates applied to losses, logits, gradients and the AdamW update.
+
+The batch decomposition: every row has T positions and the loss is the mean over all B*T
+of them, so the batch gradient is the mean of the row gradients (d loss / d theta =
+sum_b (1/B) d row_loss_b / d theta), and the batch envelope is the mean of the row
+envelopes. Rows run as single-threaded oracle calls in parallel threads (the oracle
+releases the GIL); their results are summed in fp64 in row order.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import sys
+import time
+
+import numpy as np
+
+import oracle
+from decoder_only_transformer_05_amd import synth
+from parity import (PARAM_ATOL, assert_bf16_close, assert_loss, assert_losses,
+                    assert_model_close)
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def progress(msg: str):
+    """A progress line on the real stderr (pytest captures sys.stderr)."""
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", file=sys.__stderr__, flush=True)
+
+
+def oracle_workers(B: int) -> int:
+    return max(1, min(B, int(os.environ.get("GPT2_ORACLE_WORKERS", "16"))))
+
+
+def oracle_batch(shape, p64, tok, tgt, want_logits=False, want_grads=True, row_hook=None,
+                 workers=None, label=""):
+    """Oracle forward (+ backward) of a batch as single-row runs.
+
+    Returns loss (mean over rows), losses (B,T) and, with want_grads, grads and grad_mag
+    (fp64 means over rows, summed in row order). ``row_hook(b, r)`` runs in the worker
+    thread as soon as row b is done (it gets logits and logit_mag when want_logits) and
+    may raise; the logits are dropped after it."""
+    B = tok.shape[0]
+
+    def row(b):
+        t0 = time.time()
+        r = oracle.gpt2_step(shape, p64, tok[b:b + 1], tgt[b:b + 1], want_logits=want_logits,
+                             want_grads=want_grads, want_losses=True, want_mags=True)
+        if row_hook is not None:
+            row_hook(b, r)
+        r.pop("logits", None)
+        r.pop("logit_mag", None)
+        progress(f"{label} oracle row {b} done in {time.time() - t0:.1f} s")
+        return r
+
+    out = {"losses": np.zeros(tok.shape)}
+    loss = 0.0
+    with cf.ThreadPoolExecutor(max_workers=workers or oracle_workers(B)) as ex:
+        futs = [ex.submit(row, b) for b in range(B)]
+        for b in range(B):
+            r = futs[b].result()
+            futs[b] = None
+            loss += r["loss"]
+            out["losses"][b] = r["losses"][0]
+            if want_grads:
+                if b == 0:
+                    out["grads"], out["grad_mag"] = r["grads"], r["grad_mag"]
+                else:
+                    out["grads"] += r["grads"]
+                    out["grad_mag"] += r["grad_mag"]
+            del r
+    out["loss"] = loss / B
+    if want_grads:
+        out["grads"] /= B
+        out["grad_mag"] /= B
+    return out
+
+
+def tensor_slices(shape):
+    sizes = synth.param_sizes(shape.L, shape.C, shape.V, shape.maxT)
+    off = 0
+    for name, n in zip(synth.PARAM_NAMES, sizes):
+        yield name, slice(off, off + n)
+        off += n
+
+
+def compare_grads(shape, got, ref, mag, BT, label=""):
+    """The fp32 model-level gate for each of the 16 parameter-gradient tensors (every
+    gradient entry is a sum over the B*T positions)."""
+    for name, sl in tensor_slices(shape):
+        s = assert_model_close(f"{label} grad {name}", got[sl], ref[sl], mag[sl], K=BT)
+        progress(f"{label} grad {name}: normwise {s['normwise']:.2e} max/scale "
+                 f"{s['max_rel_to_scale']:.2e} entry {s['entry_ratio']:.2f} literal "
+                 f"{s['violations']}/{s['n']}")
+
+
+def compare_grads_bf16(shape, got, ref, mag, r=5e-2, label=""):
+    worst = 0.0
+    for name, sl in tensor_slices(shape):
+        s = assert_bf16_close(f"{label} grad {name}", got[sl], ref[sl], mag[sl], r)
+        progress(f"{label} grad {name}: normwise {s['normwise']:.2e} entry "
+                 f"{s['entry_ratio']:.2f}")
+        worst = max(worst, s["normwise"])
+    return worst
+
+
+def grad_bound(ref, mag, BT):
+    """Per-entry gradient tolerance of the fp32 gate (parity.assert_model_close)."""
+    from parity import ATOL, E_IN_F32, RTOL, U32
+    return RTOL * np.abs(ref) + ATOL + (4.0 * np.sqrt(BT) * U32 + E_IN_F32) * mag
+
+
+def check_adamw_rule(params_after, params_before, grads, m_before, v_before, t, label=""):
+    """The update the GPU applied equals the oracle's AdamW rule (fp64) fed the GPU's own
+    fp32 gradient and moments, for every parameter."""
+    rp, _, _ = oracle.adamw(params_before, grads, m_before, v_before, HP["lr"], HP["beta1"],
+                            HP["beta2"], HP["eps"], HP["weight_decay"], t)
+    err = float(np.abs(params_after - rp).max())
+    progress(f"{label} AdamW rule (GPU gradients, step {t}): max |dp| {err:.2e}")
+    assert err <= 1e-6, err
+    return rp
+
+
+def check_adamw_first_step(params_after, p0, g_ref, gbound, label="", max_frac=0.3):
+    """First AdamW step against the oracle's own fp64 gradient, every parameter.
+
+    At t = 1 each parameter moves by lr * g / (|g| + eps) (+ weight decay). Where |g| is
+    near eps that map is steep (slope eps / (|g| + eps)^2), so a gradient within its
+    tolerance gbound can move the parameter by up to lr * eps * gbound / (max(|g| - gbound,
+    0) + eps)^2 (mean value theorem). Each parameter must lie within 1e-5 of the oracle's
+    update, or within 1e-6 plus that propagated amount where it is larger; the count of the
+    latter is reported and bounded."""
+    rp, _, _ = oracle.adamw(p0, g_ref, np.zeros(p0.size), np.zeros(p0.size), HP["lr"],
+                            HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], 1)
+    eps = HP["eps"]
+    dist = np.maximum(np.abs(g_ref) - gbound, 0.0) + eps
+    prop = 1e-6 + HP["lr"] * eps * gbound / (dist * dist)
+    bound = np.maximum(PARAM_ATOL, prop)
+    err = np.abs(params_after - rp)
+    n_prop = int((prop > PARAM_ATOL).sum())
+    inside = err <= PARAM_ATOL
+    progress(f"{label} AdamW vs oracle gradients: max |dp| {float(err.max()):.2e}; "
+             f"{int((~inside).sum())} of {err.size} beyond 1e-5; {n_prop} parameters "
+             f"({n_prop / err.size:.2%}) whose gradient tolerance allows more than 1e-5")
+    bad = err > bound
+    assert not bad.any(), (int(bad.sum()), float((err / bound).max()))
+    assert n_prop <= max_frac * err.size, n_prop
+    return rp
+
+
+def check_losses_and_logits_row(b, got_logits_row, r, C, label="", bf16=None):
+    """Row b's logits against the oracle row (fp32 gate, or the bf16 gate with r=bf16)."""
+    if bf16:
+        s = assert_bf16_close(f"{label} logits row {b}", got_logits_row, r["logits"][0],
+                              r["logit_mag"][0], bf16)
+        progress(f"{label} logits row {b}: normwise {s['normwise']:.2e} entry "
+                 f"{s['entry_ratio']:.2f}")
+    else:
+        s = assert_model_close(f"{label} logits row {b}", got_logits_row, r["logits"][0],
+                               r["logit_mag"][0], K=C)
+        progress(f"{label} logits row {b}: normwise {s['normwise']:.2e} max/scale "
+                 f"{s['max_rel_to_scale']:.2e} entry {s['entry_ratio']:.2f} literal "
+                 f"{s['violations']}/{s['n']}")
+
+
+__all__ = ["HP", "progress", "oracle_batch", "compare_grads", "compare_grads_bf16",
+           "grad_bound", "check_adamw_rule", "check_adamw_first_step",
+           "check_losses_and_logits_row", "assert_loss", "assert_losses", "tensor_slices"]
