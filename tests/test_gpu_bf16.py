@@ -261,31 +261,20 @@ def test_encoder_cast_adamw_bf16_rounding():
 # ---------------------------------------------------------------------------------------
 # whole steps in GPT2_DTYPE_BF16
 # ---------------------------------------------------------------------------------------
-HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+from model_harness import (HP, check_losses_and_logits_row, compare_grads_bf16,  # noqa: E402
+                           oracle_batch, progress)
+from parity import assert_bf16_close  # noqa: E402
+
 LOSS_RTOL_BF16 = 2e-2
 
 
-def normwise(a, o):
-    a, o = np.asarray(a, np.float64).ravel(), np.asarray(o, np.float64).ravel()
-    return float(np.linalg.norm(a - o) / max(np.linalg.norm(o), 1e-300))
-
-
-def check_grads(shape, got, ref, bound):
-    sizes = synth.param_sizes(shape.L, shape.C, shape.V, shape.maxT)
-    off, worst = 0, 0.0
-    for name, n in zip(synth.PARAM_NAMES, sizes):
-        e = normwise(got[off:off + n], ref[off:off + n])
-        print(f"grad {name}: normwise {e:.2e}")
-        worst = max(worst, e)
-        off += n
-    assert worst <= bound, worst
-
-
-def bf16_steps(shape, seed, B, T, steps, mode, scale_residual, grad_bound):
+def bf16_steps(shape, seed, B, T, steps, mode, scale_residual, grad_r):
+    """Each step is compared from the GPU's own fp32 master parameters, so it measures that
+    step's bf16 arithmetic alone; logits and every gradient tensor pass the bf16 gate
+    (normwise and per entry against the oracle's envelope)."""
     p0 = synth.init_params(shape, seed, scale_residual)
     m = gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, dtype="bf16")
     m.set_params(p0)
-    rp = p0.astype(np.float64)
     rm, rv = np.zeros(p0.size), np.zeros(p0.size)
     for step in range(steps):
         tok, tgt = synth.batch(seed, B, T, shape.V, step=step, mode=mode)
@@ -297,15 +286,14 @@ def bf16_steps(shape, seed, B, T, steps, mode, scale_residual, grad_bound):
         grads = m.get_grads()
         got_p = m.get_params()
         m.adamw_step(t=step + 1, **HP)
-        # the oracle steps from the GPU's own fp32 master parameters, so each step's
-        # comparison measures that step's bf16 arithmetic alone
-        ref = oracle.gpt2_step(shape, got_p.astype(np.float64), tok, tgt, want_logits=True)
+        ref = oracle.gpt2_step(shape, got_p.astype(np.float64), tok, tgt, want_logits=True,
+                               want_mags=True)
         rel = abs(loss - ref["loss"]) / abs(ref["loss"])
+        s = assert_bf16_close("logits", logits, ref["logits"], ref["logit_mag"], 2e-2)
         print(f"step {step}: loss {loss:.6f} oracle {ref['loss']:.6f} rel {rel:.2e} "
-              f"logits normwise {normwise(logits, ref['logits']):.2e}")
+              f"logits {s}")
         assert rel <= LOSS_RTOL_BF16
-        assert normwise(logits, ref["logits"]) <= 2e-2
-        check_grads(shape, grads, ref["grads"], grad_bound)
+        compare_grads_bf16(shape, grads, ref["grads"], ref["grad_mag"], grad_r)
         # AdamW on the GPU's own gradients, checked against the oracle's rule
         rp, rm, rv = oracle.adamw(got_p.astype(np.float64), grads, rm, rv, HP["lr"], HP["beta1"],
                                   HP["beta2"], HP["eps"], HP["weight_decay"], step + 1)
@@ -323,64 +311,71 @@ def test_bf16_small_multilayer_ragged_two_steps():
     bf16_steps(shape, 4243, 3, 100, 2, "stream", True, 5e-2)
 
 
-def test_bf16_774m_b8_t1024_sampled_and_properties():
+@pytest.mark.timeout(600)
+def test_bf16_774m_b8_t1024_full_rows_and_properties():
+    """The 774M bf16 workload in the benchmark's launch configuration: two full T=1024 rows
+    (per-position losses and logits) against single-row oracle forwards, the mean loss
+    near its value at init, bitwise determinism and a finite step."""
     w = synth.WORKLOADS["gpt2_774m_b8_t1024_bf16"]
     shape = w.shape
     B, T, V = w.B, w.T, shape.V
     p0 = synth.init_params(shape, w.seed, w.scale_residual)
     tok, tgt = synth.batch(w.seed, B, T, V, mode=w.token_mode)
-    rows, P = [0, 7], 32
-    with cf.ThreadPoolExecutor(max_workers=2) as ex:
-        # the losses of positions 0..31 of a row depend only on that row's first 32 tokens;
-        # the oracle runs them on the host while the GPU works
-        p64 = p0.astype(np.float64)
-        refs = [ex.submit(oracle.gpt2_step, shape, p64, tok[r:r + 1, :P], tgt[r:r + 1, :P],
-                          want_losses=True, want_grads=False) for r in rows]
-        m = gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, B, T, dtype="bf16")
-        m.set_params(p0)
-        m.zero_grad()
-        loss = m.forward(dev(tok), dev(tgt))
-        losses = torch.empty((B, T), device="cuda")
-        m.get_losses(losses)
-        got_losses = losses[rows, :P].cpu().numpy()
-        m.backward()
-        g1 = torch.empty(m.num_params, device="cuda")
-        m.get_grads(g1)
-        m.zero_grad()
-        assert m.forward(dev(tok), dev(tgt)) == loss  # deterministic
-        m.backward()
-        g2 = torch.empty(m.num_params, device="cuda")
-        m.get_grads(g2)
-        assert torch.equal(g1, g2)
-        assert bool(torch.isfinite(g1).all())
-        m.adamw_step(t=1, **HP)
-        assert np.isfinite(m.get_params()).all()
-        m.close()
-        ref_losses = np.concatenate([f.result()["losses"] for f in refs])
-    rel = np.abs(got_losses - ref_losses) / np.abs(ref_losses)
-    print("sampled per-position loss rel error: max", rel.max(), "mean", rel.mean())
+    rows = [0, 7]
+    m = gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, B, T, dtype="bf16")
+    m.set_params(p0)
+    m.zero_grad()
+    loss = m.forward(dev(tok), dev(tgt))
+    losses = torch.empty((B, T), device="cuda")
+    m.get_losses(losses)
+    got_losses = losses[rows].cpu().numpy()
+    logits = torch.empty((B, T, V), device="cuda")
+    m.get_logits(logits)
+    got_logits = logits[rows].cpu().numpy()
+    del logits
+    m.backward()
+    g1 = torch.empty(m.num_params, device="cuda")
+    m.get_grads(g1)
+    m.zero_grad()
+    assert m.forward(dev(tok), dev(tgt)) == loss  # deterministic
+    m.backward()
+    g2 = torch.empty(m.num_params, device="cuda")
+    m.get_grads(g2)
+    assert torch.equal(g1, g2)
+    assert bool(torch.isfinite(g1).all())
+    del g1, g2
+    m.adamw_step(t=1, **HP)
+    assert np.isfinite(m.get_params()).all()
+    m.close()
+
+    ref = oracle_batch(shape, p0.astype(np.float64), tok[rows], tgt[rows], want_logits=True,
+                       want_grads=False, label="774M bf16 rows",
+                       row_hook=lambda i, r: check_losses_and_logits_row(
+                           rows[i], got_logits[i], r, shape.C, label="774M bf16:", bf16=2e-2))
+    rel = np.abs(got_losses - ref["losses"]) / np.abs(ref["losses"])
+    progress(f"774M bf16 rows {rows}: per-position loss rel error max {rel.max():.2e} mean "
+             f"{rel.mean():.2e}")
     assert rel.max() <= LOSS_RTOL_BF16
     expect = math.log(V) + shape.C * 0.02 ** 2 / 2
     assert abs(loss - expect) < 0.05, (loss, expect)
 
 
+@pytest.mark.timeout(600)
 def test_bf16_774m_b1_t32_gradients():
     """Every parameter gradient of one B1 T32 step of the 774M shape against the oracle."""
     w = synth.WORKLOADS["gpt2_774m_b8_t1024_bf16"]
     shape = w.shape
     p0 = synth.init_params(shape, w.seed, w.scale_residual)
     tok, tgt = synth.batch(w.seed, 1, 32, shape.V, mode=w.token_mode)
-    with cf.ThreadPoolExecutor(max_workers=1) as ex:
-        fut = ex.submit(oracle.gpt2_step, shape, p0.astype(np.float64), tok, tgt)
-        m = gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, dtype="bf16")
-        m.set_params(p0)
-        m.zero_grad()
-        loss = m.forward(dev(tok), dev(tgt))
-        m.backward()
-        grads = m.get_grads()
-        m.close()
-        ref = fut.result()
+    m = gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, dtype="bf16")
+    m.set_params(p0)
+    m.zero_grad()
+    loss = m.forward(dev(tok), dev(tgt))
+    m.backward()
+    grads = m.get_grads()
+    m.close()
+    ref = oracle.gpt2_step(shape, p0.astype(np.float64), tok, tgt, want_mags=True)
     rel = abs(loss - ref["loss"]) / abs(ref["loss"])
     print(f"loss {loss:.6f} oracle {ref['loss']:.6f} rel {rel:.2e}")
     assert rel <= LOSS_RTOL_BF16
-    check_grads(shape, grads, ref["grads"], 5e-2)
+    compare_grads_bf16(shape, grads, ref["grads"], ref["grad_mag"], 5e-2, label="774M B1 T32")
