@@ -60,6 +60,8 @@ SIGNATURES = {
                                      _vp]),
     "gpt2_k_matmul_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
                                       _vp]),
+    "gpt2_k_matmul_backward_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int,
+                                              _int, _int, _vp]),
     "gpt2_k_attention_forward": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "gpt2_k_attention_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "gpt2_k_crossentropy_forward": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
@@ -313,6 +315,13 @@ def k_matmul_backward(dinp, dW, dbias, dout, inp, W, N, C, OC, gelu_pre=None, ld
     _check(lib().gpt2_k_matmul_backward(_ptr(dinp), _ptr(dW), _ptr(dbias), _ptr(dout), _ptr(inp),
                                         _ptr(W), _ptr(gelu_pre), N, C, OC,
                                         OC if ld_dout is None else ld_dout, current_stream()))
+
+
+def k_matmul_backward_noalloc(dinp, dW, dbias, dout, inp, W, N, C, OC, gelu_pre=None,
+                              ld_dout=None):
+    _check(lib().gpt2_k_matmul_backward_noalloc(
+        _ptr(dinp), _ptr(dW), _ptr(dbias), _ptr(dout), _ptr(inp), _ptr(W), _ptr(gelu_pre), N, C,
+        OC, OC if ld_dout is None else ld_dout, current_stream()))
 
 
 def k_attention_forward(out, lse, qkv, B, T, C, NH):

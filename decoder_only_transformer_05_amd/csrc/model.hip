@@ -953,13 +953,18 @@ int gpt2_k_matmul_forward(float* out, float* out2, const float* resid, const flo
   return gemm(g, nullptr, 0, as_stream(stream));
 }
 
-int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* dout,
-                           const float* inp, const float* W, const float* gelu_pre, int N, int C,
-                           int OC, int ld_dout, void* stream) {
+// The two GEMMs of gpt2_k_matmul_backward for caller buffers, and the floats of scratch
+// they need (split-K partials and column-sum partials).
+struct MatmulBackward {
+  Gemm d, w;
+  size_t ws = 0;
+};
+static int plan_matmul_backward(MatmulBackward& mb, float* dinp, float* dW, float* dbias,
+                                const float* dout, const float* inp, const float* W,
+                                const float* gelu_pre, int N, int C, int OC, int ld_dout) {
   if (!dout || N < 1 || C < 1 || OC < 1 || ld_dout < OC || (dinp && !W) || (dW && !inp))
     return fail(nullptr, GPT2_ERR_ARG, "bad argument");
-  hipStream_t s = as_stream(stream);
-  Gemm d;
+  Gemm& d = mb.d;
   d.A = dout;
   d.lda = ld_dout;
   d.B = W;
@@ -974,7 +979,7 @@ int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* do
     d.epi = EPI_GELU_BWD;
     d.R = gelu_pre;
   }
-  Gemm w;
+  Gemm& w = mb.w;
   w.A = dout;
   w.lda = ld_dout;
   w.a_trans = true;
@@ -989,17 +994,77 @@ int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* do
   w.epi = EPI_ACCUM;
   w.colsum = dbias;  // bias gradient fused into the weight-gradient GEMM
   size_t ws = std::max(dinp ? gemm_workspace_floats(d) : 0, dW ? gemm_workspace_floats(w) : 0);
-  ws = std::max(ws, colsum_partial_floats(N, OC));
-  float* buf = nullptr;
-  if (hipMalloc(&buf, (ws ? ws : 1) * sizeof(float)) != hipSuccess)
-    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  mb.ws = std::max(ws, colsum_partial_floats(N, OC));
+  return 0;
+}
+static int run_matmul_backward(const MatmulBackward& mb, float* dbias, int N, int OC,
+                               int ld_dout, float* buf, hipStream_t s) {
   int rc = 0;
-  if (dinp) rc = gemm(d, buf, ws, s);
-  if (!rc && dW) rc = gemm(w, buf, ws, s);
-  if (!rc && dbias && !dW) rc = colsum_accumulate(dbias, dout, N, OC, ld_dout, buf, s);
+  if (mb.d.C) rc = gemm(mb.d, buf, mb.ws, s);
+  if (!rc && mb.w.C) rc = gemm(mb.w, buf, mb.ws, s);
+  if (!rc && dbias && !mb.w.C) rc = colsum_accumulate(dbias, mb.d.A, N, OC, ld_dout, buf, s);
+  return rc;
+}
+
+int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* dout,
+                           const float* inp, const float* W, const float* gelu_pre, int N, int C,
+                           int OC, int ld_dout, void* stream) {
+  MatmulBackward mb;
+  KCHK(plan_matmul_backward(mb, dinp, dW, dbias, dout, inp, W, gelu_pre, N, C, OC, ld_dout));
+  hipStream_t s = as_stream(stream);
+  float* buf = nullptr;
+  if (hipMalloc(&buf, (mb.ws ? mb.ws : 1) * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = run_matmul_backward(mb, dbias, N, OC, ld_dout, buf, s);
   (void)hipStreamSynchronize(s);
   (void)hipFree(buf);
   return rc;
+}
+
+// ----- allocation-free matmul backward ----------------------------------------------------
+// Scratch of gpt2_k_matmul_backward_noalloc: one static array per device, which each GPU the
+// library runs on holds until the process ends. In host code `noalloc_scratch` names a host
+// stand-in, not device memory, so kernels only ever receive the device address that
+// hipGetSymbolAddress returns for the current device (looked up once per device).
+static __device__ __align__(256) float noalloc_scratch[GPT2_NOALLOC_SCRATCH_FLOATS];
+static std::mutex g_noalloc_mu;
+static float* g_noalloc_ptr[64];
+
+static int noalloc_scratch_ptr(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(nullptr, GPT2_ERR_HIP, "gpt2_k_matmul_backward_noalloc: no current device");
+  if (dev >= 64)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_k_matmul_backward_noalloc: device %d >= 64", dev);
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, GPT2_ERR_HIP, "hipGetSymbolAddress(noalloc_scratch) failed: %s",
+                  hipGetErrorString(e));
+    g_noalloc_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_noalloc_ptr[dev];
+  return 0;
+}
+
+int gpt2_k_matmul_backward_noalloc(float* dinp, float* dW, float* dbias, const float* dout,
+                                   const float* inp, const float* W, const float* gelu_pre, int N,
+                                   int C, int OC, int ld_dout, void* stream) {
+  MatmulBackward mb;
+  KCHK(plan_matmul_backward(mb, dinp, dW, dbias, dout, inp, W, gelu_pre, N, C, OC, ld_dout));
+  if (mb.ws > (size_t)GPT2_NOALLOC_SCRATCH_FLOATS)
+    return fail(nullptr, GPT2_ERR_ARG,
+                "gpt2_k_matmul_backward_noalloc: this problem needs %zu floats of scratch, "
+                "above the %d the allocation-free entry point holds (use "
+                "gpt2_k_matmul_backward)",
+                mb.ws, (int)GPT2_NOALLOC_SCRATCH_FLOATS);
+  float* scratch = nullptr;
+  KCHK(noalloc_scratch_ptr(&scratch));
+  // every scratch location a call reads (split partials, column-sum partials) is written
+  // earlier in the same call, so nothing needs clearing between calls
+  return run_matmul_backward(mb, dbias, N, OC, ld_dout, scratch, as_stream(stream));
 }
 
 int gpt2_k_attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C,

@@ -211,6 +211,22 @@ int gpt2_k_matmul_backward(float* dinp, float* dW, float* dbias, const float* do
                            const float* inp, const float* W, const float* gelu_pre, int N,
                            int C, int OC, int ld_dout, void* stream);
 
+/* Allocation-free form of gpt2_k_matmul_backward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results as gpt2_k_matmul_backward; its scratch
+ * (split-K partial products and bias-gradient partial sums) is a static device array of
+ * GPT2_NOALLOC_SCRATCH_FLOATS floats (68 MiB) that each GPU the library runs on holds
+ * until the process ends, located once per device at the first call on it. It calls no
+ * allocator and never waits for the stream. A problem whose plan needs more scratch (for
+ * example the tied lm_head weight gradient at B*T = 16384) is rejected with GPT2_ERR_ARG
+ * before anything is enqueued. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one device (two streams, or two host threads) race and must not be issued;
+ * calls in order on one stream are safe. */
+#define GPT2_NOALLOC_SCRATCH_FLOATS (17 << 20)
+int gpt2_k_matmul_backward_noalloc(float* dinp, float* dW, float* dbias, const float* dout,
+                                   const float* inp, const float* W, const float* gelu_pre,
+                                   int N, int C, int OC, int ld_dout, void* stream);
+
 /* [llm.c] 1.7, [np60] Attention: qkv (B,T,3C) -> out (B,T,C), causal softmax attention
  * per head with scale 1/sqrt(C/NH). lse (B,NH,T) receives each query row's log-sum-exp
  * of the scaled scores (what the backward needs instead of the (B,NH,T,T) matrices).
