@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgpt2_mi355x.so")
 
 GPT2_OK = 0
 ERRORS = {-1: "GPT2_ERR_ARG", -2: "GPT2_ERR_SHAPE", -3: "GPT2_ERR_TOKEN", -4: "GPT2_ERR_STATE",
-          -5: "GPT2_ERR_OOM", -6: "GPT2_ERR_HIP"}
+          -5: "GPT2_ERR_OOM", -6: "GPT2_ERR_HIP", -7: "GPT2_ERR_IO"}
 
 _vp = ctypes.c_void_p
 _int = ctypes.c_int
@@ -33,6 +33,24 @@ SIGNATURES = {
     "gpt2_set_stream": (_int, [_vp, _vp]),
     "gpt2_synchronize": (_int, [_vp]),
     "gpt2_num_params": (_sz, [_vp]),
+    "gpt2_get_config": (_int, [_vp, ctypes.POINTER(_int)]),
+    "gpt2_checkpoint_info": (_int, [ctypes.c_char_p, ctypes.POINTER(_int), ctypes.POINTER(_int),
+                                    ctypes.POINTER(_int), ctypes.POINTER(_int),
+                                    ctypes.POINTER(_int), ctypes.POINTER(_sz)]),
+    "gpt2_checkpoint_read": (_int, [ctypes.c_char_p, _vp, _sz]),
+    "gpt2_checkpoint_write": (_int, [ctypes.c_char_p, _int, _int, _int, _int, _int, _vp]),
+    "gpt2_build_from_checkpoint": (_int, [ctypes.POINTER(_vp), ctypes.c_char_p, _int, _int, _int,
+                                          _vp]),
+    "gpt2_save_checkpoint": (_int, [_vp, ctypes.c_char_p]),
+    "gpt2_dataloader_init": (_int, [ctypes.POINTER(_vp), ctypes.c_char_p, _int, _int]),
+    "gpt2_dataloader_num_batches": (_int, [_vp]),
+    "gpt2_dataloader_reset": (_int, [_vp]),
+    "gpt2_dataloader_next_batch": (_int, [_vp, _vp, _vp, _int, _vp]),
+    "gpt2_dataloader_free": (None, [_vp]),
+    "gpt2_random_u32": (ctypes.c_uint32, [ctypes.POINTER(ctypes.c_uint64)]),
+    "gpt2_random_f32": (_f, [ctypes.POINTER(ctypes.c_uint64)]),
+    "gpt2_sample": (_int, [_vp, _int, _int, _f, ctypes.POINTER(ctypes.c_int32)]),
+    "gpt2_k_sample_mult": (_int, [_vp, _vp, _int, _f, _vp]),
     "gpt2_param_layout": (_int, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "gpt2_set_params": (_int, [_vp, _vp, _int]),
     "gpt2_get_params": (_int, [_vp, _vp, _int]),
@@ -70,6 +88,13 @@ SIGNATURES = {
     "gpt2_k_adamw": (_int, [_vp, _vp, _vp, _vp, _sz, _f, _f, _f, _f, _f, _int, _vp]),
     "gpt2_k_gemm_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
                                 _int, _int, _int, _int, _vp]),
+    "gpt2_k_gemm_f16": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                               _int, _int, _int, _int, _vp]),
+    "gpt2_k_attention_forward_f16": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "gpt2_k_attention_backward_f16": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                                             _vp]),
+    "gpt2_set_loss_scale": (_int, [_vp, _f, _int]),
+    "gpt2_get_loss_scale": (_int, [_vp, ctypes.POINTER(_f), ctypes.POINTER(_int)]),
     "gpt2_k_encoder_forward_bf16": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
                                            _vp]),
     "gpt2_k_layernorm_forward_bf16": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp]),
@@ -85,7 +110,7 @@ SIGNATURES = {
     "gpt2_k_cast_bf16": (_int, [_vp, _vp, _sz, _vp]),
 }
 
-DTYPES = {"fp32": 0, "bf16": 1}
+DTYPES = {"fp32": 0, "bf16": 1, "fp16": 2}
 
 _lib = None
 
@@ -133,7 +158,8 @@ def _ptr(t, kind: str = "f32") -> int | None:
     if t is None:
         return None
     torch = _torch()
-    want = {"f32": torch.float32, "i32": torch.int32, "bf16": torch.bfloat16}[kind]
+    want = {"f32": torch.float32, "i32": torch.int32, "bf16": torch.bfloat16,
+            "f16": torch.float16}[kind]
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
     if t.dtype != want:
@@ -151,6 +177,10 @@ def _hptr(t) -> int | None:
     return _ptr(t, "bf16")
 
 
+def _f16ptr(t) -> int | None:
+    return _ptr(t, "f16")
+
+
 def _host_or_device(buf):
     """(pointer, is_device) for a torch tensor or a contiguous numpy float32 array."""
     if isinstance(buf, np.ndarray):
@@ -163,18 +193,133 @@ def _host_or_device(buf):
     return buf.data_ptr(), 1 if buf.is_cuda else 0
 
 
+def _path(p) -> bytes:
+    return os.fsencode(p)
+
+
+def checkpoint_info(path) -> dict:
+    """Configuration and parameter count of a checkpoint file (no GPU needed)."""
+    v = [_int() for _ in range(5)]
+    n = _sz()
+    _check(lib().gpt2_checkpoint_info(_path(path), *[ctypes.byref(x) for x in v],
+                                      ctypes.byref(n)))
+    return {"maxT": v[0].value, "V": v[1].value, "L": v[2].value, "H": v[3].value,
+            "C": v[4].value, "num_params": n.value}
+
+
+def checkpoint_read(path) -> np.ndarray:
+    n = checkpoint_info(path)["num_params"]
+    out = np.empty(n, np.float32)
+    _check(lib().gpt2_checkpoint_read(_path(path), out.ctypes.data, n))
+    return out
+
+
+def checkpoint_write(path, params, L, C, H, V, maxT):
+    p = np.ascontiguousarray(params, dtype=np.float32)
+    _check(lib().gpt2_checkpoint_write(_path(path), maxT, V, L, H, C, p.ctypes.data))
+
+
+class Rng:
+    """The pages' xorshift* generator (random_u32 / random_f32) on a host 64-bit state."""
+
+    def __init__(self, seed: int):
+        self.state = ctypes.c_uint64(seed)
+
+    def u32(self) -> int:
+        return int(lib().gpt2_random_u32(ctypes.byref(self.state)))
+
+    def f32(self) -> float:
+        return float(lib().gpt2_random_f32(ctypes.byref(self.state)))
+
+
+class DataLoader:
+    """Batches of (inputs, targets) from a file of int32 tokens (include/gpt2.h)."""
+
+    def __init__(self, path, B: int, T: int):
+        h = _vp()
+        _check(lib().gpt2_dataloader_init(ctypes.byref(h), _path(path), B, T))
+        self.h, self.B, self.T = h, B, T
+        self.num_batches = int(lib().gpt2_dataloader_num_batches(h))
+
+    def reset(self):
+        _check(lib().gpt2_dataloader_reset(self.h))
+
+    def next_batch(self, inputs=None, targets=None):
+        """Fills int32 (B,T) host arrays or device tensors (new host arrays if None)."""
+        if inputs is None:
+            inputs = np.empty((self.B, self.T), np.int32)
+            targets = np.empty((self.B, self.T), np.int32)
+        if isinstance(inputs, np.ndarray):
+            for a in (inputs, targets):
+                if a.dtype != np.int32 or not a.flags.c_contiguous or a.size != self.B * self.T:
+                    raise ValueError("expected contiguous int32 arrays of B*T tokens")
+            _check(lib().gpt2_dataloader_next_batch(self.h, inputs.ctypes.data,
+                                                    targets.ctypes.data, 0, None))
+        else:
+            for a in (inputs, targets):
+                if a.numel() != self.B * self.T:
+                    raise ValueError("expected tensors of B*T tokens")
+            _check(lib().gpt2_dataloader_next_batch(self.h, _iptr(inputs), _iptr(targets), 1,
+                                                    current_stream()))
+        return inputs, targets
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().gpt2_dataloader_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class GPT2:
     """One model on the current device (see include/gpt2.h for the semantics)."""
 
     def __init__(self, L: int, C: int, H: int, V: int, maxT: int, B: int = 0, T: int = 0,
-                 stream: int | None = None, dtype: str = "fp32"):
-        h = _vp()
-        st = current_stream() if stream is None else stream
-        _check(lib().gpt2_build_ex(ctypes.byref(h), L, C, H, V, maxT, DTYPES[dtype], B, T, st))
+                 stream: int | None = None, dtype: str = "fp32", _handle=None):
+        if _handle is None:
+            h = _vp()
+            st = current_stream() if stream is None else stream
+            _check(lib().gpt2_build_ex(ctypes.byref(h), L, C, H, V, maxT, DTYPES[dtype], B, T,
+                                       st))
+        else:
+            h = _handle
         self.h = h
         self.dtype = dtype
         self.L, self.C, self.H, self.V, self.maxT = L, C, H, V, maxT
         self.num_params = int(lib().gpt2_num_params(h))
+
+    @classmethod
+    def from_checkpoint(cls, path, B: int = 0, T: int = 0, stream: int | None = None,
+                        dtype: str = "fp32"):
+        h = _vp()
+        st = current_stream() if stream is None else stream
+        _check(lib().gpt2_build_from_checkpoint(ctypes.byref(h), _path(path), DTYPES[dtype], B, T,
+                                                st))
+        cfg = (_int * 5)()
+        _check(lib().gpt2_get_config(h, cfg))
+        L, C, H, V, maxT = list(cfg)
+        return cls(L, C, H, V, maxT, dtype=dtype, _handle=h)
+
+    def save_checkpoint(self, path):
+        self._c(lib().gpt2_save_checkpoint(self.h, _path(path)))
+
+    def set_loss_scale(self, scale: float, growth_interval: int = 2000):
+        self._c(lib().gpt2_set_loss_scale(self.h, scale, growth_interval))
+
+    def get_loss_scale(self):
+        """(scale, last step skipped) -- fp16 models; others report (1.0, False)."""
+        sc, sk = _f(), _int()
+        self._c(lib().gpt2_get_loss_scale(self.h, ctypes.byref(sc), ctypes.byref(sk)))
+        return float(sc.value), bool(sk.value)
+
+    def sample(self, b: int, t: int, coin: float) -> int:
+        tok = ctypes.c_int32()
+        self._c(lib().gpt2_sample(self.h, b, t, coin, ctypes.byref(tok)))
+        return int(tok.value)
 
     def close(self):
         if getattr(self, "h", None):
@@ -345,6 +490,10 @@ def k_crossentropy_backward(logits, lse, targets, dloss, N, V, ld):
                                               ld, current_stream()))
 
 
+def k_sample_mult(token, logits, V, coin):
+    _check(lib().gpt2_k_sample_mult(_iptr(token), _ptr(logits), V, coin, current_stream()))
+
+
 def k_mean(out, x, n):
     _check(lib().gpt2_k_mean(_ptr(out), _ptr(x), n, current_stream()))
 
@@ -362,6 +511,26 @@ def k_gemm_bf16(C, A, B, M, N, K, lda, ldb, ldc, a_trans=False, b_trans=False, e
     _check(lib().gpt2_k_gemm_bf16(c_ptr, _hptr(C2), _hptr(R), _hptr(A), _hptr(B), _ptr(bias),
                                   _ptr(colsum), M, N, K, lda, ldb, ldc, int(a_trans),
                                   int(b_trans), epilogue, current_stream()))
+
+
+def k_gemm_f16(C, A, B, M, N, K, lda, ldb, ldc, a_trans=False, b_trans=False, epilogue=0,
+               bias=None, C2=None, R=None, colsum=None):
+    """C (fp16, or fp32 for epilogue 3) = op(A) . op(B) with the fused epilogue."""
+    c_ptr = _ptr(C) if epilogue == 3 else _f16ptr(C)
+    _check(lib().gpt2_k_gemm_f16(c_ptr, _f16ptr(C2), _f16ptr(R), _f16ptr(A), _f16ptr(B),
+                                 _ptr(bias), _ptr(colsum), M, N, K, lda, ldb, ldc, int(a_trans),
+                                 int(b_trans), epilogue, current_stream()))
+
+
+def k_attention_forward_f16(out, lse, qkv, B, T, C, NH):
+    _check(lib().gpt2_k_attention_forward_f16(_f16ptr(out), _ptr(lse), _f16ptr(qkv), B, T, C, NH,
+                                              current_stream()))
+
+
+def k_attention_backward_f16(dqkv, dout, qkv, out, lse, B, T, C, NH):
+    _check(lib().gpt2_k_attention_backward_f16(_f16ptr(dqkv), _f16ptr(dout), _f16ptr(qkv),
+                                               _f16ptr(out), _ptr(lse), B, T, C, NH,
+                                               current_stream()))
 
 
 def k_encoder_forward_bf16(out, tok, wte, wpe, B, T, C, V, err_flag=None):

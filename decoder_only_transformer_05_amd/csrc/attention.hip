@@ -26,6 +26,8 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gpt2 {
@@ -570,6 +572,11 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_kernel(TS* __restrict__ dqkv
   }
 }
 
+template <typename TS>
+constexpr bool is_f16() {
+  return std::is_same<TS, f16_t>::value;
+}
+
 bool check_shape(int B, int T, int C, int NH, int* hsp) {
   if (B < 1 || T < 1 || C < 1 || NH < 1 || C % NH) return false;
   const int hs = C / NH;
@@ -608,7 +615,8 @@ int attention_forward_t(TS* out, float* lse, const TS* qkv, int B, int T, int C,
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   const double tri = (double)T * (T + 1) / 2.0;  // causal (query, key) pairs per head
   const double es = sizeof(TS);
-  ProfScope ps(sizeof(TS) == 4 ? "attn_fwd_kernel" : "attn_fwd_bf16_kernel",
+  ProfScope ps(sizeof(TS) == 4 ? "attn_fwd_kernel" : is_f16<TS>() ? "attn_fwd_f16_kernel"
+                                                                   : "attn_fwd_bf16_kernel",
                4.0 * B * NH * hs * tri,
                es * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
   if (hsp == 64 && hs == 64 && launch_fwd_direct(grid, stream, out, lse, qkv, T, C, NH, hs, scale_log2)) {
@@ -634,7 +642,9 @@ int rowdot_t(float* D, const TS* dout, const TS* out, int B, int T, int C, int N
   const int hs = C / NH;
   const long long rows = (long long)B * NH * T;
   const double BTC = (double)B * T * C;
-  ProfScope ps(sizeof(TS) == 4 ? "attn_bwd_rowdot_kernel" : "attn_bwd_rowdot_bf16_kernel",
+  ProfScope ps(sizeof(TS) == 4   ? "attn_bwd_rowdot_kernel"
+               : is_f16<TS>() ? "attn_bwd_rowdot_f16_kernel"
+                              : "attn_bwd_rowdot_bf16_kernel",
                2.0 * BTC, (double)sizeof(TS) * 2.0 * BTC + 4.0 * rows, stream);
   const long long n4 = (long long)B * T * (C / 4);
   const unsigned blocks = (unsigned)((n4 + 255) / 256);
@@ -682,7 +692,8 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
   if (rc) return rc;
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
-    ProfScope ps(f32 ? "attn_bwd_dkdv_kernel" : "attn_bwd_dkdv_bf16_kernel",
+    ProfScope ps(f32 ? "attn_bwd_dkdv_kernel"
+                     : is_f16<TS>() ? "attn_bwd_dkdv_f16_kernel" : "attn_bwd_dkdv_bf16_kernel",
                  6.0 * B * NH * hs * tri,
                  es * (3.0 * BTC + BTC + 2.0 * BTC) + 4.0 * (2.0 * rows + B * NH * tri), stream);
     const dim3 gk(((T + DK_KEYS - 1) / DK_KEYS) * NH * B);
@@ -696,7 +707,9 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
                                    stream);
     if (rq) return rq;
   } else {  // dQ = dS K
-    ProfScope ps(f32 ? "attn_bwd_dq_kernel" : "attn_bwd_dq_bf16_kernel", 2.0 * B * NH * hs * tri,
+    ProfScope ps(f32 ? "attn_bwd_dq_kernel"
+                     : is_f16<TS>() ? "attn_bwd_dq_f16_kernel" : "attn_bwd_dq_bf16_kernel",
+                 2.0 * B * NH * hs * tri,
                  4.0 * B * NH * tri + es * 2.0 * BTC, stream);
     if (hsp == 32) attn_bwd_dq_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
     else if (hsp == 64) attn_bwd_dq_kernel<64, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
@@ -736,6 +749,26 @@ int attention_backward(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv, cons
                               stream);
 }
 int attention_rowdot(float* D, const bf16_t* dout, const bf16_t* out, int B, int T, int C,
+                     int NH, hipStream_t stream) {
+  return rowdot_t(D, dout, out, B, T, C, NH, stream);
+}
+int attention_forward(f16_t* out, float* lse, const f16_t* qkv, int B, int T, int C, int NH,
+                      hipStream_t stream) {
+  // head sizes that are multiples of 8 use the fp16-MFMA kernel; others multiply in fp32
+  if (C % NH == 0 && attention_bf16_mma_supported(C, NH))
+    return attention_forward_f16_mma(out, lse, qkv, B, T, C, NH, stream);
+  return attention_forward_t(out, lse, qkv, B, T, C, NH, stream);
+}
+int attention_backward(f16_t* dqkv, const f16_t* dout, const f16_t* qkv, const f16_t* out,
+                       const float* lse, float* dscratch, float* ds_scratch, int B, int T, int C,
+                       int NH, hipStream_t stream) {
+  if (C % NH == 0 && attention_bf16_mma_supported(C, NH))
+    return attention_backward_f16_mma(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C,
+                                      NH, stream);
+  return attention_backward_t(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C, NH,
+                              stream);
+}
+int attention_rowdot(float* D, const f16_t* dout, const f16_t* out, int B, int T, int C,
                      int NH, hipStream_t stream) {
   return rowdot_t(D, dout, out, B, T, C, NH, stream);
 }

@@ -1,12 +1,14 @@
-// attention_bf16.hip -- causal attention of the mixed-precision step on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// attention_bf16.hip -- causal attention of the mixed-precision steps on 16-bit MFMA
+// (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x16_f16, fp32 accumulation), and the fp32
+// attention forward and dQ with split-operand products on bf16 MFMA.
 //
 // Same computation as attention.hip ("llm.c 的中文注解-20240421" sections 1.7 and 1.8;
 // flash-style: online softmax forward keeping only the row log-sum-exp, recomputation in
-// the backward), for bf16 Q, K, V, O, dO and dQKV. The score products take bf16 operands
-// with exact products and fp32 sums, as in fp32 arithmetic on the same inputs; the
-// probabilities P and the score gradients dS are rounded to bf16 where they become MFMA
-// operands. Softmax statistics, lse, rowsum(dO*O) and the dS scratch tiles stay fp32.
+// the backward), for 16-bit (bf16 or fp16: the storage type TS) Q, K, V, O, dO and dQKV.
+// The score products take 16-bit operands with exact products and fp32 sums, as in fp32
+// arithmetic on the same inputs; the probabilities P and the score gradients dS are rounded
+// to TS where they become MFMA operands. Softmax statistics, lse and rowsum(dO*O) stay
+// fp32; the dS tiles handed from the dK/dV kernel to the dQ kernel are TS.
 //
 // Register layouts. Each lane of the bf16 MFMA supplies 8 consecutive k of one row of A and
 // of one column of B; the result tile gives lane l the column l % 32 and the rows
@@ -18,6 +20,7 @@
 // way, which V^T (and, in the backward, dO^T and Q^T) do by being stored in LDS at the
 // permuted key position kpos() below: each lane's 8 keys are then one 16-byte read.
 #include <cmath>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -32,8 +35,19 @@ constexpr int NTHR = 128;  // two waves of 32 queries (or keys)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// the MFMA of storage format TS on fragments holding its raw 16-bit patterns
+template <typename TS>
+GPT2_DEVICE_INLINE f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (std::is_same<TS, f16_t>::value)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return mfma_bf16(a, b, c);
 }
 
 // position of key k (0..63 within a tile) in a permuted row: groups of 4 keys stay
@@ -43,7 +57,7 @@ GPT2_DEVICE_INLINE int kpos(int k) {
   return (k & ~15) + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
 }
 
-// LDS tiles of ROWS rows x COLS bf16 (COLS a multiple of 8): 16-byte chunk c of row r is
+// LDS tiles of ROWS rows x COLS 16-bit values (COLS a multiple of 8): 16-byte chunk c of row r is
 // stored at chunk c ^ swz(r), which spreads 32 rows read at the same chunk, and rows 8
 // apart written at the same chunk, over the banks.
 template <int COLS>
@@ -52,13 +66,11 @@ GPT2_DEVICE_INLINE int loff(int row, int c) {
   return row * COLS + ((c ^ ((row ^ (row >> 3)) & (CPR - 1))) << 3);
 }
 
-GPT2_DEVICE_INLINE uint32_t pack2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
-
-// 16 bytes (8 bf16) of row t, columns d..d+7 of a strided tensor; rows past the end and
-// columns past hs read as zero (addresses clamped into the tensor)
-GPT2_DEVICE_INLINE u32x4 load8(const bf16_t* base, long long ld, int t, int d, int T, int hs) {
+// 16 bytes (8 values of a 16-bit format) of row t, columns d..d+7 of a strided tensor; rows
+// past the end and columns past hs read as zero (addresses clamped into the tensor)
+template <typename P>
+GPT2_DEVICE_INLINE u32x4 load8(const P* base, long long ld, int t, int d, int T, int hs) {
+  static_assert(sizeof(P) == 2, "16-bit storage");
   const int tc = min(t, T - 1), dc = min(d, hs - 8);
   const u32x4 x = *reinterpret_cast<const u32x4*>(base + (long long)tc * ld + dc);
   return (t < T && d < hs) ? x : u32x4{0u, 0u, 0u, 0u};
@@ -70,15 +82,16 @@ template <int HSP>
 struct RowsTile {
   static constexpr int CPR = HSP / 8, NI = TILE * CPR / NTHR;
   u32x4 v[NI];
-  __device__ __forceinline__ void load(const bf16_t* base, long long ld, int row0, int T,
-                                       int hs, int tid) {
+  template <typename P>
+  __device__ __forceinline__ void load(const P* base, long long ld, int row0, int T, int hs,
+                                       int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int f = tid + NTHR * i;
       v[i] = load8(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* S, int tid) const {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int f = tid + NTHR * i;
@@ -95,8 +108,9 @@ struct ColsTile {
   static constexpr int BLOCKS = (TILE / 4) * DG;  // 4x8 blocks in the tile
   static constexpr int NI = (BLOCKS + NTHR - 1) / NTHR;
   u32x4 x[NI][4];
-  __device__ __forceinline__ void load(const bf16_t* base, long long ld, int row0, int T,
-                                       int hs, int tid) {
+  template <typename P>
+  __device__ __forceinline__ void load(const P* base, long long ld, int row0, int T, int hs,
+                                       int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int b = tid + NTHR * i;
@@ -106,7 +120,7 @@ struct ColsTile {
       for (int j = 0; j < 4; j++) x[i][j] = load8(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* S, int tid) const {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int b = tid + NTHR * i;
@@ -130,16 +144,16 @@ struct ColsTile {
   }
 };
 
-template <int HSP>
-GPT2_DEVICE_INLINE void tile_rows(bf16_t* S, const bf16_t* base, long long ld, int row0, int T,
+template <int HSP, typename P>
+GPT2_DEVICE_INLINE void tile_rows(uint16_t* S, const P* base, long long ld, int row0, int T,
                                   int hs, int tid) {
   RowsTile<HSP> t;
   t.load(base, ld, row0, T, hs, tid);
   t.store(S, tid);
 }
 
-template <int HSP>
-GPT2_DEVICE_INLINE void tile_cols(bf16_t* S, const bf16_t* base, long long ld, int row0, int T,
+template <int HSP, typename P>
+GPT2_DEVICE_INLINE void tile_cols(uint16_t* S, const P* base, long long ld, int row0, int T,
                                   int hs, int tid) {
   ColsTile<HSP> t;
   t.load(base, ld, row0, T, hs, tid);
@@ -157,15 +171,15 @@ GPT2_DEVICE_INLINE void tile_of_block(int ntiles, int NH, int* tile, int* head, 
 // ---------------------------------------------------------------------------------------
 // forward: a workgroup owns 64 queries (32 per wave) of one (batch, head)
 // ---------------------------------------------------------------------------------------
-template <int HSP>
-__global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restrict__ out,
-                                                                float* __restrict__ lse,
-                                                                const bf16_t* __restrict__ qkv,
-                                                                int T, int C, int NH, int hs,
-                                                                float scale_log2) {
+template <int HSP, typename TS>
+__global__ __launch_bounds__(NTHR) void attn_fwd_mma16_kernel(TS* __restrict__ out,
+                                                              float* __restrict__ lse,
+                                                              const TS* __restrict__ qkv, int T,
+                                                              int C, int NH, int hs,
+                                                              float scale_log2) {
   constexpr int KS = HSP / 16, ND = HSP / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[TILE * HSP];   // [key][d]
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[HSP * TILE];   // [d][kpos(key)]
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE * HSP];   // [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[HSP * TILE];   // [d][kpos(key)]
 
   const int nqt = (T + TILE - 1) / TILE;
   int qt, head, b;
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, lh = lane >> 5;
   const long long C3 = 3LL * C;
-  const bf16_t* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const TS* base = qkv + (long long)b * T * C3 + (long long)head * hs;
   const int q = qt * TILE + wave * 32 + r;
   const int qm = min(q, T - 1);  // lanes past the end mask as the last row; never stored
 
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
       for (int ks = 0; ks < KS; ks++) {
         const bf16x8 kf =
             *reinterpret_cast<const bf16x8*>(&Ks[loff<HSP>(32 * kb + r, 2 * ks + lh)]);
-        s[kb] = mfma_bf16(kf, qf[ks], s[kb]);
+        s[kb] = mfma16<TS>(kf, qf[ks], s[kb]);
       }
     }
     if (key0 + TILE > qt * TILE) {  // the diagonal tile (uniform): mask keys after the query
@@ -259,7 +273,7 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hh + 2 * j], scale_log2, -m_run));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hh + 2 * j + 1], scale_log2, -m_run));
           l_run += p0 + p1;
-          w[j] = pack2(p0, p1);
+          w[j] = Half16<TS>::pack2(p0, p1);
         }
         pf[kb][hh] = __builtin_bit_cast(bf16x8, w);
       }
@@ -272,14 +286,14 @@ __global__ __launch_bounds__(NTHR) void attn_fwd_bf16mma_kernel(bf16_t* __restri
         for (int hh = 0; hh < 2; hh++) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
               &Vt[loff<TILE>(32 * db + r, 4 * kb + 2 * hh + lh)]);
-          oacc[db] = mfma_bf16(vf, pf[kb][hh], oacc[db]);
+          oacc[db] = mfma16<TS>(vf, pf[kb][hh], oacc[db]);
         }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
   if (q < T) {
-    bf16_t* o = out + ((long long)b * T + q) * C + (long long)head * hs;
+    TS* o = out + ((long long)b * T + q) * C + (long long)head * hs;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
@@ -683,19 +697,19 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dq_x6_kernel(float* __restr
 // dK, dV for 64 keys (32 per wave), over the query tiles from the diagonal down. Per query
 // tile, S and dP are computed with queries down the rows and this lane's key as the column;
 // P and dS are then the B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A operands are
-// the transposed tiles dO^T and Q^T in LDS. dS^T of each causal 64x64 tile is written (bf16,
+// the transposed tiles dO^T and Q^T in LDS. dS^T of each causal 64x64 tile is written (TS,
 // [key][query]) for the dQ kernel.
-template <int HSP>
-__global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
-    bf16_t* __restrict__ dqkv, bf16_t* __restrict__ dsbuf, const bf16_t* __restrict__ dout,
-    const bf16_t* __restrict__ qkv, const float* __restrict__ lse,
+template <int HSP, typename TS>
+__global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_mma16_kernel(
+    TS* __restrict__ dqkv, uint16_t* __restrict__ dsbuf, const TS* __restrict__ dout,
+    const TS* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Drow, int T, int C, int NH, int hs, float scale,
     float scale_log2) {
   constexpr int KS = HSP / 16, ND = HSP / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[TILE * HSP];   // [q][d]
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[HSP * TILE];   // [d][kpos(q)]
-  __shared__ __attribute__((aligned(16))) bf16_t dOs[TILE * HSP];  // [q][d]
-  __shared__ __attribute__((aligned(16))) bf16_t dOt[HSP * TILE];  // [d][kpos(q)]
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[TILE * HSP];   // [q][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[HSP * TILE];   // [d][kpos(q)]
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[TILE * HSP];  // [q][d]
+  __shared__ __attribute__((aligned(16))) uint16_t dOt[HSP * TILE];  // [d][kpos(q)]
   __shared__ __attribute__((aligned(16))) float Ls[TILE];
   __shared__ __attribute__((aligned(16))) float Ds[TILE];
 
@@ -705,8 +719,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, lh = lane >> 5;
   const long long C3 = 3LL * C;
-  const bf16_t* base = qkv + (long long)b * T * C3 + (long long)head * hs;
-  const bf16_t* dobase = dout + (long long)b * T * C + (long long)head * hs;
+  const TS* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const TS* dobase = dout + (long long)b * T * C + (long long)head * hs;
   const float* lrow = lse + ((long long)b * NH + head) * T;
   const float* drow = Drow + ((long long)b * NH + head) * T;
   const int key = kt * TILE + wave * 32 + r;
@@ -741,8 +755,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
       Ds[tid] = t < T ? drow[t] : 0.f;
     }
     __syncthreads();
-    // dS^T tile (kt, qt) of this (b, head): [key][query], 64 x 64 bf16
-    bf16_t* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
+    // dS^T tile (kt, qt) of this (b, head): [key][query], 64 x 64 TS
+    uint16_t* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
                               (TILE * TILE) + (long long)(wave * 32 + r) * TILE;
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
@@ -754,7 +768,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
         lq[g4] = *reinterpret_cast<const f32x4*>(&Ls[32 * qb + 8 * g4 + 4 * lh]);
         dq[g4] = *reinterpret_cast<const f32x4*>(&Ds[32 * qb + 8 * g4 + 4 * lh]);
       }
-      u32x4 pw[2], sw[2];  // P and dS (bf16 pairs) as B operands of k step h
+      u32x4 pw[2], sw[2];  // P and dS (TS pairs) as B operands of k step h
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
@@ -765,8 +779,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
       for (int ks = 0; ks < KS; ks++) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[loff<HSP>(32 * qb + r, 2 * ks + lh)]);
         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOs[loff<HSP>(32 * qb + r, 2 * ks + lh)]);
-        s = mfma_bf16(qa, kf[ks], s);
-        dp = mfma_bf16(oa, vf[ks], dp);
+        s = mfma16<TS>(qa, kf[ks], s);
+        dp = mfma16<TS>(oa, vf[ks], dp);
       }
       // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's. The
       // exponential is taken for every entry and masked after (no branch per entry); a
@@ -793,9 +807,10 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
 #pragma unroll
         for (int j = 0; j < 4; j++) dsv[j] *= pv[j];
         const int hh = g4 >> 1, w = 2 * (g4 & 1);  // acc entries 8hh .. 8hh+7 form k step hh
-        pw[hh][w] = pack2(pv[0], pv[1]);
-        pw[hh][w + 1] = pack2(pv[2], pv[3]);
-        const uint32_t d01 = pack2(dsv[0], dsv[1]), d23 = pack2(dsv[2], dsv[3]);
+        pw[hh][w] = Half16<TS>::pack2(pv[0], pv[1]);
+        pw[hh][w + 1] = Half16<TS>::pack2(pv[2], pv[3]);
+        const uint32_t d01 = Half16<TS>::pack2(dsv[0], dsv[1]),
+                       d23 = Half16<TS>::pack2(dsv[2], dsv[3]);
         sw[hh][w] = d01;
         sw[hh][w + 1] = d23;
         // 4 consecutive queries of this key: one 8-byte store
@@ -808,14 +823,14 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
           const int c = 4 * qb + 2 * hh + lh;
           const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dOt[loff<TILE>(32 * db + r, c)]);
           const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qt[loff<TILE>(32 * db + r, c)]);
-          dvacc[db] = mfma_bf16(oa, __builtin_bit_cast(bf16x8, pw[hh]), dvacc[db]);
-          dkacc[db] = mfma_bf16(qa, __builtin_bit_cast(bf16x8, sw[hh]), dkacc[db]);
+          dvacc[db] = mfma16<TS>(oa, __builtin_bit_cast(bf16x8, pw[hh]), dvacc[db]);
+          dkacc[db] = mfma16<TS>(qa, __builtin_bit_cast(bf16x8, sw[hh]), dkacc[db]);
         }
     }
   }
   if (key < T) {
-    bf16_t* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
-    bf16_t* dv = dk + C;
+    TS* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
+    TS* dv = dk + C;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
@@ -833,13 +848,13 @@ __global__ __launch_bounds__(NTHR, 2) void attn_bwd_dkdv_bf16mma_kernel(
 
 // dQ^T[d][q] = scale * K^T[d][key] dS^T[key][q] for 64 queries (32 per wave), over key
 // tiles 0 .. qt, reading the dS^T tiles of the dK/dV kernel transposed into LDS.
-template <int HSP>
-__global__ __launch_bounds__(NTHR) void attn_bwd_dq_bf16mma_kernel(
-    bf16_t* __restrict__ dqkv, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dsbuf,
+template <int HSP, typename TS>
+__global__ __launch_bounds__(NTHR) void attn_bwd_dq_mma16_kernel(
+    TS* __restrict__ dqkv, const TS* __restrict__ qkv, const uint16_t* __restrict__ dsbuf,
     int T, int C, int NH, int hs, float scale) {
   constexpr int ND = HSP / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[HSP * TILE];   // [d][kpos(key)]
-  __shared__ __attribute__((aligned(16))) bf16_t Sq[TILE * TILE];  // [q][kpos(key)]
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[HSP * TILE];   // [d][kpos(key)]
+  __shared__ __attribute__((aligned(16))) uint16_t Sq[TILE * TILE];  // [q][kpos(key)]
 
   const int nqt = (T + TILE - 1) / TILE;
   int qt, head, b;
@@ -848,8 +863,8 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_bf16mma_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, lh = lane >> 5;
   const long long C3 = 3LL * C;
-  const bf16_t* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
-  const bf16_t* src = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, 0)) *
+  const TS* kbase = qkv + (long long)b * T * C3 + (long long)head * hs + C;
+  const uint16_t* src = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, 0)) *
                                   (TILE * TILE);
 
   f32x16 acc[ND];
@@ -883,13 +898,13 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_dq_bf16mma_kernel(
           const int c = 4 * kb + 2 * hh + lh;
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[loff<TILE>(32 * db + r, c)]);
           const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&Sq[loff<TILE>(32 * wave + r, c)]);
-          acc[db] = mfma_bf16(ka, sb, acc[db]);
+          acc[db] = mfma16<TS>(ka, sb, acc[db]);
         }
   }
   // acc[db][i]: d = 32db + 8(i/4) + 4lh + i%4, query 32 wave + r of the tile
   const int q = qt * TILE + 32 * wave + r;
   if (q < T) {
-    bf16_t* o = dqkv + ((long long)b * T + q) * C3 + (long long)head * hs;
+    TS* o = dqkv + ((long long)b * T + q) * C3 + (long long)head * hs;
 #pragma unroll
     for (int db = 0; db < ND; db++)
 #pragma unroll
@@ -949,36 +964,49 @@ bool attention_bf16_mma_supported(int C, int NH) {
   return hs % 8 == 0 && hs <= 128;
 }
 
-int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
-                               int NH, hipStream_t stream) {
+template <typename TS>
+static int attention_forward_mma16(TS* out, float* lse, const TS* qkv, int B, int T, int C,
+                                   int NH, hipStream_t stream) {
+  constexpr bool F16 = std::is_same<TS, f16_t>::value;
   if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_bf16_mma_supported(C, NH)) {
-    set_global_error("attention (bf16 MFMA): unsupported shape B=%d T=%d C=%d NH=%d", B, T, C,
-                     NH);
+    set_global_error("attention (%s MFMA): unsupported shape B=%d T=%d C=%d NH=%d",
+                     F16 ? "fp16" : "bf16", B, T, C, NH);
     return -1;
   }
   const int hs = C / NH;
   const float scale_log2 = kLog2e / sqrtf((float)hs);
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   const double tri = (double)T * (T + 1) / 2.0;
-  ProfScope ps("attn_fwd_bf16mma_kernel", 4.0 * B * NH * hs * tri,
+  ProfScope ps(F16 ? "attn_fwd_f16mma_kernel" : "attn_fwd_bf16mma_kernel",
+               4.0 * B * NH * hs * tri,
                2.0 * ((double)B * T * 3 * C + (double)B * T * C) + 4.0 * B * NH * T, stream);
-  if (hs <= 32) attn_fwd_bf16mma_kernel<32><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
-  else if (hs <= 64) attn_fwd_bf16mma_kernel<64><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
-  else attn_fwd_bf16mma_kernel<128><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  if (hs <= 32) attn_fwd_mma16_kernel<32, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else if (hs <= 64) attn_fwd_mma16_kernel<64, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
+  else attn_fwd_mma16_kernel<128, TS><<<grid, NTHR, 0, stream>>>(out, lse, qkv, T, C, NH, hs, scale_log2);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+
+int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
+                               int NH, hipStream_t stream) {
+  return attention_forward_mma16(out, lse, qkv, B, T, C, NH, stream);
+}
+int attention_forward_f16_mma(f16_t* out, float* lse, const f16_t* qkv, int B, int T, int C,
+                              int NH, hipStream_t stream) {
+  return attention_forward_mma16(out, lse, qkv, B, T, C, NH, stream);
 }
 
 }  // namespace gpt2
 
 namespace gpt2 {
-int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,
-                                const bf16_t* out, const float* lse, float* dscratch,
-                                float* ds_scratch, int B, int T, int C, int NH,
-                                hipStream_t stream) {
+template <typename TS>
+static int attention_backward_mma16(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
+                                    const float* lse, float* dscratch, float* ds_scratch, int B,
+                                    int T, int C, int NH, hipStream_t stream) {
+  constexpr bool F16 = std::is_same<TS, f16_t>::value;
   if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_bf16_mma_supported(C, NH)) {
-    set_global_error("attention (bf16 MFMA): unsupported shape B=%d T=%d C=%d NH=%d", B, T, C,
-                     NH);
+    set_global_error("attention (%s MFMA): unsupported shape B=%d T=%d C=%d NH=%d",
+                     F16 ? "fp16" : "bf16", B, T, C, NH);
     return -1;
   }
   const int hs = C / NH;
@@ -988,24 +1016,40 @@ int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* 
   const long long rows = (long long)B * NH * T;
   const int rc = attention_rowdot(dscratch, dout, out, B, T, C, NH, stream);
   if (rc) return rc;
-  bf16_t* ds = reinterpret_cast<bf16_t*>(ds_scratch);
+  uint16_t* ds = reinterpret_cast<uint16_t*>(ds_scratch);
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
   {
-    ProfScope ps("attn_bwd_dkdv_bf16mma_kernel", 6.0 * B * NH * hs * tri,
+    ProfScope ps(F16 ? "attn_bwd_dkdv_f16mma_kernel" : "attn_bwd_dkdv_bf16mma_kernel",
+                 6.0 * B * NH * hs * tri,
                  2.0 * (3.0 * BTC + BTC + 2.0 * BTC) + 4.0 * 2.0 * rows + 2.0 * B * NH * tri,
                  stream);
-    if (hs <= 32) attn_bwd_dkdv_bf16mma_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else if (hs <= 64) attn_bwd_dkdv_bf16mma_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
-    else attn_bwd_dkdv_bf16mma_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    if (hs <= 32) attn_bwd_dkdv_mma16_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else if (hs <= 64) attn_bwd_dkdv_mma16_kernel<64, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
+    else attn_bwd_dkdv_mma16_kernel<128, TS><<<grid, NTHR, 0, stream>>>(dqkv, ds, dout, qkv, lse, dscratch, T, C, NH, hs, scale, scale_log2);
   }
   {
-    ProfScope ps("attn_bwd_dq_bf16mma_kernel", 2.0 * B * NH * hs * tri,
-                 2.0 * B * NH * tri + 2.0 * 2.0 * BTC, stream);
-    if (hs <= 32) attn_bwd_dq_bf16mma_kernel<32><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
-    else if (hs <= 64) attn_bwd_dq_bf16mma_kernel<64><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
-    else attn_bwd_dq_bf16mma_kernel<128><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
+    ProfScope ps(F16 ? "attn_bwd_dq_f16mma_kernel" : "attn_bwd_dq_bf16mma_kernel",
+                 2.0 * B * NH * hs * tri, 2.0 * B * NH * tri + 2.0 * 2.0 * BTC, stream);
+    if (hs <= 32) attn_bwd_dq_mma16_kernel<32, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
+    else if (hs <= 64) attn_bwd_dq_mma16_kernel<64, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
+    else attn_bwd_dq_mma16_kernel<128, TS><<<grid, NTHR, 0, stream>>>(dqkv, qkv, ds, T, C, NH, hs, scale);
   }
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+
+int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,
+                                const bf16_t* out, const float* lse, float* dscratch,
+                                float* ds_scratch, int B, int T, int C, int NH,
+                                hipStream_t stream) {
+  return attention_backward_mma16(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C, NH,
+                                  stream);
+}
+int attention_backward_f16_mma(f16_t* dqkv, const f16_t* dout, const f16_t* qkv,
+                               const f16_t* out, const float* lse, float* dscratch,
+                               float* ds_scratch, int B, int T, int C, int NH,
+                               hipStream_t stream) {
+  return attention_backward_mma16(dqkv, dout, qkv, out, lse, dscratch, ds_scratch, B, T, C, NH,
+                                  stream);
 }
 }  // namespace gpt2

@@ -50,6 +50,48 @@ GPT2_DEVICE_INLINE float ld1(const bf16_t* p) { return bf16_to_f32(*p); }
 GPT2_DEVICE_INLINE void st1(float* p, float v) { *p = v; }
 GPT2_DEVICE_INLINE void st1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// fp16 storage (IEEE binary16: 11 significant bits, largest finite 65504). Conversion from
+// fp32 rounds to nearest, ties to even; values beyond the range become infinities.
+typedef _Float16 f16_t;
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+GPT2_DEVICE_INLINE float f16_to_f32(f16_t h) { return (float)h; }
+GPT2_DEVICE_INLINE f16_t f32_to_f16(float f) { return (f16_t)f; }
+GPT2_DEVICE_INLINE f32x4 ld4(const f16_t* p) {
+  return __builtin_convertvector(*reinterpret_cast<const f16x4_t*>(p), f32x4);
+}
+template <> struct Raw4<f16_t> { typedef f16x4_t type; };
+GPT2_DEVICE_INLINE f16x4_t raw4(const f16_t* p) { return *reinterpret_cast<const f16x4_t*>(p); }
+GPT2_DEVICE_INLINE f32x4 widen4(f16x4_t v) { return __builtin_convertvector(v, f32x4); }
+GPT2_DEVICE_INLINE void st4(f16_t* p, f32x4 v) {
+  *reinterpret_cast<f16x4_t*>(p) = __builtin_convertvector(v, f16x4_t);
+}
+GPT2_DEVICE_INLINE float ld1(const f16_t* p) { return f16_to_f32(*p); }
+GPT2_DEVICE_INLINE void st1(f16_t* p, float v) { *p = f32_to_f16(v); }
+
+// 16-bit storage formats of the mixed-precision steps, for kernels templated on them:
+// the bits of two values rounded from fp32 packed into one word (a in the low half), and
+// one value's bits widened to fp32.
+template <typename TS> struct Half16;
+template <> struct Half16<bf16_t> {
+  static GPT2_DEVICE_INLINE uint32_t pack2(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  }
+  static GPT2_DEVICE_INLINE float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static GPT2_DEVICE_INLINE float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+};
+template <> struct Half16<f16_t> {
+  static GPT2_DEVICE_INLINE uint32_t pack2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, f32_to_f16(a)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_f16(b)) << 16);
+  }
+  static GPT2_DEVICE_INLINE float lo(uint32_t w) {
+    return f16_to_f32(__builtin_bit_cast(f16_t, (uint16_t)(w & 0xFFFFu)));
+  }
+  static GPT2_DEVICE_INLINE float hi(uint32_t w) {
+    return f16_to_f32(__builtin_bit_cast(f16_t, (uint16_t)(w >> 16)));
+  }
+};
+
 // Exact split of fp32 values into three bf16 parts, x = hi + mid + lo: hi is x rounded to
 // bf16 (8 significand bits), mid the remainder x - hi rounded to bf16, lo what remains.
 // x - hi is exact in fp32 (hi is within a factor 2 of x) and, being a multiple of the last

@@ -1,5 +1,7 @@
-// gemm_bf16.hip -- the GEMMs of the mixed-precision step: bf16 operands, fp32 accumulation
-// (v_mfma_f32_32x32x16_bf16 on gfx950), bf16 or fp32 results.
+// gemm_bf16.hip -- the GEMMs of the mixed-precision steps: 16-bit operands (bf16 or fp16),
+// fp32 accumulation (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x16_f16 on gfx950), 16-bit
+// or fp32 results. The two formats share every line but the MFMA instruction and the
+// conversions, so the kernels are templated on the storage type TS.
 //
 // Same three storage patterns as the fp32 GEMMs ("llm.c 的中文注解-20240421", sections 1.5
 // and 1.6), C = op(A) . op(B):
@@ -7,7 +9,7 @@
 //   grad input   dinp = dout . W    A (M,K) row-major, B = W stored (K,N)   (b_trans)
 //   grad weight  dW  += dout^T.inp  A = dout stored (K,M), B = inp (K,N)   (a_trans, b_trans)
 // and the same fused epilogues (bias, bias+GELU, bias+residual, fp32 accumulate into the
-// master gradients, GELU backward), computed in fp32 and rounded once to bf16 on store.
+// master gradients, GELU backward), computed in fp32 and rounded once to TS on store.
 //
 // Tiling: workgroups own 256x256 tiles of C (8 waves of 128x64) or, for grids too small to
 // fill the chip, 128x128 tiles (4 waves of 64x64); each wave holds WM x WN blocks of 32x32
@@ -52,18 +54,30 @@ typedef TileCfg<128, 128, 32, 2, 2, 3, 3, 8> Tile128;
 // the 128 x 128 tile
 typedef TileCfg<256, 256, 64, 2, 4, 2, 1, 8> Tile256;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // 8 x 16 bits of either format
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// acc += a . b on the MFMA of the storage format (fragments carry the raw 16-bit patterns)
+template <typename TS>
+GPT2_DEVICE_INLINE f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 acc) {
+  if constexpr (std::is_same<TS, f16_t>::value)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
+template <typename TS>
 struct Args {
-  const bf16_t* A;
-  const bf16_t* B;
+  const TS* A;
+  const TS* B;
   void* C;
-  bf16_t* C2;
-  const bf16_t* R;
+  TS* C2;
+  const TS* R;
   const float* bias;
   float* colsum;
   int lda, ldb, ldc;
@@ -108,10 +122,10 @@ struct SlabCopy {
   long long remain;     // bytes from `tile` to the end of the operand
   uint32_t voff[PER_WAVE];
 
-  __device__ __forceinline__ void init(const bf16_t* P, int ld, int row0, long long total,
+  __device__ __forceinline__ void init(const void* P, int ld, int row0, long long total,
                                        int wave, int lane) {
     const long long at = TRANS ? (long long)row0 : (long long)row0 * ld;
-    tile = reinterpret_cast<const char*>(P + at);
+    tile = reinterpret_cast<const char*>(P) + 2 * at;
     remain = 2 * (total - at);
     step = TRANS ? 2LL * BK * ld : 2LL * BK;
 #pragma unroll
@@ -129,7 +143,7 @@ struct SlabCopy {
 
   // `live` false: a copy past the last slab, given an empty range (it reads nothing and
   // writes zeros), so that every pipeline step issues the same number of copies
-  __device__ __forceinline__ void issue(int kt, bool live, bf16_t* lds, int wave) const {
+  __device__ __forceinline__ void issue(int kt, bool live, void* lds, int wave) const {
     const long long off = live ? (long long)kt * step : 0;
     const long long left = live ? remain - off : 0;
     const int nrec = (int)(uint32_t)(left > 0xFFFFFFFFLL ? 0xFFFFFFFFLL : left > 0 ? left : 0);
@@ -175,8 +189,8 @@ GPT2_DEVICE_INLINE void wait_vmcnt() {
 }
 
 // Epilogue of four consecutive columns n..n+3 of row m (n % 4 == 0, m < M, n < N).
-template <int EPI, bool CF32>
-__device__ __forceinline__ void epilogue4(const Args& g, void* Cv, int m, int n, f32x4 v) {
+template <typename TS, int EPI, bool CF32>
+__device__ __forceinline__ void epilogue4(const Args<TS>& g, void* Cv, int m, int n, f32x4 v) {
   const long long off = (long long)m * g.ldc + n;
   const int cnt = min(4, g.N - n);
   if (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
@@ -193,7 +207,7 @@ __device__ __forceinline__ void epilogue4(const Args& g, void* Cv, int m, int n,
     if (cnt == 4) {
       r = ld4(g.R + off);
     } else {
-      for (int j = 0; j < 4; j++) r[j] = j < cnt ? bf16_to_f32(g.R[off + j]) : 0.f;
+      for (int j = 0; j < 4; j++) r[j] = j < cnt ? ld1(g.R + off + j) : 0.f;
     }
     if (EPI == EPI_RESID) v += r;
     else
@@ -209,7 +223,7 @@ __device__ __forceinline__ void epilogue4(const Args& g, void* Cv, int m, int n,
       for (int j = 0; j < cnt; j++) C[off + j] = EPI == EPI_ACCUM ? C[off + j] + v[j] : v[j];
     }
   } else {
-    bf16_t* C = static_cast<bf16_t*>(Cv);
+    TS* C = static_cast<TS*>(Cv);
     if (cnt == 4) {
       st4(C + off, v);
       if (EPI == EPI_GELU)
@@ -217,15 +231,15 @@ __device__ __forceinline__ void epilogue4(const Args& g, void* Cv, int m, int n,
                                        gelu_fwd(v[3])});
     } else {
       for (int j = 0; j < cnt; j++) {
-        C[off + j] = f32_to_bf16(v[j]);
-        if (EPI == EPI_GELU) g.C2[off + j] = f32_to_bf16(gelu_fwd(v[j]));
+        st1(C + off + j, v[j]);
+        if (EPI == EPI_GELU) st1(g.C2 + off + j, gelu_fwd(v[j]));
       }
     }
   }
 }
 
-template <class CFG, bool AT, bool BT, bool CF32, int EPI>
-__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
+template <typename TS, class CFG, bool AT, bool BT, bool CF32, int EPI>
+__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm16_kernel(Args<TS> g) {
   constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, WM = CFG::WM, WN = CFG::WN;
   constexpr int NT = CFG::NT;
   constexpr int NSTAGE = CFG::NSTAGE, NWAVES = CFG::NWAVES;
@@ -234,9 +248,9 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
   constexpr int SA = BM * BK, SB = BN * BK;
   constexpr int SA3 = NSTAGE > 3 ? SA : 8, SB3 = NSTAGE > 3 ? SB : 8;
   constexpr int SA4 = NSTAGE > 4 ? SA : 8, SB4 = NSTAGE > 4 ? SB : 8;
-  __shared__ __attribute__((aligned(1024))) bf16_t As0[SA], As1[SA], As2[SA];
-  __shared__ __attribute__((aligned(1024))) bf16_t Bs0[SB], Bs1[SB], Bs2[SB];
-  __shared__ __attribute__((aligned(16))) bf16_t As3[SA3], Bs3[SB3], As4[SA4], Bs4[SB4];
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[SA], As1[SA], As2[SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs0[SB], Bs1[SB], Bs2[SB];
+  __shared__ __attribute__((aligned(16))) uint16_t As3[SA3], Bs3[SB3], As4[SA4], Bs4[SB4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -302,17 +316,17 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
     }
   }
 
-  auto stage_a = [&](int s) -> bf16_t* {
+  auto stage_a = [&](int s) -> uint16_t* {
     return s == 0 ? As0 : s == 1 ? As1 : s == 2 ? As2 : s == 3 ? As3 : As4;
   };
-  auto stage_b = [&](int s) -> bf16_t* {
+  auto stage_b = [&](int s) -> uint16_t* {
     return s == 0 ? Bs0 : s == 1 ? Bs1 : s == 2 ? Bs2 : s == 3 ? Bs3 : Bs4;
   };
   auto issue = [&](int kt, int s) {
     ca.issue(kt, kt < nslabs, stage_a(s), wave);
     cb.issue(kt, kt < nslabs, stage_b(s), wave);
   };
-  auto compute = [&](const bf16_t* As, const bf16_t* Bs, int kt) {
+  auto compute = [&](const uint16_t* As, const uint16_t* Bs, int kt) {
     const char* pa = reinterpret_cast<const char*>(As);
     const char* pb = reinterpret_cast<const char*>(Bs);
     const int k0 = kbeg + kt * BK;
@@ -341,8 +355,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
       for (int tm = 0; tm < WM; tm++)
 #pragma unroll
         for (int tn = 0; tn < WN; tn++)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn],
-                                                                0, 0, 0);
+          acc[tm][tn] = mfma16<TS>(bfr[tn], af[tm], acc[tm][tn]);
     }
     if (do_colsum) {
       // A is stored (K, M): LDS [k][m] (k past K reads as zero: the copy stops at the
@@ -354,8 +367,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
                                                          16 * (mc ^ rswz(k & 3)));
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          csum[2 * q] += __uint_as_float(x[q] << 16);
-          csum[2 * q + 1] += __uint_as_float(x[q] & 0xFFFF0000u);
+          csum[2 * q] += Half16<TS>::lo(x[q]);
+          csum[2 * q + 1] += Half16<TS>::hi(x[q]);
         }
       }
     }
@@ -417,7 +430,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
       for (int q = 0; q < 4; q++) {
         const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
         if (n >= g.N) continue;
-        epilogue4<EPI, CF32>(g, C, m, n,
+        epilogue4<TS, EPI, CF32>(g, C, m, n,
                              f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1],
                                    acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]});
       }
@@ -428,8 +441,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(Args g) {
 // epilogue into the real output; four consecutive columns per thread.
 // With colsum_part, the last workgroups instead add the per-split column sums (split order)
 // into g.colsum.
-template <int EPI, bool CF32>
-__global__ void split_reduce_bf16_kernel(Args g, const float* __restrict__ ws, int splits,
+template <typename TS, int EPI, bool CF32>
+__global__ void split_reduce_bf16_kernel(Args<TS> g, const float* __restrict__ ws, int splits,
                                          int wld, const float* __restrict__ colsum_part) {
   // the last ceil(M / blockDim) workgroups reduce the column sums, one m per thread
   const int ncs = colsum_part ? (g.M + blockDim.x - 1) / blockDim.x : 0;
@@ -463,35 +476,35 @@ __global__ void split_reduce_bf16_kernel(Args g, const float* __restrict__ ws, i
       s += p3;
     }
     for (; z < splits; z++) s += *reinterpret_cast<const f32x4*>(src + (long long)z * zstride);
-    epilogue4<EPI, CF32>(g, g.C, m, n, s);
+    epilogue4<TS, EPI, CF32>(g, g.C, m, n, s);
   }
 }
 
 
-template <class CFG, bool AT, bool BT, bool CF32>
-void launch_epi(const Args& a, int epi, dim3 grid, hipStream_t s) {
+template <typename TS, class CFG, bool AT, bool BT, bool CF32>
+void launch_epi(const Args<TS>& a, int epi, dim3 grid, hipStream_t s) {
   constexpr int NT = CFG::NT;
   switch (epi) {
-    case EPI_STORE: gemm_bf16_kernel<CFG, AT, BT, CF32, EPI_STORE><<<grid, NT, 0, s>>>(a); break;
-    case EPI_GELU: gemm_bf16_kernel<CFG, AT, BT, false, EPI_GELU><<<grid, NT, 0, s>>>(a); break;
-    case EPI_RESID: gemm_bf16_kernel<CFG, AT, BT, false, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
-    case EPI_ACCUM: gemm_bf16_kernel<CFG, AT, BT, true, EPI_ACCUM><<<grid, NT, 0, s>>>(a); break;
-    case EPI_GELU_BWD: gemm_bf16_kernel<CFG, AT, BT, false, EPI_GELU_BWD><<<grid, NT, 0, s>>>(a); break;
+    case EPI_STORE: gemm16_kernel<TS, CFG, AT, BT, CF32, EPI_STORE><<<grid, NT, 0, s>>>(a); break;
+    case EPI_GELU: gemm16_kernel<TS, CFG, AT, BT, false, EPI_GELU><<<grid, NT, 0, s>>>(a); break;
+    case EPI_RESID: gemm16_kernel<TS, CFG, AT, BT, false, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
+    case EPI_ACCUM: gemm16_kernel<TS, CFG, AT, BT, true, EPI_ACCUM><<<grid, NT, 0, s>>>(a); break;
+    case EPI_GELU_BWD: gemm16_kernel<TS, CFG, AT, BT, false, EPI_GELU_BWD><<<grid, NT, 0, s>>>(a); break;
   }
 }
 
-template <class CFG, bool AT, bool BT>
-void launch_c(const Args& a, int epi, bool cf32, dim3 grid, hipStream_t s) {
-  if (cf32) launch_epi<CFG, AT, BT, true>(a, epi, grid, s);
-  else launch_epi<CFG, AT, BT, false>(a, epi, grid, s);
+template <typename TS, class CFG, bool AT, bool BT>
+void launch_c(const Args<TS>& a, int epi, bool cf32, dim3 grid, hipStream_t s) {
+  if (cf32) launch_epi<TS, CFG, AT, BT, true>(a, epi, grid, s);
+  else launch_epi<TS, CFG, AT, BT, false>(a, epi, grid, s);
 }
 
-template <class CFG>
-void launch(const Args& a, bool at, bool bt, int epi, bool cf32, dim3 grid, hipStream_t s) {
-  if (!at && !bt) launch_c<CFG, false, false>(a, epi, cf32, grid, s);
-  else if (!at && bt) launch_c<CFG, false, true>(a, epi, cf32, grid, s);
-  else if (at && bt) launch_c<CFG, true, true>(a, epi, cf32, grid, s);
-  else launch_c<CFG, true, false>(a, epi, cf32, grid, s);
+template <class CFG, typename TS>
+void launch(const Args<TS>& a, bool at, bool bt, int epi, bool cf32, dim3 grid, hipStream_t s) {
+  if (!at && !bt) launch_c<TS, CFG, false, false>(a, epi, cf32, grid, s);
+  else if (!at && bt) launch_c<TS, CFG, false, true>(a, epi, cf32, grid, s);
+  else if (at && bt) launch_c<TS, CFG, true, true>(a, epi, cf32, grid, s);
+  else launch_c<TS, CFG, true, false>(a, epi, cf32, grid, s);
 }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -519,7 +532,8 @@ int forced_tile() {
   const int v = e ? atoi(e) : 0;
   return v == T128 || v == T256 ? v : 0;
 }
-Plan choose_plan(const GemmBf16& g) {
+template <typename TS>
+Plan choose_plan(const GemmHalf<TS>& g) {
   const double mn = (double)g.M * g.N;
   Plan best_p{T128, 1};
   double best = 1e30;
@@ -551,15 +565,19 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-size_t gemm_bf16_workspace_floats(const GemmBf16& g) {
+template <typename TS>
+size_t gemm16_workspace_floats(const GemmHalf<TS>& g) {
   const int s = choose_plan(g).splits;
   if (s <= 1) return 0;
   return (size_t)s * g.M * split_ld(g.N) + (g.colsum ? (size_t)s * g.M : 0);
 }
 
-int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t stream) {
+template <typename TS>
+int gemm16(const GemmHalf<TS>& g, float* workspace, size_t ws_floats, hipStream_t stream) {
+  constexpr bool F16 = std::is_same<TS, f16_t>::value;
+  const char* fmt = F16 ? "f16" : "bf16";
   if (g.M <= 0 || g.N <= 0 || g.K <= 0) {
-    set_global_error("gemm_bf16: non-positive size M=%d N=%d K=%d", g.M, g.N, g.K);
+    set_global_error("gemm_%s: non-positive size M=%d N=%d K=%d", fmt, g.M, g.N, g.K);
     return -1;
   }
   // 16-byte operand loads need 16-byte aligned bases and leading dimensions that are
@@ -573,16 +591,16 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
       (g.bias && !aligned16(g.bias)) || g.lda >= (1 << 24) || g.ldb >= (1 << 24) ||
       2.0 * (g.a_trans ? g.K : g.M) * g.lda >= 4294967295.0 ||
       2.0 * (g.b_trans ? g.K : g.N) * g.ldb >= 4294967295.0) {
-    set_global_error("gemm_bf16: unsupported alignment or leading dimension (lda=%d ldb=%d "
-                     "ldc=%d)", g.lda, g.ldb, g.ldc);
+    set_global_error("gemm_%s: unsupported alignment or leading dimension (lda=%d ldb=%d "
+                     "ldc=%d)", fmt, g.lda, g.ldb, g.ldc);
     return -1;
   }
   if ((g.epi == EPI_GELU && !g.C2) || ((g.epi == EPI_RESID || g.epi == EPI_GELU_BWD) && !g.R) ||
       (g.colsum && !g.a_trans)) {
-    set_global_error("gemm_bf16: epilogue %d is missing an operand", (int)g.epi);
+    set_global_error("gemm_%s: epilogue %d is missing an operand", fmt, (int)g.epi);
     return -1;
   }
-  Args a;
+  Args<TS> a;
   a.A = g.A;
   a.B = g.B;
   a.C = g.C;
@@ -602,14 +620,14 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
   const Plan plan = choose_plan(g);
   const TileInfo ti = tile_info(plan.tile);
   int splits = plan.splits;
-  if (splits > 1 && (!workspace || ws_floats < gemm_bf16_workspace_floats(g))) splits = 1;
+  if (splits > 1 && (!workspace || ws_floats < gemm16_workspace_floats(g))) splits = 1;
   const int kt = ceil_div(g.K, ti.bk);
   const int kt_per = ceil_div(kt, splits);
   splits = ceil_div(kt, kt_per);
   a.k_split = kt_per * ti.bk;
   a.splits = splits;
   const int tiles = ceil_div(g.M, ti.bm) * ceil_div(g.N, ti.bn);
-  auto run = [&](const Args& x, int epi, bool f32out, int grid) {
+  auto run = [&](const Args<TS>& x, int epi, bool f32out, int grid) {
     const bool at = g.a_trans, bt = g.b_trans;
     if (plan.tile == T128) launch<Tile128>(x, at, bt, epi, f32out, dim3(grid), stream);
     else launch<Tile256>(x, at, bt, epi, f32out, dim3(grid), stream);
@@ -622,14 +640,14 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
   const double out_bytes = g.epi == EPI_STORE ? cb * MN : 2.0 * cb * MN;
   char name[80];
   if (splits == 1) {
-    snprintf(name, sizeof(name), "gemm_bf16_kernel<%d,%d,%d>", (int)g.a_trans, (int)g.b_trans,
-             (int)g.epi);
+    snprintf(name, sizeof(name), "gemm_%s_kernel<%d,%d,%d>", fmt, (int)g.a_trans,
+             (int)g.b_trans, (int)g.epi);
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d", g.M, g.N, g.K);
     ProfScope ps(name, flop, in_bytes + out_bytes, stream);
     run(a, g.epi, cf32, tiles);
   } else {
-    Args p = a;
+    Args<TS> p = a;
     p.C = workspace;
     p.ldc = split_ld(g.N);
     p.c_zstride = (long long)g.M * p.ldc;
@@ -639,7 +657,7 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
       p.colsum = colsum_part;
       p.colsum_zstride = g.M;
     }
-    snprintf(name, sizeof(name), "gemm_bf16_kernel<%d,%d,0>", (int)g.a_trans, (int)g.b_trans);
+    snprintf(name, sizeof(name), "gemm_%s_kernel<%d,%d,0>", fmt, (int)g.a_trans, (int)g.b_trans);
     if (profiling_detail())
       snprintf(name + strlen(name), sizeof(name) - strlen(name), " %dx%dx%d/%d", g.M, g.N, g.K,
                splits);
@@ -650,21 +668,30 @@ int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t
     const long long total = (long long)g.M * ((g.N + 3) / 4);
     int blocks = (int)((total + 255) / 256);
     if (blocks > 8192) blocks = 8192;
-    snprintf(name, sizeof(name), "split_reduce_bf16_kernel<%d>", (int)g.epi);
+    snprintf(name, sizeof(name), "split_reduce_%s_kernel<%d>", fmt, (int)g.epi);
     const float* cp = g.colsum ? colsum_part : nullptr;
     const int nblk = blocks + (cp ? ceil_div(g.M, 256) : 0);
     ProfScope ps(name, 0.0, 4.0 * MN * splits + out_bytes + (cp ? 4.0 * (splits + 2.0) * g.M : 0.0),
                  stream);
     switch (g.epi) {
-      case EPI_ACCUM: split_reduce_bf16_kernel<EPI_ACCUM, true><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-      case EPI_GELU_BWD: split_reduce_bf16_kernel<EPI_GELU_BWD, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-      case EPI_GELU: split_reduce_bf16_kernel<EPI_GELU, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-      case EPI_RESID: split_reduce_bf16_kernel<EPI_RESID, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
-      default: split_reduce_bf16_kernel<EPI_STORE, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_ACCUM: split_reduce_bf16_kernel<TS, EPI_ACCUM, true><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_GELU_BWD: split_reduce_bf16_kernel<TS, EPI_GELU_BWD, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_GELU: split_reduce_bf16_kernel<TS, EPI_GELU, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      case EPI_RESID: split_reduce_bf16_kernel<TS, EPI_RESID, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
+      default: split_reduce_bf16_kernel<TS, EPI_STORE, false><<<nblk, 256, 0, stream>>>(a, workspace, splits, p.ldc, cp); break;
     }
   }
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+
+size_t gemm_bf16_workspace_floats(const GemmBf16& g) { return gemm16_workspace_floats(g); }
+size_t gemm_f16_workspace_floats(const GemmF16& g) { return gemm16_workspace_floats(g); }
+int gemm_bf16(const GemmBf16& g, float* workspace, size_t ws_floats, hipStream_t stream) {
+  return gemm16(g, workspace, ws_floats, stream);
+}
+int gemm_f16(const GemmF16& g, float* workspace, size_t ws_floats, hipStream_t stream) {
+  return gemm16(g, workspace, ws_floats, stream);
 }
 
 }  // namespace gpt2

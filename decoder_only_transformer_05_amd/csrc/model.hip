@@ -10,6 +10,7 @@
 // reverse layer order), gpt2_adamw_step section 1.26. Every launch goes to the model's one
 // stream; the only host synchronisation is the optional 4-byte loss readback.
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -86,6 +87,12 @@ struct gpt2_model {
   float* pbuf = nullptr;
   float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
   bf16_t* pbf = nullptr;  // GPT2_DTYPE_BF16: bf16 copy of params (GEMM operands)
+  f16_t* pf16 = nullptr;  // GPT2_DTYPE_FP16: fp16 copy of params (GEMM operands)
+  // GPT2_DTYPE_FP16 loss scaling (device): {scale, 1/scale} and {overflow flag, good steps,
+  // last step skipped}; growth interval 0 = fixed scale
+  float* d_scale = nullptr;
+  int32_t* d_scaler = nullptr;
+  int growth_interval = 2000;
 
   int B = 0, T = 0;
   char* abuf = nullptr;
@@ -96,7 +103,7 @@ struct gpt2_model {
   float *ln1_mean, *ln1_rstd, *attn_lse, *ln2_mean, *ln2_rstd, *lnf_mean, *lnf_rstd, *losses,
       *xent_lse;
   float *dres, *attn_D, *attn_dS, *gemm_ws, *ln_ws, *d_loss;
-  bf16_t* dres_h = nullptr;  // GPT2_DTYPE_BF16: dres rounded to bf16 (a GEMM operand)
+  void* dres_h = nullptr;  // 16-bit dtypes: dres rounded to the activation type (a GEMM operand)
   size_t gemm_ws_floats = 0;
   int32_t *tok, *tgt, *sort_scratch, *d_err;
 
@@ -151,21 +158,28 @@ float* G(gpt2_model* md, int k) { return md->grads + md->poff[k]; }
 template <typename T> const T* W(gpt2_model* md, int k);
 template <> const float* W<float>(gpt2_model* md, int k) { return md->params + md->poff[k]; }
 template <> const bf16_t* W<bf16_t>(gpt2_model* md, int k) { return md->pbf + md->poff[k]; }
+template <> const f16_t* W<f16_t>(gpt2_model* md, int k) { return md->pf16 + md->poff[k]; }
 
 template <typename T> T* act(void* p) { return static_cast<T*>(p); }
 
 template <typename T> struct GemmOf;
 template <> struct GemmOf<float> { using type = Gemm; };
 template <> struct GemmOf<bf16_t> { using type = GemmBf16; };
+template <> struct GemmOf<f16_t> { using type = GemmF16; };
 
 size_t ws_floats(const Gemm& g) { return gemm_workspace_floats(g); }
 size_t ws_floats(const GemmBf16& g) { return gemm_bf16_workspace_floats(g); }
+size_t ws_floats(const GemmF16& g) { return gemm_f16_workspace_floats(g); }
 int run_gemm(gpt2_model* md, const Gemm& g) {
   return gemm(g, md->gemm_ws, md->gemm_ws_floats, md->stream);
 }
 int run_gemm(gpt2_model* md, const GemmBf16& g) {
   return gemm_bf16(g, md->gemm_ws, md->gemm_ws_floats, md->stream);
 }
+int run_gemm(gpt2_model* md, const GemmF16& g) {
+  return gemm_f16(g, md->gemm_ws, md->gemm_ws_floats, md->stream);
+}
+bool half_dtype(int dtype) { return dtype == GPT2_DTYPE_BF16 || dtype == GPT2_DTYPE_FP16; }
 
 // the largest split-K workspace any GEMM of a step asks for
 template <typename T>
@@ -222,7 +236,7 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
     return p;
   };
   auto F = [&](size_t n) { return reinterpret_cast<float*>(take(n * sizeof(float))); };
-  const size_t es = md->dtype == GPT2_DTYPE_BF16 ? 2 : 4;  // activation element size
+  const size_t es = half_dtype(md->dtype) ? 2 : 4;  // activation element size
   auto A = [&](size_t n) { return static_cast<void*>(take(n * es)); };
   md->encoded = A(BT * C);
   md->ln1 = A(L * BT * C);
@@ -245,9 +259,7 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
   md->losses = F(BT);
   md->xent_lse = F(BT);
   md->dres = F(BT * C);
-  md->dres_h = md->dtype == GPT2_DTYPE_BF16
-                   ? reinterpret_cast<bf16_t*>(take(BT * C * sizeof(bf16_t)))
-                   : nullptr;
+  md->dres_h = half_dtype(md->dtype) ? static_cast<void*>(take(BT * C * 2)) : nullptr;
   md->dbuf4 = A(BT * 4 * C);
   md->dln = A(BT * C);
   md->datty = A(BT * C);
@@ -256,6 +268,8 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
   md->attn_dS = F(attention_ds_scratch_floats(B, T, (int)NH));
   const size_t ws = md->dtype == GPT2_DTYPE_BF16
                         ? step_gemm_workspace<bf16_t>((int)BT, (int)C, md->V)
+                    : md->dtype == GPT2_DTYPE_FP16
+                        ? step_gemm_workspace<f16_t>((int)BT, (int)C, md->V)
                         : step_gemm_workspace<float>((int)BT, (int)C, md->V);
   md->gemm_ws_floats = ws;
   md->gemm_ws = F(ws ? ws : 1);
@@ -315,13 +329,37 @@ int ln_backward(gpt2_model* md, float* dx, float* dw, float* db, const float* do
 int ln_backward(gpt2_model* md, float* dx, float* dw, float* db, const bf16_t* dout,
                 const bf16_t* x, const float* w, const float* mean, const float* rstd, int BT,
                 bool acc) {
-  return layernorm_backward(dx, md->dres_h, dw, db, dout, x, w, mean, rstd, BT, md->C, acc,
-                            md->ln_ws, md->stream);
+  return layernorm_backward(dx, static_cast<bf16_t*>(md->dres_h), dw, db, dout, x, w, mean, rstd,
+                            BT, md->C, acc, md->ln_ws, md->stream);
+}
+int ln_backward(gpt2_model* md, float* dx, float* dw, float* db, const f16_t* dout,
+                const f16_t* x, const float* w, const float* mean, const float* rstd, int BT,
+                bool acc) {
+  return layernorm_backward(dx, static_cast<f16_t*>(md->dres_h), dw, db, dout, x, w, mean, rstd,
+                            BT, md->C, acc, md->ln_ws, md->stream);
+}
+// softmax + cross-entropy backward in place; in fp16 the gradient carries the loss scale
+int xent_backward(gpt2_model* md, float* logits, float dloss, int BT) {
+  return crossentropy_backward(logits, md->xent_lse, md->tgt, dloss, BT, md->V, md->Vp,
+                               md->stream);
+}
+int xent_backward(gpt2_model* md, bf16_t* logits, float dloss, int BT) {
+  return crossentropy_backward(logits, md->xent_lse, md->tgt, dloss, BT, md->V, md->Vp,
+                               md->stream);
+}
+int xent_backward(gpt2_model* md, f16_t* logits, float dloss, int BT) {
+  return crossentropy_backward(logits, md->xent_lse, md->tgt, dloss, md->d_scale, BT, md->V,
+                               md->Vp, md->stream);
 }
 // the residual-stream gradient as a GEMM operand
 template <typename T> const T* dres_operand(gpt2_model* md);
 template <> const float* dres_operand<float>(gpt2_model* md) { return md->dres; }
-template <> const bf16_t* dres_operand<bf16_t>(gpt2_model* md) { return md->dres_h; }
+template <> const bf16_t* dres_operand<bf16_t>(gpt2_model* md) {
+  return static_cast<const bf16_t*>(md->dres_h);
+}
+template <> const f16_t* dres_operand<f16_t>(gpt2_model* md) {
+  return static_cast<const f16_t*>(md->dres_h);
+}
 
 // "llm.c 的中文注解-20240421" section 1.23 (gpt2_forward), on md->tok / md->tgt
 template <typename T>
@@ -436,7 +474,7 @@ int backward_impl(gpt2_model* md) {
   T* logits = act<T>(md->logits);
   T* dln = act<T>(md->dln);
   // d(mean loss)/d(loss_bt) = 1/(B*T), through softmax + cross-entropy, in place
-  CHK(crossentropy_backward(logits, md->xent_lse, md->tgt, 1.0f / (float)BT, BT, V, md->Vp, s));
+  CHK(xent_backward(md, logits, 1.0f / (float)BT, BT));
   {
     GT d;  // dlnf = dlogits . wte
     d.A = logits;
@@ -590,7 +628,9 @@ int gpt2_profile_summary(char* buf, size_t len) {
   return GPT2_OK;
 }
 
-const char* gpt2_version(void) { return "gpt2-mi355x 0.2 (gfx950, fp32 and bf16 MFMA)"; }
+const char* gpt2_version(void) {
+  return "gpt2-mi355x 0.3 (gfx950; fp32, bf16 and fp16 MFMA)";
+}
 
 const char* gpt2_last_error(const gpt2_model* md) { return md ? md->err : gpt2::g_err; }
 
@@ -608,7 +648,7 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
                 "(C=%d H=%d)", C, H);
   if ((C / 4 + 63) / 64 > 8)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: C=%d above the supported 2048", C);
-  if (dtype != GPT2_DTYPE_FP32 && dtype != GPT2_DTYPE_BF16)
+  if (dtype != GPT2_DTYPE_FP32 && dtype != GPT2_DTYPE_BF16 && dtype != GPT2_DTYPE_FP16)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: dtype %d is not supported", dtype);
   if ((maxB > 0) != (maxTseq > 0) || maxTseq > maxT)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: bad preallocation shape");
@@ -637,8 +677,8 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
   }
   md->nparams = o;
   // every tensor offset must keep 16-byte alignment for the vector kernels (fp32 params;
-  // bf16 weight copy in mixed precision)
-  const size_t align = dtype == GPT2_DTYPE_BF16 ? 8 : 4;
+  // 16-bit weight copy in mixed precision)
+  const size_t align = half_dtype(dtype) ? 8 : 4;
   for (int k = 0; k < 16; k++)
     if (md->poff[k] % align) {
       delete md;
@@ -671,6 +711,26 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
       return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: memset failed");
     }
   }
+  if (dtype == GPT2_DTYPE_FP16) {
+    // the fp16 weight copy, then 256 bytes for the loss scaler state
+    void* q = nullptr;
+    if (hipMalloc(&q, stride * sizeof(f16_t) + 256) != hipSuccess || !q) {
+      (void)hipGetLastError();
+      gpt2_free(md);
+      return fail(nullptr, GPT2_ERR_OOM, "gpt2_build: cannot allocate the fp16 weight copy");
+    }
+    md->pf16 = static_cast<f16_t*>(q);
+    md->d_scale = reinterpret_cast<float*>(static_cast<char*>(q) + stride * sizeof(f16_t));
+    md->d_scaler = reinterpret_cast<int32_t*>(md->d_scale + 4);
+    const float st[2] = {65536.f, 1.f / 65536.f};
+    if (hipMemsetAsync(q, 0, stride * sizeof(f16_t) + 256, md->stream) != hipSuccess ||
+        hipMemcpyAsync(md->d_scale, st, sizeof(st), hipMemcpyHostToDevice, md->stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(md->stream) != hipSuccess) {
+      gpt2_free(md);
+      return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: initialising the fp16 state failed");
+    }
+  }
   if (hipMemsetAsync(md->pbuf, 0, 4 * stride * sizeof(float), md->stream) != hipSuccess) {
     gpt2_free(md);
     return fail(nullptr, GPT2_ERR_HIP, "gpt2_build: memset failed");
@@ -700,6 +760,7 @@ void gpt2_free(gpt2_model* md) {
   if (md->abuf) (void)hipFree(md->abuf);
   if (md->pbuf) (void)hipFree(md->pbuf);
   if (md->pbf) (void)hipFree(md->pbf);
+  if (md->pf16) (void)hipFree(md->pf16);
   delete md;
 }
 
@@ -718,6 +779,36 @@ int gpt2_synchronize(gpt2_model* md) {
 }
 
 size_t gpt2_num_params(const gpt2_model* md) { return md ? md->nparams : 0; }
+
+int gpt2_get_config(const gpt2_model* md, int cfg[5]) {
+  if (!md || !cfg) return fail(nullptr, GPT2_ERR_ARG, "gpt2_get_config: NULL");
+  cfg[0] = md->L;
+  cfg[1] = md->C;
+  cfg[2] = md->NH;
+  cfg[3] = md->V;
+  cfg[4] = md->maxT;
+  return GPT2_OK;
+}
+
+int gpt2_sample(gpt2_model* md, int b, int t, float coin, int32_t* token) {
+  if (!md || !token) return fail(md, GPT2_ERR_ARG, "gpt2_sample: NULL");
+  if (!md->logits_valid) return fail(md, GPT2_ERR_STATE, "gpt2_sample: logits are not available");
+  if (b < 0 || b >= md->B || t < 0 || t >= md->T || !(coin >= 0.f && coin < 1.f))
+    return fail(md, GPT2_ERR_ARG, "gpt2_sample: position (%d, %d) or coin %g out of range", b, t,
+                (double)coin);
+  const size_t row = ((size_t)b * md->T + t) * md->Vp;
+  // the token-sort scratch is only used by the backward, which invalidates the logits
+  int32_t* out = md->sort_scratch;
+  if (md->dtype == GPT2_DTYPE_BF16)
+    CHK(sample_mult(out, static_cast<const bf16_t*>(md->logits) + row, md->V, coin, md->stream));
+  else if (md->dtype == GPT2_DTYPE_FP16)
+    CHK(sample_mult(out, static_cast<const f16_t*>(md->logits) + row, md->V, coin, md->stream));
+  else
+    CHK(sample_mult(out, static_cast<const float*>(md->logits) + row, md->V, coin, md->stream));
+  HIPCHK(hipMemcpyAsync(token, out, sizeof(int32_t), hipMemcpyDeviceToHost, md->stream));
+  HIPCHK(hipStreamSynchronize(md->stream));
+  return GPT2_OK;
+}
 
 int gpt2_param_layout(const gpt2_model* md, size_t off[16], size_t len[16]) {
   if (!md || !off || !len) return fail(nullptr, GPT2_ERR_ARG, "gpt2_param_layout: NULL");
@@ -741,19 +832,76 @@ int gpt2_set_params(gpt2_model* md, const float* src, int src_is_device) {
   if (md && !src) return fail(md, GPT2_ERR_ARG, "gpt2_set_params: NULL source");
   int rc = xfer(md, md ? md->params : nullptr, src, nullptr, src_is_device);
   if (!rc && md->pbf) CHK(cast_f32_to_bf16(md->pbf, md->params, md->nparams, md->stream));
+  if (!rc && md->pf16) CHK(cast_f32_to_f16(md->pf16, md->params, md->nparams, md->stream));
   return rc;
 }
 int gpt2_get_params(gpt2_model* md, float* dst, int dst_is_device) {
   return xfer(md, md ? md->params : nullptr, nullptr, dst, dst_is_device);
 }
 int gpt2_get_grads(gpt2_model* md, float* dst, int dst_is_device) {
+  if (md && md->dtype == GPT2_DTYPE_FP16) {
+    // the stored gradients carry the loss scale: hand out grads / scale (exact: a power of 2)
+    if (!dst) return fail(md, GPT2_ERR_ARG, "NULL buffer");
+    if (dst_is_device) {
+      CHK(scale_copy(dst, md->grads, md->d_scale + 1, md->nparams, md->stream));
+      HIPCHK(hipStreamSynchronize(md->stream));
+      return GPT2_OK;
+    }
+    float* tmp = nullptr;
+    if (hipMalloc(&tmp, md->nparams * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(md, GPT2_ERR_OOM, "gpt2_get_grads: no memory to unscale the gradients");
+    }
+    int rc = chk(md, scale_copy(tmp, md->grads, md->d_scale + 1, md->nparams, md->stream));
+    if (!rc) rc = copy_floats(md, dst, tmp, md->nparams, hipMemcpyDeviceToHost);
+    (void)hipFree(tmp);
+    return rc;
+  }
   return xfer(md, md ? md->grads : nullptr, nullptr, dst, dst_is_device);
 }
 int gpt2_set_grads(gpt2_model* md, const float* src, int src_is_device) {
   if (md && !src) return fail(md, GPT2_ERR_ARG, "gpt2_set_grads: NULL source");
   int rc = xfer(md, md ? md->grads : nullptr, src, nullptr, src_is_device);
+  if (!rc && md->dtype == GPT2_DTYPE_FP16)  // stored with the loss scale, as backward leaves them
+    CHK(scale_copy(md->grads, md->grads, md->d_scale, md->nparams, md->stream));
   if (!rc) md->has_grads = true;
   return rc;
+}
+
+int gpt2_set_loss_scale(gpt2_model* md, float scale, int growth_interval) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (md->dtype != GPT2_DTYPE_FP16)
+    return fail(md, GPT2_ERR_ARG, "gpt2_set_loss_scale: only fp16 models scale the loss");
+  int e = 0;
+  if (!(scale >= 1.f && scale <= 16777216.f) || std::frexp(scale, &e) != 0.5f ||
+      growth_interval < 0)
+    return fail(md, GPT2_ERR_ARG, "gpt2_set_loss_scale: scale must be a power of two in "
+                "[1, 2^24] and growth_interval >= 0 (got %g, %d)", (double)scale,
+                growth_interval);
+  const float st[2] = {scale, 1.f / scale};
+  const int32_t cnt[3] = {0, 0, 0};
+  HIPCHK(hipMemcpyAsync(md->d_scale, st, sizeof(st), hipMemcpyHostToDevice, md->stream));
+  HIPCHK(hipMemcpyAsync(md->d_scaler, cnt, sizeof(cnt), hipMemcpyHostToDevice, md->stream));
+  HIPCHK(hipStreamSynchronize(md->stream));
+  md->growth_interval = growth_interval;
+  return GPT2_OK;
+}
+
+int gpt2_get_loss_scale(gpt2_model* md, float* scale, int* last_step_skipped) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (md->dtype != GPT2_DTYPE_FP16) {
+    if (scale) *scale = 1.f;
+    if (last_step_skipped) *last_step_skipped = 0;
+    return GPT2_OK;
+  }
+  float st[2];
+  int32_t cnt[3];
+  HIPCHK(hipMemcpyAsync(st, md->d_scale, sizeof(st), hipMemcpyDeviceToHost, md->stream));
+  HIPCHK(hipMemcpyAsync(cnt, md->d_scaler, sizeof(cnt), hipMemcpyDeviceToHost, md->stream));
+  HIPCHK(hipStreamSynchronize(md->stream));
+  if (scale) *scale = st[0];
+  if (last_step_skipped) *last_step_skipped = cnt[2];
+  return GPT2_OK;
 }
 int gpt2_get_adam_state(gpt2_model* md, float* m, float* v, int dst_is_device) {
   if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
@@ -775,15 +923,18 @@ int gpt2_get_losses(gpt2_model* md, float* dst, int dst_is_device) {
 int gpt2_get_logits(gpt2_model* md, float* dst, int dst_is_device) {
   if (!md || !dst) return fail(md, GPT2_ERR_ARG, "gpt2_get_logits: NULL");
   if (!md->logits_valid) return fail(md, GPT2_ERR_STATE, "logits are not available");
-  if (md->dtype == GPT2_DTYPE_BF16) {  // widen the bf16 logits through a temporary
+  if (half_dtype(md->dtype)) {  // widen the 16-bit logits through a temporary
     const size_t n = (size_t)md->B * md->T * md->Vp;
     float* tmp = nullptr;
     if (hipMalloc(&tmp, n * sizeof(float)) != hipSuccess) {
       (void)hipGetLastError();
       return fail(md, GPT2_ERR_OOM, "gpt2_get_logits: no memory to widen the logits");
     }
-    int rc = chk(md, cast_bf16_to_f32(tmp, static_cast<const bf16_t*>(md->logits), n,
-                                      md->stream));
+    int rc = chk(md, md->dtype == GPT2_DTYPE_FP16
+                         ? cast_f16_to_f32(tmp, static_cast<const f16_t*>(md->logits), n,
+                                           md->stream)
+                         : cast_bf16_to_f32(tmp, static_cast<const bf16_t*>(md->logits), n,
+                                            md->stream));
     hipError_t e = rc ? hipSuccess
                       : hipMemcpy2DAsync(dst, (size_t)md->V * sizeof(float), tmp,
                                          (size_t)md->Vp * sizeof(float),
@@ -828,6 +979,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   if (targets)
     HIPCHK(hipMemcpyAsync(md->tgt, targets, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
   if (md->dtype == GPT2_DTYPE_BF16) CHK(forward_impl<bf16_t>(md, targets != nullptr));
+  else if (md->dtype == GPT2_DTYPE_FP16) CHK(forward_impl<f16_t>(md, targets != nullptr));
   else CHK(forward_impl<float>(md, targets != nullptr));
   md->logits_valid = true;
   if (targets) md->fwd_targets = true;
@@ -858,6 +1010,7 @@ int gpt2_backward(gpt2_model* md) {
     return fail(md, GPT2_ERR_STATE, "gpt2_backward: needs a forward with targets first");
   md->logits_valid = false;
   if (md->dtype == GPT2_DTYPE_BF16) CHK(backward_impl<bf16_t>(md));
+  else if (md->dtype == GPT2_DTYPE_FP16) CHK(backward_impl<f16_t>(md));
   else CHK(backward_impl<float>(md));
   md->has_grads = true;
   return GPT2_OK;
@@ -868,6 +1021,15 @@ int gpt2_adamw_step(gpt2_model* md, float lr, float beta1, float beta2, float ep
   if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
   if (t < 1) return fail(md, GPT2_ERR_ARG, "gpt2_adamw_step: t must be >= 1 (got %d)", t);
   if (!md->has_grads) return fail(md, GPT2_ERR_STATE, "gpt2_adamw_step: no gradients yet");
+  if (md->dtype == GPT2_DTYPE_FP16) {
+    // skip the update if the scaled gradients overflowed, unscale them otherwise, then let
+    // the scaler react
+    CHK(grads_nonfinite(md->d_scaler, md->grads, md->nparams, md->stream));
+    CHK(adamw(md->params, md->grads, md->m, md->v, md->pf16, md->nparams, lr, beta1, beta2, eps,
+              weight_decay, t, md->d_scale + 1, md->d_scaler, md->stream));
+    CHK(loss_scaler_update(md->d_scale, md->d_scaler, md->growth_interval, md->stream));
+    return GPT2_OK;
+  }
   CHK(adamw(md->params, md->grads, md->m, md->v, md->pbf, md->nparams, lr, beta1, beta2, eps,
             weight_decay, t, md->stream));
   return GPT2_OK;
@@ -1102,6 +1264,12 @@ int gpt2_k_crossentropy_backward(float* logits, const float* lse, const int32_t*
   return crossentropy_backward(logits, lse, targets, dloss, N, V, ld, as_stream(stream));
 }
 
+int gpt2_k_sample_mult(int32_t* token, const float* logits, int V, float coin, void* stream) {
+  if (!token || !logits || V < 1 || !(coin >= 0.f && coin < 1.f))
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_k_sample_mult: bad argument");
+  return sample_mult(token, logits, V, coin, as_stream(stream));
+}
+
 int gpt2_k_mean(float* out, const float* x, int n, void* stream) {
   if (!out || !x) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
   return mean_reduce(out, x, n, as_stream(stream));
@@ -1136,6 +1304,42 @@ int gpt2_k_gemm_bf16(void* C, uint16_t* C2, const uint16_t* R, const uint16_t* A
   if (ws && hipMalloc(&buf, ws * sizeof(float)) != hipSuccess)
     return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
   int rc = gemm_bf16(g, buf, ws, s);
+  if (buf) {
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(buf);
+  }
+  return rc;
+}
+
+int gpt2_k_gemm_f16(void* C, uint16_t* C2, const uint16_t* R, const uint16_t* A,
+                     const uint16_t* B, const float* bias, float* colsum, int M, int N, int K,
+                     int lda, int ldb, int ldc, int a_trans, int b_trans, int epilogue,
+                     void* stream) {
+  if (!C || !A || !B || epilogue < 0 || epilogue > 4)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_k_gemm_f16: bad argument");
+  GemmF16 g;
+  g.A = reinterpret_cast<const f16_t*>(A);
+  g.lda = lda;
+  g.a_trans = a_trans != 0;
+  g.B = reinterpret_cast<const f16_t*>(B);
+  g.ldb = ldb;
+  g.b_trans = b_trans != 0;
+  g.C = C;
+  g.ldc = ldc;
+  g.C2 = reinterpret_cast<f16_t*>(C2);
+  g.R = reinterpret_cast<const f16_t*>(R);
+  g.bias = bias;
+  g.colsum = colsum;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi = static_cast<Epilogue>(epilogue);
+  hipStream_t s = as_stream(stream);
+  const size_t ws = M > 0 && N > 0 && K > 0 ? gemm_f16_workspace_floats(g) : 0;
+  float* buf = nullptr;
+  if (ws && hipMalloc(&buf, ws * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = gemm_f16(g, buf, ws, s);
   if (buf) {
     (void)hipStreamSynchronize(s);
     (void)hipFree(buf);
@@ -1190,6 +1394,31 @@ int gpt2_k_attention_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const u
   if (hipMalloc(&D, (nD + nS) * sizeof(float)) != hipSuccess)
     return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
   int rc = attention_backward(dqkv, dout, qkv, out, lse, D, D + nD, B, T, C, NH, s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(D);
+  return rc;
+}
+
+int gpt2_k_attention_forward_f16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
+                                 int C, int NH, void* stream) {
+  if (!out || !lse || !qkv) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  return attention_forward(reinterpret_cast<f16_t*>(out), lse,
+                           reinterpret_cast<const f16_t*>(qkv), B, T, C, NH, as_stream(stream));
+}
+
+int gpt2_k_attention_backward_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                                  const uint16_t* out, const float* lse, int B, int T, int C,
+                                  int NH, void* stream) {
+  if (!dqkv || !dout || !qkv || !out || !lse || B < 1 || T < 1 || NH < 1)
+    return fail(nullptr, GPT2_ERR_ARG, "bad argument");
+  hipStream_t s = as_stream(stream);
+  const size_t nD = (size_t)B * NH * T, nS = attention_ds_scratch_floats(B, T, NH);
+  float* D = nullptr;
+  if (hipMalloc(&D, (nD + nS) * sizeof(float)) != hipSuccess)
+    return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
+  int rc = attention_backward(reinterpret_cast<f16_t*>(dqkv), reinterpret_cast<const f16_t*>(dout),
+                              reinterpret_cast<const f16_t*>(qkv),
+                              reinterpret_cast<const f16_t*>(out), lse, D, D + nD, B, T, C, NH, s);
   (void)hipStreamSynchronize(s);
   (void)hipFree(D);
   return rc;

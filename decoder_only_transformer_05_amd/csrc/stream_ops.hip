@@ -242,10 +242,10 @@ GPT2_DEVICE_INLINE void lnb_fetch(R (&dy)[VPL], R (&xv)[VPL], const T* dout, con
 // take no registers across rows), then the four slices are added in wave order. A wave's
 // next row of dout and x is loaded while the current one is computed; the dx being
 // accumulated into is loaded at the start of its row and used after the two row sums.
-// dx is fp32; with bf16 activations dx_copy (if not null) receives dx rounded to bf16.
+// dx is fp32; with 16-bit activations dx_copy (if not null) receives dx rounded to T.
 template <int VPL, typename T>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
-    float* __restrict__ dx, bf16_t* __restrict__ dx_copy, float* __restrict__ partial,
+    float* __restrict__ dx, T* __restrict__ dx_copy, float* __restrict__ partial,
     const T* __restrict__ dout, const T* __restrict__ x, const float* __restrict__ w,
     const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C,
     int accumulate, int rows_per_block) {
@@ -431,15 +431,18 @@ __global__ __launch_bounds__(256) void xent_fwd_kernel(float* __restrict__ losse
   }
 }
 
-// in place: logits[r, v] <- (softmax - onehot(target)) * dloss for v < V, 0 on the padding.
+// in place: logits[r, v] <- (softmax - onehot(target)) * dloss for v < V, 0 on the padding;
+// with dscale (device, may be null) the factor is dloss * *dscale (a loss scale).
 // One 16-byte vector per thread over a flat grid: a workgroup covers 256 vectors of one row
 // (`chunks` workgroups per row), so the whole matrix streams in address order.
 template <typename T>
 __global__ __launch_bounds__(256) void xent_bwd_kernel(T* __restrict__ logits,
                                                        const float* __restrict__ lse,
                                                        const int32_t* __restrict__ targets,
-                                                       float dloss, int V, int ld, int chunks) {
+                                                       float dloss, const float* dscale, int V,
+                                                       int ld, int chunks) {
   constexpr int G = 16 / (4 * sizeof(T));  // groups of 4 elements per thread
+  if (dscale) dloss *= *dscale;
   const int row = blockIdx.x / chunks;
   const int c0 = ((blockIdx.x - row * chunks) * 256 + threadIdx.x) * 4 * G;
   if (c0 >= ld) return;
@@ -494,16 +497,24 @@ GPT2_DEVICE_INLINE float adamw_one(float& p, float g, float& m, float& v, float 
   return p;
 }
 
+// With a loss scale (inv_scale, device, may be null) the gradients are the scaled ones and
+// are multiplied by *inv_scale first; a nonzero *skip (device, may be null) leaves every
+// parameter and moment unchanged (the step's gradients overflowed).
+template <typename TP>
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
                                                     const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
-                                                    bf16_t* __restrict__ pbf, long long n4,
+                                                    TP* __restrict__ pbf, long long n4,
                                                     long long n, float lr, float b1, float b2,
                                                     float eps, float wd, float inv_c1,
-                                                    float inv_c2) {
+                                                    float inv_c2, const float* inv_scale,
+                                                    const int32_t* skip) {
+  if (skip && *skip) return;
+  const float gs = inv_scale ? *inv_scale : 1.f;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i < n4) {
     f32x4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
+    if (inv_scale) gg *= gs;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       float pj = pp[j], mj = mm[j], vj = vv[j];
@@ -520,15 +531,63 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
     const long long e = 4 * n4 + (i - n4);
     if (e >= n) return;
     float pe = p[e], me = m[e], ve = v[e];
-    adamw_one(pe, g[e], me, ve, lr, b1, b2, eps, wd, inv_c1, inv_c2);
+    adamw_one(pe, inv_scale ? g[e] * gs : g[e], me, ve, lr, b1, b2, eps, wd, inv_c1, inv_c2);
     p[e] = pe;
     m[e] = me;
     v[e] = ve;
-    if (pbf) pbf[e] = f32_to_bf16(pe);
+    if (pbf) st1(pbf + e, pe);
   }
 }
 
-// fp32 <-> bf16 copies (round to nearest even)
+// flag = 1 if any of the n gradients is an infinity or a NaN (the loss-scaled backward
+// overflowed); one float4 per thread
+__global__ __launch_bounds__(256) void nonfinite_kernel(int32_t* __restrict__ flag,
+                                                        const float* __restrict__ g, long long n4,
+                                                        long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  bool bad = false;
+  if (i < n4) {
+    const f32x4 x = ld4(g + 4 * i);
+    bad = !(isfinite(x[0]) && isfinite(x[1]) && isfinite(x[2]) && isfinite(x[3]));
+  } else {
+    const long long e = 4 * n4 + (i - n4);
+    if (e < n) bad = !isfinite(g[e]);
+  }
+  if (bad) *flag = 1;  // every writer stores the same value
+}
+
+// Dynamic loss scale, after each step's check: state = {scale, 1/scale}, counters =
+// {overflow flag, good steps since the last change, last step skipped}. An overflow halves
+// the scale (not below 1) and marks the step skipped; growth_interval steps in a row without
+// one double it (not above 2^24); growth_interval 0 keeps the scale fixed. The flag is
+// cleared for the next step.
+__global__ void scaler_update_kernel(float* __restrict__ state, int32_t* __restrict__ cnt,
+                                     int growth_interval) {
+  const int overflow = cnt[0];
+  cnt[2] = overflow;
+  cnt[0] = 0;
+  float s = state[0];
+  if (overflow) {
+    if (growth_interval > 0) s = fmaxf(1.f, s * 0.5f);
+    cnt[1] = 0;
+  } else if (growth_interval > 0 && ++cnt[1] >= growth_interval) {
+    s = fminf(16777216.f, s * 2.f);
+    cnt[1] = 0;
+  }
+  state[0] = s;
+  state[1] = 1.f / s;
+}
+
+// dst = src * (*factor), n floats (a power-of-two loss scale: exact)
+__global__ void scale_copy_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                  const float* __restrict__ factor, long long n) {
+  const float f = *factor;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    dst[i] = src[i] * f;
+}
+
+// fp32 <-> 16-bit copies (round to nearest even)
 template <typename TD, typename TS>
 __global__ void cast_kernel(TD* __restrict__ dst, const TS* __restrict__ src, long long n) {
   const long long n4 = n / 4;
@@ -572,6 +631,11 @@ int encoder_forward(bf16_t* out, const int32_t* tok, const float* wte, const flo
                     int T, int C, int V, int32_t* err_flag, hipStream_t stream) {
   return encoder_forward_t(out, tok, wte, wpe, B, T, C, V, err_flag, stream,
                            "encoder_fwd_bf16_kernel");
+}
+int encoder_forward(f16_t* out, const int32_t* tok, const float* wte, const float* wpe, int B,
+                    int T, int C, int V, int32_t* err_flag, hipStream_t stream) {
+  return encoder_forward_t(out, tok, wte, wpe, B, T, C, V, err_flag, stream,
+                           "encoder_fwd_f16_kernel");
 }
 
 size_t encoder_sort_scratch_ints(int BT, int V) { return (size_t)2 * V + BT; }
@@ -644,6 +708,11 @@ int layernorm_forward(bf16_t* out, float* mean, float* rstd, const bf16_t* x, co
   return layernorm_forward_t(out, mean, rstd, x, w, b, N, C, stream,
                              "layernorm_fwd_bf16_kernel");
 }
+int layernorm_forward(f16_t* out, float* mean, float* rstd, const f16_t* x, const float* w,
+                      const float* b, int N, int C, hipStream_t stream) {
+  return layernorm_forward_t(out, mean, rstd, x, w, b, N, C, stream,
+                             "layernorm_fwd_f16_kernel");
+}
 
 size_t layernorm_partial_floats(int N, int C) {
   const int rows = lnb_rows(N);
@@ -652,7 +721,7 @@ size_t layernorm_partial_floats(int N, int C) {
 
 namespace {
 template <typename T>
-int layernorm_backward_t(float* dx, bf16_t* dx_copy, float* dw, float* db, const T* dout,
+int layernorm_backward_t(float* dx, T* dx_copy, float* dw, float* db, const T* dout,
                          const T* x, const float* w, const float* mean, const float* rstd, int N,
                          int C, bool accumulate_dx, float* partial, hipStream_t stream,
                          const char* name) {
@@ -688,7 +757,7 @@ int layernorm_backward_t(float* dx, bf16_t* dx_copy, float* dw, float* db, const
 int layernorm_backward(float* dx, float* dw, float* db, const float* dout, const float* x,
                        const float* w, const float* mean, const float* rstd, int N, int C,
                        bool accumulate_dx, float* partial, hipStream_t stream) {
-  return layernorm_backward_t(dx, (bf16_t*)nullptr, dw, db, dout, x, w, mean, rstd, N, C,
+  return layernorm_backward_t(dx, (float*)nullptr, dw, db, dout, x, w, mean, rstd, N, C,
                               accumulate_dx, partial, stream, "layernorm_bwd_kernel");
 }
 int layernorm_backward(float* dx, bf16_t* dx_copy, float* dw, float* db, const bf16_t* dout,
@@ -696,6 +765,12 @@ int layernorm_backward(float* dx, bf16_t* dx_copy, float* dw, float* db, const b
                        int N, int C, bool accumulate_dx, float* partial, hipStream_t stream) {
   return layernorm_backward_t(dx, dx_copy, dw, db, dout, x, w, mean, rstd, N, C, accumulate_dx,
                               partial, stream, "layernorm_bwd_bf16_kernel");
+}
+int layernorm_backward(float* dx, f16_t* dx_copy, float* dw, float* db, const f16_t* dout,
+                       const f16_t* x, const float* w, const float* mean, const float* rstd,
+                       int N, int C, bool accumulate_dx, float* partial, hipStream_t stream) {
+  return layernorm_backward_t(dx, dx_copy, dw, db, dout, x, w, mean, rstd, N, C, accumulate_dx,
+                              partial, stream, "layernorm_bwd_f16_kernel");
 }
 
 namespace {
@@ -715,7 +790,8 @@ int crossentropy_forward_t(float* losses, float* lse, const T* logits, const int
 
 template <typename T>
 int crossentropy_backward_t(T* logits, const float* lse, const int32_t* targets, float dloss,
-                            int N, int V, int ld, hipStream_t stream, const char* name) {
+                            const float* dscale, int N, int V, int ld, hipStream_t stream,
+                            const char* name) {
   if (N < 1 || V < 1 || ld < V || ld % 4 || !aligned16(logits)) {
     set_global_error("crossentropy_backward: bad arguments");
     return -1;
@@ -727,7 +803,8 @@ int crossentropy_backward_t(T* logits, const float* lse, const int32_t* targets,
     return -1;
   }
   ProfScope ps(name, 3.0 * N * V, 2.0 * sizeof(T) * N * ld + 8.0 * N, stream);
-  xent_bwd_kernel<T><<<N * chunks, 256, 0, stream>>>(logits, lse, targets, dloss, V, ld, chunks);
+  xent_bwd_kernel<T><<<N * chunks, 256, 0, stream>>>(logits, lse, targets, dloss, dscale, V, ld,
+                                                     chunks);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
@@ -745,13 +822,23 @@ int crossentropy_forward(float* losses, float* lse, const bf16_t* logits, const 
 }
 int crossentropy_backward(float* logits, const float* lse, const int32_t* targets, float dloss,
                           int N, int V, int ld, hipStream_t stream) {
-  return crossentropy_backward_t(logits, lse, targets, dloss, N, V, ld, stream,
-                                 "xent_bwd_kernel");
+  return crossentropy_backward_t(logits, lse, targets, dloss, (const float*)nullptr, N, V, ld,
+                                 stream, "xent_bwd_kernel");
 }
 int crossentropy_backward(bf16_t* logits, const float* lse, const int32_t* targets, float dloss,
                           int N, int V, int ld, hipStream_t stream) {
-  return crossentropy_backward_t(logits, lse, targets, dloss, N, V, ld, stream,
-                                 "xent_bwd_bf16_kernel");
+  return crossentropy_backward_t(logits, lse, targets, dloss, (const float*)nullptr, N, V, ld,
+                                 stream, "xent_bwd_bf16_kernel");
+}
+int crossentropy_forward(float* losses, float* lse, const f16_t* logits, const int32_t* targets,
+                         int N, int V, int ld, int32_t* err_flag, hipStream_t stream) {
+  return crossentropy_forward_t(losses, lse, logits, targets, N, V, ld, err_flag, stream,
+                                "xent_fwd_f16_kernel");
+}
+int crossentropy_backward(f16_t* logits, const float* lse, const int32_t* targets, float dloss,
+                          const float* dscale, int N, int V, int ld, hipStream_t stream) {
+  return crossentropy_backward_t(logits, lse, targets, dloss, dscale, N, V, ld, stream,
+                                 "xent_bwd_f16_kernel");
 }
 
 int mean_reduce(float* out, const float* x, int n, hipStream_t stream) {
@@ -762,8 +849,11 @@ int mean_reduce(float* out, const float* x, int n, hipStream_t stream) {
   return 0;
 }
 
-int adamw(float* p, const float* g, float* m, float* v, bf16_t* pbf, size_t n, float lr,
-          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream) {
+namespace {
+template <typename TP>
+int adamw_t(float* p, const float* g, float* m, float* v, TP* pbf, size_t n, float lr,
+            float beta1, float beta2, float eps, float wd, int t, const float* inv_scale,
+            const int32_t* skip, hipStream_t stream) {
   if (t < 1 || !aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v) ||
       (pbf && ((uintptr_t)pbf & 7))) {
     set_global_error("adamw: bad arguments (t=%d)", t);
@@ -775,14 +865,82 @@ int adamw(float* p, const float* g, float* m, float* v, bf16_t* pbf, size_t n, f
   ProfScope ps("adamw_kernel", 12.0 * n, (pbf ? 30.0 : 28.0) * n, stream);
   const long long threads = n4 + (long long)(n - 4 * n4);
   if (threads == 0) return 0;
-  adamw_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
-      p, g, m, v, pbf, n4, (long long)n, lr, beta1, beta2, eps, wd, inv_c1, inv_c2);
+  adamw_kernel<TP><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
+      p, g, m, v, pbf, n4, (long long)n, lr, beta1, beta2, eps, wd, inv_c1, inv_c2, inv_scale,
+      skip);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+}  // namespace
+
+int adamw(float* p, const float* g, float* m, float* v, bf16_t* pbf, size_t n, float lr,
+          float beta1, float beta2, float eps, float wd, int t, hipStream_t stream) {
+  return adamw_t(p, g, m, v, pbf, n, lr, beta1, beta2, eps, wd, t, nullptr, nullptr, stream);
+}
+int adamw(float* p, const float* g, float* m, float* v, f16_t* pf16, size_t n, float lr,
+          float beta1, float beta2, float eps, float wd, int t, const float* inv_scale,
+          const int32_t* skip, hipStream_t stream) {
+  return adamw_t(p, g, m, v, pf16, n, lr, beta1, beta2, eps, wd, t, inv_scale, skip, stream);
+}
+
+int grads_nonfinite(int32_t* flag, const float* g, size_t n, hipStream_t stream) {
+  if (!aligned16(g)) {
+    set_global_error("grads_nonfinite: misaligned gradients");
+    return -1;
+  }
+  const long long n4 = (long long)(n / 4), threads = n4 + (long long)(n - 4 * n4);
+  if (threads == 0) return 0;
+  ProfScope ps("nonfinite_kernel", 0.0, 4.0 * n, stream);
+  nonfinite_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(flag, g, n4,
+                                                                         (long long)n);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int loss_scaler_update(float* state, int32_t* counters, int growth_interval,
+                       hipStream_t stream) {
+  scaler_update_kernel<<<1, 1, 0, stream>>>(state, counters, growth_interval);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int scale_copy(float* dst, const float* src, const float* factor, size_t n, hipStream_t stream) {
+  if (n == 0) return 0;
+  ProfScope ps("scale_copy_kernel", (double)n, 8.0 * n, stream);
+  scale_copy_kernel<<<blocks_for((long long)n, 256, 16384), 256, 0, stream>>>(dst, src, factor,
+                                                                              (long long)n);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
 
 int cast_f32_to_bf16(bf16_t* dst, const float* src, size_t n, hipStream_t stream) {
   if (((uintptr_t)dst & 7) || !aligned16(src)) {
+    set_global_error("cast: misaligned buffers");
+    return -1;
+  }
+  if (n == 0) return 0;
+  ProfScope ps("cast_kernel", 0.0, 6.0 * n, stream);
+  cast_kernel<<<blocks_for((long long)n / 4 + 1, 256, 16384), 256, 0, stream>>>(dst, src,
+                                                                                 (long long)n);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int cast_f32_to_f16(f16_t* dst, const float* src, size_t n, hipStream_t stream) {
+  if (((uintptr_t)dst & 7) || !aligned16(src)) {
+    set_global_error("cast: misaligned buffers");
+    return -1;
+  }
+  if (n == 0) return 0;
+  ProfScope ps("cast_kernel", 0.0, 6.0 * n, stream);
+  cast_kernel<<<blocks_for((long long)n / 4 + 1, 256, 16384), 256, 0, stream>>>(dst, src,
+                                                                                 (long long)n);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+int cast_f16_to_f32(float* dst, const f16_t* src, size_t n, hipStream_t stream) {
+  if (!aligned16(dst) || ((uintptr_t)src & 7)) {
     set_global_error("cast: misaligned buffers");
     return -1;
   }

@@ -147,7 +147,7 @@ class Workload:
     shape: ModelShape
     B: int
     T: int
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32", "bf16" or "fp16"
     scale_residual: bool
     token_mode: str
     seed: int
@@ -158,7 +158,8 @@ class Workload:
     weight_decay: float = 0.0
 
 
-# The five workloads: a tiny model, GPT-2 124M at two batch sizes, 350M, and 774M in bf16.
+# The workloads: a tiny model, GPT-2 124M at two batch sizes, 350M, and 774M in bf16 and in
+# fp16.
 WORKLOADS = {
     "tiny": Workload("tiny L1 C16 H4 V27 B4 T16 fp32", ModelShape(1, 16, 4, 27, 16), 4, 16,
                      "fp32", False, "independent", seed=1337),
@@ -173,4 +174,8 @@ WORKLOADS = {
     "gpt2_774m_b8_t1024_bf16": Workload("gpt2-774M B8 T1024 bf16",
                                         ModelShape(36, 1280, 20, 50257, 1024), 8, 1024,
                                         "bf16", True, "stream", seed=1341),
+    # the same shape and inputs in fp16 with loss scaling (the pages' "fp16 or lower")
+    "gpt2_774m_b8_t1024_fp16": Workload("gpt2-774M B8 T1024 fp16",
+                                        ModelShape(36, 1280, 20, 50257, 1024), 8, 1024,
+                                        "fp16", True, "stream", seed=1341),
 }

@@ -41,7 +41,8 @@ enum {
   GPT2_ERR_TOKEN = -3, /* a token or target outside [0, V) */
   GPT2_ERR_STATE = -4, /* call out of order (backward before a forward with targets, ...) */
   GPT2_ERR_OOM = -5,   /* device allocation failed */
-  GPT2_ERR_HIP = -6    /* a HIP runtime call failed */
+  GPT2_ERR_HIP = -6,   /* a HIP runtime call failed */
+  GPT2_ERR_IO = -7     /* a file could not be opened, read or written, or is malformed */
 };
 
 /* Arithmetic of the training step.
@@ -59,7 +60,18 @@ enum {
  *   stream gradient, the parameter gradients, the master parameters and the AdamW moments
  *   stay fp32. The ABI is unchanged: parameters, gradients, logits and losses are read
  *   and written as fp32. */
-enum { GPT2_DTYPE_FP32 = 0, GPT2_DTYPE_BF16 = 1 };
+/* GPT2_DTYPE_FP16: the same mixed precision with IEEE fp16 (11 significant bits, largest
+ *   finite 65504) in place of bf16, on fp16 MFMA. fp16's narrow exponent range needs loss
+ *   scaling: the backward starts from d(mean loss)/d(loss) = S/(B*T) with a power-of-two
+ *   loss scale S (2^16 at build), so every activation gradient is S times the true one and
+ *   stays clear of fp16 underflow; the parameter gradients accumulate the scaled values in
+ *   fp32. gpt2_adamw_step first checks them: if any is infinite or NaN (an fp16 overflow in
+ *   the backward), the step leaves parameters and moments unchanged ("skipped") and S is
+ *   halved; otherwise it applies AdamW to the gradients divided by S, and after every
+ *   growth_interval (2000) steps in a row without an overflow S doubles (at most 2^24).
+ *   gpt2_get_grads / gpt2_set_grads exchange unscaled gradients (exact: S is a power of
+ *   two). The scaler lives on the device; no step waits for it. */
+enum { GPT2_DTYPE_FP32 = 0, GPT2_DTYPE_BF16 = 1, GPT2_DTYPE_FP16 = 2 };
 
 /* ---------------------------------------------------------------------------------------
  * Model lifetime and parameters
@@ -74,8 +86,8 @@ enum { GPT2_DTYPE_FP32 = 0, GPT2_DTYPE_BF16 = 1 };
  * *out receives the handle, or NULL on error. */
 int gpt2_build(gpt2_model** out, int L, int C, int H, int V, int maxT);
 
-/* As gpt2_build, plus: dtype (GPT2_DTYPE_FP32 or GPT2_DTYPE_BF16; bf16 also needs every
- * parameter tensor to start at a multiple of 8 elements); if maxB > 0 and maxTseq > 0 the
+/* As gpt2_build, plus: dtype (GPT2_DTYPE_FP32, GPT2_DTYPE_BF16 or GPT2_DTYPE_FP16; the
+ * 16-bit dtypes also need every parameter tensor to start at a multiple of 8 elements); if maxB > 0 and maxTseq > 0 the
  * activation block is allocated now for exactly B = maxB, T = maxTseq; stream is the
  * hipStream_t the model enqueues all its work on (NULL = the null stream). */
 int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dtype,
@@ -91,6 +103,9 @@ int gpt2_set_stream(gpt2_model* model, void* stream);
 /* Block until all work enqueued on the model's stream has finished. Reports
  * GPT2_ERR_TOKEN if a forward since the last check saw an out-of-range token. */
 int gpt2_synchronize(gpt2_model* model);
+
+/* The model's configuration ([llm.c] 1.20 GPT2Config): cfg = {L, C, NH, V, maxT}. */
+int gpt2_get_config(const gpt2_model* model, int cfg[5]);
 
 /* Number of fp32 parameters: the sum of the 16 tensor sizes of [llm.c] 1.22. */
 size_t gpt2_num_params(const gpt2_model* model);
@@ -109,6 +124,14 @@ int gpt2_get_params(gpt2_model* model, float* dst, int dst_is_device);
 int gpt2_get_grads(gpt2_model* model, float* dst, int dst_is_device);
 /* Overwrite the gradients (flat layout); lets a caller run gpt2_adamw_step on given grads. */
 int gpt2_set_grads(gpt2_model* model, const float* src, int src_is_device);
+/* GPT2_DTYPE_FP16 loss scaling (see GPT2_DTYPE_FP16): set the scale S (a power of two in
+ * [1, 2^24]) and the growth interval (steps without overflow before S doubles; 0 keeps S
+ * fixed, though an overflowing step is still skipped); waits for the stream. ERR_ARG for
+ * other dtypes or bad values. gpt2_get_loss_scale waits for the stream and returns S and
+ * whether the last gpt2_adamw_step was skipped (1) or applied (0); other dtypes report
+ * S = 1, not skipped. Either output pointer may be NULL. */
+int gpt2_set_loss_scale(gpt2_model* model, float scale, int growth_interval);
+int gpt2_get_loss_scale(gpt2_model* model, float* scale, int* last_step_skipped);
 /* AdamW first and second moments (flat layout); either pointer may be NULL. */
 int gpt2_get_adam_state(gpt2_model* model, float* m, float* v, int dst_is_device);
 
@@ -147,6 +170,62 @@ int gpt2_backward(gpt2_model* model);
  * t is the 1-based step count (ERR_ARG if t < 1). */
 int gpt2_adamw_step(gpt2_model* model, float lr, float beta1, float beta2, float eps,
                     float weight_decay, int t);
+
+/* ---------------------------------------------------------------------------------------
+ * Checkpoints, token files, sampling
+ * ------------------------------------------------------------------------------------- */
+
+/* Checkpoint files in the format [llm.c] 1.22 gpt2_build_from_checkpoint reads: 256 int32
+ * (magic 20240326, version 1, maxT, V, L, NH, C, then zeros), followed by the fp32
+ * parameters in the flat order of gpt2_param_layout ([llm.c] 1.16). Native byte order.
+ * gpt2_checkpoint_info checks the header (magic, version, positive sizes) and that the file
+ * holds exactly the parameters the header implies, and returns the configuration (any
+ * output pointer may be NULL). gpt2_checkpoint_read reads the n = num_params floats into
+ * host memory (ERR_ARG if n differs). gpt2_checkpoint_write writes a checkpoint from host
+ * parameters (count implied by the sizes). Malformed or unreadable files: GPT2_ERR_IO.
+ * These three need no GPU. */
+int gpt2_checkpoint_info(const char* path, int* maxT, int* V, int* L, int* NH, int* C,
+                         size_t* num_params);
+int gpt2_checkpoint_read(const char* path, float* params, size_t n);
+int gpt2_checkpoint_write(const char* path, int maxT, int V, int L, int NH, int C,
+                          const float* params);
+/* gpt2_build_ex with the configuration and parameters of a checkpoint file (the remaining
+ * arguments as for gpt2_build_ex); *out is NULL on error. */
+int gpt2_build_from_checkpoint(gpt2_model** out, const char* path, int dtype, int maxB,
+                               int maxTseq, void* stream);
+/* Write the model's current fp32 parameters as a checkpoint (waits for the stream). */
+int gpt2_save_checkpoint(gpt2_model* model, const char* path);
+
+/* Token files as [llm.c] 1.28 - 1.32 DataLoader reads them: a flat file of int32 tokens.
+ * Each batch is the next window of B*T+1 tokens: inputs = window[0, B*T), targets =
+ * window[1, B*T+1) (shifted by one); the window then advances by B*T tokens, and starts
+ * again at the beginning of the file when the next window would run past its end.
+ * gpt2_dataloader_init: ERR_IO if the file cannot be opened, ERR_ARG if it holds fewer than
+ * B*T+1 tokens. gpt2_dataloader_num_batches: file size / (B*T*4), as the page counts.
+ * gpt2_dataloader_next_batch copies the batch into inputs and targets (B*T int32 each; host
+ * memory, or device memory when dst_is_device, copied on `stream` and waited for). Token
+ * values are not checked here (gpt2_forward checks them against V). */
+typedef struct gpt2_dataloader gpt2_dataloader;
+int gpt2_dataloader_init(gpt2_dataloader** out, const char* path, int B, int T);
+int gpt2_dataloader_num_batches(const gpt2_dataloader* loader);
+int gpt2_dataloader_reset(gpt2_dataloader* loader);
+int gpt2_dataloader_next_batch(gpt2_dataloader* loader, int32_t* inputs, int32_t* targets,
+                               int dst_is_device, void* stream);
+void gpt2_dataloader_free(gpt2_dataloader* loader);
+
+/* [llm.c] 1.33 random_u32: xorshift* on a 64-bit state (shifts 12, 25, 27; the upper 32 bits
+ * of the state times 0x2545F4914F6CDD1D). The state must not be 0. [llm.c] 1.34 random_f32:
+ * the upper 24 bits of the next draw over 2^24, a float in [0, 1). Host functions. */
+uint32_t gpt2_random_u32(uint64_t* state);
+float gpt2_random_f32(uint64_t* state);
+
+/* [llm.c] 1.35 sample_mult on the probabilities softmax(logits[b, t, :]) of the model's
+ * last forward (valid between a forward and the next backward, else ERR_STATE): the
+ * smallest token index i whose cumulative probability exceeds coin (coin in [0, 1), e.g.
+ * from gpt2_random_f32), or V - 1 if rounding leaves every cumulative value at or below
+ * coin. The probabilities and their running sum are fp32, the sum in index order within
+ * fixed chunks. Waits for the stream and stores the index in *token (host). */
+int gpt2_sample(gpt2_model* model, int b, int t, float coin, int32_t* token);
 
 /* Launch profiler. gpt2_profile_enable(1) clears the record and from then on brackets every
  * kernel launch of the library with two HIP events on the launch's stream, tagged with the
@@ -254,6 +333,10 @@ int gpt2_k_crossentropy_forward(float* losses, float* lse, const float* logits,
 int gpt2_k_crossentropy_backward(float* logits, const float* lse, const int32_t* targets,
                                  float dloss, int N, int V, int ld, void* stream);
 
+/* [llm.c] 1.35 on one row of fp32 logits (device, V entries): *token (device int32) = the
+ * index drawn with coin, as gpt2_sample. */
+int gpt2_k_sample_mult(int32_t* token, const float* logits, int V, float coin, void* stream);
+
 /* Mean of n floats into *out (device float), summed in a fixed order. */
 int gpt2_k_mean(float* out, const float* x, int n, void* stream);
 
@@ -280,6 +363,22 @@ int gpt2_k_gemm_bf16(void* C, uint16_t* C2, const uint16_t* R, const uint16_t* A
                      const uint16_t* B, const float* bias, float* colsum, int M, int N, int K,
                      int lda, int ldb, int ldc, int a_trans, int b_trans, int epilogue,
                      void* stream);
+
+/* The same GEMM on fp16 operands (uint16_t arrays holding IEEE binary16 values; results
+ * rounded to fp16 to nearest even) with fp16 MFMA and fp32 accumulation; arguments and
+ * requirements as gpt2_k_gemm_bf16. */
+int gpt2_k_gemm_f16(void* C, uint16_t* C2, const uint16_t* R, const uint16_t* A,
+                    const uint16_t* B, const float* bias, float* colsum, int M, int N, int K,
+                    int lda, int ldb, int ldc, int a_trans, int b_trans, int epilogue,
+                    void* stream);
+
+/* [llm.c] 1.7, 1.8 on fp16 qkv, out, dout and dqkv (lse fp32), as the bf16 forms: fp16
+ * MFMA products for head sizes that are multiples of 8, P and dS rounded to fp16. */
+int gpt2_k_attention_forward_f16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
+                                 int C, int NH, void* stream);
+int gpt2_k_attention_backward_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                                  const uint16_t* out, const float* lse, int B, int T, int C,
+                                  int NH, void* stream);
 
 /* [llm.c] 1.1 with a bf16 result: out (B,T,C) bf16 = wte[tok] + wpe[t] (fp32 tables). */
 int gpt2_k_encoder_forward_bf16(uint16_t* out, const int32_t* tok, const float* wte,

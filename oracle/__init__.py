@@ -54,6 +54,7 @@ _SIGS = {
     "oracle_adamw": (None, [_i64, _D, _D, _D, _D, ctypes.c_double, ctypes.c_double,
                             ctypes.c_double, ctypes.c_double, ctypes.c_double, _int]),
     "oracle_num_params": (_i64, [_int, _int, _int, _int]),
+    "oracle_sample_mult": (_int, [_D, _int, ctypes.c_double]),
     "oracle_gpt2_step": (_int, [_int, _int, _int, _int, _int, _D, _I, _I, _int, _int, _D, _D,
                                 _D, _D]),
     "oracle_gpt2_step_mag": (_int, [_int, _int, _int, _int, _int, _D, _I, _I, _int, _int, _D,
@@ -233,6 +234,12 @@ def crossentropy_softmax_backward(logits, targets, dlosses):
     lib().oracle_crossentropy_softmax_backward(_d(dz), _d(z), _i(i32(targets).reshape(-1)),
                                                _d(f64(dlosses).reshape(-1)), N, V)
     return dz
+
+
+def sample_mult(probs, coin) -> int:
+    """Index drawn from ``probs`` (summing to 1) with ``coin`` in [0, 1)."""
+    p = f64(probs).ravel()
+    return int(lib().oracle_sample_mult(_d(p), p.size, float(coin)))
 
 
 def adamw(p, g, m, v, lr, b1, b2, eps, wd, t):

@@ -551,6 +551,18 @@ void oracle_crossentropy_softmax_backward(double* dlogits, const double* logits,
   }
 }
 
+// [llm.c] 1.35 sample_mult: walk the cumulative distribution of probs (which sum to 1) and
+// return the first index whose cumulative value exceeds coin (coin in [0, 1)); if rounding
+// leaves every cumulative value at or below coin, the last index.
+int oracle_sample_mult(const double* probs, int n, double coin) {
+  double cdf = 0.0;
+  for (int i = 0; i < n; i++) {
+    cdf += probs[i];
+    if (coin < cdf) return i;
+  }
+  return n - 1;
+}
+
 // [llm.c] 1.26 gpt2_update (AdamW, as torch.optim.AdamW which the page cites):
 // m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2; mhat = m/(1-b1^t); vhat = v/(1-b2^t);
 // p -= lr (mhat / (sqrt(vhat) + eps) + wd p), with p the value before this update.

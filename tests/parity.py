@@ -16,10 +16,22 @@ Tolerance readings (fp32 path against the fp64 oracle):
     and bounded (a small fraction of the entries, all of them where terms cancel);
 - parameters after AdamW: max |a - o| <= 1e-5 (see the AdamW tests for the entries whose
   gradient is too small for that bound to be meaningful).
-bf16 mixed precision (the 774M workload): loss within 2e-2 relative; logits and gradients
-normwise within 2e-2 and 5e-2, and per entry |a - o| <= r |o| + r * mag with r the same
-2e-2 or 5e-2 (each bf16 rounding moves a factor by up to 2^-9 of itself, and about a
-hundred roundings lie on each path).
+16-bit mixed precision (bf16, and fp16 with a quarter of bf16's tolerances): loss within
+2e-2 relative; logits and gradients normwise within r = 2e-2 and 5e-2 (each bf16 rounding
+moves a factor by up to 2^-9 of itself, and about a hundred roundings lie on each path) --
+these measure the precision. The per-entry gates detect structural errors: an entry whose
+terms do not cancel (|o| close to mag) must not be off by a sizeable fraction of itself,
+as a wrong index, a dropped tile edge or a padded row would make it: logits (sums over C)
+|a - o| <= r |o| + 2r * mag; weight, bias and LayerNorm gradients |a - o| <= r |o| +
+0.5 * mag: with few positions (32 at the 774M B1 T32 check) a sum's factors carry the error
+of 36 layers relative to their rows' scale rather than to their own size, and the measured
+worst entry reaches 20% of its envelope in bf16 (4% in fp16) while the tensor is within
+1.2e-2 normwise. The embedding tables (wte, wpe) are
+gated row by row instead (each row's relative 2-norm error <= r; rows the oracle leaves at
+zero must be exactly zero): their entries sum a handful of residual-stream gradient entries,
+and those carry the bf16 error of the whole backward relative to their row's scale, so an
+entry that cancels to near zero upstream (measured: 1e-3 of its row) has an error far above
+its own envelope while its row is within 1.5%.
 """
 from __future__ import annotations
 
@@ -88,8 +100,10 @@ def assert_model_close(name, a, o, mag, K, rtol=RTOL, atol=ATOL, e_in=E_IN_F32,
     return s
 
 
-def assert_bf16_close(name, a, o, mag, r):
-    """bf16 gate: normwise <= r and per entry |a - o| <= r |o| + r mag."""
+def assert_bf16_close(name, a, o, mag, r, r_mag=None):
+    """bf16 gate: normwise <= r and per entry |a - o| <= r |o| + r_mag mag (r_mag = 2r by
+    default)."""
+    r_mag = 2 * r if r_mag is None else r_mag
     a = np.asarray(a, dtype=np.float64).ravel()
     o = np.asarray(o, dtype=np.float64).ravel()
     mag = np.asarray(mag, dtype=np.float64).ravel()
@@ -97,13 +111,32 @@ def assert_bf16_close(name, a, o, mag, r):
     err = np.abs(a - o)
     nw = float(np.linalg.norm(a - o) / max(np.linalg.norm(o), 1e-300))
     assert nw <= r, f"{name}: normwise {nw:.3e} > {r}"
-    ratio = err / (r * np.abs(o) + r * mag + 1e-30)
+    ratio = err / (r * np.abs(o) + r_mag * mag + 1e-30)
     if (ratio > 1).any():
         i = int(np.argmax(ratio))
         raise AssertionError(f"{name}: {int((ratio > 1).sum())} of {err.size} entries outside "
-                             f"{r}|o| + {r} mag; worst at {i}: got {a[i]!r} want {o[i]!r} "
+                             f"{r}|o| + {r_mag} mag; worst at {i}: got {a[i]!r} want {o[i]!r} "
                              f"mag {mag[i]:.3e}")
     return {"normwise": nw, "entry_ratio": float(ratio.max()) if err.size else 0.0}
+
+
+def assert_bf16_rows(name, a, o, ncols, r):
+    """bf16 gate for a table of rows: each row's relative 2-norm error <= r, rows that are
+    zero in the oracle exactly zero."""
+    a = np.asarray(a, dtype=np.float64).reshape(-1, ncols)
+    o = np.asarray(o, dtype=np.float64).reshape(-1, ncols)
+    err = np.linalg.norm(a - o, axis=1)
+    nrm = np.linalg.norm(o, axis=1)
+    zero = nrm == 0
+    assert not np.any(err[zero]), f"{name}: {int((err[zero] > 0).sum())} rows should be zero"
+    rel = err[~zero] / nrm[~zero]
+    if rel.size and rel.max() > r:
+        i = int(np.flatnonzero(~zero)[rel.argmax()])
+        raise AssertionError(f"{name}: {int((rel > r).sum())} rows above {r}; worst row {i} "
+                             f"at {rel.max():.3e}")
+    nw = float(np.linalg.norm(a - o) / max(np.linalg.norm(o), 1e-300))
+    assert nw <= r, f"{name}: normwise {nw:.3e} > {r}"
+    return {"normwise": nw, "worst_row": float(rel.max()) if rel.size else 0.0}
 
 
 def assert_close_mag(name, a, o, mag, K, rtol=RTOL, atol=ATOL, operand_u=0.0):
