@@ -8,6 +8,10 @@
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown table.
 
+``mfma`` (python -m ...profsum mfma OUT_MD COUNTER_CSV "COMMAND") turns a ``--pmc
+SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_*`` run into the MFMA busy
+fraction and executed MFMA work per kernel.
+
 ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the benchmark
 (counter_collection.csv, KiB per dispatch) into HBM bytes per launch of one kernel. The
 counters are scaled by what they read for a plain device copy of COPY_BYTES bytes each way
@@ -97,7 +101,7 @@ def traffic_json(dst: str, kernel: str, fetch_csv: str, write_csv: str, copy_fet
     write_b = w[1] / w[0] * 1024.0 * scale_w
     rec = {"kernel": kernel, "dispatches": f[0], "fetch_bytes_per_launch": round(fetch_b),
            "write_bytes_per_launch": round(write_b),
-           "bytes_per_launch": round(fetch_b + write_b),
+           "bytes_per_launch": round(fetch_b) + round(write_b),
            "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": cf_kib,
                                 "write_kib": cw_kib, "fetch_scale": scale_f,
                                 "write_scale": scale_w},
@@ -131,6 +135,41 @@ def traffic_md(dst: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
             fh.write(f"| {k} | {n} | {f / 1e6:.2f} | {w / 1e6:.2f} |\n")
 
 
+def mfma_md(dst: str, csv_path: str, command: str, simds: int = 1024) -> None:
+    """Per kernel: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD
+    count, as rocprofv3's MfmaUtil) and the MFMA work the counters saw (512 flops per MOP)."""
+    acc: dict = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = short_name(r["Kernel_Name"])
+        d = acc.setdefault(k, {})
+        c = r["Counter_Name"]
+        d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+        if c == "GRBM_GUI_ACTIVE":
+            d["n"] = d.get("n", 0) + 1
+    rows = []
+    for k, d in acc.items():
+        gui = d.get("GRBM_GUI_ACTIVE", 0.0)
+        if not gui or not d.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            continue
+        util = 100.0 * d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds)
+        mops = {f: d.get(f"SQ_INSTS_VALU_MFMA_MOPS_{f}", 0.0) * 512 / d["n"] / 1e9
+                for f in ("BF16", "F16", "F32")}
+        rows.append((k, d["n"], util, mops, gui / d["n"]))
+    rows.sort(key=lambda r: -r[4] * r[1])
+    with open(dst, "w") as fh:
+        fh.write("# MFMA busy per kernel (rocprofv3 counters)\n\n"
+                 f"Command (from the repository root, on one MI355X):\n\n```\n{command}\n```\n\n"
+                 "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), summed "
+                 "over the kernel's dispatches (rocprofv3's MfmaUtil). GFLOP/launch = "
+                 "SQ_INSTS_VALU_MFMA_MOPS_* x 512 per dispatch (executed MFMA work, by operand "
+                 "type).\n\n"
+                 "| kernel | dispatches | MFMA busy % | bf16 GFLOP/launch | f16 GFLOP/launch | "
+                 "f32 GFLOP/launch | GPU cycles/launch |\n|---|---|---|---|---|---|---|\n")
+        for k, n, util, mops, cyc in rows:
+            fh.write(f"| {k} | {n} | {util:.1f} | {mops['BF16']:.1f} | {mops['F16']:.1f} | "
+                     f"{mops['F32']:.1f} | {cyc:.0f} |\n")
+
+
 def main(argv: list[str]) -> int:
     if argv[:1] == ["stats"] and len(argv) == 5:
         stats_md(*argv[1:])
@@ -142,6 +181,9 @@ def main(argv: list[str]) -> int:
         return 0
     if argv[:1] == ["traffic-table"] and len(argv) == 8:
         traffic_md(argv[1], argv[2], argv[3], argv[4], argv[5], float(argv[6]), argv[7])
+        return 0
+    if argv[:1] == ["mfma"] and len(argv) == 4:
+        mfma_md(argv[1], argv[2], argv[3])
         return 0
     print(__doc__, file=sys.stderr)
     return 2
