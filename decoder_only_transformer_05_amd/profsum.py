@@ -38,7 +38,63 @@ KERNEL_SOURCES = {
 }
 
 
+_SIMPLE_TYPES = {"f": "float", "t": "unsigned short", "DF16_": "_Float16", "DF16b": "__bf16",
+                 "i": "int", "b": "bool"}
+
+
+def _template_args(m: str, i: int) -> tuple[list[str], int]:
+    """Template arguments of a mangled name starting at m[i] == 'I' (the few forms the
+    library's kernels use); returns them and the index past the closing 'E'."""
+    assert m[i] == "I"
+    i += 1
+    out = []
+    while m[i] != "E":
+        if m.startswith("Li", i) or m.startswith("Lb", i):
+            j = m.index("E", i)
+            out.append(m[i + 2:j])
+            i = j + 1
+            continue
+        for k, v in _SIMPLE_TYPES.items():
+            if m.startswith(k, i):
+                out.append(v)
+                i += len(k)
+                break
+        else:
+            mm = re.match(r"NS0_(\d+)", m[i:])
+            if not mm:
+                raise ValueError(m[i:])
+            i += len(mm.group(0))
+            name = m[i:i + int(mm.group(1))]
+            i += int(mm.group(1))
+            if m[i] == "I":
+                args, i = _template_args(m, i)
+                name += "<" + ",".join(args) + ">"
+            assert m[i] == "E"
+            i += 1
+            out.append(name)
+    return out, i + 1
+
+
+def demangle(n: str) -> str:
+    """Kernel names the profiler left mangled (it does for some _Float16 instances):
+    name<args> for the forms above, else the name unchanged."""
+    mm = re.match(r"_ZN4gpt212_GLOBAL__N_1(\d+)", n)
+    if not mm:
+        return n
+    i = len(mm.group(0))
+    name = n[i:i + int(mm.group(1))]
+    i += int(mm.group(1))
+    try:
+        if i < len(n) and n[i] == "I":
+            args, _ = _template_args(n, i)
+            name += "<" + ",".join(args) + ">"
+    except (ValueError, AssertionError, IndexError):
+        return n
+    return name
+
+
 def short_name(n: str) -> str:
+    n = demangle(n)
     n = n.replace("void ", "").replace("gpt2::(anonymous namespace)::", "")
     n = re.sub(r"\(.*", "", n)
     return n.replace("true", "1").replace("false", "0").replace(", ", ",")
@@ -135,9 +191,15 @@ def traffic_md(dst: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
             fh.write(f"| {k} | {n} | {f / 1e6:.2f} | {w / 1e6:.2f} |\n")
 
 
-def mfma_md(dst: str, csv_path: str, command: str, simds: int = 1024) -> None:
-    """Per kernel: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD
-    count, as rocprofv3's MfmaUtil) and the MFMA work the counters saw (512 flops per MOP)."""
+def mfma_md(dst: str, csv_path: str, command: str, simds: int = 1024, xcds: int = 8) -> None:
+    """Per kernel: MFMA busy and the MFMA work the counters saw.
+
+    GRBM_GUI_ACTIVE is counted by the GRBM of each of the 8 XCDs and summed (on kernels over
+    100 us it reads 8x the clock times the kernel's duration), so the kernel's GPU cycles are
+    GRBM_GUI_ACTIVE / 8 and MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs).
+    Executed MFMA work is SQ_INSTS_VALU_MFMA_MOPS_* x 512 flops; against the cycles and the
+    per-SIMD MFMA rate (1024 flops per cycle for bf16/fp16, 64 for fp32) it gives the fraction
+    of the MFMA peak at the clock the kernel ran at, a second reading of the same quantity."""
     acc: dict = {}
     for r in csv.DictReader(open(csv_path)):
         k = short_name(r["Kernel_Name"])
@@ -146,28 +208,37 @@ def mfma_md(dst: str, csv_path: str, command: str, simds: int = 1024) -> None:
         d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
         if c == "GRBM_GUI_ACTIVE":
             d["n"] = d.get("n", 0) + 1
+            d["ns"] = d.get("ns", 0) + int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    rate = {"BF16": 1024.0, "F16": 1024.0, "F32": 64.0}
     rows = []
     for k, d in acc.items():
         gui = d.get("GRBM_GUI_ACTIVE", 0.0)
         if not gui or not d.get("SQ_VALU_MFMA_BUSY_CYCLES"):
             continue
-        util = 100.0 * d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds)
-        mops = {f: d.get(f"SQ_INSTS_VALU_MFMA_MOPS_{f}", 0.0) * 512 / d["n"] / 1e9
-                for f in ("BF16", "F16", "F32")}
-        rows.append((k, d["n"], util, mops, gui / d["n"]))
-    rows.sort(key=lambda r: -r[4] * r[1])
+        cyc = gui / xcds
+        util = 100.0 * d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
+        mops = {f: d.get(f"SQ_INSTS_VALU_MFMA_MOPS_{f}", 0.0) * 512 for f in rate}
+        frac = 100.0 * sum(mops[f] / rate[f] for f in rate) / (cyc * simds)
+        rows.append((k, d["n"], util, frac, {f: mops[f] / d["n"] / 1e9 for f in rate},
+                     cyc / d["n"], cyc / d["ns"]))
+    rows.sort(key=lambda r: -r[5] * r[1])
     with open(dst, "w") as fh:
         fh.write("# MFMA busy per kernel (rocprofv3 counters)\n\n"
                  f"Command (from the repository root, on one MI355X):\n\n```\n{command}\n```\n\n"
-                 "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), summed "
-                 "over the kernel's dispatches (rocprofv3's MfmaUtil). GFLOP/launch = "
-                 "SQ_INSTS_VALU_MFMA_MOPS_* x 512 per dispatch (executed MFMA work, by operand "
-                 "type).\n\n"
-                 "| kernel | dispatches | MFMA busy % | bf16 GFLOP/launch | f16 GFLOP/launch | "
-                 "f32 GFLOP/launch | GPU cycles/launch |\n|---|---|---|---|---|---|---|\n")
-        for k, n, util, mops, cyc in rows:
-            fh.write(f"| {k} | {n} | {util:.1f} | {mops['BF16']:.1f} | {mops['F16']:.1f} | "
-                     f"{mops['F32']:.1f} | {cyc:.0f} |\n")
+                 "GPU cycles = GRBM_GUI_ACTIVE / 8: the counter is summed over the GRBMs of the 8 "
+                 "XCDs (it reads 8x clock x duration). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                 "(GPU cycles x 1024 SIMDs). Executed work = SQ_INSTS_VALU_MFMA_MOPS_* x 512 "
+                 "flops per dispatch; `work / peak` divides it by GPU cycles x 1024 SIMDs x the "
+                 "per-SIMD MFMA rate (1024 flops/cycle bf16 and fp16, 64 fp32), the same "
+                 "fraction from the instruction counts. All dispatches of the run (warmup and "
+                 "timed steps) are summed; the clock column is GPU cycles over the dispatches' "
+                 "time stamps (under counter collection).\n\n"
+                 "| kernel | dispatches | MFMA busy % | work / peak % | bf16 GFLOP/launch | "
+                 "f16 GFLOP/launch | f32 GFLOP/launch | GPU cycles/launch | clock GHz |\n"
+                 "|---|---|---|---|---|---|---|---|---|\n")
+        for k, n, util, frac, mops, cyc, ghz in rows:
+            fh.write(f"| {k} | {n} | {util:.1f} | {frac:.1f} | {mops['BF16']:.1f} | "
+                     f"{mops['F16']:.1f} | {mops['F32']:.1f} | {cyc:.0f} | {ghz:.2f} |\n")
 
 
 def main(argv: list[str]) -> int:
