@@ -28,6 +28,7 @@
 
 #include <type_traits>
 
+#include "attn_order.h"
 #include "kernels.h"
 
 namespace gpt2 {
@@ -292,29 +293,6 @@ GPT2_DEVICE_INLINE long long tri_tiles(int n) { return (long long)n * (n + 1) / 
 // operand comes from a 16-byte LDS read. With 64-dim heads this fits two waves per SIMD.
 constexpr int DK_KEYS = 128, DK_THR = 256;
 
-// Block order of the dK/dV grid: XCD-local (as tile_of_block), and inside each XCD's share
-// all first key blocks (the most query tiles) before all second ones, and so on, so the
-// longest blocks start first. Falls back to the plain XCD-local order when the grid does not
-// split evenly.
-GPT2_DEVICE_INLINE void dkdv_block(int nkb, int NH, int* kb, int* head, int* b) {
-  const int n = gridDim.x;
-  const int per = n >> 3;
-  int bh, k;
-  if ((n & 7) == 0 && per % nkb == 0) {
-    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-    const int groups = per / nkb;  // (batch, head) pairs on this XCD
-    k = idx / groups;
-    bh = xcd * groups + idx % groups;
-  } else {
-    const int lid = xcd_logical_block(blockIdx.x, n);
-    k = lid % nkb;
-    bh = lid / nkb;
-  }
-  *kb = k;
-  *head = bh % NH;
-  *b = bh / NH;
-}
-
 template <int HSP, typename TS>
 __global__ __launch_bounds__(DK_THR) __attribute__((amdgpu_waves_per_eu(HSP <= 64 ? 2 : 1)))
 void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
@@ -331,7 +309,7 @@ void attn_bwd_dkdv_kernel(TS* __restrict__ dqkv, float* __restrict__ dsbuf,
 
   const int nkb = (T + DK_KEYS - 1) / DK_KEYS;
   int kb, head, b;
-  dkdv_block(nkb, NH, &kb, &head, &b);
+  key_block_of(nkb, NH, &kb, &head, &b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   const long long C3 = 3LL * C;
@@ -691,7 +669,13 @@ int attention_backward_t(TS* dqkv, const TS* dout, const TS* qkv, const TS* out,
   const int rc = rowdot_t(dscratch, dout, out, B, T, C, NH, stream);
   if (rc) return rc;
   dim3 grid(((T + TILE - 1) / TILE) * NH * B);
-  {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
+  if (f32 && attn_x6(C, NH) && attention_dkdv_x6_supported(C, NH)) {
+    const int rk = attention_dkdv_x6(reinterpret_cast<float*>(dqkv), ds_scratch,
+                                     reinterpret_cast<const float*>(dout),
+                                     reinterpret_cast<const float*>(qkv), lse, dscratch, B, T, C,
+                                     NH, stream);
+    if (rk) return rk;
+  } else {  // dK, dV: the products dV = P^T dO and dK = dS^T Q (plus the dP = dO V^T they need)
     ProfScope ps(f32 ? "attn_bwd_dkdv_kernel"
                      : is_f16<TS>() ? "attn_bwd_dkdv_f16_kernel" : "attn_bwd_dkdv_bf16_kernel",
                  6.0 * B * NH * hs * tri,

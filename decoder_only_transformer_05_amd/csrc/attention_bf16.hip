@@ -22,6 +22,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "attn_order.h"
 #include "kernels.h"
 
 namespace gpt2 {
@@ -36,6 +37,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -689,6 +692,210 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dq_x6_kernel(float* __restr
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// dK, dV on fp32 tensors with split-operand products. A workgroup owns DX6_KEYS = 128 keys
+// (four waves of 32) of one (batch, head) and walks the 64-query tiles from its diagonal
+// down. K and V of the lane's key are split once into registers; each query tile of Q and
+// dO is split into three bf16 planes per tensor, [query][d] in LDS with the 16-byte chunk c
+// of row q at chunk c ^ qswz(q). That one layout serves both uses:
+//   S = Q K^T and dP = dO V^T take Q and dO as the A operand, a lane reading 8 consecutive
+//   head dims of its query (16-byte reads; 8 consecutive rows hit 8 different chunks);
+//   dV^T = dO^T P and dK^T = Q^T dS take dO^T and Q^T as the A operand, read with
+//   transposing reads (ds_read_b64_tr_b16): lanes 4j .. 4j+3 of a 16-lane group read 16
+//   head dims of query row j of a run of four, and lane i receives head dim i of the four
+//   rows. The two reads of a fragment take the query runs 16h + 4lh and 16h + 8 + 4lh, the
+//   order in which the S / dP accumulators hold a lane's queries, so P and dS (split in
+//   registers) are the B operands as they stand. For four consecutive rows qswz takes
+//   values 2j + s, so the two chunks a row run reads land on eight different chunks.
+// The fp32 dS of each causal 64x64 tile is written ([query][key]) for the dQ kernel, as
+// attn_bwd_dkdv_kernel does.
+// ---------------------------------------------------------------------------------------
+constexpr int DX6_KEYS = X6_QT;
+GPT2_DEVICE_INLINE int qswz(int q) { return ((q & 3) << 1) | ((q >> 2) & 1); }
+// element offset of head dims 8c .. 8c+7 of row q in a 64-wide plane
+GPT2_DEVICE_INLINE int qoff(int q, int c) { return q * 64 + ((c ^ qswz(q)) << 3); }
+
+template <int HSP>
+__global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dkdv_x6_kernel(
+    float* __restrict__ dqkv, float* __restrict__ dsbuf, const float* __restrict__ dout,
+    const float* __restrict__ qkv, const float* __restrict__ lse,
+    const float* __restrict__ Drow, int T, int C, int NH, int hs, float scale,
+    float scale_log2) {
+  static_assert(HSP == 64, "64-wide planes");
+  constexpr int KS = HSP / 16, ND = HSP / 32, CPR = HSP / 8;
+  constexpr int PQ = TILE * HSP;  // elements of one plane
+  __shared__ __attribute__((aligned(16))) bf16_t Qp[3 * PQ];  // [plane][q][d]
+  __shared__ __attribute__((aligned(16))) bf16_t Op[3 * PQ];  // dO, same layout
+  __shared__ __attribute__((aligned(16))) float Ls[TILE];
+  __shared__ __attribute__((aligned(16))) float Ds[TILE];
+
+  const int nkb = (T + DX6_KEYS - 1) / DX6_KEYS;
+  int kb, head, b;
+  key_block_of(nkb, NH, &kb, &head, &b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, lh = lane >> 5;
+  const int i16 = lane & 15, g1 = (lane >> 4) & 1;  // lane in its 16-lane group, group parity
+  const long long C3 = 3LL * C;
+  const float* base = qkv + (long long)b * T * C3 + (long long)head * hs;
+  const float* dobase = dout + (long long)b * T * C + (long long)head * hs;
+  const float* lrow = lse + ((long long)b * NH + head) * T;
+  const float* drow = Drow + ((long long)b * NH + head) * T;
+  const int key0 = kb * DX6_KEYS + wave * 32;  // first key of this wave
+  const int key = key0 + r;
+  const int km = min(key, T - 1);
+  const int kt = key0 / TILE;             // this wave's 64-key tile in the dS layout
+  const int kcol = key0 - kt * TILE + r;  // this lane's column in that tile
+
+  // this lane's key and value, d = 16ks + 8lh .. +7, as three parts each
+  bf16x8 kh[KS], kmd[KS], kl[KS], vh[KS], vmd[KS], vl[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    f32x4 x, y;
+    u32x4 h, m, l;
+    load8f(base + C, C3, km, 16 * ks + 8 * lh, T, hs, x, y);
+    split8(x, y, h, m, l);
+    kh[ks] = __builtin_bit_cast(bf16x8, h);
+    kmd[ks] = __builtin_bit_cast(bf16x8, m);
+    kl[ks] = __builtin_bit_cast(bf16x8, l);
+    load8f(base + 2 * C, C3, km, 16 * ks + 8 * lh, T, hs, x, y);
+    split8(x, y, h, m, l);
+    vh[ks] = __builtin_bit_cast(bf16x8, h);
+    vmd[ks] = __builtin_bit_cast(bf16x8, m);
+    vl[ks] = __builtin_bit_cast(bf16x8, l);
+  }
+  f32x16 dvacc[ND], dkacc[ND];  // [d][key]
+#pragma unroll
+  for (int db = 0; db < ND; db++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      dvacc[db][i] = 0.f;
+      dkacc[db][i] = 0.f;
+    }
+
+  // transposing-read address of this lane for k step hh of sub-block qb, head-dim block db
+  // (first of the two reads; the second is 8 rows on)
+  auto tr_off = [&](int qb, int hh, int db) {
+    const int q = 32 * qb + 16 * hh + 4 * lh + (i16 >> 2);
+    const int d = 32 * db + 16 * g1 + 4 * (i16 & 3);
+    return qoff(q, d >> 3) + (d & 7);
+  };
+  auto frag_tr8 = [&](const bf16_t* p) -> bf16x8 {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * HSP));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  const int nqt = (T + TILE - 1) / TILE;
+  for (int qt = kb * DX6_KEYS / TILE; qt < nqt; qt++) {
+    const int q0 = qt * TILE;
+    __syncthreads();
+    // Q and dO rows q0 .. q0+63 -> three planes each; chunk f: row f / 8, head dims 8 (f % 8)
+#pragma unroll
+    for (int i = 0; i < TILE * CPR / X6_NT; i++) {
+      const int f = tid + X6_NT * i, row = f / CPR, c = f % CPR;
+      const int o = qoff(row, c);
+      f32x4 x, y;
+      u32x4 h, m, l;
+      load8f(base, C3, q0 + row, 8 * c, T, hs, x, y);
+      split8(x, y, h, m, l);
+      *reinterpret_cast<u32x4*>(Qp + o) = h;
+      *reinterpret_cast<u32x4*>(Qp + PQ + o) = m;
+      *reinterpret_cast<u32x4*>(Qp + 2 * PQ + o) = l;
+      load8f(dobase, C, q0 + row, 8 * c, T, hs, x, y);
+      split8(x, y, h, m, l);
+      *reinterpret_cast<u32x4*>(Op + o) = h;
+      *reinterpret_cast<u32x4*>(Op + PQ + o) = m;
+      *reinterpret_cast<u32x4*>(Op + 2 * PQ + o) = l;
+    }
+    if (tid < TILE) {
+      const bool ok = q0 + tid < T;
+      const int t = min(q0 + tid, T - 1);
+      Ls[tid] = ok ? lrow[t] * kLog2e : 0.f;
+      Ds[tid] = ok ? drow[t] : 0.f;
+    }
+    __syncthreads();
+    if (q0 + TILE <= key0) continue;  // every query of the tile precedes this wave's keys
+    // dS tile (qt, kt) of this (b, head): 64 x 64 floats, [query][key]; this lane writes
+    // column kcol of rows 4lh + (32qb + 8(i/4) + i%4)
+    float* dst = dsbuf + (((long long)b * NH + head) * tri_tiles(nqt) + tri_index(qt, kt)) *
+                             (TILE * TILE) + 4 * lh * TILE + kcol;
+#pragma unroll 1
+    for (int qb = 0; qb < 2; qb++) {
+      if (q0 + 32 * qb + 32 <= key0) {  // every query of the sub-block precedes the keys
+#pragma unroll
+        for (int i = 0; i < 16; i++) dst[(32 * qb + 8 * (i / 4) + (i % 4)) * TILE] = 0.f;
+        continue;
+      }
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const int o = qoff(32 * qb + r, 2 * ks + lh);
+        s = mfma_x6(*reinterpret_cast<const bf16x8*>(&Qp[o]),
+                    *reinterpret_cast<const bf16x8*>(&Qp[PQ + o]),
+                    *reinterpret_cast<const bf16x8*>(&Qp[2 * PQ + o]), kh[ks], kmd[ks], kl[ks], s);
+        dp = mfma_x6(*reinterpret_cast<const bf16x8*>(&Op[o]),
+                     *reinterpret_cast<const bf16x8*>(&Op[PQ + o]),
+                     *reinterpret_cast<const bf16x8*>(&Op[2 * PQ + o]), vh[ks], vmd[ks], vl[ks],
+                     dp);
+      }
+      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's; the
+      // exponential is taken for every entry and masked after
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int qo = 32 * qb + 8 * (i / 4) + (i % 4);  // query - 4lh
+        const int qa = q0 + qo + 4 * lh;
+        const bool ok = qa < T && qa >= key;
+        const float e = __builtin_amdgcn_exp2f(s[i] * scale_log2 - Ls[qo + 4 * lh]);
+        const float p = ok ? e : 0.f;
+        s[i] = p;
+        dp[i] = p * (dp[i] - Ds[qo + 4 * lh]);
+        dst[qo * TILE] = dp[i];  // 32 lanes store 32 consecutive keys
+      }
+      // dV^T[d][key] += dO^T[d][q] P[q][key], dK^T[d][key] += Q^T[d][q] dS[q][key]; k step
+      // hh takes accumulator entries 8hh .. 8hh+7 (queries 16hh + 4lh + {0..3, 8..11})
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        u32x4 ph, pm, pl, sh, sm, sl;
+        split8(f32x4{s[8 * hh], s[8 * hh + 1], s[8 * hh + 2], s[8 * hh + 3]},
+               f32x4{s[8 * hh + 4], s[8 * hh + 5], s[8 * hh + 6], s[8 * hh + 7]}, ph, pm, pl);
+        split8(f32x4{dp[8 * hh], dp[8 * hh + 1], dp[8 * hh + 2], dp[8 * hh + 3]},
+               f32x4{dp[8 * hh + 4], dp[8 * hh + 5], dp[8 * hh + 6], dp[8 * hh + 7]}, sh, sm, sl);
+#pragma unroll
+        for (int db = 0; db < ND; db++) {
+          const int o = tr_off(qb, hh, db);
+          dvacc[db] = mfma_x6(frag_tr8(Op + o), frag_tr8(Op + PQ + o), frag_tr8(Op + 2 * PQ + o),
+                              __builtin_bit_cast(bf16x8, ph), __builtin_bit_cast(bf16x8, pm),
+                              __builtin_bit_cast(bf16x8, pl), dvacc[db]);
+          dkacc[db] = mfma_x6(frag_tr8(Qp + o), frag_tr8(Qp + PQ + o), frag_tr8(Qp + 2 * PQ + o),
+                              __builtin_bit_cast(bf16x8, sh), __builtin_bit_cast(bf16x8, sm),
+                              __builtin_bit_cast(bf16x8, sl), dkacc[db]);
+        }
+      }
+    }
+  }
+  if (key < T) {
+    float* dk = dqkv + ((long long)b * T + key) * C3 + C + (long long)head * hs;
+    float* dv = dk + C;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+#pragma unroll
+      for (int ig = 0; ig < 4; ig++) {
+        const int d = 32 * db + 8 * ig + 4 * lh;
+        if (d < hs) {
+          st4(dk + d, f32x4{dkacc[db][4 * ig] * scale, dkacc[db][4 * ig + 1] * scale,
+                            dkacc[db][4 * ig + 2] * scale, dkacc[db][4 * ig + 3] * scale});
+          st4(dv + d, f32x4{dvacc[db][4 * ig], dvacc[db][4 * ig + 1], dvacc[db][4 * ig + 2],
+                            dvacc[db][4 * ig + 3]});
+        }
+      }
+  }
+}
+
 
 // ---------------------------------------------------------------------------------------
 // backward
@@ -957,6 +1164,32 @@ int attention_dq_x6(float* dqkv, const float* qkv, const float* ds_scratch, int 
   else attn_bwd_dq_x6_kernel<128><<<grid, X6_NT, 0, stream>>>(dqkv, qkv, ds_scratch, T, C, NH, hs, scale);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
+}
+
+int attention_dkdv_x6(float* dqkv, float* ds_scratch, const float* dout, const float* qkv,
+                      const float* lse, const float* D, int B, int T, int C, int NH,
+                      hipStream_t stream) {
+  if (B < 1 || T < 1 || NH < 1 || C % NH || !attention_dkdv_x6_supported(C, NH)) {
+    set_global_error("attention dK/dV (split operands): unsupported shape B=%d T=%d C=%d NH=%d",
+                     B, T, C, NH);
+    return -1;
+  }
+  const int hs = C / NH;
+  const float scale = 1.0f / sqrtf((float)hs);
+  dim3 grid(((T + DX6_KEYS - 1) / DX6_KEYS) * NH * B);
+  const double tri = (double)T * (T + 1) / 2.0, BTC = (double)B * T * C;
+  ProfScope ps("attn_bwd_dkdv_x6_kernel", 8.0 * B * NH * hs * tri,
+               4.0 * (3.0 * BTC + BTC + 2.0 * BTC) + 4.0 * (2.0 * B * NH * T + B * NH * tri),
+               stream);
+  attn_bwd_dkdv_x6_kernel<64><<<grid, X6_NT, 0, stream>>>(dqkv, ds_scratch, dout, qkv, lse, D, T,
+                                                          C, NH, hs, scale, scale * kLog2e);
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
+
+bool attention_dkdv_x6_supported(int C, int NH) {
+  const int hs = NH > 0 ? C / NH : 0;
+  return NH > 0 && C % NH == 0 && hs % 8 == 0 && hs > 32 && hs <= 64;
 }
 
 bool attention_bf16_mma_supported(int C, int NH) {

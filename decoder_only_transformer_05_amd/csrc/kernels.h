@@ -108,6 +108,12 @@ int attention_forward_x6(float* out, float* lse, const float* qkv, int B, int T,
 // with split-operand products (same conditions and switch as attention_forward_x6)
 int attention_dq_x6(float* dqkv, const float* qkv, const float* ds_scratch, int B, int T, int C,
                     int NH, hipStream_t stream);
+// dK, dV (and the fp32 dS tiles for attention_dq_x6) with split-operand products, for head
+// sizes in (32, 64] that are multiples of 8; D = rowsum(dout * out) per (b, head, query)
+bool attention_dkdv_x6_supported(int C, int NH);
+int attention_dkdv_x6(float* dqkv, float* ds_scratch, const float* dout, const float* qkv,
+                      const float* lse, const float* D, int B, int T, int C, int NH,
+                      hipStream_t stream);
 int attention_forward_bf16_mma(bf16_t* out, float* lse, const bf16_t* qkv, int B, int T, int C,
                                int NH, hipStream_t stream);
 int attention_backward_bf16_mma(bf16_t* dqkv, const bf16_t* dout, const bf16_t* qkv,

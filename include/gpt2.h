@@ -49,9 +49,9 @@ enum {
  * GPT2_DTYPE_FP32: every tensor fp32. Each fp32 product of the GEMMs, of the attention
  *   forward and of the attention dQ is formed as six bf16 MFMA products of an exact
  *   three-way bf16 split of its operands (within 2^-23 of the exact product) with fp32
- *   accumulation; the attention dK/dV products run on fp32 MFMA (see
- *   gpt2_k_matmul_forward and gpt2_k_attention_forward for the switches that select fp32
- *   MFMA products throughout).
+ *   accumulation; so are the attention dK/dV products for head sizes in (32, 64] (other
+ *   head sizes: fp32 MFMA; see gpt2_k_matmul_forward and gpt2_k_attention_forward for the
+ *   switches that select fp32 MFMA products throughout).
  * GPT2_DTYPE_BF16: mixed precision, the extension to "fp16 or lower" that the llm.c
  *   overview names as a next step: GEMM operands (a bf16 copy of the weights, refreshed
  *   by every gpt2_set_params and gpt2_adamw_step) and all activation tensors are stored
@@ -310,8 +310,9 @@ int gpt2_k_matmul_backward_noalloc(float* dinp, float* dW, float* dbias, const f
  * per head with scale 1/sqrt(C/NH). lse (B,NH,T) receives each query row's log-sum-exp
  * of the scaled scores (what the backward needs instead of the (B,NH,T,T) matrices).
  * For head sizes that are multiples of 8 the forward and the dQ products of the backward
- * are formed as six bf16 MFMA products of exact three-way operand splits (fp32 accuracy,
- * as for the GEMMs); GPT2_ATTN_F32_PRODUCTS=fp32 selects fp32 MFMA products. */
+ * (and the dK/dV products when the head size is also in (32, 64]) are formed as six bf16
+ * MFMA products of exact three-way operand splits (fp32 accuracy, as for the GEMMs);
+ * GPT2_ATTN_F32_PRODUCTS=fp32 selects fp32 MFMA products. */
 int gpt2_k_attention_forward(float* out, float* lse, const float* qkv, int B, int T, int C,
                              int NH, void* stream);
 
