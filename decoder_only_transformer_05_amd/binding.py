@@ -94,6 +94,8 @@ SIGNATURES = {
     "gpt2_k_attention_backward_f16": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
                                              _vp]),
     "gpt2_set_loss_scale": (_int, [_vp, _f, _int]),
+    "gpt2_set_loss_grad_in_forward": (_int, [_vp, _int]),
+    "gpt2_k_crossentropy_fused": (_int, [_vp, _vp, _vp, _vp, _vp, _f, _int, _int, _int, _vp, _vp]),
     "gpt2_get_loss_scale": (_int, [_vp, ctypes.POINTER(_f), ctypes.POINTER(_int)]),
     "gpt2_k_encoder_forward_bf16": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp,
                                            _vp]),
@@ -307,6 +309,9 @@ class GPT2:
     def save_checkpoint(self, path):
         self._c(lib().gpt2_save_checkpoint(self.h, _path(path)))
 
+    def set_loss_grad_in_forward(self, on: bool):
+        self._c(lib().gpt2_set_loss_grad_in_forward(self.h, 1 if on else 0))
+
     def set_loss_scale(self, scale: float, growth_interval: int = 2000):
         self._c(lib().gpt2_set_loss_scale(self.h, scale, growth_interval))
 
@@ -488,6 +493,12 @@ def k_crossentropy_forward(losses, lse, logits, targets, N, V, ld, err_flag=None
 def k_crossentropy_backward(logits, lse, targets, dloss, N, V, ld):
     _check(lib().gpt2_k_crossentropy_backward(_ptr(logits), _ptr(lse), _iptr(targets), dloss, N, V,
                                               ld, current_stream()))
+
+
+def k_crossentropy_fused(losses, lse, dlogits, logits, targets, dloss, N, V, ld, err_flag=None):
+    _check(lib().gpt2_k_crossentropy_fused(_ptr(losses), _ptr(lse), _ptr(dlogits), _ptr(logits),
+                                           _iptr(targets), dloss, N, V, ld, _iptr(err_flag),
+                                           current_stream()))
 
 
 def k_sample_mult(token, logits, V, coin):

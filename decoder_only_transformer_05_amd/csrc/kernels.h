@@ -191,6 +191,19 @@ int crossentropy_forward(float* losses, float* lse, const f16_t* logits, const i
 // dscale (device, may be null): the gradient is also multiplied by *dscale (a loss scale)
 int crossentropy_backward(f16_t* logits, const float* lse, const int32_t* targets, float dloss,
                           const float* dscale, int N, int V, int ld, hipStream_t stream);
+// Cross-entropy forward and backward in one pass (losses, lse and dlogits =
+// (softmax - onehot) * dloss [* *dscale], into a buffer apart from the logits); ld at most
+// crossentropy_fused_max_ld()
+int crossentropy_fused_max_ld();
+int crossentropy_fused(float* losses, float* lse, float* dlogits, const float* logits,
+                       const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                       int ld, int32_t* err_flag, hipStream_t stream);
+int crossentropy_fused(float* losses, float* lse, bf16_t* dlogits, const bf16_t* logits,
+                       const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                       int ld, int32_t* err_flag, hipStream_t stream);
+int crossentropy_fused(float* losses, float* lse, f16_t* dlogits, const f16_t* logits,
+                       const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                       int ld, int32_t* err_flag, hipStream_t stream);
 int mean_reduce(float* out, const float* x, int n, hipStream_t stream);
 // pbf (may be null): bf16 copy of the updated parameters
 int adamw(float* p, const float* g, float* m, float* v, bf16_t* pbf, size_t n, float lr,

@@ -99,6 +99,7 @@ struct gpt2_model {
   // activation tensors: fp32 or bf16 storage by dtype (per layer where noted)
   void *encoded, *ln1, *qkv, *atty, *res2, *ln2, *fch, *fchg, *res3, *lnf, *logits;
   void *dbuf4, *dln, *datty, *dqkv;
+  void* dlogits = nullptr;  // loss gradient of the logits, written by the forward (if enabled)
   // fp32 in both modes: statistics, losses, the residual-stream gradient, scratch
   float *ln1_mean, *ln1_rstd, *attn_lse, *ln2_mean, *ln2_rstd, *lnf_mean, *lnf_rstd, *losses,
       *xent_lse;
@@ -109,6 +110,8 @@ struct gpt2_model {
 
   bool fwd_targets = false;  // last forward had targets
   bool logits_valid = false; // logits buffer holds logits (not their gradient)
+  bool loss_grad_in_forward = true;  // a forward with targets also writes dlogits
+  bool dlogits_valid = false;        // dlogits holds the gradient for the last forward
   bool has_grads = false;    // a backward or set_grads happened since build
   char err[512] = "";
 };
@@ -256,6 +259,9 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
   md->lnf_mean = F(BT);
   md->lnf_rstd = F(BT);
   md->logits = A(BT * md->Vp);
+  md->dlogits = md->loss_grad_in_forward && md->Vp <= crossentropy_fused_max_ld()
+                    ? A(BT * md->Vp)
+                    : nullptr;
   md->losses = F(BT);
   md->xent_lse = F(BT);
   md->dres = F(BT * C);
@@ -457,8 +463,17 @@ int forward_impl(gpt2_model* md, bool with_targets) {
   lm.K = C;
   CHK(run_gemm(md, lm));
   if (with_targets) {
-    CHK(crossentropy_forward(md->losses, md->xent_lse, logits, md->tgt, BT, V, md->Vp,
-                             md->d_err, s));
+    if (md->dlogits && md->loss_grad_in_forward) {
+      // losses and, for the backward, d(mean loss)/d(logits) (times the loss scale in fp16)
+      CHK(crossentropy_fused(md->losses, md->xent_lse, act<T>(md->dlogits), logits, md->tgt,
+                             1.0f / (float)BT,
+                             md->dtype == GPT2_DTYPE_FP16 ? md->d_scale : nullptr, BT, V,
+                             md->Vp, md->d_err, s));
+      md->dlogits_valid = true;
+    } else {
+      CHK(crossentropy_forward(md->losses, md->xent_lse, logits, md->tgt, BT, V, md->Vp,
+                               md->d_err, s));
+    }
     CHK(mean_reduce(md->d_loss, md->losses, BT, s));
   }
   return GPT2_OK;
@@ -471,10 +486,12 @@ int backward_impl(gpt2_model* md) {
   const int B = md->B, T_ = md->T, L = md->L, C = md->C, NH = md->NH, V = md->V, BT = B * T_;
   const size_t NC = (size_t)BT * C;
   hipStream_t s = md->stream;
-  T* logits = act<T>(md->logits);
   T* dln = act<T>(md->dln);
-  // d(mean loss)/d(loss_bt) = 1/(B*T), through softmax + cross-entropy, in place
-  CHK(xent_backward(md, logits, 1.0f / (float)BT, BT));
+  // d(mean loss)/d(loss_bt) = 1/(B*T), through softmax + cross-entropy: written by the forward
+  // into dlogits, else here, in place of the logits
+  T* logits = act<T>(md->logits);
+  if (!md->dlogits_valid) CHK(xent_backward(md, logits, 1.0f / (float)BT, BT));
+  else logits = act<T>(md->dlogits);
   {
     GT d;  // dlnf = dlogits . wte
     d.A = logits;
@@ -868,6 +885,15 @@ int gpt2_set_grads(gpt2_model* md, const float* src, int src_is_device) {
   return rc;
 }
 
+int gpt2_set_loss_grad_in_forward(gpt2_model* md, int on) {
+  if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
+  if (on && md->abuf && !md->dlogits)
+    return fail(md, GPT2_ERR_STATE, "gpt2_set_loss_grad_in_forward: the model was sized "
+                "without the gradient buffer (turn it on before the first forward)");
+  md->loss_grad_in_forward = on != 0;
+  return GPT2_OK;
+}
+
 int gpt2_set_loss_scale(gpt2_model* md, float scale, int growth_interval) {
   if (!md) return fail(nullptr, GPT2_ERR_ARG, "NULL model");
   if (md->dtype != GPT2_DTYPE_FP16)
@@ -975,6 +1001,7 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   hipStream_t s = md->stream;
   md->fwd_targets = false;
   md->logits_valid = false;
+  md->dlogits_valid = false;
   HIPCHK(hipMemcpyAsync(md->tok, tokens, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
   if (targets)
     HIPCHK(hipMemcpyAsync(md->tgt, targets, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
@@ -1009,9 +1036,11 @@ int gpt2_backward(gpt2_model* md) {
   if (!md->fwd_targets || !md->logits_valid)
     return fail(md, GPT2_ERR_STATE, "gpt2_backward: needs a forward with targets first");
   md->logits_valid = false;
-  if (md->dtype == GPT2_DTYPE_BF16) CHK(backward_impl<bf16_t>(md));
-  else if (md->dtype == GPT2_DTYPE_FP16) CHK(backward_impl<f16_t>(md));
-  else CHK(backward_impl<float>(md));
+  const int rc = md->dtype == GPT2_DTYPE_BF16   ? backward_impl<bf16_t>(md)
+                 : md->dtype == GPT2_DTYPE_FP16 ? backward_impl<f16_t>(md)
+                                                : backward_impl<float>(md);
+  md->dlogits_valid = false;
+  if (rc) return rc;
   md->has_grads = true;
   return GPT2_OK;
 }
@@ -1262,6 +1291,17 @@ int gpt2_k_crossentropy_backward(float* logits, const float* lse, const int32_t*
                                  float dloss, int N, int V, int ld, void* stream) {
   if (!logits || !lse || !targets) return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
   return crossentropy_backward(logits, lse, targets, dloss, N, V, ld, as_stream(stream));
+}
+
+int gpt2_k_crossentropy_fused(float* losses, float* lse, float* dlogits, const float* logits,
+                              const int32_t* targets, float dloss, int N, int V, int ld,
+                              int32_t* err_flag, void* stream) {
+  if (!losses || !lse || !dlogits || !logits || !targets)
+    return fail(nullptr, GPT2_ERR_ARG, "NULL pointer");
+  if (dlogits == logits)
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_k_crossentropy_fused: dlogits must not alias logits");
+  return crossentropy_fused(losses, lse, dlogits, logits, targets, dloss, nullptr, N, V, ld,
+                            err_flag, as_stream(stream));
 }
 
 int gpt2_k_sample_mult(int32_t* token, const float* logits, int V, float coin, void* stream) {

@@ -466,6 +466,85 @@ __global__ __launch_bounds__(256) void xent_bwd_kernel(T* __restrict__ logits,
   }
 }
 
+// Forward and backward of the softmax cross-entropy in one pass over the logits: per row the
+// log-sum-exp, the loss lse - z[target] (as xent_fwd_kernel) and the gradient
+// dlogits = (softmax - onehot(target)) * dloss (as xent_bwd_kernel, zero on the padding),
+// written to a separate buffer so the logits stay. One 1024-thread workgroup per row keeps
+// the row in registers (CH vectors of 4 per thread, vector c4 = thread + 1024 k), so the
+// logits are read once and the gradient written once; the row's running (max, sum) pairs
+// are merged across the 16 waves in wave order.
+constexpr int XF_THREADS = 1024;
+template <typename T, int CH>
+__global__ __launch_bounds__(XF_THREADS) void xent_fused_kernel(
+    float* __restrict__ losses, float* __restrict__ lse_out, T* __restrict__ dlogits,
+    const T* __restrict__ logits, const int32_t* __restrict__ targets, float dloss,
+    const float* dscale, int V, int ld, int32_t* err) {
+  __shared__ float sm[XF_THREADS / 64], ss[XF_THREADS / 64];
+  const int row = blockIdx.x;
+  const T* z = logits + (long long)row * ld;
+  T* dz = dlogits + (long long)row * ld;
+  const int L4 = ld / 4;
+  f32x4 v[CH];
+#pragma unroll
+  for (int k = 0; k < CH; k++) {
+    const int c4 = threadIdx.x + XF_THREADS * k;
+    v[k] = c4 < L4 ? ld4(z + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m = -INFINITY, s = 0.f;
+#pragma unroll
+  for (int k = 0; k < CH; k++) {
+    const int c = 4 * (threadIdx.x + XF_THREADS * k);
+    if (c >= V) break;
+    f32x4 w = v[k];
+    if (c + 3 >= V) {
+      if (c + 1 >= V) w[1] = -INFINITY;
+      if (c + 2 >= V) w[2] = -INFINITY;
+      if (c + 3 >= V) w[3] = -INFINITY;
+    }
+    const float mx = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
+    if (mx > m) {
+      s *= __expf(m - mx);
+      m = mx;
+    }
+    s += (__expf(w[0] - m) + __expf(w[1] - m)) + (__expf(w[2] - m) + __expf(w[3] - m));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    lse_merge(m, s, m2, s2);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  float M = sm[0], S = ss[0];
+  for (int k = 1; k < XF_THREADS / 64; k++) lse_merge(M, S, sm[k], ss[k]);
+  const float lse = M + logf(S);
+  int y = targets[row];
+  if (y < 0 || y >= V) {
+    if (err && threadIdx.x == 0) *err = 1;
+    y = 0;
+  }
+  if (threadIdx.x == 0) {
+    losses[row] = lse - ld1(z + y);
+    lse_out[row] = lse;
+  }
+  if (dscale) dloss *= *dscale;
+#pragma unroll
+  for (int k = 0; k < CH; k++) {
+    const int c4 = threadIdx.x + XF_THREADS * k;
+    if (c4 >= L4) break;
+    const int c = 4 * c4;
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      o[j] = c + j < V ? (__expf(v[k][j] - lse) - (c + j == y ? 1.f : 0.f)) * dloss : 0.f;
+    st4(dz + c, o);
+  }
+}
+
 // mean of n values by one workgroup, in a fixed order
 __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
                                                     const float* __restrict__ x, int n) {
@@ -808,6 +887,31 @@ int crossentropy_backward_t(T* logits, const float* lse, const int32_t* targets,
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }
+
+template <typename T>
+int crossentropy_fused_t(float* losses, float* lse, T* dlogits, const T* logits,
+                         const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                         int ld, int32_t* err_flag, hipStream_t stream, const char* name) {
+  if (N < 1 || V < 1 || ld < V || ld % 4 || !aligned16(logits) || !aligned16(dlogits) ||
+      ld > crossentropy_fused_max_ld()) {
+    set_global_error("crossentropy_fused: bad arguments (V=%d ld=%d)", V, ld);
+    return -1;
+  }
+  ProfScope ps(name, 4.0 * N * V, 2.0 * sizeof(T) * N * ld + 12.0 * N, stream);
+  const int per = (ld / 4 + XF_THREADS - 1) / XF_THREADS;  // vectors of 4 per thread
+#define XF_LAUNCH(CH)                                                                      \
+  xent_fused_kernel<T, CH><<<N, XF_THREADS, 0, stream>>>(losses, lse, dlogits, logits,     \
+                                                         targets, dloss, dscale, V, ld, err_flag)
+  if (per <= 1) XF_LAUNCH(1);
+  else if (per <= 2) XF_LAUNCH(2);
+  else if (per <= 4) XF_LAUNCH(4);
+  else if (per <= 8) XF_LAUNCH(8);
+  else if (per <= 13) XF_LAUNCH(13);
+  else XF_LAUNCH(16);
+#undef XF_LAUNCH
+  GPT2_HIP_OK(hipGetLastError());
+  return 0;
+}
 }  // namespace
 
 int crossentropy_forward(float* losses, float* lse, const float* logits, const int32_t* targets,
@@ -839,6 +943,26 @@ int crossentropy_backward(f16_t* logits, const float* lse, const int32_t* target
                           const float* dscale, int N, int V, int ld, hipStream_t stream) {
   return crossentropy_backward_t(logits, lse, targets, dloss, dscale, N, V, ld, stream,
                                  "xent_bwd_f16_kernel");
+}
+
+int crossentropy_fused_max_ld() { return 16 * 4 * XF_THREADS; }
+int crossentropy_fused(float* losses, float* lse, float* dlogits, const float* logits,
+                       const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                       int ld, int32_t* err_flag, hipStream_t stream) {
+  return crossentropy_fused_t(losses, lse, dlogits, logits, targets, dloss, dscale, N, V, ld,
+                              err_flag, stream, "xent_fused_kernel");
+}
+int crossentropy_fused(float* losses, float* lse, bf16_t* dlogits, const bf16_t* logits,
+                       const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                       int ld, int32_t* err_flag, hipStream_t stream) {
+  return crossentropy_fused_t(losses, lse, dlogits, logits, targets, dloss, dscale, N, V, ld,
+                              err_flag, stream, "xent_fused_bf16_kernel");
+}
+int crossentropy_fused(float* losses, float* lse, f16_t* dlogits, const f16_t* logits,
+                       const int32_t* targets, float dloss, const float* dscale, int N, int V,
+                       int ld, int32_t* err_flag, hipStream_t stream) {
+  return crossentropy_fused_t(losses, lse, dlogits, logits, targets, dloss, dscale, N, V, ld,
+                              err_flag, stream, "xent_fused_f16_kernel");
 }
 
 int mean_reduce(float* out, const float* x, int n, hipStream_t stream) {

@@ -150,11 +150,21 @@ int gpt2_get_adam_state(gpt2_model* model, float* m, float* v, int dst_is_device
 int gpt2_forward(gpt2_model* model, const int32_t* tokens, const int32_t* targets, int B,
                  int T, float* mean_loss);
 
-/* Per-position losses (B,T) and the logits (B,T,V) of the last forward. The logits buffer
- * is reused for their gradient by gpt2_backward, so gpt2_get_logits is valid only
- * between a forward and the next backward (else ERR_STATE). */
+/* Per-position losses (B,T) and the logits (B,T,V) of the last forward. gpt2_get_logits is
+ * valid only between a forward and the next backward (else ERR_STATE): the backward may
+ * reuse the logits buffer for their gradient. */
 int gpt2_get_losses(gpt2_model* model, float* dst, int dst_is_device);
 int gpt2_get_logits(gpt2_model* model, float* dst, int dst_is_device);
+
+/* Where the loss gradient of the logits ([llm.c] 1.15) is formed. With on = 1 (the default)
+ * a forward with targets computes the losses and d(mean loss)/d(logits) in one pass over
+ * the logits (gpt2_k_crossentropy_fused) into a buffer of its own, the size of the logits,
+ * that the next gpt2_backward reads; with on = 0 the forward only computes the losses and
+ * the backward forms the gradient in place of the logits (one more pass over them, no extra
+ * buffer; for forward-only evaluation). Takes effect at the next forward; turning it on
+ * after the first forward of a model built with it off is ERR_STATE (the buffer is sized
+ * with the activations). Results agree to rounding either way. */
+int gpt2_set_loss_grad_in_forward(gpt2_model* model, int on);
 
 /* Set all parameter gradients to zero ([llm.c] 1.24 gpt2_zero_grad). The library writes,
  * rather than accumulates, every activation gradient, so only parameter gradients need
@@ -333,6 +343,14 @@ int gpt2_k_crossentropy_forward(float* losses, float* lse, const float* logits,
  * dloss for v < V, and 0 for V <= v < ld. */
 int gpt2_k_crossentropy_backward(float* logits, const float* lse, const int32_t* targets,
                                  float dloss, int N, int V, int ld, void* stream);
+
+/* [llm.c] 1.13 - 1.15 in one pass: per row as gpt2_k_crossentropy_forward (losses, lse,
+ * err_flag), and dlogits[r,v] = (exp(logits[r,v] - lse[r]) - [v == target[r]]) * dloss for
+ * v < V, 0 for V <= v < ld, written to dlogits (N x ld, distinct from logits, which are
+ * left unchanged). ld must be at most 65536; ERR_ARG otherwise. */
+int gpt2_k_crossentropy_fused(float* losses, float* lse, float* dlogits, const float* logits,
+                              const int32_t* targets, float dloss, int N, int V, int ld,
+                              int32_t* err_flag, void* stream);
 
 /* [llm.c] 1.35 on one row of fp32 logits (device, V entries): *token (device int32) = the
  * index drawn with coin, as gpt2_sample. */

@@ -237,6 +237,54 @@ def test_crossentropy_forward_backward(N, V, ld):
     assert np.all(g[:, V:] == 0.0)
 
 
+@pytest.mark.parametrize("N,V,ld", [(37, 50257, 50304), (64, 27, 28), (5, 3, 4), (3, 5000, 5004),
+                                     (2, 65536, 65536)])
+def test_crossentropy_fused(N, V, ld):
+    # one pass: losses and lse as the forward, dlogits as the backward, logits unchanged;
+    # the ld values span each register-block count of the kernel (1 .. 16 vectors a thread)
+    r = rng(N + V + 1)
+    z = np.zeros((N, ld), np.float32)
+    z[:, :V] = r.normal(0, 2.0, (N, V))
+    z[:, V:] = 123.0  # padding must be ignored
+    y = r.integers(0, V, N).astype(np.int32)
+    y[0] = V - 1  # the last real column
+    logits = dev(z)
+    dl = torch.full((N, ld), float("nan"), device="cuda")
+    losses = torch.empty(N, device="cuda")
+    lse = torch.empty(N, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gb.k_crossentropy_fused(losses, lse, dl, logits, dev(y), 1.0 / N, N, V, ld, err)
+    rl = oracle.crossentropy_forward(z[:, :V], y)
+    assert_close("fused xent loss", host(losses), rl, rtol=1e-5, atol=1e-6)
+    assert int(host(err)[0]) == 0
+    rd = oracle.crossentropy_softmax_backward(z[:, :V], y, np.full(N, 1.0 / N))
+    g = host(dl)
+    assert_close("fused xent dlogits", g[:, :V], rd)
+    assert np.all(g[:, V:] == 0.0)
+    assert np.array_equal(host(logits), z)
+    # the same lse as the separate forward kernel up to rounding
+    lse2 = torch.empty(N, device="cuda")
+    gb.k_crossentropy_forward(torch.empty(N, device="cuda"), lse2, logits, dev(y), N, V, ld)
+    assert_close("fused lse", host(lse), host(lse2), rtol=1e-6, atol=1e-6)
+
+
+def test_crossentropy_fused_flags_bad_target_and_rejects_aliasing():
+    N, V = 4, 27
+    z = dev(np.zeros((N, 28), np.float32))
+    y = dev(np.array([1, 2, 27, -1], np.int32))
+    losses, lse = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+    dl = torch.empty((N, 28), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gb.k_crossentropy_fused(losses, lse, dl, z, y, 0.25, N, V, 28, err)
+    assert int(host(err)[0]) == 1
+    assert np.all(np.isfinite(host(losses))) and np.all(np.isfinite(host(dl)))
+    with pytest.raises(gb.GPT2Error):
+        gb.k_crossentropy_fused(losses, lse, z, z, y, 0.25, N, V, 28, err)
+    with pytest.raises(gb.GPT2Error):  # rows longer than the kernel holds
+        big = torch.zeros((1, 65540), device="cuda")
+        gb.k_crossentropy_fused(losses, lse, big, big.clone(), y, 1.0, 1, 65540, 65540, err)
+
+
 def test_crossentropy_flags_bad_target():
     N, V = 4, 27
     z = dev(np.zeros((N, 28), np.float32))

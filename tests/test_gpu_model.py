@@ -43,10 +43,15 @@ def make_model(shape, B=0, T=0):
     return gb.GPT2(shape.L, shape.C, shape.H, shape.V, shape.maxT, B, T)
 
 
-def run_steps(shape, wl_seed, B, T, steps, token_mode, scale_residual):
-    """The oracle follows its own trajectory (its own gradients into its own AdamW)."""
+def run_steps(shape, wl_seed, B, T, steps, token_mode, scale_residual,
+              loss_grad_in_forward=True):
+    """The oracle follows its own trajectory (its own gradients into its own AdamW).
+    loss_grad_in_forward False: the backward forms the loss gradient in place of the logits
+    (gpt2_set_loss_grad_in_forward(0)) instead of reading the forward's fused pass."""
     p0 = synth.init_params(shape, wl_seed, scale_residual)
     m = make_model(shape)
+    if not loss_grad_in_forward:
+        m.set_loss_grad_in_forward(False)
     m.set_params(p0)
     rp, rm, rv = p0.astype(np.float64), np.zeros(p0.size), np.zeros(p0.size)
     for step in range(steps):
@@ -81,6 +86,32 @@ def test_tiny_one_step_and_ten_steps():
 def test_small_multilayer_ragged_three_steps():
     shape = synth.ModelShape(L=2, C=64, H=4, V=1000, maxT=128)
     run_steps(shape, 4242, 3, 100, 3, "stream", True)
+
+
+def test_small_multilayer_ragged_loss_grad_in_backward():
+    shape = synth.ModelShape(L=2, C=64, H=4, V=1000, maxT=128)
+    run_steps(shape, 4242, 3, 100, 3, "stream", True, loss_grad_in_forward=False)
+
+
+def test_loss_grad_in_forward_switch():
+    """Turning the fused loss gradient on after a forward of a model sized without its
+    buffer is refused; off and on again with the buffer present is allowed."""
+    shape = synth.ModelShape(L=1, C=16, H=4, V=27, maxT=16)
+    tok, tgt = synth.batch(7, 2, 8, shape.V, step=0, mode="stream")
+    m = make_model(shape)
+    m.set_loss_grad_in_forward(False)
+    m.set_params(synth.init_params(shape, 7, True))
+    m.forward(dev_i32(tok), dev_i32(tgt))
+    with pytest.raises(gb.GPT2Error) as e:
+        m.set_loss_grad_in_forward(True)
+    assert e.value.code == -4  # GPT2_ERR_STATE
+    m.close()
+    m = make_model(shape)
+    m.set_params(synth.init_params(shape, 7, True))
+    m.forward(dev_i32(tok), dev_i32(tgt))
+    m.set_loss_grad_in_forward(False)
+    m.set_loss_grad_in_forward(True)
+    m.close()
 
 
 @pytest.mark.timeout(600)
