@@ -62,89 +62,75 @@ __global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const float* __
   }
 }
 
-// Stable sort of positions by token, in one workgroup of 1024 threads:
-// count[v] = occurrences (integer atomics: the counts do not depend on order);
-// offset = exclusive prefix sum of count; then positions are placed chunk by chunk
-// (1024 at a time, in order), each at offset[v] + (earlier occurrences of v), so within a
-// token positions stay ascending. scratch: count[V], offset[V]; out: sorted[BT].
+// Stable sort of positions by token, in two fully parallel steps.
+// token_chunk_sort_kernel: one 1024-thread workgroup per chunk of 1024 consecutive
+// positions sorts the chunk's keys (token << 10 | position in the chunk) with a bitonic
+// network in LDS; the last chunk is padded with keys above every real key.
+// token_merge_kernel: the place of a key in the whole sorted order is its index in its own
+// chunk plus, for every earlier chunk, the number of keys with a token at most its own and,
+// for every later chunk, the number with a token below its own (lower bounds by binary
+// search in the sorted chunks, eight chunks searched in lockstep). Equal tokens thus keep
+// position order, and the result is a function of the tokens alone.
+// scratch: sorted[BT], keys[nchunks * 1024].
 constexpr int SORT_THREADS = 1024;
-__global__ __launch_bounds__(SORT_THREADS) void token_sort_kernel(int32_t* __restrict__ sorted,
-                                                                  int32_t* __restrict__ count,
-                                                                  int32_t* __restrict__ offset,
-                                                                  const int32_t* __restrict__ tok,
-                                                                  int BT, int V) {
-  __shared__ int32_t part[SORT_THREADS];
-  __shared__ int32_t chunk_tok[SORT_THREADS];
+constexpr int32_t SORT_PAD = 0x7FFFFFFF;
+__global__ __launch_bounds__(SORT_THREADS) void token_chunk_sort_kernel(
+    int32_t* __restrict__ keys, const int32_t* __restrict__ tok, int BT, int V) {
+  __shared__ int32_t key_s[SORT_THREADS];
   const int tid = threadIdx.x;
-  for (int v = tid; v < V; v += SORT_THREADS) count[v] = 0;
+  const int c0 = blockIdx.x * SORT_THREADS, i = c0 + tid;
+  key_s[tid] = i < BT ? (clamp_tok(tok[i], V) << 10) | tid : SORT_PAD;
   __syncthreads();
-  for (int i = tid; i < BT; i += SORT_THREADS) atomicAdd(&count[clamp_tok(tok[i], V)], 1);
-  __threadfence_block();
-  __syncthreads();
-  // exclusive scan: each thread owns a contiguous segment of the vocabulary
-  const int seg = (V + SORT_THREADS - 1) / SORT_THREADS;
-  const int v0 = min(V, tid * seg), v1 = min(V, v0 + seg);
-  int s = 0;
-  for (int v = v0; v < v1; v++) s += count[v];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < SORT_THREADS; o <<= 1) {  // inclusive Hillis-Steele scan
-    int add = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  int run = part[tid] - s;
-  for (int v = v0; v < v1; v++) {
-    offset[v] = run;
-    run += count[v];
-  }
-  __threadfence_block();
-  __syncthreads();
-  // place positions, 1024 at a time: the chunk is sorted by (token, position) with a
-  // bitonic network in LDS, so each position's rank among the chunk's occurrences of its
-  // token is its distance from the start of its run; offset[v] then advances by the run
-  for (int c0 = 0; c0 < BT; c0 += SORT_THREADS) {
-    const int i = c0 + tid;
-    // key: token in the high bits, position within the chunk in the low 10 bits
-    chunk_tok[tid] = i < BT ? (clamp_tok(tok[i], V) << 10) | tid : 0x7FFFFFFF;
-    __syncthreads();
-    for (int k = 2; k <= SORT_THREADS; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        const int partner = tid ^ j;
-        if (partner > tid) {
-          const int a = chunk_tok[tid], b = chunk_tok[partner];
-          const bool up = (tid & k) == 0;
-          if ((a > b) == up) {
-            chunk_tok[tid] = b;
-            chunk_tok[partner] = a;
-          }
+  for (int k = 2; k <= SORT_THREADS; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int partner = tid ^ j;
+      if (partner > tid) {
+        const int a = key_s[tid], b = key_s[partner];
+        const bool up = (tid & k) == 0;
+        if ((a > b) == up) {
+          key_s[tid] = b;
+          key_s[partner] = a;
         }
-        __syncthreads();
+      }
+      __syncthreads();
+    }
+  }
+  keys[c0 + tid] = key_s[tid];
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void token_merge_kernel(
+    int32_t* __restrict__ sorted, const int32_t* __restrict__ keys, int nchunks) {
+  constexpr int G = 8;  // chunks searched together
+  const int c = blockIdx.x, j = threadIdx.x;
+  const int key = keys[c * SORT_THREADS + j];
+  if (key == SORT_PAD) return;
+  const int v = key >> 10;
+  int dest = j;
+  for (int g0 = 0; g0 < nchunks; g0 += G) {
+    int lo[G];
+#pragma unroll
+    for (int u = 0; u < G; u++) lo[u] = 0;
+#pragma unroll
+    for (int step = SORT_THREADS / 2; step > 0; step >>= 1) {
+#pragma unroll
+      for (int u = 0; u < G; u++) {
+        const int c2 = g0 + u;
+        if (c2 < nchunks && c2 != c) {
+          const int bound = c2 < c ? (v + 1) << 10 : v << 10;
+          if (keys[c2 * SORT_THREADS + lo[u] + step - 1] < bound) lo[u] += step;
+        }
       }
     }
-    // run starts: part[x] = x where the token changes, then a max-scan gives each slot
-    // the start of its run
-    const int key = chunk_tok[tid];
-    const int v = key >> 10;
-    const bool valid = key != 0x7FFFFFFF;
-    part[tid] = (tid == 0 || (chunk_tok[tid - 1] >> 10) != v) ? tid : 0;
-    __syncthreads();
-    for (int o = 1; o < SORT_THREADS; o <<= 1) {
-      const int other = tid >= o ? part[tid - o] : 0;
-      __syncthreads();
-      part[tid] = max(part[tid], other);
-      __syncthreads();
+#pragma unroll
+    for (int u = 0; u < G; u++) {
+      const int c2 = g0 + u;
+      if (c2 < nchunks && c2 != c) {
+        const int bound = c2 < c ? (v + 1) << 10 : v << 10;
+        dest += lo[u] + (keys[c2 * SORT_THREADS + lo[u]] < bound ? 1 : 0);
+      }
     }
-    const int start = part[tid];
-    const bool last = valid && (tid == SORT_THREADS - 1 || (chunk_tok[tid + 1] >> 10) != v);
-    if (valid) sorted[offset[v] + (tid - start)] = c0 + (key & 1023);
-    __threadfence_block();
-    __syncthreads();  // every slot of a run has read offset[v]
-    if (last) offset[v] += tid - start + 1;
-    __threadfence_block();
-    __syncthreads();
   }
+  sorted[dest] = c * SORT_THREADS + (key & 1023);
 }
 
 // One wave per sorted index j; the wave that starts a run of equal tokens adds the run's
@@ -717,7 +703,11 @@ int encoder_forward(f16_t* out, const int32_t* tok, const float* wte, const floa
                            "encoder_fwd_f16_kernel");
 }
 
-size_t encoder_sort_scratch_ints(int BT, int V) { return (size_t)2 * V + BT; }
+size_t encoder_sort_scratch_ints(int BT, int V) {
+  (void)V;
+  const size_t padded = (size_t)(BT + SORT_THREADS - 1) / SORT_THREADS * SORT_THREADS;
+  return (size_t)BT + padded;
+}
 
 int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok, int B,
                      int T, int C, int V, int32_t* scratch, hipStream_t stream) {
@@ -726,9 +716,13 @@ int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t*
     return -1;
   }
   const int BT = B * T;
-  int32_t* count = scratch;
-  int32_t* offset = scratch + V;
-  int32_t* sorted = scratch + 2 * (size_t)V;
+  if (V >= (1 << 21)) {  // keys hold the token in their upper 21 bits
+    set_global_error("encoder_backward: vocabulary of %d tokens is too large", V);
+    return -1;
+  }
+  int32_t* sorted = scratch;
+  const int nchunks = (BT + SORT_THREADS - 1) / SORT_THREADS;
+  int32_t* keys = sorted + BT;
   {
     ProfScope ps("encoder_bwd_wpe_kernel", (double)BT * C, 4.0 * ((double)BT * C + 2.0 * T * C),
                  stream);
@@ -736,8 +730,12 @@ int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t*
         dwpe, dout, B, T, C);
   }
   {
-    ProfScope ps("token_sort_kernel", 0.0, 4.0 * (3.0 * BT + 3.0 * V), stream);
-    token_sort_kernel<<<1, SORT_THREADS, 0, stream>>>(sorted, count, offset, tok, BT, V);
+    ProfScope ps("token_chunk_sort_kernel", 0.0, 4.0 * 2.0 * BT, stream);
+    token_chunk_sort_kernel<<<nchunks, SORT_THREADS, 0, stream>>>(keys, tok, BT, V);
+  }
+  {
+    ProfScope ps("token_merge_kernel", 0.0, 4.0 * 2.0 * BT, stream);
+    token_merge_kernel<<<nchunks, SORT_THREADS, 0, stream>>>(sorted, keys, nchunks);
   }
   ProfScope ps("encoder_bwd_wte_kernel", (double)BT * C, 4.0 * (3.0 * BT * C + 2.0 * BT), stream);
   encoder_bwd_wte_kernel<<<(BT + 3) / 4, 256, 0, stream>>>(dwte, dout, tok, sorted, BT, C, V);

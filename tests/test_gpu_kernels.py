@@ -296,7 +296,8 @@ def test_crossentropy_flags_bad_target():
     assert np.all(np.isfinite(host(losses)))
 
 
-@pytest.mark.parametrize("B,T,C,V", [(4, 33, 64, 50), (2, 16, 16, 27), (8, 1024, 768, 50257)])
+@pytest.mark.parametrize("B,T,C,V", [(4, 33, 64, 50), (2, 16, 16, 27), (8, 1024, 768, 50257),
+                                     (3, 700, 16, 40)])
 def test_encoder_forward_backward(B, T, C, V):
     r = rng(B + T + C)
     maxT = T + 3
@@ -324,6 +325,15 @@ def test_encoder_forward_backward(B, T, C, V):
     dwte2 = dev(dwte0)
     gb.k_encoder_backward(dwte2, dev(dwpe0), dev(d), dev(tok), B, T, C, V)
     assert np.array_equal(host(dwte2), g1)
+    # and it is the fp32 sum of each token's rows taken in ascending position order, added
+    # to the old row (positions sorted stably by token, across the sort's 1024-position
+    # chunks): checked bitwise on the tokens that occur
+    flat, dflat = tok.reshape(-1), d.reshape(-1, C)
+    for v in np.unique(flat)[:64]:
+        acc = np.zeros(C, np.float32)
+        for i in np.nonzero(flat == v)[0]:
+            acc = acc + dflat[i]
+        assert np.array_equal(g1[v], dwte0[v] + acc), v
 
 
 def test_encoder_flags_bad_token():
