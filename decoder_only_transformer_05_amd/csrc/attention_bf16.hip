@@ -843,15 +843,16 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dkdv_x6_kernel(
                      *reinterpret_cast<const bf16x8*>(&Op[2 * PQ + o]), vh[ks], vmd[ks], vl[ks],
                      dp);
       }
-      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's; the
-      // exponential is taken for every entry and masked after
+      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's. A
+      // sub-block whose 32 queries all follow the wave's 32 keys and lie before T needs no
+      // mask (uniform test); elsewhere the exponential is taken and masked after.
+      const bool nomask = q0 + 32 * qb >= key0 + 31 && q0 + 32 * qb + 32 <= T;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const int qo = 32 * qb + 8 * (i / 4) + (i % 4);  // query - 4lh
         const int qa = q0 + qo + 4 * lh;
-        const bool ok = qa < T && qa >= key;
         const float e = __builtin_amdgcn_exp2f(s[i] * scale_log2 - Ls[qo + 4 * lh]);
-        const float p = ok ? e : 0.f;
+        const float p = nomask || (qa < T && qa >= key) ? e : 0.f;
         s[i] = p;
         dp[i] = p * (dp[i] - Ds[qo + 4 * lh]);
         dst[qo * TILE] = dp[i];  // 32 lanes store 32 consecutive keys
