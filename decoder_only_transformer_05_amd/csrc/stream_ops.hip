@@ -18,6 +18,26 @@ namespace {
 // index leaves its buffer
 GPT2_DEVICE_INLINE int clamp_tok(int v, int V) { return (v < 0 || v >= V) ? 0 : v; }
 
+// Loads and stores marked nontemporal (not kept in the caches), for the AdamW streams, which
+// are read and written once per step and not read again soon. A probe on this GPU: an
+// AdamW-shaped stream of 124M parameters (four reads, three writes) at 5.30 TB/s with plain
+// accesses, 5.50 TB/s nontemporal; AdamW itself 642 -> 583 us at 124M. (The one-pass
+// cross-entropy was 2% slower with them and keeps plain accesses.)
+GPT2_DEVICE_INLINE f32x4 ld4_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+GPT2_DEVICE_INLINE void st4_nt(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+GPT2_DEVICE_INLINE void st4_nt(bf16_t* p, f32x4 v) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(p));
+}
+GPT2_DEVICE_INLINE void st4_nt(f16_t* p, f32x4 v) {
+  __builtin_nontemporal_store(__builtin_convertvector(v, f16x4_t), reinterpret_cast<f16x4_t*>(p));
+}
+
 int blocks_for(long long n, int per_block, int cap) {
   long long b = (n + per_block - 1) / per_block;
   if (b > cap) b = cap;
@@ -578,7 +598,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
   const float gs = inv_scale ? *inv_scale : 1.f;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i < n4) {
-    f32x4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
+    f32x4 pp = ld4_nt(p + 4 * i), gg = ld4_nt(g + 4 * i), mm = ld4_nt(m + 4 * i),
+          vv = ld4_nt(v + 4 * i);
     if (inv_scale) gg *= gs;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -588,10 +609,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
       mm[j] = mj;
       vv[j] = vj;
     }
-    st4(p + 4 * i, pp);
-    st4(m + 4 * i, mm);
-    st4(v + 4 * i, vv);
-    if (pbf) st4(pbf + 4 * i, pp);
+    st4_nt(p + 4 * i, pp);
+    st4_nt(m + 4 * i, mm);
+    st4_nt(v + 4 * i, vv);
+    if (pbf) st4_nt(pbf + 4 * i, pp);
   } else {
     const long long e = 4 * n4 + (i - n4);
     if (e >= n) return;
