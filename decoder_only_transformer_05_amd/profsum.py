@@ -4,7 +4,7 @@
     python -m decoder_only_transformer_05_amd.profsum traffic OUT_JSON KERNEL \\
         FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_BYTES "COMMANDS"
     python -m decoder_only_transformer_05_amd.profsum traffic-table OUT_MD \\
-        FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_BYTES "COMMANDS"
+        FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_BYTES "COMMANDS" [KERNEL_TABLE]
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown table.
 
@@ -168,13 +168,34 @@ def traffic_json(dst: str, kernel: str, fetch_csv: str, write_csv: str, copy_fet
     return rec
 
 
+def algorithmic_bytes(kernel_table: str) -> dict:
+    """Algorithmic bytes per launch by kernel, from a `bench.py --kernel-table` file (the
+    library's launch profile: each launch's bytes as the method defines them)."""
+    with open(kernel_table) as fh:
+        t = json.load(fh)["kernels"]
+    return {k: v["bytes"] / v["launches"] for k, v in t.items() if v.get("launches")}
+
+
+def _lookup(alg: dict, kernel: str):
+    """The launch-profile entry of a profiler kernel name: the same name, else the name
+    without its template arguments (the profile names some kernels without them)."""
+    if kernel in alg:
+        return alg[kernel]
+    base = kernel.split("<")[0]
+    return alg.get(base)
+
+
 def traffic_md(dst: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
-               copy_write_csv: str, copy_bytes: float, command: str) -> None:
-    """Calibrated HBM bytes per launch of every kernel of the run, largest total first."""
+               copy_write_csv: str, copy_bytes: float, command: str,
+               kernel_table: str | None = None) -> None:
+    """Calibrated HBM bytes per launch of every kernel of the run, largest total first; with
+    a launch-profile table, also each kernel's algorithmic bytes and the measured/algorithmic
+    ratio."""
     fe = counter_per_kernel(fetch_csv, "FETCH_SIZE")
     wr = counter_per_kernel(write_csv, "WRITE_SIZE")
     sf = copy_bytes / (copy_kib(copy_fetch_csv, "FETCH_SIZE") * 1024.0)
     sw = copy_bytes / (copy_kib(copy_write_csv, "WRITE_SIZE") * 1024.0)
+    alg = algorithmic_bytes(kernel_table) if kernel_table else None
     rows = []
     for k in fe:
         n, f = fe[k]
@@ -185,10 +206,22 @@ def traffic_md(dst: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
         fh.write("# HBM traffic per kernel launch (FETCH_SIZE / WRITE_SIZE, calibrated)\n\n"
                  f"Commands (from the repository root, on one MI355X):\n\n```\n{command}\n```\n\n"
                  f"Scale factors from a plain {copy_bytes / 2**30:.0f} GiB device copy: fetch x{sf:.3f}, "
-                 f"write x{sw:.3f} (the counters' KiB times these give bytes).\n\n"
-                 "| kernel | dispatches | fetch MB/launch | write MB/launch |\n|---|---|---|---|\n")
+                 f"write x{sw:.3f} (the counters' KiB times these give bytes).\n\n")
+        if alg is None:
+            fh.write("| kernel | dispatches | fetch MB/launch | write MB/launch |\n"
+                     "|---|---|---|---|\n")
+            for k, n, f, w in rows:
+                fh.write(f"| {k} | {n} | {f / 1e6:.2f} | {w / 1e6:.2f} |\n")
+            return
+        fh.write("Algorithmic bytes: what the method reads and writes per launch (the library's "
+                 "launch profile, `bench.py --kernel-table`); for the GEMMs and attention the "
+                 "operands and results once each.\n\n"
+                 "| kernel | dispatches | fetch MB/launch | write MB/launch | algorithmic MB/launch "
+                 "| measured / algorithmic |\n|---|---|---|---|---|---|\n")
         for k, n, f, w in rows:
-            fh.write(f"| {k} | {n} | {f / 1e6:.2f} | {w / 1e6:.2f} |\n")
+            a = _lookup(alg, k)
+            extra = (f"| {a / 1e6:.2f} | {(f + w) / a:.2f} |" if a else "| | |")
+            fh.write(f"| {k} | {n} | {f / 1e6:.2f} | {w / 1e6:.2f} {extra}\n")
 
 
 def mfma_md(dst: str, csv_path: str, command: str, simds: int = 1024, xcds: int = 8) -> None:
@@ -250,8 +283,9 @@ def main(argv: list[str]) -> int:
                            float(argv[7]), argv[8])
         print(json.dumps(rec, indent=1))
         return 0
-    if argv[:1] == ["traffic-table"] and len(argv) == 8:
-        traffic_md(argv[1], argv[2], argv[3], argv[4], argv[5], float(argv[6]), argv[7])
+    if argv[:1] == ["traffic-table"] and len(argv) in (8, 9):
+        traffic_md(argv[1], argv[2], argv[3], argv[4], argv[5], float(argv[6]), argv[7],
+                   argv[8] if len(argv) == 9 else None)
         return 0
     if argv[:1] == ["mfma"] and len(argv) == 4:
         mfma_md(argv[1], argv[2], argv[3])

@@ -54,3 +54,49 @@ def test_traffic_records_are_current():
         workload = workload[len("".join(c if c.isalnum() else "_"
                                         for c in rec["kernel"]).strip("_")) + 1:]
         assert bench.measured_traffic(rec["kernel"], workload) == rec["bytes_per_launch"]
+
+
+def _counter_csv(path, counter, rows):
+    """A rocprofv3 counter_collection.csv with the columns profsum reads."""
+    with open(path, "w") as fh:
+        fh.write('"Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+        for name, value, t0, t1 in rows:
+            fh.write(f'"{name}","{counter}",{value},{t0},{t1}\n')
+
+
+def test_profsum_tables(tmp_path):
+    # mangled _Float16 instances are named as the profiler names the others
+    assert profsum.short_name(
+        "_ZN4gpt212_GLOBAL__N_117xent_fused_kernelIDF16_Li13ELi0EEEvPfS2_PT_PKS3_PKifPKfiiPi"
+    ) == "xent_fused_kernel<_Float16,13,0>"
+    assert profsum.short_name(
+        "void gpt2::(anonymous namespace)::gemm_x6_kernel<256, true, true, 0>(gpt2::Args)"
+    ) == "gemm_x6_kernel<256,1,1,0>"
+    # traffic: counters in KiB per dispatch, scaled by the copy calibration (fetch reads half),
+    # joined with the launch profile's algorithmic bytes (by name, else without template args)
+    k = "void gpt2::(anonymous namespace)::adamw_kernel<unsigned short>(float*)"
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(k, 1000.0, 0, 1), (k, 1000.0, 2, 3)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(k, 1500.0, 0, 1), (k, 1500.0, 2, 3)])
+    _counter_csv(tmp_path / "cf.csv", "FETCH_SIZE", [("copy", 512.0, 0, 1)])
+    _counter_csv(tmp_path / "cw.csv", "WRITE_SIZE", [("copy", 1024.0, 0, 1)])
+    with open(tmp_path / "kt.json", "w") as fh:
+        json.dump({"kernels": {"adamw_kernel": {"bytes": 2 * 2.5e6, "launches": 2}}}, fh)
+    out = tmp_path / "t.md"
+    profsum.traffic_md(str(out), str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                       str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1048576.0, "cmd",
+                       str(tmp_path / "kt.json"))
+    row = [l for l in out.read_text().splitlines() if l.startswith("| adamw_kernel")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "2" and cells[2] == "2.05" and cells[3] == "1.54"  # MB per launch
+    assert cells[4] == "2.50" and cells[5] == "1.43"
+    # MFMA busy: GRBM_GUI_ACTIVE summed over 8 XCDs; busy cycles over cycles x 1024 SIMDs
+    g = "void gpt2::(anonymous namespace)::gemm_x6_kernel<256, true, true, 0>(gpt2::Args)"
+    with open(tmp_path / "m.csv", "w") as fh:
+        fh.write('"Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+        fh.write(f'"{g}","GRBM_GUI_ACTIVE",{8 * 1000},0,500\n')
+        fh.write(f'"{g}","SQ_VALU_MFMA_BUSY_CYCLES",{1024 * 600},0,500\n')
+        fh.write(f'"{g}","SQ_INSTS_VALU_MFMA_MOPS_BF16",{1024 * 1024 * 600 / 512},0,500\n')
+    profsum.mfma_md(str(tmp_path / "m.md"), str(tmp_path / "m.csv"), "cmd")
+    row = [l for l in (tmp_path / "m.md").read_text().splitlines() if l.startswith("| gemm")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[2] == "60.0" and cells[3] == "60.0" and cells[8] == "2.00"
