@@ -665,6 +665,8 @@ int gpt2_build_ex(gpt2_model** out, int L, int C, int H, int V, int maxT, int dt
                 "(C=%d H=%d)", C, H);
   if ((C / 4 + 63) / 64 > 8)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: C=%d above the supported 2048", C);
+  if (V >= (1 << 21))  // the embedding backward's token sort keeps tokens in 21 bits
+    return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: V=%d at or above the supported 2^21", V);
   if (dtype != GPT2_DTYPE_FP32 && dtype != GPT2_DTYPE_BF16 && dtype != GPT2_DTYPE_FP16)
     return fail(nullptr, GPT2_ERR_ARG, "gpt2_build: dtype %d is not supported", dtype);
   if ((maxB > 0) != (maxTseq > 0) || maxTseq > maxT)

@@ -82,7 +82,8 @@ enum { GPT2_DTYPE_FP32 = 0, GPT2_DTYPE_BF16 = 1, GPT2_DTYPE_FP16 = 2 };
  * block holding parameters, gradients and the two AdamW moments (4 x num_params fp32),
  * all zero. Activations are allocated as one flat block at the first gpt2_forward, for
  * that call's B and T ([llm.c] 1.23 allocates lazily; 1.19 one allocation).
- * Requires C % H == 0, C % 4 == 0 and (C/H) % 4 == 0 with C/H <= 128; all sizes >= 1.
+ * Requires C % H == 0, C % 4 == 0 and (C/H) % 4 == 0 with C/H <= 128, C <= 2048 and
+ * V < 2^21; all sizes >= 1.
  * *out receives the handle, or NULL on error. */
 int gpt2_build(gpt2_model** out, int L, int C, int H, int V, int maxT);
 
@@ -266,7 +267,8 @@ int gpt2_k_encoder_forward(float* out, const int32_t* tok, const float* wte, con
                            int B, int T, int C, int V, int32_t* err_flag, void* stream);
 
 /* [llm.c] 1.2: dwte[tok[b,t]] += dout[b,t]; dwpe[t] += sum_b dout[b,t]. Deterministic:
- * rows of one token are summed in ascending (b,t) order. Tokens must be in [0,V). */
+ * rows of one token are summed in ascending (b,t) order. Tokens must be in [0,V) (others
+ * count as token 0); V below 2^21 (ERR_ARG otherwise). */
 int gpt2_k_encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
                             int B, int T, int C, int V, void* stream);
 

@@ -46,6 +46,8 @@ def test_version_string():
     (1, 16, 4, 0, 16),      # V < 1
     (1, 16, 4, 27, 0),      # maxT < 1
     (1, 1024, 4, 27, 16),   # head size 256 > 128
+    (1, 4096, 32, 27, 16),  # C above 2048
+    (1, 16, 4, 1 << 21, 16),  # V at 2^21: the token sort keeps tokens in 21 bits
 ])
 def test_build_rejects_bad_shapes_without_a_device(dims):
     lib = binding.lib()
