@@ -858,19 +858,34 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dkdv_x6_kernel(
                      *reinterpret_cast<const bf16x8*>(&Op[2 * PQ + o]), vh[ks], vmd[ks], vl[ks],
                      dp);
       }
-      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's. A
-      // sub-block whose 32 queries all follow the wave's 32 keys and lie before T needs no
-      // mask (uniform test); elsewhere the exponential is taken and masked after.
+      // s[i], dp[i]: query 32qb + 8(i/4) + 4lh + i%4 of the tile, key = this lane's. The
+      // lane's 16 row statistics are four runs of four consecutive rows, read as 16-byte
+      // vectors; the exponential is taken for every entry and masked after (no branch per
+      // entry). A sub-block whose 32 queries all follow the wave's 32 keys and lie before T
+      // needs no mask (uniform test).
       const bool nomask = q0 + 32 * qb >= key0 + 31 && q0 + 32 * qb + 32 <= T;
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int qo = 32 * qb + 8 * (i / 4) + (i % 4);  // query - 4lh
-        const int qa = q0 + qo + 4 * lh;
-        const float e = __builtin_amdgcn_exp2f(s[i] * scale_log2 - Ls[qo + 4 * lh]);
-        const float p = nomask || (qa < T && qa >= key) ? e : 0.f;
-        s[i] = p;
-        dp[i] = p * (dp[i] - Ds[qo + 4 * lh]);
-        dst[qo * TILE] = dp[i];  // 32 lanes store 32 consecutive keys
+      for (int g4 = 0; g4 < 4; g4++) {
+        const int qo = 32 * qb + 8 * g4 + 4 * lh;  // first of the run
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[qo]);
+        const f32x4 dq = *reinterpret_cast<const f32x4*>(&Ds[qo]);
+        float pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) pv[j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g4 + j], scale_log2, -lq[j]));
+        if (!nomask) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const int qa = q0 + qo + j;
+            if (!(qa < T && qa >= key)) pv[j] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int i = 4 * g4 + j;
+          s[i] = pv[j];
+          dp[i] = pv[j] * (dp[i] - dq[j]);
+          dst[(qo - 4 * lh + j) * TILE] = dp[i];  // 32 lanes store 32 consecutive keys
+        }
       }
       // dV^T[d][key] += dO^T[d][q] P[q][key], dK^T[d][key] += Q^T[d][q] dS[q][key]; k step
       // hh takes accumulator entries 8hh .. 8hh+7 (queries 16hh + 4lh + {0..3, 8..11})
