@@ -373,12 +373,18 @@ struct RowsTileX6 {
 
 // Transposed tile of fp32 rows -> three bf16 planes S[p][d][kpos(row)] (64 columns each; with
 // KPOS false S[p][d][row]): a thread (of NT) moves blocks of 4 rows x 8 columns, split per
-// row, then transposed per plane
+// row, then transposed per plane. Block b takes head dims 8 (b % DG) and the row run
+// rq = run(b / DG): with kpos, run swaps bits 0 and 1, so the 16 lanes that write together
+// pair runs 4 positions apart (the two 8-byte halves of a 16-byte chunk) rather than runs
+// one chunk apart, whose writes to rows of one parity met in the same banks.
 template <int HSP, int NT, bool KPOS = true>
 struct ColsTileX6 {
   static constexpr int DG = HSP / 8;
   static constexpr int BLOCKS = (TILE / 4) * DG;
   static constexpr int NI = (BLOCKS + NT - 1) / NT;
+  static __device__ __forceinline__ int run(int j) {
+    return KPOS ? (j & ~3) | ((j & 1) << 1) | ((j >> 1) & 1) : j;
+  }
   f32x4 v[NI][4][2];
   __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
                                        int hs, int tid) {
@@ -386,7 +392,7 @@ struct ColsTileX6 {
     for (int i = 0; i < NI; i++) {
       const int b = tid + NT * i;
       if (BLOCKS % NT && b >= BLOCKS) break;
-      const int dg = b % DG, rq = b / DG;
+      const int dg = b % DG, rq = run(b / DG);
 #pragma unroll
       for (int j = 0; j < 4; j++) load8f(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs, v[i][j][0], v[i][j][1]);
     }
@@ -396,7 +402,7 @@ struct ColsTileX6 {
     for (int i = 0; i < NI; i++) {
       const int b = tid + NT * i;
       if (BLOCKS % NT && b >= BLOCKS) break;
-      const int dg = b % DG, rq = b / DG;
+      const int dg = b % DG, rq = run(b / DG);
       const int p = KPOS ? kpos(4 * rq) : 4 * rq;
       u32x4 x[3][4];  // [plane][row]
 #pragma unroll
@@ -714,19 +720,28 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dq_x6_kernel(float* __restr
 // dO is split into three bf16 planes per tensor, [query][d] in LDS with the 16-byte chunk c
 // of row q at chunk c ^ qswz(q). That one layout serves both uses:
 //   S = Q K^T and dP = dO V^T take Q and dO as the A operand, a lane reading 8 consecutive
-//   head dims of its query (16-byte reads; 8 consecutive rows hit 8 different chunks);
+//   head dims of its query (16-byte reads);
 //   dV^T = dO^T P and dK^T = Q^T dS take dO^T and Q^T as the A operand, read with
 //   transposing reads (ds_read_b64_tr_b16): lanes 4j .. 4j+3 of a 16-lane group read 16
 //   head dims of query row j of a run of four, and lane i receives head dim i of the four
 //   rows. The two reads of a fragment take the query runs 16h + 4lh and 16h + 8 + 4lh, the
 //   order in which the S / dP accumulators hold a lane's queries, so P and dS (split in
-//   registers) are the B operands as they stand. For four consecutive rows qswz takes
-//   values 2j + s, so the two chunks a row run reads land on eight different chunks.
+//   registers) are the B operands as they stand.
+// qswz is linear in the bits of q (bits 0..3 map to 2, 6, 3, 4) and makes both read
+// patterns conflict-free on the 64 four-byte banks of gfx950's LDS (and on 32): a row is
+// 128 bytes, so even rows fill banks 0-31 and odd rows 32-63, and the 16 rows of a 16-lane
+// row read take 8 different chunks among the even rows and 8 among the odd ones (a swizzle
+// of bits 0..2 alone repeats every 8 rows: two-way conflicts, counted by
+// SQ_LDS_BANK_CONFLICT); each transposing read of 32 lanes (either grouping of the four
+// 16-lane groups) touches every bank once. Since qswz(q + 8) = qswz(q) ^ 4, the second read
+// of head-dim block db (8 rows on) sits at the first read's offset for block db ^ 1.
 // The fp32 dS of each causal 64x64 tile is written ([query][key]) for the dQ kernel, as
 // attn_bwd_dkdv_kernel does.
 // ---------------------------------------------------------------------------------------
 constexpr int DX6_KEYS = X6_QT;
-GPT2_DEVICE_INLINE int qswz(int q) { return ((q & 3) << 1) | ((q >> 2) & 1); }
+GPT2_DEVICE_INLINE int qswz(int q) {
+  return ((q & 1) * 2) ^ (((q >> 1) & 1) * 6) ^ (((q >> 2) & 1) * 3) ^ (((q >> 3) & 1) * 4);
+}
 // element offset of head dims 8c .. 8c+7 of row q in a 64-wide plane
 GPT2_DEVICE_INLINE int qoff(int q, int c) { return q * 64 + ((c ^ qswz(q)) << 3); }
 
@@ -788,15 +803,16 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dkdv_x6_kernel(
     }
 
   // transposing-read address of this lane for k step hh of sub-block qb, head-dim block db
-  // (first of the two reads; the second is 8 rows on)
+  // (the first of the two reads, rows with bit 3 clear; the second, 8 rows on, is at
+  // tr_off(qb, hh, db ^ 1) + 8 HSP)
   auto tr_off = [&](int qb, int hh, int db) {
     const int q = 32 * qb + 16 * hh + 4 * lh + (i16 >> 2);
     const int d = 32 * db + 16 * g1 + 4 * (i16 & 3);
     return qoff(q, d >> 3) + (d & 7);
   };
-  auto frag_tr8 = [&](const bf16_t* p) -> bf16x8 {
+  auto frag_tr8 = [&](const bf16_t* p, const bf16_t* p8) -> bf16x8 {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * HSP));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p8 + 8 * HSP));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
@@ -898,11 +914,13 @@ __global__ __launch_bounds__(X6_NT, 2) void attn_bwd_dkdv_x6_kernel(
                f32x4{dp[8 * hh + 4], dp[8 * hh + 5], dp[8 * hh + 6], dp[8 * hh + 7]}, sh, sm, sl);
 #pragma unroll
         for (int db = 0; db < ND; db++) {
-          const int o = tr_off(qb, hh, db);
-          dvacc[db] = mfma_x6(frag_tr8(Op + o), frag_tr8(Op + PQ + o), frag_tr8(Op + 2 * PQ + o),
+          const int o = tr_off(qb, hh, db), o8 = tr_off(qb, hh, db ^ 1);
+          dvacc[db] = mfma_x6(frag_tr8(Op + o, Op + o8), frag_tr8(Op + PQ + o, Op + PQ + o8),
+                              frag_tr8(Op + 2 * PQ + o, Op + 2 * PQ + o8),
                               __builtin_bit_cast(bf16x8, ph), __builtin_bit_cast(bf16x8, pm),
                               __builtin_bit_cast(bf16x8, pl), dvacc[db]);
-          dkacc[db] = mfma_x6(frag_tr8(Qp + o), frag_tr8(Qp + PQ + o), frag_tr8(Qp + 2 * PQ + o),
+          dkacc[db] = mfma_x6(frag_tr8(Qp + o, Qp + o8), frag_tr8(Qp + PQ + o, Qp + PQ + o8),
+                              frag_tr8(Qp + 2 * PQ + o, Qp + 2 * PQ + o8),
                               __builtin_bit_cast(bf16x8, sh), __builtin_bit_cast(bf16x8, sm),
                               __builtin_bit_cast(bf16x8, sl), dkacc[db]);
         }

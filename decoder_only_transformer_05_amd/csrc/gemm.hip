@@ -437,13 +437,17 @@ GPT2_DEVICE_INLINE f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 acc) {
 // chunk c (8 k) of row r at chunk c ^ ((r >> 3) & 1), so the 16-byte fragment reads of 32
 // consecutive rows cover all banks; an operand stored (K, rows) as [k][row], chunk c (8 rows)
 // of k-row k at chunk c ^ rswz<R>(k % 4), read with transposing reads, whose four k-rows
-// then fall on disjoint banks: with R = 256 (512-byte k-rows) the XOR moves them by 0, 96,
-// 192 and 160 bytes, with R = 192 (384-byte k-rows, every other one 128 bytes on) by 0, 0,
-// 32 and 32 (the XOR stays inside the row's 24 chunks).
+// then fall on disjoint banks. gfx950's LDS has 64 four-byte banks and serves a transposing
+// read 32 lanes at a time: four k-rows of 64 bytes each. With R = 256 (512-byte k-rows) the
+// XOR moves the four by 0, 96, 192 and 160 bytes; with R = 192 (384-byte k-rows, every other
+// one 128 bytes on) by 0, 32, 64 and 96, so the two k-rows of each parity differ by 64
+// bytes (the XOR stays inside the row's 24 chunks). The earlier 0, 0, 32, 32 was
+// conflict-free for 16 lanes at a time but not for 32 (SQ_LDS_BANK_CONFLICT counted 0.66
+// conflict cycles per LDS cycle in the grad-input GEMMs).
 template <int R>
 GPT2_DEVICE_INLINE int rswz(int j) {
   static_assert(R == 256 || R == 192, "k-row length");
-  return R == 256 ? (0xAC60 >> (4 * j)) & 15 : (0x2200 >> (4 * j)) & 15;
+  return R == 256 ? (0xAC60 >> (4 * j)) & 15 : (0x6420 >> (4 * j)) & 15;
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
