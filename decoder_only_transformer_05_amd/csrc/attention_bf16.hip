@@ -342,6 +342,25 @@ GPT2_DEVICE_INLINE void load8f(const float* base, long long ld, int t, int d, in
   }
 }
 
+// The same load with the zeroing left to the caller: returns whether row t, columns d..d+7
+// hold values (else the caller replaces x, y by zeros when it uses them). Staging code
+// applies it when it stores, so the loads of the next tile stay in flight meanwhile (a
+// select right after the load would make the compiler wait for them there).
+GPT2_DEVICE_INLINE bool load8f_raw(const float* base, long long ld, int t, int d, int T, int hs,
+                                   f32x4& x, f32x4& y) {
+  const int tc = min(t, T - 1), dc = min(d, hs - 8);
+  const float* p = base + (long long)tc * ld + dc;
+  x = *reinterpret_cast<const f32x4*>(p);
+  y = *reinterpret_cast<const f32x4*>(p + 4);
+  return t < T && d < hs;
+}
+GPT2_DEVICE_INLINE void zero_unless(bool ok, f32x4& x, f32x4& y) {
+  if (!ok) {
+    x = f32x4{0.f, 0.f, 0.f, 0.f};
+    y = x;
+  }
+}
+
 // Natural tile of fp32 rows -> three bf16 planes S[p][row][d] (HSP columns each, loff
 // layout), staged by NT threads
 template <int HSP, int NT>
@@ -349,18 +368,22 @@ struct RowsTileX6 {
   static constexpr int CPR = HSP / 8, NI = TILE * CPR / NT;
   static_assert(NI * NT == TILE * CPR, "whole chunks per thread");
   f32x4 v[NI][2];
+  uint32_t ok;  // bit i: chunk i holds values (else it is stored as zeros)
   __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
                                        int hs, int tid) {
+    ok = 0;
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int f = tid + NT * i;
-      load8f(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs, v[i][0], v[i][1]);
+      ok |= (uint32_t)load8f_raw(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs, v[i][0],
+                                 v[i][1]) << i;
     }
   }
-  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+  __device__ __forceinline__ void store(bf16_t* S, int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int f = tid + NT * i;
+      zero_unless((ok >> i) & 1, v[i][0], v[i][1]);
       u32x4 h, m, l;
       split8(v[i][0], v[i][1], h, m, l);
       const int o = loff<HSP>(f / CPR, f % CPR);
@@ -386,18 +409,22 @@ struct ColsTileX6 {
     return KPOS ? (j & ~3) | ((j & 1) << 1) | ((j >> 1) & 1) : j;
   }
   f32x4 v[NI][4][2];
+  uint32_t ok;  // bit 4 i + j: row j of block i holds values (else it is stored as zeros)
   __device__ __forceinline__ void load(const float* base, long long ld, int row0, int T,
                                        int hs, int tid) {
+    ok = 0;
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int b = tid + NT * i;
       if (BLOCKS % NT && b >= BLOCKS) break;
       const int dg = b % DG, rq = run(b / DG);
 #pragma unroll
-      for (int j = 0; j < 4; j++) load8f(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs, v[i][j][0], v[i][j][1]);
+      for (int j = 0; j < 4; j++)
+        ok |= (uint32_t)load8f_raw(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs, v[i][j][0],
+                                   v[i][j][1]) << (4 * i + j);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* S, int tid) const {
+  __device__ __forceinline__ void store(bf16_t* S, int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int b = tid + NT * i;
@@ -406,7 +433,10 @@ struct ColsTileX6 {
       const int p = KPOS ? kpos(4 * rq) : 4 * rq;
       u32x4 x[3][4];  // [plane][row]
 #pragma unroll
-      for (int j = 0; j < 4; j++) split8(v[i][j][0], v[i][j][1], x[0][j], x[1][j], x[2][j]);
+      for (int j = 0; j < 4; j++) {
+        zero_unless((ok >> (4 * i + j)) & 1, v[i][j][0], v[i][j][1]);
+        split8(v[i][j][0], v[i][j][1], x[0][j], x[1][j], x[2][j]);
+      }
 #pragma unroll
       for (int pl = 0; pl < 3; pl++)
 #pragma unroll
