@@ -745,48 +745,117 @@ __device__ __forceinline__ void gemm_x6s_body(const Args& g) {
   }
 
   float* C = g.C + (long long)z * g.c_zstride;
-  // GELU: the pre-activation and the activation are written in two passes over the tile
-  constexpr int EPI1 = EPI == EPI_GELU ? EPI_STORE : EPI;
+  // Epilogue. On gfx9 the vector-memory counter covers stores as well as loads, so a load
+  // waited for between stores also waits for every store issued before it. The bias of the
+  // thread's columns is therefore added before any store, and the operand rows an epilogue
+  // reads (residual, GELU pre-activation, or C itself) are loaded for the next 32-row block
+  // before the current block is stored. The arithmetic is that of epilogue4, in the same
+  // order.
+  constexpr bool HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr bool READS = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_ACCUM;
+  const bool vec = (g.ldc & 3) == 0;
+  auto col = [&](int tn, int q) { return n0 + wn0 + 32 * tn + 8 * q + 4 * h; };
+  auto row = [&](int tm) { return m0 + wm0 + 32 * tm + r; };
+  // the bias of each column, added into the accumulators before anything is stored
+  if (HAS_BIAS && g.bias) {
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = col(tn, q);
+        f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+        if (n + 3 < g.N) bv = *reinterpret_cast<const f32x4*>(g.bias + n);
+        else
+          for (int j = 0; j < 4; j++)
+            if (n + j < g.N) bv[j] = g.bias[n + j];
+#pragma unroll
+        for (int tm = 0; tm < TM; tm++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) acc[tm][tn][4 * q + j] += bv[j];
+      }
+  }
+  const float* rsrc = EPI == EPI_ACCUM ? C : g.R;
+  f32x4 rv[TN][4];  // operand values of one row block
+  auto load_rows = [&](int tm) {
+    const int m = row(tm);
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = col(tn, q);
+        rv[tn][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m >= g.M || n >= g.N) continue;
+        const long long off = (long long)m * g.ldc + n;
+        if (vec && n + 3 < g.N) rv[tn][q] = *reinterpret_cast<const f32x4*>(rsrc + off);
+        else
+          for (int j = 0; j < 4; j++)
+            if (n + j < g.N) rv[tn][q][j] = rsrc[off + j];
+      }
+  };
+  // per row block: the values are combined into the accumulators, then the next block's
+  // operand loads are issued, then this block's stores (so a later wait for those loads
+  // never waits for these stores)
+  if (READS) load_rows(0);
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
-    const int m = m0 + wm0 + 32 * tm + r;
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        f32x4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                   acc[tm][tn][4 * q + 3]};
+        if (READS) {
+          if (EPI == EPI_GELU_BWD) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) v[j] *= gelu_bwd(rv[tn][q][j]);
+          } else {
+            v += rv[tn][q];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[tm][tn][4 * q + j] = v[j];
+      }
+    if (READS && tm + 1 < TM) load_rows(tm + 1);
+    const int m = row(tm);
     if (m >= g.M) continue;
 #pragma unroll
     for (int tn = 0; tn < TN; tn++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
+        const int n = col(tn, q);
         if (n >= g.N) continue;
-        epilogue4<EPI1>(g, C, m, n,
-                        f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
-                              acc[tm][tn][4 * q + 3]});
+        const f32x4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                         acc[tm][tn][4 * q + 3]};
+        const long long off = (long long)m * g.ldc + n;
+        if (vec && n + 3 < g.N) *reinterpret_cast<f32x4*>(C + off) = v;
+        else
+          for (int j = 0; j < 4; j++)
+            if (n + j < g.N) C[off + j] = v[j];
       }
   }
+  // GELU: the activation of the (biased) pre-activation now in acc, written in a second pass
+  // over the tile (interleaved with the pre-activation, the two streams of partial lines had
+  // cost extra write traffic)
   if (EPI == EPI_GELU) {
 #pragma unroll
     for (int tm = 0; tm < TM; tm++) {
-      const int m = m0 + wm0 + 32 * tm + r;
+      const int m = row(tm);
       if (m >= g.M) continue;
 #pragma unroll
       for (int tn = 0; tn < TN; tn++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
+          const int n = col(tn, q);
           if (n >= g.N) continue;
+          const f32x4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                           acc[tm][tn][4 * q + 3]};
           const long long off = (long long)m * g.ldc + n;
-          const int cnt = min(4, g.N - n);
-          f32x4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
-                     acc[tm][tn][4 * q + 3]};
-          if (g.bias) {
-            if (cnt == 4) v += *reinterpret_cast<const f32x4*>(g.bias + n);
-            else
-              for (int j = 0; j < cnt; j++) v[j] += g.bias[n + j];
-          }
-          if (cnt == 4 && (g.ldc & 3) == 0)
+          if (vec && n + 3 < g.N)
             *reinterpret_cast<f32x4*>(g.C2 + off) =
                 f32x4{gelu_fwd(v[0]), gelu_fwd(v[1]), gelu_fwd(v[2]), gelu_fwd(v[3])};
           else
-            for (int j = 0; j < cnt; j++) g.C2[off + j] = gelu_fwd(v[j]);
+            for (int j = 0; j < 4; j++)
+              if (n + j < g.N) g.C2[off + j] = gelu_fwd(v[j]);
         }
     }
   }
