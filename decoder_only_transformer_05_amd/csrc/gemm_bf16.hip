@@ -238,6 +238,41 @@ __device__ __forceinline__ void epilogue4(const Args<TS>& g, void* Cv, int m, in
   }
 }
 
+// epilogue4 with the bias already in v and the values the epilogue reads (residual, GELU
+// pre-activation, or the fp32 C to accumulate into) passed in as r
+template <typename TS, int EPI, bool CF32>
+__device__ __forceinline__ void epilogue4_pre(const Args<TS>& g, void* Cv, int m, int n, f32x4 v,
+                                              f32x4 r) {
+  const long long off = (long long)m * g.ldc + n;
+  const int cnt = min(4, g.N - n);
+  if (EPI == EPI_RESID) v += r;
+  if (EPI == EPI_GELU_BWD)
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] *= gelu_bwd(r[j]);
+  if (CF32) {
+    float* C = static_cast<float*>(Cv);
+    if (EPI == EPI_ACCUM) v += r;
+    if (cnt == 4) {
+      *reinterpret_cast<f32x4*>(C + off) = v;
+    } else {
+      for (int j = 0; j < cnt; j++) C[off + j] = v[j];
+    }
+  } else {
+    TS* C = static_cast<TS*>(Cv);
+    if (cnt == 4) {
+      st4(C + off, v);
+      if (EPI == EPI_GELU)
+        st4(g.C2 + off, f32x4{gelu_fwd(v[0]), gelu_fwd(v[1]), gelu_fwd(v[2]),
+                                       gelu_fwd(v[3])});
+    } else {
+      for (int j = 0; j < cnt; j++) {
+        st1(C + off + j, v[j]);
+        if (EPI == EPI_GELU) st1(g.C2 + off + j, gelu_fwd(v[j]));
+      }
+    }
+  }
+}
+
 template <typename TS, class CFG, bool AT, bool BT, bool CF32, int EPI>
 __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm16_kernel(Args<TS> g) {
   constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, WM = CFG::WM, WN = CFG::WN;
@@ -419,20 +454,78 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm16_kernel(Args<TS> g) {
 
   void* C = CF32 ? static_cast<void*>(static_cast<float*>(g.C) + (long long)z * g.c_zstride)
                  : g.C;
-  // acc[tm][tn][4q + j]: row m = m0 + wm0 + 32 tm + r, column n = n0 + wn0 + 32 tn + 8q + 4h + j
+  // acc[tm][tn][4q + j]: row m = m0 + wm0 + 32 tm + r, column n = n0 + wn0 + 32 tn + 8q + 4h + j.
+  // One vector-memory counter covers loads and stores, so a load waited for between stores
+  // also waits for every store issued before it: the bias is added into the accumulators
+  // before anything is stored, and the rows an epilogue reads (residual, GELU pre-activation,
+  // or the fp32 C it accumulates into) are loaded for the next 32-row block before the
+  // current block is stored. epilogue4 then runs with the bias already applied and the row
+  // values passed in; the arithmetic and its order are unchanged.
+  constexpr bool HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr bool READS = EPI == EPI_RESID || EPI == EPI_GELU_BWD || (CF32 && EPI == EPI_ACCUM);
+  auto col = [&](int tn, int q) { return n0 + wn0 + 32 * tn + 8 * q + 4 * h; };
+  if (HAS_BIAS && g.bias) {
+#pragma unroll
+    for (int tn = 0; tn < WN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = col(tn, q);
+        f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+        if (n + 3 < g.N) bv = *reinterpret_cast<const f32x4*>(g.bias + n);
+        else
+          for (int j = 0; j < 4; j++)
+            if (n + j < g.N) bv[j] = g.bias[n + j];
+#pragma unroll
+        for (int tm = 0; tm < WM; tm++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) acc[tm][tn][4 * q + j] += bv[j];
+      }
+  }
+  f32x4 rv[WN][4];
+  auto load_rows = [&](int tm) {
+    const int m = m0 + wm0 + 32 * tm + r;
+#pragma unroll
+    for (int tn = 0; tn < WN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = col(tn, q);
+        rv[tn][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m >= g.M || n >= g.N) continue;
+        const long long off = (long long)m * g.ldc + n;
+        const int cnt = min(4, g.N - n);
+        if (EPI == EPI_ACCUM) {
+          const float* Cf = static_cast<const float*>(C);
+          if (cnt == 4) rv[tn][q] = *reinterpret_cast<const f32x4*>(Cf + off);
+          else
+            for (int j = 0; j < cnt; j++) rv[tn][q][j] = Cf[off + j];
+        } else {
+          if (cnt == 4) rv[tn][q] = ld4(g.R + off);
+          else
+            for (int j = 0; j < cnt; j++) rv[tn][q][j] = ld1(g.R + off + j);
+        }
+      }
+  };
+  if (READS) load_rows(0);
 #pragma unroll
   for (int tm = 0; tm < WM; tm++) {
     const int m = m0 + wm0 + 32 * tm + r;
+    f32x4 rcur[WN][4];
+#pragma unroll
+    for (int tn = 0; tn < WN; tn++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) rcur[tn][q] = rv[tn][q];
+    if (READS && tm + 1 < WM) load_rows(tm + 1);
     if (m >= g.M) continue;
 #pragma unroll
     for (int tn = 0; tn < WN; tn++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int n = n0 + wn0 + 32 * tn + 8 * q + 4 * h;
+        const int n = col(tn, q);
         if (n >= g.N) continue;
-        epilogue4<TS, EPI, CF32>(g, C, m, n,
-                             f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1],
-                                   acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]});
+        epilogue4_pre<TS, EPI, CF32>(g, C, m, n,
+                                     f32x4{acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1],
+                                           acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]},
+                                     rcur[tn][q]);
       }
   }
 }
