@@ -78,6 +78,17 @@ GPT2_DEVICE_INLINE u32x4 load8(const P* base, long long ld, int t, int d, int T,
   const u32x4 x = *reinterpret_cast<const u32x4*>(base + (long long)tc * ld + dc);
   return (t < T && d < hs) ? x : u32x4{0u, 0u, 0u, 0u};
 }
+// The same load with the zeroing left to the caller (returns whether the values are real):
+// the tile structs below apply it when they store, so the loads of the next tile stay in
+// flight until then (a select right after the load makes the compiler wait for it there).
+template <typename P>
+GPT2_DEVICE_INLINE bool load8_raw(const P* base, long long ld, int t, int d, int T, int hs,
+                                  u32x4& x) {
+  static_assert(sizeof(P) == 2, "16-bit storage");
+  const int tc = min(t, T - 1), dc = min(d, hs - 8);
+  x = *reinterpret_cast<const u32x4*>(base + (long long)tc * ld + dc);
+  return t < T && d < hs;
+}
 
 // Natural tile: rows row0 .. row0+63 of the tensor -> S[row][d] (HSP columns). load()
 // fills registers, store() writes them, so a tile can be fetched ahead of its use.
@@ -85,20 +96,23 @@ template <int HSP>
 struct RowsTile {
   static constexpr int CPR = HSP / 8, NI = TILE * CPR / NTHR;
   u32x4 v[NI];
+  uint32_t ok;  // bit i: chunk i holds values (else it is stored as zeros)
   template <typename P>
   __device__ __forceinline__ void load(const P* base, long long ld, int row0, int T, int hs,
                                        int tid) {
+    ok = 0;
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int f = tid + NTHR * i;
-      v[i] = load8(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs);
+      ok |= (uint32_t)load8_raw(base, ld, row0 + f / CPR, 8 * (f % CPR), T, hs, v[i]) << i;
     }
   }
   __device__ __forceinline__ void store(uint16_t* S, int tid) const {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int f = tid + NTHR * i;
-      *reinterpret_cast<u32x4*>(S + loff<HSP>(f / CPR, f % CPR)) = v[i];
+      *reinterpret_cast<u32x4*>(S + loff<HSP>(f / CPR, f % CPR)) =
+          (ok >> i) & 1 ? v[i] : u32x4{0u, 0u, 0u, 0u};
     }
   }
 };
@@ -111,23 +125,30 @@ struct ColsTile {
   static constexpr int BLOCKS = (TILE / 4) * DG;  // 4x8 blocks in the tile
   static constexpr int NI = (BLOCKS + NTHR - 1) / NTHR;
   u32x4 x[NI][4];
+  uint32_t ok;  // bit 4 i + j: row j of block i holds values (else it is stored as zeros)
   template <typename P>
   __device__ __forceinline__ void load(const P* base, long long ld, int row0, int T, int hs,
                                        int tid) {
+    ok = 0;
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int b = tid + NTHR * i;
       if (BLOCKS % NTHR && b >= BLOCKS) break;
       const int dg = b % DG, rq = b / DG;  // columns 8dg .. +7, rows 4rq .. +3
 #pragma unroll
-      for (int j = 0; j < 4; j++) x[i][j] = load8(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs);
+      for (int j = 0; j < 4; j++)
+        ok |= (uint32_t)load8_raw(base, ld, row0 + 4 * rq + j, 8 * dg, T, hs, x[i][j])
+              << (4 * i + j);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* S, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* S, int tid) {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int b = tid + NTHR * i;
       if (BLOCKS % NTHR && b >= BLOCKS) break;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (!((ok >> (4 * i + j)) & 1)) x[i][j] = u32x4{0u, 0u, 0u, 0u};
       const int dg = b % DG, rq = b / DG;
       const int p = kpos(4 * rq);  // a multiple of 4: the 4 rows stay consecutive
 #pragma unroll
