@@ -53,6 +53,9 @@ typedef TileCfg<128, 128, 32, 2, 2, 3, 3, 8> Tile128;
 // contiguous), 2 stages of 64 KB, one workgroup per CU: half the operand bytes per flop of
 // the 128 x 128 tile
 typedef TileCfg<256, 256, 64, 2, 4, 2, 1, 8> Tile256;
+// 256 x 192: 8 waves of 64 x 96, slabs of 64 k, 2 stages of 56 KB, one workgroup per CU:
+// 8192 x 1280 outputs in 224 tiles (one round, no split of K) where 256 x 256 leaves 160
+typedef TileCfg<256, 192, 64, 4, 2, 2, 1, 8> Tile192;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // 8 x 16 bits of either format
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -92,13 +95,22 @@ struct Args {
 // the 16-byte chunk c of row r holds the row's chunk c ^ kswz(r), which spreads the 16-byte
 // fragment reads (consecutive rows, one chunk) over all banks. An operand stored
 // (K, rows) keeps that layout in LDS, [k][row] (R elements per k); chunk c of k-row k holds
-// chunk c ^ rswz(k % 4), so the four k-rows that one transposing read touches fall on
-// different banks.
+// chunk c ^ rswz<R>(k % 4), so the four k-rows that one transposing read touches fall on
+// different banks. A transposing read serves 32 lanes at a time: four k-rows of 64 bytes
+// each, which must cover disjoint banks (64 banks of 4 bytes). k-rows of 256 or 512 bytes
+// start on the same bank: the XOR moves the four by 0, 96, 192 and 160 bytes. k-rows of 384
+// bytes (R = 192) start 128 bytes apart in turn: the XOR moves them by 0, 32, 64 and 96
+// bytes, so the two k-rows of each parity differ by 64 bytes, and every chunk stays inside
+// its row's 24.
 template <int BK>
 GPT2_DEVICE_INLINE int kswz(int row) {
   return BK == 32 ? ((row >> 1) ^ (row >> 3)) & 3 : (row ^ (row >> 3)) & 7;
 }
-GPT2_DEVICE_INLINE int rswz(int j) { return (0xAC60 >> (4 * j)) & 15; }  // 0, 6, 12, 10
+template <int R>
+GPT2_DEVICE_INLINE int rswz(int j) {
+  static_assert(R == 128 || R == 256 || R == 192, "k-row length");
+  return R == 192 ? (0x6420 >> (4 * j)) & 15 : (0xAC60 >> (4 * j)) & 15;
+}
 
 // word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family GPUs
 constexpr int kBufferFlags = 0x00020000;
@@ -136,7 +148,7 @@ struct SlabCopy {
         voff[j] = (uint32_t)(row * ld + 8 * (p ^ kswz<BK>(row))) * 2u;
       } else {
         const int k = b / (2 * R), p = (b % (2 * R)) >> 4;
-        voff[j] = (uint32_t)(k * ld + 8 * (p ^ rswz(k & 3))) * 2u;
+        voff[j] = (uint32_t)(k * ld + 8 * (p ^ rswz<R>(k & 3))) * 2u;
       }
     }
   }
@@ -339,7 +351,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm16_kernel(Args<TS> g) {
     if (!AT) rda[q] = (wm0 + 32 * q + r) * 2 * BK + 16 * (h ^ kswz<BK>(wm0 + 32 * q + r));
     else {
       const int n = wm0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
-      rda[q] = (8 * h + (i16 >> 2)) * 2 * BM + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
+      rda[q] = (8 * h + (i16 >> 2)) * 2 * BM + 16 * ((n >> 3) ^ rswz<BM>(i16 >> 2)) + 8 * (i16 & 1);
     }
   }
 #pragma unroll
@@ -347,7 +359,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm16_kernel(Args<TS> g) {
     if (!BT) rdb[q] = (wn0 + 32 * q + r) * 2 * BK + 16 * (h ^ kswz<BK>(wn0 + 32 * q + r));
     else {
       const int n = wn0 + 32 * q + 16 * (g16 & 1) + 4 * (i16 & 3);
-      rdb[q] = (8 * h + (i16 >> 2)) * 2 * BN + 16 * ((n >> 3) ^ rswz(i16 >> 2)) + 8 * (i16 & 1);
+      rdb[q] = (8 * h + (i16 >> 2)) * 2 * BN + 16 * ((n >> 3) ^ rswz<BN>(i16 >> 2)) + 8 * (i16 & 1);
     }
   }
 
@@ -399,7 +411,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm16_kernel(Args<TS> g) {
       for (int j = 0; j < BK / KG; j++) {
         const int k = tid / CHUNKS + KG * j, mc = tid % CHUNKS;
         const u32x4 x = *reinterpret_cast<const u32x4*>(pa + k * 2 * BM +
-                                                         16 * (mc ^ rswz(k & 3)));
+                                                         16 * (mc ^ rswz<BM>(k & 3)));
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           csum[2 * q] += Half16<TS>::lo(x[q]);
@@ -605,7 +617,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 // Tile shape and K splits from a wave-quantisation cost model: each shape's workgroups run
 // in rounds of OCC per CU (256 CUs) at that shape's measured fraction of the bf16 MFMA peak;
 // split partials and their reduction move at 5 TB/s.
-enum TileKind { T128 = 1, T256 = 2 };
+enum TileKind { T128 = 1, T256 = 2, T192 = 3 };
 struct Plan {
   int tile;    // TileKind
   int splits;
@@ -616,21 +628,23 @@ struct TileInfo {
 };
 TileInfo tile_info(int t) {
   if (t == T128) return {Tile128::BM, Tile128::BN, Tile128::BK, Tile128::OCC, 0.26};
+  if (t == T192) return {Tile192::BM, Tile192::BN, Tile192::BK, Tile192::OCC, 0.33};
   return {Tile256::BM, Tile256::BN, Tile256::BK, Tile256::OCC, 0.34};
 }
-// GPT2_GEMM_BF16_TILE=1 (128 x 128) or 2 (256 x 256) in the environment pins the tile shape
-// (tests of both kernels, measurements); anything else leaves the choice to the model
+// GPT2_GEMM_BF16_TILE=1 (128 x 128), 2 (256 x 256) or 3 (256 x 192) in the environment pins
+// the tile shape (tests of every kernel, measurements); anything else leaves the choice to
+// the model
 int forced_tile() {
   const char* e = getenv("GPT2_GEMM_BF16_TILE");
   const int v = e ? atoi(e) : 0;
-  return v == T128 || v == T256 ? v : 0;
+  return v == T128 || v == T256 || v == T192 ? v : 0;
 }
 template <typename TS>
 Plan choose_plan(const GemmHalf<TS>& g) {
   const double mn = (double)g.M * g.N;
   Plan best_p{T128, 1};
   double best = 1e30;
-  for (int t = T128; t <= T256; t++) {
+  for (int t = T128; t <= T192; t++) {
     if (forced_tile() && t != forced_tile()) continue;
     const TileInfo ti = tile_info(t);
     const int kt = ceil_div(g.K, ti.bk);
@@ -723,6 +737,7 @@ int gemm16(const GemmHalf<TS>& g, float* workspace, size_t ws_floats, hipStream_
   auto run = [&](const Args<TS>& x, int epi, bool f32out, int grid) {
     const bool at = g.a_trans, bt = g.b_trans;
     if (plan.tile == T128) launch<Tile128>(x, at, bt, epi, f32out, dim3(grid), stream);
+    else if (plan.tile == T192) launch<Tile192>(x, at, bt, epi, f32out, dim3(grid), stream);
     else launch<Tile256>(x, at, bt, epi, f32out, dim3(grid), stream);
   };
 

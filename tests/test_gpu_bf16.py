@@ -66,6 +66,8 @@ CASES = [
     (136, 72, 130, 1, 0),
     # more tiles than CUs (both tile shapes), with ragged edges
     (4100, 4104, 136, 0, 0), (4100, 4104, 200, 0, 1), (4104, 4100, 72, 1, 1),
+    # 1280 output columns (the 774M model's width): seven 192-wide tiles, the last one ragged
+    (1000, 1280, 520, 0, 0), (1000, 1280, 520, 0, 1),
 ]
 
 
@@ -80,13 +82,13 @@ def stored(op, trans, ld_pad=0):
     return buf, ld
 
 
-@pytest.mark.parametrize("tile", ["1", "2"])
+@pytest.mark.parametrize("tile", ["1", "2", "3"])
 @pytest.mark.parametrize("M,N,K,at,bt", CASES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
 def test_gemm_bf16(M, N, K, at, bt, epi, tile, monkeypatch):
-    """Both tile shapes of the bf16 GEMM: 128 x 128 tiles with 32-deep K slabs and 256 x 256
-    tiles with 64-deep slabs (the library picks one per shape; the environment variable pins
-    it)."""
+    """Every tile shape of the bf16 GEMM: 128 x 128 tiles with 32-deep K slabs, 256 x 256 and
+    256 x 192 tiles with 64-deep slabs (the library picks one per shape; the environment
+    variable pins it)."""
     monkeypatch.setenv("GPT2_GEMM_BF16_TILE", tile)
     if K > 1000 and epi in (1, 2):
         pytest.skip("long-K shapes run with the epilogues the step uses with them")
