@@ -56,6 +56,17 @@ typedef TileCfg<256, 256, 64, 2, 4, 2, 1, 8> Tile256;
 // 256 x 192: 8 waves of 64 x 96, slabs of 64 k, 2 stages of 56 KB, one workgroup per CU:
 // 8192 x 1280 outputs in 224 tiles (one round, no split of K) where 256 x 256 leaves 160
 typedef TileCfg<256, 192, 64, 4, 2, 2, 1, 8> Tile192;
+// 256 x 320: 8 waves of 64 x 160, slabs of 64 k, 2 stages of 72 KB, one workgroup per CU:
+// 8192 x 5120 outputs in 512 tiles (two whole rounds) where 256 x 256 needs 2.5
+typedef TileCfg<256, 320, 64, 4, 2, 2, 1, 8> Tile320;
+// Epilogues that read a tensor (residual, GELU pre-activation, the fp32 C they accumulate
+// into) load the next row block's values while the current one is stored. With the 10
+// accumulator blocks of the 256 x 320 tile those values do not fit beside the accumulators
+// (the kernels spill hundreds of registers), so that tile runs only the epilogues that read
+// nothing; the planner gives it no other.
+template <class CFG>
+constexpr bool kReadingEpilogues = CFG::WM * CFG::WN <= 8;
+bool epi_reads(int epi) { return epi == EPI_RESID || epi == EPI_GELU_BWD || epi == EPI_ACCUM; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // 8 x 16 bits of either format
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -108,8 +119,8 @@ GPT2_DEVICE_INLINE int kswz(int row) {
 }
 template <int R>
 GPT2_DEVICE_INLINE int rswz(int j) {
-  static_assert(R == 128 || R == 256 || R == 192, "k-row length");
-  return R == 192 ? (0x6420 >> (4 * j)) & 15 : (0xAC60 >> (4 * j)) & 15;
+  static_assert(R == 128 || R == 256 || R == 192 || R == 320, "k-row length");
+  return R == 192 || R == 320 ? (0x6420 >> (4 * j)) & 15 : (0xAC60 >> (4 * j)) & 15;
 }
 
 // word 3 of a raw (untyped, unswizzled) buffer resource on gfx9-family GPUs
@@ -592,9 +603,18 @@ void launch_epi(const Args<TS>& a, int epi, dim3 grid, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: gemm16_kernel<TS, CFG, AT, BT, CF32, EPI_STORE><<<grid, NT, 0, s>>>(a); break;
     case EPI_GELU: gemm16_kernel<TS, CFG, AT, BT, false, EPI_GELU><<<grid, NT, 0, s>>>(a); break;
-    case EPI_RESID: gemm16_kernel<TS, CFG, AT, BT, false, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
-    case EPI_ACCUM: gemm16_kernel<TS, CFG, AT, BT, true, EPI_ACCUM><<<grid, NT, 0, s>>>(a); break;
-    case EPI_GELU_BWD: gemm16_kernel<TS, CFG, AT, BT, false, EPI_GELU_BWD><<<grid, NT, 0, s>>>(a); break;
+    case EPI_RESID:
+      if constexpr (kReadingEpilogues<CFG>)
+        gemm16_kernel<TS, CFG, AT, BT, false, EPI_RESID><<<grid, NT, 0, s>>>(a);
+      break;
+    case EPI_ACCUM:
+      if constexpr (kReadingEpilogues<CFG>)
+        gemm16_kernel<TS, CFG, AT, BT, true, EPI_ACCUM><<<grid, NT, 0, s>>>(a);
+      break;
+    case EPI_GELU_BWD:
+      if constexpr (kReadingEpilogues<CFG>)
+        gemm16_kernel<TS, CFG, AT, BT, false, EPI_GELU_BWD><<<grid, NT, 0, s>>>(a);
+      break;
   }
 }
 
@@ -617,7 +637,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 // Tile shape and K splits from a wave-quantisation cost model: each shape's workgroups run
 // in rounds of OCC per CU (256 CUs) at that shape's measured fraction of the bf16 MFMA peak;
 // split partials and their reduction move at 5 TB/s.
-enum TileKind { T128 = 1, T256 = 2, T192 = 3 };
+enum TileKind { T128 = 1, T256 = 2, T192 = 3, T320 = 4 };
 struct Plan {
   int tile;    // TileKind
   int splits;
@@ -629,27 +649,30 @@ struct TileInfo {
 TileInfo tile_info(int t) {
   if (t == T128) return {Tile128::BM, Tile128::BN, Tile128::BK, Tile128::OCC, 0.26};
   if (t == T192) return {Tile192::BM, Tile192::BN, Tile192::BK, Tile192::OCC, 0.33};
+  if (t == T320) return {Tile320::BM, Tile320::BN, Tile320::BK, Tile320::OCC, 0.34};
   return {Tile256::BM, Tile256::BN, Tile256::BK, Tile256::OCC, 0.34};
 }
-// GPT2_GEMM_BF16_TILE=1 (128 x 128), 2 (256 x 256) or 3 (256 x 192) in the environment pins
-// the tile shape (tests of every kernel, measurements); anything else leaves the choice to
-// the model
+// GPT2_GEMM_BF16_TILE=1 (128 x 128), 2 (256 x 256), 3 (256 x 192) or 4 (256 x 320) in the
+// environment pins the tile shape (tests of every kernel, measurements; pinned to 256 x 320,
+// an epilogue that reads a tensor runs split or on the default 128 x 128 tile); anything
+// else leaves the choice to the model
 int forced_tile() {
   const char* e = getenv("GPT2_GEMM_BF16_TILE");
   const int v = e ? atoi(e) : 0;
-  return v == T128 || v == T256 || v == T192 ? v : 0;
+  return v >= T128 && v <= T320 ? v : 0;
 }
 template <typename TS>
 Plan choose_plan(const GemmHalf<TS>& g) {
   const double mn = (double)g.M * g.N;
   Plan best_p{T128, 1};
   double best = 1e30;
-  for (int t = T128; t <= T192; t++) {
+  for (int t = T128; t <= T320; t++) {
     if (forced_tile() && t != forced_tile()) continue;
     const TileInfo ti = tile_info(t);
     const int kt = ceil_div(g.K, ti.bk);
     const double tiles = (double)ceil_div(g.M, ti.bm) * ceil_div(g.N, ti.bn);
     for (int s = 1; s <= 16; s++) {
+      if (t == T320 && s == 1 && epi_reads(g.epi)) continue;  // (split launches store only)
       const int kper = ceil_div(kt, s);
       if (s > 1 && kper * ti.bk < 128) break;
       if (s > 1 && ceil_div(kt, kper) != s) continue;
@@ -738,6 +761,7 @@ int gemm16(const GemmHalf<TS>& g, float* workspace, size_t ws_floats, hipStream_
     const bool at = g.a_trans, bt = g.b_trans;
     if (plan.tile == T128) launch<Tile128>(x, at, bt, epi, f32out, dim3(grid), stream);
     else if (plan.tile == T192) launch<Tile192>(x, at, bt, epi, f32out, dim3(grid), stream);
+    else if (plan.tile == T320) launch<Tile320>(x, at, bt, epi, f32out, dim3(grid), stream);
     else launch<Tile256>(x, at, bt, epi, f32out, dim3(grid), stream);
   };
 

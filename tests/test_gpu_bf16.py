@@ -68,6 +68,8 @@ CASES = [
     (4100, 4104, 136, 0, 0), (4100, 4104, 200, 0, 1), (4104, 4100, 72, 1, 1),
     # 1280 output columns (the 774M model's width): seven 192-wide tiles, the last one ragged
     (1000, 1280, 520, 0, 0), (1000, 1280, 520, 0, 1),
+    # 5120 output columns (the 774M MLP width): sixteen 320-wide tiles
+    (600, 5120, 264, 0, 0), (600, 5120, 264, 0, 1),
 ]
 
 
@@ -82,13 +84,14 @@ def stored(op, trans, ld_pad=0):
     return buf, ld
 
 
-@pytest.mark.parametrize("tile", ["1", "2", "3"])
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K,at,bt", CASES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
 def test_gemm_bf16(M, N, K, at, bt, epi, tile, monkeypatch):
-    """Every tile shape of the bf16 GEMM: 128 x 128 tiles with 32-deep K slabs, 256 x 256 and
-    256 x 192 tiles with 64-deep slabs (the library picks one per shape; the environment
-    variable pins it)."""
+    """Every tile shape of the bf16 GEMM: 128 x 128 tiles with 32-deep K slabs, 256 x 256,
+    256 x 192 and 256 x 320 tiles with 64-deep slabs (the library picks one per shape; the
+    environment variable pins it; the 256 x 320 tile takes no epilogue that reads a tensor,
+    so pinned to it those epilogues run split or on 128 x 128 tiles)."""
     monkeypatch.setenv("GPT2_GEMM_BF16_TILE", tile)
     if K > 1000 and epi in (1, 2):
         pytest.skip("long-K shapes run with the epilogues the step uses with them")

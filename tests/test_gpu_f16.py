@@ -74,7 +74,7 @@ def stored(op, trans):
     return buf, ld
 
 
-@pytest.mark.parametrize("tile", ["1", "2", "3"])
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K,at,bt", CASES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
 def test_gemm_f16(M, N, K, at, bt, epi, tile, monkeypatch):
