@@ -155,8 +155,9 @@ int encoder_forward(bf16_t* out, const int32_t* tok, const float* wte, const flo
                     int T, int C, int V, int32_t* err_flag, hipStream_t stream);
 int encoder_forward(f16_t* out, const int32_t* tok, const float* wte, const float* wpe, int B,
                     int T, int C, int V, int32_t* err_flag, hipStream_t stream);
-// sorted-token scratch: encoder_sort_scratch_ints(B*T, V) ints
-size_t encoder_sort_scratch_ints(int BT, int V);
+// scratch of the embedding backward (sorted tokens, dwte partials):
+// encoder_sort_scratch_ints(B*T, V, C) 4-byte words, 16-byte aligned
+size_t encoder_sort_scratch_ints(int BT, int V, int C);
 int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok, int B,
                      int T, int C, int V, int32_t* scratch, hipStream_t stream);
 int layernorm_forward(float* out, float* mean, float* rstd, const float* x, const float* w,

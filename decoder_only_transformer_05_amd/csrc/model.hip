@@ -284,7 +284,7 @@ size_t carve_activations(gpt2_model* md, char* base, int B, int T) {
   md->tok = reinterpret_cast<int32_t*>(take(BT * sizeof(int32_t)));
   md->tgt = reinterpret_cast<int32_t*>(take(BT * sizeof(int32_t)));
   md->sort_scratch =
-      reinterpret_cast<int32_t*>(take(encoder_sort_scratch_ints((int)BT, md->V) * sizeof(int32_t)));
+      reinterpret_cast<int32_t*>(take(encoder_sort_scratch_ints((int)BT, md->V, (int)C) * sizeof(int32_t)));
   md->d_err = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
   return off;
 }
@@ -1089,7 +1089,7 @@ int gpt2_k_encoder_backward(float* dwte, float* dwpe, const float* dout, const i
     return fail(nullptr, GPT2_ERR_ARG, "bad argument");
   hipStream_t s = as_stream(stream);
   int32_t* scratch = nullptr;
-  if (hipMalloc(&scratch, encoder_sort_scratch_ints(B * T, V) * sizeof(int32_t)) != hipSuccess)
+  if (hipMalloc(&scratch, encoder_sort_scratch_ints(B * T, V, C) * sizeof(int32_t)) != hipSuccess)
     return fail(nullptr, GPT2_ERR_OOM, "scratch allocation failed");
   int rc = encoder_backward(dwte, dwpe, dout, tok, B, T, C, V, scratch, s);
   (void)hipStreamSynchronize(s);

@@ -153,23 +153,87 @@ __global__ __launch_bounds__(SORT_THREADS) void token_merge_kernel(
   sorted[dest] = c * SORT_THREADS + (key & 1023);
 }
 
-// One wave per sorted index j; the wave that starts a run of equal tokens adds the run's
-// rows (in ascending position order) to that token's dwte row.
-__global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, const float* __restrict__ dout,
+// dwte: positions sorted by (token, position) form one run per token. Runs are cut at every
+// multiple of WTE_CHUNK sorted indices, so no wave sums more than WTE_CHUNK rows however
+// skewed the tokens are (a frequent token of real text repeats hundreds of times in a
+// batch). One wave per sorted index j; the waves at a run start or at a chunk boundary
+// inside a run each sum their piece of rows in ascending position order. A piece that is a
+// whole run is added to the token's dwte row at once; the pieces of a run that crosses
+// chunk boundaries go to a partial buffer (per chunk: the piece that starts it, continuing
+// an earlier run, and the piece of the run that starts in it and goes on past its end),
+// and encoder_bwd_wte_span_kernel adds them up in chunk order. Fixed summation order, no
+// atomics: bitwise reproducible.
+constexpr int WTE_CHUNK = 32;
+__global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, float* __restrict__ part,
+                                       const float* __restrict__ dout,
                                        const int32_t* __restrict__ tok,
                                        const int32_t* __restrict__ sorted, int BT, int C,
                                        int V) {
   const int j = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (j >= BT) return;
-  const int v = clamp_tok(tok[sorted[j]], V);
-  if (j > 0 && clamp_tok(tok[sorted[j - 1]], V) == v) return;
-  float* dst = dwte + (long long)v * C;
+  if (j >= BT) return;  // wave-uniform
+  // lane l looks at sorted index j - 1 + l, l = 0 .. WTE_CHUNK + 1
+  const int k = j - 1 + lane;
+  const bool in = lane <= WTE_CHUNK + 1 && k >= 0 && k < BT;
+  const int pos = in ? sorted[k] : 0;
+  const int t = in ? clamp_tok(tok[pos], V) : -1;
+  const int v = __shfl(t, 1, 64);          // token at j
+  const bool head = __shfl(t, 0, 64) == v;  // the run began before j (lane 0 holds -1 if j = 0)
+  if (head && j % WTE_CHUNK != 0) return;   // neither a run start nor a chunk boundary
+  // the piece ends at the first index e > j holding another token, at BT, or at the next chunk
+  // boundary (always within lanes 2 .. WTE_CHUNK + 1)
+  const bool stop = lane >= 2 && lane <= WTE_CHUNK + 1 &&
+                    (k >= BT || t != v || k % WTE_CHUNK == 0);
+  const int le = __ffsll((unsigned long long)__ballot(stop)) - 1;
+  const int e = j - 1 + le;
+  const bool tail = e < BT && __shfl(t, le, 64) == v;  // the run goes on past the boundary e
+  const int nrow = e - j;
+  const int chunk = j / WTE_CHUNK;
+  float* dst = !head && !tail ? dwte + (long long)v * C
+                              : part + (2LL * chunk + (head ? 0 : 1)) * C;
   for (int c = 4 * lane; c < C; c += 256) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int k = j; k < BT && clamp_tok(tok[sorted[k]], V) == v; k++)
-      s += ld4(dout + (long long)sorted[k] * C + c);
-    st4(dst + c, ld4(dst + c) + s);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int r = 0; r < nrow; r++) {
+      const int p = __builtin_amdgcn_readlane(pos, r + 1);
+      acc += ld4(dout + (long long)p * C + c);
+    }
+    if (!head && !tail) st4(dst + c, ld4(dst + c) + acc);
+    else st4(dst + c, acc);
+  }
+}
+
+// One wave per chunk: if a run starts in the chunk and goes on past its end, add its piece
+// in this chunk and the leading pieces of the following chunks it covers, in that order, to
+// the token's dwte row.
+__global__ void encoder_bwd_wte_span_kernel(float* __restrict__ dwte,
+                                            const float* __restrict__ part,
+                                            const int32_t* __restrict__ tok,
+                                            const int32_t* __restrict__ sorted, int BT, int C,
+                                            int V) {
+  const int nch = (BT + WTE_CHUNK - 1) / WTE_CHUNK;
+  const int c = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (c >= nch) return;
+  const int jl = min(BT, (c + 1) * WTE_CHUNK) - 1;  // last index of the chunk
+  if (jl + 1 >= BT) return;
+  const int u = clamp_tok(tok[sorted[jl]], V);
+  if (clamp_tok(tok[sorted[jl + 1]], V) != u) return;                       // ends here
+  if (c > 0 && clamp_tok(tok[sorted[c * WTE_CHUNK - 1]], V) == u) return;   // began earlier
+  // last chunk of the run: the first chunk c2 > c whose next chunk does not start with u
+  int last = -1;
+  for (int base = c + 1; last < 0; base += 64) {
+    const int c2 = base + lane;
+    const int nx = (c2 + 1) * WTE_CHUNK;
+    const bool more = c2 < nch && nx < BT && clamp_tok(tok[sorted[nx]], V) == u;
+    const unsigned long long m = __ballot(c2 < nch && !more);
+    if (m) last = base + __ffsll(m) - 1;
+  }
+  float* dst = dwte + (long long)u * C;
+  for (int col = 4 * lane; col < C; col += 256) {
+    f32x4 acc = ld4(part + (2LL * c + 1) * C + col);
+    for (int c2 = c + 1; c2 <= last; c2++) acc += ld4(part + 2LL * c2 * C + col);
+    st4(dst + col, ld4(dst + col) + acc);
   }
 }
 
@@ -724,10 +788,11 @@ int encoder_forward(f16_t* out, const int32_t* tok, const float* wte, const floa
                            "encoder_fwd_f16_kernel");
 }
 
-size_t encoder_sort_scratch_ints(int BT, int V) {
+size_t encoder_sort_scratch_ints(int BT, int V, int C) {
   (void)V;
   const size_t padded = (size_t)(BT + SORT_THREADS - 1) / SORT_THREADS * SORT_THREADS;
-  return (size_t)BT + padded;
+  const size_t nch = (size_t)(BT + WTE_CHUNK - 1) / WTE_CHUNK;
+  return 2 * nch * (size_t)C + (size_t)BT + padded;
 }
 
 int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok, int B,
@@ -741,7 +806,11 @@ int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t*
     set_global_error("encoder_backward: vocabulary of %d tokens is too large", V);
     return -1;
   }
-  int32_t* sorted = scratch;
+  // scratch: dwte partials (2 per chunk of WTE_CHUNK sorted indices, C floats each), the
+  // sorted positions, the sort keys
+  const int nwch = (BT + WTE_CHUNK - 1) / WTE_CHUNK;
+  float* part = reinterpret_cast<float*>(scratch);
+  int32_t* sorted = scratch + 2LL * nwch * C;
   const int nchunks = (BT + SORT_THREADS - 1) / SORT_THREADS;
   int32_t* keys = sorted + BT;
   {
@@ -758,8 +827,15 @@ int encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t*
     ProfScope ps("token_merge_kernel", 0.0, 4.0 * 2.0 * BT, stream);
     token_merge_kernel<<<nchunks, SORT_THREADS, 0, stream>>>(sorted, keys, nchunks);
   }
-  ProfScope ps("encoder_bwd_wte_kernel", (double)BT * C, 4.0 * (3.0 * BT * C + 2.0 * BT), stream);
-  encoder_bwd_wte_kernel<<<(BT + 3) / 4, 256, 0, stream>>>(dwte, dout, tok, sorted, BT, C, V);
+  {
+    ProfScope ps("encoder_bwd_wte_kernel", (double)BT * C, 4.0 * (3.0 * BT * C + 2.0 * BT),
+                 stream);
+    encoder_bwd_wte_kernel<<<(BT + 3) / 4, 256, 0, stream>>>(dwte, part, dout, tok, sorted, BT,
+                                                            C, V);
+  }
+  ProfScope ps("encoder_bwd_wte_span_kernel", 0.0, 4.0 * 2.0 * nwch, stream);
+  encoder_bwd_wte_span_kernel<<<(nwch + 3) / 4, 256, 0, stream>>>(dwte, part, tok, sorted, BT, C,
+                                                                 V);
   GPT2_HIP_OK(hipGetLastError());
   return 0;
 }

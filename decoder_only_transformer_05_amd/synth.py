@@ -123,16 +123,37 @@ def tokens_uniform(seed: int, start: int, count: int, V: int) -> np.ndarray:
         return ((hi * np.uint64(V)) >> np.uint64(32)).astype(np.int32)
 
 
+_ZIPF_CDF: dict = {}
+
+
+def tokens_zipf(seed: int, start: int, count: int, V: int, exponent: float = 1.0) -> np.ndarray:
+    """int32 tokens in [0, V) with P(k) proportional to 1/(k+1)^exponent (Zipf's law, the
+    rank-frequency shape of word and sub-word counts in text; token k is the k-th most
+    frequent), by inverting the cumulative distribution at the stream's uniforms."""
+    key = (V, exponent)
+    if key not in _ZIPF_CDF:
+        w = 1.0 / np.arange(1, V + 1, dtype=np.float64) ** exponent
+        cdf = np.cumsum(w)
+        _ZIPF_CDF[key] = cdf / cdf[-1]
+    u = uniform01(seed, start, count)
+    return np.minimum(np.searchsorted(_ZIPF_CDF[key], u, side="right"), V - 1).astype(np.int32)
+
+
 def batch(seed: int, B: int, T: int, V: int, step: int = 0,
           mode: str = "stream") -> tuple[np.ndarray, np.ndarray]:
     """(inputs, targets), each int32 (B, T).
 
     mode "stream": the token stream advances by B*T per step and targets are the inputs
-    shifted by one; mode "independent": inputs and targets are separate uniform draws.
+    shifted by one; mode "independent": inputs and targets are separate uniform draws;
+    mode "zipf": as "stream" with Zipf-distributed tokens (exponent 1) in place of uniform
+    ones, the skew of real text (many repeats of the frequent tokens in every batch).
     """
     n = B * T
     if mode == "stream":
         s = tokens_uniform(seed, step * n, n + 1, V)
+        return s[:n].reshape(B, T).copy(), s[1:].reshape(B, T).copy()
+    if mode == "zipf":
+        s = tokens_zipf(seed, step * n, n + 1, V)
         return s[:n].reshape(B, T).copy(), s[1:].reshape(B, T).copy()
     if mode == "independent":
         s = tokens_uniform(seed, step * 2 * n, 2 * n, V)
@@ -158,8 +179,8 @@ class Workload:
     weight_decay: float = 0.0
 
 
-# The workloads: a tiny model, GPT-2 124M at two batch sizes, 350M, and 774M in bf16 and in
-# fp16.
+# The workloads: a tiny model, GPT-2 124M at two batch sizes (and on Zipf-distributed tokens),
+# 350M, and 774M in bf16 and in fp16.
 WORKLOADS = {
     "tiny": Workload("tiny L1 C16 H4 V27 B4 T16 fp32", ModelShape(1, 16, 4, 27, 16), 4, 16,
                      "fp32", False, "independent", seed=1337),
@@ -168,6 +189,10 @@ WORKLOADS = {
     "gpt2_124m_b16_t1024": Workload("gpt2-124M B16 T1024 fp32",
                                     ModelShape(12, 768, 12, 50257, 1024), 16, 1024, "fp32",
                                     True, "stream", seed=1339),
+    # the same step on Zipf-distributed tokens (the token skew of real text)
+    "gpt2_124m_b16_t1024_zipf": Workload("gpt2-124M B16 T1024 fp32, Zipf tokens",
+                                         ModelShape(12, 768, 12, 50257, 1024), 16, 1024, "fp32",
+                                         True, "zipf", seed=1339),
     "gpt2_350m_b8_t1024": Workload("gpt2-350M B8 T1024 fp32",
                                    ModelShape(24, 1024, 16, 50257, 1024), 8, 1024, "fp32",
                                    True, "stream", seed=1340),

@@ -267,8 +267,10 @@ int gpt2_k_encoder_forward(float* out, const int32_t* tok, const float* wte, con
                            int B, int T, int C, int V, int32_t* err_flag, void* stream);
 
 /* [llm.c] 1.2: dwte[tok[b,t]] += dout[b,t]; dwpe[t] += sum_b dout[b,t]. Deterministic:
- * rows of one token are summed in ascending (b,t) order. Tokens must be in [0,V) (others
- * count as token 0); V below 2^21 (ERR_ARG otherwise). */
+ * rows of one token are summed in ascending (b,t) order, in pieces cut at every multiple of
+ * 32 in the order of positions sorted by (token, position), the piece sums added in order
+ * and then to dwte. Tokens must be in [0,V) (others count as token 0); V below 2^21
+ * (ERR_ARG otherwise). Allocates and frees its own scratch; synchronizes the stream. */
 int gpt2_k_encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tok,
                             int B, int T, int C, int V, void* stream);
 

@@ -12,6 +12,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 from decoder_only_transformer_05_amd import binding as gb  # noqa: E402
+from decoder_only_transformer_05_amd import synth  # noqa: E402
 
 
 def dev(a, dtype=None):
@@ -296,15 +297,45 @@ def test_crossentropy_flags_bad_target():
     assert np.all(np.isfinite(host(losses)))
 
 
-@pytest.mark.parametrize("B,T,C,V", [(4, 33, 64, 50), (2, 16, 16, 27), (8, 1024, 768, 50257),
-                                     (3, 700, 16, 40)])
-def test_encoder_forward_backward(B, T, C, V):
+WTE_CHUNK = 32  # the dwte scatter cuts each token's run of sorted positions at multiples of this
+
+
+def dwte_piecewise(flat, dflat, v):
+    """The fp32 sum of token v's rows in the scatter's order: positions ascending, summed in
+    pieces cut at multiples of WTE_CHUNK in the (token, position) sorted order, the pieces
+    then added in order."""
+    idx = np.nonzero(flat == v)[0]
+    first = int(np.count_nonzero(flat < v))  # sorted index of the run's first position
+    acc, piece = None, np.zeros(dflat.shape[1], np.float32)
+    for k, i in enumerate(idx):
+        if k > 0 and (first + k) % WTE_CHUNK == 0:
+            acc = piece if acc is None else acc + piece
+            piece = np.zeros(dflat.shape[1], np.float32)
+        piece = piece + dflat[i]
+    return piece if acc is None else acc + piece
+
+
+@pytest.mark.parametrize("B,T,C,V,mode", [(4, 33, 64, 50, "uniform"), (2, 16, 16, 27, "uniform"),
+                                          (8, 1024, 768, 50257, "uniform"),
+                                          (3, 700, 16, 40, "uniform"),
+                                          (16, 1024, 768, 50257, "zipf"),
+                                          (3, 700, 16, 40, "one token"),
+                                          (2, 100, 64, 7, "few tokens")])
+def test_encoder_forward_backward(B, T, C, V, mode):
+    """Embedding gather and scatter. The Zipf case (the token skew of text: the commonest
+    token some 1,500 times in B16 T1024) and the one-token case (one run of 2,100 positions)
+    cut runs into many pieces; "few tokens" puts run ends at every offset from the cuts."""
     r = rng(B + T + C)
     maxT = T + 3
     wte, wpe = f32(r.normal(size=(V, C))), f32(r.normal(size=(maxT, C)))
-    tok = r.integers(0, V, (B, T)).astype(np.int32)
-    tok[0, : min(T, 9)] = 3  # repeated tokens collide in the scatter
-    tok[-1, -1] = 3
+    if mode == "zipf":
+        tok = synth.batch(1339, B, T, V, mode="zipf")[0]
+    elif mode == "one token":
+        tok = np.full((B, T), 5, np.int32)
+    else:
+        tok = r.integers(0, V, (B, T)).astype(np.int32)
+        tok[0, : min(T, 9)] = 3  # repeated tokens collide in the scatter
+        tok[-1, -1] = 3
     out = torch.empty((B, T, C), device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     gb.k_encoder_forward(out, dev(tok), dev(wte), dev(wpe), B, T, C, V, err)
@@ -325,15 +356,14 @@ def test_encoder_forward_backward(B, T, C, V):
     dwte2 = dev(dwte0)
     gb.k_encoder_backward(dwte2, dev(dwpe0), dev(d), dev(tok), B, T, C, V)
     assert np.array_equal(host(dwte2), g1)
-    # and it is the fp32 sum of each token's rows taken in ascending position order, added
-    # to the old row (positions sorted stably by token, across the sort's 1024-position
-    # chunks): checked bitwise on the tokens that occur
+    # and it is the fp32 sum of each token's rows taken in ascending position order (in
+    # pieces of the sorted order, see dwte_piecewise), added to the old row (positions sorted
+    # stably by token, across the sort's 1024-position chunks): checked bitwise on the
+    # tokens that occur, the most frequent first
     flat, dflat = tok.reshape(-1), d.reshape(-1, C)
-    for v in np.unique(flat)[:64]:
-        acc = np.zeros(C, np.float32)
-        for i in np.nonzero(flat == v)[0]:
-            acc = acc + dflat[i]
-        assert np.array_equal(g1[v], dwte0[v] + acc), v
+    vals, counts = np.unique(flat, return_counts=True)
+    for v in vals[np.argsort(-counts, kind="stable")][:64]:
+        assert np.array_equal(g1[v], dwte0[v] + dwte_piecewise(flat, dflat, v)), v
 
 
 def test_encoder_flags_bad_token():
