@@ -193,7 +193,6 @@ __global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, float* __restri
                               : part + (2LL * chunk + (head ? 0 : 1)) * C;
   for (int c = 4 * lane; c < C; c += 256) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
     for (int r = 0; r < nrow; r++) {
       const int p = __builtin_amdgcn_readlane(pos, r + 1);
       acc += ld4(dout + (long long)p * C + c);
@@ -310,8 +309,8 @@ GPT2_DEVICE_INLINE void lnb_fetch(R (&dy)[VPL], R (&xv)[VPL], const T* dout, con
 // per workgroup, partial[blk][0][:] = sum of n*dout, partial[blk][1][:] = sum of dout over
 // its rows. Each wave sums its rows in order into its own LDS slice (so the column sums
 // take no registers across rows), then the four slices are added in wave order. A wave's
-// next row of dout and x is loaded while the current one is computed; the dx being
-// accumulated into is loaded at the start of its row and used after the two row sums.
+// next row of dout and x, and the dx that row accumulates into, are loaded while the
+// current row is computed.
 // dx is fp32; with 16-bit activations dx_copy (if not null) receives dx rounded to T.
 template <int VPL, typename T>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
@@ -337,10 +336,20 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(N, r0 + rows_per_block);
   typename Raw4<T>::type dyn[VPL], xn[VPL];  // the next row, as stored
+  f32x4 dxn[VPL];                             // and the dx it accumulates into
   float mun = 0.f, rsn = 0.f;
   int row = r0 + wave;
+  auto fetch_dx = [&](int rw) {
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+      const int c4 = lane + 64 * i;
+      dxn[i] = c4 < C4 && accumulate ? ld4(dx + (long long)rw * C + 4 * c4)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
   if (row < r1) {
     lnb_fetch<VPL>(dyn, xn, dout, x, row, C, lane);
+    fetch_dx(row);
     mun = mean[row];
     rsn = rstd[row];
   }
@@ -351,15 +360,12 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     for (int i = 0; i < VPL; i++) {
       dy[i] = widen4(dyn[i]);
       nv[i] = widen4(xn[i]);
+      dxo[i] = dxn[i];
     }
     float* dxr = dx + (long long)row * C;
-#pragma unroll
-    for (int i = 0; i < VPL; i++) {
-      const int c4 = lane + 64 * i;
-      dxo[i] = c4 < C4 && accumulate ? ld4(dxr + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     if (row + 4 < r1) {
       lnb_fetch<VPL>(dyn, xn, dout, x, row + 4, C, lane);
+      fetch_dx(row + 4);
       mun = mean[row + 4];
       rsn = rstd[row + 4];
     }
